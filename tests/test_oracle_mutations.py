@@ -1,0 +1,141 @@
+"""Plausible mistakes planted in the oracle (on the CPU, in this process only)
+must each make at least one pin fail: evidence that the pins constrain every
+step of the oracle, not just its happy path."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle.engram_oracle as E
+import tests.test_oracle_pins as P
+
+
+def _mix_oldest_first(cells, multipliers, n):
+    out = np.zeros(cells.shape[:-1], dtype=np.uint64)
+    for i in range(n):
+        out ^= cells[..., i].astype(np.uint64) * np.uint64(multipliers[n - 1 - i])
+    return out
+
+
+def _mix_add(cells, multipliers, n):
+    out = np.zeros(cells.shape[:-1], dtype=np.uint64)
+    for i in range(n):
+        out += cells[..., i].astype(np.uint64) * np.uint64(multipliers[i])
+    return out
+
+
+def _offsets_inclusive(primes):
+    offs, acc = [], 0
+    for p in primes:
+        acc += int(p)
+        offs.append(acc)
+    return offs, acc
+
+
+def _primes_strictly_above(base, count):
+    out, n = [], base + 1
+    while len(out) < count:
+        if E.is_prime(n):
+            out.append(n)
+        n += 1
+    return out
+
+
+def _cells_block_newer(xc, pad, n_cells, hist=None):
+    """Wrong cascade: a DEAD cell in the window also blanks the newer cells."""
+    cells, dead = _orig["ngram_cells"](xc, pad, n_cells, hist)
+    xc = np.asarray(xc, dtype=np.int64)
+    for t in range(1, xc.shape[1]):
+        older_dead = (xc[:, max(0, t - n_cells + 1):t] == E.DEAD).any(axis=1)
+        cells[older_dead, t, :] = pad
+    return cells, dead
+
+
+def _cells_no_pad_history(xc, pad, n_cells, hist=None):
+    cells, dead = _orig["ngram_cells"](xc, pad, n_cells, hist)
+    cells[:, 0, 1:] = 0
+    return cells, dead
+
+
+def _e8m0_bias128(code):
+    return math.nan if code == 0xFF else math.ldexp(1.0, code - 128)
+
+
+def _round_truncate(x):
+    x = np.asarray(x, dtype=np.float64).astype(np.float32)
+    return (x.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _gate_over_d(h, k, v, q_w, k_w, dead, eps, clamp=0.0):
+    d = h.shape[-1]
+    return _orig["gate"](h, k, v, q_w, k_w, dead, eps, clamp) if d == 1 else \
+        _orig["gate"](np.asarray(h) / math.sqrt(d), k, v, q_w, k_w, dead, eps, clamp)
+
+
+def _gate_plain_sigmoid(h, k, v, q_w, k_w, dead, eps, clamp=0.0):
+    h = np.asarray(h, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    d = h.shape[-1]
+    w = np.asarray(q_w) * np.asarray(k_w)
+    rh = 1 / np.sqrt(np.mean(h * h, -1) + eps)
+    rk = 1 / np.sqrt(np.mean(k * k, -1) + eps)
+    s = np.sum(h * w[None] * k, -1) * rh * rk / math.sqrt(d)
+    a = 1 / (1 + np.exp(-s))
+    a = np.where(np.asarray(dead)[:, None], 0.0, a)
+    return a, h + a[:, :, None] * np.asarray(v)[:, None, :]
+
+
+def _gate_no_weights(h, k, v, q_w, k_w, dead, eps, clamp=0.0):
+    return _orig["gate"](h, k, v, np.ones_like(q_w), np.ones_like(k_w), dead, eps, clamp)
+
+
+def _project_transposed(e, wkv):
+    w = np.asarray(wkv, dtype=np.float64)
+    if w.shape[0] == w.shape[1]:
+        return np.asarray(e, dtype=np.float64) @ w
+    return np.asarray(e, dtype=np.float64) @ w.T[::-1]
+
+
+_orig = {name: getattr(E, name) for name in
+         ("mix_values", "segment_offsets", "primes_from", "ngram_cells", "gate", "project",
+          "round_to_bf16_bits")}
+
+MUTATIONS = [
+    ("mix_values", _mix_oldest_first, [P.test_worked_example_mix_and_indices]),
+    ("mix_values", _mix_add, [P.test_worked_example_mix_and_indices]),
+    ("segment_offsets", _offsets_inclusive, [P.test_worked_example_through_single_table]),
+    ("primes_from", _primes_strictly_above, [P.test_primes_against_sympy]),
+    ("ngram_cells", _cells_block_newer, [P.test_pad_and_dead_cells_c0]),
+    ("ngram_cells", _cells_no_pad_history, [P.test_pad_and_dead_cells_c0]),
+    ("round_to_bf16_bits", _round_truncate, [P.test_round_to_bf16_against_torch]),
+    ("gate", _gate_over_d, [P.test_gate_closed_forms]),
+    ("gate", _gate_plain_sigmoid, [P.test_gate_closed_forms]),
+    ("gate", _gate_no_weights, [P.test_gate_weights_multiply_the_dot]),
+    ("project", _project_transposed, [P.test_projection_one_hot_picks_weight_columns]),
+]
+
+
+@pytest.mark.parametrize("name,mutant,pins", MUTATIONS,
+                         ids=[m[1].__name__ for m in MUTATIONS])
+def test_planted_mistake_is_caught(monkeypatch, name, mutant, pins):
+    monkeypatch.setattr(E, name, mutant)
+    monkeypatch.setattr(P.O, name, mutant, raising=False)
+    caught = False
+    for pin in pins:
+        try:
+            pin()
+        except AssertionError:
+            caught = True
+    assert caught, f"planted mistake in {name} ({mutant.__name__}) passed every pin"
+
+
+def test_planted_scale_bias_is_caught(monkeypatch):
+    table = np.array([_e8m0_bias128(c) for c in range(256)], dtype=np.float64)
+    monkeypatch.setattr(E, "E8M0_TABLE", table)
+    with pytest.raises(AssertionError):
+        P.test_dequant_exhaustive_against_torch_float8()
+
+
+def test_unmutated_pins_pass():
+    for pins in {id(p): p for m in MUTATIONS for p in m[2]}.values():
+        pins()

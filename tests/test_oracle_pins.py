@@ -1,0 +1,546 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these re-types an oracle formula: each compares the oracle with a value
+printed on a page (tests/golden/, with citations), a library routine that
+computes the same thing independently (sympy's primes, torch's float8 and
+bfloat16 conversions), a closed form, an invariant, or brute force.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import sympy
+import torch
+
+import oracle as O
+from workloads import C0, C1, C2, C4, gen
+
+
+def _golden(name):
+    with open(os.path.join(os.path.dirname(__file__), "golden", name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# hash: worked example, prime table, segments
+# ---------------------------------------------------------------------------
+
+def test_worked_example_mix_and_indices():
+    g = _golden("worked_example.json")
+    toks = np.array([g["compressed_tokens"]], dtype=np.int64)
+    mult = g["multipliers_newest_first"]
+    cells, dead = O.ngram_cells(toks, pad=0, n_cells=3)
+    assert not dead.any()
+    t = toks.shape[1] - 1
+    for n_str, exp in g["expected"].items():
+        n = int(n_str)
+        mix = O.mix_values(cells[:, t:t + 1], mult, n)
+        assert int(mix[0, 0]) == exp["mix"]
+        idx = O.head_rows(mix, g["primes_per_order"][n_str], [0, 0])[0, 0]
+        assert idx.tolist() == exp["indices"]
+
+
+def test_worked_example_through_single_table():
+    """Same example through hash_rows: one physical table, offsets = cumsum."""
+    g = _golden("worked_example.json")
+    primes = g["primes_per_order"]["2"] + g["primes_per_order"]["3"]
+    offs, R = O.segment_offsets(primes)
+    assert offs == [0, 101, 204, 311] and R == 420
+    ident = np.arange(256, dtype=np.int32)
+    ids = np.array([g["compressed_tokens"]], dtype=np.int32)
+    rows, _ = O.hash_rows(ids, ident, 256, 0, g["multipliers_newest_first"] + [0],
+                          primes, offs, max_ngram=3, heads=2)
+    e2, e3 = g["expected"]["2"]["indices"], g["expected"]["3"]["indices"]
+    assert rows[3].tolist() == [e2[0], e2[1] + 101, e3[0] + 204, e3[1] + 311]
+    # the leading token lies outside both windows of the last position
+    ids2 = ids.copy()
+    ids2[0, 0] = 7
+    rows2, _ = O.hash_rows(ids2, ident, 256, 0, g["multipliers_newest_first"] + [0],
+                           primes, offs, max_ngram=3, heads=2)
+    assert rows2[3].tolist() == rows[3].tolist()
+
+
+def test_prime_table_of_both_layers():
+    g = _golden("prime_table.json")
+    n = g["primes_per_layer"]
+    p = O.primes_from(g["engram_vocab_size"], 2 * n)
+    for li, layer in enumerate(g["layers"]):
+        seg = p[li * n:(li + 1) * n]
+        assert min(seg) == layer["min_prime"]
+        assert max(seg) == layer["max_prime"]
+        assert sum(seg) == layer["sum"]
+        assert O.segment_offsets(seg)[1] == g["config"]["engram_num_embeddings"][li]
+
+
+def test_primes_against_sympy():
+    for base, count in ((1009, 6), (1_000_000, 24), (16_000_000, 30), (2, 10), (90, 5)):
+        got = O.primes_from(base, count)
+        exp = []
+        q = sympy.nextprime(base - 1)
+        while len(exp) < count:
+            exp.append(int(q))
+            q = sympy.nextprime(q)
+        assert got == exp
+
+
+def test_config_table_values():
+    g = _golden("prime_table.json")["config"]
+    assert C1.compressed_vocab == g["engram_compressed_vocab_size"]
+    assert C1.raw_vocab == g["raw_vocab_size"]
+    assert C1.max_ngram == g["engram_max_ngram_size"]
+    assert C1.heads == g["engram_n_heads"]
+    assert C1.row_dim == g["engram_head_dim"]
+    assert C1.segments * C1.row_dim == 6144
+
+
+def test_layer_facts():
+    f = _golden("layer_facts.json")
+    assert f["rows_per_token_per_layer"] == C1.segments
+    assert f["row_bytes"] == gen.ROW_BYTES
+    assert abs(C1.segments * gen.ROW_BYTES / 1000 - f["bytes_per_token_per_layer_approx_kb"]) < 0.05
+    assert abs(2 * C1.segments * gen.ROW_BYTES / 1024 - f["two_layer_kib_approx"]) < 0.35
+    g = _golden("prime_table.json")["config"]
+    params = sum(g["engram_num_embeddings"]) * g["engram_head_dim"] / 1e9
+    assert abs(params - f["two_table_params_billion_approx"]) < 0.05
+
+
+def _c1_setup(w=C1, tokens=None):
+    tm, mult = gen.hash_setup(w)
+    primes = O.primes_from(w.prime_base, w.segments)
+    offs, R = O.segment_offsets(primes)
+    ids, spans = gen.token_ids(w)
+    if tokens is not None:
+        ids = ids[:, :tokens]
+    return tm, mult, primes, offs, R, ids, spans
+
+
+def test_segments_disjoint_and_cover_table():
+    tm, mult, primes, offs, R, ids, _ = _c1_setup()
+    rows, _ = O.hash_rows(ids, tm, C1.compressed_vocab, int(tm[0]), mult, primes, offs,
+                          C1.max_ngram, C1.heads)
+    assert rows.shape == (C1.tokens, 24)
+    lo = np.array(offs)
+    hi = lo + np.array(primes)
+    assert np.all(rows >= lo) and np.all(rows < hi)
+    assert hi[-1] == R and np.all(lo[1:] == hi[:-1])
+    assert R == _golden("prime_table.json")["config"]["engram_num_embeddings"][0]
+
+
+# ---------------------------------------------------------------------------
+# hash: order sensitivity, incremental mixing, overflow, CRT bound
+# ---------------------------------------------------------------------------
+
+def test_order_sensitivity_all_pairs_c0():
+    _, mult = gen.hash_setup(C0)
+    V = C0.compressed_vocab
+    a, b = np.meshgrid(np.arange(V), np.arange(V), indexing="ij")
+    sel = a != b
+    ab = np.stack([a[sel], b[sel]], -1)       # cells: c0 = A (newest), c1 = B
+    ba = ab[:, ::-1]
+    assert not np.any(O.mix_values(ab, mult, 2) == O.mix_values(ba, mult, 2))
+
+
+def test_order_sensitivity_sampled_full_vocab():
+    _, mult = gen.hash_setup(C1)
+    rng = np.random.default_rng(5)
+    a = rng.integers(0, C1.compressed_vocab, 200_000)
+    b = rng.integers(0, C1.compressed_vocab, 200_000)
+    keep = a != b
+    ab = np.stack([a[keep], b[keep]], -1)
+    assert not np.any(O.mix_values(ab, mult, 2) == O.mix_values(ab[:, ::-1], mult, 2))
+
+
+def test_incremental_mixing():
+    tm, mult, *_ , ids, _ = _c1_setup(tokens=512)
+    xc = O.compress(ids, tm, C1.compressed_vocab)
+    cells, _ = O.ngram_cells(xc, int(tm[0]), 4)
+    m2, m3, m4 = (O.mix_values(cells, mult, n) for n in (2, 3, 4))
+    c = cells.astype(np.uint64)
+    assert np.array_equal(m3, m2 ^ (c[..., 2] * np.uint64(mult[2])))
+    assert np.array_equal(m4, m3 ^ (c[..., 3] * np.uint64(mult[3])))
+
+
+def test_heads_share_one_mix():
+    """The 8 heads of an order are one 64-bit mix taken mod 8 primes: the head
+    rows are congruent to a single value modulo each prime (CRT reconstruction
+    recovers the same mix from any 3 heads at base 16,000,000)."""
+    tm, mult, primes, offs, R, ids, _ = _c1_setup(tokens=64)
+    rows, _ = O.hash_rows(ids, tm, C1.compressed_vocab, int(tm[0]), mult, primes, offs, 4, 8)
+    xc = O.compress(ids, tm, C1.compressed_vocab)
+    cells, _ = O.ngram_cells(xc, int(tm[0]), 4)
+    for n in (2, 3, 4):
+        mix = O.mix_values(cells, mult, n).reshape(-1)
+        z = rows[:, (n - 2) * 8:(n - 1) * 8] - np.array(offs[(n - 2) * 8:(n - 1) * 8])
+        for t in range(0, 64, 7):
+            for trio in ((0, 1, 2), (3, 5, 7)):
+                ps = [primes[(n - 2) * 8 + k] for k in trio]
+                rs = [int(z[t, k]) for k in trio]
+                rec, mod = sympy.ntheory.modular.crt(ps, rs)
+                assert int(rec) == int(mix[t]) and mod > 2 ** 63
+
+
+def test_no_overflow():
+    for w in (C0, C1):
+        _, mult = gen.hash_setup(w)
+        lim = O.multiplier_limit(w.compressed_vocab)
+        assert lim == ((1 << 63) - 1) // w.compressed_vocab
+        for m in mult:
+            assert m % 2 == 1 and 0 < m <= lim
+            assert (w.compressed_vocab - 1) * m <= (1 << 63) - 1
+    tm, mult, primes, offs, R, ids, _ = _c1_setup()
+    xc = O.compress(ids, tm, C1.compressed_vocab)
+    cells, _ = O.ngram_cells(xc, int(tm[0]), 4)
+    for n in (2, 3, 4):
+        assert int(O.mix_values(cells, mult, n).max()) < (1 << 63)
+
+
+def test_crt_bound_closed_form():
+    two63 = 2 ** 63
+    for base, bound in ((16_000_000, 2), (1_000_000, 3)):
+        p = sorted(O.primes_from(base, 24))
+        # fewest-digit products decide: any bound+1 primes multiply past 2^63
+        assert math.prod(p[:bound + 1]) > two63
+        assert math.prod(p[:bound]) < two63 or bound == 2
+    p16 = sorted(O.primes_from(16_000_000, 24))
+    assert math.prod(p16[:3]) > 4.0e21            # page: about 4 x 10^21
+
+
+def test_crt_bound_brute_force_tiny():
+    primes = [11, 13, 17, 19, 23, 29, 31, 37]
+    offs = [0] * 8
+    lim = 11 * 13 * 17
+    a = np.arange(lim, dtype=np.uint64)
+    z = O.head_rows(a, primes, offs)                 # [lim, 8]
+    worst = 0
+    for i in range(lim - 1):
+        shared = (z[i + 1:] == z[i]).sum(axis=1)
+        worst = max(worst, int(shared.max()))
+    assert worst == 2
+    # tight: b = a + 11*13 shares exactly heads {11, 13}
+    for a0 in (0, 5, 100, 2000):
+        b0 = a0 + 11 * 13
+        same = np.nonzero(O.head_rows(np.array([a0], np.uint64), primes, offs)[0]
+                          == O.head_rows(np.array([b0], np.uint64), primes, offs)[0])[0]
+        assert same.tolist() == [0, 1]
+
+
+def test_crt_bound_full_shape():
+    tm, mult, primes, offs, R, ids, _ = _c1_setup()
+    P = primes[8:16]                               # order 3 heads
+    rng = np.random.default_rng(9)
+    xc = O.compress(ids, tm, C1.compressed_vocab)
+    cells, _ = O.ngram_cells(xc, int(tm[0]), 4)
+    mix = np.unique(O.mix_values(cells, mult, 3).reshape(-1))
+    z = O.head_rows(mix, P, [0] * 8)
+    i = rng.integers(0, len(mix), 200_000)
+    j = rng.integers(0, len(mix), 200_000)
+    keep = i != j
+    assert (z[i[keep]] == z[j[keep]]).sum(axis=1).max() <= 2
+    for (hi, hj) in ((0, 1), (2, 7), (4, 5)):
+        a0 = int(mix[3])
+        b0 = a0 + P[hi] * P[hj]
+        same = np.nonzero(O.head_rows(np.array([a0], np.uint64), P, [0] * 8)[0]
+                          == O.head_rows(np.array([b0], np.uint64), P, [0] * 8)[0])[0]
+        assert same.tolist() == sorted([hi, hj])
+
+
+# ---------------------------------------------------------------------------
+# hash: pad and DEAD semantics, history
+# ---------------------------------------------------------------------------
+
+def test_pad_and_dead_cells_c0():
+    tm, mult = gen.hash_setup(C0)
+    pad = int(tm[0])
+    ids, spans = gen.token_ids(C0)
+    assert spans[0] == [(20, 28)]
+    xc = O.compress(ids, tm, C0.compressed_vocab)
+    cells, dead = O.ngram_cells(xc, pad, 4)
+    c = cells[0]
+    x = xc[0]
+    assert c[0].tolist() == [x[0], pad, pad, pad]
+    assert c[1].tolist() == [x[1], x[0], pad, pad]
+    assert c[2].tolist() == [x[2], x[1], x[0], pad]
+    assert dead[0, 20:28].all() and not dead[0, :20].any() and not dead[0, 28:].any()
+    for t in range(20, 28):
+        assert c[t].tolist() == [pad] * 4
+    assert c[28].tolist() == [x[28], pad, pad, pad]
+    assert c[29].tolist() == [x[29], x[28], pad, pad]
+    assert c[30].tolist() == [x[30], x[29], x[28], pad]
+    for t in list(range(3, 20)) + list(range(31, 64)):
+        assert c[t].tolist() == [x[t], x[t - 1], x[t - 2], x[t - 3]]
+
+
+def test_dead_rows_are_the_all_pad_ngram():
+    tm, mult = gen.hash_setup(C0)
+    pad = int(tm[0])
+    primes = O.primes_from(C0.prime_base, C0.segments)
+    offs, R = O.segment_offsets(primes)
+    ids, _ = gen.token_ids(C0)
+    rows, _ = O.hash_rows(ids, tm, C0.compressed_vocab, pad, mult, primes, offs, 4, 2)
+    all_pad = np.array([[0, pad, pad, pad, pad]])[:, 1:]
+    # an all-pad sequence of length 4 gives the all-pad n-gram at t = 3
+    pad_raw = np.zeros((1, 4), np.int32)
+    rows_pad, _ = O.hash_rows(pad_raw, tm, C0.compressed_vocab, pad, mult, primes, offs, 4, 2)
+    for t in range(20, 28):
+        assert rows[t].tolist() == rows_pad[3].tolist()
+    assert all_pad.shape == (1, 4)
+
+
+def test_invalid_ids_count_as_dead():
+    tm, mult, primes, offs, R, ids, _ = _c1_setup(tokens=64)
+    pad = int(tm[0])
+    bad = ids[:1].copy()
+    bad[0, 10] = C1.raw_vocab + 5
+    bad[0, 20] = -7
+    dead = ids[:1].copy()
+    dead[0, 10] = -1
+    dead[0, 20] = -1
+    r1, h1 = O.hash_rows(bad, tm, C1.compressed_vocab, pad, mult, primes, offs, 4, 8)
+    r2, h2 = O.hash_rows(dead, tm, C1.compressed_vocab, pad, mult, primes, offs, 4, 8)
+    assert np.array_equal(r1, r2) and np.array_equal(h1, h2)
+
+
+@pytest.mark.parametrize("splits", [(1,), (2,), (3,), (5, 17), (255, 256, 257), (1, 2, 3, 4)])
+def test_chunked_prefill_equals_one_shot(splits):
+    tm, mult, primes, offs, R, ids, _ = _c1_setup()
+    pad = int(tm[0])
+    seq = ids[:2, 600:1200].copy()          # crosses a DEAD span boundary in some rows
+    seq[1, 255:259] = -1
+    full, hfull = O.hash_rows(seq, tm, C1.compressed_vocab, pad, mult, primes, offs, 4, 8)
+    full = full.reshape(2, -1, 24)
+    bounds = [0] + list(splits) + [seq.shape[1]]
+    hist = None
+    parts = []
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        r, hist = O.hash_rows(seq[:, a:b], tm, C1.compressed_vocab, pad, mult, primes, offs,
+                              4, 8, hist=hist)
+        parts.append(r.reshape(2, b - a, 24))
+    assert np.array_equal(np.concatenate(parts, axis=1), full)
+    assert np.array_equal(hist, hfull)
+
+
+def test_decode_with_history_equals_prefill_tail():
+    tm, mult, primes, offs, R, ids, _ = _c1_setup()
+    pad = int(tm[0])
+    seq = ids[:4, 1000:1040].copy()
+    seq[2, 37] = -1
+    seq[3, 39] = -1
+    full, _ = O.hash_rows(seq, tm, C1.compressed_vocab, pad, mult, primes, offs, 4, 8)
+    full = full.reshape(4, -1, 24)
+    _, hist = O.hash_rows(seq[:, :-1], tm, C1.compressed_vocab, pad, mult, primes, offs, 4, 8)
+    step, hist2 = O.hash_rows(seq[:, -1:], tm, C1.compressed_vocab, pad, mult, primes, offs,
+                              4, 8, hist=hist)
+    assert np.array_equal(step.reshape(4, 24), full[:, -1])
+    xc = O.compress(seq, tm, C1.compressed_vocab)
+    assert np.array_equal(hist2, xc[:, -3:].astype(np.int32))
+
+
+def test_history_of_short_chunks():
+    tm, mult, primes, offs, R, ids, _ = _c1_setup(tokens=8)
+    pad = int(tm[0])
+    xc = O.compress(ids[:1], tm, C1.compressed_vocab)
+    _, h = O.hash_rows(ids[:1, :1], tm, C1.compressed_vocab, pad, mult, primes, offs, 4, 8)
+    assert h[0].tolist() == [pad, pad, int(xc[0, 0])]
+    _, h0 = O.hash_rows(ids[:1, :0], tm, C1.compressed_vocab, pad, mult, primes, offs, 4, 8,
+                        hist=np.array([[5, -1, 7]], np.int32))
+    assert h0[0].tolist() == [5, -1, 7]
+
+
+def test_decode_dead_sequence_reads_all_pad_rows():
+    """C4's sequence 0: new id DEAD, history all DEAD -> the all-pad n-gram."""
+    tm, mult = gen.hash_setup(C4)
+    pad = int(tm[0])
+    primes = O.primes_from(C4.prime_base, 24)
+    offs, _ = O.segment_offsets(primes)
+    ids, _ = gen.token_ids(C4)
+    hist = gen.history(C4, tm)
+    assert ids[0, 0] == -1 and hist[0].tolist() == [-1, -1, -1]
+    rows, hout = O.hash_rows(ids, tm, C4.compressed_vocab, pad, mult, primes, offs, 4, 8,
+                             hist=hist)
+    pad4, _ = O.hash_rows(np.zeros((1, 4), np.int32), tm, C4.compressed_vocab, pad, mult,
+                          primes, offs, 4, 8)
+    assert rows[0].tolist() == pad4[3].tolist()
+    assert hout[0].tolist() == [-1, -1, -1]
+
+
+# ---------------------------------------------------------------------------
+# dequantisation and bf16 rounding against torch's float8 / bfloat16
+# ---------------------------------------------------------------------------
+
+def test_dequant_exhaustive_against_torch_float8():
+    codes = np.arange(256, dtype=np.uint8)
+    q = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).float()
+    s = torch.from_numpy(codes.copy()).view(torch.float8_e8m0fnu).float()
+    prod = (q[None, :] * s[:, None])                 # [scale, code], exact in fp32
+    ref = prod.to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    rows = np.zeros((256, 8, 264), dtype=np.uint8)   # 8 rows per scale cover 256 codes
+    for S in range(256):
+        for r in range(8):
+            rows[S, r, :256] = codes[(r * 32 + np.arange(256)) % 256]
+            rows[S, r, 256:] = S
+    got = O.dequant_rows_bf16(rows.reshape(-1, 264)).reshape(256, 8, 256)
+    for S in range(256):
+        for r in range(8):
+            cs = (r * 32 + np.arange(256)) % 256
+            exp = ref[S, cs]
+            g = got[S, r]
+            nan_e = np.isnan(prod[S, cs].numpy())
+            nan_g = ((g & 0x7F80) == 0x7F80) & ((g & 0x7F) != 0)
+            assert np.array_equal(nan_e, nan_g)
+            assert np.array_equal(g[~nan_e], exp[~nan_e])
+    # the workloads' scale range 120..134 never leaves the bf16 normal range
+    for S in range(120, 135):
+        fin = ~np.isnan(prod[S].numpy())
+        v = np.abs(prod[S].numpy()[fin]).astype(np.float64)
+        v = v[v > 0]
+        assert v.min() >= 2.0 ** -126 and v.max() < 2.0 ** 128
+
+
+def test_round_to_bf16_against_torch():
+    rng = np.random.default_rng(3)
+    parts = [
+        rng.standard_normal(200_000).astype(np.float32) * np.float32(1e3),
+        (rng.integers(0, 2 ** 32, 200_000, dtype=np.uint64).astype(np.uint32)).view(np.float32),
+        np.array([0.0, -0.0, 1.0, 1.00390625, 1.01171875, 3.3895314e38, -3.3895314e38,
+                  1e-40, -1e-42, 1.17549435e-38, 9.18e-41, np.inf, -np.inf], dtype=np.float32),
+    ]
+    x = np.concatenate(parts)
+    x = x[~np.isnan(x)]
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    got = O.round_to_bf16_bits(x.astype(np.float64))
+    assert np.array_equal(got, ref)
+    # halfway cases built to exercise ties-to-even on both sides
+    base = rng.integers(0, 2 ** 15, 10_000).astype(np.uint32) << np.uint32(16)
+    half = (base | np.uint32(0x8000)).view(np.float32)
+    half = half[np.isfinite(half)]
+    ref = torch.from_numpy(half.copy()).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    assert np.array_equal(O.round_to_bf16_bits(half.astype(np.float64)), ref)
+
+
+def test_gather_zero_rows_and_copy():
+    table = np.arange(40 * 8, dtype=np.float32).reshape(40, 8)
+    rid = np.array([[0, 39, 40, -1], [7, 1_000_000, 3, 3]], dtype=np.int64)
+    e = O.gather_f32(table, rid).reshape(2, 4, 8)
+    assert np.array_equal(e[0, 0], table[0]) and np.array_equal(e[0, 1], table[39])
+    assert not e[0, 2].any() and not e[0, 3].any() and not e[1, 1].any()
+    assert np.array_equal(e[1, 2], table[3]) and np.array_equal(e[1, 0], table[7])
+    rows = gen.table_rows(11, np.arange(16))
+    got = O.gather_e4m3(lambda r: gen.table_rows(11, r), np.array([[3, 16, -2, 15]]), 16)
+    got = got.reshape(4, 256)
+    assert not got[1].any() and not got[2].any()
+    assert np.array_equal(got[0], O.dequant_rows_bf16(rows[3])[0])
+    assert np.array_equal(got[3], O.dequant_rows_bf16(rows[15])[0])
+
+
+def test_table_rows_format():
+    rows = gen.table_rows(2002, np.array([0, 1, 24_003_915, 384_006_167]))
+    pay, sc = rows[:, :256], rows[:, 256:]
+    assert not np.any(pay == 0x7F) and not np.any(pay == 0xFF)
+    assert sc.min() >= 120 and sc.max() <= 134
+
+
+# ---------------------------------------------------------------------------
+# projection and gate: special cases and closed forms
+# ---------------------------------------------------------------------------
+
+def test_projection_one_hot_picks_weight_columns():
+    rng = np.random.default_rng(1)
+    W = rng.standard_normal((40, 24))              # [(hc+1)*d, K]
+    e = np.zeros((24, 24))
+    e[np.arange(24), np.arange(24)] = 1.0
+    kv = O.project(e, W)
+    assert np.array_equal(kv, W.T)
+    e2 = np.zeros((3, 24))
+    e2[0, 5] = 2.0
+    e2[1, 0] = -0.5
+    e2[1, 23] = 4.0
+    kv2 = O.project(e2, W)
+    assert np.array_equal(kv2[0], 2.0 * W[:, 5])
+    assert np.array_equal(kv2[1], -0.5 * W[:, 0] + 4.0 * W[:, 23])
+    assert not kv2[2].any()
+
+
+def _unit_gate(h, k, d, dead=False, clamp=0.0, eps=1e-6):
+    ones = np.ones((1, d))
+    v = np.ones((1, d))
+    return O.gate(h.reshape(1, 1, d), k.reshape(1, 1, d), v, ones, ones,
+                  np.array([dead]), eps=eps, clamp=clamp)
+
+
+def test_gate_closed_forms():
+    f = _golden("layer_facts.json")
+    d = f["d"]
+    rng = np.random.default_rng(2)
+    h = rng.standard_normal(d)
+    # h parallel to k: s = sqrt(d) (up to eps), alpha = sigmoid(d^(1/4))
+    a, _ = _unit_gate(h, 3.0 * h, d)
+    s = math.sqrt(d)
+    assert abs(s - f["s_max_abs"]) < 0.05
+    assert abs(math.sqrt(s) - f["signed_sqrt_max_abs"]) < 0.05
+    assert abs(a[0, 0] - 1 / (1 + math.exp(-math.sqrt(s)))) < 1e-9
+    assert abs(a[0, 0] - 0.99979) < 1e-5
+    a, _ = _unit_gate(h, -h, d)
+    assert abs(a[0, 0] - 1 / (1 + math.exp(math.sqrt(s)))) < 1e-9
+    assert abs(a[0, 0] - 2.1e-4) < 1e-5
+    # h orthogonal to k: s = 0, alpha = 1/2
+    k = rng.standard_normal(d)
+    k -= h * (k @ h) / (h @ h)
+    a, _ = _unit_gate(h, k, d)
+    assert abs(a[0, 0] - 0.5) < 1e-6       # |s| ~ 1e-16 residue, amplified by the root
+    # cosine: s = sqrt(d) cos(theta) for unit weights, |s| <= sqrt(d)
+    for _ in range(5):
+        k = rng.standard_normal(d)
+        cos = (h @ k) / np.linalg.norm(h) / np.linalg.norm(k)
+        a, _ = _unit_gate(h, k, d)
+        sg = math.copysign(math.sqrt(abs(s * cos)), cos)
+        assert abs(a[0, 0] - 1 / (1 + math.exp(-sg))) < 1e-6
+
+
+def test_gate_is_scale_invariant_and_clamped():
+    d = 256
+    rng = np.random.default_rng(4)
+    h, k = rng.standard_normal(d), rng.standard_normal(d)
+    a1, _ = _unit_gate(h, k, d, eps=0.0)
+    a2, _ = _unit_gate(7.0 * h, 0.25 * k, d, eps=0.0)
+    assert abs(a1[0, 0] - a2[0, 0]) < 1e-9
+    # eps sits inside the root: a tiny k is damped towards s = 0
+    a3, _ = _unit_gate(h, 1e-6 * k, d, eps=1e-6)
+    assert abs(a3[0, 0] - 0.5) < abs(a1[0, 0] - 0.5) / 10
+    k0 = k - h * (k @ h) / (h @ h)           # s = 0
+    a, _ = _unit_gate(h, k0, d, clamp=4.0)
+    assert abs(abs(a[0, 0] - 0.5) - abs(1 / (1 + math.exp(-2.0)) - 0.5)) < 1e-9
+
+
+def test_gate_dead_and_zero_value_leave_h():
+    d, hc, T = 64, 2, 3
+    rng = np.random.default_rng(6)
+    h = rng.standard_normal((T, hc, d))
+    k = rng.standard_normal((T, hc, d))
+    v = rng.standard_normal((T, d))
+    qw = 1 + 0.1 * rng.standard_normal((hc, d))
+    kw = 1 + 0.1 * rng.standard_normal((hc, d))
+    dead = np.array([False, True, False])
+    a, h2 = O.gate(h, k, v, qw, kw, dead, 1e-6)
+    assert np.all(a[1] == 0) and np.array_equal(h2[1], h[1])
+    assert np.all((a[[0, 2]] > 0) & (a[[0, 2]] < 1))
+    np.testing.assert_allclose(h2[0], h[0] + a[0][:, None] * v[0][None], rtol=0, atol=1e-12)
+    a0, h3 = O.gate(h, k, np.zeros_like(v), qw, kw, np.zeros(T, bool), 1e-6)
+    assert np.array_equal(h3, h)
+
+
+def test_gate_weights_multiply_the_dot():
+    """With q_w * k_w = c on one stream the score scales by c (before the root)."""
+    d = 128
+    rng = np.random.default_rng(8)
+    h = rng.standard_normal((1, 1, d))
+    k = h + 0.3 * rng.standard_normal((1, 1, d))
+    v = np.zeros((1, d))
+    one = np.ones((1, d))
+    a1, _ = O.gate(h, k, v, one, one, np.array([False]), 0.0)
+    a2, _ = O.gate(h, k, v, 2.0 * one, 0.5 * one, np.array([False]), 0.0)
+    a3, _ = O.gate(h, k, v, 0.5 * one, 0.5 * one, np.array([False]), 0.0)
+    logit = lambda a: math.log(a / (1 - a))
+    assert abs(a1[0, 0] - a2[0, 0]) < 1e-12
+    assert abs(logit(a3[0, 0]) ** 2 - 0.25 * logit(a1[0, 0]) ** 2) < 1e-9
