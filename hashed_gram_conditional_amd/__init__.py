@@ -1,0 +1,14 @@
+"""Engram conditional-memory layer forward for MI355X (gfx950).
+
+The computation runs in the HIP kernels of ``libengram.so`` behind the C ABI of
+``include/engram.h``; this package is its thin Python binding (torch tensors
+in, raw pointers out). Importing it fails if the library is not built.
+"""
+from ._binding import (  # noqa: F401
+    DEAD, MAX_NGRAM, MAX_SEGMENTS, ROW_BYTES, ROW_E4M3_E8M0_264, ROW_F32,
+    OK, EINVAL, EVOCAB, EMULT, ESHAPE, EWORKSPACE, EHIP, EPRIMES,
+    EngramError, HashParams, ForwardDesc, LIB, LIB_PATH,
+    status_string, hash_params, forward_desc,
+    engram_make_primes, engram_check_token_map, engram_hash, engram_gather,
+    engram_project, engram_gate, engram_forward_workspace_size, engram_forward,
+)

@@ -1,0 +1,196 @@
+"""ctypes binding of libengram.so (include/engram.h).
+
+Argument marshalling only: torch tensors are passed as raw device pointers and
+every step runs in the library's HIP kernels. There is no fallback: importing
+this module fails loudly when the built library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libengram.so")
+
+DEAD = -1
+MAX_NGRAM = 8
+MAX_SEGMENTS = 64
+ROW_BYTES = 264
+ROW_E4M3_E8M0_264 = 0
+ROW_F32 = 1
+
+OK, EINVAL, EVOCAB, EMULT, ESHAPE, EWORKSPACE, EHIP, EPRIMES = 0, -1, -2, -3, -4, -5, -6, -7
+
+
+class EngramError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class HashParams(ctypes.Structure):
+    _fields_ = [
+        ("raw_vocab", ctypes.c_int32),
+        ("compressed_vocab", ctypes.c_int32),
+        ("max_ngram", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("pad_id", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("token_map", ctypes.c_void_p),
+        ("multipliers", ctypes.c_int64 * MAX_NGRAM),
+        ("primes", ctypes.c_int64 * MAX_SEGMENTS),
+        ("offsets", ctypes.c_int64 * MAX_SEGMENTS),
+    ]
+
+
+class ForwardDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64),
+        ("seq", ctypes.c_int64),
+        ("hc", ctypes.c_int32),
+        ("dim", ctypes.c_int32),
+        ("table_rows", ctypes.c_int64),
+        ("row_format", ctypes.c_int32),
+        ("row_dim", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+        ("gate_clamp", ctypes.c_float),
+    ]
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(python hashed_gram_conditional_amd/build.py)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "engram_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "engram_sizeof_hash_params": (SZ, []),
+        "engram_sizeof_forward_desc": (SZ, []),
+        "engram_make_primes": (ctypes.c_int, [I64, I32, P, P, P]),
+        "engram_check_token_map": (ctypes.c_int, [P, I32, I32]),
+        "engram_hash": (ctypes.c_int, [P, P, I64, I64, P, P, P, P]),
+        "engram_gather": (ctypes.c_int, [P, I64, I32, I32, P, I64, P, P]),
+        "engram_project": (ctypes.c_int, [P, P, P, I64, I64, I64, I32, P]),
+        "engram_gate": (ctypes.c_int, [P, P, I32, P, P, P, P, P, P]),
+        "engram_forward_workspace_size": (SZ, [P, P]),
+        "engram_forward": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if lib.engram_sizeof_hash_params() != ctypes.sizeof(HashParams):
+        raise ImportError("engram_hash_params layout mismatch between binding and library")
+    if lib.engram_sizeof_forward_desc() != ctypes.sizeof(ForwardDesc):
+        raise ImportError("engram_forward_desc layout mismatch between binding and library")
+    return lib
+
+
+LIB = _load()
+LIB_PATH = _LIB_PATH
+
+
+def status_string(status: int) -> str:
+    return LIB.engram_status_string(int(status)).decode()
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise EngramError(status, where)
+
+
+def hash_params(raw_vocab: int, compressed_vocab: int, max_ngram: int, heads: int,
+                pad_id: int, token_map, multipliers: Sequence[int], primes: Sequence[int],
+                offsets: Sequence[int]) -> HashParams:
+    """Fill an engram_hash_params (token_map: device int32 tensor or pointer)."""
+    p = HashParams()
+    p.raw_vocab, p.compressed_vocab = raw_vocab, compressed_vocab
+    p.max_ngram, p.heads, p.pad_id, p.reserved = max_ngram, heads, pad_id, 0
+    p.token_map = _ptr(token_map)
+    for i, m in enumerate(multipliers):
+        p.multipliers[i] = int(m)
+    for j, (pr, off) in enumerate(zip(primes, offsets)):
+        p.primes[j] = int(pr)
+        p.offsets[j] = int(off)
+    return p
+
+
+def forward_desc(batch: int, seq: int, hc: int, dim: int, table_rows: int, row_format: int,
+                 row_dim: int, eps: float = 1e-6, gate_clamp: float = 0.0) -> ForwardDesc:
+    d = ForwardDesc()
+    d.batch, d.seq, d.hc, d.dim = batch, seq, hc, dim
+    d.table_rows, d.row_format, d.row_dim = table_rows, row_format, row_dim
+    d.eps, d.gate_clamp = eps, gate_clamp
+    return d
+
+
+def engram_make_primes(base: int, count: int):
+    """[host] (primes, offsets, total_rows) of the first ``count`` primes >= base."""
+    pr = (ctypes.c_int64 * max(count, 1))()
+    off = (ctypes.c_int64 * max(count, 1))()
+    tot = ctypes.c_int64()
+    _check(LIB.engram_make_primes(base, count, ctypes.addressof(pr), ctypes.addressof(off),
+                                  ctypes.addressof(tot)), "engram_make_primes")
+    return list(pr)[:count], list(off)[:count], tot.value
+
+
+def engram_check_token_map(token_map, raw_vocab: int, compressed_vocab: int) -> int:
+    """[host] status of the start-up check of a host int32 map (numpy array)."""
+    import numpy as np
+    arr = np.ascontiguousarray(token_map, dtype=np.int32)
+    return LIB.engram_check_token_map(arr.ctypes.data, raw_vocab, compressed_vocab)
+
+
+def engram_hash(params: HashParams, ids, batch: int, seq: int, hist_in, hist_out, row_ids,
+                stream=None):
+    _check(LIB.engram_hash(ctypes.byref(params), _ptr(ids), batch, seq, _ptr(hist_in),
+                           _ptr(hist_out), _ptr(row_ids), _stream(stream)), "engram_hash")
+
+
+def engram_gather(table, table_rows: int, row_format: int, row_dim: int, row_ids, n_ids: int,
+                  out, stream=None):
+    _check(LIB.engram_gather(_ptr(table), table_rows, row_format, row_dim, _ptr(row_ids),
+                             n_ids, _ptr(out), _stream(stream)), "engram_gather")
+
+
+def engram_project(e, wkv, kv, tokens: int, in_dim: int, out_dim: int, act_f32: int,
+                   stream=None):
+    _check(LIB.engram_project(_ptr(e), _ptr(wkv), _ptr(kv), tokens, in_dim, out_dim, act_f32,
+                              _stream(stream)), "engram_project")
+
+
+def engram_gate(desc: ForwardDesc, ids, raw_vocab: int, kv, q_w, k_w, h, gate_out,
+                stream=None):
+    _check(LIB.engram_gate(ctypes.byref(desc), _ptr(ids), raw_vocab, _ptr(kv), _ptr(q_w),
+                           _ptr(k_w), _ptr(h), _ptr(gate_out), _stream(stream)), "engram_gate")
+
+
+def engram_forward_workspace_size(params: HashParams, desc: ForwardDesc) -> int:
+    return int(LIB.engram_forward_workspace_size(ctypes.byref(params), ctypes.byref(desc)))
+
+
+def engram_forward(params: HashParams, desc: ForwardDesc, ids, hist_in, hist_out, table, wkv,
+                   q_w, k_w, h, gate_out, workspace, workspace_bytes: int, stream=None):
+    _check(LIB.engram_forward(ctypes.byref(params), ctypes.byref(desc), _ptr(ids),
+                              _ptr(hist_in), _ptr(hist_out), _ptr(table), _ptr(wkv),
+                              _ptr(q_w), _ptr(k_w), _ptr(h), _ptr(gate_out),
+                              _ptr(workspace), workspace_bytes, _stream(stream)),
+           "engram_forward")

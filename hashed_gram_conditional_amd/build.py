@@ -1,0 +1,41 @@
+"""Build step of libengram.so: compiles the HIP sources for gfx950 in-tree.
+
+Run ``python hashed_gram_conditional_amd/build.py`` (or ``__graft_entry__.build()``).
+"""
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SOURCES = ["hash.hip", "gather.hip", "gemm.hip", "gate.hip", "engram_api.hip"]
+LIB = os.path.join(PKG, "libengram.so")
+
+# Packed-fp32 instructions are disabled for every HIP translation unit.
+HIP_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc():
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return os.path.join(rocm, "bin", "hipcc")
+
+
+def build_library(verbose: bool = False) -> str:
+    srcs = [os.path.join(PKG, "csrc", s) for s in SOURCES]
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *srcs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed building {LIB}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build_library(verbose=True))

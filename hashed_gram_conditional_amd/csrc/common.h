@@ -1,0 +1,71 @@
+// Shared device helpers of the Engram HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "engram.h"
+
+namespace engram {
+
+constexpr int kWave = 64;
+
+// bf16 bit pattern of a float, rounded to nearest with ties to even. Exact for
+// subnormals (the encoding is linear there) and rounds finite overflow to inf.
+// NaN inputs are handled by the callers that can see them.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) {
+  return __uint_as_float(b16 << 16);
+}
+
+// Two bf16 (low half = first element) from two floats, nearest-even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+__device__ __forceinline__ float warp_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+}  // namespace engram
+
+// Launchers implemented by the kernel translation units. They validate nothing:
+// the C-ABI layer checks every argument first. Each returns hipSuccess or the
+// launch error.
+struct EngramHashArgs {
+  int32_t raw_vocab, compressed_vocab, max_ngram, heads, segments, pad_id;
+  uint64_t mult[ENGRAM_MAX_NGRAM];
+  uint32_t prime[ENGRAM_MAX_SEGMENTS];
+  uint64_t recip[ENGRAM_MAX_SEGMENTS];   // floor((2^64 - 1) / prime)
+  int64_t offset[ENGRAM_MAX_SEGMENTS];
+};
+
+hipError_t engram_launch_hash(const EngramHashArgs &a, const int32_t *token_map,
+                              const int32_t *ids, int64_t batch, int64_t seq,
+                              const int32_t *hist_in, int32_t *hist_out,
+                              int64_t *row_ids, hipStream_t stream);
+
+hipError_t engram_launch_gather_e4m3(const uint8_t *table, int64_t table_rows,
+                                     const int64_t *row_ids, int64_t n_ids,
+                                     uint16_t *out, hipStream_t stream);
+
+hipError_t engram_launch_gather_f32(const float *table, int64_t table_rows,
+                                    int32_t row_dim, const int64_t *row_ids,
+                                    int64_t n_ids, float *out, hipStream_t stream);
+
+hipError_t engram_launch_gemm_bf16(const uint16_t *e, const uint16_t *w, uint16_t *kv,
+                                   int64_t m, int64_t n, int64_t k, hipStream_t stream);
+
+hipError_t engram_launch_gemm_f32(const float *e, const float *w, float *kv, int64_t m,
+                                  int64_t n, int64_t k, hipStream_t stream);
+
+hipError_t engram_launch_gate(bool f32, const int32_t *ids, int32_t raw_vocab,
+                              const void *kv, const float *q_w, const float *k_w,
+                              void *h, float *gate_out, int64_t tokens, int32_t hc,
+                              int32_t dim, float eps, float clamp, hipStream_t stream);

@@ -1,0 +1,337 @@
+// C ABI of the Engram layer forward: argument validation on the host, then the
+// stage launches on the caller's stream. Declarations and the contract of every
+// entry point are in include/engram.h.
+#include <stdlib.h>
+#include <string.h>
+
+#include "common.h"
+
+namespace {
+
+constexpr int64_t kInt63Max = INT64_MAX;
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ---- deterministic Miller-Rabin for 64-bit integers --------------------------
+// The bases 2, 3, 5, 7, 11, 13, 17, 19, 23, 29, 31 and 37 decide primality for
+// every n < 3.3 * 10^24 (Sorenson & Webster, "Strong pseudoprimes to twelve
+// prime bases", Math. Comp. 86, 2017).
+uint64_t mulmod(uint64_t a, uint64_t b, uint64_t m) {
+  return (uint64_t)((unsigned __int128)a * b % m);
+}
+
+uint64_t powmod(uint64_t a, uint64_t e, uint64_t m) {
+  uint64_t r = 1 % m;
+  a %= m;
+  while (e) {
+    if (e & 1) r = mulmod(r, a, m);
+    a = mulmod(a, a, m);
+    e >>= 1;
+  }
+  return r;
+}
+
+bool is_prime_mr(uint64_t n) {
+  static const uint64_t bases[] = {2, 3, 5, 7, 11, 13, 17, 19, 23, 29, 31, 37};
+  if (n < 2) return false;
+  for (uint64_t p : bases) {
+    if (n % p == 0) return n == p;
+  }
+  uint64_t d = n - 1;
+  int s = 0;
+  while ((d & 1) == 0) {
+    d >>= 1;
+    ++s;
+  }
+  for (uint64_t a : bases) {
+    uint64_t x = powmod(a, d, n);
+    if (x == 1 || x == n - 1) continue;
+    bool composite = true;
+    for (int i = 1; i < s; ++i) {
+      x = mulmod(x, x, n);
+      if (x == n - 1) {
+        composite = false;
+        break;
+      }
+    }
+    if (composite) return false;
+  }
+  return true;
+}
+
+// ---- validation -----------------------------------------------------------------
+int check_hash_params(const engram_hash_params *p) {
+  if (p == nullptr) return ENGRAM_EINVAL;
+  if (p->raw_vocab < 1 || p->compressed_vocab < 1 || p->reserved != 0) return ENGRAM_EINVAL;
+  if (p->max_ngram < 2 || p->max_ngram > ENGRAM_MAX_NGRAM || p->heads < 1) return ENGRAM_ESHAPE;
+  if ((int64_t)(p->max_ngram - 1) * p->heads > ENGRAM_MAX_SEGMENTS) return ENGRAM_ESHAPE;
+  if (p->pad_id < 0 || p->pad_id >= p->compressed_vocab) return ENGRAM_EINVAL;
+  if (p->token_map == nullptr || !aligned(p->token_map, 4)) return ENGRAM_EINVAL;
+  const int64_t bound = kInt63Max / p->compressed_vocab;
+  for (int i = 0; i < p->max_ngram; ++i) {
+    const int64_t m = p->multipliers[i];
+    if (m < 1 || m > bound || (m & 1) == 0) return ENGRAM_EMULT;
+  }
+  const int S = (p->max_ngram - 1) * p->heads;
+  int64_t acc = 0;
+  for (int j = 0; j < S; ++j) {
+    const int64_t pr = p->primes[j];
+    if (pr < 2 || pr > (int64_t)UINT32_MAX) return ENGRAM_EPRIMES;
+    if (p->offsets[j] != acc) return ENGRAM_EPRIMES;
+    acc += pr;
+  }
+  return ENGRAM_OK;
+}
+
+int64_t total_rows(const engram_hash_params *p) {
+  const int S = (p->max_ngram - 1) * p->heads;
+  return p->offsets[S - 1] + p->primes[S - 1];
+}
+
+EngramHashArgs make_hash_args(const engram_hash_params *p) {
+  EngramHashArgs a;
+  memset(&a, 0, sizeof(a));
+  a.raw_vocab = p->raw_vocab;
+  a.compressed_vocab = p->compressed_vocab;
+  a.max_ngram = p->max_ngram;
+  a.heads = p->heads;
+  a.segments = (p->max_ngram - 1) * p->heads;
+  a.pad_id = p->pad_id;
+  for (int i = 0; i < p->max_ngram; ++i) a.mult[i] = (uint64_t)p->multipliers[i];
+  for (int j = 0; j < a.segments; ++j) {
+    a.prime[j] = (uint32_t)p->primes[j];
+    a.recip[j] = UINT64_MAX / (uint64_t)p->primes[j];
+    a.offset[j] = p->offsets[j];
+  }
+  return a;
+}
+
+int check_desc(const engram_forward_desc *d) {
+  if (d == nullptr) return ENGRAM_EINVAL;
+  if (d->batch < 0 || d->seq < 0) return ENGRAM_ESHAPE;
+  if (d->hc < 1 || d->hc > 8) return ENGRAM_ESHAPE;
+  if (d->dim < 8 || d->dim % 8 != 0 || d->dim > 8192) return ENGRAM_ESHAPE;
+  if (d->row_format != ENGRAM_ROW_E4M3_E8M0_264 && d->row_format != ENGRAM_ROW_F32)
+    return ENGRAM_EINVAL;
+  if (d->row_format == ENGRAM_ROW_E4M3_E8M0_264 && d->row_dim != ENGRAM_ROW_DIM_E4M3)
+    return ENGRAM_ESHAPE;
+  if (d->row_format == ENGRAM_ROW_F32 && (d->row_dim < 4 || d->row_dim % 4 != 0))
+    return ENGRAM_ESHAPE;
+  if (!(d->eps >= 0.f) || !(d->gate_clamp >= 0.f)) return ENGRAM_EINVAL;
+  return ENGRAM_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *engram_status_string(int status) {
+  switch (status) {
+    case ENGRAM_OK: return "ok";
+    case ENGRAM_EINVAL: return "invalid argument (null or misaligned pointer, bad value)";
+    case ENGRAM_EVOCAB: return "compressed vocabulary does not match the token map";
+    case ENGRAM_EMULT: return "multiplier even, < 1 or above (2^63-1)/compressed_vocab";
+    case ENGRAM_ESHAPE: return "inconsistent shapes";
+    case ENGRAM_EWORKSPACE: return "workspace missing or too small";
+    case ENGRAM_EHIP: return "HIP launch failed";
+    case ENGRAM_EPRIMES: return "bad primes/offsets or rows beyond the table";
+    default: return "unknown status";
+  }
+}
+
+size_t engram_sizeof_hash_params(void) { return sizeof(engram_hash_params); }
+
+size_t engram_sizeof_forward_desc(void) { return sizeof(engram_forward_desc); }
+
+int engram_make_primes(int64_t base, int32_t count, int64_t *primes_out, int64_t *offsets_out,
+                       int64_t *total_rows_out) {
+  if (count < 0 || base < 2 || (count > 0 && (primes_out == nullptr || offsets_out == nullptr)))
+    return ENGRAM_EINVAL;
+  uint64_t n = (uint64_t)base;
+  int64_t acc = 0;
+  for (int32_t j = 0; j < count; ++n) {
+    if (n > UINT32_MAX) return ENGRAM_EINVAL;
+    if (is_prime_mr(n)) {
+      primes_out[j] = (int64_t)n;
+      offsets_out[j] = acc;
+      acc += (int64_t)n;
+      ++j;
+    }
+  }
+  if (total_rows_out) *total_rows_out = acc;
+  return ENGRAM_OK;
+}
+
+int engram_check_token_map(const int32_t *token_map, int32_t raw_vocab,
+                           int32_t compressed_vocab) {
+  if (token_map == nullptr || raw_vocab < 1 || compressed_vocab < 1) return ENGRAM_EINVAL;
+  uint8_t *seen = (uint8_t *)calloc((size_t)compressed_vocab, 1);
+  if (seen == nullptr) return ENGRAM_EINVAL;
+  int32_t hit = 0;
+  int rc = ENGRAM_OK;
+  for (int32_t i = 0; i < raw_vocab; ++i) {
+    const int32_t v = token_map[i];
+    if (v < 0 || v >= compressed_vocab) {
+      rc = ENGRAM_EVOCAB;
+      break;
+    }
+    if (!seen[v]) {
+      seen[v] = 1;
+      ++hit;
+    }
+  }
+  if (rc == ENGRAM_OK && hit != compressed_vocab) rc = ENGRAM_EVOCAB;
+  free(seen);
+  return rc;
+}
+
+int engram_hash(const engram_hash_params *params, const int32_t *ids, int64_t batch,
+                int64_t seq, const int32_t *hist_in, int32_t *hist_out, int64_t *row_ids,
+                hipStream_t stream) {
+  int rc = check_hash_params(params);
+  if (rc != ENGRAM_OK) return rc;
+  if (batch < 0 || seq < 0) return ENGRAM_ESHAPE;
+  const int64_t ntok = batch * seq;
+  if (ntok > 0 && (ids == nullptr || row_ids == nullptr)) return ENGRAM_EINVAL;
+  if (!aligned(ids, 4) || !aligned(row_ids, 8) || !aligned(hist_in, 4) || !aligned(hist_out, 4))
+    return ENGRAM_EINVAL;
+  if (ntok > (int64_t)INT32_MAX * 64) return ENGRAM_ESHAPE;
+  const EngramHashArgs a = make_hash_args(params);
+  return hip_status(engram_launch_hash(a, params->token_map, ids, batch, seq, hist_in, hist_out,
+                                       row_ids, stream));
+}
+
+int engram_gather(const void *table, int64_t table_rows, int32_t row_format, int32_t row_dim,
+                  const int64_t *row_ids, int64_t n_ids, void *out, hipStream_t stream) {
+  if (n_ids < 0 || table_rows < 0) return ENGRAM_ESHAPE;
+  if (row_format == ENGRAM_ROW_E4M3_E8M0_264) {
+    if (row_dim != ENGRAM_ROW_DIM_E4M3) return ENGRAM_ESHAPE;
+  } else if (row_format == ENGRAM_ROW_F32) {
+    if (row_dim < 4 || row_dim % 4 != 0) return ENGRAM_ESHAPE;
+  } else {
+    return ENGRAM_EINVAL;
+  }
+  if (n_ids == 0) return ENGRAM_OK;
+  if (row_ids == nullptr || out == nullptr || (table == nullptr && table_rows > 0))
+    return ENGRAM_EINVAL;
+  if (!aligned(table, 16) || !aligned(row_ids, 8) || !aligned(out, 16)) return ENGRAM_EINVAL;
+  hipError_t e;
+  if (row_format == ENGRAM_ROW_E4M3_E8M0_264)
+    e = engram_launch_gather_e4m3((const uint8_t *)table, table_rows, row_ids, n_ids,
+                                  (uint16_t *)out, stream);
+  else
+    e = engram_launch_gather_f32((const float *)table, table_rows, row_dim, row_ids, n_ids,
+                                 (float *)out, stream);
+  return hip_status(e);
+}
+
+int engram_project(const void *e, const void *wkv, void *kv, int64_t tokens, int64_t in_dim,
+                   int64_t out_dim, int32_t act_f32, hipStream_t stream) {
+  if (tokens < 0 || in_dim < 1 || out_dim < 1) return ENGRAM_ESHAPE;
+  if (act_f32 != 0 && act_f32 != 1) return ENGRAM_EINVAL;
+  if (act_f32) {
+    if (in_dim % 4 || out_dim % 4) return ENGRAM_ESHAPE;
+  } else {
+    if (in_dim % 64 || out_dim % 8) return ENGRAM_ESHAPE;
+  }
+  if (tokens > INT32_MAX || out_dim > INT32_MAX || in_dim > INT32_MAX) return ENGRAM_ESHAPE;
+  if (tokens == 0) return ENGRAM_OK;
+  if (e == nullptr || wkv == nullptr || kv == nullptr) return ENGRAM_EINVAL;
+  if (!aligned(e, 16) || !aligned(wkv, 16) || !aligned(kv, 16)) return ENGRAM_EINVAL;
+  hipError_t err = act_f32 ? engram_launch_gemm_f32((const float *)e, (const float *)wkv,
+                                                    (float *)kv, tokens, out_dim, in_dim, stream)
+                           : engram_launch_gemm_bf16((const uint16_t *)e, (const uint16_t *)wkv,
+                                                     (uint16_t *)kv, tokens, out_dim, in_dim,
+                                                     stream);
+  return hip_status(err);
+}
+
+int engram_gate(const engram_forward_desc *desc, const int32_t *ids, int32_t raw_vocab,
+                const void *kv, const float *q_w, const float *k_w, void *h, float *gate_out,
+                hipStream_t stream) {
+  int rc = check_desc(desc);
+  if (rc != ENGRAM_OK) return rc;
+  if (raw_vocab < 1) return ENGRAM_EINVAL;
+  const int64_t ntok = desc->batch * desc->seq;
+  if (ntok == 0) return ENGRAM_OK;
+  if (ids == nullptr || kv == nullptr || q_w == nullptr || k_w == nullptr || h == nullptr)
+    return ENGRAM_EINVAL;
+  if (!aligned(ids, 4) || !aligned(kv, 16) || !aligned(q_w, 16) || !aligned(k_w, 16) ||
+      !aligned(h, 16) || !aligned(gate_out, 4))
+    return ENGRAM_EINVAL;
+  if (ntok > INT32_MAX) return ENGRAM_ESHAPE;
+  return hip_status(engram_launch_gate(desc->row_format == ENGRAM_ROW_F32, ids, raw_vocab, kv,
+                                       q_w, k_w, h, gate_out, ntok, desc->hc, desc->dim,
+                                       desc->eps, desc->gate_clamp, stream));
+}
+
+size_t engram_forward_workspace_size(const engram_hash_params *params,
+                                     const engram_forward_desc *desc) {
+  if (check_hash_params(params) != ENGRAM_OK || check_desc(desc) != ENGRAM_OK) return 0;
+  const int64_t ntok = desc->batch * desc->seq;
+  const int64_t S = (int64_t)(params->max_ngram - 1) * params->heads;
+  const size_t esz = desc->row_format == ENGRAM_ROW_F32 ? 4 : 2;
+  return align256((size_t)ntok * S * 8) + align256((size_t)ntok * S * desc->row_dim * esz) +
+         align256((size_t)ntok * (desc->hc + 1) * desc->dim * esz);
+}
+
+int engram_forward(const engram_hash_params *params, const engram_forward_desc *desc,
+                   const int32_t *ids, const int32_t *hist_in, int32_t *hist_out,
+                   const void *table, const void *wkv, const float *q_w, const float *k_w,
+                   void *h, float *gate_out, void *workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+  int rc = check_hash_params(params);
+  if (rc != ENGRAM_OK) return rc;
+  rc = check_desc(desc);
+  if (rc != ENGRAM_OK) return rc;
+  if (total_rows(params) > desc->table_rows) return ENGRAM_EPRIMES;
+  const int64_t ntok = desc->batch * desc->seq;
+  const int64_t S = (int64_t)(params->max_ngram - 1) * params->heads;
+  const bool f32 = desc->row_format == ENGRAM_ROW_F32;
+  const int64_t in_dim = S * desc->row_dim;
+  const int64_t out_dim = (int64_t)(desc->hc + 1) * desc->dim;
+  if (!f32 && in_dim % 64) return ENGRAM_ESHAPE;
+  if (ntok > INT32_MAX) return ENGRAM_ESHAPE;
+  if (ntok > 0) {
+    if (ids == nullptr || table == nullptr || wkv == nullptr || q_w == nullptr ||
+        k_w == nullptr || h == nullptr)
+      return ENGRAM_EINVAL;
+    if (!aligned(ids, 4) || !aligned(table, 16) || !aligned(wkv, 16) || !aligned(q_w, 16) ||
+        !aligned(k_w, 16) || !aligned(h, 16) || !aligned(gate_out, 4))
+      return ENGRAM_EINVAL;
+    const size_t need = engram_forward_workspace_size(params, desc);
+    if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
+      return ENGRAM_EWORKSPACE;
+  }
+  if (!aligned(hist_in, 4) || !aligned(hist_out, 4)) return ENGRAM_EINVAL;
+
+  char *ws = (char *)workspace;
+  const size_t esz = f32 ? 4 : 2;
+  int64_t *row_ids = (int64_t *)ws;
+  void *e = ws + align256((size_t)ntok * S * 8);
+  void *kv = (char *)e + align256((size_t)ntok * in_dim * esz);
+
+  const EngramHashArgs a = make_hash_args(params);
+  hipError_t err = engram_launch_hash(a, params->token_map, ids, desc->batch, desc->seq,
+                                      hist_in, hist_out, row_ids, stream);
+  if (err != hipSuccess || ntok == 0) return hip_status(err);
+  err = f32 ? engram_launch_gather_f32((const float *)table, desc->table_rows, desc->row_dim,
+                                       row_ids, ntok * S, (float *)e, stream)
+            : engram_launch_gather_e4m3((const uint8_t *)table, desc->table_rows, row_ids,
+                                        ntok * S, (uint16_t *)e, stream);
+  if (err != hipSuccess) return ENGRAM_EHIP;
+  err = f32 ? engram_launch_gemm_f32((const float *)e, (const float *)wkv, (float *)kv, ntok,
+                                     out_dim, in_dim, stream)
+            : engram_launch_gemm_bf16((const uint16_t *)e, (const uint16_t *)wkv,
+                                      (uint16_t *)kv, ntok, out_dim, in_dim, stream);
+  if (err != hipSuccess) return ENGRAM_EHIP;
+  err = engram_launch_gate(f32, ids, params->raw_vocab, kv, q_w, k_w, h, gate_out, ntok,
+                           desc->hc, desc->dim, desc->eps, desc->gate_clamp, stream);
+  return hip_status(err);
+}
+
+}  // extern "C"

@@ -1,0 +1,209 @@
+// Step 5 of the Engram layer: context gate per hyper-connection stream and the
+// residual update.
+//
+// Pages: "DeepSeek-V4.1 模型结构（5）：记忆，Engram", "门控：用当前的上下文决定查到的向量用多少"
+// (s^(m) = RMSNorm(h^(m)) . RMSNorm(k^(m)) / sqrt(d), h^(m) += alpha^(m) v, one
+// shared v for all streams), "sigmoid 之前多一步带符号的平方根" (the signed
+// square root before the sigmoid, with a clamp on |s|) and the image-token
+// paragraph (gate 0 at DEAD positions); "ds4.c 学习笔记 · Engram", "消费：学习投影 +
+// 余弦门控" (the learned scales q_w * k_w inside the dot, eps inside the
+// reciprocal roots of the mean squares, the update rounded to bf16 once) and
+// "布局与哈希探测" item 4 (masked rows are left untouched).
+//
+// One block of 256 threads per token. Each thread owns CPT chunks of 4
+// elements per stream; it keeps its h chunks in registers between the three
+// reductions (sum h^2, sum k^2, sum h q_w k_w k per stream) and the update, so
+// h is read once and written once. All arithmetic is fp32.
+#include "common.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxHc = 8;
+
+template <bool F32>
+struct Chunk;
+template <>
+struct Chunk<false> {   // 4 bf16
+  uint2 v;
+  __device__ __forceinline__ void load(const void *p, int64_t i) {
+    v = reinterpret_cast<const uint2 *>(p)[i];
+  }
+  __device__ __forceinline__ float operator[](int e) const {
+    const uint32_t w = e < 2 ? v.x : v.y;
+    return engram::bf16_to_f32((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+  }
+  __device__ __forceinline__ static void store(void *p, int64_t i, const float f[4]) {
+    uint2 o;
+    o.x = engram::pack_bf16x2(f[0], f[1]);
+    o.y = engram::pack_bf16x2(f[2], f[3]);
+    reinterpret_cast<uint2 *>(p)[i] = o;
+  }
+};
+template <>
+struct Chunk<true> {    // 4 fp32
+  float4 v;
+  __device__ __forceinline__ void load(const void *p, int64_t i) {
+    v = reinterpret_cast<const float4 *>(p)[i];
+  }
+  __device__ __forceinline__ float operator[](int e) const {
+    return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+  }
+  __device__ __forceinline__ static void store(void *p, int64_t i, const float f[4]) {
+    reinterpret_cast<float4 *>(p)[i] = make_float4(f[0], f[1], f[2], f[3]);
+  }
+};
+
+template <bool F32, int CPT>
+__global__ __launch_bounds__(kThreads) void gate_kernel(
+    const int32_t *__restrict__ ids, int32_t raw_vocab, const void *__restrict__ kv,
+    const float *__restrict__ q_w, const float *__restrict__ k_w, void *__restrict__ h,
+    float *__restrict__ gate_out, int hc, int dim, float eps, float clamp) {
+  __shared__ float red[kThreads / engram::kWave][3 * kMaxHc];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int32_t x = ids[t];
+  if (x < 0 || x >= raw_vocab) {          // DEAD: gate 0, streams untouched
+    if (gate_out != nullptr && tid < hc) gate_out[t * hc + tid] = 0.f;
+    return;
+  }
+  const int cps = dim >> 2;                       // chunks per stream
+  const int64_t kv_row = t * (int64_t)(hc + 1) * cps;
+  const int64_t h_row = t * (int64_t)hc * cps;
+
+  Chunk<F32> hv[kMaxHc][CPT];
+  Chunk<F32> vv[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int ci = tid + c * kThreads;
+    if (ci < cps) vv[c].load(kv, kv_row + (int64_t)hc * cps + ci);
+  }
+  float shh[kMaxHc], skk[kMaxHc], shk[kMaxHc];
+#pragma unroll
+  for (int m = 0; m < kMaxHc; ++m) {
+    shh[m] = 0.f;
+    skk[m] = 0.f;
+    shk[m] = 0.f;
+    if (m < hc) {
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int ci = tid + c * kThreads;
+        if (ci < cps) {
+          Chunk<F32> kc;
+          hv[m][c].load(h, h_row + (int64_t)m * cps + ci);
+          kc.load(kv, kv_row + (int64_t)m * cps + ci);
+          const float4 qw = reinterpret_cast<const float4 *>(q_w + (int64_t)m * dim)[ci];
+          const float4 kw = reinterpret_cast<const float4 *>(k_w + (int64_t)m * dim)[ci];
+          const float w[4] = {qw.x * kw.x, qw.y * kw.y, qw.z * kw.z, qw.w * kw.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float he = hv[m][c][e];
+            const float ke = kc[e];
+            shh[m] = fmaf(he, he, shh[m]);
+            skk[m] = fmaf(ke, ke, skk[m]);
+            shk[m] = fmaf(he * w[e], ke, shk[m]);
+          }
+        }
+      }
+    }
+  }
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+#pragma unroll
+  for (int m = 0; m < kMaxHc; ++m) {
+    if (m < hc) {
+      const float a = engram::warp_sum(shh[m]);
+      const float b = engram::warp_sum(skk[m]);
+      const float c = engram::warp_sum(shk[m]);
+      if (lane == 0) {
+        red[wave][3 * m + 0] = a;
+        red[wave][3 * m + 1] = b;
+        red[wave][3 * m + 2] = c;
+      }
+    }
+  }
+  __syncthreads();
+  const float inv_d = 1.0f / (float)dim;
+  const float inv_sqrt_d = 1.0f / sqrtf((float)dim);
+  float alpha[kMaxHc];
+#pragma unroll
+  for (int m = 0; m < kMaxHc; ++m) {
+    alpha[m] = 0.f;
+    if (m < hc) {
+      float a = 0.f, b = 0.f, c = 0.f;
+#pragma unroll
+      for (int w = 0; w < kThreads / engram::kWave; ++w) {
+        a += red[w][3 * m + 0];
+        b += red[w][3 * m + 1];
+        c += red[w][3 * m + 2];
+      }
+      const float rh = 1.0f / sqrtf(a * inv_d + eps);
+      const float rk = 1.0f / sqrtf(b * inv_d + eps);
+      const float s = c * rh * rk * inv_sqrt_d;
+      const float z = copysignf(sqrtf(fmaxf(fabsf(s), clamp)), s);
+      alpha[m] = 1.0f / (1.0f + expf(-z));
+    }
+  }
+  if (gate_out != nullptr && tid < hc) {
+#pragma unroll
+    for (int m = 0; m < kMaxHc; ++m)
+      if (m == tid) gate_out[t * hc + m] = alpha[m];
+  }
+#pragma unroll
+  for (int m = 0; m < kMaxHc; ++m) {
+    if (m < hc) {
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int ci = tid + c * kThreads;
+        if (ci < cps) {
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = fmaf(alpha[m], vv[c][e], hv[m][c][e]);
+          Chunk<F32>::store(h, h_row + (int64_t)m * cps + ci, o);
+        }
+      }
+    }
+  }
+}
+
+template <bool F32>
+hipError_t launch(int cpt, const int32_t *ids, int32_t raw_vocab, const void *kv,
+                  const float *q_w, const float *k_w, void *h, float *gate_out,
+                  int64_t tokens, int hc, int dim, float eps, float clamp,
+                  hipStream_t stream) {
+#define ENGRAM_GATE_CASE(N)                                                                 \
+  case N:                                                                                   \
+    hipLaunchKernelGGL((gate_kernel<F32, N>), dim3((unsigned)tokens), dim3(kThreads), 0,    \
+                       stream, ids, raw_vocab, kv, q_w, k_w, h, gate_out, hc, dim, eps,     \
+                       clamp);                                                              \
+    break;
+  switch (cpt) {
+    ENGRAM_GATE_CASE(1)
+    ENGRAM_GATE_CASE(2)
+    ENGRAM_GATE_CASE(3)
+    ENGRAM_GATE_CASE(4)
+    ENGRAM_GATE_CASE(5)
+    ENGRAM_GATE_CASE(6)
+    ENGRAM_GATE_CASE(7)
+    ENGRAM_GATE_CASE(8)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef ENGRAM_GATE_CASE
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t engram_launch_gate(bool f32, const int32_t *ids, int32_t raw_vocab, const void *kv,
+                              const float *q_w, const float *k_w, void *h, float *gate_out,
+                              int64_t tokens, int32_t hc, int32_t dim, float eps, float clamp,
+                              hipStream_t stream) {
+  if (tokens <= 0) return hipSuccess;
+  const int cps = dim / 4;
+  const int cpt = (cps + kThreads - 1) / kThreads;
+  return f32 ? launch<true>(cpt, ids, raw_vocab, kv, q_w, k_w, h, gate_out, tokens, hc, dim,
+                            eps, clamp, stream)
+             : launch<false>(cpt, ids, raw_vocab, kv, q_w, k_w, h, gate_out, tokens, hc, dim,
+                             eps, clamp, stream);
+}

@@ -1,0 +1,145 @@
+// Step 3 of the Engram layer: gather table rows and dequantise them to bf16.
+//
+// Pages: "ds4.c 学习笔记 · Engram", "布局与哈希探测" (264-byte rows) and
+// "永不常驻的 I/O 设计" (256 E4M3 bytes + 8 E8M0 scales, 32 values per scale);
+// "DeepSeek-V4.1 模型结构（5）：记忆，Engram", "196B 参数怎么存、怎么取" (rows
+// dequantise independently); "条件记忆：DeepSeek V4.1 Engram 如何用 O(1) 查表换掉一层计算",
+// §2.3 (bf16 output) and §五 (out-of-range rows read as zeros).
+//
+// E4M3 rows: a half-wave (32 lanes) owns one row; lane l reads payload bytes
+// 8l..8l+7 (one dwordx2; rows start 8-byte aligned because 264 = 8 * 33) and
+// the scale byte l/4, and writes 8 bf16 (one dwordx4), so each half-wave reads
+// 256 contiguous bytes and writes 512 contiguous bytes. A wave keeps 16 rows in
+// flight (8 row pairs) before converting any of them, to cover HBM latency on
+// random rows.
+//
+// Dequantisation is exact. For scales 10..246 no value can leave the bf16
+// normal range, so the hardware OCP-E4M3 -> f32 conversion, one multiply by the
+// power of two 2^(s-127) and truncation to the upper 16 bits are exact. Other
+// scales take an integer path: the E4M3 magnitude bits placed at the f32
+// exponent/mantissa position give value * 2^-120 (subnormal codes become f32
+// denormals, kept by the denormal mode), ldexp by s - 7 is exact or overflows,
+// and one nearest-even rounding to bf16 handles bf16 subnormals.
+#include "common.h"
+
+namespace {
+
+constexpr int kSlots = 8;                 // row pairs per wave
+constexpr int kRowsPerWave = 2 * kSlots;
+constexpr int kThreads = 256;
+constexpr int kRowsPerBlock = kRowsPerWave * (kThreads / engram::kWave);
+
+__device__ __forceinline__ uint32_t dequant_byte_exact(uint32_t byte, uint32_t s) {
+  const uint32_t sign = (byte & 0x80u) << 8;
+  const uint32_t mag = byte & 0x7Fu;
+  if (mag == 0x7Fu || s == 0xFFu) return 0x7FC0u | sign;     // E4M3 NaN, E8M0 NaN
+  const float f = ldexpf(__uint_as_float(mag << 20), (int)s - 7);
+  return engram::f32_to_bf16_rne(f) | sign;
+}
+
+__device__ __forceinline__ uint32_t dequant_pair_fast(uint32_t word, float scale, bool hi) {
+  const auto f = hi ? __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true)
+                    : __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
+  const uint32_t lo32 = __float_as_uint(f[0] * scale);
+  const uint32_t hi32 = __float_as_uint(f[1] * scale);
+  return (lo32 >> 16) | (hi32 & 0xFFFF0000u);
+}
+
+__device__ __forceinline__ uint4 dequant8(uint2 q, uint32_t s) {
+  uint4 o;
+  if (s - 10u <= 236u) {
+    const float scale = __uint_as_float(s << 23);
+    o.x = dequant_pair_fast(q.x, scale, false);
+    o.y = dequant_pair_fast(q.x, scale, true);
+    o.z = dequant_pair_fast(q.y, scale, false);
+    o.w = dequant_pair_fast(q.y, scale, true);
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t word = i < 2 ? q.x : q.y;
+      const int sh = (i & 1) * 16;
+      w[i] = dequant_byte_exact((word >> sh) & 0xFFu, s) |
+             (dequant_byte_exact((word >> (sh + 8)) & 0xFFu, s) << 16);
+    }
+    o = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  return o;
+}
+
+__global__ __launch_bounds__(kThreads) void gather_e4m3_kernel(
+    const uint8_t *__restrict__ table, int64_t table_rows, const int64_t *__restrict__ row_ids,
+    int64_t n, uint16_t *__restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5;
+  const int l = lane & 31;
+  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const int64_t base = wave * kRowsPerWave;
+
+  int64_t r[kSlots];
+#pragma unroll
+  for (int s = 0; s < kSlots; ++s) {
+    const int64_t idx = base + 2 * s + half;
+    r[s] = idx < n ? row_ids[idx] : -1;
+  }
+  uint2 q[kSlots];
+  uint32_t sc[kSlots];
+#pragma unroll
+  for (int s = 0; s < kSlots; ++s) {
+    if ((uint64_t)r[s] < (uint64_t)table_rows) {
+      const uint8_t *row = table + r[s] * ENGRAM_ROW_BYTES;
+      q[s] = *reinterpret_cast<const uint2 *>(row + 8 * l);
+      sc[s] = row[ENGRAM_ROW_DIM_E4M3 + (l >> 2)];
+    } else {
+      q[s] = make_uint2(0u, 0u);
+      sc[s] = 0u;
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < kSlots; ++s) {
+    const int64_t idx = base + 2 * s + half;
+    if (idx < n) {
+      const uint4 o = ((uint64_t)r[s] < (uint64_t)table_rows) ? dequant8(q[s], sc[s])
+                                                               : make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4 *>(out + idx * ENGRAM_ROW_DIM_E4M3 + 8 * l) = o;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void gather_f32_kernel(
+    const float *__restrict__ table, int64_t table_rows, int32_t row_dim,
+    const int64_t *__restrict__ row_ids, int64_t n, float *__restrict__ out) {
+  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int cpr = row_dim >> 2;
+  const int64_t i = g / cpr;
+  const int c = (int)(g - i * cpr);
+  if (i >= n) return;
+  const int64_t r = row_ids[i];
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if ((uint64_t)r < (uint64_t)table_rows)
+    v = reinterpret_cast<const float4 *>(table + r * row_dim)[c];
+  reinterpret_cast<float4 *>(out + i * row_dim)[c] = v;
+}
+
+}  // namespace
+
+hipError_t engram_launch_gather_e4m3(const uint8_t *table, int64_t table_rows,
+                                     const int64_t *row_ids, int64_t n_ids, uint16_t *out,
+                                     hipStream_t stream) {
+  if (n_ids <= 0) return hipSuccess;
+  const int64_t blocks = (n_ids + kRowsPerBlock - 1) / kRowsPerBlock;
+  hipLaunchKernelGGL(gather_e4m3_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                     table, table_rows, row_ids, n_ids, out);
+  return hipGetLastError();
+}
+
+hipError_t engram_launch_gather_f32(const float *table, int64_t table_rows, int32_t row_dim,
+                                    const int64_t *row_ids, int64_t n_ids, float *out,
+                                    hipStream_t stream) {
+  if (n_ids <= 0) return hipSuccess;
+  const int64_t work = n_ids * (row_dim / 4);
+  const int64_t blocks = (work + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(gather_f32_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                     table, table_rows, row_dim, row_ids, n_ids, out);
+  return hipGetLastError();
+}

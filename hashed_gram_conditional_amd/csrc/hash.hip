@@ -1,0 +1,158 @@
+// Steps 1-2 of the Engram layer: compressed ids, multiply-XOR n-gram mixes and
+// per-head prime moduli into one offset table.
+//
+// Pages: "DeepSeek-V4.1 模型结构（5）：记忆，Engram", eq. (H), the items under it
+// (orders are computed incrementally; the heads of an order share one mix;
+// sequence starts pad), the image-token paragraph (DEAD cascade) and
+// "一层只有一张表" (segment offsets); "ds4.c 学习笔记 · Engram", "布局与哈希探测"
+// (3-token hash state); "条件记忆：DeepSeek V4.1 Engram 如何用 O(1) 查表换掉一层计算",
+// §4.4 (decode fuses the hash with the history commit).
+//
+// Layout: one block of 256 threads owns 256 consecutive flat tokens. Phase 1:
+// one thread per token builds the look-back cells and the N-1 mixes into LDS.
+// Phase 2: the block writes its 256 x S int64 row ids as one contiguous,
+// fully coalesced span, each thread reducing mixes modulo the primes.
+//
+// mix < 2^63 and p < 2^32, and gfx950 has no 64-bit integer divide, so
+// x mod p uses the precomputed reciprocal r = floor((2^64-1)/p): q = hi64(x r)
+// is floor(x/p) or one less (the error term x(1 + (2^64-1) mod p) / (p 2^64)
+// is below 1), so one conditional subtraction gives the exact remainder
+// (Barrett, "Implementing the RSA public key encryption algorithm on a standard
+// digital signal processor", CRYPTO 1986).
+#include "common.h"
+
+namespace {
+
+constexpr int kTok = 256;
+
+__device__ __forceinline__ int32_t cell_value(const EngramHashArgs &a,
+                                              const int32_t *__restrict__ token_map,
+                                              const int32_t *__restrict__ row,
+                                              const int32_t *__restrict__ hist, int64_t u) {
+  // Value of the cell at chunk position u (u < 0: the history before the chunk):
+  // a compressed id, or -1 for DEAD.
+  const int H = a.max_ngram - 1;
+  if (u >= 0) {
+    const int32_t x = row[u];
+    if (x < 0 || x >= a.raw_vocab) return -1;
+    const int32_t v = token_map[x];
+    return (v >= 0 && v < a.compressed_vocab) ? v : -1;
+  }
+  if (hist != nullptr) {
+    const int32_t v = hist[H + u];
+    return (v >= 0 && v < a.compressed_vocab) ? v : -1;
+  }
+  return a.pad_id;
+}
+
+__global__ __launch_bounds__(kTok) void hash_kernel(
+    EngramHashArgs a, const int32_t *__restrict__ token_map, const int32_t *__restrict__ ids,
+    int64_t batch, int64_t seq, const int32_t *hist_in, int32_t *hist_out,
+    int64_t *__restrict__ row_ids, int commit_history) {
+  __shared__ uint64_t s_mix[ENGRAM_MAX_NGRAM - 1][kTok];
+  __shared__ uint64_t s_recip[ENGRAM_MAX_SEGMENTS];
+  __shared__ int64_t s_off[ENGRAM_MAX_SEGMENTS];
+  __shared__ uint32_t s_prime[ENGRAM_MAX_SEGMENTS];
+
+  const int tid = threadIdx.x;
+  const int S = a.segments;
+  const int N = a.max_ngram;
+  const int H = N - 1;
+  if (tid < S) {
+    s_prime[tid] = a.prime[tid];
+    s_recip[tid] = a.recip[tid];
+    s_off[tid] = a.offset[tid];
+  }
+
+  const int64_t ntok = batch * seq;
+  const int64_t tok0 = (int64_t)blockIdx.x * kTok;
+  const int64_t g = tok0 + tid;
+  if (g < ntok) {
+    const int64_t b = g / seq;
+    const int64_t t = g - b * seq;
+    const int32_t *row = ids + b * seq;
+    const int32_t *hist = hist_in ? hist_in + b * H : nullptr;
+    int32_t vals[ENGRAM_MAX_NGRAM];
+    bool blocked = false;
+    uint64_t mix = 0;
+#pragma unroll
+    for (int i = 0; i < ENGRAM_MAX_NGRAM; ++i) {
+      if (i < N) {
+        const int32_t v = cell_value(a, token_map, row, hist, t - i);
+        vals[i] = v;
+        // A DEAD cell blocks itself and every older cell: they hash as the pad id.
+        blocked = blocked || (v < 0);
+        const uint64_t c = blocked ? (uint64_t)a.pad_id : (uint64_t)v;
+        // Orders build on each other: mix_{n+1} = mix_n ^ x'_{t-n} m_n.
+        mix ^= c * a.mult[i];
+        if (i >= 1) s_mix[i - 1][tid] = mix;
+      }
+    }
+    if (commit_history) {
+      // T == 1: this thread is its sequence's only token. Every history read
+      // above precedes these writes, so hist_out may alias hist_in.
+#pragma unroll
+      for (int s = 0; s < ENGRAM_MAX_NGRAM - 1; ++s)
+        if (s < H) hist_out[b * H + s] = vals[H - 1 - s];
+    }
+  }
+  __syncthreads();
+
+  const int64_t left = ntok - tok0;
+  const int ntb = left < kTok ? (int)left : kTok;
+  const int total = ntb * S;
+  int64_t *out = row_ids + tok0 * S;
+  for (int o = tid; o < total; o += kTok) {
+    const int lt = o / S;
+    const int j = o - lt * S;
+    const uint64_t x = s_mix[j / a.heads][lt];
+    const uint64_t p = s_prime[j];
+    uint64_t r = x - __umul64hi(x, s_recip[j]) * p;
+    if (r >= p) r -= p;
+    out[o] = (int64_t)r + s_off[j];
+  }
+}
+
+// History after a chunk of T != 1 tokens, one thread per sequence. Runs after
+// hash_kernel on the same stream, so hist_out may alias hist_in.
+__global__ void history_kernel(EngramHashArgs a, const int32_t *__restrict__ token_map,
+                               const int32_t *__restrict__ ids, int64_t batch, int64_t seq,
+                               const int32_t *hist_in, int32_t *hist_out) {
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= batch) return;
+  const int H = a.max_ngram - 1;
+  const int32_t *row = ids + b * seq;
+  const int32_t *hist = hist_in ? hist_in + b * H : nullptr;
+  int32_t vals[ENGRAM_MAX_NGRAM - 1];
+#pragma unroll
+  for (int s = 0; s < ENGRAM_MAX_NGRAM - 1; ++s)
+    if (s < H) vals[s] = cell_value(a, token_map, row, hist, seq - H + s);
+#pragma unroll
+  for (int s = 0; s < ENGRAM_MAX_NGRAM - 1; ++s)
+    if (s < H) hist_out[b * H + s] = vals[s];
+}
+
+}  // namespace
+
+hipError_t engram_launch_hash(const EngramHashArgs &a, const int32_t *token_map,
+                              const int32_t *ids, int64_t batch, int64_t seq,
+                              const int32_t *hist_in, int32_t *hist_out, int64_t *row_ids,
+                              hipStream_t stream) {
+  const int64_t ntok = batch * seq;
+  const bool fused = hist_out != nullptr && seq == 1;
+  if (ntok > 0) {
+    const int64_t blocks = (ntok + kTok - 1) / kTok;
+    hipLaunchKernelGGL(hash_kernel, dim3((unsigned)blocks), dim3(kTok), 0, stream, a,
+                       token_map, ids, batch, seq, hist_in, hist_out, row_ids, fused ? 1 : 0);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (hist_out != nullptr && !fused && batch > 0) {
+    const int threads = 128;
+    const int64_t blocks = (batch + threads - 1) / threads;
+    hipLaunchKernelGGL(history_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, a,
+                       token_map, ids, batch, seq, hist_in, hist_out);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}

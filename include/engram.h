@@ -1,0 +1,230 @@
+/*
+ * engram.h -- C ABI of the Engram conditional-memory layer forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (pages cited by title, then section / equation / table):
+ *   [P1] "DeepSeek-V4.1 模型结构（5）：记忆，Engram"
+ *   [P2] "Engram条件记忆：DeepSeek-V4.1-Flash中196B稀疏参数N-gram哈希查表的实现原理"
+ *   [P3] "条件记忆：DeepSeek V4.1 Engram 如何用 O(1) 查表换掉一层计算"
+ *   [P4] "ds4.c 学习笔记 · Engram"
+ *   [P5] "DeepSeek Engram 详解：把静态知识从计算里拆出来"
+ *
+ *   1. x' = P(x): raw token id -> compressed id ([P1] "tokenizer 压缩").
+ *   2. mix_{t,n} = XOR_{i<n} x'_{t-i} m_i; row_{t,n,k} = (mix mod p_{n,k}) + off_{n,k}
+ *      ([P1] eq. (H) and "一层只有一张表").
+ *   3. Gather the S = (N-1) K rows of 264 bytes (256 E4M3 + 8 E8M0 scales, one
+ *      scale per 32 values) and dequantise them to bf16 ([P4] "布局与哈希探测";
+ *      [P1] "196B 参数怎么存、怎么取").
+ *   4. kv = e W: hc keys and one value in one projection ([P1] "每条流一个 key
+ *      的设计沿用自原版"; [P5] §4.3).
+ *   5. Per stream m: s = RMSNorm(h_m) . RMSNorm(k_m) / sqrt(d) with the learned
+ *      scales q_w * k_w, alpha = sigmoid(sign(s) sqrt(max(|s|, clamp))),
+ *      h_m <- bf16(h_m + alpha v); alpha = 0 and h untouched at DEAD positions
+ *      ([P1] "门控", "sigmoid 之前多一步带符号的平方根"; [P4] "消费：学习投影 +
+ *      余弦门控").
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device memory unless marked [host]. The caller owns every
+ *     buffer; the library allocates nothing, keeps no state between calls and
+ *     never synchronises: work is enqueued on `stream` (0 = null stream) and
+ *     completes asynchronously.
+ *   - All arrays are dense row-major. Device pointers must be 16-byte aligned.
+ *   - Arguments are validated on the host before any launch; a failed check
+ *     returns a negative engram_status and enqueues nothing. A failed launch
+ *     returns ENGRAM_EHIP.
+ *   - Device data cannot be validated synchronously, so it follows conventions:
+ *     a raw id outside [0, V) (the DEAD marker -1 included), or one the token
+ *     map sends outside [0, V'), is a DEAD cell; a history entry outside
+ *     [0, V') is DEAD; a row id outside [0, rows) gathers a zero row ([P3] §五:
+ *     out-of-range rows output zero rows). The gate decides DEAD positions from
+ *     the raw id alone, so a map must pass engram_check_token_map first.
+ *   - Calls that write overlapping buffers on different streams race.
+ */
+#ifndef ENGRAM_H
+#define ENGRAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ENGRAM_DEAD (-1)
+#define ENGRAM_MAX_NGRAM 8        /* N, largest n-gram order (orders 2..N) */
+#define ENGRAM_MAX_SEGMENTS 64    /* S = (N - 1) * K */
+#define ENGRAM_ROW_BYTES 264      /* E4M3 row: 256 payload bytes + 8 scale bytes */
+#define ENGRAM_ROW_DIM_E4M3 256
+
+typedef enum engram_status {
+  ENGRAM_OK = 0,
+  ENGRAM_EINVAL = -1,     /* null / misaligned pointer, negative size, bad enum  */
+  ENGRAM_EVOCAB = -2,     /* compressed vocabulary does not match the token map  */
+  ENGRAM_EMULT = -3,      /* multiplier even, < 1 or > floor((2^63-1)/V')         */
+  ENGRAM_ESHAPE = -4,     /* inconsistent shapes                                  */
+  ENGRAM_EWORKSPACE = -5, /* workspace missing or too small                       */
+  ENGRAM_EHIP = -6,       /* a HIP launch failed                                  */
+  ENGRAM_EPRIMES = -7     /* prime < 2 or >= 2^32, offsets not the prefix sums,
+                             or rows beyond the table                             */
+} engram_status;
+
+typedef enum engram_row_format {
+  ENGRAM_ROW_E4M3_E8M0_264 = 0, /* uint8 [rows, 264]: 256 E4M3FN bytes in element
+                                   order, then 8 E8M0 scales; value =
+                                   E4M3(q_c) * 2^(s_{c/32} - 127), emitted as bf16 */
+  ENGRAM_ROW_F32 = 1            /* float [rows, row_dim], copied verbatim          */
+} engram_row_format;
+
+/*
+ * Hash setup of one Engram layer ([P1] eq. (H); [P2] config.json table;
+ * [P3] §2.2, §4.3). Passed by pointer, read on the host at call time; the
+ * numeric fields travel to the kernels by value.
+ */
+typedef struct engram_hash_params {
+  int32_t raw_vocab;          /* V (129280)                                        */
+  int32_t compressed_vocab;   /* V' (99092): the vocabulary the multipliers are
+                                 bounded for ([P1] §"哈希函数", item on overflow)   */
+  int32_t max_ngram;          /* N, orders 2..N; 2 <= N <= ENGRAM_MAX_NGRAM (4)    */
+  int32_t heads;              /* K heads per order (8); S = (N-1) K segments       */
+  int32_t pad_id;             /* compressed pad id, in [0, V')                     */
+  int32_t reserved;           /* must be 0                                         */
+  const int32_t *token_map;   /* device [V], values in [0, V'); validate once with
+                                 engram_check_token_map                            */
+  int64_t multipliers[ENGRAM_MAX_NGRAM]; /* m_0..m_{N-1}; m_i multiplies the token
+                                 i positions back; odd, 1 <= m <= (2^63-1)/V'      */
+  int64_t primes[ENGRAM_MAX_SEGMENTS];   /* p_j of segment j = (n-2) K + k,
+                                 2 <= p_j < 2^32                                   */
+  int64_t offsets[ENGRAM_MAX_SEGMENTS];  /* off_j = p_0 + ... + p_{j-1}            */
+} engram_hash_params;
+
+/* Shapes and constants of one forward call. */
+typedef struct engram_forward_desc {
+  int64_t batch;              /* B sequences                                       */
+  int64_t seq;                /* T tokens per sequence in this chunk (decode: 1)   */
+  int32_t hc;                 /* hyper-connection streams (4); 1 <= hc <= 8        */
+  int32_t dim;                /* d, stream width (5120); multiple of 8             */
+  int64_t table_rows;         /* R, rows of the table; >= sum of the primes        */
+  int32_t row_format;         /* engram_row_format                                 */
+  int32_t row_dim;            /* 256 for E4M3 rows; multiple of 4 for fp32 rows    */
+  float eps;                  /* RMS epsilon (1e-6)                                */
+  float gate_clamp;           /* c in sqrt(max(|s|, c)) (0)                        */
+} engram_forward_desc;
+
+/* Message for a status code (static storage). */
+const char *engram_status_string(int status);
+
+/* sizeof the two structs as this library was built, for bindings to check. */
+size_t engram_sizeof_hash_params(void);
+size_t engram_sizeof_forward_desc(void);
+
+/*
+ * [host] Segment sizes and offsets: the first `count` primes >= base, in
+ * ascending order, one per segment and never reused, and their exclusive
+ * prefix sums ([P1] "一层只有一张表": the row count is the sum of the 24
+ * primes found upward from 16,000,000). Deterministic Miller-Rabin.
+ * primes_out, offsets_out: [host] int64 [count]; total_rows_out: [host] or NULL.
+ * Errors: ENGRAM_EINVAL (count < 0, null, base < 2 or a prime >= 2^32).
+ */
+int engram_make_primes(int64_t base, int32_t count, int64_t *primes_out,
+                       int64_t *offsets_out, int64_t *total_rows_out);
+
+/*
+ * [host] Start-up check that the compression map matches the configured
+ * compressed vocabulary: every value in [0, V'), every compressed id used, and
+ * so max + 1 == V' ([P1] §"哈希函数": a mismatch means every row id is wrong;
+ * [P3] §2.1). token_map: [host] int32 [raw_vocab].
+ * Errors: ENGRAM_EINVAL, ENGRAM_EVOCAB.
+ */
+int engram_check_token_map(const int32_t *token_map, int32_t raw_vocab,
+                           int32_t compressed_vocab);
+
+/*
+ * Steps 1-2: row ids of every (position, segment).
+ *   ids      int32 [B, T] raw ids, -1 = DEAD (image or padding position)
+ *   hist_in  int32 [B, N-1] or NULL. The N-1 cells before this chunk, oldest
+ *            first: compressed ids or -1 (DEAD). NULL = sequence start: those
+ *            cells are the pad id, looked up like any id ([P1] §"哈希函数";
+ *            [P4] "布局与哈希探测": the hash state is the tail of 3 tokens).
+ *   hist_out int32 [B, N-1] or NULL. State after the chunk: the last N-1
+ *            positions' compressed ids (-1 at DEAD), older slots shifted in from
+ *            hist_in (or the pad id). May alias hist_in.
+ *   row_ids  int64 [B*T, S], row_ids[t, (n-2) K + k] = (mix_{t,n} mod p) + off.
+ * A DEAD cell blocks itself and every older cell, which then hash as the pad id;
+ * at a DEAD position every cell is blocked ([P1] image-token paragraph; [P2]
+ * "多模态细节"; [P4] item 4). B or T may be 0.
+ * Errors: ENGRAM_EINVAL, ENGRAM_EMULT, ENGRAM_EPRIMES, ENGRAM_ESHAPE, ENGRAM_EHIP.
+ */
+int engram_hash(const engram_hash_params *params, const int32_t *ids, int64_t batch,
+                int64_t seq, const int32_t *hist_in, int32_t *hist_out,
+                int64_t *row_ids, hipStream_t stream);
+
+/*
+ * Step 3: gather and dequantise rows ([P3] §2.3: fp8 E4M3 payload and E8M0
+ * block scales, bf16 output; [P4] "永不常驻的 I/O 设计": 32 values share a scale).
+ *   table    row_format rows: uint8 [table_rows, 264] or float [table_rows, row_dim]
+ *   row_ids  int64 [n_ids]; ids outside [0, table_rows) give zero rows
+ *   out      [n_ids, row_dim] bf16 (E4M3 rows, row_dim = 256) or float (fp32 rows)
+ * Dequantisation is exact: E4M3(q) * 2^(s - 127) rounded once to bf16 (nearest,
+ * ties to even; NaN codes and scale 0xFF give NaN).
+ * Errors: ENGRAM_EINVAL, ENGRAM_ESHAPE, ENGRAM_EHIP.
+ */
+int engram_gather(const void *table, int64_t table_rows, int32_t row_format,
+                  int32_t row_dim, const int64_t *row_ids, int64_t n_ids, void *out,
+                  hipStream_t stream);
+
+/*
+ * Step 4: kv = e W ([P1] "每条流一个 key 的设计沿用自原版": one 6144 x 25600
+ * matrix; [P4] "消费": the weight is stored with the 6144 inputs innermost).
+ *   e    [tokens, in_dim]       bf16 (act_f32 = 0) or float (act_f32 = 1)
+ *   wkv  [out_dim, in_dim]      same type; row c holds the weights of output c
+ *   kv   [tokens, out_dim]      same type; fp32 accumulation, bf16 rounded to
+ *                               nearest-even
+ * bf16 requires in_dim % 64 == 0 and out_dim % 8 == 0; fp32 requires in_dim % 4
+ * == 0 and out_dim % 4 == 0.
+ * Errors: ENGRAM_EINVAL, ENGRAM_ESHAPE, ENGRAM_EHIP.
+ */
+int engram_project(const void *e, const void *wkv, void *kv, int64_t tokens,
+                   int64_t in_dim, int64_t out_dim, int32_t act_f32, hipStream_t stream);
+
+/*
+ * Step 5: gate and residual update, given kv.
+ *   desc     shapes (batch, seq, hc, dim, row_format selects bf16 or fp32 I/O,
+ *            eps, gate_clamp); table fields are ignored
+ *   ids      int32 [B, T] raw ids; a position with an id outside [0, raw_vocab)
+ *            is DEAD: alpha = 0 and its h is left untouched
+ *   kv       [B*T, (hc+1) dim]: keys k^(0..hc-1) then the value v
+ *   q_w, k_w float [hc, dim]: learned scales of stream m in row m
+ *   h        [B, T, hc, dim] in/out, bf16 (E4M3 format) or float (fp32 format)
+ *   gate_out float [B*T, hc] or NULL
+ * Errors: ENGRAM_EINVAL, ENGRAM_ESHAPE, ENGRAM_EHIP.
+ */
+int engram_gate(const engram_forward_desc *desc, const int32_t *ids, int32_t raw_vocab,
+                const void *kv, const float *q_w, const float *k_w, void *h,
+                float *gate_out, hipStream_t stream);
+
+/* Bytes of workspace engram_forward needs (row ids, e and kv), or 0 on bad args. */
+size_t engram_forward_workspace_size(const engram_hash_params *params,
+                                     const engram_forward_desc *desc);
+
+/*
+ * Steps 1-5 for one chunk of B sequences x T tokens, on one stream.
+ *   ids, hist_in, hist_out   as engram_hash
+ *   table                    as engram_gather, desc->row_format / row_dim
+ *   wkv                      [(hc+1) dim, S row_dim], bf16 (E4M3) or float (fp32)
+ *   q_w, k_w, h, gate_out    as engram_gate
+ *   workspace                device, >= engram_forward_workspace_size bytes,
+ *                            256-byte aligned; contents are scratch
+ * Errors: any of the stage errors, ENGRAM_EWORKSPACE.
+ */
+int engram_forward(const engram_hash_params *params, const engram_forward_desc *desc,
+                   const int32_t *ids, const int32_t *hist_in, int32_t *hist_out,
+                   const void *table, const void *wkv, const float *q_w,
+                   const float *k_w, void *h, float *gate_out, void *workspace,
+                   size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENGRAM_H */

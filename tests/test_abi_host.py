@@ -1,0 +1,152 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/engram.h declares, and rejects bad arguments before
+launching anything (no compute call reaches the device here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from workloads import C0, C1, gen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+E = pytest.importorskip("hashed_gram_conditional_amd")
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+# The validation tests hand the library made-up device addresses that every
+# check must reject before any launch; they only run where no GPU is visible.
+host_only = pytest.mark.skipif(_gpu_visible(), reason="fake device pointers: host-only test")
+
+
+def _declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(engram_[a-z_0-9]+)\s*\(",
+                                src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert len(names) >= 11, names
+    lib = ctypes.CDLL(E.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layouts_match():
+    assert E.LIB.engram_sizeof_hash_params() == ctypes.sizeof(E.HashParams)
+    assert E.LIB.engram_sizeof_forward_desc() == ctypes.sizeof(E.ForwardDesc)
+
+
+@pytest.mark.parametrize("base,count", [(1009, 6), (1_000_000, 24), (16_000_000, 48),
+                                        (2, 30), (4_294_967_000, 3)])
+def test_library_primes_equal_oracle_primes(base, count):
+    p, off, tot = E.engram_make_primes(base, count)
+    po = O.primes_from(base, count)
+    oo, to = O.segment_offsets(po)
+    assert p == po and off == oo and tot == to
+
+
+def test_make_primes_rejects_beyond_32_bits():
+    with pytest.raises(E.EngramError):
+        E.engram_make_primes(4_294_967_290, 2)
+
+
+def test_token_map_check():
+    tm, _ = gen.hash_setup(C1)
+    assert E.engram_check_token_map(tm, C1.raw_vocab, C1.compressed_vocab) == E.OK
+    assert E.engram_check_token_map(tm, C1.raw_vocab, C1.compressed_vocab + 1) == E.EVOCAB
+    bad = tm.copy()
+    bad[5] = C1.compressed_vocab
+    assert E.engram_check_token_map(bad, C1.raw_vocab, C1.compressed_vocab) == E.EVOCAB
+
+
+def _params(w=C0, **kw):
+    tm, mult = gen.hash_setup(w)
+    p, off, _ = E.engram_make_primes(w.prime_base, w.segments)
+    args = dict(raw_vocab=w.raw_vocab, compressed_vocab=w.compressed_vocab,
+                max_ngram=w.max_ngram, heads=w.heads, pad_id=int(tm[0]), token_map=0x1000,
+                multipliers=mult, primes=p, offsets=off)
+    args.update(kw)
+    return E.hash_params(**args)
+
+
+def _hash_status(params, ids=0x2000, B=1, T=4, rows=0x3000):
+    return E.LIB.engram_hash(ctypes.byref(params), ids, B, T, None, None, rows, None)
+
+
+@host_only
+def test_hash_argument_validation():
+    _, mult = gen.hash_setup(C0)
+    lim = O.multiplier_limit(C0.compressed_vocab)
+    assert _hash_status(_params(multipliers=[mult[0] + 1] + mult[1:])) == E.EMULT   # even
+    assert _hash_status(_params(multipliers=[lim + 2] + mult[1:])) == E.EMULT       # too big
+    assert _hash_status(_params(multipliers=[-1] + mult[1:])) == E.EMULT
+    p, off, _ = E.engram_make_primes(C0.prime_base, C0.segments)
+    assert _hash_status(_params(offsets=[0] + off[2:] + [0])) == E.EPRIMES
+    assert _hash_status(_params(primes=[1] + p[1:])) == E.EPRIMES
+    assert _hash_status(_params(pad_id=C0.compressed_vocab)) == E.EINVAL
+    assert _hash_status(_params(token_map=0)) == E.EINVAL
+    assert _hash_status(_params(max_ngram=9)) == E.ESHAPE
+    assert _hash_status(_params(max_ngram=1)) == E.ESHAPE
+    assert _hash_status(_params(heads=0)) == E.ESHAPE
+    assert _hash_status(_params(), ids=0x2001) == E.EINVAL          # misaligned
+    assert _hash_status(_params(), ids=None) == E.EINVAL
+    assert _hash_status(_params(), B=-1) == E.ESHAPE
+
+
+@host_only
+def test_gather_project_gate_validation():
+    L = E.LIB
+    assert L.engram_gather(0x1000, 10, 0, 128, 0x2000, 4, 0x3000, None) == E.ESHAPE
+    assert L.engram_gather(0x1000, 10, 7, 256, 0x2000, 4, 0x3000, None) == E.EINVAL
+    assert L.engram_gather(0x1000, 10, 0, 256, 0x2004, 4, 0x3000, None) == E.EINVAL
+    assert L.engram_gather(0x1000, 10, 1, 30, 0x2000, 4, 0x3000, None) == E.ESHAPE
+    assert L.engram_gather(None, 0, 0, 256, None, 0, None, None) == E.OK      # empty
+    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, 100, 64, 0, None) == E.ESHAPE
+    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, 128, 60, 0, None) == E.ESHAPE
+    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, 128, 64, 2, None) == E.EINVAL
+    assert L.engram_project(0x1008, 0x2000, 0x3000, 4, 128, 64, 0, None) == E.EINVAL
+    d = E.forward_desc(1, 4, 4, 5120, 100, 0, 256)
+    bad = E.forward_desc(1, 4, 9, 5120, 100, 0, 256)
+    assert L.engram_gate(ctypes.byref(bad), 0x1000, 10, 0x2000, 0x3000, 0x4000, 0x5000, None,
+                         None) == E.ESHAPE
+    bad = E.forward_desc(1, 4, 4, 5124, 100, 0, 256)
+    assert L.engram_gate(ctypes.byref(bad), 0x1000, 10, 0x2000, 0x3000, 0x4000, 0x5000, None,
+                         None) == E.ESHAPE
+    assert L.engram_gate(ctypes.byref(d), None, 10, 0x2000, 0x3000, 0x4000, 0x5000, None,
+                         None) == E.EINVAL
+
+
+@host_only
+def test_forward_validation_and_workspace_size():
+    p = _params(C1)
+    d = E.forward_desc(4, 8192, 4, 5120, 384_006_168, 0, 256)
+    n = E.engram_forward_workspace_size(p, d)
+    T = 4 * 8192
+    assert n == T * 24 * 8 + T * 6144 * 2 + T * 25600 * 2
+    L = E.LIB
+    args = [0x1000, None, None, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None]
+    assert L.engram_forward(ctypes.byref(p), ctypes.byref(d), *args, 0x10000, n - 1,
+                            None) == E.EWORKSPACE
+    assert L.engram_forward(ctypes.byref(p), ctypes.byref(d), *args, 0x10010, n,
+                            None) == E.EWORKSPACE                   # not 256-aligned
+    small = E.forward_desc(4, 8192, 4, 5120, 384_006_167, 0, 256)   # rows < sum of primes
+    assert L.engram_forward(ctypes.byref(p), ctypes.byref(small), *args, 0x10000, n,
+                            None) == E.EPRIMES
+    assert E.status_string(E.EPRIMES).startswith("bad primes")

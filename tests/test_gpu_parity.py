@@ -1,0 +1,480 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Row ids and dequantised rows must match bit for bit; projections within a
+bound derived from fp32 accumulation; gates and updated streams within
+|gpu - oracle| <= 1e-3 + 2e-2 |oracle|. Every input is seeded and synthetic
+(workloads/). Full-size workloads are checked on sampled tokens that the oracle
+computes one by one, always including the DEAD-span boundaries.
+"""
+import dataclasses
+import gc
+
+import numpy as np
+import pytest
+
+import oracle as O
+from tests.gpu_util import ATOL, RTOL, assert_close, gemm_tolerance, oracle_rows, oracle_setup, say
+from workloads import C0, C1, C2, C3, C4, gen
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import hashed_gram_conditional_amd as E  # noqa: E402
+from workloads.device import bf16_bits, fill_table, to_device  # noqa: E402
+from workloads.harness import GpuWorkload  # noqa: E402
+
+DEV = "cuda"
+
+# small bf16 layers that still span several tiles and ragged tails
+S_A = dataclasses.replace(C3, name="S_A", seed=1100, batch=2, seq=150, prime_base=5000, hc=2,
+                          dim=136, dead_random=(1, 16), table_seed=3001)
+S_B = dataclasses.replace(C3, name="S_B", seed=1101, batch=3, seq=77, max_ngram=3, heads=2,
+                          prime_base=2000, hc=3, dim=64, dead_random=(1, 5), table_seed=3002,
+                          hash_setup_seed=None)
+
+
+def _cleanup():
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _gpu_rows(gw, ids=None, hist_in=None, hist_out=None, batch=None, seq=None):
+    w = gw.w
+    ids = gw.ids if ids is None else ids
+    batch = w.batch if batch is None else batch
+    seq = w.seq if seq is None else seq
+    rows = torch.full((max(batch * seq, 1), w.segments), -7, dtype=torch.int64, device=DEV)
+    E.engram_hash(gw.params, ids, batch, seq, hist_in, hist_out, rows)
+    torch.cuda.synchronize()
+    return rows[:batch * seq].cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+# hash
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("w", [C0, C1, S_A, S_B], ids=lambda w: w.name)
+def test_hash_bit_exact(w):
+    say(f"hash {w.name}: B={w.batch} T={w.seq} S={w.segments}")
+    gw = GpuWorkload(w, table=False, dense=False)
+    primes, offs, R = oracle_setup(w)
+    assert gw.primes == primes and gw.offsets == offs and gw.rows == R
+    hout = torch.full((w.batch, w.max_ngram - 1), -9, dtype=torch.int32, device=DEV)
+    got = _gpu_rows(gw, hist_out=hout)
+    exp, exp_hist = oracle_rows(gw)
+    assert np.array_equal(got, exp)
+    assert np.array_equal(hout.cpu().numpy(), exp_hist)
+
+
+def test_hash_c4_decode_history():
+    gw = GpuWorkload(C4, table=False, dense=False)
+    hout = torch.empty((C4.batch, 3), dtype=torch.int32, device=DEV)
+    got = _gpu_rows(gw, hist_in=gw.hist_in, hist_out=hout)
+    exp, exp_hist = oracle_rows(gw)
+    assert np.array_equal(got, exp)
+    assert np.array_equal(hout.cpu().numpy(), exp_hist)
+    # history updated in place (hist_out aliases hist_in), two decode steps
+    h = gw.hist_in.clone()
+    ids2 = gw.ids_np.copy()
+    ids2[5, 0] = -1
+    for step_ids in (gw.ids_np, ids2):
+        prev = h.cpu().numpy()
+        got = _gpu_rows(gw, ids=to_device(step_ids), hist_in=h, hist_out=h)
+        exp, exp_hist = oracle_rows(gw, ids=step_ids, hist=prev)
+        assert np.array_equal(got, exp)
+        assert np.array_equal(h.cpu().numpy(), exp_hist)
+
+
+@pytest.mark.parametrize("splits", [(1,), (2, 3), (100, 101, 260), (511,)])
+def test_hash_chunks_equal_one_shot(splits):
+    gw = GpuWorkload(C1, table=False, dense=False)
+    ids = gw.ids_np[:3, :600].copy()
+    ids[1, 98:102] = -1
+    exp, exp_hist = oracle_rows(gw, ids=ids, use_hist=False)
+    exp = exp.reshape(3, 600, -1)
+    hist = torch.empty((3, 3), dtype=torch.int32, device=DEV)
+    bounds = [0] + list(splits) + [600]
+    parts = []
+    for i, (a, b) in enumerate(zip(bounds[:-1], bounds[1:])):
+        chunk = to_device(np.ascontiguousarray(ids[:, a:b]))
+        r = _gpu_rows(gw, ids=chunk, batch=3, seq=b - a, hist_in=hist if i else None,
+                      hist_out=hist)
+        parts.append(r.reshape(3, b - a, -1))
+    assert np.array_equal(np.concatenate(parts, axis=1), exp)
+    assert np.array_equal(hist.cpu().numpy(), exp_hist)
+
+
+def test_hash_edge_cases():
+    gw = GpuWorkload(C0, table=False, dense=False)
+    V = C0.raw_vocab
+    # T = 0 with a history: the state passes through unchanged; B = 0 is a no-op
+    hin = to_device(np.array([[3, -1, 5]], np.int32))
+    hout = torch.full((1, 3), -9, dtype=torch.int32, device=DEV)
+    empty = torch.empty((1, 0), dtype=torch.int32, device=DEV)
+    E.engram_hash(gw.params, empty, 1, 0, hin, hout, None)
+    E.engram_hash(gw.params, empty, 0, 5, None, None, None)
+    torch.cuda.synchronize()
+    assert hout.cpu().numpy().tolist() == [[3, -1, 5]]
+    # short chunks without a history, invalid raw ids and history entries, all-DEAD
+    cases = [
+        np.array([[7]], np.int32),
+        np.array([[7, 9]], np.int32),
+        np.array([[V, -5, 3, V + 100, 2, -1, 8]], np.int32),
+        np.full((2, 9), -1, np.int32),
+    ]
+    for ids in cases:
+        got = _gpu_rows(gw, ids=to_device(ids), batch=ids.shape[0], seq=ids.shape[1])
+        exp, _ = oracle_rows(gw, ids=ids, use_hist=False)
+        assert np.array_equal(got, exp), ids
+    bad_hist = np.array([[120, -3, 4]], np.int32)         # 120 >= V' = 97
+    hin = to_device(bad_hist)
+    ids = np.array([[5, 6]], np.int32)
+    got = _gpu_rows(gw, ids=to_device(ids), batch=1, seq=2, hist_in=hin)
+    exp, _ = oracle_rows(gw, ids=ids, hist=bad_hist)
+    assert np.array_equal(got, exp)
+
+
+# ---------------------------------------------------------------------------
+# gather + dequant
+# ---------------------------------------------------------------------------
+
+def test_dequant_exhaustive_all_code_scale_pairs():
+    rows = np.zeros((256, 8, 264), dtype=np.uint8)
+    codes = np.arange(256, dtype=np.uint8)
+    for s in range(256):
+        for r in range(8):
+            rows[s, r, :256] = codes[(r * 32 + np.arange(256)) % 256]
+            rows[s, r, 256:] = s
+    rows = rows.reshape(-1, 264)
+    table = to_device(rows)
+    rid = to_device(np.arange(rows.shape[0], dtype=np.int64))
+    out = torch.empty((rows.shape[0], 256), dtype=torch.bfloat16, device=DEV)
+    E.engram_gather(table, rows.shape[0], E.ROW_E4M3_E8M0_264, 256, rid, rows.shape[0], out)
+    torch.cuda.synchronize()
+    got = bf16_bits(out)
+    exp = O.dequant_rows_bf16(rows)
+    nan_e = ((exp & 0x7F80) == 0x7F80) & ((exp & 0x7F) != 0)
+    nan_g = ((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)
+    assert np.array_equal(nan_e, nan_g)
+    mism = (got != exp) & ~nan_e
+    assert not mism.any(), (np.argwhere(mism)[:5], got[mism][:5], exp[mism][:5])
+
+
+def test_table_generator_matches_host_twin():
+    rows = 50_000
+    t = torch.empty((rows, 264), dtype=torch.uint8, device=DEV)
+    fill_table(t, 2002, row_begin=24_000_000 - rows)
+    sample = np.array([0, 1, 2, 777, rows // 2, rows - 2, rows - 1])
+    got = t[torch.from_numpy(sample).to(DEV)].cpu().numpy()
+    exp = gen.table_rows(2002, sample + 24_000_000 - rows)
+    assert np.array_equal(got, exp)
+
+
+def test_gather_f32_c0():
+    gw = GpuWorkload(C0, dense=False)
+    rid_np, _ = oracle_rows(gw)
+    rid_np = rid_np.copy()
+    rid_np[3, 1] = gw.rows            # out of range -> zeros
+    rid_np[5, 0] = -4
+    rid = to_device(rid_np.reshape(-1))
+    out = torch.empty((rid_np.size, C0.row_dim), dtype=torch.float32, device=DEV)
+    E.engram_gather(gw.table, gw.rows, E.ROW_F32, C0.row_dim, rid, rid_np.size, out)
+    torch.cuda.synchronize()
+    exp = O.gather_f32(gw.dense_np["table"], rid_np)
+    assert np.array_equal(out.cpu().numpy().reshape(exp.shape), exp)
+
+
+def test_gather_out_of_range_and_ragged():
+    seed = 4242
+    R = 1000
+    t = torch.empty((R, 264), dtype=torch.uint8, device=DEV)
+    fill_table(t, seed)
+    rng = np.random.default_rng(0)
+    for n in (1, 15, 17, 63, 65, 333):
+        rid_np = rng.integers(-3, R + 3, n).astype(np.int64)
+        rid_np[0] = R
+        out = torch.full((n, 256), 7.0, dtype=torch.bfloat16, device=DEV)
+        E.engram_gather(t, R, E.ROW_E4M3_E8M0_264, 256, to_device(rid_np), n, out)
+        torch.cuda.synchronize()
+        exp = O.gather_e4m3(lambda r: gen.table_rows(seed, r), rid_np.reshape(n, 1), R)
+        assert np.array_equal(bf16_bits(out), exp)
+
+
+def test_gather_c2_full_size_sampled():
+    say("C2 gather: table 24,003,916 x 264 B, 131072 tokens x 24 rows")
+    gw = GpuWorkload(C2)
+    try:
+        rows = torch.empty((C2.tokens, 24), dtype=torch.int64, device=DEV)
+        E.engram_hash(gw.params, gw.ids, C2.batch, C2.seq, None, None, rows)
+        out = torch.empty((C2.tokens * 24, 256), dtype=torch.bfloat16, device=DEV)
+        E.engram_gather(gw.table, gw.rows, E.ROW_E4M3_E8M0_264, 256, rows, C2.tokens * 24, out)
+        torch.cuda.synchronize()
+        exp_rows, _ = oracle_rows(gw)
+        assert np.array_equal(rows.cpu().numpy(), exp_rows)
+        rng = np.random.default_rng(12)
+        sample = np.unique(np.concatenate([rng.integers(0, C2.tokens * 24, 6000),
+                                           np.arange(24), C2.tokens * 24 - 1 - np.arange(24)]))
+        got = bf16_bits(out[torch.from_numpy(sample).to(DEV)])
+        exp = O.gather_e4m3(gw.fetch_rows, exp_rows.reshape(-1)[sample].reshape(-1, 1), gw.rows)
+        assert np.array_equal(got, exp)
+    finally:
+        gw.free()
+        _cleanup()
+
+
+# ---------------------------------------------------------------------------
+# projection
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(1, 8, 64), (31, 264, 192), (257, 520, 1024),
+                                   (300, 408, 6144), (600, 256, 128), (513, 1032, 256)])
+def test_project_bf16_shapes(M, N, K):
+    rng = np.random.default_rng(M * 7 + N)
+    e = gen.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32) * 3)
+    w = gen.f32_to_bf16_bits(rng.standard_normal((N, K)).astype(np.float32) * 0.05)
+    kv = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    E.engram_project(to_device(e), to_device(w), kv, M, K, N, 0)
+    torch.cuda.synchronize()
+    got = O.bf16_bits_to_f64(bf16_bits(kv))
+    ef, wf = O.bf16_bits_to_f64(e), O.bf16_bits_to_f64(w)
+    exact = O.project(ef, wf)
+    tol = gemm_tolerance(ef, wf, exact, True)
+    assert_close(got, exact, f"kv {M}x{N}x{K}", atol=0.0, rtol=0.0, extra=tol)
+
+
+def test_project_one_hot_exact():
+    M, N, K = 130, 264, 256
+    rng = np.random.default_rng(3)
+    w = gen.f32_to_bf16_bits(rng.standard_normal((N, K)).astype(np.float32))
+    e = np.zeros((M, K), np.uint16)
+    ks = rng.integers(0, K, M)
+    e[np.arange(M), ks] = 0x3F80                      # 1.0
+    kv = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    E.engram_project(to_device(e), to_device(w), kv, M, K, N, 0)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(kv), w.T[ks])
+
+
+def test_project_f32():
+    rng = np.random.default_rng(4)
+    for M, N, K in ((64, 128, 192), (5, 12, 8)):
+        e = rng.standard_normal((M, K)).astype(np.float32)
+        w = rng.standard_normal((N, K)).astype(np.float32)
+        kv = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        E.engram_project(to_device(e), to_device(w), kv, M, K, N, 1)
+        torch.cuda.synchronize()
+        exact = O.project(e, w)
+        assert_close(kv.cpu().numpy(), exact, "kv f32", atol=0, rtol=0,
+                     extra=gemm_tolerance(e, w, exact, False))
+
+
+# ---------------------------------------------------------------------------
+# forward, stage by stage and end to end
+# ---------------------------------------------------------------------------
+
+def _bits(t):
+    return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
+
+
+def _h_values(gw, h_dev):
+    if gw.f32:
+        return h_dev.cpu().numpy().astype(np.float64)
+    return O.bf16_bits_to_f64(bf16_bits(h_dev))
+
+
+def _h_input(gw):
+    h = gw.dense_np["h"]
+    return h.astype(np.float64) if gw.f32 else O.bf16_bits_to_f64(h)
+
+
+def _check_forward(gw, h_out_dev, gates_dev, tokens, kv_dev=None):
+    """Oracle on ``tokens`` against the device results of a full forward."""
+    w = gw.w
+    rid, _ = oracle_rows(gw)
+    dead = gw.dead_np()
+    h_in = _h_input(gw).reshape(w.tokens, w.hc, w.dim)
+    res = O.forward_tokens(tokens, rid, dead, fetch_rows=gw.fetch_rows,
+                           table_f32=gw.dense_np.get("table"), table_rows=gw.rows,
+                           wkv=(gw.dense_np["wkv"] if gw.f32 else
+                                O.bf16_bits_to_f64(gw.dense_np["wkv"])),
+                           q_w=gw.dense_np["q_w"], k_w=gw.dense_np["k_w"], h=h_in, hc=w.hc,
+                           dim=w.dim, eps=w.eps, clamp=w.gate_clamp, bf16=not gw.f32)
+    tok_dev = torch.from_numpy(np.asarray(tokens)).to(DEV)
+    h_got = _h_values(gw, h_out_dev.reshape(w.tokens, w.hc, w.dim)[tok_dev])
+    a_got = gates_dev[tok_dev].cpu().numpy().astype(np.float64)
+    assert_close(a_got, res["alpha"], f"{w.name} gates")
+    d = dead[tokens]
+    assert np.all(a_got[d] == 0.0)
+    # DEAD rows are left bit-identical
+    assert np.array_equal(h_got[d], h_in[tokens][d])
+    extra = 0.0
+    if kv_dev is not None:
+        # the projection's own bounded difference propagates through alpha * v
+        kv_got = kv_dev.reshape(w.tokens, w.hc + 1, w.dim)[tok_dev]
+        kv_got = (kv_got.cpu().numpy().astype(np.float64) if gw.f32 else
+                  O.bf16_bits_to_f64(bf16_bits(kv_got)))
+        exact = O.project(res["e"], gw.dense_np["wkv"] if gw.f32 else
+                          O.bf16_bits_to_f64(gw.dense_np["wkv"])).reshape(kv_got.shape)
+        wf = gw.dense_np["wkv"] if gw.f32 else O.bf16_bits_to_f64(gw.dense_np["wkv"])
+        tol = gemm_tolerance(res["e"], wf, exact.reshape(len(tokens), -1),
+                             not gw.f32).reshape(kv_got.shape)
+        assert_close(kv_got, exact, f"{w.name} kv", atol=0, rtol=0, extra=tol)
+        dv = np.abs(kv_got[:, w.hc, :] - res["kv"][:, w.hc, :])
+        extra = res["alpha"][:, :, None] * dv[:, None, :]
+    assert_close(h_got, res["h_out"], f"{w.name} h", extra=extra)
+    return res
+
+
+def _run_stages(gw):
+    """engram_hash -> engram_gather -> engram_project -> engram_gate, returning
+    the intermediate device tensors; h is updated in place."""
+    w = gw.w
+    T, S = w.tokens, w.segments
+    dt = torch.float32 if gw.f32 else torch.bfloat16
+    rows = torch.empty((T, S), dtype=torch.int64, device=DEV)
+    E.engram_hash(gw.params, gw.ids, w.batch, w.seq, gw.hist_in, None, rows)
+    e = torch.empty((T, S * w.row_dim), dtype=dt, device=DEV)
+    E.engram_gather(gw.table, gw.rows, gw.row_format, w.row_dim, rows, T * S, e)
+    kv = torch.empty((T, (w.hc + 1) * w.dim), dtype=dt, device=DEV)
+    E.engram_project(e, gw.wkv, kv, T, S * w.row_dim, (w.hc + 1) * w.dim, int(gw.f32))
+    gates = torch.empty((T, w.hc), dtype=torch.float32, device=DEV)
+    E.engram_gate(gw.desc, gw.ids, w.raw_vocab, kv, gw.q_w, gw.k_w, gw.h, gates)
+    torch.cuda.synchronize()
+    return rows, e, kv, gates
+
+
+def _forward(gw, h):
+    w = gw.w
+    ws, n = gw.workspace()
+    gates = torch.full((w.tokens, w.hc), -1.0, dtype=torch.float32, device=DEV)
+    E.engram_forward(gw.params, gw.desc, gw.ids, gw.hist_in, None, gw.table, gw.wkv, gw.q_w,
+                     gw.k_w, h, gates, ws, n)
+    torch.cuda.synchronize()
+    return gates
+
+
+@pytest.mark.parametrize("w", [C0, S_A, S_B], ids=lambda w: w.name)
+def test_forward_full_small(w):
+    say(f"forward {w.name}: tokens={w.tokens} hc={w.hc} d={w.dim} S={w.segments}")
+    gw = GpuWorkload(w)
+    h0 = gw.h.clone()
+    rows, e, kv, gates = _run_stages(gw)
+    _check_forward(gw, gw.h, gates, np.arange(w.tokens), kv_dev=kv)
+    # the fused entry point computes the same bits as the stage entry points
+    h1 = h0.clone()
+    g1 = _forward(gw, h1)
+    assert torch.equal(_bits(h1), _bits(gw.h))
+    assert torch.equal(g1, gates)
+
+
+def test_forward_stagewise_gate_on_device_kv():
+    """Gate fed the device's own kv: isolates the gate from projection rounding."""
+    gw = GpuWorkload(S_A)
+    h_in = _h_input(gw).reshape(S_A.tokens, S_A.hc, S_A.dim)
+    rows, e, kv, gates = _run_stages(gw)
+    kvf = O.bf16_bits_to_f64(bf16_bits(kv)).reshape(S_A.tokens, S_A.hc + 1, S_A.dim)
+    a, h_out = O.gate(h_in, kvf[:, :S_A.hc], kvf[:, S_A.hc], gw.dense_np["q_w"],
+                      gw.dense_np["k_w"], gw.dead_np(), S_A.eps, S_A.gate_clamp)
+    assert_close(gates.cpu().numpy(), a, "gates")
+    h_got = _h_values(gw, gw.h).reshape(h_out.shape)
+    assert_close(h_got, O.bf16_bits_to_f64(O.round_to_bf16_bits(h_out)), "h")
+    # e equals the oracle's gather bit for bit
+    rid, _ = oracle_rows(gw)
+    assert np.array_equal(rows.cpu().numpy(), rid)
+    assert np.array_equal(bf16_bits(e).reshape(-1, 256),
+                          O.gather_e4m3(gw.fetch_rows, rid, gw.rows).reshape(-1, 256))
+
+
+def test_forward_chunked_and_deterministic():
+    gw = GpuWorkload(S_A)
+    w = S_A
+    h_ref = gw.h.clone()
+    g_ref = _forward(gw, h_ref)
+    h_again = gw.h.clone()
+    g_again = _forward(gw, h_again)
+    assert torch.equal(h_ref.view(torch.int16), h_again.view(torch.int16))
+    assert torch.equal(g_ref, g_again)
+    # two chunks carrying the hash history reproduce the one-shot bits
+    cut = 61
+    h_chunks = gw.h.clone()
+    hist = torch.empty((w.batch, 3), dtype=torch.int32, device=DEV)
+    gates = []
+    for a, b in ((0, cut), (cut, w.seq)):
+        sub = dataclasses.replace(w, seq=b - a)
+        d = E.forward_desc(w.batch, b - a, w.hc, w.dim, gw.rows, gw.row_format, w.row_dim,
+                           w.eps, w.gate_clamp)
+        ids = gw.ids[:, a:b].contiguous()
+        hc_ = h_chunks[:, a:b].contiguous()
+        n = E.engram_forward_workspace_size(gw.params, d)
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=DEV)
+        g = torch.empty((w.batch * (b - a), w.hc), dtype=torch.float32, device=DEV)
+        E.engram_forward(gw.params, d, ids, hist if a else None, hist, gw.table, gw.wkv,
+                         gw.q_w, gw.k_w, hc_, g, ws, n)
+        h_chunks[:, a:b] = hc_
+        gates.append(g.reshape(w.batch, b - a, w.hc))
+        del sub
+    torch.cuda.synchronize()
+    assert torch.equal(h_chunks.view(torch.int16), h_ref.view(torch.int16))
+    assert torch.equal(torch.cat(gates, 1).reshape(-1, w.hc), g_ref)
+
+
+def _sample_tokens(gw, n_random, seed):
+    w = gw.w
+    rng = np.random.default_rng(seed)
+    pick = set(rng.integers(0, w.tokens, n_random).tolist()) | {0, w.tokens - 1}
+    for b, spans in enumerate(gw.spans):
+        for a, e in spans:
+            for t in (a - 2, a - 1, a, e - 1, e, e + 1, e + 2, e + 3):
+                if 0 <= t < w.seq:
+                    pick.add(b * w.seq + t)
+    return np.array(sorted(pick))
+
+
+def test_forward_c3_full_size_sampled():
+    say("C3 forward: 4x8192 tokens, 6.34 GB table, wkv [25600, 6144], h [4,8192,4,5120]")
+    gw = GpuWorkload(C3)
+    try:
+        h0 = gw.h.clone()
+        rows, e, kv, gates = _run_stages(gw)
+        tokens = _sample_tokens(gw, 24, 31)
+        say(f"  oracle on {len(tokens)} sampled tokens")
+        _check_forward(gw, gw.h, gates, tokens, kv_dev=kv)
+        del rows, e
+        h1 = h0
+        g1 = _forward(gw, h1)
+        assert torch.equal(h1.view(torch.int16), gw.h.view(torch.int16))
+        assert torch.equal(g1, gates)
+    finally:
+        gw.free()
+        _cleanup()
+
+
+def test_forward_c4_decode_full_table():
+    say("C4 decode: 256 x 1 token, 384,006,168-row (101.4 GB) table")
+    gw = GpuWorkload(C4)
+    try:
+        h0 = gw.h.clone()
+        rows, e, kv, gates = _run_stages(gw)
+        rng = np.random.default_rng(5)
+        tokens = np.unique(np.concatenate([[0, 1, 255], rng.integers(0, 256, 29)]))
+        _check_forward(gw, gw.h, gates, tokens, kv_dev=kv)
+        assert gates[0].abs().sum().item() == 0.0
+        assert torch.equal(gw.h[0].view(torch.int16), h0[0].view(torch.int16))
+        # the fused decode step: same bits, and the history after the token
+        ws, n = gw.workspace()
+        g1 = torch.empty((C4.tokens, C4.hc), dtype=torch.float32, device=DEV)
+        hout = torch.empty((C4.batch, 3), dtype=torch.int32, device=DEV)
+        E.engram_forward(gw.params, gw.desc, gw.ids, gw.hist_in, hout, gw.table, gw.wkv,
+                         gw.q_w, gw.k_w, h0, g1, ws, n)
+        torch.cuda.synchronize()
+        _, exp_hist = oracle_rows(gw)
+        assert np.array_equal(hout.cpu().numpy(), exp_hist)
+        assert torch.equal(h0.view(torch.int16), gw.h.view(torch.int16))
+        assert torch.equal(g1, gates)
+    finally:
+        gw.free()
+        _cleanup()
