@@ -1,0 +1,242 @@
+"""Benchmark of the Engram layer forward on one MI355X.
+
+Workload: the full prefill layer forward at the pages' shape -- 4 sequences x
+8192 Zipf(1.1) tokens with 2 DEAD spans of 256 per sequence, the 24 (order,
+head) segments of primes from 1,000,000 (24,003,916 rows x 264 B = 6.34 GB,
+generated on the device), wkv bf16 [25600, 6144], hc = 4 streams of width 5120.
+All inputs are seeded synthetic data already resident in HBM when timing
+starts.
+
+One step = one pass of the whole hot path over the batch: engram_hash ->
+engram_gather -> engram_project -> engram_gate, the four launches that
+engram_forward makes, called through the C ABI on torch's current stream with
+HIP events between them. W untimed warmup steps, then K timed steps bracketed by
+torch.cuda.synchronize(). Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Engram layer tokens/s (hash+gather+gate) and gather GB/s vs HBM peak, 1 GPU"
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0         # MI355X dense bf16 MFMA
+# Algorithmic bytes per token of the gather: 24 row ids (int64) read, 24 rows of
+# 264 B read, 6144 bf16 written.
+GATHER_BYTES_PER_TOKEN = 24 * 8 + 24 * 264 + 6144 * 2
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def measured_traffic(kernel: str, source: str):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 PMC summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by the counter's reading for a copy of
+    known size), or None when no summary matches the current kernel source."""
+    import glob
+    import hashlib
+    sha = hashlib.sha256(open(os.path.join(ROOT, source), "rb").read()).hexdigest()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for line in open(path):
+            f = line.split()
+            if len(f) >= 3 and f[0] == "traffic" and f[1] == kernel:
+                kv = dict(x.split("=", 1) for x in f[2:])
+                if kv.get("sha256") != sha:
+                    continue
+                fetch = float(kv["fetch_kib"]) * 1024 * float(kv["fetch_scale"])
+                write = float(kv["write_kib"]) * 1024 * float(kv["write_scale"])
+                return {"bytes": round(fetch + write), "read": round(fetch), "written": round(write),
+                        "source": os.path.relpath(path, ROOT)}
+    return None
+
+
+def cpu_baseline(gw, target_s: float = 10.0, max_tokens: int = 8192):
+    """The oracle as it stands, timed on the host on a bounded sample: all five
+    steps for the first n tokens of sequence 0 (table rows materialised in host
+    RAM beforehand, so the gather reads memory rather than regenerating rows)."""
+    import oracle as O
+    from workloads import gen
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        cores = int(blas[0]["num_threads"]) if blas else 1
+    except Exception:
+        cores = os.cpu_count() or 1
+    w = gw.w
+    primes = O.primes_from(w.prime_base, w.segments)
+    offs, R = O.segment_offsets(primes)
+    wkv = O.bf16_bits_to_f64(gw.dense_np["wkv"])
+    q_w, k_w = gw.dense_np["q_w"], gw.dense_np["k_w"]
+    h_seq0 = gw.dense_np["h"][0]
+    ids0 = gw.ids_np[:1]
+    dead0 = (ids0[0] < 0) | (ids0[0] >= w.raw_vocab)
+
+    def run(n):
+        ids = np.ascontiguousarray(ids0[:, :n])
+        rid_all, _ = O.hash_rows(ids, gw.token_map_np, w.compressed_vocab, gw.pad, gw.mult,
+                                 primes, offs, w.max_ngram, w.heads)
+        need = np.unique(rid_all)
+        host_rows = gen.table_rows(w.table_seed, need)
+
+        def fetch(r):
+            return host_rows[np.searchsorted(need, r)]
+
+        h = O.bf16_bits_to_f64(h_seq0[:n])
+        t0 = time.perf_counter()
+        rid, _ = O.hash_rows(ids, gw.token_map_np, w.compressed_vocab, gw.pad, gw.mult,
+                             primes, offs, w.max_ngram, w.heads)
+        O.forward_tokens(np.arange(n), rid, dead0[:n], fetch_rows=fetch, table_rows=R,
+                         wkv=wkv, q_w=q_w, k_w=k_w, h=h, hc=w.hc, dim=w.dim, eps=w.eps,
+                         clamp=w.gate_clamp, bf16=True)
+        return time.perf_counter() - t0
+
+    n = 64
+    dt = run(n)
+    while dt < target_s / 4 and n < max_tokens:
+        n = min(max_tokens, int(n * max(2.0, min(16.0, target_s / max(dt, 1e-3)))))
+        dt = run(n)
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n} tokens of sequence 0 of the same prefill workload, all five "
+                      f"steps in fp64 numpy, table rows pre-read into host RAM; {dt:.2f} s "
+                      f"on {os.cpu_count()} host CPUs (BLAS threads {cores})"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures the layer on one GPU only; the sharded design "
+              "is described in DESIGN.md and no multi-GPU run is made.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import hashed_gram_conditional_amd as E
+    from workloads import C3
+    from workloads.harness import GpuWorkload
+
+    torch.cuda.set_device(0)
+    t_setup = time.perf_counter()
+    gw = GpuWorkload(C3)
+    w = gw.w
+    T, S = w.tokens, w.segments
+    K_in, N_out = S * w.row_dim, (w.hc + 1) * w.dim
+    rows = torch.empty((T, S), dtype=torch.int64, device="cuda")
+    e = torch.empty((T, K_in), dtype=torch.bfloat16, device="cuda")
+    kv = torch.empty((T, N_out), dtype=torch.bfloat16, device="cuda")
+    gates = torch.empty((T, w.hc), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    log(f"setup {time.perf_counter() - t_setup:.1f} s: {T} tokens, table {gw.rows} rows")
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+
+    def step(evs):
+        if evs:
+            evs[0].record(stream)
+        E.engram_hash(gw.params, gw.ids, w.batch, w.seq, None, None, rows)
+        if evs:
+            evs[1].record(stream)
+        E.engram_gather(gw.table, gw.rows, gw.row_format, w.row_dim, rows, T * S, e)
+        if evs:
+            evs[2].record(stream)
+        E.engram_project(e, gw.wkv, kv, T, K_in, N_out, 0)
+        if evs:
+            evs[3].record(stream)
+        E.engram_gate(gw.desc, gw.ids, w.raw_vocab, kv, gw.q_w, gw.k_w, gw.h, gates)
+        if evs:
+            evs[4].record(stream)
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = np.mean([[s[j].elapsed_time(s[j + 1]) for j in range(4)] for s in ev], axis=0)
+    ms_per_step = 1e3 * wall / args.steps
+
+    # the fused entry point, for comparison (same launches, one call)
+    ws, nws = gw.workspace()
+    fe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for _ in range(2):
+        E.engram_forward(gw.params, gw.desc, gw.ids, None, None, gw.table, gw.wkv, gw.q_w,
+                         gw.k_w, gw.h, gates, ws, nws)
+    fe[0].record(stream)
+    for _ in range(args.steps):
+        E.engram_forward(gw.params, gw.desc, gw.ids, None, None, gw.table, gw.wkv, gw.q_w,
+                         gw.k_w, gw.h, gates, ws, nws)
+    fe[1].record(stream)
+    torch.cuda.synchronize()
+    forward_ms = fe[0].elapsed_time(fe[1]) / args.steps
+
+    flops = 2.0 * T * N_out * K_in
+    gemm_tflops = flops / (stage_ms[2] * 1e-3) / 1e12
+    gather_gbps = GATHER_BYTES_PER_TOKEN * T / (stage_ms[1] * 1e-3) / 1e9
+    tokens_per_s = T / (ms_per_step * 1e-3)
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill layer forward: 4 x 8192 Zipf tokens, 24 segments of "
+                               "primes from 1,000,000 (24,003,916 x 264 B rows), wkv "
+                               "6144 -> 5 x 5120, hc 4 x 5120",
+                   "batch": w.batch, "seq": w.seq, "segments": S, "hc": w.hc, "dim": w.dim,
+                   "table_rows": gw.rows},
+        "roofline": {"bound": "mfma", "kernel": "gemm_bf16_kernel (engram_project)",
+                     "achieved": round(gemm_tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic("gemm_bf16_kernel",
+                                                 "hashed_gram_conditional_amd/csrc/gemm.hip"),
+                     "algorithmic_flop": flops},
+        "gather": {"kernel": "gather_e4m3_kernel (engram_gather)",
+                   "achieved": round(gather_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                   "frac": round(gather_gbps / HBM_PEAK_GBPS, 4),
+                   "bytes_per_token": GATHER_BYTES_PER_TOKEN},
+        "stages_ms": {"hash": round(stage_ms[0], 4), "gather": round(stage_ms[1], 4),
+                      "project": round(stage_ms[2], 4), "gate": round(stage_ms[3], 4)},
+        "engram_forward_ms": round(forward_ms, 4),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(gw)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
