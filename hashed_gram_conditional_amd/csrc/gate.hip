@@ -10,47 +10,55 @@
 // reciprocal roots of the mean squares, the update rounded to bf16 once) and
 // "布局与哈希探测" item 4 (masked rows are left untouched).
 //
-// One block of 256 threads per token. Each thread owns CPT chunks of 4
-// elements per stream; it keeps its h chunks in registers between the three
-// reductions (sum h^2, sum k^2, sum h q_w k_w k per stream) and the update, so
-// h is read once and written once. All arithmetic is fp32.
+// One block of 128 threads per token. Each thread owns CPT chunks of 8
+// elements per stream (16-byte bf16 accesses). The three reductions per stream
+// (sum h^2, sum k^2, sum h q_w k_w k) run first; the update then reads the
+// token's h again, which the L2 still holds (40 KiB per token), instead of
+// keeping it in registers, so more blocks fit per CU. All arithmetic is fp32.
 #include "common.h"
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 128;
 constexpr int kMaxHc = 8;
+constexpr int kChunk = 8;        // elements per chunk
 
 template <bool F32>
 struct Chunk;
 template <>
-struct Chunk<false> {   // 4 bf16
-  uint2 v;
+struct Chunk<false> {   // 8 bf16
+  uint4 v;
   __device__ __forceinline__ void load(const void *p, int64_t i) {
-    v = reinterpret_cast<const uint2 *>(p)[i];
+    v = reinterpret_cast<const uint4 *>(p)[i];
   }
   __device__ __forceinline__ float operator[](int e) const {
-    const uint32_t w = e < 2 ? v.x : v.y;
+    const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
     return engram::bf16_to_f32((e & 1) ? (w >> 16) : (w & 0xFFFFu));
   }
-  __device__ __forceinline__ static void store(void *p, int64_t i, const float f[4]) {
-    uint2 o;
+  __device__ __forceinline__ static void store(void *p, int64_t i, const float f[8]) {
+    uint4 o;
     o.x = engram::pack_bf16x2(f[0], f[1]);
     o.y = engram::pack_bf16x2(f[2], f[3]);
-    reinterpret_cast<uint2 *>(p)[i] = o;
+    o.z = engram::pack_bf16x2(f[4], f[5]);
+    o.w = engram::pack_bf16x2(f[6], f[7]);
+    reinterpret_cast<uint4 *>(p)[i] = o;
   }
 };
 template <>
-struct Chunk<true> {    // 4 fp32
-  float4 v;
+struct Chunk<true> {    // 8 fp32
+  float4 a, b;
   __device__ __forceinline__ void load(const void *p, int64_t i) {
-    v = reinterpret_cast<const float4 *>(p)[i];
+    a = reinterpret_cast<const float4 *>(p)[2 * i];
+    b = reinterpret_cast<const float4 *>(p)[2 * i + 1];
   }
   __device__ __forceinline__ float operator[](int e) const {
-    return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+    const float4 &q = e < 4 ? a : b;
+    const int r = e & 3;
+    return r == 0 ? q.x : r == 1 ? q.y : r == 2 ? q.z : q.w;
   }
-  __device__ __forceinline__ static void store(void *p, int64_t i, const float f[4]) {
-    reinterpret_cast<float4 *>(p)[i] = make_float4(f[0], f[1], f[2], f[3]);
+  __device__ __forceinline__ static void store(void *p, int64_t i, const float f[8]) {
+    reinterpret_cast<float4 *>(p)[2 * i] = make_float4(f[0], f[1], f[2], f[3]);
+    reinterpret_cast<float4 *>(p)[2 * i + 1] = make_float4(f[4], f[5], f[6], f[7]);
   }
 };
 
@@ -67,11 +75,10 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(
     if (gate_out != nullptr && tid < hc) gate_out[t * hc + tid] = 0.f;
     return;
   }
-  const int cps = dim >> 2;                       // chunks per stream
+  const int cps = dim / kChunk;                   // chunks per stream
   const int64_t kv_row = t * (int64_t)(hc + 1) * cps;
   const int64_t h_row = t * (int64_t)hc * cps;
 
-  Chunk<F32> hv[kMaxHc][CPT];
   Chunk<F32> vv[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
@@ -89,15 +96,17 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(
       for (int c = 0; c < CPT; ++c) {
         const int ci = tid + c * kThreads;
         if (ci < cps) {
-          Chunk<F32> kc;
-          hv[m][c].load(h, h_row + (int64_t)m * cps + ci);
+          Chunk<F32> hc_, kc;
+          hc_.load(h, h_row + (int64_t)m * cps + ci);
           kc.load(kv, kv_row + (int64_t)m * cps + ci);
-          const float4 qw = reinterpret_cast<const float4 *>(q_w + (int64_t)m * dim)[ci];
-          const float4 kw = reinterpret_cast<const float4 *>(k_w + (int64_t)m * dim)[ci];
-          const float w[4] = {qw.x * kw.x, qw.y * kw.y, qw.z * kw.z, qw.w * kw.w};
+          const float4 *qp = reinterpret_cast<const float4 *>(q_w + (int64_t)m * dim) + 2 * ci;
+          const float4 *kp = reinterpret_cast<const float4 *>(k_w + (int64_t)m * dim) + 2 * ci;
+          const float4 q0 = qp[0], q1 = qp[1], k0 = kp[0], k1 = kp[1];
+          const float w[8] = {q0.x * k0.x, q0.y * k0.y, q0.z * k0.z, q0.w * k0.w,
+                              q1.x * k1.x, q1.y * k1.y, q1.z * k1.z, q1.w * k1.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float he = hv[m][c][e];
+          for (int e = 0; e < 8; ++e) {
+            const float he = hc_[e];
             const float ke = kc[e];
             shh[m] = fmaf(he, he, shh[m]);
             skk[m] = fmaf(ke, ke, skk[m]);
@@ -156,9 +165,11 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(
       for (int c = 0; c < CPT; ++c) {
         const int ci = tid + c * kThreads;
         if (ci < cps) {
-          float o[4];
+          Chunk<F32> hc_;
+          hc_.load(h, h_row + (int64_t)m * cps + ci);
+          float o[8];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = fmaf(alpha[m], vv[c][e], hv[m][c][e]);
+          for (int e = 0; e < 8; ++e) o[e] = fmaf(alpha[m], vv[c][e], hc_[e]);
           Chunk<F32>::store(h, h_row + (int64_t)m * cps + ci, o);
         }
       }
@@ -200,7 +211,7 @@ hipError_t engram_launch_gate(bool f32, const int32_t *ids, int32_t raw_vocab, c
                               int64_t tokens, int32_t hc, int32_t dim, float eps, float clamp,
                               hipStream_t stream) {
   if (tokens <= 0) return hipSuccess;
-  const int cps = dim / 4;
+  const int cps = dim / kChunk;
   const int cpt = (cps + kThreads - 1) / kThreads;
   return f32 ? launch<true>(cpt, ids, raw_vocab, kv, q_w, k_w, h, gate_out, tokens, hc, dim,
                             eps, clamp, stream)

@@ -6,17 +6,23 @@
 // weight is stored with the 6144 inputs innermost).
 //
 // bf16 path: C[m, n] = sum_k E[m, k] W[n, k]; both operands are K-contiguous.
-// One block of 4 waves computes a 256 (n) x 256 (m) tile; each wave a 128 x 128
-// quarter as 4 x 4 v_mfma_f32_32x32x16_bf16 tiles with fp32 accumulators.
-// W rows feed the MFMA's first operand and E rows the second, so each lane's
-// accumulator holds 4 consecutive output columns of one token and the epilogue
-// writes 8-byte bf16 quads.
+// One block of 8 waves (2 per SIMD) computes a 256 (n) x 256 (m) tile; wave w
+// owns a 128 (n) x 64 (m) quarter-strip as 4 x 2 v_mfma_f32_32x32x16_bf16 tiles
+// with fp32 accumulators. W rows feed the MFMA's first operand and E rows the
+// second, so each lane's accumulator holds 4 consecutive output columns of one
+// token and the epilogue writes 8-byte bf16 quads.
 //
-// The K loop stages 256 x 64 tiles of both operands in LDS, double-buffered
-// (2 x 64 KiB): global loads of step k+1 are in flight while step k's MFMAs run.
-// Each LDS row is 128 bytes (8 chunks of 16 bytes); chunk c of row r is stored
-// at slot c ^ (r & 7), so the 16-byte fragment reads of 8 consecutive rows hit
-// 8 different bank groups.
+// K advances in steps of 64 through two 64 KiB LDS stages. Operand tiles move
+// global -> LDS by direct buffer loads (no VGPR staging): instruction i of wave
+// w fills 1 KiB = 8 rows of 128 bytes, lane p landing in row (4w + i) * 8 +
+// p / 8, 16-byte slot p % 8. Chunk c of row r is stored in slot
+// c ^ (r & 7) ^ ((r >> 3) & 1), so the 16-byte fragment reads of any 16
+// consecutive rows touch 16 distinct 16-byte bank groups (and any 8 rows 8),
+// which keeps the reads free of bank conflicts. The loads of step k+1 fly while
+// step k's MFMAs run. One barrier per step sits before the last MFMAs of the
+// step, so the first fragments of step k+1 are read while those MFMAs drain.
+// Buffer loads past the operand panel's last valid row return zeros, which
+// covers the M and N edges.
 //
 // Blocks are renumbered so that the blocks the hardware places on one XCD (it
 // deals block ids round-robin over 8 XCDs) form one contiguous range, and tiles
@@ -27,33 +33,24 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+#define ENGRAM_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
 constexpr int BM = 256;       // tokens per tile
 constexpr int BN = 256;       // output columns per tile
 constexpr int BK = 64;        // K per stage
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
-constexpr int kChunks = BK / 8;                       // 16-byte chunks per LDS row
-constexpr int kLoads = BM * kChunks / kThreads;       // 16-byte loads per thread per operand
-
 // Buffer resource word 3 for gfx9-family raw buffers (no format, no swizzle).
 constexpr int kBufferFlags = 0x00020000;
-
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * BK + ((chunk ^ (row & 7)) << 3);
-}
-
-__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
-  return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
-}
 
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
     const uint16_t *__restrict__ E, const uint16_t *__restrict__ W, uint16_t *__restrict__ C,
     int M, int N, int K, int tiles_m, int tiles_n) {
-  __shared__ __align__(16) uint16_t sW[2 * BN * BK];   // [2][BN][BK]
-  __shared__ __align__(16) uint16_t sE[2 * BM * BK];   // [2][BM][BK]
+  __shared__ __align__(1024) uint16_t sW0[BN * BK];
+  __shared__ __align__(1024) uint16_t sW1[BN * BK];
+  __shared__ __align__(1024) uint16_t sE0[BM * BK];
+  __shared__ __align__(1024) uint16_t sE1[BM * BK];
 
   // ---- tile assignment ----
   const int nblocks = tiles_m * tiles_n;
@@ -65,107 +62,111 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
   const int first_m = group * kGroupM;
   const int gsize = min(tiles_m - first_m, kGroupM);
   const int local = bid - group * in_group;
-  const int tile_m = first_m + local % gsize;
-  const int tile_n = local / gsize;
-  const int m0 = tile_m * BM;
-  const int n0 = tile_n * BN;
+  const int m0 = (first_m + local % gsize) * BM;
+  const int n0 = (local / gsize) * BN;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wn = wave >> 1;     // which 128 output columns
-  const int wm = wave & 1;      // which 128 tokens
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // 0..7
+  const int wn = wave >> 2;        // which 128 output columns
+  const int wm = wave & 3;         // which 64 tokens
 
-  // ---- global -> register staging through buffer loads ----
-  // One buffer resource per operand panel (its 256 rows x K); loads past the
-  // panel's last valid row return zeros, which covers the M and N edges. Thread
-  // tid stages 16-byte chunk c = tid % 8 of rows tid / 8 + 32 i, i < 8; the
-  // K step advances the uniform offset only.
   const int rows_w = min(BN, N - n0);
   const int rows_e = min(BM, M - m0);
   const __amdgpu_buffer_rsrc_t rsW = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(W + (int64_t)n0 * K), 0, rows_w * K * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t rsE = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(E + (int64_t)m0 * K), 0, rows_e * K * 2, kBufferFlags);
-  const int lrow = tid / kChunks;
-  const int lchunk = tid % kChunks;
-  const int voff = (lrow * K + lchunk * 8) * 2;
-  const int row_stride = (kThreads / kChunks) * K * 2;     // 32 rows, bytes
-  const int lds_off = swz(lrow, lchunk);                   // + i * 32 rows
-  uint4 rW[kLoads], rE[kLoads];
+  // Direct loads: row (4w + i) * 8 + p / 8 has (row & 7) = p / 8 and
+  // ((row >> 3) & 1) = i & 1, so lane p fetches logical chunk
+  // (p % 8) ^ (p / 8) ^ (i & 1) of its row.
+  const int dl_c0 = (lane & 7) ^ (lane >> 3);
+  const int dl_row = wave * 32 + (lane >> 3);
+  const int dl_v0 = (dl_row * K + dl_c0 * 8) * 2;
+  const int dl_v1 = (dl_row * K + (dl_c0 ^ 1) * 8) * 2;
+  const int rstride8 = 8 * K * 2;
+  // Fragment reads: lane l reads row (base + l % 32), K-chunk 2 kk + l / 32.
+  const int frow = lane & 31;
+  const int fk = lane >> 5;
+  const int fsw = (frow & 7) ^ ((frow >> 3) & 1);
+  const int a_base = (wn * 128 + frow) * BK;
+  const int b_base = (wm * 64 + frow) * BK;
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
   const int KT = K / BK;
-#pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    rW[i] = load16(rsW, voff, i * row_stride);
-    rE[i] = load16(rsE, voff, i * row_stride);
+
+#define ENGRAM_ISSUE(kt_, dW, dE)                                                             \
+  _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                           \
+    const int vo = (i & 1) ? dl_v1 : dl_v0;                                                 \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, ENGRAM_LDS((dW) + (wave * 4 + i) * 512),  \
+                                             16, vo, i * rstride8 + (kt_) * BK * 2, 0, 0);  \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsE, ENGRAM_LDS((dE) + (wave * 4 + i) * 512),  \
+                                             16, vo, i * rstride8 + (kt_) * BK * 2, 0, 0);  \
   }
-#pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    *reinterpret_cast<uint4 *>(sW + lds_off + i * 32 * BK) = rW[i];
-    *reinterpret_cast<uint4 *>(sE + lds_off + i * 32 * BK) = rE[i];
-  }
+#define ENGRAM_FRAGS(buf_w, buf_e, kk, dst_a, dst_b)                                          \
+  _Pragma("unroll") for (int i = 0; i < 4; ++i) dst_a[i] =                                  \
+      *reinterpret_cast<const bf16x8 *>((buf_w) + a_base + i * 32 * BK +                    \
+                                        ((((kk) * 2 + fk) ^ fsw) << 3));                     \
+  _Pragma("unroll") for (int j = 0; j < 2; ++j) dst_b[j] =                                  \
+      *reinterpret_cast<const bf16x8 *>((buf_e) + b_base + j * 32 * BK +                    \
+                                        ((((kk) * 2 + fk) ^ fsw) << 3));
+#define ENGRAM_MMA(A, B, I0, I1)                                                              \
+  _Pragma("unroll") for (int i = I0; i < I1; ++i)                                           \
+  _Pragma("unroll") for (int j = 0; j < 2; ++j)                                             \
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[i], B[j], acc[i][j], 0, 0, 0);
+// Per 16-byte fragment step: issue the 6 reads of the next step, then 8 MFMAs.
+#define ENGRAM_SCHED(id)                                                                      \
+  __builtin_amdgcn_sched_group_barrier(0x100, 6, id);                                       \
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, id);
+
+  ENGRAM_ISSUE(0, sW0, sE0);
   __syncthreads();
-
-  const int frow = lane & 31;       // row within a 32-row MFMA tile
-  const int fk = lane >> 5;         // which 8-wide K half of a 16-wide step
-
+  bf16x8 a0[4], b0[2], a1[4], b1[2];
+  ENGRAM_FRAGS(sW0, sE0, 0, a0, b0);
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
+    const bool odd = kt & 1;
+    const uint16_t *cW = odd ? sW1 : sW0;
+    const uint16_t *cE = odd ? sE1 : sE0;
+    uint16_t *nW = odd ? sW0 : sW1;
+    uint16_t *nE = odd ? sE0 : sE1;
+    // Stage kt+1 refills the buffer last read in step kt-1; every wave finished
+    // those reads before the previous barrier.
     if (kt + 1 < KT) {
-      const int koff = (kt + 1) * BK * 2;
-#pragma unroll
-      for (int i = 0; i < kLoads; ++i) {
-        rW[i] = load16(rsW, voff, koff + i * row_stride);
-        rE[i] = load16(rsE, voff, koff + i * row_stride);
-      }
+      ENGRAM_ISSUE(kt + 1, nW, nE);
     }
-    const uint16_t *cW = sW + cur * BN * BK;
-    const uint16_t *cE = sE + cur * BM * BK;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wn * 128 + i * 32 + frow;
-        a[i] = *reinterpret_cast<const bf16x8 *>(cW + swz(row, kk * 2 + fk));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = wm * 128 + j * 32 + frow;
-        b[j] = *reinterpret_cast<const bf16x8 *>(cE + swz(row, kk * 2 + fk));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < KT) {
-      uint16_t *nW = sW + (cur ^ 1) * BN * BK;
-      uint16_t *nE = sE + (cur ^ 1) * BM * BK;
-#pragma unroll
-      for (int i = 0; i < kLoads; ++i) {
-        *reinterpret_cast<uint4 *>(nW + lds_off + i * 32 * BK) = rW[i];
-        *reinterpret_cast<uint4 *>(nE + lds_off + i * 32 * BK) = rE[i];
-      }
-    }
+    ENGRAM_FRAGS(cW, cE, 1, a1, b1);
+    ENGRAM_MMA(a0, b0, 0, 4);
+    ENGRAM_SCHED(0);
+    ENGRAM_FRAGS(cW, cE, 2, a0, b0);
+    ENGRAM_MMA(a1, b1, 0, 4);
+    ENGRAM_SCHED(1);
+    ENGRAM_FRAGS(cW, cE, 3, a1, b1);
+    ENGRAM_MMA(a0, b0, 0, 4);
+    ENGRAM_SCHED(2);
+    ENGRAM_MMA(a1, b1, 0, 2);
+    // Stage kt+1 has landed in every wave's view, and every read of stage kt
+    // has completed, once all waves pass here.
     __syncthreads();
+    if (kt + 1 < KT) {
+      ENGRAM_FRAGS(nW, nE, 0, a0, b0);
+    }
+    ENGRAM_MMA(a1, b1, 2, 4);
   }
+#undef ENGRAM_ISSUE
+#undef ENGRAM_FRAGS
+#undef ENGRAM_MMA
+#undef ENGRAM_SCHED
 
   // ---- epilogue: accumulator r of tile (i, j) is output column
-  // n0 + wn*128 + i*32 + (r/4)*8 + (lane/32)*4 + r%4 of token m0 + wm*128 + j*32 + lane%32.
+  // n0 + wn*128 + i*32 + (r/4)*8 + (lane/32)*4 + r%4 of token m0 + wm*64 + j*32 + lane%32.
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int m = m0 + wm * 128 + j * 32 + frow;
+  for (int j = 0; j < 2; ++j) {
+    const int m = m0 + wm * 64 + j * 32 + frow;
     if (m >= M) continue;
     uint16_t *crow = C + (int64_t)m * N;
 #pragma unroll
