@@ -117,6 +117,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-step measurement on the 101 GB table")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -235,7 +237,74 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(gw)
+    if not args.no_decode:
+        del rows, e, kv, gates, ws
+        gw.free()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        out["decode"] = decode_bench(args.steps, args.warmup)
     print(json.dumps(out), flush=True)
+
+
+def decode_bench(steps: int, warmup: int):
+    """Decode step on the full-size table: 256 sequences x 1 new token with a
+    3-token history, 384,006,168 rows (101.4 GB) in HBM; engram_forward per step
+    with the history carried in place."""
+    import torch
+    import hashed_gram_conditional_amd as E
+    from workloads import C4
+    from workloads.harness import GpuWorkload
+
+    t0 = time.perf_counter()
+    gw = GpuWorkload(C4)
+    w = gw.w
+    ws, nws = gw.workspace()
+    gates = torch.empty((w.tokens, w.hc), dtype=torch.float32, device="cuda")
+    hist = gw.hist_in.clone()
+    torch.cuda.synchronize()
+    log(f"decode setup {time.perf_counter() - t0:.1f} s: table {gw.rows} rows")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        E.engram_forward(gw.params, gw.desc, gw.ids, hist, hist, gw.table, gw.wkv, gw.q_w,
+                         gw.k_w, gw.h, gates, ws, nws)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        E.engram_forward(gw.params, gw.desc, gw.ids, hist, hist, gw.table, gw.wkv, gw.q_w,
+                         gw.k_w, gw.h, gates, ws, nws)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[steps]) / steps
+    # per-stage breakdown through the stage entry points
+    T, S = w.tokens, w.segments
+    K_in, N_out = S * w.row_dim, (w.hc + 1) * w.dim
+    rows = torch.empty((T, S), dtype=torch.int64, device="cuda")
+    e = torch.empty((T, K_in), dtype=torch.bfloat16, device="cuda")
+    kv = torch.empty((T, N_out), dtype=torch.bfloat16, device="cuda")
+    se = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for i in range(steps):
+        se[i][0].record(stream)
+        E.engram_hash(gw.params, gw.ids, w.batch, w.seq, hist, None, rows)
+        se[i][1].record(stream)
+        E.engram_gather(gw.table, gw.rows, gw.row_format, w.row_dim, rows, T * S, e)
+        se[i][2].record(stream)
+        E.engram_project(e, gw.wkv, kv, T, K_in, N_out, 0)
+        se[i][3].record(stream)
+        E.engram_gate(gw.desc, gw.ids, w.raw_vocab, kv, gw.q_w, gw.k_w, gw.h, gates)
+        se[i][4].record(stream)
+    torch.cuda.synchronize()
+    st = np.mean([[x[j].elapsed_time(x[j + 1]) for j in range(4)] for x in se], axis=0)
+    wkv_bytes = N_out * K_in * 2
+    res = {"workload": "decode: 256 sequences x 1 token with a 3-token history, 24 segments of "
+                       "primes from 16,000,000 (384,006,168 x 264 B = 101.4 GB table), hc 4 x 5120",
+           "tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+           "stages_ms": {"hash": round(st[0], 4), "gather": round(st[1], 4),
+                         "project": round(st[2], 4), "gate": round(st[3], 4)},
+           "project_weight_stream": {"achieved": round(wkv_bytes / (st[2] * 1e-3) / 1e9, 1),
+                                     "peak": HBM_PEAK_GBPS, "unit": "GB/s"}}
+    gw.free()
+    return res
 
 
 if __name__ == "__main__":

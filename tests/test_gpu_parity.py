@@ -478,3 +478,43 @@ def test_forward_c4_decode_full_table():
     finally:
         gw.free()
         _cleanup()
+
+
+@pytest.mark.parametrize("hc,dim,f32", [(1, 8, False), (3, 136, False), (8, 8192, False),
+                                        (4, 5120, False), (2, 64, True), (8, 1032, True)])
+def test_gate_shapes(hc, dim, f32):
+    """The gate alone, on the device's inputs, against the oracle's gate."""
+    rng = np.random.default_rng(hc * 1000 + dim)
+    T = 37
+    raw = rng.integers(0, 100, T).astype(np.int32)
+    raw[[3, 20]] = -1
+    raw[30] = 100                                   # >= raw_vocab: DEAD
+    q_w = (1 + 0.1 * rng.standard_normal((hc, dim))).astype(np.float32)
+    k_w = (1 + 0.1 * rng.standard_normal((hc, dim))).astype(np.float32)
+    h = rng.standard_normal((T, hc, dim)).astype(np.float32)
+    kv = (50 * rng.standard_normal((T, hc + 1, dim))).astype(np.float32)
+    kv[5, 0] = h[5, 0] * 3.0                        # a parallel key: gate near 1
+    kv[6, 0] = -h[6, 0]                             # an opposite key: gate near 0
+    if not f32:
+        h = O.bf16_bits_to_f64(gen.f32_to_bf16_bits(h)).astype(np.float32)
+        kv = O.bf16_bits_to_f64(gen.f32_to_bf16_bits(kv)).astype(np.float32)
+        h_dev = to_device(gen.f32_to_bf16_bits(h))
+        kv_dev = to_device(gen.f32_to_bf16_bits(kv))
+    else:
+        h_dev, kv_dev = to_device(h), to_device(kv)
+    fmt = E.ROW_F32 if f32 else E.ROW_E4M3_E8M0_264
+    d = E.forward_desc(1, T, hc, dim, 0, fmt, 32 if f32 else 256, 1e-6, 0.0)
+    gates = torch.full((T, hc), -1.0, dtype=torch.float32, device=DEV)
+    E.engram_gate(d, to_device(raw.reshape(1, T)), 100, kv_dev, to_device(q_w), to_device(k_w),
+                  h_dev, gates)
+    torch.cuda.synchronize()
+    dead = (raw < 0) | (raw >= 100)
+    a, h_out = O.gate(h.astype(np.float64), kv[:, :hc].astype(np.float64),
+                      kv[:, hc].astype(np.float64), q_w, k_w, dead, 1e-6, 0.0)
+    assert_close(gates.cpu().numpy(), a, f"gates hc={hc} d={dim}")
+    # parallel / opposite key: |s| close to sqrt(d), so alpha near sigmoid(+-d^(1/4))
+    lim = 1.0 / (1.0 + np.exp(-0.8 * dim ** 0.25))
+    assert a[5, 0] > lim and a[6, 0] < 1.0 - lim
+    got = (h_dev.cpu().numpy() if f32 else O.bf16_bits_to_f64(bf16_bits(h_dev)))
+    assert_close(got.reshape(h_out.shape), h_out, f"h hc={hc} d={dim}")
+    assert np.array_equal(got.reshape(h_out.shape)[dead], h[dead])
