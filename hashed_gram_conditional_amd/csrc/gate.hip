@@ -10,7 +10,8 @@
 // reciprocal roots of the mean squares, the update rounded to bf16 once) and
 // "布局与哈希探测" item 4 (masked rows are left untouched).
 //
-// One block of 128 threads per token. Each thread owns CPT chunks of 8
+// One block per token: 128 threads when there are enough tokens to fill the
+// chip, 512 when there are few (decode). Each thread owns CPT chunks of 8
 // elements per stream (16-byte bf16 accesses). The three reductions per stream
 // (sum h^2, sum k^2, sum h q_w k_w k) run first; the update then reads the
 // token's h again, which the L2 still holds (40 KiB per token), instead of
@@ -19,7 +20,7 @@
 
 namespace {
 
-constexpr int kThreads = 128;
+constexpr int kMaxThreads = 512;
 constexpr int kMaxHc = 8;
 constexpr int kChunk = 8;        // elements per chunk
 
@@ -63,13 +64,14 @@ struct Chunk<true> {    // 8 fp32
 };
 
 template <bool F32, int CPT>
-__global__ __launch_bounds__(kThreads) void gate_kernel(
+__global__ __launch_bounds__(kMaxThreads) void gate_kernel(
     const int32_t *__restrict__ ids, int32_t raw_vocab, const void *__restrict__ kv,
     const float *__restrict__ q_w, const float *__restrict__ k_w, void *__restrict__ h,
     float *__restrict__ gate_out, int hc, int dim, float eps, float clamp) {
-  __shared__ float red[kThreads / engram::kWave][3 * kMaxHc];
+  __shared__ float red[kMaxThreads / engram::kWave][3 * kMaxHc];
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x;
+  const int nthreads = blockDim.x;
   const int32_t x = ids[t];
   if (x < 0 || x >= raw_vocab) {          // DEAD: gate 0, streams untouched
     if (gate_out != nullptr && tid < hc) gate_out[t * hc + tid] = 0.f;
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(
   Chunk<F32> vv[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
-    const int ci = tid + c * kThreads;
+    const int ci = tid + c * nthreads;
     if (ci < cps) vv[c].load(kv, kv_row + (int64_t)hc * cps + ci);
   }
   float shh[kMaxHc], skk[kMaxHc], shk[kMaxHc];
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(
     if (m < hc) {
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
-        const int ci = tid + c * kThreads;
+        const int ci = tid + c * nthreads;
         if (ci < cps) {
           Chunk<F32> hc_, kc;
           hc_.load(h, h_row + (int64_t)m * cps + ci);
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(
     if (m < hc) {
       float a = 0.f, b = 0.f, c = 0.f;
 #pragma unroll
-      for (int w = 0; w < kThreads / engram::kWave; ++w) {
+      for (int w = 0; w < (nthreads >> 6); ++w) {
         a += red[w][3 * m + 0];
         b += red[w][3 * m + 1];
         c += red[w][3 * m + 2];
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(
     if (m < hc) {
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
-        const int ci = tid + c * kThreads;
+        const int ci = tid + c * nthreads;
         if (ci < cps) {
           Chunk<F32> hc_;
           hc_.load(h, h_row + (int64_t)m * cps + ci);
@@ -178,13 +180,13 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(
 }
 
 template <bool F32>
-hipError_t launch(int cpt, const int32_t *ids, int32_t raw_vocab, const void *kv,
+hipError_t launch(int cpt, int threads, const int32_t *ids, int32_t raw_vocab, const void *kv,
                   const float *q_w, const float *k_w, void *h, float *gate_out,
                   int64_t tokens, int hc, int dim, float eps, float clamp,
                   hipStream_t stream) {
 #define ENGRAM_GATE_CASE(N)                                                                 \
   case N:                                                                                   \
-    hipLaunchKernelGGL((gate_kernel<F32, N>), dim3((unsigned)tokens), dim3(kThreads), 0,    \
+    hipLaunchKernelGGL((gate_kernel<F32, N>), dim3((unsigned)tokens), dim3(threads), 0,     \
                        stream, ids, raw_vocab, kv, q_w, k_w, h, gate_out, hc, dim, eps,     \
                        clamp);                                                              \
     break;
@@ -211,10 +213,19 @@ hipError_t engram_launch_gate(bool f32, const int32_t *ids, int32_t raw_vocab, c
                               int64_t tokens, int32_t hc, int32_t dim, float eps, float clamp,
                               hipStream_t stream) {
   if (tokens <= 0) return hipSuccess;
+  int dev = 0, cus = 256;
+  hipError_t err = hipGetDevice(&dev);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
   const int cps = dim / kChunk;
-  const int cpt = (cps + kThreads - 1) / kThreads;
-  return f32 ? launch<true>(cpt, ids, raw_vocab, kv, q_w, k_w, h, gate_out, tokens, hc, dim,
-                            eps, clamp, stream)
-             : launch<false>(cpt, ids, raw_vocab, kv, q_w, k_w, h, gate_out, tokens, hc, dim,
-                             eps, clamp, stream);
+  // 128-thread blocks need about 8 tokens per CU to keep HBM busy; below that,
+  // spread each token over more lanes.
+  int threads = tokens >= 8 * (int64_t)cus ? 128 : kMaxThreads;
+  const int needed = ((cps + engram::kWave - 1) / engram::kWave) * engram::kWave;
+  if (threads > needed) threads = needed;
+  const int cpt = (cps + threads - 1) / threads;
+  return f32 ? launch<true>(cpt, threads, ids, raw_vocab, kv, q_w, k_w, h, gate_out, tokens, hc,
+                            dim, eps, clamp, stream)
+             : launch<false>(cpt, threads, ids, raw_vocab, kv, q_w, k_w, h, gate_out, tokens, hc,
+                             dim, eps, clamp, stream);
 }

@@ -6,16 +6,19 @@
 // weight is stored with the 6144 inputs innermost).
 //
 // bf16 path: C[m, n] = sum_k E[m, k] W[n, k]; both operands are K-contiguous.
-// One block of 8 waves (2 per SIMD) computes a 256 (n) x 256 (m) tile; wave w
-// owns a 128 (n) x 64 (m) quarter-strip as 4 x 2 v_mfma_f32_32x32x16_bf16 tiles
-// with fp32 accumulators. W rows feed the MFMA's first operand and E rows the
+// One block of 8 waves (2 per SIMD) computes a TN (n) x 256 (m) tile, TN = 256
+// or 128; wave w owns a TN/2 (n) x 64 (m) strip as (TN/64) x 2
+// v_mfma_f32_32x32x16_bf16 tiles with fp32 accumulators. TN = 128 is used when
+// 256-wide tiles would leave CUs idle (small token counts: decode), which
+// doubles the tile count without splitting K, so the results are the same bits. W rows feed the MFMA's first operand and E rows the
 // second, so each lane's accumulator holds 4 consecutive output columns of one
 // token and the epilogue writes 8-byte bf16 quads.
 //
-// K advances in steps of 64 through two 64 KiB LDS stages. Operand tiles move
-// global -> LDS by direct buffer loads (no VGPR staging): instruction i of wave
-// w fills 1 KiB = 8 rows of 128 bytes, lane p landing in row (4w + i) * 8 +
-// p / 8, 16-byte slot p % 8. Chunk c of row r is stored in slot
+// K advances in steps of 64 through two LDS stages (2 x 64 KiB at TN = 256).
+// Operand tiles move global -> LDS by direct buffer loads (no VGPR staging):
+// instruction i of wave w fills 1 KiB = 8 rows of 128 bytes, lane p landing in
+// row (R w + i) * 8 + p / 8 (R = rows / 64 instructions per wave), 16-byte slot
+// p % 8. Chunk c of row r is stored in slot
 // c ^ (r & 7) ^ ((r >> 3) & 1), so the 16-byte fragment reads of any 16
 // consecutive rows touch 16 distinct 16-byte bank groups (and any 8 rows 8),
 // which keeps the reads free of bank conflicts. The loads of step k+1 fly while
@@ -36,7 +39,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 #define ENGRAM_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
 constexpr int BM = 256;       // tokens per tile
-constexpr int BN = 256;       // output columns per tile
 constexpr int BK = 64;        // K per stage
 constexpr int kThreads = 512;
 constexpr int kGroupM = 8;
@@ -44,9 +46,12 @@ constexpr int kXcds = 8;
 // Buffer resource word 3 for gfx9-family raw buffers (no format, no swizzle).
 constexpr int kBufferFlags = 0x00020000;
 
+template <int BN>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
     const uint16_t *__restrict__ E, const uint16_t *__restrict__ W, uint16_t *__restrict__ C,
     int M, int N, int K, int tiles_m, int tiles_n) {
+  constexpr int TI = BN / 64;          // 32-row MFMA tiles per wave along n
+  constexpr int WR = BN / 64;          // W-panel direct loads per wave per stage
   __shared__ __align__(1024) uint16_t sW0[BN * BK];
   __shared__ __align__(1024) uint16_t sW1[BN * BK];
   __shared__ __align__(1024) uint16_t sE0[BM * BK];
@@ -67,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // 0..7
-  const int wn = wave >> 2;        // which 128 output columns
+  const int wn = wave >> 2;        // which BN/2 output columns
   const int wm = wave & 3;         // which 64 tokens
 
   const int rows_w = min(BN, N - n0);
@@ -76,24 +81,27 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
       const_cast<uint16_t *>(W + (int64_t)n0 * K), 0, rows_w * K * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t rsE = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(E + (int64_t)m0 * K), 0, rows_e * K * 2, kBufferFlags);
-  // Direct loads: row (4w + i) * 8 + p / 8 has (row & 7) = p / 8 and
-  // ((row >> 3) & 1) = i & 1, so lane p fetches logical chunk
+  // Direct loads: row (R w + i) * 8 + p / 8 has (row & 7) = p / 8 and, R being
+  // even, ((row >> 3) & 1) = i & 1, so lane p fetches logical chunk
   // (p % 8) ^ (p / 8) ^ (i & 1) of its row.
   const int dl_c0 = (lane & 7) ^ (lane >> 3);
-  const int dl_row = wave * 32 + (lane >> 3);
-  const int dl_v0 = (dl_row * K + dl_c0 * 8) * 2;
-  const int dl_v1 = (dl_row * K + (dl_c0 ^ 1) * 8) * 2;
+  const int dl_rw = wave * WR * 8 + (lane >> 3);
+  const int dl_re = wave * 32 + (lane >> 3);
+  const int dl_w0 = (dl_rw * K + dl_c0 * 8) * 2;
+  const int dl_w1 = (dl_rw * K + (dl_c0 ^ 1) * 8) * 2;
+  const int dl_e0 = (dl_re * K + dl_c0 * 8) * 2;
+  const int dl_e1 = (dl_re * K + (dl_c0 ^ 1) * 8) * 2;
   const int rstride8 = 8 * K * 2;
   // Fragment reads: lane l reads row (base + l % 32), K-chunk 2 kk + l / 32.
   const int frow = lane & 31;
   const int fk = lane >> 5;
   const int fsw = (frow & 7) ^ ((frow >> 3) & 1);
-  const int a_base = (wn * 128 + frow) * BK;
+  const int a_base = (wn * (BN / 2) + frow) * BK;
   const int b_base = (wm * 64 + frow) * BK;
 
-  f32x16 acc[4][2];
+  f32x16 acc[TI][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -101,15 +109,18 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
   const int KT = K / BK;
 
 #define ENGRAM_ISSUE(kt_, dW, dE)                                                             \
+  _Pragma("unroll") for (int i = 0; i < WR; ++i) {                                          \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, ENGRAM_LDS((dW) + (wave * WR + i) * 512), \
+                                             16, (i & 1) ? dl_w1 : dl_w0,                   \
+                                             i * rstride8 + (kt_) * BK * 2, 0, 0);          \
+  }                                                                                         \
   _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                           \
-    const int vo = (i & 1) ? dl_v1 : dl_v0;                                                 \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, ENGRAM_LDS((dW) + (wave * 4 + i) * 512),  \
-                                             16, vo, i * rstride8 + (kt_) * BK * 2, 0, 0);  \
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsE, ENGRAM_LDS((dE) + (wave * 4 + i) * 512),  \
-                                             16, vo, i * rstride8 + (kt_) * BK * 2, 0, 0);  \
+                                             16, (i & 1) ? dl_e1 : dl_e0,                   \
+                                             i * rstride8 + (kt_) * BK * 2, 0, 0);          \
   }
 #define ENGRAM_FRAGS(buf_w, buf_e, kk, dst_a, dst_b)                                          \
-  _Pragma("unroll") for (int i = 0; i < 4; ++i) dst_a[i] =                                  \
+  _Pragma("unroll") for (int i = 0; i < TI; ++i) dst_a[i] =                                 \
       *reinterpret_cast<const bf16x8 *>((buf_w) + a_base + i * 32 * BK +                    \
                                         ((((kk) * 2 + fk) ^ fsw) << 3));                     \
   _Pragma("unroll") for (int j = 0; j < 2; ++j) dst_b[j] =                                  \
@@ -119,14 +130,15 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
   _Pragma("unroll") for (int i = I0; i < I1; ++i)                                           \
   _Pragma("unroll") for (int j = 0; j < 2; ++j)                                             \
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[i], B[j], acc[i][j], 0, 0, 0);
-// Per 16-byte fragment step: issue the 6 reads of the next step, then 8 MFMAs.
+// Per 16-byte fragment step: issue the TI + 2 reads of the next step, then the
+// 2 TI MFMAs.
 #define ENGRAM_SCHED(id)                                                                      \
-  __builtin_amdgcn_sched_group_barrier(0x100, 6, id);                                       \
-  __builtin_amdgcn_sched_group_barrier(0x008, 8, id);
+  __builtin_amdgcn_sched_group_barrier(0x100, TI + 2, id);                                  \
+  __builtin_amdgcn_sched_group_barrier(0x008, 2 * TI, id);
 
   ENGRAM_ISSUE(0, sW0, sE0);
   __syncthreads();
-  bf16x8 a0[4], b0[2], a1[4], b1[2];
+  bf16x8 a0[TI], b0[2], a1[TI], b1[2];
   ENGRAM_FRAGS(sW0, sE0, 0, a0, b0);
   for (int kt = 0; kt < KT; ++kt) {
     const bool odd = kt & 1;
@@ -140,22 +152,22 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
       ENGRAM_ISSUE(kt + 1, nW, nE);
     }
     ENGRAM_FRAGS(cW, cE, 1, a1, b1);
-    ENGRAM_MMA(a0, b0, 0, 4);
+    ENGRAM_MMA(a0, b0, 0, TI);
     ENGRAM_SCHED(0);
     ENGRAM_FRAGS(cW, cE, 2, a0, b0);
-    ENGRAM_MMA(a1, b1, 0, 4);
+    ENGRAM_MMA(a1, b1, 0, TI);
     ENGRAM_SCHED(1);
     ENGRAM_FRAGS(cW, cE, 3, a1, b1);
-    ENGRAM_MMA(a0, b0, 0, 4);
+    ENGRAM_MMA(a0, b0, 0, TI);
     ENGRAM_SCHED(2);
-    ENGRAM_MMA(a1, b1, 0, 2);
+    ENGRAM_MMA(a1, b1, 0, TI / 2);
     // Stage kt+1 has landed in every wave's view, and every read of stage kt
     // has completed, once all waves pass here.
     __syncthreads();
     if (kt + 1 < KT) {
       ENGRAM_FRAGS(nW, nE, 0, a0, b0);
     }
-    ENGRAM_MMA(a1, b1, 2, 4);
+    ENGRAM_MMA(a1, b1, TI / 2, TI);
   }
 #undef ENGRAM_ISSUE
 #undef ENGRAM_FRAGS
@@ -163,17 +175,17 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
 #undef ENGRAM_SCHED
 
   // ---- epilogue: accumulator r of tile (i, j) is output column
-  // n0 + wn*128 + i*32 + (r/4)*8 + (lane/32)*4 + r%4 of token m0 + wm*64 + j*32 + lane%32.
+  // n0 + wn*BN/2 + i*32 + (r/4)*8 + (lane/32)*4 + r%4 of token m0 + wm*64 + j*32 + lane%32.
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int m = m0 + wm * 64 + j * 32 + frow;
     if (m >= M) continue;
     uint16_t *crow = C + (int64_t)m * N;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < TI; ++i) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * 128 + i * 32 + g * 8 + fk * 4;
+        const int n = n0 + wn * (BN / 2) + i * 32 + g * 8 + fk * 4;
         if (n < N) {
           uint2 v;
           v.x = engram::pack_bf16x2(acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1]);
@@ -206,10 +218,22 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *__restrict__
 hipError_t engram_launch_gemm_bf16(const uint16_t *e, const uint16_t *w, uint16_t *kv,
                                    int64_t m, int64_t n, int64_t k, hipStream_t stream) {
   if (m <= 0 || n <= 0) return hipSuccess;
+  int dev = 0, cus = 256;
+  hipError_t err = hipGetDevice(&dev);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
   const int tiles_m = (int)((m + BM - 1) / BM);
-  const int tiles_n = (int)((n + BN - 1) / BN);
-  hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads),
-                     0, stream, e, w, kv, (int)m, (int)n, (int)k, tiles_m, tiles_n);
+  const int tiles_n256 = (int)((n + 255) / 256);
+  if ((int64_t)tiles_m * tiles_n256 >= cus) {
+    hipLaunchKernelGGL(gemm_bf16_kernel<256>, dim3((unsigned)(tiles_m * tiles_n256)),
+                       dim3(kThreads), 0, stream, e, w, kv, (int)m, (int)n, (int)k, tiles_m,
+                       tiles_n256);
+  } else {
+    const int tiles_n128 = (int)((n + 127) / 128);
+    hipLaunchKernelGGL(gemm_bf16_kernel<128>, dim3((unsigned)(tiles_m * tiles_n128)),
+                       dim3(kThreads), 0, stream, e, w, kv, (int)m, (int)n, (int)k, tiles_m,
+                       tiles_n128);
+  }
   return hipGetLastError();
 }
 

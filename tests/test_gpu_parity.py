@@ -230,8 +230,11 @@ def test_gather_c2_full_size_sampled():
 # projection
 # ---------------------------------------------------------------------------
 
+# Fewer than one 256 x 256 tile per CU selects 128-wide tiles; the last two
+# shapes (>= 256 tiles of 256 x 256) take the 256-wide path, with ragged edges.
 @pytest.mark.parametrize("M,N,K", [(1, 8, 64), (31, 264, 192), (257, 520, 1024),
-                                   (300, 408, 6144), (600, 256, 128), (513, 1032, 256)])
+                                   (300, 408, 6144), (600, 256, 128), (513, 1032, 256),
+                                   (4100, 4008, 128), (2304, 7176, 64)])
 def test_project_bf16_shapes(M, N, K):
     rng = np.random.default_rng(M * 7 + N)
     e = gen.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32) * 3)
