@@ -25,7 +25,10 @@ OK, EINVAL, EVOCAB, EMULT, ESHAPE, EWORKSPACE, EHIP, EPRIMES = 0, -1, -2, -3, -4
 class EngramError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
-        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        msg = f"{where}: {status_string(status)} (status {status})"
+        if status == EHIP:
+            msg += f": {LIB.engram_last_hip_error().decode()}"
+        super().__init__(msg)
 
 
 class HashParams(ctypes.Structure):
@@ -61,10 +64,21 @@ def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is not built; run __graft_entry__.build() "
                           "(python hashed_gram_conditional_amd/build.py)")
+    # The library needs libamdhip64.so.7. torch ships its own HIP runtime under
+    # that soname and loads it by another name; if the library were loaded
+    # first, the process would end up with two HIP runtimes and the library's
+    # would see no device. Importing torch first makes the dynamic linker bind
+    # the library to torch's runtime, the one that owns the device memory and
+    # streams the library is handed.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(_LIB_PATH)
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     sig = {
         "engram_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "engram_last_hip_error": (ctypes.c_char_p, []),
         "engram_sizeof_hash_params": (SZ, []),
         "engram_sizeof_forward_desc": (SZ, []),
         "engram_make_primes": (ctypes.c_int, [I64, I32, P, P, P]),

@@ -123,7 +123,14 @@ int check_desc(const engram_forward_desc *d) {
   return ENGRAM_OK;
 }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP; }
+// The last HIP error an entry point returned ENGRAM_EHIP for, per host thread.
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return ENGRAM_OK;
+  g_last_hip_error = e;
+  return ENGRAM_EHIP;
+}
 
 }  // namespace
 
@@ -142,6 +149,8 @@ const char *engram_status_string(int status) {
     default: return "unknown status";
   }
 }
+
+const char *engram_last_hip_error(void) { return hipGetErrorString(g_last_hip_error); }
 
 size_t engram_sizeof_hash_params(void) { return sizeof(engram_hash_params); }
 
@@ -323,12 +332,12 @@ int engram_forward(const engram_hash_params *params, const engram_forward_desc *
                                        row_ids, ntok * S, (float *)e, stream)
             : engram_launch_gather_e4m3((const uint8_t *)table, desc->table_rows, row_ids,
                                         ntok * S, (uint16_t *)e, stream);
-  if (err != hipSuccess) return ENGRAM_EHIP;
+  if (err != hipSuccess) return hip_status(err);
   err = f32 ? engram_launch_gemm_f32((const float *)e, (const float *)wkv, (float *)kv, ntok,
                                      out_dim, in_dim, stream)
             : engram_launch_gemm_bf16((const uint16_t *)e, (const uint16_t *)wkv,
                                       (uint16_t *)kv, ntok, out_dim, in_dim, stream);
-  if (err != hipSuccess) return ENGRAM_EHIP;
+  if (err != hipSuccess) return hip_status(err);
   err = engram_launch_gate(f32, ids, params->raw_vocab, kv, q_w, k_w, h, gate_out, ntok,
                            desc->hc, desc->dim, desc->eps, desc->gate_clamp, stream);
   return hip_status(err);

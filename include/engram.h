@@ -25,13 +25,14 @@
  *
  * Conventions for every entry point:
  *   - Pointers are device memory unless marked [host]. The caller owns every
- *     buffer; the library allocates nothing, keeps no state between calls and
- *     never synchronises: work is enqueued on `stream` (0 = null stream) and
+ *     buffer; the library allocates nothing, keeps no state between calls
+ *     (beyond a per-thread record of the last HIP error) and never
+ *     synchronises: work is enqueued on `stream` (0 = null stream) and
  *     completes asynchronously.
  *   - All arrays are dense row-major. Device pointers must be 16-byte aligned.
  *   - Arguments are validated on the host before any launch; a failed check
  *     returns a negative engram_status and enqueues nothing. A failed launch
- *     returns ENGRAM_EHIP.
+ *     returns ENGRAM_EHIP; engram_last_hip_error names the HIP error behind it.
  *   - Device data cannot be validated synchronously, so it follows conventions:
  *     a raw id outside [0, V) (the DEAD marker -1 included), or one the token
  *     map sends outside [0, V'), is a DEAD cell; a history entry outside
@@ -113,6 +114,11 @@ typedef struct engram_forward_desc {
 
 /* Message for a status code (static storage). */
 const char *engram_status_string(int status);
+
+/* hipGetErrorString of the HIP error behind the last ENGRAM_EHIP an entry
+ * point returned on the calling host thread ("no error" if none). This record
+ * is the library's only state; it is per thread and never cleared. */
+const char *engram_last_hip_error(void);
 
 /* sizeof the two structs as this library was built, for bindings to check. */
 size_t engram_sizeof_hash_params(void);

@@ -150,3 +150,18 @@ def test_forward_validation_and_workspace_size():
     assert L.engram_forward(ctypes.byref(p), ctypes.byref(small), *args, 0x10000, n,
                             None) == E.EPRIMES
     assert E.status_string(E.EPRIMES).startswith("bad primes")
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    # torch carries its own HIP runtime; the library must bind to that one even
+    # when it is imported first, or the process holds two runtimes and the
+    # library's sees no device.
+    import subprocess
+    import sys
+    code = ("import hashed_gram_conditional_amd, torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1"
