@@ -220,10 +220,10 @@ def main():
                                "6144 -> 5 x 5120, hc 4 x 5120",
                    "batch": w.batch, "seq": w.seq, "segments": S, "hc": w.hc, "dim": w.dim,
                    "table_rows": gw.rows},
-        "roofline": {"bound": "mfma", "kernel": "gemm_bf16_kernel<256> (engram_project)",
+        "roofline": {"bound": "mfma", "kernel": "gemm_bf16_kernel (engram_project)",
                      "achieved": round(gemm_tflops, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic("gemm_bf16_kernel<256>",
+                     "traffic": measured_traffic("gemm_bf16_kernel",
                                                  "hashed_gram_conditional_amd/csrc/gemm.hip"),
                      "algorithmic_flop": flops},
         "gather": {"kernel": "gather_e4m3_kernel (engram_gather)",

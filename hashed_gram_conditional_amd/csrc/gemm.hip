@@ -5,31 +5,41 @@
 // compute per "196B 参数怎么存、怎么取"); "ds4.c 学习笔记 · Engram", "消费" (the
 // weight is stored with the 6144 inputs innermost).
 //
-// bf16 path: C[m, n] = sum_k E[m, k] W[n, k]; both operands are K-contiguous.
-// One block of 8 waves (2 per SIMD) computes a TN (n) x 256 (m) tile, TN = 256
-// or 128; wave w owns a TN/2 (n) x 64 (m) strip as (TN/64) x 2
-// v_mfma_f32_32x32x16_bf16 tiles with fp32 accumulators. TN = 128 is used when
-// 256-wide tiles would leave CUs idle (small token counts: decode), which
-// doubles the tile count without splitting K, so the results are the same bits. W rows feed the MFMA's first operand and E rows the
-// second, so each lane's accumulator holds 4 consecutive output columns of one
-// token and the epilogue writes 8-byte bf16 quads.
+// bf16 path: C[m, n] = sum_k E[m, k] W[n, k]; both operands are K-contiguous,
+// fp32 accumulation in v_mfma_f32_32x32x16_bf16, one bf16 rounding at the end.
+// W rows feed the MFMA's first operand and E rows the second, so each lane's
+// accumulator holds 4 consecutive output columns of one token and the epilogue
+// writes 8-byte bf16 quads. K advances in steps of 64 through two LDS stages.
+// In LDS, 16-byte chunk c of a 128-byte row r sits in slot
+// c ^ (r & 7) ^ ((r >> 3) & 1): the fragment reads of any 16 consecutive rows
+// (one b128 read phase) then touch 16 distinct bank groups, and so do the
+// stores of two consecutive rows.
 //
-// K advances in steps of 64 through two LDS stages (2 x 64 KiB at TN = 256).
-// Operand tiles move global -> LDS by direct buffer loads (no VGPR staging):
-// instruction i of wave w fills 1 KiB = 8 rows of 128 bytes, lane p landing in
-// row (R w + i) * 8 + p / 8 (R = rows / 64 instructions per wave), 16-byte slot
-// p % 8. Chunk c of row r is stored in slot
-// c ^ (r & 7) ^ ((r >> 3) & 1), so the 16-byte fragment reads of any 16
-// consecutive rows touch 16 distinct 16-byte bank groups (and any 8 rows 8),
-// which keeps the reads free of bank conflicts. The loads of step k+1 fly while
-// step k's MFMAs run. One barrier per step sits before the last MFMAs of the
-// step, so the first fragments of step k+1 are read while those MFMAs drain.
-// Buffer loads past the operand panel's last valid row return zeros, which
-// covers the M and N edges.
+// Two kernels, both over 256-token tiles:
 //
-// Blocks are renumbered so that the blocks the hardware places on one XCD (it
-// deals block ids round-robin over 8 XCDs) form one contiguous range, and tiles
-// are walked in groups of 8 token-tiles sharing weight tiles, for L2 reuse.
+// gemm_bf16_kernel (256 x 256 tiles, enough tiles to fill the chip). 4 waves,
+// one per SIMD, each owning a 128 x 128 block of outputs (16 MFMA tiles, 256
+// accumulator registers). Operands move global -> VGPR -> LDS: the loads of
+// step k+2 are issued during step k, and the LDS stores of step k+1 happen
+// during step k, so every load has one full step to arrive. Both are spread
+// evenly over the step's four 16-deep sub-steps (4 loads and 4 stores among
+// 16 MFMAs each); issuing a step's 64 KiB of loads in one burst stalls MFMA
+// issue while every CU's requests queue in L2 at the same moment. Each
+// sub-step first reads the next sub-step's fragments, so their LDS latency is
+// hidden behind 16 MFMAs. One barrier per step (LDS counter only; the loads in
+// flight stay in flight) sits before the step's last 8 MFMAs.
+//
+// gemm_bf16_narrow_kernel (128 x 256 tiles, used when 256-wide tiles would
+// leave CUs idle: small token counts, decode). 8 waves (2 per SIMD), each a
+// 64 x 64 block; operand tiles go global -> LDS by direct buffer loads one
+// step ahead, with one barrier per step. Halving the tile width doubles the
+// tile count without splitting K, so both kernels give the same bits.
+//
+// Buffer loads past an operand panel's last valid row return zeros, which
+// covers the M and N edges. Blocks are renumbered so that the blocks the
+// hardware places on one XCD (it deals block ids round-robin over 8 XCDs) form
+// one contiguous range, and tiles are walked in groups of 8 token-tiles
+// sharing weight tiles, for L2 reuse.
 #include "common.h"
 
 namespace {
@@ -40,24 +50,16 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 256;       // tokens per tile
 constexpr int BK = 64;        // K per stage
-constexpr int kThreads = 512;
+constexpr int kWideThreads = 256;
+constexpr int kNarrowThreads = 512;
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
 // Buffer resource word 3 for gfx9-family raw buffers (no format, no swizzle).
 constexpr int kBufferFlags = 0x00020000;
 
-template <int BN>
-__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
-    const uint16_t *__restrict__ E, const uint16_t *__restrict__ W, uint16_t *__restrict__ C,
-    int M, int N, int K, int tiles_m, int tiles_n) {
-  constexpr int TI = BN / 64;          // 32-row MFMA tiles per wave along n
-  constexpr int WR = BN / 64;          // W-panel direct loads per wave per stage
-  __shared__ __align__(1024) uint16_t sW0[BN * BK];
-  __shared__ __align__(1024) uint16_t sW1[BN * BK];
-  __shared__ __align__(1024) uint16_t sE0[BM * BK];
-  __shared__ __align__(1024) uint16_t sE1[BM * BK];
-
-  // ---- tile assignment ----
+// Tile origin of this block: block ids are renumbered so that each XCD's
+// blocks are contiguous, then walked in groups of kGroupM token-tiles.
+__device__ __forceinline__ void tile_origin(int tiles_m, int tiles_n, int bn, int &m0, int &n0) {
   const int nblocks = tiles_m * tiles_n;
   int bid = blockIdx.x;
   const int full = (nblocks / kXcds) * kXcds;
@@ -67,8 +69,201 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
   const int first_m = group * kGroupM;
   const int gsize = min(tiles_m - first_m, kGroupM);
   const int local = bid - group * in_group;
-  const int m0 = (first_m + local % gsize) * BM;
-  const int n0 = (local / gsize) * BN;
+  m0 = (first_m + local % gsize) * BM;
+  n0 = (local / gsize) * bn;
+}
+
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
+  return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+}
+
+__global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_bf16_kernel(const uint16_t *__restrict__ E, const uint16_t *__restrict__ W,
+                      uint16_t *__restrict__ C, int M, int N, int K, int tiles_m, int tiles_n) {
+  constexpr int BN = 256;
+  __shared__ __align__(1024) uint16_t sW[2][BN * BK];
+  __shared__ __align__(1024) uint16_t sE[2][BM * BK];
+  int m0, n0;
+  tile_origin(tiles_m, tiles_n, BN, m0, n0);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // 0..3
+  const int wn = wave >> 1;        // which 128 output columns
+  const int wm = wave & 1;         // which 128 tokens
+
+  const int rows_w = min(BN, N - n0);
+  const int rows_e = min(BM, M - m0);
+  const __amdgpu_buffer_rsrc_t rsW = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(W + (int64_t)n0 * K), 0, rows_w * K * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rsE = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(E + (int64_t)m0 * K), 0, rows_e * K * 2, kBufferFlags);
+  // A step's operands are 16 chunks of 16 bytes per thread: chunk i < 8 is W
+  // row i*32 + t/8, chunk i >= 8 is E row (i-8)*32 + t/8, 16-byte column t%8 of
+  // the step's 128-byte K slice. Its LDS slot follows the swizzle; since i*32
+  // is a multiple of 16, the slot depends on t only.
+  const int g_row = tid >> 3;
+  const int g_chunk = tid & 7;
+  const int g_voff = (g_row * K + g_chunk * 8) * 2;
+  const int g_rstride = 32 * K * 2;
+  const int s_off = g_row * BK + ((g_chunk ^ (g_row & 7) ^ ((g_row >> 3) & 1)) << 3);
+  // Fragment reads: lane l reads row (base + l % 32), K-chunk 2 kk + l / 32.
+  const int frow = lane & 31;
+  const int fk = lane >> 5;
+  const int fsw = (frow & 7) ^ ((frow >> 3) & 1);
+  const int a_base = (wn * 128 + frow) * BK;
+  const int b_base = (wm * 128 + frow) * BK;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  const int KT = K / BK;
+  uint4 g0[16], g1[16];
+
+// Quarter q of a step's chunks: loads, then LDS stores.
+#define ENGRAM_LOADQ(g, kt_, q)                                                               \
+  _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                           \
+    if ((q) < 2)                                                                            \
+      g[(q) * 4 + i] = load16(rsW, g_voff, ((q) * 4 + i) * g_rstride + (kt_) * BK * 2);     \
+    else                                                                                    \
+      g[(q) * 4 + i] = load16(rsE, g_voff, ((q) * 4 + i - 8) * g_rstride + (kt_) * BK * 2); \
+  }
+#define ENGRAM_STOREQ(g, st, q)                                                               \
+  _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                           \
+    if ((q) < 2)                                                                            \
+      *reinterpret_cast<uint4 *>(&sW[st][s_off + ((q) * 4 + i) * 32 * BK]) = g[(q) * 4 + i]; \
+    else                                                                                    \
+      *reinterpret_cast<uint4 *>(&sE[st][s_off + ((q) * 4 + i - 8) * 32 * BK]) =           \
+          g[(q) * 4 + i];                                                                   \
+  }
+#define ENGRAM_FRAGS(st, kk, dst_a, dst_b)                                                    \
+  _Pragma("unroll") for (int i = 0; i < 4; ++i) dst_a[i] = *reinterpret_cast<const bf16x8 *>( \
+      &sW[st][a_base + i * 32 * BK + ((((kk) * 2 + fk) ^ fsw) << 3)]);                      \
+  _Pragma("unroll") for (int j = 0; j < 4; ++j) dst_b[j] = *reinterpret_cast<const bf16x8 *>( \
+      &sE[st][b_base + j * 32 * BK + ((((kk) * 2 + fk) ^ fsw) << 3)]);
+#define ENGRAM_MMA(A, B, I0, I1)                                                              \
+  _Pragma("unroll") for (int i = I0; i < I1; ++i)                                           \
+  _Pragma("unroll") for (int j = 0; j < 4; ++j)                                             \
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[i], B[j], acc[i][j], 0, 0, 0);
+// The barrier waits for this wave's LDS traffic only; the global loads of the
+// next steps stay in flight (their users wait for them individually).
+#define ENGRAM_LDS_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
+#define ENGRAM_FENCE() __builtin_amdgcn_sched_barrier(0)
+#define ENGRAM_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+// Sub-step order: 8 fragment reads each after an MFMA, then loads (0x020) and
+// LDS stores (0x200) alternating with the remaining MFMAs.
+#define ENGRAM_SUBSTEP_ORDER()                                                                \
+  for (int s_ = 0; s_ < 8; ++s_) { ENGRAM_GROUP(0x100, 1); ENGRAM_GROUP(0x008, 1); }         \
+  for (int s_ = 0; s_ < 4; ++s_) {                                                          \
+    ENGRAM_GROUP(0x020, 1); ENGRAM_GROUP(0x008, 1); ENGRAM_GROUP(0x200, 1); ENGRAM_GROUP(0x008, 1); \
+  }
+
+  bf16x8 a0[4], b0[4], a1[4], b1[4];
+  // Prologue: step 0 into stage 0, step 1 in flight. Loads of steps at or past
+  // KT read other rows of the panel or zeros and are never stored.
+  ENGRAM_LOADQ(g0, 0, 0) ENGRAM_LOADQ(g0, 0, 1) ENGRAM_LOADQ(g0, 0, 2) ENGRAM_LOADQ(g0, 0, 3)
+  ENGRAM_LOADQ(g1, 1, 0) ENGRAM_LOADQ(g1, 1, 1) ENGRAM_LOADQ(g1, 1, 2) ENGRAM_LOADQ(g1, 1, 3)
+  ENGRAM_STOREQ(g0, 0, 0) ENGRAM_STOREQ(g0, 0, 1) ENGRAM_STOREQ(g0, 0, 2) ENGRAM_STOREQ(g0, 0, 3)
+  ENGRAM_LDS_BARRIER();
+  ENGRAM_FRAGS(0, 0, a0, b0);
+
+// Step kt computes from stage P, loads step kt+2 into gP and stores step kt+1
+// (held in gQ) into stage Q. Stage Q was last read in step kt-1, which every
+// wave finished before the previous barrier. Stores past the last step land in
+// a stage that is never read again.
+#define ENGRAM_STEP(P, Q, gP, gQ)                                                             \
+  {                                                                                         \
+    ENGRAM_FRAGS(P, 1, a1, b1);                                                             \
+    ENGRAM_LOADQ(gP, kt + 2, 0);                                                            \
+    ENGRAM_STOREQ(gQ, Q, 0);                                                                \
+    ENGRAM_MMA(a0, b0, 0, 4);                                                               \
+    ENGRAM_SUBSTEP_ORDER();                                                                 \
+    ENGRAM_FENCE();                                                                         \
+    ENGRAM_FRAGS(P, 2, a0, b0);                                                             \
+    ENGRAM_LOADQ(gP, kt + 2, 1);                                                            \
+    ENGRAM_STOREQ(gQ, Q, 1);                                                                \
+    ENGRAM_MMA(a1, b1, 0, 4);                                                               \
+    ENGRAM_SUBSTEP_ORDER();                                                                 \
+    ENGRAM_FENCE();                                                                         \
+    ENGRAM_FRAGS(P, 3, a1, b1);                                                             \
+    ENGRAM_LOADQ(gP, kt + 2, 2);                                                            \
+    ENGRAM_STOREQ(gQ, Q, 2);                                                                \
+    ENGRAM_MMA(a0, b0, 0, 4);                                                               \
+    ENGRAM_SUBSTEP_ORDER();                                                                 \
+    ENGRAM_FENCE();                                                                         \
+    ENGRAM_LOADQ(gP, kt + 2, 3);                                                            \
+    ENGRAM_STOREQ(gQ, Q, 3);                                                                \
+    ENGRAM_MMA(a1, b1, 0, 2);                                                               \
+    for (int s_ = 0; s_ < 4; ++s_) {                                                        \
+      ENGRAM_GROUP(0x020, 1); ENGRAM_GROUP(0x008, 1); ENGRAM_GROUP(0x200, 1); ENGRAM_GROUP(0x008, 1); \
+    }                                                                                       \
+    ENGRAM_FENCE();                                                                         \
+    ENGRAM_LDS_BARRIER();                                                                   \
+    ENGRAM_FENCE();                                                                         \
+    ENGRAM_FRAGS(Q, 0, a0, b0);                                                             \
+    ENGRAM_MMA(a1, b1, 2, 4);                                                               \
+    for (int s_ = 0; s_ < 8; ++s_) { ENGRAM_GROUP(0x100, 1); ENGRAM_GROUP(0x008, 1); }       \
+    ENGRAM_FENCE();                                                                         \
+  }
+  // Two steps per iteration keep the register double buffers g0 / g1 static.
+  int kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    ENGRAM_STEP(0, 1, g0, g1);
+    ++kt;
+    ENGRAM_STEP(1, 0, g1, g0);
+    --kt;
+  }
+  if (kt < KT) ENGRAM_STEP(0, 1, g0, g1);
+#undef ENGRAM_STEP
+#undef ENGRAM_SUBSTEP_ORDER
+#undef ENGRAM_GROUP
+#undef ENGRAM_FENCE
+#undef ENGRAM_LDS_BARRIER
+#undef ENGRAM_MMA
+#undef ENGRAM_FRAGS
+#undef ENGRAM_STOREQ
+#undef ENGRAM_LOADQ
+
+  // Epilogue: accumulator r of tile (i, j) is output column
+  // n0 + wn*128 + i*32 + (r/4)*8 + (lane/32)*4 + r%4 of token m0 + wm*128 + j*32 + lane%32.
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + wm * 128 + j * 32 + frow;
+    if (m >= M) continue;
+    uint16_t *crow = C + (int64_t)m * N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * 128 + i * 32 + g * 8 + fk * 4;
+        if (n < N) {
+          uint2 v;
+          v.x = engram::pack_bf16x2(acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1]);
+          v.y = engram::pack_bf16x2(acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]);
+          *reinterpret_cast<uint2 *>(crow + n) = v;
+        }
+      }
+    }
+  }
+}
+
+template <int BN>
+__global__ __launch_bounds__(kNarrowThreads) void gemm_bf16_narrow_kernel(
+    const uint16_t *__restrict__ E, const uint16_t *__restrict__ W, uint16_t *__restrict__ C,
+    int M, int N, int K, int tiles_m, int tiles_n) {
+  constexpr int TI = BN / 64;          // 32-row MFMA tiles per wave along n
+  constexpr int WR = BN / 64;          // W-panel direct loads per wave per stage
+  __shared__ __align__(1024) uint16_t sW0[BN * BK];
+  __shared__ __align__(1024) uint16_t sW1[BN * BK];
+  __shared__ __align__(1024) uint16_t sE0[BM * BK];
+  __shared__ __align__(1024) uint16_t sE1[BM * BK];
+
+  int m0, n0;
+  tile_origin(tiles_m, tiles_n, BN, m0, n0);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // 0..7
@@ -225,14 +420,14 @@ hipError_t engram_launch_gemm_bf16(const uint16_t *e, const uint16_t *w, uint16_
   const int tiles_m = (int)((m + BM - 1) / BM);
   const int tiles_n256 = (int)((n + 255) / 256);
   if ((int64_t)tiles_m * tiles_n256 >= cus) {
-    hipLaunchKernelGGL(gemm_bf16_kernel<256>, dim3((unsigned)(tiles_m * tiles_n256)),
-                       dim3(kThreads), 0, stream, e, w, kv, (int)m, (int)n, (int)k, tiles_m,
+    hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)(tiles_m * tiles_n256)),
+                       dim3(kWideThreads), 0, stream, e, w, kv, (int)m, (int)n, (int)k, tiles_m,
                        tiles_n256);
   } else {
     const int tiles_n128 = (int)((n + 127) / 128);
-    hipLaunchKernelGGL(gemm_bf16_kernel<128>, dim3((unsigned)(tiles_m * tiles_n128)),
-                       dim3(kThreads), 0, stream, e, w, kv, (int)m, (int)n, (int)k, tiles_m,
-                       tiles_n128);
+    hipLaunchKernelGGL(gemm_bf16_narrow_kernel<128>, dim3((unsigned)(tiles_m * tiles_n128)),
+                       dim3(kNarrowThreads), 0, stream, e, w, kv, (int)m, (int)n, (int)k,
+                       tiles_m, tiles_n128);
   }
   return hipGetLastError();
 }

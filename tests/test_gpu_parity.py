@@ -230,11 +230,12 @@ def test_gather_c2_full_size_sampled():
 # projection
 # ---------------------------------------------------------------------------
 
-# Fewer than one 256 x 256 tile per CU selects 128-wide tiles; the last two
-# shapes (>= 256 tiles of 256 x 256) take the 256-wide path, with ragged edges.
+# Fewer than one 256 x 256 tile per CU selects 128-wide tiles; the last three
+# shapes (>= 256 tiles of 256 x 256) take the 256-wide path, with ragged edges
+# and 2, 1 and 7 K-steps (the wide kernel runs two steps per loop iteration).
 @pytest.mark.parametrize("M,N,K", [(1, 8, 64), (31, 264, 192), (257, 520, 1024),
                                    (300, 408, 6144), (600, 256, 128), (513, 1032, 256),
-                                   (4100, 4008, 128), (2304, 7176, 64)])
+                                   (4100, 4008, 128), (2304, 7176, 64), (4097, 4104, 448)])
 def test_project_bf16_shapes(M, N, K):
     rng = np.random.default_rng(M * 7 + N)
     e = gen.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32) * 3)
@@ -247,6 +248,23 @@ def test_project_bf16_shapes(M, N, K):
     exact = O.project(ef, wf)
     tol = gemm_tolerance(ef, wf, exact, True)
     assert_close(got, exact, f"kv {M}x{N}x{K}", atol=0.0, rtol=0.0, extra=tol)
+
+
+def test_project_wide_equals_narrow():
+    # Both tile shapes accumulate each output over K in the same order with the
+    # same MFMA, so the rows a few-token call (narrow tiles) shares with a
+    # many-token call (wide tiles) must carry identical bits.
+    M, N, K = 4100, 4008, 1088
+    rng = np.random.default_rng(11)
+    e = to_device(gen.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32)))
+    w = to_device(gen.f32_to_bf16_bits(rng.standard_normal((N, K)).astype(np.float32) * 0.05))
+    wide = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    E.engram_project(e, w, wide, M, K, N, 0)
+    m = 300
+    narrow = torch.empty((m, N), dtype=torch.bfloat16, device=DEV)
+    E.engram_project(e[:m].contiguous(), w, narrow, m, K, N, 0)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(wide[:m]), bf16_bits(narrow))
 
 
 def test_project_one_hot_exact():
