@@ -97,6 +97,28 @@ def segment_offsets(primes: Sequence[int]):
     return offs, acc
 
 
+def layer_primes(base: int, layers: int, per_layer: int):
+    """Primes, offsets and row counts of several Engram layers' tables.
+
+    [P1] "一层只有一张表" and its table: the two layers' 24 primes each come
+    from one upward search from the base with no prime used twice (layer 1:
+    16000057..16000463, sum 384006168; layer 14: 16000477..16000889, sum
+    384016682), and each layer has its own physical table whose row count is
+    the sum of that layer's primes. [P3] §2.2: primes are drawn in (layer,
+    order, head) order from one ascending sequence. Offsets therefore restart
+    at 0 in every layer. Returns three lists indexed by layer.
+    """
+    p = primes_from(base, layers * per_layer)
+    primes, offsets, rows = [], [], []
+    for li in range(layers):
+        seg = p[li * per_layer:(li + 1) * per_layer]
+        offs, total = segment_offsets(seg)
+        primes.append(seg)
+        offsets.append(offs)
+        rows.append(total)
+    return primes, offsets, rows
+
+
 def multiplier_limit(compressed_vocab: int) -> int:
     """[P1] §"哈希函数" item "乘子不会让乘积溢出": multipliers stay below
     (2^63 - 1) / V' so that no compressed id times a multiplier leaves int64."""
@@ -212,6 +234,28 @@ def hash_rows(ids: np.ndarray, token_map: np.ndarray, compressed_vocab: int, pad
     ext = np.concatenate([prev, xc], axis=1)
     hist_out = ext[:, ext.shape[1] - H:].astype(np.int32)
     return rows.reshape(B * T, S), hist_out
+
+
+def hash_rows_layers(ids: np.ndarray, token_map: np.ndarray, compressed_vocab: int, pad: int,
+                     multipliers: Sequence[Sequence[int]], primes: Sequence[Sequence[int]],
+                     offsets: Sequence[Sequence[int]], max_ngram: int, heads: int,
+                     hist: Optional[np.ndarray] = None):
+    """Row ids of several Engram layers over the same tokens: int64
+    [L, B*T, S], layer l addressing its own table, and the shared history.
+
+    [P1] "一层只有一张表": each layer draws its own multipliers and primes, so
+    the same n-gram lands on unrelated rows in the two layers. [P3] §2.4: the
+    row ids of every Engram layer depend on the token ids only and are all
+    computed before the layer loop, then handed to each layer. The cells (and
+    so the history) do not depend on the layer.
+    """
+    out, hist_out = [], None
+    for li in range(len(multipliers)):
+        rows, h = hash_rows(ids, token_map, compressed_vocab, pad, multipliers[li], primes[li],
+                            offsets[li], max_ngram, heads, hist)
+        out.append(rows)
+        hist_out = h
+    return np.stack(out), hist_out
 
 
 # ----------------------------------------------------------------------------

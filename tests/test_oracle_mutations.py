@@ -96,9 +96,33 @@ def _project_transposed(e, wkv):
     return np.asarray(e, dtype=np.float64) @ w.T[::-1]
 
 
+def _layer_offsets_continue(base, layers, per_layer):
+    """Wrong: one offset sequence over all layers instead of one table per layer."""
+    p = E.primes_from(base, layers * per_layer)
+    offs, _ = E.segment_offsets(p)
+    primes = [p[i * per_layer:(i + 1) * per_layer] for i in range(layers)]
+    offsets = [offs[i * per_layer:(i + 1) * per_layer] for i in range(layers)]
+    return primes, offsets, [sum(x) for x in primes]
+
+
+def _layer_primes_restart(base, layers, per_layer):
+    """Wrong: every layer restarts the prime search at the base."""
+    p = E.primes_from(base, per_layer)
+    offs, total = E.segment_offsets(p)
+    return [list(p)] * layers, [list(offs)] * layers, [total] * layers
+
+
+def _layers_share_multipliers(ids, token_map, compressed_vocab, pad, multipliers, primes, offsets,
+                              max_ngram, heads, hist=None):
+    """Wrong: the first layer's multipliers serve every layer."""
+    return _orig["hash_rows_layers"](ids, token_map, compressed_vocab, pad,
+                                     [multipliers[0]] * len(multipliers), primes, offsets,
+                                     max_ngram, heads, hist)
+
+
 _orig = {name: getattr(E, name) for name in
          ("mix_values", "segment_offsets", "primes_from", "ngram_cells", "gate", "project",
-          "round_to_bf16_bits")}
+          "round_to_bf16_bits", "layer_primes", "hash_rows_layers")}
 
 MUTATIONS = [
     ("mix_values", _mix_oldest_first, [P.test_worked_example_mix_and_indices]),
@@ -112,6 +136,10 @@ MUTATIONS = [
     ("gate", _gate_plain_sigmoid, [P.test_gate_closed_forms]),
     ("gate", _gate_no_weights, [P.test_gate_weights_multiply_the_dot]),
     ("project", _project_transposed, [P.test_projection_one_hot_picks_weight_columns]),
+    ("layer_primes", _layer_offsets_continue, [P.test_layer_primes_match_both_layers_table]),
+    ("layer_primes", _layer_primes_restart, [P.test_layer_primes_match_both_layers_table]),
+    ("hash_rows_layers", _layers_share_multipliers,
+     [P.test_layers_with_own_multipliers_hit_unrelated_rows]),
 ]
 
 

@@ -74,6 +74,62 @@ def test_prime_table_of_both_layers():
         assert O.segment_offsets(seg)[1] == g["config"]["engram_num_embeddings"][li]
 
 
+def test_layer_primes_match_both_layers_table():
+    g = _golden("prime_table.json")
+    n = g["primes_per_layer"]
+    primes, offs, rows = O.layer_primes(g["engram_vocab_size"], 2, n)
+    for li, layer in enumerate(g["layers"]):
+        assert len(primes[li]) == n
+        assert min(primes[li]) == layer["min_prime"]
+        assert max(primes[li]) == layer["max_prime"]
+        assert sum(primes[li]) == layer["sum"]
+        assert rows[li] == g["config"]["engram_num_embeddings"][li]
+        assert offs[li][0] == 0 and offs[li][-1] + primes[li][-1] == rows[li]
+    assert max(primes[0]) < min(primes[1])
+
+
+def _two_layer_case(tokens=512):
+    tm, _ = gen.hash_setup(C1)
+    mults = gen.layer_multipliers(C1, 2)
+    primes, offs, rows = O.layer_primes(C1.prime_base, 2, C1.segments)
+    ids = gen.token_ids(C1)[0][:, :tokens]
+    return tm, mults, primes, offs, rows, ids
+
+
+def _layers(ids, tm, mults, primes, offs, hist=None):
+    return O.hash_rows_layers(ids, tm, C1.compressed_vocab, int(tm[0]), mults, primes, offs,
+                              C1.max_ngram, C1.heads, hist)
+
+
+def test_two_layer_rows_stay_in_each_layers_segments():
+    tm, mults, primes, offs, rows_per_layer, ids = _two_layer_case()
+    rows, hist = _layers(ids, tm, mults, primes, offs)
+    assert rows.shape == (2, ids.size, C1.segments)
+    for li in range(2):
+        lo = np.array(offs[li])
+        hi = lo + np.array(primes[li])
+        assert np.all(rows[li] >= lo) and np.all(rows[li] < hi)
+        assert hi[-1] == rows_per_layer[li]
+    # the history depends on the tokens only, not on the layer
+    _, h1 = O.hash_rows(ids, tm, C1.compressed_vocab, int(tm[0]), mults[0], primes[0], offs[0],
+                        C1.max_ngram, C1.heads)
+    assert np.array_equal(hist, h1)
+    # exchanging the layers' parameters exchanges their row ids
+    swapped, _ = _layers(ids, tm, mults[::-1], primes[::-1], offs[::-1])
+    assert np.array_equal(swapped[0], rows[1]) and np.array_equal(swapped[1], rows[0])
+
+
+def test_layers_with_own_multipliers_hit_unrelated_rows():
+    # P1: each layer draws its own multipliers, so even over the same primes the
+    # same n-gram lands on unrelated rows; the same multipliers land on the same rows.
+    tm, mults, primes, offs, _, ids = _two_layer_case()
+    assert mults[0] != mults[1]
+    own, _ = _layers(ids, tm, mults, [primes[0]] * 2, [offs[0]] * 2)
+    assert np.mean(own[0] == own[1]) < 0.01
+    same, _ = _layers(ids, tm, [mults[0]] * 2, [primes[0]] * 2, [offs[0]] * 2)
+    assert np.array_equal(same[0], same[1])
+
+
 def test_primes_against_sympy():
     for base, count in ((1009, 6), (1_000_000, 24), (16_000_000, 30), (2, 10), (90, 5)):
         got = O.primes_from(base, count)

@@ -44,7 +44,7 @@ SCALE_CHOICES = 15
 
 # child stream index of each tensor
 S_TOKEN_MAP, S_MULT, S_ZIPF_PERM, S_IDS, S_DEAD, S_TABLE_F32, S_WKV, S_QW, S_KW, \
-    S_H, S_HIST = range(11)
+    S_H, S_HIST, S_MULT_LAYERS = range(12)
 
 _CHUNK = 1 << 22
 
@@ -174,6 +174,14 @@ def hash_setup(w: EngramWorkload):
     tm = token_map(w.raw_vocab, w.compressed_vocab, _rng(w.setup_seed, S_TOKEN_MAP))
     mult = multipliers(w.compressed_vocab, w.max_ngram, _rng(w.setup_seed, S_MULT))
     return tm, mult
+
+
+def layer_multipliers(w: EngramWorkload, layers: int) -> list:
+    """Multipliers of ``layers`` Engram layers sharing this hash setup: layer 0
+    keeps ``hash_setup``'s, later layers draw their own from a separate stream."""
+    _, first = hash_setup(w)
+    rng = _rng(w.setup_seed, S_MULT_LAYERS)
+    return [first] + [multipliers(w.compressed_vocab, w.max_ngram, rng) for _ in range(layers - 1)]
 
 
 def token_ids(w: EngramWorkload):
