@@ -234,6 +234,7 @@ def main():
                       "project": round(stage_ms[2], 4), "gate": round(stage_ms[3], 4)},
         "engram_forward_ms": round(forward_ms, 4),
     }
+    out["hash_layers"] = hash_layers_bench(max(args.steps, 20))
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(gw)
@@ -244,6 +245,51 @@ def main():
         torch.cuda.empty_cache()
         out["decode"] = decode_bench(args.steps, args.warmup)
     print(json.dumps(out), flush=True)
+
+
+def hash_layers_bench(reps: int):
+    """Row ids of the two Engram layers (the pages' layer-1 and layer-14 primes,
+    each layer with its own multipliers) for 8 x 4096 tokens: one
+    engram_hash_layers pass against one engram_hash call per layer. Each figure
+    is the mean over ``reps`` back-to-back launches between two HIP events."""
+    import torch
+    import hashed_gram_conditional_amd as E
+    from workloads import C1, gen
+    from workloads.harness import GpuWorkload
+
+    gw = GpuWorkload(C1, table=False, dense=False)
+    w = gw.w
+    L, T, S = 2, w.tokens, w.segments
+    mults = gen.layer_multipliers(w, L)
+    primes, offs, table_rows = E.engram_make_layer_primes(w.prime_base, L, S)
+    params = [E.hash_params(w.raw_vocab, w.compressed_vocab, w.max_ngram, w.heads, gw.pad,
+                            gw.token_map, mults[i], primes[i], offs[i]) for i in range(L)]
+    rows = torch.empty((L, T, S), dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return 1e3 * a.elapsed_time(b) / reps
+
+    one = timed(lambda: E.engram_hash_layers(params, gw.ids, w.batch, w.seq, None, None, rows))
+    two = timed(lambda: [E.engram_hash(params[i], gw.ids, w.batch, w.seq, None, None, rows[i])
+                         for i in range(L)])
+    nbytes = T * (4 + L * S * 8)
+    del rows
+    gw.free()
+    return {"workload": "two Engram layers hashed in one pass: 8 x 4096 Zipf tokens with DEAD "
+                        "spans, 2 x 24 segments, primes from 16,000,000 (tables of "
+                        f"{table_rows[0]:,} and {table_rows[1]:,} rows)",
+            "one_pass_us": round(one, 2), "one_call_per_layer_us": round(two, 2),
+            "bytes_per_token": 4 + L * S * 8,
+            "achieved_GBps": round(nbytes / (one * 1e-6) / 1e9, 1)}
 
 
 def decode_bench(steps: int, warmup: int):

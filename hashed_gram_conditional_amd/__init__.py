@@ -5,10 +5,11 @@ The computation runs in the HIP kernels of ``libengram.so`` behind the C ABI of
 in, raw pointers out). Importing it fails if the library is not built.
 """
 from ._binding import (  # noqa: F401
-    DEAD, MAX_NGRAM, MAX_SEGMENTS, ROW_BYTES, ROW_E4M3_E8M0_264, ROW_F32,
+    DEAD, MAX_NGRAM, MAX_SEGMENTS, MAX_LAYERS, MAX_TOTAL_SEGMENTS, ROW_BYTES, ROW_E4M3_E8M0_264, ROW_F32,
     OK, EINVAL, EVOCAB, EMULT, ESHAPE, EWORKSPACE, EHIP, EPRIMES,
     EngramError, HashParams, ForwardDesc, LIB, LIB_PATH,
     status_string, hash_params, forward_desc,
-    engram_make_primes, engram_check_token_map, engram_hash, engram_gather,
+    engram_make_primes, engram_make_layer_primes, engram_check_token_map, engram_hash,
+    engram_hash_layers, engram_gather,
     engram_project, engram_gate, engram_forward_workspace_size, engram_forward,
 )

@@ -15,6 +15,8 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libengram.
 DEAD = -1
 MAX_NGRAM = 8
 MAX_SEGMENTS = 64
+MAX_LAYERS = 4
+MAX_TOTAL_SEGMENTS = 128
 ROW_BYTES = 264
 ROW_E4M3_E8M0_264 = 0
 ROW_F32 = 1
@@ -82,6 +84,8 @@ def _load():
         "engram_sizeof_hash_params": (SZ, []),
         "engram_sizeof_forward_desc": (SZ, []),
         "engram_make_primes": (ctypes.c_int, [I64, I32, P, P, P]),
+        "engram_make_layer_primes": (ctypes.c_int, [I64, I32, I32, P, P, P]),
+        "engram_hash_layers": (ctypes.c_int, [P, I32, P, I64, I64, P, P, P, P]),
         "engram_check_token_map": (ctypes.c_int, [P, I32, I32]),
         "engram_hash": (ctypes.c_int, [P, P, I64, I64, P, P, P, P]),
         "engram_gather": (ctypes.c_int, [P, I64, I32, I32, P, I64, P, P]),
@@ -166,6 +170,20 @@ def engram_make_primes(base: int, count: int):
     return list(pr)[:count], list(off)[:count], tot.value
 
 
+def engram_make_layer_primes(base: int, layers: int, per_layer: int):
+    """[host] (primes, offsets, rows), each a list per layer: one ascending prime
+    sequence from ``base`` dealt to the layers, offsets restarting per layer."""
+    n = max(layers * per_layer, 1)
+    pr = (ctypes.c_int64 * n)()
+    off = (ctypes.c_int64 * n)()
+    rows = (ctypes.c_int64 * max(layers, 1))()
+    _check(LIB.engram_make_layer_primes(base, layers, per_layer, ctypes.addressof(pr),
+                                        ctypes.addressof(off), ctypes.addressof(rows)),
+           "engram_make_layer_primes")
+    cut = lambda a: [list(a)[l * per_layer:(l + 1) * per_layer] for l in range(layers)]
+    return cut(pr), cut(off), list(rows)[:layers]
+
+
 def engram_check_token_map(token_map, raw_vocab: int, compressed_vocab: int) -> int:
     """[host] status of the start-up check of a host int32 map (numpy array)."""
     import numpy as np
@@ -177,6 +195,15 @@ def engram_hash(params: HashParams, ids, batch: int, seq: int, hist_in, hist_out
                 stream=None):
     _check(LIB.engram_hash(ctypes.byref(params), _ptr(ids), batch, seq, _ptr(hist_in),
                            _ptr(hist_out), _ptr(row_ids), _stream(stream)), "engram_hash")
+
+
+def engram_hash_layers(params: Sequence[HashParams], ids, batch: int, seq: int, hist_in,
+                       hist_out, row_ids, stream=None):
+    """Row ids of len(params) layers into row_ids [layers, batch*seq, S]."""
+    arr = (HashParams * len(params))(*params)
+    _check(LIB.engram_hash_layers(ctypes.addressof(arr), len(params), _ptr(ids), batch, seq,
+                                  _ptr(hist_in), _ptr(hist_out), _ptr(row_ids), _stream(stream)),
+           "engram_hash_layers")
 
 
 def engram_gather(table, table_rows: int, row_format: int, row_dim: int, row_ids, n_ids: int,

@@ -38,12 +38,14 @@ __device__ __forceinline__ float warp_sum(float v) {
 // Launchers implemented by the kernel translation units. They validate nothing:
 // the C-ABI layer checks every argument first. Each returns hipSuccess or the
 // launch error.
+// Hash setup of `layers` Engram layers sharing one token map; segment j of
+// layer l is entry l * segments + j of the per-segment arrays.
 struct EngramHashArgs {
-  int32_t raw_vocab, compressed_vocab, max_ngram, heads, segments, pad_id;
-  uint64_t mult[ENGRAM_MAX_NGRAM];
-  uint32_t prime[ENGRAM_MAX_SEGMENTS];
-  uint64_t recip[ENGRAM_MAX_SEGMENTS];   // floor((2^64 - 1) / prime)
-  int64_t offset[ENGRAM_MAX_SEGMENTS];
+  int32_t raw_vocab, compressed_vocab, max_ngram, heads, segments, pad_id, layers;
+  uint64_t mult[ENGRAM_MAX_LAYERS][ENGRAM_MAX_NGRAM];
+  uint32_t prime[ENGRAM_MAX_TOTAL_SEGMENTS];
+  uint64_t recip[ENGRAM_MAX_TOTAL_SEGMENTS];   // floor((2^64 - 1) / prime)
+  int64_t offset[ENGRAM_MAX_TOTAL_SEGMENTS];
 };
 
 hipError_t engram_launch_hash(const EngramHashArgs &a, const int32_t *token_map,

@@ -90,7 +90,9 @@ int64_t total_rows(const engram_hash_params *p) {
   return p->offsets[S - 1] + p->primes[S - 1];
 }
 
-EngramHashArgs make_hash_args(const engram_hash_params *p) {
+// Kernel arguments for `layers` validated parameter sets that agree on every
+// shared field (checked by check_layer_params).
+EngramHashArgs make_hash_args(const engram_hash_params *p, int layers) {
   EngramHashArgs a;
   memset(&a, 0, sizeof(a));
   a.raw_vocab = p->raw_vocab;
@@ -99,13 +101,37 @@ EngramHashArgs make_hash_args(const engram_hash_params *p) {
   a.heads = p->heads;
   a.segments = (p->max_ngram - 1) * p->heads;
   a.pad_id = p->pad_id;
-  for (int i = 0; i < p->max_ngram; ++i) a.mult[i] = (uint64_t)p->multipliers[i];
-  for (int j = 0; j < a.segments; ++j) {
-    a.prime[j] = (uint32_t)p->primes[j];
-    a.recip[j] = UINT64_MAX / (uint64_t)p->primes[j];
-    a.offset[j] = p->offsets[j];
+  a.layers = layers;
+  for (int l = 0; l < layers; ++l) {
+    const engram_hash_params *q = p + l;
+    for (int i = 0; i < q->max_ngram; ++i) a.mult[l][i] = (uint64_t)q->multipliers[i];
+    for (int j = 0; j < a.segments; ++j) {
+      const int js = l * a.segments + j;
+      a.prime[js] = (uint32_t)q->primes[j];
+      a.recip[js] = UINT64_MAX / (uint64_t)q->primes[j];
+      a.offset[js] = q->offsets[j];
+    }
   }
   return a;
+}
+
+// Several layers hashed together: each set valid on its own, all sharing the
+// token map and its vocabularies, the n-gram shape and the pad id.
+int check_layer_params(const engram_hash_params *p, int32_t layers) {
+  if (p == nullptr) return ENGRAM_EINVAL;
+  if (layers < 1 || layers > ENGRAM_MAX_LAYERS) return ENGRAM_ESHAPE;
+  for (int32_t l = 0; l < layers; ++l) {
+    const int rc = check_hash_params(p + l);
+    if (rc != ENGRAM_OK) return rc;
+    const engram_hash_params &q = p[l];
+    if (q.raw_vocab != p->raw_vocab || q.compressed_vocab != p->compressed_vocab ||
+        q.max_ngram != p->max_ngram || q.heads != p->heads || q.pad_id != p->pad_id ||
+        q.token_map != p->token_map)
+      return ENGRAM_EINVAL;
+  }
+  if ((int64_t)layers * (p->max_ngram - 1) * p->heads > ENGRAM_MAX_TOTAL_SEGMENTS)
+    return ENGRAM_ESHAPE;
+  return ENGRAM_OK;
 }
 
 int check_desc(const engram_forward_desc *d) {
@@ -175,6 +201,26 @@ int engram_make_primes(int64_t base, int32_t count, int64_t *primes_out, int64_t
   return ENGRAM_OK;
 }
 
+int engram_make_layer_primes(int64_t base, int32_t layers, int32_t per_layer,
+                             int64_t *primes_out, int64_t *offsets_out, int64_t *rows_out) {
+  if (layers < 1 || per_layer < 0) return ENGRAM_EINVAL;
+  const int64_t count = (int64_t)layers * per_layer;
+  if (count > INT32_MAX) return ENGRAM_EINVAL;
+  // One ascending sequence, dealt to the layers in order; offsets restart per layer.
+  int rc = engram_make_primes(base, (int32_t)count, primes_out, offsets_out, nullptr);
+  if (rc != ENGRAM_OK) return rc;
+  for (int32_t l = 0; l < layers; ++l) {
+    int64_t acc = 0;
+    for (int32_t j = 0; j < per_layer; ++j) {
+      const int64_t k = (int64_t)l * per_layer + j;
+      offsets_out[k] = acc;
+      acc += primes_out[k];
+    }
+    if (rows_out) rows_out[l] = acc;
+  }
+  return ENGRAM_OK;
+}
+
 int engram_check_token_map(const int32_t *token_map, int32_t raw_vocab,
                            int32_t compressed_vocab) {
   if (token_map == nullptr || raw_vocab < 1 || compressed_vocab < 1) return ENGRAM_EINVAL;
@@ -198,10 +244,10 @@ int engram_check_token_map(const int32_t *token_map, int32_t raw_vocab,
   return rc;
 }
 
-int engram_hash(const engram_hash_params *params, const int32_t *ids, int64_t batch,
-                int64_t seq, const int32_t *hist_in, int32_t *hist_out, int64_t *row_ids,
-                hipStream_t stream) {
-  int rc = check_hash_params(params);
+int engram_hash_layers(const engram_hash_params *params, int32_t layers, const int32_t *ids,
+                       int64_t batch, int64_t seq, const int32_t *hist_in, int32_t *hist_out,
+                       int64_t *row_ids, hipStream_t stream) {
+  int rc = check_layer_params(params, layers);
   if (rc != ENGRAM_OK) return rc;
   if (batch < 0 || seq < 0) return ENGRAM_ESHAPE;
   const int64_t ntok = batch * seq;
@@ -209,9 +255,15 @@ int engram_hash(const engram_hash_params *params, const int32_t *ids, int64_t ba
   if (!aligned(ids, 4) || !aligned(row_ids, 8) || !aligned(hist_in, 4) || !aligned(hist_out, 4))
     return ENGRAM_EINVAL;
   if (ntok > (int64_t)INT32_MAX * 64) return ENGRAM_ESHAPE;
-  const EngramHashArgs a = make_hash_args(params);
+  const EngramHashArgs a = make_hash_args(params, layers);
   return hip_status(engram_launch_hash(a, params->token_map, ids, batch, seq, hist_in, hist_out,
                                        row_ids, stream));
+}
+
+int engram_hash(const engram_hash_params *params, const int32_t *ids, int64_t batch,
+                int64_t seq, const int32_t *hist_in, int32_t *hist_out, int64_t *row_ids,
+                hipStream_t stream) {
+  return engram_hash_layers(params, 1, ids, batch, seq, hist_in, hist_out, row_ids, stream);
 }
 
 int engram_gather(const void *table, int64_t table_rows, int32_t row_format, int32_t row_dim,
@@ -324,7 +376,7 @@ int engram_forward(const engram_hash_params *params, const engram_forward_desc *
   void *e = ws + align256((size_t)ntok * S * 8);
   void *kv = (char *)e + align256((size_t)ntok * in_dim * esz);
 
-  const EngramHashArgs a = make_hash_args(params);
+  const EngramHashArgs a = make_hash_args(params, 1);
   hipError_t err = engram_launch_hash(a, params->token_map, ids, desc->batch, desc->seq,
                                       hist_in, hist_out, row_ids, stream);
   if (err != hipSuccess || ntok == 0) return hip_status(err);

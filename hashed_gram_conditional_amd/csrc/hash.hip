@@ -9,9 +9,14 @@
 // §4.4 (decode fuses the hash with the history commit).
 //
 // Layout: one block of 256 threads owns 256 consecutive flat tokens. Phase 1:
-// one thread per token builds the look-back cells and the N-1 mixes into LDS.
-// Phase 2: the block writes its 256 x S int64 row ids as one contiguous,
-// fully coalesced span, each thread reducing mixes modulo the primes.
+// one thread per token builds the look-back cells once, then each layer's N-1
+// mixes (its own multipliers) into LDS. Phase 2: for each layer the block
+// writes its 256 x S int64 row ids as one contiguous, fully coalesced span of
+// that layer's [tokens, S] slice, each thread reducing mixes modulo the
+// layer's primes. Several layers in one pass follow "条件记忆：DeepSeek V4.1
+// Engram 如何用 O(1) 查表换掉一层计算" §2.4 (every layer's ids are known before
+// the layer loop) and "DeepSeek-V4.1 模型结构（5）：记忆，Engram", "一层只有一张表"
+// (each layer has its own primes and multipliers).
 //
 // mix < 2^63 and p < 2^32, and gfx950 has no 64-bit integer divide, so
 // x mod p uses the precomputed reciprocal r = floor((2^64-1)/p): q = hi64(x r)
@@ -45,23 +50,26 @@ __device__ __forceinline__ int32_t cell_value(const EngramHashArgs &a,
   return a.pad_id;
 }
 
+template <int L>
 __global__ __launch_bounds__(kTok) void hash_kernel(
     EngramHashArgs a, const int32_t *__restrict__ token_map, const int32_t *__restrict__ ids,
     int64_t batch, int64_t seq, const int32_t *hist_in, int32_t *hist_out,
     int64_t *__restrict__ row_ids, int commit_history) {
-  __shared__ uint64_t s_mix[ENGRAM_MAX_NGRAM - 1][kTok];
-  __shared__ uint64_t s_recip[ENGRAM_MAX_SEGMENTS];
-  __shared__ int64_t s_off[ENGRAM_MAX_SEGMENTS];
-  __shared__ uint32_t s_prime[ENGRAM_MAX_SEGMENTS];
+  constexpr int kSeg = L * ENGRAM_MAX_SEGMENTS < ENGRAM_MAX_TOTAL_SEGMENTS
+                           ? L * ENGRAM_MAX_SEGMENTS : ENGRAM_MAX_TOTAL_SEGMENTS;
+  __shared__ uint64_t s_mix[L][ENGRAM_MAX_NGRAM - 1][kTok];
+  __shared__ uint64_t s_recip[kSeg];
+  __shared__ int64_t s_off[kSeg];
+  __shared__ uint32_t s_prime[kSeg];
 
   const int tid = threadIdx.x;
   const int S = a.segments;
   const int N = a.max_ngram;
   const int H = N - 1;
-  if (tid < S) {
-    s_prime[tid] = a.prime[tid];
-    s_recip[tid] = a.recip[tid];
-    s_off[tid] = a.offset[tid];
+  for (int j = tid; j < L * S; j += kTok) {
+    s_prime[j] = a.prime[j];
+    s_recip[j] = a.recip[j];
+    s_off[j] = a.offset[j];
   }
 
   const int64_t ntok = batch * seq;
@@ -73,8 +81,8 @@ __global__ __launch_bounds__(kTok) void hash_kernel(
     const int32_t *row = ids + b * seq;
     const int32_t *hist = hist_in ? hist_in + b * H : nullptr;
     int32_t vals[ENGRAM_MAX_NGRAM];
+    uint64_t cells[ENGRAM_MAX_NGRAM];
     bool blocked = false;
-    uint64_t mix = 0;
 #pragma unroll
     for (int i = 0; i < ENGRAM_MAX_NGRAM; ++i) {
       if (i < N) {
@@ -82,10 +90,19 @@ __global__ __launch_bounds__(kTok) void hash_kernel(
         vals[i] = v;
         // A DEAD cell blocks itself and every older cell: they hash as the pad id.
         blocked = blocked || (v < 0);
-        const uint64_t c = blocked ? (uint64_t)a.pad_id : (uint64_t)v;
-        // Orders build on each other: mix_{n+1} = mix_n ^ x'_{t-n} m_n.
-        mix ^= c * a.mult[i];
-        if (i >= 1) s_mix[i - 1][tid] = mix;
+        cells[i] = blocked ? (uint64_t)a.pad_id : (uint64_t)v;
+      }
+    }
+#pragma unroll
+    for (int l = 0; l < L; ++l) {
+      uint64_t mix = 0;
+#pragma unroll
+      for (int i = 0; i < ENGRAM_MAX_NGRAM; ++i) {
+        if (i < N) {
+          // Orders build on each other: mix_{n+1} = mix_n ^ x'_{t-n} m_n.
+          mix ^= cells[i] * a.mult[l][i];
+          if (i >= 1) s_mix[l][i - 1][tid] = mix;
+        }
       }
     }
     if (commit_history) {
@@ -101,15 +118,19 @@ __global__ __launch_bounds__(kTok) void hash_kernel(
   const int64_t left = ntok - tok0;
   const int ntb = left < kTok ? (int)left : kTok;
   const int total = ntb * S;
-  int64_t *out = row_ids + tok0 * S;
-  for (int o = tid; o < total; o += kTok) {
-    const int lt = o / S;
-    const int j = o - lt * S;
-    const uint64_t x = s_mix[j / a.heads][lt];
-    const uint64_t p = s_prime[j];
-    uint64_t r = x - __umul64hi(x, s_recip[j]) * p;
-    if (r >= p) r -= p;
-    out[o] = (int64_t)r + s_off[j];
+#pragma unroll
+  for (int l = 0; l < L; ++l) {
+    int64_t *out = row_ids + (int64_t)l * ntok * S + tok0 * S;
+    for (int o = tid; o < total; o += kTok) {
+      const int lt = o / S;
+      const int j = o - lt * S;
+      const int js = l * S + j;
+      const uint64_t x = s_mix[l][j / a.heads][lt];
+      const uint64_t p = s_prime[js];
+      uint64_t r = x - __umul64hi(x, s_recip[js]) * p;
+      if (r >= p) r -= p;
+      out[o] = (int64_t)r + s_off[js];
+    }
   }
 }
 
@@ -141,9 +162,28 @@ hipError_t engram_launch_hash(const EngramHashArgs &a, const int32_t *token_map,
   const int64_t ntok = batch * seq;
   const bool fused = hist_out != nullptr && seq == 1;
   if (ntok > 0) {
-    const int64_t blocks = (ntok + kTok - 1) / kTok;
-    hipLaunchKernelGGL(hash_kernel, dim3((unsigned)blocks), dim3(kTok), 0, stream, a,
-                       token_map, ids, batch, seq, hist_in, hist_out, row_ids, fused ? 1 : 0);
+    const dim3 grid((unsigned)((ntok + kTok - 1) / kTok));
+    const int commit = fused ? 1 : 0;
+    switch (a.layers) {
+      case 1:
+        hipLaunchKernelGGL(hash_kernel<1>, grid, dim3(kTok), 0, stream, a, token_map, ids, batch,
+                           seq, hist_in, hist_out, row_ids, commit);
+        break;
+      case 2:
+        hipLaunchKernelGGL(hash_kernel<2>, grid, dim3(kTok), 0, stream, a, token_map, ids, batch,
+                           seq, hist_in, hist_out, row_ids, commit);
+        break;
+      case 3:
+        hipLaunchKernelGGL(hash_kernel<3>, grid, dim3(kTok), 0, stream, a, token_map, ids, batch,
+                           seq, hist_in, hist_out, row_ids, commit);
+        break;
+      case 4:
+        hipLaunchKernelGGL(hash_kernel<4>, grid, dim3(kTok), 0, stream, a, token_map, ids, batch,
+                           seq, hist_in, hist_out, row_ids, commit);
+        break;
+      default:
+        return hipErrorInvalidValue;
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

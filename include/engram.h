@@ -55,6 +55,8 @@ extern "C" {
 #define ENGRAM_DEAD (-1)
 #define ENGRAM_MAX_NGRAM 8        /* N, largest n-gram order (orders 2..N) */
 #define ENGRAM_MAX_SEGMENTS 64    /* S = (N - 1) * K */
+#define ENGRAM_MAX_LAYERS 4       /* Engram layers hashed in one engram_hash_layers call */
+#define ENGRAM_MAX_TOTAL_SEGMENTS 128  /* layers * S in one engram_hash_layers call */
 #define ENGRAM_ROW_BYTES 264      /* E4M3 row: 256 payload bytes + 8 scale bytes */
 #define ENGRAM_ROW_DIM_E4M3 256
 
@@ -136,6 +138,22 @@ int engram_make_primes(int64_t base, int32_t count, int64_t *primes_out,
                        int64_t *offsets_out, int64_t *total_rows_out);
 
 /*
+ * [host] Tables of several Engram layers: the first layers * per_layer primes
+ * >= base, ascending and never reused, dealt to the layers in order (layer l
+ * takes primes [l * per_layer, (l + 1) * per_layer)); each layer has its own
+ * table, so offsets restart at 0 in every layer and rows_out[l] is the sum of
+ * layer l's primes ([P1] "一层只有一张表" and its table of the two layers:
+ * 16000057..16000463, sum 384006168, then 16000477..16000889, sum 384016682;
+ * [P3] §2.2: primes drawn in (layer, order, head) order).
+ * primes_out, offsets_out: [host] int64 [layers * per_layer], layer-major;
+ * rows_out: [host] int64 [layers] or NULL.
+ * Errors: ENGRAM_EINVAL (layers < 1, per_layer < 0, null, base < 2 or a prime
+ * >= 2^32).
+ */
+int engram_make_layer_primes(int64_t base, int32_t layers, int32_t per_layer,
+                             int64_t *primes_out, int64_t *offsets_out, int64_t *rows_out);
+
+/*
  * [host] Start-up check that the compression map matches the configured
  * compressed vocabulary: every value in [0, V'), every compressed id used, and
  * so max + 1 == V' ([P1] §"哈希函数": a mismatch means every row id is wrong;
@@ -164,6 +182,29 @@ int engram_check_token_map(const int32_t *token_map, int32_t raw_vocab,
 int engram_hash(const engram_hash_params *params, const int32_t *ids, int64_t batch,
                 int64_t seq, const int32_t *hist_in, int32_t *hist_out,
                 int64_t *row_ids, hipStream_t stream);
+
+/*
+ * Steps 1-2 for several Engram layers over the same tokens, in one pass: the
+ * cells (and the history) are built once, then each layer mixes them with its
+ * own multipliers and reduces them modulo its own primes ([P1] "一层只有一张表":
+ * the layers' primes and multipliers are drawn independently, so an n-gram
+ * lands on unrelated rows; [P3] §2.4: every layer's row ids depend on the
+ * token ids only and are computed before the layer loop).
+ *   params   [host] engram_hash_params [layers]. All layers share raw_vocab,
+ *            compressed_vocab, max_ngram, heads, pad_id and token_map; each
+ *            has its own multipliers, primes and offsets (offsets of its own
+ *            table, see engram_make_layer_primes).
+ *   layers   1 <= layers <= ENGRAM_MAX_LAYERS, layers * S <= ENGRAM_MAX_TOTAL_SEGMENTS.
+ *   row_ids  int64 [layers, B*T, S]: layer l's ids are the contiguous slice
+ *            row_ids + l * B*T*S, ready for that layer's engram_gather.
+ *   ids, hist_in, hist_out as for engram_hash (the history has no layer).
+ * With layers = 1 this is engram_hash.
+ * Errors: ENGRAM_EINVAL (also: the layers disagree on a shared field),
+ * ENGRAM_EMULT, ENGRAM_EPRIMES, ENGRAM_ESHAPE, ENGRAM_EHIP.
+ */
+int engram_hash_layers(const engram_hash_params *params, int32_t layers, const int32_t *ids,
+                       int64_t batch, int64_t seq, const int32_t *hist_in, int32_t *hist_out,
+                       int64_t *row_ids, hipStream_t stream);
 
 /*
  * Step 3: gather and dequantise rows ([P3] §2.3: fp8 E4M3 payload and E8M0

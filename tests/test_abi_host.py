@@ -62,6 +62,13 @@ def test_library_primes_equal_oracle_primes(base, count):
     assert p == po and off == oo and tot == to
 
 
+@pytest.mark.parametrize("base,layers,per_layer", [(16_000_000, 2, 24), (1009, 3, 6),
+                                                    (1_000_000, 4, 24), (2, 1, 5)])
+def test_library_layer_primes_equal_oracle(base, layers, per_layer):
+    assert E.engram_make_layer_primes(base, layers, per_layer) == \
+        O.layer_primes(base, layers, per_layer)
+
+
 def test_make_primes_rejects_beyond_32_bits():
     with pytest.raises(E.EngramError):
         E.engram_make_primes(4_294_967_290, 2)
@@ -108,6 +115,44 @@ def test_hash_argument_validation():
     assert _hash_status(_params(), ids=0x2001) == E.EINVAL          # misaligned
     assert _hash_status(_params(), ids=None) == E.EINVAL
     assert _hash_status(_params(), B=-1) == E.ESHAPE
+
+
+def _hash_layers_status(params, layers=None, ids=0x2000, B=1, T=4, rows=0x3000):
+    arr = (E.HashParams * len(params))(*params)
+    n = len(params) if layers is None else layers
+    return E.LIB.engram_hash_layers(ctypes.addressof(arr), n, ids, B, T, None, None, rows, None)
+
+
+@host_only
+def test_hash_layers_validation():
+    w = C1
+    tm, _ = gen.hash_setup(w)
+    mults = gen.layer_multipliers(w, 4)
+    primes, offs, _ = E.engram_make_layer_primes(w.prime_base, 4, w.segments)
+
+    def layer(li, **kw):
+        args = dict(raw_vocab=w.raw_vocab, compressed_vocab=w.compressed_vocab,
+                    max_ngram=w.max_ngram, heads=w.heads, pad_id=int(tm[0]), token_map=0x1000,
+                    multipliers=mults[li], primes=primes[li], offsets=offs[li])
+        args.update(kw)
+        return E.hash_params(**args)
+
+    two = [layer(0), layer(1)]
+    assert _hash_layers_status(two, ids=None) == E.EINVAL         # shapes fine, ids null
+    assert _hash_layers_status(two, layers=0) == E.ESHAPE
+    assert _hash_layers_status(two * 3, layers=5) == E.ESHAPE
+    assert _hash_layers_status([layer(0), layer(1, token_map=0x1100)]) == E.EINVAL
+    assert _hash_layers_status([layer(0), layer(1, pad_id=int(tm[0]) + 1)]) == E.EINVAL
+    assert _hash_layers_status([layer(0), layer(1, compressed_vocab=w.compressed_vocab - 1)]) \
+        == E.EINVAL
+    assert _hash_layers_status([layer(0), layer(1, multipliers=[2] + mults[1][1:])]) == E.EMULT
+    assert _hash_layers_status([layer(0), layer(1, offsets=[0] * w.segments)]) == E.EPRIMES
+    # 4 layers of 24 segments fit; 3 layers of 56 (N = 8, K = 8) exceed 128
+    assert _hash_layers_status([layer(i) for i in range(4)], ids=None) == E.EINVAL
+    big = E.engram_make_layer_primes(w.prime_base, 3, 56)
+    wide = [E.hash_params(w.raw_vocab, w.compressed_vocab, 8, 8, int(tm[0]), 0x1000,
+                          [1] * 8, big[0][i], big[1][i]) for i in range(3)]
+    assert _hash_layers_status(wide) == E.ESHAPE
 
 
 @host_only

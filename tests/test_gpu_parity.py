@@ -227,6 +227,92 @@ def test_gather_c2_full_size_sampled():
 
 
 # ---------------------------------------------------------------------------
+# several Engram layers hashed in one pass
+# ---------------------------------------------------------------------------
+
+def _layer_setup(gw, layers):
+    w = gw.w
+    mults = gen.layer_multipliers(w, layers)
+    primes, offs, rows = E.engram_make_layer_primes(w.prime_base, layers, w.segments)
+    po, oo, ro = O.layer_primes(w.prime_base, layers, w.segments)
+    assert (primes, offs, rows) == (po, oo, ro)
+    params = [E.hash_params(w.raw_vocab, w.compressed_vocab, w.max_ngram, w.heads, gw.pad,
+                            gw.token_map, mults[li], primes[li], offs[li])
+              for li in range(layers)]
+    return mults, primes, offs, params
+
+
+def _gpu_layer_rows(gw, params, ids=None, hist_in=None, hist_out=None, batch=None, seq=None):
+    w = gw.w
+    ids = gw.ids if ids is None else ids
+    batch = w.batch if batch is None else batch
+    seq = w.seq if seq is None else seq
+    n = batch * seq
+    rows = torch.full((len(params), max(n, 1), w.segments), -7, dtype=torch.int64, device=DEV)
+    E.engram_hash_layers(params, ids, batch, seq, hist_in, hist_out, rows)
+    torch.cuda.synchronize()
+    return rows[:, :n].cpu().numpy()
+
+
+def _oracle_layer_rows(gw, mults, primes, offs, ids=None, hist=None):
+    w = gw.w
+    ids = gw.ids_np if ids is None else ids
+    return O.hash_rows_layers(ids, gw.token_map_np, w.compressed_vocab, gw.pad, mults, primes,
+                              offs, w.max_ngram, w.heads, hist=hist)
+
+
+@pytest.mark.parametrize("w,layers", [(C0, 3), (C0, 4), (C1, 2), (S_B, 2)],
+                         ids=["C0x3", "C0x4", "C1x2", "S_Bx2"])
+def test_hash_layers_bit_exact(w, layers):
+    say(f"hash {layers} layers {w.name}: B={w.batch} T={w.seq} S={w.segments}")
+    gw = GpuWorkload(w, table=False, dense=False)
+    mults, primes, offs, params = _layer_setup(gw, layers)
+    hout = torch.full((w.batch, w.max_ngram - 1), -9, dtype=torch.int32, device=DEV)
+    got = _gpu_layer_rows(gw, params, hist_out=hout)
+    exp, exp_hist = _oracle_layer_rows(gw, mults, primes, offs)
+    assert got.shape == (layers, w.tokens, w.segments)
+    assert np.array_equal(got, exp)
+    assert np.array_equal(hout.cpu().numpy(), exp_hist)
+    # layer 0 carries the single-layer setup, so it equals engram_hash
+    assert np.array_equal(got[0], _gpu_rows(gw))
+
+
+def test_hash_layers_decode_in_place():
+    say("hash 2 layers C4 decode")
+    gw = GpuWorkload(C4, table=False, dense=False)
+    mults, primes, offs, params = _layer_setup(gw, 2)
+    h = gw.hist_in.clone()
+    ids2 = gw.ids_np.copy()
+    ids2[7, 0] = -1
+    for step_ids in (gw.ids_np, ids2):
+        prev = h.cpu().numpy()
+        got = _gpu_layer_rows(gw, params, ids=to_device(step_ids), hist_in=h, hist_out=h)
+        exp, exp_hist = _oracle_layer_rows(gw, mults, primes, offs, ids=step_ids, hist=prev)
+        assert np.array_equal(got, exp)
+        assert np.array_equal(h.cpu().numpy(), exp_hist)
+
+
+def test_hash_layers_chunks_equal_one_shot():
+    say("hash 2 layers C1 chunks")
+    gw = GpuWorkload(C1, table=False, dense=False)
+    mults, primes, offs, params = _layer_setup(gw, 2)
+    ids = gw.ids_np[:3, :600].copy()
+    ids[2, 300:305] = -1
+    exp, exp_hist = _oracle_layer_rows(gw, mults, primes, offs, ids=ids)
+    exp = exp.reshape(2, 3, 600, -1)
+    hist = torch.empty((3, 3), dtype=torch.int32, device=DEV)
+    bounds = [0, 100, 101, 260, 600]
+    parts = []
+    for i, (a, b) in enumerate(zip(bounds[:-1], bounds[1:])):
+        chunk = to_device(np.ascontiguousarray(ids[:, a:b]))
+        r = _gpu_layer_rows(gw, params, ids=chunk, batch=3, seq=b - a,
+                            hist_in=hist if i else None, hist_out=hist)
+        parts.append(r.reshape(2, 3, b - a, -1))
+    assert np.array_equal(np.concatenate(parts, axis=2), exp)
+    assert np.array_equal(hist.cpu().numpy(), exp_hist)
+
+
+# ---------------------------------------------------------------------------
 # projection
 # ---------------------------------------------------------------------------
 
