@@ -328,6 +328,8 @@ def decode_bench(steps: int, warmup: int):
     rows = torch.empty((T, S), dtype=torch.int64, device="cuda")
     e = torch.empty((T, K_in), dtype=torch.bfloat16, device="cuda")
     kv = torch.empty((T, N_out), dtype=torch.bfloat16, device="cuda")
+    pws_n = E.engram_project_workspace_size(T, K_in, N_out, 0)
+    pws = torch.empty(max(pws_n, 1), dtype=torch.uint8, device="cuda")
     se = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     for i in range(steps):
         se[i][0].record(stream)
@@ -335,7 +337,7 @@ def decode_bench(steps: int, warmup: int):
         se[i][1].record(stream)
         E.engram_gather(gw.table, gw.rows, gw.row_format, w.row_dim, rows, T * S, e)
         se[i][2].record(stream)
-        E.engram_project(e, gw.wkv, kv, T, K_in, N_out, 0)
+        E.engram_project(e, gw.wkv, kv, T, K_in, N_out, 0, pws, pws_n)
         se[i][3].record(stream)
         E.engram_gate(gw.desc, gw.ids, w.raw_vocab, kv, gw.q_w, gw.k_w, gw.h, gates)
         se[i][4].record(stream)

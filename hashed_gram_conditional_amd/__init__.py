@@ -11,5 +11,6 @@ from ._binding import (  # noqa: F401
     status_string, hash_params, forward_desc,
     engram_make_primes, engram_make_layer_primes, engram_check_token_map, engram_hash,
     engram_hash_layers, engram_gather,
-    engram_project, engram_gate, engram_forward_workspace_size, engram_forward,
+    engram_project, engram_project_workspace_size, engram_gate, engram_forward_workspace_size,
+    engram_forward,
 )

@@ -89,7 +89,8 @@ def _load():
         "engram_check_token_map": (ctypes.c_int, [P, I32, I32]),
         "engram_hash": (ctypes.c_int, [P, P, I64, I64, P, P, P, P]),
         "engram_gather": (ctypes.c_int, [P, I64, I32, I32, P, I64, P, P]),
-        "engram_project": (ctypes.c_int, [P, P, P, I64, I64, I64, I32, P]),
+        "engram_project": (ctypes.c_int, [P, P, P, I64, I64, I64, I32, P, SZ, P]),
+        "engram_project_workspace_size": (SZ, [I64, I64, I64, I32]),
         "engram_gate": (ctypes.c_int, [P, P, I32, P, P, P, P, P, P]),
         "engram_forward_workspace_size": (SZ, [P, P]),
         "engram_forward": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
@@ -212,10 +213,15 @@ def engram_gather(table, table_rows: int, row_format: int, row_dim: int, row_ids
                              n_ids, _ptr(out), _stream(stream)), "engram_gather")
 
 
+def engram_project_workspace_size(tokens: int, in_dim: int, out_dim: int, act_f32: int) -> int:
+    return LIB.engram_project_workspace_size(tokens, in_dim, out_dim, act_f32)
+
+
 def engram_project(e, wkv, kv, tokens: int, in_dim: int, out_dim: int, act_f32: int,
-                   stream=None):
+                   workspace=None, workspace_bytes: int = 0, stream=None):
     _check(LIB.engram_project(_ptr(e), _ptr(wkv), _ptr(kv), tokens, in_dim, out_dim, act_f32,
-                              _stream(stream)), "engram_project")
+                              _ptr(workspace), workspace_bytes, _stream(stream)),
+           "engram_project")
 
 
 def engram_gate(desc: ForwardDesc, ids, raw_vocab: int, kv, q_w, k_w, h, gate_out,

@@ -62,7 +62,11 @@ hipError_t engram_launch_gather_f32(const float *table, int64_t table_rows,
                                     int64_t n_ids, float *out, hipStream_t stream);
 
 hipError_t engram_launch_gemm_bf16(const uint16_t *e, const uint16_t *w, uint16_t *kv,
-                                   int64_t m, int64_t n, int64_t k, hipStream_t stream);
+                                   int64_t m, int64_t n, int64_t k, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
+// Workspace the bf16 projection uses for a split-K schedule (0 when none).
+hipError_t engram_gemm_bf16_workspace(int64_t m, int64_t n, int64_t k, size_t *bytes);
 
 hipError_t engram_launch_gemm_f32(const float *e, const float *w, float *kv, int64_t m,
                                   int64_t n, int64_t k, hipStream_t stream);

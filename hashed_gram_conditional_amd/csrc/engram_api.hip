@@ -290,8 +290,17 @@ int engram_gather(const void *table, int64_t table_rows, int32_t row_format, int
   return hip_status(e);
 }
 
+size_t engram_project_workspace_size(int64_t tokens, int64_t in_dim, int64_t out_dim,
+                                     int32_t act_f32) {
+  if (act_f32 != 0 || tokens <= 0 || in_dim < 1 || out_dim < 1) return 0;
+  size_t bytes = 0;
+  if (engram_gemm_bf16_workspace(tokens, out_dim, in_dim, &bytes) != hipSuccess) return 0;
+  return bytes;
+}
+
 int engram_project(const void *e, const void *wkv, void *kv, int64_t tokens, int64_t in_dim,
-                   int64_t out_dim, int32_t act_f32, hipStream_t stream) {
+                   int64_t out_dim, int32_t act_f32, void *workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
   if (tokens < 0 || in_dim < 1 || out_dim < 1) return ENGRAM_ESHAPE;
   if (act_f32 != 0 && act_f32 != 1) return ENGRAM_EINVAL;
   if (act_f32) {
@@ -303,11 +312,16 @@ int engram_project(const void *e, const void *wkv, void *kv, int64_t tokens, int
   if (tokens == 0) return ENGRAM_OK;
   if (e == nullptr || wkv == nullptr || kv == nullptr) return ENGRAM_EINVAL;
   if (!aligned(e, 16) || !aligned(wkv, 16) || !aligned(kv, 16)) return ENGRAM_EINVAL;
+  if (workspace != nullptr) {
+    if (!aligned(workspace, 256) ||
+        workspace_bytes < engram_project_workspace_size(tokens, in_dim, out_dim, act_f32))
+      return ENGRAM_EWORKSPACE;
+  }
   hipError_t err = act_f32 ? engram_launch_gemm_f32((const float *)e, (const float *)wkv,
                                                     (float *)kv, tokens, out_dim, in_dim, stream)
                            : engram_launch_gemm_bf16((const uint16_t *)e, (const uint16_t *)wkv,
                                                      (uint16_t *)kv, tokens, out_dim, in_dim,
-                                                     stream);
+                                                     workspace, workspace_bytes, stream);
   return hip_status(err);
 }
 
@@ -335,9 +349,13 @@ size_t engram_forward_workspace_size(const engram_hash_params *params,
   if (check_hash_params(params) != ENGRAM_OK || check_desc(desc) != ENGRAM_OK) return 0;
   const int64_t ntok = desc->batch * desc->seq;
   const int64_t S = (int64_t)(params->max_ngram - 1) * params->heads;
-  const size_t esz = desc->row_format == ENGRAM_ROW_F32 ? 4 : 2;
-  return align256((size_t)ntok * S * 8) + align256((size_t)ntok * S * desc->row_dim * esz) +
-         align256((size_t)ntok * (desc->hc + 1) * desc->dim * esz);
+  const bool f32 = desc->row_format == ENGRAM_ROW_F32;
+  const size_t esz = f32 ? 4 : 2;
+  const int64_t in_dim = S * desc->row_dim;
+  const int64_t out_dim = (int64_t)(desc->hc + 1) * desc->dim;
+  return align256((size_t)ntok * S * 8) + align256((size_t)ntok * in_dim * esz) +
+         align256((size_t)ntok * out_dim * esz) +
+         engram_project_workspace_size(ntok, in_dim, out_dim, f32 ? 1 : 0);
 }
 
 int engram_forward(const engram_hash_params *params, const engram_forward_desc *desc,
@@ -375,6 +393,8 @@ int engram_forward(const engram_hash_params *params, const engram_forward_desc *
   int64_t *row_ids = (int64_t *)ws;
   void *e = ws + align256((size_t)ntok * S * 8);
   void *kv = (char *)e + align256((size_t)ntok * in_dim * esz);
+  char *gemm_ws = (char *)kv + align256((size_t)ntok * out_dim * esz);
+  const size_t gemm_ws_bytes = workspace_bytes - (size_t)(gemm_ws - ws);
 
   const EngramHashArgs a = make_hash_args(params, 1);
   hipError_t err = engram_launch_hash(a, params->token_map, ids, desc->batch, desc->seq,
@@ -388,7 +408,8 @@ int engram_forward(const engram_hash_params *params, const engram_forward_desc *
   err = f32 ? engram_launch_gemm_f32((const float *)e, (const float *)wkv, (float *)kv, ntok,
                                      out_dim, in_dim, stream)
             : engram_launch_gemm_bf16((const uint16_t *)e, (const uint16_t *)wkv,
-                                      (uint16_t *)kv, ntok, out_dim, in_dim, stream);
+                                      (uint16_t *)kv, ntok, out_dim, in_dim, gemm_ws,
+                                      gemm_ws_bytes, stream);
   if (err != hipSuccess) return hip_status(err);
   err = engram_launch_gate(f32, ids, params->raw_vocab, kv, q_w, k_w, h, gate_out, ntok,
                            desc->hc, desc->dim, desc->eps, desc->gate_clamp, stream);

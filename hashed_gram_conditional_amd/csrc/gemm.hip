@@ -78,14 +78,24 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rs, int voff, int
   return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
 }
 
-__global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_bf16_kernel(const uint16_t *__restrict__ E, const uint16_t *__restrict__ W,
-                      uint16_t *__restrict__ C, int M, int N, int K, int tiles_m, int tiles_n) {
-  constexpr int BN = 256;
-  __shared__ __align__(1024) uint16_t sW[2][BN * BK];
-  __shared__ __align__(1024) uint16_t sE[2][BM * BK];
-  int m0, n0;
-  tile_origin(tiles_m, tiles_n, BN, m0, n0);
+constexpr int BN = 256;          // wide tile width
+constexpr int kWideOutputs = 256; // accumulators per thread of a wide tile
+
+struct WideLds {
+  uint16_t w[2][BN * BK];
+  uint16_t e[2][BM * BK];
+};
+
+// K-steps [ks, ke) of the wide tile at (m0, n0), accumulated into acc (which
+// the caller zeroes). Starts with a block barrier, so the LDS stages may be
+// reused from a previous tile. Loads of steps at or past ke read other rows of
+// the panel or zeros and are never used.
+__device__ __forceinline__ void wide_tile(const uint16_t *__restrict__ E,
+                                          const uint16_t *__restrict__ W, int M, int N, int K,
+                                          int m0, int n0, int ks, int ke, f32x16 (&acc)[4][4],
+                                          WideLds &lds) {
+  uint16_t (*sW)[BN * BK] = lds.w;
+  uint16_t (*sE)[BM * BK] = lds.e;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // 0..3
@@ -114,14 +124,6 @@ void gemm_bf16_kernel(const uint16_t *__restrict__ E, const uint16_t *__restrict
   const int a_base = (wn * 128 + frow) * BK;
   const int b_base = (wm * 128 + frow) * BK;
 
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  const int KT = K / BK;
   uint4 g0[16], g1[16];
 
 // Quarter q of a step's chunks: loads, then LDS stores.
@@ -163,10 +165,12 @@ void gemm_bf16_kernel(const uint16_t *__restrict__ E, const uint16_t *__restrict
   }
 
   bf16x8 a0[4], b0[4], a1[4], b1[4];
-  // Prologue: step 0 into stage 0, step 1 in flight. Loads of steps at or past
-  // KT read other rows of the panel or zeros and are never stored.
-  ENGRAM_LOADQ(g0, 0, 0) ENGRAM_LOADQ(g0, 0, 1) ENGRAM_LOADQ(g0, 0, 2) ENGRAM_LOADQ(g0, 0, 3)
-  ENGRAM_LOADQ(g1, 1, 0) ENGRAM_LOADQ(g1, 1, 1) ENGRAM_LOADQ(g1, 1, 2) ENGRAM_LOADQ(g1, 1, 3)
+  // Prologue: step ks into stage 0, step ks+1 in flight; every wave is done
+  // with the stages first.
+  __syncthreads();
+  ENGRAM_LOADQ(g0, ks, 0) ENGRAM_LOADQ(g0, ks, 1) ENGRAM_LOADQ(g0, ks, 2) ENGRAM_LOADQ(g0, ks, 3)
+  ENGRAM_LOADQ(g1, ks + 1, 0) ENGRAM_LOADQ(g1, ks + 1, 1) ENGRAM_LOADQ(g1, ks + 1, 2)
+  ENGRAM_LOADQ(g1, ks + 1, 3)
   ENGRAM_STOREQ(g0, 0, 0) ENGRAM_STOREQ(g0, 0, 1) ENGRAM_STOREQ(g0, 0, 2) ENGRAM_STOREQ(g0, 0, 3)
   ENGRAM_LDS_BARRIER();
   ENGRAM_FRAGS(0, 0, a0, b0);
@@ -210,14 +214,14 @@ void gemm_bf16_kernel(const uint16_t *__restrict__ E, const uint16_t *__restrict
     ENGRAM_FENCE();                                                                         \
   }
   // Two steps per iteration keep the register double buffers g0 / g1 static.
-  int kt = 0;
-  for (; kt + 1 < KT; kt += 2) {
+  int kt = ks;
+  for (; kt + 1 < ke; kt += 2) {
     ENGRAM_STEP(0, 1, g0, g1);
     ++kt;
     ENGRAM_STEP(1, 0, g1, g0);
     --kt;
   }
-  if (kt < KT) ENGRAM_STEP(0, 1, g0, g1);
+  if (kt < ke) ENGRAM_STEP(0, 1, g0, g1);
 #undef ENGRAM_STEP
 #undef ENGRAM_SUBSTEP_ORDER
 #undef ENGRAM_GROUP
@@ -228,8 +232,18 @@ void gemm_bf16_kernel(const uint16_t *__restrict__ E, const uint16_t *__restrict
 #undef ENGRAM_STOREQ
 #undef ENGRAM_LOADQ
 
-  // Epilogue: accumulator r of tile (i, j) is output column
-  // n0 + wn*128 + i*32 + (r/4)*8 + (lane/32)*4 + r%4 of token m0 + wm*128 + j*32 + lane%32.
+}
+
+// bf16 store of a finished wide tile. Accumulator r of tile (i, j) is output
+// column n0 + wn*128 + i*32 + (r/4)*8 + (lane/32)*4 + r%4 of token
+// m0 + wm*128 + j*32 + lane%32.
+__device__ __forceinline__ void wide_store_bf16(const f32x16 (&acc)[4][4],
+                                                uint16_t *__restrict__ C, int M, int N, int m0,
+                                                int n0) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wn = wave >> 1, wm = wave & 1;
+  const int frow = lane & 31, fk = lane >> 5;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int m = m0 + wm * 128 + j * 32 + frow;
@@ -251,26 +265,153 @@ void gemm_bf16_kernel(const uint16_t *__restrict__ E, const uint16_t *__restrict
   }
 }
 
-template <int BN>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+}
+
+__global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_bf16_kernel(const uint16_t *__restrict__ E, const uint16_t *__restrict__ W,
+                      uint16_t *__restrict__ C, int M, int N, int K, int tiles_m, int tiles_n) {
+  __shared__ __align__(1024) WideLds lds;
+  int m0, n0;
+  tile_origin(tiles_m, tiles_n, BN, m0, n0);
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  wide_tile(E, W, M, N, K, m0, n0, 0, K / BK, acc, lds);
+  wide_store_bf16(acc, C, M, N, m0, n0);
+}
+
+// ---- stream-K schedule for calls with fewer wide tiles than CUs ----------------
+// The (tile, K-step) units, tile-major, are dealt to G persistent blocks in
+// equal contiguous ranges: block b owns units [floor(b U / G), floor((b+1) U / G)).
+// A tile a block covers whole is stored as bf16 at once. A tile split between
+// blocks leaves one fp32 piece per block: a block's first piece goes to its
+// slot 0 and its last to slot 1 (the pieces between are whole tiles). The
+// fixup kernel then sums a tile's pieces in block order, so every result is
+// reproducible for a given shape and CU count.
+struct StreamK {
+  int64_t units;      // tiles * KT
+  int blocks;         // G
+  int kt;             // K-steps per tile
+  int tiles_m;
+  __device__ __forceinline__ int64_t start(int b) const { return (int64_t)b * units / blocks; }
+  // the block owning unit x: the largest b with start(b) <= x
+  __device__ __forceinline__ int owner(int64_t x) const {
+    const int64_t b = ((x + 1) * blocks + units - 1) / units - 1;
+    return (int)(b < blocks - 1 ? b : blocks - 1);
+  }
+};
+
+// Partial accumulators, thread-major per register so that one store
+// instruction of a wave covers 256 contiguous bytes: value r of thread t of
+// slot s of block b sits at ws[((b * 2 + s) * kWideOutputs + r) * kWideThreads + t].
+__device__ __forceinline__ float *piece_slot(float *ws, int b, int s) {
+  return ws + ((int64_t)(b * 2 + s) * kWideOutputs) * kWideThreads;
+}
+
+__global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_bf16_streamk_kernel(const uint16_t *__restrict__ E, const uint16_t *__restrict__ W,
+                              uint16_t *__restrict__ C, float *__restrict__ ws, int M, int N,
+                              int K, StreamK sk) {
+  __shared__ __align__(1024) WideLds lds;
+  const int b = blockIdx.x;
+  const int64_t u0 = sk.start(b), u1 = sk.start(b + 1);
+  const int tid = threadIdx.x;
+  f32x16 acc[4][4];
+  for (int64_t u = u0; u < u1;) {
+    const int64_t tile = u / sk.kt;
+    const int ks = (int)(u - tile * sk.kt);
+    const int ke = (int)min((int64_t)sk.kt, (int64_t)ks + (u1 - u));
+    const int m0 = (int)(tile % sk.tiles_m) * BM;
+    const int n0 = (int)(tile / sk.tiles_m) * BN;
+    zero_acc(acc);
+    wide_tile(E, W, M, N, K, m0, n0, ks, ke, acc, lds);
+    if (ks == 0 && ke == sk.kt) {
+      wide_store_bf16(acc, C, M, N, m0, n0);
+    } else {
+      float *dst = piece_slot(ws, b, u == u0 ? 0 : 1) + tid;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dst[((i * 4 + j) * 16 + r) * kWideThreads] = acc[i][j][r];
+    }
+    u += ke - ks;
+  }
+}
+
+// Sums the pieces of a split tile in block order and stores bf16. Block
+// (tile, part) handles accumulator registers [part * 16, part * 16 + 16) of
+// all 256 threads of the tile: four quads of consecutive output columns per
+// thread, loads coalesced across threads. Tiles one block finished whole exit
+// at once.
+constexpr int kFixupRegs = 16;
+constexpr int kFixupParts = kWideOutputs / kFixupRegs;
+
+__global__ __launch_bounds__(kWideThreads) void gemm_streamk_fixup_kernel(
+    const float *__restrict__ ws, uint16_t *__restrict__ C, int M, int N, StreamK sk) {
+  const int64_t tile = blockIdx.x / kFixupParts;
+  const int part = blockIdx.x % kFixupParts;
+  const int first = sk.owner(tile * sk.kt);
+  const int last = sk.owner((tile + 1) * sk.kt - 1);
+  if (first == last) return;
+  const int t = threadIdx.x;
+  float v[kFixupRegs];
+#pragma unroll
+  for (int q = 0; q < kFixupRegs; ++q) v[q] = 0.f;
+  for (int b = first; b <= last; ++b) {
+    // block b's piece of this tile is its first one iff its range starts here
+    const int slot = (sk.start(b) / sk.kt == tile) ? 0 : 1;
+    const float *src = piece_slot(const_cast<float *>(ws), b, slot) +
+                       (int64_t)part * kFixupRegs * kWideThreads + t;
+#pragma unroll
+    for (int q = 0; q < kFixupRegs; ++q) v[q] += src[q * kWideThreads];
+  }
+  // register index (i*4 + j)*16 + r, r in [0, 16): part = i*4 + j
+  const int i = part >> 2, j = part & 3;
+  const int lane = t & 63, wave = t >> 6;
+  const int wn = wave >> 1, wm = wave & 1;
+  const int m = (int)(tile % sk.tiles_m) * BM + wm * 128 + j * 32 + (lane & 31);
+  if (m >= M) return;
+  uint16_t *crow = C + (int64_t)m * N;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int n = (int)(tile / sk.tiles_m) * BN + wn * 128 + i * 32 + g * 8 + (lane >> 5) * 4;
+    if (n < N) {
+      uint2 o;
+      o.x = engram::pack_bf16x2(v[g * 4 + 0], v[g * 4 + 1]);
+      o.y = engram::pack_bf16x2(v[g * 4 + 2], v[g * 4 + 3]);
+      *reinterpret_cast<uint2 *>(crow + n) = o;
+    }
+  }
+}
+
+template <int TN>
 __global__ __launch_bounds__(kNarrowThreads) void gemm_bf16_narrow_kernel(
     const uint16_t *__restrict__ E, const uint16_t *__restrict__ W, uint16_t *__restrict__ C,
     int M, int N, int K, int tiles_m, int tiles_n) {
-  constexpr int TI = BN / 64;          // 32-row MFMA tiles per wave along n
-  constexpr int WR = BN / 64;          // W-panel direct loads per wave per stage
-  __shared__ __align__(1024) uint16_t sW0[BN * BK];
-  __shared__ __align__(1024) uint16_t sW1[BN * BK];
+  constexpr int TI = TN / 64;          // 32-row MFMA tiles per wave along n
+  constexpr int WR = TN / 64;          // W-panel direct loads per wave per stage
+  __shared__ __align__(1024) uint16_t sW0[TN * BK];
+  __shared__ __align__(1024) uint16_t sW1[TN * BK];
   __shared__ __align__(1024) uint16_t sE0[BM * BK];
   __shared__ __align__(1024) uint16_t sE1[BM * BK];
 
   int m0, n0;
-  tile_origin(tiles_m, tiles_n, BN, m0, n0);
+  tile_origin(tiles_m, tiles_n, TN, m0, n0);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // 0..7
-  const int wn = wave >> 2;        // which BN/2 output columns
+  const int wn = wave >> 2;        // which TN/2 output columns
   const int wm = wave & 3;         // which 64 tokens
 
-  const int rows_w = min(BN, N - n0);
+  const int rows_w = min(TN, N - n0);
   const int rows_e = min(BM, M - m0);
   const __amdgpu_buffer_rsrc_t rsW = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(W + (int64_t)n0 * K), 0, rows_w * K * 2, kBufferFlags);
@@ -291,7 +432,7 @@ __global__ __launch_bounds__(kNarrowThreads) void gemm_bf16_narrow_kernel(
   const int frow = lane & 31;
   const int fk = lane >> 5;
   const int fsw = (frow & 7) ^ ((frow >> 3) & 1);
-  const int a_base = (wn * (BN / 2) + frow) * BK;
+  const int a_base = (wn * (TN / 2) + frow) * BK;
   const int b_base = (wm * 64 + frow) * BK;
 
   f32x16 acc[TI][2];
@@ -370,7 +511,7 @@ __global__ __launch_bounds__(kNarrowThreads) void gemm_bf16_narrow_kernel(
 #undef ENGRAM_SCHED
 
   // ---- epilogue: accumulator r of tile (i, j) is output column
-  // n0 + wn*BN/2 + i*32 + (r/4)*8 + (lane/32)*4 + r%4 of token m0 + wm*64 + j*32 + lane%32.
+  // n0 + wn*TN/2 + i*32 + (r/4)*8 + (lane/32)*4 + r%4 of token m0 + wm*64 + j*32 + lane%32.
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int m = m0 + wm * 64 + j * 32 + frow;
@@ -380,7 +521,7 @@ __global__ __launch_bounds__(kNarrowThreads) void gemm_bf16_narrow_kernel(
     for (int i = 0; i < TI; ++i) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * (BN / 2) + i * 32 + g * 8 + fk * 4;
+        const int n = n0 + wn * (TN / 2) + i * 32 + g * 8 + fk * 4;
         if (n < N) {
           uint2 v;
           v.x = engram::pack_bf16x2(acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1]);
@@ -410,25 +551,72 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *__restrict__
 
 }  // namespace
 
-hipError_t engram_launch_gemm_bf16(const uint16_t *e, const uint16_t *w, uint16_t *kv,
-                                   int64_t m, int64_t n, int64_t k, hipStream_t stream) {
-  if (m <= 0 || n <= 0) return hipSuccess;
-  int dev = 0, cus = 256;
+namespace {
+
+hipError_t cu_count(int &cus) {
+  int dev = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  return err;
+}
+
+// The stream-K schedule of a call, or blocks = 0 when whole wide tiles fill the CUs.
+hipError_t plan_streamk(int64_t m, int64_t n, int64_t k, StreamK &sk) {
+  int cus = 0;
+  const hipError_t err = cu_count(cus);
   if (err != hipSuccess) return err;
-  const int tiles_m = (int)((m + BM - 1) / BM);
-  const int tiles_n256 = (int)((n + 255) / 256);
-  if ((int64_t)tiles_m * tiles_n256 >= cus) {
+  const int64_t tiles_m = (m + BM - 1) / BM;
+  const int64_t tiles = tiles_m * ((n + BN - 1) / BN);
+  sk.tiles_m = (int)tiles_m;
+  sk.kt = (int)(k / BK);
+  sk.units = tiles * sk.kt;
+  sk.blocks = tiles >= cus ? 0 : (int)(sk.units < cus ? sk.units : cus);
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t engram_gemm_bf16_workspace(int64_t m, int64_t n, int64_t k, size_t *bytes) {
+  *bytes = 0;
+  if (m <= 0 || n <= 0) return hipSuccess;
+  StreamK sk;
+  const hipError_t err = plan_streamk(m, n, k, sk);
+  if (err != hipSuccess) return err;
+  *bytes = (size_t)sk.blocks * 2 * kWideOutputs * kWideThreads * sizeof(float);
+  return hipSuccess;
+}
+
+hipError_t engram_launch_gemm_bf16(const uint16_t *e, const uint16_t *w, uint16_t *kv,
+                                   int64_t m, int64_t n, int64_t k, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  if (m <= 0 || n <= 0) return hipSuccess;
+  StreamK sk;
+  hipError_t err = plan_streamk(m, n, k, sk);
+  if (err != hipSuccess) return err;
+  const int tiles_m = sk.tiles_m;
+  const int tiles_n256 = (int)((n + BN - 1) / BN);
+  if (sk.blocks == 0) {
     hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)(tiles_m * tiles_n256)),
                        dim3(kWideThreads), 0, stream, e, w, kv, (int)m, (int)n, (int)k, tiles_m,
                        tiles_n256);
-  } else {
-    const int tiles_n128 = (int)((n + 127) / 128);
-    hipLaunchKernelGGL(gemm_bf16_narrow_kernel<128>, dim3((unsigned)(tiles_m * tiles_n128)),
-                       dim3(kNarrowThreads), 0, stream, e, w, kv, (int)m, (int)n, (int)k,
-                       tiles_m, tiles_n128);
+    return hipGetLastError();
   }
+  const size_t need = (size_t)sk.blocks * 2 * kWideOutputs * kWideThreads * sizeof(float);
+  if (workspace != nullptr && workspace_bytes >= need) {
+    hipLaunchKernelGGL(gemm_bf16_streamk_kernel, dim3((unsigned)sk.blocks), dim3(kWideThreads), 0,
+                       stream, e, w, kv, (float *)workspace, (int)m, (int)n, (int)k, sk);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(gemm_streamk_fixup_kernel,
+                       dim3((unsigned)(tiles_m * tiles_n256 * kFixupParts)), dim3(kWideThreads),
+                       0, stream, (const float *)workspace, kv, (int)m, (int)n, sk);
+    return hipGetLastError();
+  }
+  // No workspace: 128-wide tiles over the whole K.
+  const int tiles_n128 = (int)((n + 127) / 128);
+  hipLaunchKernelGGL(gemm_bf16_narrow_kernel<128>, dim3((unsigned)(tiles_m * tiles_n128)),
+                     dim3(kNarrowThreads), 0, stream, e, w, kv, (int)m, (int)n, (int)k, tiles_m,
+                     tiles_n128);
   return hipGetLastError();
 }
 

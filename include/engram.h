@@ -227,12 +227,27 @@ int engram_gather(const void *table, int64_t table_rows, int32_t row_format,
  *   wkv  [out_dim, in_dim]      same type; row c holds the weights of output c
  *   kv   [tokens, out_dim]      same type; fp32 accumulation, bf16 rounded to
  *                               nearest-even
+ *   workspace, workspace_bytes
+ *        NULL, or at least engram_project_workspace_size bytes, 256-byte
+ *        aligned. With fewer 256 x 256 output tiles than the GPU has CUs
+ *        (small token counts: decode) a bf16 call splits K over the CUs and
+ *        keeps fp32 partial tiles there, summed afterwards in a fixed order
+ *        (the result depends only on the shape and the CU count); with NULL it
+ *        uses narrower tiles over the whole K instead. Contents need not be
+ *        initialised and are clobbered.
  * bf16 requires in_dim % 64 == 0 and out_dim % 8 == 0; fp32 requires in_dim % 4
  * == 0 and out_dim % 4 == 0.
- * Errors: ENGRAM_EINVAL, ENGRAM_ESHAPE, ENGRAM_EHIP.
+ * Errors: ENGRAM_EINVAL, ENGRAM_ESHAPE, ENGRAM_EWORKSPACE (non-NULL and too
+ * small or misaligned), ENGRAM_EHIP.
  */
 int engram_project(const void *e, const void *wkv, void *kv, int64_t tokens,
-                   int64_t in_dim, int64_t out_dim, int32_t act_f32, hipStream_t stream);
+                   int64_t in_dim, int64_t out_dim, int32_t act_f32, void *workspace,
+                   size_t workspace_bytes, hipStream_t stream);
+
+/* [host] Bytes of workspace engram_project uses for these sizes on the current
+ * device (0 if it needs none, on bad arguments or on a HIP error). */
+size_t engram_project_workspace_size(int64_t tokens, int64_t in_dim, int64_t out_dim,
+                                     int32_t act_f32);
 
 /*
  * Step 5: gate and residual update, given kv.
@@ -250,7 +265,8 @@ int engram_gate(const engram_forward_desc *desc, const int32_t *ids, int32_t raw
                 const void *kv, const float *q_w, const float *k_w, void *h,
                 float *gate_out, hipStream_t stream);
 
-/* Bytes of workspace engram_forward needs (row ids, e and kv), or 0 on bad args. */
+/* Bytes of workspace engram_forward needs (row ids, e, kv and the projection's
+ * workspace), or 0 on bad args. */
 size_t engram_forward_workspace_size(const engram_hash_params *params,
                                      const engram_forward_desc *desc);
 

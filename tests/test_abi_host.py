@@ -163,10 +163,12 @@ def test_gather_project_gate_validation():
     assert L.engram_gather(0x1000, 10, 0, 256, 0x2004, 4, 0x3000, None) == E.EINVAL
     assert L.engram_gather(0x1000, 10, 1, 30, 0x2000, 4, 0x3000, None) == E.ESHAPE
     assert L.engram_gather(None, 0, 0, 256, None, 0, None, None) == E.OK      # empty
-    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, 100, 64, 0, None) == E.ESHAPE
-    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, 128, 60, 0, None) == E.ESHAPE
-    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, 128, 64, 2, None) == E.EINVAL
-    assert L.engram_project(0x1008, 0x2000, 0x3000, 4, 128, 64, 0, None) == E.EINVAL
+    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, 100, 64, 0, None, 0, None) == E.ESHAPE
+    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, 128, 60, 0, None, 0, None) == E.ESHAPE
+    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, 128, 64, 2, None, 0, None) == E.EINVAL
+    assert L.engram_project(0x1008, 0x2000, 0x3000, 4, 128, 64, 0, None, 0, None) == E.EINVAL
+    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, 128, 64, 0, 0x4010, 1 << 30, None) \
+        == E.EWORKSPACE                                              # not 256-aligned
     d = E.forward_desc(1, 4, 4, 5120, 100, 0, 256)
     bad = E.forward_desc(1, 4, 9, 5120, 100, 0, 256)
     assert L.engram_gate(ctypes.byref(bad), 0x1000, 10, 0x2000, 0x3000, 0x4000, 0x5000, None,
