@@ -326,6 +326,36 @@ def dequant_rows_bf16(row_bytes: np.ndarray) -> np.ndarray:
     return round_to_bf16_bits(val)
 
 
+def mx_values(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Block-scaled FP8 values: element k of a row is E4M3(code[k]) times
+    E8M0(scale[k // 32]), exact in float64.
+
+    [P4] "永不常驻的 I/O 设计": the encoding e4m3_e8m0_32 (32 elements share
+    one E8M0 scale); [P3] §2.3: the projection weight is block-FP8 beside the
+    table's e4m3 + e8m0 rows. Reading: the weight uses the table's own block
+    encoding, one scale per 32 consecutive inputs of an output row.
+    codes uint8 [..., K], scales uint8 [..., K/32].
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    assert codes.shape[-1] == 32 * scales.shape[-1]
+    return E4M3_TABLE[codes] * np.repeat(E8M0_TABLE[scales], 32, axis=-1)
+
+
+def gather_rows(fetch_rows: Callable[[np.ndarray], np.ndarray], row_ids: np.ndarray,
+                table_rows: int) -> np.ndarray:
+    """The looked-up rows themselves, bytes unchanged: uint8 [T, S, 264], all
+    zeros for ids outside [0, R) ([P3] §五: such rows output zero rows)."""
+    row_ids = np.asarray(row_ids, dtype=np.int64)
+    T, S = row_ids.shape
+    flat = row_ids.reshape(-1)
+    ok = (flat >= 0) & (flat < table_rows)
+    out = np.zeros((flat.size, 264), dtype=np.uint8)
+    if ok.any():
+        out[ok] = fetch_rows(flat[ok])
+    return out.reshape(T, S, 264)
+
+
 def gather_e4m3(fetch_rows: Callable[[np.ndarray], np.ndarray], row_ids: np.ndarray,
                 table_rows: int) -> np.ndarray:
     """e[t, j*256:(j+1)*256] = dequant(table[row_ids[t, j]]), zeros outside [0, R)

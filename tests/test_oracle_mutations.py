@@ -96,6 +96,14 @@ def _project_transposed(e, wkv):
     return np.asarray(e, dtype=np.float64) @ w.T[::-1]
 
 
+def _mx_block16(codes, scales):
+    """Wrong: one scale per 16 elements, the first half of the scales reused."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    sc = np.asarray(scales, dtype=np.uint8)
+    per16 = np.repeat(E.E8M0_TABLE[sc], 16, axis=-1)
+    return E.E4M3_TABLE[codes] * np.concatenate([per16, per16], axis=-1)[..., :codes.shape[-1]]
+
+
 def _layer_offsets_continue(base, layers, per_layer):
     """Wrong: one offset sequence over all layers instead of one table per layer."""
     p = E.primes_from(base, layers * per_layer)
@@ -122,7 +130,7 @@ def _layers_share_multipliers(ids, token_map, compressed_vocab, pad, multipliers
 
 _orig = {name: getattr(E, name) for name in
          ("mix_values", "segment_offsets", "primes_from", "ngram_cells", "gate", "project",
-          "round_to_bf16_bits", "layer_primes", "hash_rows_layers")}
+          "round_to_bf16_bits", "layer_primes", "hash_rows_layers", "mx_values")}
 
 MUTATIONS = [
     ("mix_values", _mix_oldest_first, [P.test_worked_example_mix_and_indices]),
@@ -140,6 +148,7 @@ MUTATIONS = [
     ("layer_primes", _layer_primes_restart, [P.test_layer_primes_match_both_layers_table]),
     ("hash_rows_layers", _layers_share_multipliers,
      [P.test_layers_with_own_multipliers_hit_unrelated_rows]),
+    ("mx_values", _mx_block16, [P.test_mx_values_one_scale_per_32_inputs]),
 ]
 
 

@@ -130,6 +130,41 @@ def test_layers_with_own_multipliers_hit_unrelated_rows():
     assert np.array_equal(same[0], same[1])
 
 
+def test_mx_values_one_scale_per_32_inputs():
+    # code 0x38 is 1.0; block b carries scale 127 + b - 4, so element k is 2^(k//32 - 4)
+    K = 256
+    codes = np.full((3, K), 0x38, np.uint8)
+    codes[1] = 0xB8                                   # -1.0
+    codes[2, ::2] = 0x00                              # +0
+    scales = np.tile(np.arange(123, 131, dtype=np.uint8), (3, 1))
+    v = O.mx_values(codes, scales)
+    expect = np.exp2(np.arange(K) // 32 - 4.0)
+    assert np.array_equal(v[0], expect)
+    assert np.array_equal(v[1], -expect)
+    assert np.array_equal(v[2, 1::2], expect[1::2]) and not v[2, ::2].any()
+
+
+def test_mx_values_equal_the_table_rows_dequant():
+    # a table row is one MX block row of 256: its bytes give the same values
+    rng = np.random.default_rng(21)
+    rows = gen.table_rows(77, rng.integers(0, 10 ** 8, 64))
+    v = O.mx_values(rows[:, :256], rows[:, 256:])
+    assert np.array_equal(v, O.bf16_bits_to_f64(O.dequant_rows_bf16(rows)))
+
+
+def test_gather_rows_are_the_table_bytes():
+    rng = np.random.default_rng(22)
+    R = 1000
+    ids = rng.integers(-3, R + 3, (5, 6))
+    fetch = lambda r: gen.table_rows(9, r)
+    raw = O.gather_rows(fetch, ids, R)
+    ok = (ids >= 0) & (ids < R)
+    assert np.array_equal(raw[ok], gen.table_rows(9, ids[ok]))
+    assert not raw[~ok].any()
+    deq = O.bf16_bits_to_f64(O.dequant_rows_bf16(raw.reshape(-1, 264))).reshape(5, -1)
+    assert np.array_equal(deq, O.bf16_bits_to_f64(O.gather_e4m3(fetch, ids, R)))
+
+
 def test_primes_against_sympy():
     for base, count in ((1009, 6), (1_000_000, 24), (16_000_000, 30), (2, 10), (90, 5)):
         got = O.primes_from(base, count)

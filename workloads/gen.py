@@ -44,7 +44,7 @@ SCALE_CHOICES = 15
 
 # child stream index of each tensor
 S_TOKEN_MAP, S_MULT, S_ZIPF_PERM, S_IDS, S_DEAD, S_TABLE_F32, S_WKV, S_QW, S_KW, \
-    S_H, S_HIST, S_MULT_LAYERS = range(12)
+    S_H, S_HIST, S_MULT_LAYERS, S_WKV_MX = range(13)
 
 _CHUNK = 1 << 22
 
@@ -182,6 +182,67 @@ def layer_multipliers(w: EngramWorkload, layers: int) -> list:
     _, first = hash_setup(w)
     rng = _rng(w.setup_seed, S_MULT_LAYERS)
     return [first] + [multipliers(w.compressed_vocab, w.max_ngram, rng) for _ in range(layers - 1)]
+
+
+_E4M3_POS = None
+
+
+def _e4m3_positive_grid():
+    """The 126 positive finite E4M3FN values (codes 0x01..0x7E), ascending."""
+    global _E4M3_POS
+    if _E4M3_POS is None:
+        vals = []
+        for c in range(1, 0x7F):
+            e, m = (c >> 3) & 15, c & 7
+            vals.append(2.0 ** -6 * m / 8 if e == 0 else 2.0 ** (e - 7) * (1 + m / 8))
+        _E4M3_POS = np.array(vals, dtype=np.float64)
+    return _E4M3_POS
+
+
+def quantize_mx_e4m3(x: np.ndarray):
+    """OCP MX quantisation of float rows [..., K] (K % 32 == 0) to E4M3 codes and
+    one E8M0 scale per 32 values: shared exponent floor(log2(amax)) - 8 (8 being
+    E4M3's largest exponent), each value divided by it and rounded to the
+    nearest E4M3 value, ties to the even code, saturating at 448."""
+    x = np.asarray(x, dtype=np.float64)
+    blocks = x.reshape(x.shape[:-1] + (x.shape[-1] // 32, 32))
+    amax = np.abs(blocks).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        se = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8, -127)
+    se = np.clip(se, -127, 127)
+    q = np.abs(blocks) / np.exp2(se)[..., None]
+    grid = _e4m3_positive_grid()
+    hi = np.clip(np.searchsorted(grid, q), 0, grid.size - 1)
+    lo = np.clip(hi - 1, 0, grid.size - 1)
+    dlo, dhi = q - grid[lo], grid[hi] - q
+    code_lo, code_hi = lo + 1, hi + 1
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (code_hi % 2 == 0))
+    code = np.where(pick_hi, code_hi, code_lo)
+    code = np.where(q < grid[0] / 2, 0, code)                    # rounds to zero
+    code = np.where(q > grid[-1], grid.size, code)               # saturate at 448
+    code = code | (np.signbit(blocks).astype(np.int64) << 7)
+    codes = code.astype(np.uint8).reshape(x.shape)
+    scales = (se + 127).astype(np.uint8)
+    return codes, scales
+
+
+def wkv_mx(w: EngramWorkload):
+    """The projection weight in block-scaled FP8: N(0, 0.02) values of shape
+    [(hc+1) d, S * row_dim] quantised by ``quantize_mx_e4m3`` (codes, scales)."""
+    n, k = (w.hc + 1) * w.dim, w.segments * w.row_dim
+    codes = np.empty((n, k), dtype=np.uint8)
+    scales = np.empty((n, k // 32), dtype=np.uint8)
+    kids = np.random.SeedSequence(w.seed).spawn(16)[S_WKV_MX].spawn((n + 1023) // 1024)
+
+    def work(i):
+        a, b = i * 1024, min(n, (i + 1) * 1024)
+        x = np.random.default_rng(kids[i]).normal(0.0, 0.02, (b - a, k))
+        codes[a:b], scales[a:b] = quantize_mx_e4m3(x)
+
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(work, range(len(kids))))
+    return codes, scales
 
 
 def token_ids(w: EngramWorkload):
