@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 METRIC = "Engram layer tokens/s (hash+gather+gate) and gather GB/s vs HBM peak, 1 GPU"
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0         # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0          # MI355X dense fp8 MFMA
 # Algorithmic bytes per token of the gather: 24 row ids (int64) read, 24 rows of
 # 264 B read, 6144 bf16 written.
 GATHER_BYTES_PER_TOKEN = 24 * 8 + 24 * 264 + 6144 * 2
@@ -235,6 +236,7 @@ def main():
         "engram_forward_ms": round(forward_ms, 4),
     }
     out["hash_layers"] = hash_layers_bench(max(args.steps, 20))
+    out["fp8_wkv"] = fp8_prefill_bench(gw, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(gw)
@@ -245,6 +247,68 @@ def main():
         torch.cuda.empty_cache()
         out["decode"] = decode_bench(args.steps, args.warmup)
     print(json.dumps(out), flush=True)
+
+
+def fp8_prefill_bench(gw, steps: int, warmup: int):
+    """The same prefill layer with the projection weight in block-scaled FP8 (E4M3
+    values, one E8M0 scale per 32 inputs, quantised from the bf16 run's N(0, 0.02)
+    distribution): engram_hash -> engram_gather_rows -> engram_project_mx ->
+    engram_gate, per-stage HIP events as in the bf16 run."""
+    import torch
+    import hashed_gram_conditional_amd as E
+    from workloads import gen
+    from workloads.device import to_device
+
+    w = gw.w
+    T, S = w.tokens, w.segments
+    N_out = (w.hc + 1) * w.dim
+    codes, scales = gen.wkv_mx(w)
+    wc, wsc = to_device(codes), to_device(scales)
+    rows = torch.empty((T, S), dtype=torch.int64, device="cuda")
+    e_rows = torch.empty((T, S, 264), dtype=torch.uint8, device="cuda")
+    kv = torch.empty((T, N_out), dtype=torch.bfloat16, device="cuda")
+    gates = torch.empty((T, w.hc), dtype=torch.float32, device="cuda")
+    n_ws = E.engram_project_mx_workspace_size(T, S, N_out)
+    pws = torch.empty(max(n_ws, 256), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+
+    def step(evs):
+        if evs:
+            evs[0].record(stream)
+        E.engram_hash(gw.params, gw.ids, w.batch, w.seq, None, None, rows)
+        if evs:
+            evs[1].record(stream)
+        E.engram_gather_rows(gw.table, gw.rows, rows, T * S, e_rows)
+        if evs:
+            evs[2].record(stream)
+        E.engram_project_mx(e_rows, S, wc, wsc, kv, T, N_out, pws if n_ws else None, n_ws)
+        if evs:
+            evs[3].record(stream)
+        E.engram_gate(gw.desc, gw.ids, w.raw_vocab, kv, gw.q_w, gw.k_w, gw.h, gates)
+        if evs:
+            evs[4].record(stream)
+
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = np.mean([[s[j].elapsed_time(s[j + 1]) for j in range(4)] for s in ev], axis=0)
+    ms = 1e3 * wall / steps
+    tflops = 2.0 * T * N_out * S * 256 / (st[2] * 1e-3) / 1e12
+    del rows, e_rows, kv, gates, pws, wc, wsc
+    return {"workload": "prefill layer forward as above, projection weight in block-scaled FP8 "
+                        "(E4M3 + one E8M0 scale per 32 inputs), rows fed to the FP8 MFMA "
+                        "without dequantisation",
+            "tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+            "stages_ms": {"hash": round(st[0], 4), "gather_rows": round(st[1], 4),
+                          "project_mx": round(st[2], 4), "gate": round(st[3], 4)},
+            "project_mx": {"achieved": round(tflops, 2), "peak": FP8_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(tflops / FP8_PEAK_TFLOPS, 4)}}
 
 
 def hash_layers_bench(reps: int):

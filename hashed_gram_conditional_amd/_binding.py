@@ -93,6 +93,11 @@ def _load():
         "engram_project_workspace_size": (SZ, [I64, I64, I64, I32]),
         "engram_gate": (ctypes.c_int, [P, P, I32, P, P, P, P, P, P]),
         "engram_forward_workspace_size": (SZ, [P, P]),
+        "engram_gather_rows": (ctypes.c_int, [P, I64, P, I64, P, P]),
+        "engram_project_mx": (ctypes.c_int, [P, I32, P, P, P, I64, I64, P, SZ, P]),
+        "engram_project_mx_workspace_size": (SZ, [I64, I32, I64]),
+        "engram_forward_mx_workspace_size": (SZ, [P, P]),
+        "engram_forward_mx": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "engram_forward": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
@@ -241,3 +246,33 @@ def engram_forward(params: HashParams, desc: ForwardDesc, ids, hist_in, hist_out
                               _ptr(q_w), _ptr(k_w), _ptr(h), _ptr(gate_out),
                               _ptr(workspace), workspace_bytes, _stream(stream)),
            "engram_forward")
+
+
+def engram_gather_rows(table, table_rows: int, row_ids, n_ids: int, out, stream=None):
+    _check(LIB.engram_gather_rows(_ptr(table), table_rows, _ptr(row_ids), n_ids, _ptr(out),
+                                  _stream(stream)), "engram_gather_rows")
+
+
+def engram_project_mx_workspace_size(tokens: int, segments: int, out_dim: int) -> int:
+    return LIB.engram_project_mx_workspace_size(tokens, segments, out_dim)
+
+
+def engram_project_mx(e_rows, segments: int, w_codes, w_scales, kv, tokens: int, out_dim: int,
+                      workspace=None, workspace_bytes: int = 0, stream=None):
+    _check(LIB.engram_project_mx(_ptr(e_rows), segments, _ptr(w_codes), _ptr(w_scales),
+                                 _ptr(kv), tokens, out_dim, _ptr(workspace), workspace_bytes,
+                                 _stream(stream)), "engram_project_mx")
+
+
+def engram_forward_mx_workspace_size(params: HashParams, desc: ForwardDesc) -> int:
+    return LIB.engram_forward_mx_workspace_size(ctypes.byref(params), ctypes.byref(desc))
+
+
+def engram_forward_mx(params: HashParams, desc: ForwardDesc, ids, hist_in, hist_out, table,
+                      w_codes, w_scales, q_w, k_w, h, gate_out, workspace, workspace_bytes: int,
+                      stream=None):
+    _check(LIB.engram_forward_mx(ctypes.byref(params), ctypes.byref(desc), _ptr(ids),
+                                 _ptr(hist_in), _ptr(hist_out), _ptr(table), _ptr(w_codes),
+                                 _ptr(w_scales), _ptr(q_w), _ptr(k_w), _ptr(h), _ptr(gate_out),
+                                 _ptr(workspace), workspace_bytes, _stream(stream)),
+           "engram_forward_mx")

@@ -57,6 +57,10 @@ hipError_t engram_launch_gather_e4m3(const uint8_t *table, int64_t table_rows,
                                      const int64_t *row_ids, int64_t n_ids,
                                      uint16_t *out, hipStream_t stream);
 
+hipError_t engram_launch_gather_rows(const uint8_t *table, int64_t table_rows,
+                                     const int64_t *row_ids, int64_t n_ids, uint8_t *out,
+                                     hipStream_t stream);
+
 hipError_t engram_launch_gather_f32(const float *table, int64_t table_rows,
                                     int32_t row_dim, const int64_t *row_ids,
                                     int64_t n_ids, float *out, hipStream_t stream);
@@ -67,6 +71,15 @@ hipError_t engram_launch_gemm_bf16(const uint16_t *e, const uint16_t *w, uint16_
 
 // Workspace the bf16 projection uses for a split-K schedule (0 when none).
 hipError_t engram_gemm_bf16_workspace(int64_t m, int64_t n, int64_t k, size_t *bytes);
+
+// Block-scaled FP8 projection: W codes [n, 256 S] and scales [n, 8 S], e the
+// looked-up 264-byte rows [m, S, 264]; kv bf16 [m, n]. Split-K as for bf16
+// when a large enough workspace is given.
+hipError_t engram_launch_gemm_mx(const uint8_t *w_codes, const uint8_t *w_scales,
+                                 const uint8_t *e_rows, int32_t segments, uint16_t *kv,
+                                 int64_t m, int64_t n, void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+hipError_t engram_gemm_mx_workspace(int64_t m, int64_t n, int32_t segments, size_t *bytes);
 
 hipError_t engram_launch_gemm_f32(const float *e, const float *w, float *kv, int64_t m,
                                   int64_t n, int64_t k, hipStream_t stream);

@@ -290,6 +290,45 @@ int engram_gather(const void *table, int64_t table_rows, int32_t row_format, int
   return hip_status(e);
 }
 
+int engram_gather_rows(const void *table, int64_t table_rows, const int64_t *row_ids,
+                       int64_t n_ids, void *out, hipStream_t stream) {
+  if (n_ids < 0 || table_rows < 0) return ENGRAM_ESHAPE;
+  if (n_ids == 0) return ENGRAM_OK;
+  if (row_ids == nullptr || out == nullptr || (table == nullptr && table_rows > 0))
+    return ENGRAM_EINVAL;
+  if (!aligned(table, 8) || !aligned(row_ids, 8) || !aligned(out, 8)) return ENGRAM_EINVAL;
+  return hip_status(engram_launch_gather_rows((const uint8_t *)table, table_rows, row_ids,
+                                              n_ids, (uint8_t *)out, stream));
+}
+
+size_t engram_project_mx_workspace_size(int64_t tokens, int32_t segments, int64_t out_dim) {
+  if (tokens <= 0 || segments < 1 || out_dim < 1) return 0;
+  size_t bytes = 0;
+  if (engram_gemm_mx_workspace(tokens, out_dim, segments, &bytes) != hipSuccess) return 0;
+  return bytes;
+}
+
+int engram_project_mx(const void *e_rows, int32_t segments, const void *w_codes,
+                      const void *w_scales, void *kv, int64_t tokens, int64_t out_dim,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (tokens < 0 || segments < 1 || segments > ENGRAM_MAX_SEGMENTS || out_dim < 1)
+    return ENGRAM_ESHAPE;
+  if (out_dim % 8 || tokens > INT32_MAX || out_dim > INT32_MAX) return ENGRAM_ESHAPE;
+  if (tokens == 0) return ENGRAM_OK;
+  if (e_rows == nullptr || w_codes == nullptr || w_scales == nullptr || kv == nullptr)
+    return ENGRAM_EINVAL;
+  if (!aligned(e_rows, 8) || !aligned(w_codes, 16) || !aligned(w_scales, 4) || !aligned(kv, 16))
+    return ENGRAM_EINVAL;
+  if (workspace != nullptr) {
+    if (!aligned(workspace, 256) ||
+        workspace_bytes < engram_project_mx_workspace_size(tokens, segments, out_dim))
+      return ENGRAM_EWORKSPACE;
+  }
+  return hip_status(engram_launch_gemm_mx((const uint8_t *)w_codes, (const uint8_t *)w_scales,
+                                          (const uint8_t *)e_rows, segments, (uint16_t *)kv,
+                                          tokens, out_dim, workspace, workspace_bytes, stream));
+}
+
 size_t engram_project_workspace_size(int64_t tokens, int64_t in_dim, int64_t out_dim,
                                      int32_t act_f32) {
   if (act_f32 != 0 || tokens <= 0 || in_dim < 1 || out_dim < 1) return 0;
@@ -412,6 +451,69 @@ int engram_forward(const engram_hash_params *params, const engram_forward_desc *
                                       gemm_ws_bytes, stream);
   if (err != hipSuccess) return hip_status(err);
   err = engram_launch_gate(f32, ids, params->raw_vocab, kv, q_w, k_w, h, gate_out, ntok,
+                           desc->hc, desc->dim, desc->eps, desc->gate_clamp, stream);
+  return hip_status(err);
+}
+
+size_t engram_forward_mx_workspace_size(const engram_hash_params *params,
+                                        const engram_forward_desc *desc) {
+  if (check_hash_params(params) != ENGRAM_OK || check_desc(desc) != ENGRAM_OK) return 0;
+  if (desc->row_format != ENGRAM_ROW_E4M3_E8M0_264) return 0;
+  const int64_t ntok = desc->batch * desc->seq;
+  const int32_t S = (params->max_ngram - 1) * params->heads;
+  const int64_t out_dim = (int64_t)(desc->hc + 1) * desc->dim;
+  return align256((size_t)ntok * S * 8) + align256((size_t)ntok * S * ENGRAM_ROW_BYTES) +
+         align256((size_t)ntok * out_dim * 2) +
+         engram_project_mx_workspace_size(ntok, S, out_dim);
+}
+
+int engram_forward_mx(const engram_hash_params *params, const engram_forward_desc *desc,
+                      const int32_t *ids, const int32_t *hist_in, int32_t *hist_out,
+                      const void *table, const void *w_codes, const void *w_scales,
+                      const float *q_w, const float *k_w, void *h, float *gate_out,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_hash_params(params);
+  if (rc != ENGRAM_OK) return rc;
+  rc = check_desc(desc);
+  if (rc != ENGRAM_OK) return rc;
+  if (desc->row_format != ENGRAM_ROW_E4M3_E8M0_264) return ENGRAM_EINVAL;
+  if (total_rows(params) > desc->table_rows) return ENGRAM_EPRIMES;
+  const int64_t ntok = desc->batch * desc->seq;
+  const int32_t S = (params->max_ngram - 1) * params->heads;
+  const int64_t out_dim = (int64_t)(desc->hc + 1) * desc->dim;
+  if (ntok > INT32_MAX) return ENGRAM_ESHAPE;
+  if (ntok > 0) {
+    if (ids == nullptr || table == nullptr || w_codes == nullptr || w_scales == nullptr ||
+        q_w == nullptr || k_w == nullptr || h == nullptr)
+      return ENGRAM_EINVAL;
+    if (!aligned(ids, 4) || !aligned(table, 8) || !aligned(w_codes, 16) ||
+        !aligned(w_scales, 4) || !aligned(q_w, 16) || !aligned(k_w, 16) || !aligned(h, 16) ||
+        !aligned(gate_out, 4))
+      return ENGRAM_EINVAL;
+    const size_t need = engram_forward_mx_workspace_size(params, desc);
+    if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
+      return ENGRAM_EWORKSPACE;
+  }
+  if (!aligned(hist_in, 4) || !aligned(hist_out, 4)) return ENGRAM_EINVAL;
+
+  char *ws = (char *)workspace;
+  int64_t *row_ids = (int64_t *)ws;
+  uint8_t *e_rows = (uint8_t *)(ws + align256((size_t)ntok * S * 8));
+  uint16_t *kv = (uint16_t *)((char *)e_rows + align256((size_t)ntok * S * ENGRAM_ROW_BYTES));
+  char *gemm_ws = (char *)kv + align256((size_t)ntok * out_dim * 2);
+  const size_t gemm_ws_bytes = workspace_bytes - (size_t)(gemm_ws - ws);
+
+  const EngramHashArgs a = make_hash_args(params, 1);
+  hipError_t err = engram_launch_hash(a, params->token_map, ids, desc->batch, desc->seq,
+                                      hist_in, hist_out, row_ids, stream);
+  if (err != hipSuccess || ntok == 0) return hip_status(err);
+  err = engram_launch_gather_rows((const uint8_t *)table, desc->table_rows, row_ids, ntok * S,
+                                  e_rows, stream);
+  if (err != hipSuccess) return hip_status(err);
+  err = engram_launch_gemm_mx((const uint8_t *)w_codes, (const uint8_t *)w_scales, e_rows, S, kv,
+                              ntok, out_dim, gemm_ws, gemm_ws_bytes, stream);
+  if (err != hipSuccess) return hip_status(err);
+  err = engram_launch_gate(false, ids, params->raw_vocab, kv, q_w, k_w, h, gate_out, ntok,
                            desc->hc, desc->dim, desc->eps, desc->gate_clamp, stream);
   return hip_status(err);
 }

@@ -1,4 +1,5 @@
-// Step 3 of the Engram layer: gather table rows and dequantise them to bf16.
+// Step 3 of the Engram layer: gather table rows and dequantise them to bf16
+// (or copy them unchanged for the block-scaled FP8 projection).
 //
 // Pages: "ds4.c 学习笔记 · Engram", "布局与哈希探测" (264-byte rows) and
 // "永不常驻的 I/O 设计" (256 E4M3 bytes + 8 E8M0 scales, 32 values per scale);
@@ -121,7 +122,37 @@ __global__ __launch_bounds__(kThreads) void gather_f32_kernel(
   reinterpret_cast<float4 *>(out + i * row_dim)[c] = v;
 }
 
+// Rows copied unchanged (the block-scaled FP8 projection consumes them as
+// they are): one thread per 8-byte word, 33 words per 264-byte row, so
+// consecutive threads cover a row's contiguous bytes. Ids outside [0, rows)
+// give zero rows.
+constexpr int kRowWords = ENGRAM_ROW_BYTES / 8;
+
+__global__ __launch_bounds__(kThreads) void gather_rows_kernel(
+    const uint8_t *__restrict__ table, int64_t table_rows, const int64_t *__restrict__ row_ids,
+    int64_t n_ids, uint8_t *__restrict__ out) {
+  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (g >= n_ids * kRowWords) return;
+  const int64_t i = g / kRowWords;
+  const int w = (int)(g - i * kRowWords);
+  const int64_t r = row_ids[i];
+  uint2 v = make_uint2(0u, 0u);
+  if (r >= 0 && r < table_rows)
+    v = *reinterpret_cast<const uint2 *>(table + r * ENGRAM_ROW_BYTES + (int64_t)w * 8);
+  *reinterpret_cast<uint2 *>(out + i * ENGRAM_ROW_BYTES + (int64_t)w * 8) = v;
+}
+
 }  // namespace
+
+hipError_t engram_launch_gather_rows(const uint8_t *table, int64_t table_rows,
+                                     const int64_t *row_ids, int64_t n_ids, uint8_t *out,
+                                     hipStream_t stream) {
+  if (n_ids <= 0) return hipSuccess;
+  const int64_t blocks = (n_ids * kRowWords + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                     table, table_rows, row_ids, n_ids, out);
+  return hipGetLastError();
+}
 
 hipError_t engram_launch_gather_e4m3(const uint8_t *table, int64_t table_rows,
                                      const int64_t *row_ids, int64_t n_ids, uint16_t *out,

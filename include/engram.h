@@ -221,6 +221,19 @@ int engram_gather(const void *table, int64_t table_rows, int32_t row_format,
                   hipStream_t stream);
 
 /*
+ * Step 3 for the block-scaled FP8 projection: the looked-up rows, bytes
+ * unchanged (256 E4M3 codes then 8 E8M0 scales each; [P4] "永不常驻的 I/O 设计"),
+ * which engram_project_mx consumes without dequantisation. A row id outside
+ * [0, table_rows) gives a zero row ([P3] §五).
+ *   table    uint8 [table_rows, 264], 8-byte aligned
+ *   row_ids  int64 [n_ids]
+ *   out      uint8 [n_ids, 264], 8-byte aligned
+ * Errors: ENGRAM_EINVAL, ENGRAM_ESHAPE, ENGRAM_EHIP.
+ */
+int engram_gather_rows(const void *table, int64_t table_rows, const int64_t *row_ids,
+                       int64_t n_ids, void *out, hipStream_t stream);
+
+/*
  * Step 4: kv = e W ([P1] "每条流一个 key 的设计沿用自原版": one 6144 x 25600
  * matrix; [P4] "消费": the weight is stored with the 6144 inputs innermost).
  *   e    [tokens, in_dim]       bf16 (act_f32 = 0) or float (act_f32 = 1)
@@ -248,6 +261,30 @@ int engram_project(const void *e, const void *wkv, void *kv, int64_t tokens,
  * device (0 if it needs none, on bad arguments or on a HIP error). */
 size_t engram_project_workspace_size(int64_t tokens, int64_t in_dim, int64_t out_dim,
                                      int32_t act_f32);
+
+/*
+ * Step 4 with a block-scaled FP8 weight ([P3] §2.3: the projection weight is
+ * block-FP8 beside the fp8 e4m3 + e8m0 table; [P5] §4.3: the projections fuse
+ * into one dense FP8 matrix product). Reading: the weight uses the table's own
+ * block encoding, E4M3 values with one E8M0 scale per 32 consecutive inputs.
+ * kv[t, c] = sum_k e[t, k] W[c, k] with e[t, 256 j + i] = E4M3(row_j[i]) *
+ * 2^(row_j[256 + i / 32] - 127) taken straight from the looked-up rows (exact
+ * products, fp32 accumulation in gfx950's block-scaled FP8 MFMA), rounded once
+ * to bf16 nearest-even.
+ *   e_rows   uint8 [tokens, segments, 264]: engram_gather_rows output
+ *   w_codes  uint8 [out_dim, 256 segments], 16-byte aligned
+ *   w_scales uint8 [out_dim, 8 segments] (E8M0, bias 127), 4-byte aligned
+ *   kv       bf16 [tokens, out_dim]; out_dim % 8 == 0
+ *   workspace as for engram_project, sized by engram_project_mx_workspace_size
+ * Errors: ENGRAM_EINVAL, ENGRAM_ESHAPE, ENGRAM_EWORKSPACE, ENGRAM_EHIP.
+ */
+int engram_project_mx(const void *e_rows, int32_t segments, const void *w_codes,
+                      const void *w_scales, void *kv, int64_t tokens, int64_t out_dim,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* [host] Bytes of workspace engram_project_mx uses (0 if none, on bad arguments
+ * or on a HIP error). */
+size_t engram_project_mx_workspace_size(int64_t tokens, int32_t segments, int64_t out_dim);
 
 /*
  * Step 5: gate and residual update, given kv.
@@ -285,6 +322,23 @@ int engram_forward(const engram_hash_params *params, const engram_forward_desc *
                    const void *table, const void *wkv, const float *q_w,
                    const float *k_w, void *h, float *gate_out, void *workspace,
                    size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The whole layer with the block-scaled FP8 weight: engram_hash,
+ * engram_gather_rows, engram_project_mx and engram_gate in one call. Arguments
+ * as for engram_forward, except the weight (w_codes, w_scales as for
+ * engram_project_mx); desc->row_format must be ENGRAM_ROW_E4M3_E8M0_264 and h
+ * is bf16. The workspace holds row ids, the looked-up rows, kv and the
+ * projection's workspace.
+ * Errors: as engram_forward.
+ */
+size_t engram_forward_mx_workspace_size(const engram_hash_params *params,
+                                        const engram_forward_desc *desc);
+int engram_forward_mx(const engram_hash_params *params, const engram_forward_desc *desc,
+                      const int32_t *ids, const int32_t *hist_in, int32_t *hist_out,
+                      const void *table, const void *w_codes, const void *w_scales,
+                      const float *q_w, const float *k_w, void *h, float *gate_out,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

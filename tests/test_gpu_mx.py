@@ -1,0 +1,142 @@
+"""Parity of the block-scaled FP8 path (engram_gather_rows, engram_project_mx,
+engram_forward_mx) with the CPU oracle. The looked-up rows match bit for bit;
+the projection stays within the FP8 MFMA's measured precision bound and is
+exact where every output has a single product; gates and streams follow the
+same tolerance as the bf16 path."""
+import numpy as np
+import pytest
+
+import oracle as O
+from tests.gpu_util import ATOL, RTOL, assert_close, gemm_tolerance_mx, oracle_rows, say
+from workloads import C3, gen
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import hashed_gram_conditional_amd as E  # noqa: E402
+from workloads.device import bf16_bits, to_device  # noqa: E402
+from workloads.harness import GpuWorkload  # noqa: E402
+from tests.test_gpu_parity import S_A, S_B, _h_input, _h_values, _sample_tokens  # noqa: E402
+
+DEV = "cuda"
+
+
+def _rows_of(seed, ids):
+    return gen.table_rows(seed, np.asarray(ids, dtype=np.int64))
+
+
+def test_gather_rows_bit_exact():
+    say("gather_rows: 5000 ids incl. out-of-range")
+    rng = np.random.default_rng(31)
+    R = 100_000
+    table = torch.from_numpy(gen.table_rows(5, np.arange(R))).to(DEV)
+    ids = rng.integers(-5, R + 5, 5000).astype(np.int64)
+    out = torch.full((ids.size, 264), 0xAB, dtype=torch.uint8, device=DEV)
+    E.engram_gather_rows(table, R, to_device(ids), ids.size, out)
+    torch.cuda.synchronize()
+    exp = O.gather_rows(lambda r: gen.table_rows(5, r), ids.reshape(-1, 1), R).reshape(-1, 264)
+    assert np.array_equal(out.cpu().numpy(), exp)
+
+
+def _mx_case(M, N, S, seed):
+    rng = np.random.default_rng(seed)
+    rows = _rows_of(seed, rng.integers(0, 10 ** 9, M * S)).reshape(M, S, 264)
+    codes, scales = gen.quantize_mx_e4m3(rng.normal(0.0, 0.02, (N, S * 256)))
+    e = O.mx_values(rows[:, :, :256].reshape(M, S * 256), rows[:, :, 256:].reshape(M, S * 8))
+    w = O.mx_values(codes, scales)
+    return rows, codes, scales, e, w
+
+
+def _project_mx(rows, codes, scales, M, N, S, with_ws):
+    n = E.engram_project_mx_workspace_size(M, S, N) if with_ws else 0
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=DEV) if n else None
+    kv = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    E.engram_project_mx(to_device(rows), S, to_device(codes), to_device(scales), kv, M, N, ws, n)
+    torch.cuda.synchronize()
+    return O.bf16_bits_to_f64(bf16_bits(kv))
+
+
+# shapes: tiny, ragged, a wide-tile grid (>= 256 tiles), the decode shape split
+# over the CUs, odd K-step counts (S = 1, 3: 2 and 6 steps; S = 5: 10)
+@pytest.mark.parametrize("M,N,S", [(1, 8, 1), (31, 264, 3), (300, 520, 24), (257, 1032, 5),
+                                   (4100, 4104, 1), (256, 25600, 24)])
+def test_project_mx_against_oracle(M, N, S):
+    say(f"project_mx {M}x{N} S={S}")
+    rows, codes, scales, e, w = _mx_case(M, N, S, M * 7 + N + S)
+    exact = O.project(e, w)
+    tol = gemm_tolerance_mx(e, w, exact)
+    for with_ws in (True, False):
+        got = _project_mx(rows, codes, scales, M, N, S, with_ws)
+        assert_close(got, exact, f"kv mx {M}x{N} S={S} ws={with_ws}", atol=0, rtol=0, extra=tol)
+
+
+def test_project_mx_single_products_exact():
+    # each token's rows hold one nonzero code (1.0 = 0x38) under scale 127 + d,
+    # so kv[t, c] = 2^d W[c, k_t], exact in bf16
+    M, N, S = 600, 1032, 4
+    rng = np.random.default_rng(5)
+    rows = np.zeros((M, S, 264), np.uint8)
+    rows[:, :, 256:] = 127
+    ks = rng.integers(0, S * 256, M)
+    d = rng.integers(-3, 4, M)
+    for t in range(M):
+        j, i = divmod(int(ks[t]), 256)
+        rows[t, j, i] = 0x38
+        rows[t, j, 256 + i // 32] = 127 + d[t]
+    codes, scales = gen.quantize_mx_e4m3(rng.normal(0.0, 0.02, (N, S * 256)))
+    w = O.mx_values(codes, scales)
+    exp = O.round_to_bf16_bits(np.exp2(d)[:, None] * w.T[ks])
+    for with_ws in (True, False):
+        got = _project_mx(rows, codes, scales, M, N, S, with_ws)
+        assert np.array_equal(O.round_to_bf16_bits(got), exp)
+
+
+def _check_forward_mx(gw, h_dev, gates_dev, tokens):
+    w = gw.w
+    rid, _ = oracle_rows(gw)
+    dead = gw.dead_np()
+    h_in = _h_input(gw).reshape(w.tokens, w.hc, w.dim)
+    wf = O.mx_values(*gw.wkv_mx_np)
+    res = O.forward_tokens(tokens, rid, dead, fetch_rows=gw.fetch_rows, table_rows=gw.rows,
+                           wkv=wf, q_w=gw.dense_np["q_w"], k_w=gw.dense_np["k_w"], h=h_in,
+                           hc=w.hc, dim=w.dim, eps=w.eps, clamp=w.gate_clamp, bf16=True)
+    tok = torch.from_numpy(np.asarray(tokens)).to(DEV)
+    a_got = gates_dev[tok].cpu().numpy().astype(np.float64)
+    h_got = _h_values(gw, h_dev.reshape(w.tokens, w.hc, w.dim)[tok])
+    # the projection's bounded difference enters the gate through k and the update through v
+    exact = O.project(res["e"], wf).reshape(len(tokens), w.hc + 1, w.dim)
+    tol = gemm_tolerance_mx(res["e"], wf, exact.reshape(len(tokens), -1))
+    tol = tol.reshape(len(tokens), w.hc + 1, w.dim)
+    extra_h = res["alpha"][:, :, None] * tol[:, None, w.hc, :]
+    assert_close(a_got, res["alpha"], f"{w.name} mx gates")
+    assert np.all(a_got[dead[tokens]] == 0.0)
+    assert np.array_equal(h_got[dead[tokens]], h_in[tokens][dead[tokens]])
+    assert_close(h_got, res["h_out"], f"{w.name} mx h", extra=extra_h)
+
+
+@pytest.mark.parametrize("w", [S_A, S_B], ids=lambda w: w.name)
+def test_forward_mx_small(w):
+    say(f"forward_mx {w.name}: tokens={w.tokens}")
+    gw = GpuWorkload(w, wkv_mx=True)
+    ws, n = gw.workspace_mx()
+    gates = torch.full((w.tokens, w.hc), -1.0, dtype=torch.float32, device=DEV)
+    E.engram_forward_mx(gw.params, gw.desc, gw.ids, None, None, gw.table, gw.w_codes,
+                        gw.w_scales, gw.q_w, gw.k_w, gw.h, gates, ws, n)
+    torch.cuda.synchronize()
+    _check_forward_mx(gw, gw.h, gates, np.arange(w.tokens))
+
+
+def test_forward_mx_prefill_sampled():
+    say("forward_mx C3 (4 x 8192 tokens), sampled tokens")
+    gw = GpuWorkload(C3, wkv_mx=True)
+    ws, n = gw.workspace_mx()
+    gates = torch.empty((C3.tokens, C3.hc), dtype=torch.float32, device=DEV)
+    E.engram_forward_mx(gw.params, gw.desc, gw.ids, None, None, gw.table, gw.w_codes,
+                        gw.w_scales, gw.q_w, gw.k_w, gw.h, gates, ws, n)
+    torch.cuda.synchronize()
+    _check_forward_mx(gw, gw.h, gates, _sample_tokens(gw, 96, 7))
+    del ws
+    gw.free()

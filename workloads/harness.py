@@ -13,7 +13,7 @@ from .device import fill_table, to_device
 
 class GpuWorkload:
     def __init__(self, w: EngramWorkload, device: str = "cuda", table: bool = True,
-                 dense: bool = True):
+                 dense: bool = True, wkv_mx: bool = False):
         import torch
         import hashed_gram_conditional_amd as E
 
@@ -52,6 +52,12 @@ class GpuWorkload:
                 fill_table(self.table, w.table_seed)
         self.desc = E.forward_desc(w.batch, w.seq, w.hc, w.dim, self.rows, self.row_format,
                                    w.row_dim, w.eps, w.gate_clamp)
+        # the projection weight in block-scaled FP8 (codes, scales), host and device
+        self.wkv_mx_np = None
+        if wkv_mx:
+            self.wkv_mx_np = gen.wkv_mx(w)
+            self.w_codes = to_device(self.wkv_mx_np[0], device)
+            self.w_scales = to_device(self.wkv_mx_np[1], device)
 
     @property
     def tokens(self) -> int:
@@ -70,7 +76,13 @@ class GpuWorkload:
         n = self.E.engram_forward_workspace_size(self.params, self.desc)
         return torch.empty(max(n, 256), dtype=torch.uint8, device=self.device), n
 
+    def workspace_mx(self):
+        import torch
+        n = self.E.engram_forward_mx_workspace_size(self.params, self.desc)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=self.device), n
+
     def free(self):
-        for name in ("table", "wkv", "q_w", "k_w", "h", "ids", "token_map", "hist_in"):
+        for name in ("table", "wkv", "q_w", "k_w", "h", "ids", "token_map", "hist_in",
+                     "w_codes", "w_scales"):
             if hasattr(self, name):
                 setattr(self, name, None)
