@@ -120,6 +120,8 @@ def main():
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-step measurement on the 101 GB table")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode-step measurement (profiling its kernels)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -134,6 +136,9 @@ def main():
     from workloads.harness import GpuWorkload
 
     torch.cuda.set_device(0)
+    if args.decode_only:
+        print(json.dumps({"decode": decode_bench(args.steps, args.warmup)}), flush=True)
+        return
     t_setup = time.perf_counter()
     gw = GpuWorkload(C3)
     w = gw.w
