@@ -448,8 +448,11 @@ __device__ __forceinline__ uint32_t load4(__amdgpu_buffer_rsrc_t rs, int voff, i
 // Registers: the B fragments of a 64-input chunk are double-buffered, the A
 // fragments stream one tile ahead (both A fragments the MFMAs after the barrier
 // need are read before it, as other waves then start refilling the stage).
-__device__ __forceinline__ void wide_tile_mx(const MxOperands &op, int M, int N, int m0, int n0,
-                                             int ks, int ke, f32x16 (&acc)[4][4], MxLds &lds) {
+__device__ __forceinline__ void wide_tile_mx(
+    const MxOperands &op, int M, int N, int m0, int n0, int ks, int ke, f32x16 (&acc)[4][4],
+    uint8_t *__restrict__ w0, uint8_t *__restrict__ w1, uint8_t *__restrict__ e0,
+    uint8_t *__restrict__ e1, uint32_t *__restrict__ ws0, uint32_t *__restrict__ ws1,
+    uint32_t *__restrict__ es0, uint32_t *__restrict__ es1) {
   const int K = op.segments * 256;
   const int KB = K / 32;                       // scale bytes per W row
   const int RS = op.segments * kRowBytes;      // bytes per e row
@@ -486,40 +489,48 @@ __device__ __forceinline__ void wide_tile_mx(const MxOperands &op, int M, int N,
   const int dl_v1 = dl_row * K + (dl_c0 ^ 1) * 16;
   uint4 g[8];
   uint32_t ges = 0;
+// Stage buffers are distinct restrict pointers, so the compiler can tell the
+// direct loads into one stage from reads of the other and waits for nothing.
+#define MX_W(st) ((st) ? w1 : w0)
+#define MX_E(st) ((st) ? e1 : e0)
+#define MX_WS(st) ((st) ? ws1 : ws0)
+#define MX_ES(st) ((st) ? es1 : es0)
 #define MX_WOFF(kt_) ((kt_) * kMxBk)
 #define MX_EOFF(kt_) (((kt_) >> 1) * kRowBytes + ((kt_) & 1) * kMxBk)
 #define MX_ESOFF(kt_) (((kt_) >> 1) * kRowBytes + 256 + ((kt_) & 1) * 4)
 // Half q of a step: q = 0 the W codes and scales, q = 1 the e codes and scales.
-// 9 direct loads per thread: W codes of step kt_ (8) and its scales (1) into stage st.
-#define MX_DMAW(kt_, st)                                                                      \
-  _Pragma("unroll") for (int i = 0; i < 8; ++i)                                             \
+// Direct loads of W: code chunk i (i < 8) or the scales (i = 8) of step kt_ into stage st.
+#define MX_DMAW1(kt_, st, i)                                                                  \
+  if ((i) < 8)                                                                              \
     __builtin_amdgcn_raw_ptr_buffer_load_lds(                                               \
-        rsW, (__attribute__((address_space(3))) void *)&lds.w[st][(wave * 8 + i) * 1024],   \
-        16, (i & 1) ? dl_v1 : dl_v0, i * 8 * K + MX_WOFF(kt_), 0, 0);                       \
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                 \
-      rsWs, (__attribute__((address_space(3))) void *)&lds.ws[st][wave * 64], 4, tid * KB,  \
-      (kt_) * 4, 0, 0);
-// 9 register loads per thread: e codes and scales of step kt_, and their LDS stores.
-#define MX_LOADE(kt_)                                                                         \
-  _Pragma("unroll") for (int i = 0; i < 8; ++i)                                             \
-    g[i] = load16(rsE, ge_voff, i * 32 * RS + MX_EOFF(kt_));                                \
-  ges = load4(rsE, tid * RS, MX_ESOFF(kt_));
-#define MX_STOREE(st)                                                                         \
-  _Pragma("unroll") for (int i = 0; i < 8; ++i)                                             \
-    *reinterpret_cast<uint4 *>(&lds.e[st][s_off + i * 32 * kMxBk]) = g[i];                  \
-  lds.es[st][tid] = ges;
-// The step's direct W loads have landed once at most the 9 e loads issued
-// after them are outstanding.
+        rsW, (__attribute__((address_space(3))) void *)&MX_W(st)[(wave * 8 + (i)) * 1024],  \
+        16, ((i) & 1) ? dl_v1 : dl_v0, (i) * 8 * K + MX_WOFF(kt_), 0, 0);                   \
+  else                                                                                      \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(                                               \
+        rsWs, (__attribute__((address_space(3))) void *)&MX_WS(st)[wave * 64], 4, tid * KB, \
+        (kt_) * 4, 0, 0);
+// e chunk i (i < 8) or the scales (i = 8): store the staged step into stage st,
+// then reload the register with step kt_.
+#define MX_EPAIR(st, i, kt_)                                                                  \
+  if ((i) < 8) {                                                                            \
+    *reinterpret_cast<uint4 *>(&MX_E(st)[s_off + (i) * 32 * kMxBk]) = g[i];                 \
+    g[i] = load16(rsE, ge_voff, (i) * 32 * RS + MX_EOFF(kt_));                              \
+  } else {                                                                                  \
+    MX_ES(st)[tid] = ges;                                                                   \
+    ges = load4(rsE, tid * RS, MX_ESOFF(kt_));                                              \
+  }
+// W copies of a step are issued right after the previous barrier; the 9 e
+// reloads that follow them may stay in flight across the next barrier.
 #define MX_BARRIER() asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory")
 #define MX_FRAG(buf, base, c, t)                                                              \
   join16(*reinterpret_cast<const uint4 *>(&(buf)[(base) + (t) * 32 * kMxBk + ((c) ? f1lo : f0lo)]), \
          *reinterpret_cast<const uint4 *>(&(buf)[(base) + (t) * 32 * kMxBk + ((c) ? f1hi : f0hi)]))
-#define MX_FRAGA(st, c, t) MX_FRAG(lds.w[st], a_base, c, t)
+#define MX_FRAGA(st, c, t) MX_FRAG(MX_W(st), a_base, c, t)
 #define MX_FRAGSB(st, c, dst)                                                                 \
-  _Pragma("unroll") for (int j = 0; j < 4; ++j) dst[j] = MX_FRAG(lds.e[st], b_base, c, j);
+  _Pragma("unroll") for (int j = 0; j < 4; ++j) dst[j] = MX_FRAG(MX_E(st), b_base, c, j);
 #define MX_SCALES(st, sA, sB)                                                                 \
-  _Pragma("unroll") for (int i = 0; i < 4; ++i) sA[i] = lds.ws[st][a_srow + i * 32];        \
-  _Pragma("unroll") for (int j = 0; j < 4; ++j) sB[j] = lds.es[st][b_srow + j * 32];
+  _Pragma("unroll") for (int i = 0; i < 4; ++i) sA[i] = MX_WS(st)[a_srow + i * 32];         \
+  _Pragma("unroll") for (int j = 0; j < 4; ++j) sB[j] = MX_ES(st)[b_srow + j * 32];
 // scale byte of 32-input block 2c + h of the step
 #define MX_SB(word, c) ((int)(((word) >> (8 * (2 * (c) + h))) & 0xFFu))
 #define MX_TILE(i, afrag, bfr, sbv, sa_in)                                                    \
@@ -535,72 +546,86 @@ __device__ __forceinline__ void wide_tile_mx(const MxOperands &op, int M, int N,
   i32x8 bC[4], bN[4], aC, aN;
   uint32_t aS[4], bS[4];
   int sbv[4], sa2, sa3;
+  // Prologue: W of steps ks and ks+1 by direct loads, e of step ks into stage 0,
+  // e of step ks+1 staged in registers.
   __syncthreads();
-  MX_DMAW(ks, 0)
-  MX_LOADE(ks)
-  MX_STOREE(0)
-  MX_LOADE(ks + 1)
-  MX_BARRIER();
+  _Pragma("unroll") for (int i = 0; i < 9; ++i) { MX_DMAW1(ks, 0, i) }
+  _Pragma("unroll") for (int i = 0; i < 8; ++i)
+    g[i] = load16(rsE, ge_voff, i * 32 * RS + MX_EOFF(ks));
+  ges = load4(rsE, tid * RS, MX_ESOFF(ks));
+  _Pragma("unroll") for (int i = 0; i < 9; ++i) { MX_EPAIR(0, i, ks + 1) }
+  _Pragma("unroll") for (int i = 0; i < 9; ++i) { MX_DMAW1(ks + 1, 1, i) }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   MX_FRAGSB(0, 0, bC)
   aC = MX_FRAGA(0, 0, 0);
   MX_SCALES(0, aS, bS)
 
+// Step kt reads stage P. Before its barrier it stores the staged e of step
+// kt+1 into stage Q and restages e of step kt+2 (9 pairs over the first five
+// tiles); after the barrier stage P is free and takes W of step kt+2.
 #define MX_STEP(P, Q)                                                                         \
   {                                                                                         \
-    /* chunk 0 of stage P: next chunk's B fragments, half 0 of the staging */              \
     _Pragma("unroll") for (int j = 0; j < 4; ++j) sbv[j] = MX_SB(bS[j], 0);                 \
     MX_FRAGSB(P, 1, bN)                                                                     \
-    MX_STOREE(Q)                                                                            \
-    MX_DMAW(kt + 1, Q)                                                                      \
+    MX_EPAIR(Q, 0, kt + 2) MX_EPAIR(Q, 1, kt + 2)                                           \
     aN = MX_FRAGA(P, 0, 1);                                                                 \
-    MX_TILE(0, aC, bC, sbv, MX_SB(aS[0], 0))                                                       \
-    for (int s_ = 0; s_ < 4; ++s_) {                                                        \
-      MX_GROUP(0x100, 2); MX_GROUP(0x008, 1); MX_GROUP(0x200, 2); MX_GROUP(0x020, 1);       \
+    MX_TILE(0, aC, bC, sbv, MX_SB(aS[0], 0))                                                \
+    for (int s_ = 0; s_ < 2; ++s_) {                                                        \
+      MX_GROUP(0x100, 4); MX_GROUP(0x008, 1); MX_GROUP(0x200, 1); MX_GROUP(0x020, 1);       \
+      MX_GROUP(0x008, 1);                                                                   \
     }                                                                                       \
     MX_FENCE();                                                                             \
+    MX_EPAIR(Q, 2, kt + 2) MX_EPAIR(Q, 3, kt + 2)                                           \
     aC = MX_FRAGA(P, 0, 2);                                                                 \
-    MX_TILE(1, aN, bC, sbv, MX_SB(aS[1], 0))                                                       \
-    for (int s_ = 0; s_ < 4; ++s_) {                                                        \
-      MX_GROUP(0x100, 1); MX_GROUP(0x008, 1); MX_GROUP(0x020, 1);                           \
+    MX_TILE(1, aN, bC, sbv, MX_SB(aS[1], 0))                                                \
+    for (int s_ = 0; s_ < 2; ++s_) {                                                        \
+      MX_GROUP(0x100, 1); MX_GROUP(0x008, 1); MX_GROUP(0x200, 1); MX_GROUP(0x020, 1);       \
+      MX_GROUP(0x008, 1);                                                                   \
     }                                                                                       \
     MX_FENCE();                                                                             \
+    MX_EPAIR(Q, 4, kt + 2) MX_EPAIR(Q, 5, kt + 2)                                           \
     aN = MX_FRAGA(P, 0, 3);                                                                 \
-    MX_TILE(2, aC, bC, sbv, MX_SB(aS[2], 0))                                                       \
-    for (int s_ = 0; s_ < 4; ++s_) { MX_GROUP(0x100, 1); MX_GROUP(0x008, 1); }              \
-    MX_FENCE();                                                                             \
-    aC = MX_FRAGA(P, 1, 0);                                                                 \
-    MX_TILE(3, aN, bC, sbv, MX_SB(aS[3], 0))                                                       \
-    for (int s_ = 0; s_ < 4; ++s_) { MX_GROUP(0x100, 1); MX_GROUP(0x008, 1); }              \
-    MX_FENCE();                                                                             \
-    /* chunk 1 of stage P: half 1 of the staging; all of P's A fragments before the barrier */ \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) sbv[j] = MX_SB(bS[j], 1);                 \
-    MX_LOADE(kt + 2)                                                                        \
-    aN = MX_FRAGA(P, 1, 1);                                                                 \
-    MX_TILE(0, aC, bN, sbv, MX_SB(aS[0], 1))                                                       \
-    for (int s_ = 0; s_ < 4; ++s_) {                                                        \
-      MX_GROUP(0x100, 1); MX_GROUP(0x008, 1); MX_GROUP(0x020, 2);                           \
+    MX_TILE(2, aC, bC, sbv, MX_SB(aS[2], 0))                                                \
+    for (int s_ = 0; s_ < 2; ++s_) {                                                        \
+      MX_GROUP(0x100, 1); MX_GROUP(0x008, 1); MX_GROUP(0x200, 1); MX_GROUP(0x020, 1);       \
+      MX_GROUP(0x008, 1);                                                                   \
     }                                                                                       \
+    MX_FENCE();                                                                             \
+    MX_EPAIR(Q, 6, kt + 2) MX_EPAIR(Q, 7, kt + 2)                                           \
+    aC = MX_FRAGA(P, 1, 0);                                                                 \
+    MX_TILE(3, aN, bC, sbv, MX_SB(aS[3], 0))                                                \
+    for (int s_ = 0; s_ < 2; ++s_) {                                                        \
+      MX_GROUP(0x100, 1); MX_GROUP(0x008, 1); MX_GROUP(0x200, 1); MX_GROUP(0x020, 1);       \
+      MX_GROUP(0x008, 1);                                                                   \
+    }                                                                                       \
+    MX_FENCE();                                                                             \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) sbv[j] = MX_SB(bS[j], 1);                 \
+    MX_EPAIR(Q, 8, kt + 2)                                                                  \
+    aN = MX_FRAGA(P, 1, 1);                                                                 \
+    MX_TILE(0, aC, bN, sbv, MX_SB(aS[0], 1))                                                \
     MX_FENCE();                                                                             \
     MX_TILE(1, aN, bN, sbv, MX_SB(aS[1], 1))                                                \
     aC = MX_FRAGA(P, 1, 2);                                                                 \
     aN = MX_FRAGA(P, 1, 3);                                                                 \
     sa2 = MX_SB(aS[2], 1);                                                                  \
     sa3 = MX_SB(aS[3], 1);                                                                  \
-    for (int s_ = 0; s_ < 4; ++s_) {                                                        \
-      MX_GROUP(0x100, 1); MX_GROUP(0x008, 1); MX_GROUP(0x200, 1); MX_GROUP(0x020, 1);       \
-    }                                                                                       \
+    for (int s_ = 0; s_ < 2; ++s_) { MX_GROUP(0x008, 1); MX_GROUP(0x100, 1); MX_GROUP(0x008, 1); } \
     MX_FENCE();                                                                             \
     MX_BARRIER();                                                                           \
     MX_FENCE();                                                                             \
-    /* stage Q (step kt+1): B fragments of chunk 0, its scales, A tile 0 */                \
+    /* stage Q (step kt+1): its fragments and scales; stage P takes W of step kt+2 */       \
     MX_FRAGSB(Q, 0, bC)                                                                     \
     MX_SCALES(Q, aS, bS)                                                                    \
+    MX_DMAW1(kt + 2, P, 0) MX_DMAW1(kt + 2, P, 1) MX_DMAW1(kt + 2, P, 2)                    \
+    MX_DMAW1(kt + 2, P, 3) MX_DMAW1(kt + 2, P, 4)                                           \
     MX_TILE(2, aC, bN, sbv, sa2)                                                            \
-    for (int s_ = 0; s_ < 4; ++s_) { MX_GROUP(0x100, 3); MX_GROUP(0x008, 1); }              \
+    for (int s_ = 0; s_ < 4; ++s_) { MX_GROUP(0x100, 3); MX_GROUP(0x008, 1); MX_GROUP(0x020, 1); } \
     MX_FENCE();                                                                             \
+    MX_DMAW1(kt + 2, P, 5) MX_DMAW1(kt + 2, P, 6) MX_DMAW1(kt + 2, P, 7)                    \
+    MX_DMAW1(kt + 2, P, 8)                                                                  \
     MX_TILE(3, aN, bN, sbv, sa3)                                                            \
     aC = MX_FRAGA(Q, 0, 0);                                                                 \
-    for (int s_ = 0; s_ < 4; ++s_) { MX_GROUP(0x100, 1); MX_GROUP(0x008, 1); }              \
+    for (int s_ = 0; s_ < 4; ++s_) { MX_GROUP(0x100, 1); MX_GROUP(0x008, 1); MX_GROUP(0x020, 1); } \
     MX_FENCE();                                                                             \
   }
   int kt = ks;
@@ -611,6 +636,8 @@ __device__ __forceinline__ void wide_tile_mx(const MxOperands &op, int M, int N,
     --kt;
   }
   if (kt < ke) MX_STEP(0, 1)
+  // Direct loads issued for steps past ke must land before the stages are reused.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #undef MX_STEP
 #undef MX_GROUP
 #undef MX_FENCE
@@ -621,12 +648,15 @@ __device__ __forceinline__ void wide_tile_mx(const MxOperands &op, int M, int N,
 #undef MX_FRAGA
 #undef MX_FRAG
 #undef MX_BARRIER
-#undef MX_STOREE
-#undef MX_LOADE
-#undef MX_DMAW
+#undef MX_EPAIR
+#undef MX_DMAW1
 #undef MX_ESOFF
 #undef MX_EOFF
 #undef MX_WOFF
+#undef MX_W
+#undef MX_E
+#undef MX_WS
+#undef MX_ES
 }
 
 __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -637,7 +667,8 @@ void gemm_mx_kernel(MxOperands op, uint16_t *__restrict__ C, int M, int N, int t
   tile_origin(tiles_m, tiles_n, BN, m0, n0);
   f32x16 acc[4][4];
   zero_acc(acc);
-  wide_tile_mx(op, M, N, m0, n0, 0, op.segments * 256 / kMxBk, acc, lds);
+  wide_tile_mx(op, M, N, m0, n0, 0, op.segments * 256 / kMxBk, acc, lds.w[0], lds.w[1],
+               lds.e[0], lds.e[1], lds.ws[0], lds.ws[1], lds.es[0], lds.es[1]);
   wide_store_bf16(acc, C, M, N, m0, n0);
 }
 
@@ -656,7 +687,8 @@ void gemm_mx_streamk_kernel(MxOperands op, uint16_t *__restrict__ C, float *__re
     const int m0 = (int)(tile % sk.tiles_m) * BM;
     const int n0 = (int)(tile / sk.tiles_m) * BN;
     zero_acc(acc);
-    wide_tile_mx(op, M, N, m0, n0, ks, ke, acc, lds);
+    wide_tile_mx(op, M, N, m0, n0, ks, ke, acc, lds.w[0], lds.w[1], lds.e[0], lds.e[1],
+                 lds.ws[0], lds.ws[1], lds.es[0], lds.es[1]);
     if (ks == 0 && ke == sk.kt) {
       wide_store_bf16(acc, C, M, N, m0, n0);
     } else {
