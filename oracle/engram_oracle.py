@@ -35,7 +35,13 @@ Readings of points the pages leave open (each listed in the design notes):
   sqrt(d) (P1 "门控" eq. for s^(m)); the RMS has eps inside the root and no
   weight, and the weights q_w * k_w multiply the dot (P4 "消费：学习投影 + 余弦门控");
 * kv and h are rounded to bf16 where the device path stores bf16 (P4: the
-  residual update is bf16(h + gate * bf16(v))).
+  residual update is bf16(h + gate * bf16(v)));
+* the papers' plain gate sigmoid(s) ignores the clamp (P5 §4.1);
+* the short convolution branch (P5 §4.2) gives every channel of every stream
+  its own filter and no bias, tap j meets the value (taps - 1 - j) * dilation
+  positions back, its RMSNorm runs per stream and position with eps inside the
+  root, the convolution input is zero before the sequence start, and a DEAD
+  position contributes V~ = 0 and keeps its streams.
 """
 from __future__ import annotations
 
@@ -407,7 +413,7 @@ def project(e: np.ndarray, wkv: np.ndarray) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 def gate(h: np.ndarray, k: np.ndarray, v: np.ndarray, q_w: np.ndarray, k_w: np.ndarray,
-         dead: np.ndarray, eps: float, clamp: float = 0.0):
+         dead: np.ndarray, eps: float, clamp: float = 0.0, mode: str = "signed_sqrt"):
     """Gate alpha [T, hc] and updated streams h + alpha * v, in float64.
 
     [P1] "门控" and "sigmoid 之前多一步带符号的平方根":
@@ -417,9 +423,14 @@ def gate(h: np.ndarray, k: np.ndarray, v: np.ndarray, q_w: np.ndarray, k_w: np.n
     multiply the dot, and eps sits inside each reciprocal root of mean squares.
     [P1] image-token paragraph: the gate at a DEAD position is 0, and [P4]
     item 4: such rows are returned untouched.
+    mode "plain" is the papers' own gate alpha = sigmoid(s) ([P5] §4.1, the
+    equation for alpha_t; [P1] "sigmoid 之前多一步带符号的平方根" names it as the
+    formula the signed root departs from); clamp does not enter it.
 
     h, k: [T, hc, d]; v: [T, d]; q_w, k_w: [hc, d]; dead: [T] bool.
     """
+    if mode not in ("signed_sqrt", "plain"):
+        raise ValueError(f"unknown gate mode {mode!r}")
     h = np.asarray(h, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -429,11 +440,108 @@ def gate(h: np.ndarray, k: np.ndarray, v: np.ndarray, q_w: np.ndarray, k_w: np.n
     rk = 1.0 / np.sqrt(np.mean(k * k, axis=-1) + eps)
     dot = np.sum(h * w[None, :, :] * k, axis=-1)
     s = dot * rh * rk / math.sqrt(d)
-    alpha = 1.0 / (1.0 + np.exp(-np.copysign(np.sqrt(np.maximum(np.abs(s), clamp)), s)))
+    if mode == "plain":
+        z = s
+    else:
+        z = np.copysign(np.sqrt(np.maximum(np.abs(s), clamp)), s)
+    alpha = 1.0 / (1.0 + np.exp(-z))
     alpha = np.where(np.asarray(dead)[:, None], 0.0, alpha)
     h_out = h + alpha[:, :, None] * v[:, None, :]
     h_out = np.where(np.asarray(dead)[:, None, None], h, h_out)
     return alpha, h_out
+
+
+# ----------------------------------------------------------------------------
+# Short convolution branch after the gate (the papers' variant)
+# ----------------------------------------------------------------------------
+
+def conv_history_len(taps: int, dilation: int) -> int:
+    """Positions before the current one that a causal convolution of ``taps``
+    taps spaced ``dilation`` apart reaches: (taps - 1) * dilation, 9 for the
+    papers' 4 taps at dilation 3 ([P5] §4.2: position t uses t, t-3, t-6, t-9;
+    [P5] §9.5: a decode state covering the past 9 positions)."""
+    if taps < 1 or dilation < 1:
+        raise ValueError("taps and dilation must be >= 1")
+    return (taps - 1) * dilation
+
+
+def rms_norm(x: np.ndarray, weight: Optional[np.ndarray], eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) over the last axis, times ``weight`` (ones if
+    None). Reading: the branch's RMSNorm normalises each stream's d channels at
+    one position, like the gate's, with eps inside the root."""
+    x = np.asarray(x, dtype=np.float64)
+    y = x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    if weight is not None:
+        y = y * np.asarray(weight, dtype=np.float64)
+    return y
+
+
+def short_conv(vt: np.ndarray, conv_w: np.ndarray, norm_w: Optional[np.ndarray],
+               dilation: int, eps: float, hist: Optional[np.ndarray] = None) -> np.ndarray:
+    """Y = SiLU(Conv1D(RMSNorm(V~))) + V~ over each sequence, in float64.
+
+    [P5] §4.2, the equation for Y: a short depthwise causal convolution of the
+    RMS-normalised gated values, SiLU, plus the gated values themselves; kernel
+    size 4 and dilation equal to the largest n-gram order (3) in the papers'
+    setting, one filter per channel. [P3] §三 states the same branch as
+    value + short_conv(value). Readings: every channel of every stream has its
+    own filter and no bias; tap j of a filter multiplies the value
+    (taps - 1 - j) * dilation positions back (the causal Conv1D whose last tap
+    meets the current position); before the sequence start, or before
+    ``hist``, the normalised input is zero.
+
+    vt: [B, T, hc, d] gated values alpha v (zero at DEAD positions);
+    conv_w: [hc, d, taps]; norm_w: [hc, d] or None;
+    hist: [B, L, hc, d] gated values of the L = (taps - 1) * dilation positions
+    before the chunk, or None for a sequence start.
+    """
+    vt = np.asarray(vt, dtype=np.float64)
+    B, T, hc, d = vt.shape
+    w = np.asarray(conv_w, dtype=np.float64)
+    taps = w.shape[-1]
+    L = conv_history_len(taps, dilation)
+    # the causal convolution pads its (normalised) input with zeros
+    n_prev = np.zeros((B, L, hc, d)) if hist is None else \
+        rms_norm(np.asarray(hist, dtype=np.float64).reshape(B, L, hc, d), norm_w, eps)
+    n = np.concatenate([n_prev, rms_norm(vt, norm_w, eps)], axis=1)
+    u = np.zeros_like(vt)
+    for j in range(taps):
+        back = (taps - 1 - j) * dilation
+        u += w[None, None, :, :, j] * n[:, L - back:L - back + T]
+    silu = u / (1.0 + np.exp(-u))
+    return silu + vt
+
+
+def gate_conv(h: np.ndarray, k: np.ndarray, v: np.ndarray, q_w: np.ndarray, k_w: np.ndarray,
+              dead: np.ndarray, eps: float, clamp: float, conv_w: np.ndarray,
+              norm_w: Optional[np.ndarray], dilation: int, conv_eps: float,
+              hist: Optional[np.ndarray] = None, mode: str = "signed_sqrt"):
+    """The gate followed by the short convolution branch, in float64.
+
+    [P5] §4.1-§4.2: V~ = alpha v per stream, Y = SiLU(Conv1D(RMSNorm(V~))) + V~,
+    H += Y. At a DEAD position alpha = 0, so V~ = 0 there as the neighbours'
+    convolution sees it, and that position's streams are left untouched, as
+    without the branch (reading: [P1]'s forced-zero gate and [P4] item 4 carry
+    over to the whole update).
+
+    h, k: [B, T, hc, d]; v: [B, T, d]; dead: [B, T] bool; hist as short_conv.
+    Returns alpha [B, T, hc], h_out [B, T, hc, d] and the gated values of the
+    last L positions of hist followed by this chunk (the next chunk's hist).
+    """
+    h = np.asarray(h, dtype=np.float64)
+    B, T, hc, d = h.shape
+    alpha, _ = gate(h.reshape(B * T, hc, d), np.asarray(k).reshape(B * T, hc, d),
+                    np.asarray(v).reshape(B * T, d), q_w, k_w,
+                    np.asarray(dead).reshape(B * T), eps, clamp, mode=mode)
+    alpha = alpha.reshape(B, T, hc)
+    vt = alpha[..., None] * np.asarray(v, dtype=np.float64)[:, :, None, :]
+    y = short_conv(vt, conv_w, norm_w, dilation, conv_eps, hist)
+    dead = np.asarray(dead).reshape(B, T)
+    h_out = np.where(dead[:, :, None, None], h, h + y)
+    L = conv_history_len(np.asarray(conv_w).shape[-1], dilation)
+    prev = np.zeros((B, L, hc, d)) if hist is None else np.asarray(hist, dtype=np.float64)
+    tail = np.concatenate([prev, vt], axis=1)[:, T:]
+    return alpha, h_out, tail
 
 
 # ----------------------------------------------------------------------------

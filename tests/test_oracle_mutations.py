@@ -66,13 +66,13 @@ def _round_truncate(x):
     return (x.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
-def _gate_over_d(h, k, v, q_w, k_w, dead, eps, clamp=0.0):
+def _gate_over_d(h, k, v, q_w, k_w, dead, eps, clamp=0.0, mode="signed_sqrt"):
     d = h.shape[-1]
-    return _orig["gate"](h, k, v, q_w, k_w, dead, eps, clamp) if d == 1 else \
-        _orig["gate"](np.asarray(h) / math.sqrt(d), k, v, q_w, k_w, dead, eps, clamp)
+    return _orig["gate"](h, k, v, q_w, k_w, dead, eps, clamp, mode) if d == 1 else \
+        _orig["gate"](np.asarray(h) / math.sqrt(d), k, v, q_w, k_w, dead, eps, clamp, mode)
 
 
-def _gate_plain_sigmoid(h, k, v, q_w, k_w, dead, eps, clamp=0.0):
+def _gate_plain_sigmoid(h, k, v, q_w, k_w, dead, eps, clamp=0.0, mode="signed_sqrt"):
     h = np.asarray(h, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     d = h.shape[-1]
@@ -85,8 +85,70 @@ def _gate_plain_sigmoid(h, k, v, q_w, k_w, dead, eps, clamp=0.0):
     return a, h + a[:, :, None] * np.asarray(v)[:, None, :]
 
 
-def _gate_no_weights(h, k, v, q_w, k_w, dead, eps, clamp=0.0):
-    return _orig["gate"](h, k, v, np.ones_like(q_w), np.ones_like(k_w), dead, eps, clamp)
+def _gate_no_weights(h, k, v, q_w, k_w, dead, eps, clamp=0.0, mode="signed_sqrt"):
+    return _orig["gate"](h, k, v, np.ones_like(q_w), np.ones_like(k_w), dead, eps, clamp, mode)
+
+
+def _gate_mode_ignored(h, k, v, q_w, k_w, dead, eps, clamp=0.0, mode="signed_sqrt"):
+    return _orig["gate"](h, k, v, q_w, k_w, dead, eps, clamp)
+
+
+def _short_conv_taps_reversed(vt, conv_w, norm_w, dilation, eps, hist=None):
+    return _orig["short_conv"](vt, np.asarray(conv_w)[..., ::-1], norm_w, dilation, eps, hist)
+
+
+def _short_conv_no_dilation(vt, conv_w, norm_w, dilation, eps, hist=None):
+    return _orig["short_conv"](vt, conv_w, norm_w, 1, eps, None)
+
+
+def _short_conv_no_residual(vt, conv_w, norm_w, dilation, eps, hist=None):
+    return _orig["short_conv"](vt, conv_w, norm_w, dilation, eps, hist) - np.asarray(vt)
+
+
+def _short_conv_sigmoid(vt, conv_w, norm_w, dilation, eps, hist=None):
+    """Wrong: sigmoid(u) where SiLU(u) = u sigmoid(u) belongs."""
+    y = _orig["short_conv"](vt, conv_w, norm_w, dilation, eps, hist) - np.asarray(vt)
+    # invert SiLU numerically is awkward; rebuild u from the definition instead
+    vt = np.asarray(vt, dtype=np.float64)
+    w = np.asarray(conv_w, dtype=np.float64)
+    taps, L = w.shape[-1], (w.shape[-1] - 1) * dilation
+    B, T, hc, d = vt.shape
+    n_prev = np.zeros((B, L, hc, d)) if hist is None else E.rms_norm(hist, norm_w, eps)
+    n = np.concatenate([n_prev, E.rms_norm(vt, norm_w, eps)], axis=1)
+    u = sum(w[None, None, :, :, j] * n[:, L - (taps - 1 - j) * dilation:][:, :T]
+            for j in range(taps))
+    return 1 / (1 + np.exp(-u)) + vt
+
+
+def _rms_norm_eps_outside(x, weight, eps):
+    x = np.asarray(x, dtype=np.float64)
+    y = x / (np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) + eps)
+    return y if weight is None else y * weight
+
+
+def _rms_norm_over_streams(x, weight, eps):
+    x = np.asarray(x, dtype=np.float64)
+    y = x / np.sqrt(np.mean(x * x, axis=(-2, -1), keepdims=True) + eps)
+    return y if weight is None else y * weight
+
+
+def _gate_conv_updates_dead(h, k, v, q_w, k_w, dead, eps, clamp, conv_w, norm_w, dilation,
+                            conv_eps, hist=None, mode="signed_sqrt"):
+    a, _, tail = _orig["gate_conv"](h, k, v, q_w, k_w, dead, eps, clamp, conv_w, norm_w,
+                                    dilation, conv_eps, hist, mode)
+    vt = a[..., None] * np.asarray(v)[:, :, None, :]
+    return a, np.asarray(h) + E.short_conv(vt, conv_w, norm_w, dilation, conv_eps, hist), tail
+
+
+def _gate_conv_tail_ignores_hist(h, k, v, q_w, k_w, dead, eps, clamp, conv_w, norm_w, dilation,
+                                 conv_eps, hist=None, mode="signed_sqrt"):
+    a, ho, tail = _orig["gate_conv"](h, k, v, q_w, k_w, dead, eps, clamp, conv_w, norm_w,
+                                     dilation, conv_eps, hist, mode)
+    T = np.asarray(h).shape[1]
+    if T < tail.shape[1]:
+        tail = tail.copy()
+        tail[:, :tail.shape[1] - T] = 0.0
+    return a, ho, tail
 
 
 def _project_transposed(e, wkv):
@@ -130,7 +192,8 @@ def _layers_share_multipliers(ids, token_map, compressed_vocab, pad, multipliers
 
 _orig = {name: getattr(E, name) for name in
          ("mix_values", "segment_offsets", "primes_from", "ngram_cells", "gate", "project",
-          "round_to_bf16_bits", "layer_primes", "hash_rows_layers", "mx_values")}
+          "round_to_bf16_bits", "layer_primes", "hash_rows_layers", "mx_values", "short_conv",
+          "rms_norm", "gate_conv")}
 
 MUTATIONS = [
     ("mix_values", _mix_oldest_first, [P.test_worked_example_mix_and_indices]),
@@ -149,6 +212,18 @@ MUTATIONS = [
     ("hash_rows_layers", _layers_share_multipliers,
      [P.test_layers_with_own_multipliers_hit_unrelated_rows]),
     ("mx_values", _mx_block16, [P.test_mx_values_one_scale_per_32_inputs]),
+    ("gate", _gate_mode_ignored, [P.test_plain_gate_closed_forms]),
+    ("short_conv", _short_conv_taps_reversed, [P.test_short_conv_equals_torch_rmsnorm_conv1d_silu,
+                                               P.test_short_conv_tiny_by_hand]),
+    ("short_conv", _short_conv_no_dilation, [P.test_short_conv_reaches_t_minus_3_6_9]),
+    ("short_conv", _short_conv_no_residual, [P.test_short_conv_zero_filters_leave_the_gated_value]),
+    ("short_conv", _short_conv_sigmoid, [P.test_short_conv_tiny_by_hand]),
+    ("rms_norm", _rms_norm_eps_outside, [P.test_short_conv_equals_torch_rmsnorm_conv1d_silu]),
+    ("rms_norm", _rms_norm_over_streams, [P.test_short_conv_equals_torch_rmsnorm_conv1d_silu]),
+    ("gate_conv", _gate_conv_updates_dead, [P.test_gate_conv_dead_positions]),
+    ("gate_conv", _gate_conv_tail_ignores_hist,
+     [lambda: P.test_gate_conv_chunked_equals_one_shot((4, 5)),
+      lambda: P.test_gate_conv_chunked_equals_one_shot((10, 1, 1, 1))]),
 ]
 
 

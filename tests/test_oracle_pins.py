@@ -635,3 +635,182 @@ def test_gate_weights_multiply_the_dot():
     logit = lambda a: math.log(a / (1 - a))
     assert abs(a1[0, 0] - a2[0, 0]) < 1e-12
     assert abs(logit(a3[0, 0]) ** 2 - 0.25 * logit(a1[0, 0]) ** 2) < 1e-9
+
+
+# ----------------------------------------------------------------------------
+# The papers' variants: plain sigmoid gate, short convolution branch
+# ----------------------------------------------------------------------------
+
+def test_plain_gate_closed_forms():
+    """[P5] §4.1: alpha = sigmoid(s); [P1] "门控": s = sqrt(d) cos(theta)."""
+    f = _golden("layer_facts.json")
+    d = f["d"]
+    rng = np.random.default_rng(12)
+    h = rng.standard_normal(d)
+    ones = np.ones((1, d))
+
+    def plain(h, k, dd=d, eps=0.0, clamp=0.0):
+        a, _ = O.gate(h.reshape(1, 1, dd), k.reshape(1, 1, dd), np.ones((1, dd)),
+                      np.ones((1, dd)), np.ones((1, dd)), np.array([False]), eps=eps,
+                      clamp=clamp, mode="plain")
+        return a[0, 0]
+
+    # parallel at d = 5120: s = sqrt(d) = 71.55, the gate saturates
+    assert abs(plain(h, 2.0 * h) - 1 / (1 + math.exp(-math.sqrt(d)))) < 1e-12
+    assert plain(-h, h) < 1e-30
+    # d = 4, h = k: s = 2 exactly, plain sigmoid(2) against the signed root's sigmoid(sqrt 2)
+    x = np.array([1.0, -2.0, 0.5, 3.0])
+    assert abs(plain(x, x, dd=4) - 1 / (1 + math.exp(-2.0))) < 1e-12
+    a_sq, _ = O.gate(x.reshape(1, 1, 4), x.reshape(1, 1, 4), np.ones((1, 4)), np.ones((1, 4)),
+                     np.ones((1, 4)), np.array([False]), eps=0.0)
+    assert abs(a_sq[0, 0] - 1 / (1 + math.exp(-math.sqrt(2.0)))) < 1e-12
+    # orthogonal: 1/2; the clamp only enters the signed root
+    k = rng.standard_normal(d)
+    k -= h * (k @ h) / (h @ h)
+    assert abs(plain(h, k) - 0.5) < 1e-9
+    assert abs(plain(h, k, clamp=4.0) - 0.5) < 1e-9
+    for _ in range(4):
+        k = rng.standard_normal(d)
+        cos = (h @ k) / np.linalg.norm(h) / np.linalg.norm(k)
+        assert abs(plain(h, k) - 1 / (1 + math.exp(-math.sqrt(d) * cos))) < 1e-9
+    with pytest.raises(ValueError):
+        O.gate(h.reshape(1, 1, d), h.reshape(1, 1, d), ones, ones, ones, np.array([False]),
+               eps=0.0, mode="softmax")
+
+
+def _conv_case(B=2, T=14, hc=2, d=16, taps=4, seed=20):
+    rng = np.random.default_rng(seed)
+    vt = rng.standard_normal((B, T, hc, d))
+    w = rng.standard_normal((hc, d, taps))
+    g = 1 + 0.2 * rng.standard_normal((hc, d))
+    return vt, w, g
+
+
+def test_short_conv_zero_filters_leave_the_gated_value():
+    """[P5] §4.2: filters start at zero, so the branch starts as V~ itself."""
+    vt, w, g = _conv_case()
+    y = O.short_conv(vt, np.zeros_like(w), g, 3, 1e-6)
+    assert np.array_equal(y, vt)
+    rng = np.random.default_rng(21)
+    B, T, hc, d = 2, 7, 3, 32
+    h, k = rng.standard_normal((2, B, T, hc, d))
+    v = rng.standard_normal((B, T, d))
+    qw, kw = 1 + 0.1 * rng.standard_normal((2, hc, d))
+    dead = rng.random((B, T)) < 0.2
+    a0, h0 = O.gate(h.reshape(-1, hc, d), k.reshape(-1, hc, d), v.reshape(-1, d), qw, kw,
+                    dead.reshape(-1), 1e-6)
+    a1, h1, _ = O.gate_conv(h, k, v, qw, kw, dead, 1e-6, 0.0, np.zeros((hc, d, 4)), None, 3,
+                            1e-6)
+    assert np.array_equal(a1.reshape(-1, hc), a0)
+    np.testing.assert_allclose(h1.reshape(-1, hc, d), h0, rtol=0, atol=1e-13)
+
+
+def test_short_conv_equals_torch_rmsnorm_conv1d_silu():
+    """The whole branch as library routines: rms_norm, a grouped (depthwise)
+    conv1d padded by (taps-1)*dilation and cut to T outputs, silu."""
+    import torch.nn.functional as F
+    for taps, dil in ((4, 3), (1, 1), (2, 1), (3, 5)):
+        vt, w, g = _conv_case(taps=taps, seed=22 + taps)
+        B, T, hc, d = vt.shape
+        y = O.short_conv(vt, w, g, dil, 1e-5)
+        x = torch.from_numpy(vt)
+        xn = F.rms_norm(x, (d,), None, 1e-5) * torch.from_numpy(g)   # [B, T, hc, d]
+        xc = xn.reshape(B, T, hc * d).transpose(1, 2)                   # [B, C, T]
+        wt = torch.from_numpy(w).reshape(hc * d, 1, taps)
+        u = F.conv1d(xc, wt, padding=(taps - 1) * dil, dilation=dil, groups=hc * d)[..., :T]
+        ref = (F.silu(u).transpose(1, 2).reshape(B, T, hc, d) + x).numpy()
+        np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_short_conv_reaches_t_minus_3_6_9():
+    """[P5] §4.2: with 4 taps at dilation 3 position t uses t, t-3, t-6, t-9;
+    each stream is normalised and filtered on its own, each sequence too."""
+    vt, w, g = _conv_case(B=2, T=20, hc=2)
+    y0 = O.short_conv(vt, w, g, 3, 1e-6)
+    t0 = 4
+    vt2 = vt.copy()
+    vt2[1, t0, 0, 5] += 0.75
+    changed = np.any(O.short_conv(vt2, w, g, 3, 1e-6) != y0, axis=-1)   # [B, T, hc]
+    expect = np.zeros_like(changed)
+    expect[1, [t0, t0 + 3, t0 + 6, t0 + 9], 0] = True
+    assert np.array_equal(changed, expect)
+    assert O.conv_history_len(4, 3) == 9
+    # depthwise: one channel's filter moves only that channel
+    w2 = w.copy()
+    w2[1, 7, 2] += 1.0
+    diff = O.short_conv(vt, w2, g, 3, 1e-6) != y0
+    assert diff[:, :, 1, 7].any() and not np.delete(diff.reshape(2, 20, -1), 16 + 7, axis=2).any()
+
+
+def test_short_conv_tiny_by_hand():
+    """d = 2, one stream, V~ = (a, -a): RMSNorm gives (1, -1) times the norm
+    weight (eps 0), so Y = SiLU(u) + V~ with u a weighted sum of those."""
+    sig = lambda x: 1 / (1 + math.exp(-x))
+    a = 0.3
+    vt = np.array([a, -a]).reshape(1, 1, 1, 2)
+    w = np.array([2.0, 3.0]).reshape(1, 2, 1)
+    y = O.short_conv(vt, w, None, 1, 0.0).reshape(2)
+    assert abs(y[0] - (2 * sig(2) + a)) < 1e-14
+    assert abs(y[1] - (-3 * sig(-3) - a)) < 1e-14
+    # two taps, dilation 2, three positions; values (a,-a), (b,-b), (c,-c)
+    vals = [0.3, -1.5, 2.0]
+    vt = np.array([[v, -v] for v in vals]).reshape(1, 3, 1, 2)
+    w = np.array([[0.5, 4.0], [-1.0, 2.0]]).reshape(1, 2, 2)            # [hc, d, taps]
+    g = np.array([[1.0, 0.5]])
+    y = O.short_conv(vt, w, g, 2, 0.0).reshape(3, 2)
+    sgn = lambda x: math.copysign(1.0, x)
+    for t in range(3):
+        n_now = [sgn(vals[t]) * 1.0, -sgn(vals[t]) * 0.5]
+        n_back = [0.0, 0.0] if t < 2 else [sgn(vals[t - 2]), -sgn(vals[t - 2]) * 0.5]
+        for c in range(2):
+            u = w[0, c, 1] * n_now[c] + w[0, c, 0] * n_back[c]
+            assert abs(y[t, c] - (u * sig(u) + (vals[t] if c == 0 else -vals[t]))) < 1e-14
+
+
+@pytest.mark.parametrize("splits", [(1,), (2, 3), (4, 5), (9,), (10, 1, 1, 1), (13,)])
+def test_gate_conv_chunked_equals_one_shot(splits):
+    """Chunks that carry the last 9 gated values on equal the whole sequence
+    ([P5] §9.5: chunked prefill and decode keep the convolution's history)."""
+    rng = np.random.default_rng(30)
+    B, T, hc, d = 2, 16, 2, 24
+    h, k = rng.standard_normal((2, B, T, hc, d))
+    v = rng.standard_normal((B, T, d))
+    qw, kw = 1 + 0.1 * rng.standard_normal((2, hc, d))
+    cw = 0.5 * rng.standard_normal((hc, d, 4))
+    nw = 1 + 0.1 * rng.standard_normal((hc, d))
+    dead = rng.random((B, T)) < 0.15
+    a, ho, tail = O.gate_conv(h, k, v, qw, kw, dead, 1e-6, 0.0, cw, nw, 3, 1e-6)
+    hist, t0, pa, ph = None, 0, [], []
+    for n in list(splits) + [T - sum(splits)]:
+        sl = slice(t0, t0 + n)
+        a_, h_, hist = O.gate_conv(h[:, sl], k[:, sl], v[:, sl], qw, kw, dead[:, sl], 1e-6, 0.0,
+                                   cw, nw, 3, 1e-6, hist)
+        pa.append(a_)
+        ph.append(h_)
+        t0 += n
+    np.testing.assert_allclose(np.concatenate(pa, 1), a, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(np.concatenate(ph, 1), ho, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(hist, tail, rtol=0, atol=1e-14)
+    assert hist.shape == (B, 9, hc, d)
+    vt = a[..., None] * v[:, :, None, :]
+    np.testing.assert_allclose(tail, vt[:, -9:], rtol=0, atol=1e-14)
+
+
+def test_gate_conv_dead_positions():
+    """A DEAD position keeps its streams and feeds V~ = 0 to its neighbours."""
+    rng = np.random.default_rng(31)
+    B, T, hc, d = 1, 12, 2, 16
+    h, k = rng.standard_normal((2, B, T, hc, d))
+    v = rng.standard_normal((B, T, d))
+    qw = kw = np.ones((hc, d))
+    cw = rng.standard_normal((hc, d, 4))
+    dead = np.zeros((B, T), bool)
+    dead[0, 6] = True            # its own branch input is 0, but it reaches t = 3 and t = 0
+    a, ho, _ = O.gate_conv(h, k, v, qw, kw, dead, 1e-6, 0.0, cw, None, 3, 1e-6)
+    assert np.array_equal(ho[0, 6], h[0, 6]) and np.all(a[0, 6] == 0)
+    vt = a[..., None] * v[:, :, None, :]
+    assert not vt[0, 6].any()
+    y = O.short_conv(vt, cw, None, 3, 1e-6)
+    assert np.abs(y[0, 6]).min() > 0            # the branch is not zero there, yet h stays
+    live = ~dead[0]
+    np.testing.assert_allclose(ho[0, live], h[0, live] + y[0, live], rtol=0, atol=1e-13)
