@@ -20,6 +20,10 @@ MAX_TOTAL_SEGMENTS = 128
 ROW_BYTES = 264
 ROW_E4M3_E8M0_264 = 0
 ROW_F32 = 1
+GATE_SIGNED_SQRT = 0
+GATE_PLAIN = 1
+MAX_CONV_TAPS = 8
+MAX_CONV_HISTORY = 64
 
 OK, EINVAL, EVOCAB, EMULT, ESHAPE, EWORKSPACE, EHIP, EPRIMES = 0, -1, -2, -3, -4, -5, -6, -7
 
@@ -59,6 +63,23 @@ class ForwardDesc(ctypes.Structure):
         ("row_dim", ctypes.c_int32),
         ("eps", ctypes.c_float),
         ("gate_clamp", ctypes.c_float),
+        ("gate_mode", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class ShortConv(ctypes.Structure):
+    _fields_ = [
+        ("taps", ctypes.c_int32),
+        ("dilation", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+        ("reserved", ctypes.c_int32),
+        ("weight", ctypes.c_void_p),
+        ("norm_weight", ctypes.c_void_p),
+        ("state_v_in", ctypes.c_void_p),
+        ("state_s_in", ctypes.c_void_p),
+        ("state_v_out", ctypes.c_void_p),
+        ("state_s_out", ctypes.c_void_p),
     ]
 
 
@@ -83,6 +104,11 @@ def _load():
         "engram_last_hip_error": (ctypes.c_char_p, []),
         "engram_sizeof_hash_params": (SZ, []),
         "engram_sizeof_forward_desc": (SZ, []),
+        "engram_sizeof_short_conv": (SZ, []),
+        "engram_gate_conv_workspace_size": (SZ, [P]),
+        "engram_gate_conv": (ctypes.c_int, [P, P, P, I32, P, P, P, P, P, P, SZ, P]),
+        "engram_forward_conv_workspace_size": (SZ, [P, P]),
+        "engram_forward_conv": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "engram_make_primes": (ctypes.c_int, [I64, I32, P, P, P]),
         "engram_make_layer_primes": (ctypes.c_int, [I64, I32, I32, P, P, P]),
         "engram_hash_layers": (ctypes.c_int, [P, I32, P, I64, I64, P, P, P, P]),
@@ -108,6 +134,8 @@ def _load():
         raise ImportError("engram_hash_params layout mismatch between binding and library")
     if lib.engram_sizeof_forward_desc() != ctypes.sizeof(ForwardDesc):
         raise ImportError("engram_forward_desc layout mismatch between binding and library")
+    if lib.engram_sizeof_short_conv() != ctypes.sizeof(ShortConv):
+        raise ImportError("engram_short_conv layout mismatch between binding and library")
     return lib
 
 
@@ -158,12 +186,25 @@ def hash_params(raw_vocab: int, compressed_vocab: int, max_ngram: int, heads: in
 
 
 def forward_desc(batch: int, seq: int, hc: int, dim: int, table_rows: int, row_format: int,
-                 row_dim: int, eps: float = 1e-6, gate_clamp: float = 0.0) -> ForwardDesc:
+                 row_dim: int, eps: float = 1e-6, gate_clamp: float = 0.0,
+                 gate_mode: int = GATE_SIGNED_SQRT) -> ForwardDesc:
     d = ForwardDesc()
     d.batch, d.seq, d.hc, d.dim = batch, seq, hc, dim
     d.table_rows, d.row_format, d.row_dim = table_rows, row_format, row_dim
-    d.eps, d.gate_clamp = eps, gate_clamp
+    d.eps, d.gate_clamp, d.gate_mode = eps, gate_clamp, gate_mode
     return d
+
+
+def short_conv(weight, taps: int = 4, dilation: int = 3, eps: float = 1e-6, norm_weight=None,
+               state_v_in=None, state_s_in=None, state_v_out=None,
+               state_s_out=None) -> ShortConv:
+    """The short convolution branch's descriptor; tensors are kept by the caller."""
+    c = ShortConv()
+    c.taps, c.dilation, c.eps = taps, dilation, eps
+    c.weight, c.norm_weight = _ptr(weight), _ptr(norm_weight)
+    c.state_v_in, c.state_s_in = _ptr(state_v_in), _ptr(state_s_in)
+    c.state_v_out, c.state_s_out = _ptr(state_v_out), _ptr(state_s_out)
+    return c
 
 
 def engram_make_primes(base: int, count: int):
@@ -276,3 +317,29 @@ def engram_forward_mx(params: HashParams, desc: ForwardDesc, ids, hist_in, hist_
                                  _ptr(w_scales), _ptr(q_w), _ptr(k_w), _ptr(h), _ptr(gate_out),
                                  _ptr(workspace), workspace_bytes, _stream(stream)),
            "engram_forward_mx")
+
+
+def engram_gate_conv_workspace_size(desc: ForwardDesc) -> int:
+    return int(LIB.engram_gate_conv_workspace_size(ctypes.byref(desc)))
+
+
+def engram_gate_conv(desc: ForwardDesc, conv: ShortConv, ids, raw_vocab: int, kv, q_w, k_w, h,
+                     gate_out, workspace, workspace_bytes: int, stream=None):
+    _check(LIB.engram_gate_conv(ctypes.byref(desc), ctypes.byref(conv), _ptr(ids), raw_vocab,
+                                _ptr(kv), _ptr(q_w), _ptr(k_w), _ptr(h), _ptr(gate_out),
+                                _ptr(workspace), workspace_bytes, _stream(stream)),
+           "engram_gate_conv")
+
+
+def engram_forward_conv_workspace_size(params: HashParams, desc: ForwardDesc) -> int:
+    return int(LIB.engram_forward_conv_workspace_size(ctypes.byref(params), ctypes.byref(desc)))
+
+
+def engram_forward_conv(params: HashParams, desc: ForwardDesc, conv: ShortConv, ids, hist_in,
+                        hist_out, table, wkv, q_w, k_w, h, gate_out, workspace,
+                        workspace_bytes: int, stream=None):
+    _check(LIB.engram_forward_conv(ctypes.byref(params), ctypes.byref(desc), ctypes.byref(conv),
+                                   _ptr(ids), _ptr(hist_in), _ptr(hist_out), _ptr(table),
+                                   _ptr(wkv), _ptr(q_w), _ptr(k_w), _ptr(h), _ptr(gate_out),
+                                   _ptr(workspace), workspace_bytes, _stream(stream)),
+           "engram_forward_conv")

@@ -33,6 +33,59 @@ __device__ __forceinline__ float warp_sum(float v) {
   return v;
 }
 
+// Eight consecutive elements of a bf16 (F32 = false) or fp32 row, addressed by
+// chunk index: one 16-byte or two 16-byte accesses.
+template <bool F32>
+struct Chunk8;
+template <>
+struct Chunk8<false> {
+  uint4 v;
+  __device__ __forceinline__ void load(const void *p, int64_t i) {
+    v = reinterpret_cast<const uint4 *>(p)[i];
+  }
+  __device__ __forceinline__ void zero() { v = make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ void put(void *p, int64_t i) const {
+    reinterpret_cast<uint4 *>(p)[i] = v;
+  }
+  __device__ __forceinline__ float operator[](int e) const {
+    const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+    return bf16_to_f32((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+  }
+  __device__ __forceinline__ static void store(void *p, int64_t i, const float f[8]) {
+    uint4 o;
+    o.x = pack_bf16x2(f[0], f[1]);
+    o.y = pack_bf16x2(f[2], f[3]);
+    o.z = pack_bf16x2(f[4], f[5]);
+    o.w = pack_bf16x2(f[6], f[7]);
+    reinterpret_cast<uint4 *>(p)[i] = o;
+  }
+};
+template <>
+struct Chunk8<true> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const void *p, int64_t i) {
+    a = reinterpret_cast<const float4 *>(p)[2 * i];
+    b = reinterpret_cast<const float4 *>(p)[2 * i + 1];
+  }
+  __device__ __forceinline__ void zero() {
+    a = make_float4(0.f, 0.f, 0.f, 0.f);
+    b = a;
+  }
+  __device__ __forceinline__ void put(void *p, int64_t i) const {
+    reinterpret_cast<float4 *>(p)[2 * i] = a;
+    reinterpret_cast<float4 *>(p)[2 * i + 1] = b;
+  }
+  __device__ __forceinline__ float operator[](int e) const {
+    const float4 &q = e < 4 ? a : b;
+    const int r = e & 3;
+    return r == 0 ? q.x : r == 1 ? q.y : r == 2 ? q.z : q.w;
+  }
+  __device__ __forceinline__ static void store(void *p, int64_t i, const float f[8]) {
+    reinterpret_cast<float4 *>(p)[2 * i] = make_float4(f[0], f[1], f[2], f[3]);
+    reinterpret_cast<float4 *>(p)[2 * i + 1] = make_float4(f[4], f[5], f[6], f[7]);
+  }
+};
+
 }  // namespace engram
 
 // Launchers implemented by the kernel translation units. They validate nothing:
@@ -84,7 +137,27 @@ hipError_t engram_gemm_mx_workspace(int64_t m, int64_t n, int32_t segments, size
 hipError_t engram_launch_gemm_f32(const float *e, const float *w, float *kv, int64_t m,
                                   int64_t n, int64_t k, hipStream_t stream);
 
+// stats == NULL: the gate and the residual update. stats != NULL (float
+// [tokens, hc + 1]): gates and the value row's mean square per token, h
+// untouched. plain selects sigmoid(s) over the signed root.
 hipError_t engram_launch_gate(bool f32, const int32_t *ids, int32_t raw_vocab,
                               const void *kv, const float *q_w, const float *k_w,
-                              void *h, float *gate_out, int64_t tokens, int32_t hc,
-                              int32_t dim, float eps, float clamp, hipStream_t stream);
+                              void *h, float *gate_out, float *stats, int64_t tokens,
+                              int32_t hc, int32_t dim, float eps, float clamp, int plain,
+                              hipStream_t stream);
+
+// Short convolution branch and its history (conv.hip).
+struct EngramConvArgs {
+  int taps, dilation, history;   // history = (taps - 1) * dilation
+  float eps;
+  const float *weight;           // [hc, dim, taps]
+  const float *norm_weight;      // [hc, dim] or NULL
+  const void *state_v_in;        // [batch, history, dim] kv dtype, or NULL
+  const float *state_s_in;       // [batch, history, hc + 1]
+  void *state_v_out;             // or NULL
+  float *state_s_out;
+};
+hipError_t engram_launch_short_conv(bool f32, const EngramConvArgs &c, const int32_t *ids,
+                                    int32_t raw_vocab, const void *kv, const float *stats,
+                                    void *h, int64_t batch, int64_t seq, int32_t hc,
+                                    int32_t dim, hipStream_t stream);

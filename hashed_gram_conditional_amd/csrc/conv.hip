@@ -1,0 +1,215 @@
+// The short convolution branch after the gate, and its history across chunks.
+//
+// Pages: "DeepSeek Engram 详解：把静态知识从计算里拆出来" §4.2 (Y = SiLU(Conv1D(
+// RMSNorm(V~))) + V~ on the gated values V~ = alpha v, depthwise and causal,
+// kernel size 4 at dilation 3 so that position t reads t, t-3, t-6, t-9, filters
+// starting at zero, H += Y) and §9.5 (decode and chunked prefill keep the past 9
+// positions); "条件记忆：DeepSeek V4.1 Engram 如何用 O(1) 查表换掉一层计算" §三
+// (output = value + short_conv(value)); "DeepSeek-V4.1 模型结构（5）：记忆，Engram",
+// "V4.1 相对原版的两处改动" (the branch the original design had after the gate).
+//
+// The gate kernel has already stored, per token, the hc gates and the mean
+// square of the value row v. The gated value of stream m is alpha_m v, so its
+// RMS is |alpha_m| rms(v): the normalised input is
+//   n = alpha_m v / sqrt(alpha_m^2 mean(v^2) + eps) * g_m
+// and no (token, stream) vector has to be reduced again. Each thread owns one
+// stream and 8 channels, keeps their filters (8 x taps) and norm weights in
+// registers, and walks a run of consecutive tokens, so the filters are read once
+// per run. The value rows a token reaches lie at most (taps - 1) dilation rows
+// back and are shared by the hc streams and the run's neighbours: they come from
+// the L2. h is read and written once. Arithmetic is fp32; h is rounded once.
+//
+// The history of a sequence is the last L = (taps - 1) dilation positions in
+// factored form: their value rows (kv's dtype) and [alpha_0..alpha_{hc-1},
+// mean(v^2)] (fp32), which rebuild V~ exactly as the chunk's own positions do.
+#include "common.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunk = 8;
+
+template <bool F32, int TAPS>
+__global__ __launch_bounds__(kThreads) void short_conv_kernel(
+    EngramConvArgs c, const int32_t *__restrict__ ids, int32_t raw_vocab,
+    const void *__restrict__ kv, const float *__restrict__ stats, void *__restrict__ h,
+    int64_t ntok, int64_t seq, int hc, int dim, int tpb) {
+  const int cps = dim / kChunk;
+  const int p = blockIdx.y * kThreads + threadIdx.x;
+  if (p >= hc * cps) return;
+  const int m = p / cps;
+  const int ci = p - m * cps;
+
+  float w[kChunk][TAPS];
+  {
+    const float4 *wp =
+        reinterpret_cast<const float4 *>(c.weight + ((int64_t)m * dim + ci * kChunk) * TAPS);
+#pragma unroll
+    for (int q = 0; q < 2 * TAPS; ++q) {
+      const float4 f = wp[q];
+      const float fv[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[(4 * q + r) / TAPS][(4 * q + r) % TAPS] = fv[r];
+    }
+  }
+  float g[kChunk];
+  if (c.norm_weight != nullptr) {
+    const float4 *gp = reinterpret_cast<const float4 *>(c.norm_weight + (int64_t)m * dim) + 2 * ci;
+    const float4 g0 = gp[0], g1 = gp[1];
+    g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
+    g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < kChunk; ++e) g[e] = 1.f;
+  }
+
+  const int64_t kv_row = (int64_t)(hc + 1) * cps;   // chunks per kv row
+  const int64_t t0 = (int64_t)blockIdx.x * tpb;
+  const int64_t t1 = t0 + tpb < ntok ? t0 + tpb : ntok;
+  for (int64_t t = t0; t < t1; ++t) {
+    const int32_t x = ids[t];
+    if (x < 0 || x >= raw_vocab) continue;          // DEAD: streams untouched
+    const int64_t b = t / seq;
+    const int64_t s = t - b * seq;
+    float u[kChunk], vt[kChunk];
+#pragma unroll
+    for (int e = 0; e < kChunk; ++e) {
+      u[e] = 0.f;
+      vt[e] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < TAPS; ++j) {
+      const int64_t back = (int64_t)(TAPS - 1 - j) * c.dilation;
+      engram::Chunk8<F32> v;
+      float a, ms;
+      if (s >= back) {                                // inside the chunk
+        const int64_t row = t - back;
+        v.load(kv, row * kv_row + (int64_t)hc * cps + ci);
+        a = stats[row * (hc + 1) + m];
+        ms = stats[row * (hc + 1) + hc];
+      } else if (c.state_v_in != nullptr) {           // the sequence's history
+        const int64_t srow = b * c.history + c.history + (s - back);
+        v.load(c.state_v_in, srow * cps + ci);
+        a = c.state_s_in[srow * (hc + 1) + m];
+        ms = c.state_s_in[srow * (hc + 1) + hc];
+      } else {
+        continue;                                     // before the sequence start: zero
+      }
+      const float r = a / sqrtf(a * a * ms + c.eps);
+#pragma unroll
+      for (int e = 0; e < kChunk; ++e) u[e] = fmaf(w[e][j], r * v[e] * g[e], u[e]);
+      if (j == TAPS - 1) {
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) vt[e] = a * v[e];
+      }
+    }
+    const int64_t hi = (t * hc + m) * (int64_t)cps + ci;
+    engram::Chunk8<F32> hh;
+    hh.load(h, hi);
+    float o[kChunk];
+#pragma unroll
+    for (int e = 0; e < kChunk; ++e) o[e] = hh[e] + (u[e] / (1.f + expf(-u[e])) + vt[e]);
+    engram::Chunk8<F32>::store(h, hi, o);
+  }
+}
+
+// History after the chunk: position q of the new history is entry q + T of
+// [old history (L) ; chunk (T)]. One block column per sequence; each thread
+// owns one 8-element column of the value rows (and the first hc + 1 threads of
+// the first block one column of the scalars) and walks q upwards, so a read
+// never meets an entry this call has already overwritten: the output may alias
+// the input. Runs after the convolution on the same stream.
+template <bool F32>
+__global__ __launch_bounds__(kThreads) void conv_state_kernel(
+    EngramConvArgs c, const void *__restrict__ kv, const float *__restrict__ stats,
+    int64_t seq, int hc, int dim) {
+  const int64_t b = blockIdx.x;
+  const int cps = dim / kChunk;
+  const int ci = blockIdx.y * kThreads + threadIdx.x;
+  const int L = c.history;
+  const int64_t kv_row = (int64_t)(hc + 1) * cps;
+  if (ci < cps) {
+    for (int q = 0; q < L; ++q) {
+      const int64_t x = q + seq;
+      engram::Chunk8<F32> v;
+      if (x >= L)
+        v.load(kv, (b * seq + x - L) * kv_row + (int64_t)hc * cps + ci);
+      else if (c.state_v_in != nullptr)
+        v.load(c.state_v_in, (b * L + x) * cps + ci);
+      else
+        v.zero();
+      v.put(c.state_v_out, (b * L + q) * cps + ci);
+    }
+  }
+  if (blockIdx.y == 0 && (int)threadIdx.x <= hc) {
+    const int col = threadIdx.x;
+    for (int q = 0; q < L; ++q) {
+      const int64_t x = q + seq;
+      float f = 0.f;
+      if (x >= L)
+        f = stats[(b * seq + x - L) * (hc + 1) + col];
+      else if (c.state_s_in != nullptr)
+        f = c.state_s_in[(b * L + x) * (hc + 1) + col];
+      c.state_s_out[(b * L + q) * (hc + 1) + col] = f;
+    }
+  }
+}
+
+template <bool F32>
+hipError_t launch(const EngramConvArgs &c, const int32_t *ids, int32_t raw_vocab, const void *kv,
+                  const float *stats, void *h, int64_t batch, int64_t seq, int hc, int dim,
+                  hipStream_t stream) {
+  const int64_t ntok = batch * seq;
+  const int cps = dim / kChunk;
+  if (ntok > 0) {
+    int dev = 0, cus = 256;
+    hipError_t err = hipGetDevice(&dev);
+    if (err == hipSuccess)
+      err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
+    const int gy = (hc * cps + kThreads - 1) / kThreads;
+    // Runs of up to 16 tokens per thread while that still leaves about 8
+    // blocks per CU; one token per run for decode-sized calls.
+    int64_t tpb = ntok * gy / (8 * (int64_t)cus);
+    tpb = tpb < 1 ? 1 : tpb > 16 ? 16 : tpb;
+    const dim3 grid((unsigned)((ntok + tpb - 1) / tpb), (unsigned)gy);
+#define ENGRAM_CONV_CASE(N)                                                                 \
+  case N:                                                                                   \
+    hipLaunchKernelGGL((short_conv_kernel<F32, N>), grid, dim3(kThreads), 0, stream, c, ids, \
+                       raw_vocab, kv, stats, h, ntok, seq, hc, dim, (int)tpb);              \
+    break;
+    switch (c.taps) {
+      ENGRAM_CONV_CASE(1)
+      ENGRAM_CONV_CASE(2)
+      ENGRAM_CONV_CASE(3)
+      ENGRAM_CONV_CASE(4)
+      ENGRAM_CONV_CASE(5)
+      ENGRAM_CONV_CASE(6)
+      ENGRAM_CONV_CASE(7)
+      ENGRAM_CONV_CASE(8)
+      default:
+        return hipErrorInvalidValue;
+    }
+#undef ENGRAM_CONV_CASE
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (c.state_v_out != nullptr && batch > 0 && c.history > 0) {
+    const int cols = cps > hc + 1 ? cps : hc + 1;
+    const dim3 grid((unsigned)batch, (unsigned)((cols + kThreads - 1) / kThreads));
+    hipLaunchKernelGGL((conv_state_kernel<F32>), grid, dim3(kThreads), 0, stream, c, kv, stats,
+                       seq, hc, dim);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t engram_launch_short_conv(bool f32, const EngramConvArgs &c, const int32_t *ids,
+                                    int32_t raw_vocab, const void *kv, const float *stats,
+                                    void *h, int64_t batch, int64_t seq, int32_t hc,
+                                    int32_t dim, hipStream_t stream) {
+  return f32 ? launch<true>(c, ids, raw_vocab, kv, stats, h, batch, seq, hc, dim, stream)
+             : launch<false>(c, ids, raw_vocab, kv, stats, h, batch, seq, hc, dim, stream);
+}

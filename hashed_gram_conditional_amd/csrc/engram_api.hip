@@ -146,7 +146,45 @@ int check_desc(const engram_forward_desc *d) {
   if (d->row_format == ENGRAM_ROW_F32 && (d->row_dim < 4 || d->row_dim % 4 != 0))
     return ENGRAM_ESHAPE;
   if (!(d->eps >= 0.f) || !(d->gate_clamp >= 0.f)) return ENGRAM_EINVAL;
+  if (d->gate_mode != ENGRAM_GATE_SIGNED_SQRT && d->gate_mode != ENGRAM_GATE_PLAIN)
+    return ENGRAM_EINVAL;
+  if (d->reserved != 0) return ENGRAM_EINVAL;
   return ENGRAM_OK;
+}
+
+int check_conv(const engram_short_conv *c) {
+  if (c == nullptr || c->reserved != 0) return ENGRAM_EINVAL;
+  if (c->taps < 1 || c->taps > ENGRAM_MAX_CONV_TAPS || c->dilation < 1) return ENGRAM_ESHAPE;
+  if ((int64_t)(c->taps - 1) * c->dilation > ENGRAM_MAX_CONV_HISTORY) return ENGRAM_ESHAPE;
+  if (!(c->eps > 0.f) || !(c->eps < INFINITY)) return ENGRAM_EINVAL;
+  if (c->weight == nullptr || !aligned(c->weight, 16) || !aligned(c->norm_weight, 16))
+    return ENGRAM_EINVAL;
+  if ((c->state_v_in == nullptr) != (c->state_s_in == nullptr) ||
+      (c->state_v_out == nullptr) != (c->state_s_out == nullptr))
+    return ENGRAM_EINVAL;
+  if (!aligned(c->state_v_in, 16) || !aligned(c->state_v_out, 16) ||
+      !aligned(c->state_s_in, 4) || !aligned(c->state_s_out, 4))
+    return ENGRAM_EINVAL;
+  return ENGRAM_OK;
+}
+
+EngramConvArgs make_conv_args(const engram_short_conv *c) {
+  EngramConvArgs a;
+  a.taps = c->taps;
+  a.dilation = c->dilation;
+  a.history = (c->taps - 1) * c->dilation;
+  a.eps = c->eps;
+  a.weight = c->weight;
+  a.norm_weight = c->norm_weight;
+  a.state_v_in = c->state_v_in;
+  a.state_s_in = c->state_s_in;
+  a.state_v_out = c->state_v_out;
+  a.state_s_out = c->state_s_out;
+  return a;
+}
+
+size_t gate_conv_workspace(const engram_forward_desc *d) {
+  return align256((size_t)(d->batch * d->seq) * (size_t)(d->hc + 1) * sizeof(float));
 }
 
 // The last HIP error an entry point returned ENGRAM_EHIP for, per host thread.
@@ -181,6 +219,8 @@ const char *engram_last_hip_error(void) { return hipGetErrorString(g_last_hip_er
 size_t engram_sizeof_hash_params(void) { return sizeof(engram_hash_params); }
 
 size_t engram_sizeof_forward_desc(void) { return sizeof(engram_forward_desc); }
+
+size_t engram_sizeof_short_conv(void) { return sizeof(engram_short_conv); }
 
 int engram_make_primes(int64_t base, int32_t count, int64_t *primes_out, int64_t *offsets_out,
                        int64_t *total_rows_out) {
@@ -379,8 +419,48 @@ int engram_gate(const engram_forward_desc *desc, const int32_t *ids, int32_t raw
     return ENGRAM_EINVAL;
   if (ntok > INT32_MAX) return ENGRAM_ESHAPE;
   return hip_status(engram_launch_gate(desc->row_format == ENGRAM_ROW_F32, ids, raw_vocab, kv,
-                                       q_w, k_w, h, gate_out, ntok, desc->hc, desc->dim,
-                                       desc->eps, desc->gate_clamp, stream));
+                                       q_w, k_w, h, gate_out, nullptr, ntok, desc->hc,
+                                       desc->dim, desc->eps, desc->gate_clamp, desc->gate_mode,
+                                       stream));
+}
+
+size_t engram_gate_conv_workspace_size(const engram_forward_desc *desc) {
+  if (check_desc(desc) != ENGRAM_OK) return 0;
+  return gate_conv_workspace(desc);
+}
+
+int engram_gate_conv(const engram_forward_desc *desc, const engram_short_conv *conv,
+                     const int32_t *ids, int32_t raw_vocab, const void *kv, const float *q_w,
+                     const float *k_w, void *h, float *gate_out, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_desc(desc);
+  if (rc != ENGRAM_OK) return rc;
+  rc = check_conv(conv);
+  if (rc != ENGRAM_OK) return rc;
+  if (raw_vocab < 1) return ENGRAM_EINVAL;
+  const int64_t ntok = desc->batch * desc->seq;
+  if (ntok > INT32_MAX) return ENGRAM_ESHAPE;
+  if (ntok > 0) {
+    if (ids == nullptr || kv == nullptr || q_w == nullptr || k_w == nullptr || h == nullptr)
+      return ENGRAM_EINVAL;
+    if (!aligned(ids, 4) || !aligned(kv, 16) || !aligned(q_w, 16) || !aligned(k_w, 16) ||
+        !aligned(h, 16) || !aligned(gate_out, 4))
+      return ENGRAM_EINVAL;
+    if (workspace == nullptr || workspace_bytes < gate_conv_workspace(desc) ||
+        !aligned(workspace, 256))
+      return ENGRAM_EWORKSPACE;
+  }
+  const bool f32 = desc->row_format == ENGRAM_ROW_F32;
+  float *stats = (float *)workspace;
+  if (ntok > 0) {
+    hipError_t err = engram_launch_gate(f32, ids, raw_vocab, kv, q_w, k_w, h, gate_out, stats,
+                                        ntok, desc->hc, desc->dim, desc->eps, desc->gate_clamp,
+                                        desc->gate_mode, stream);
+    if (err != hipSuccess) return hip_status(err);
+  }
+  return hip_status(engram_launch_short_conv(f32, make_conv_args(conv), ids, raw_vocab, kv, stats,
+                                             h, desc->batch, desc->seq, desc->hc, desc->dim,
+                                             stream));
 }
 
 size_t engram_forward_workspace_size(const engram_hash_params *params,
@@ -397,15 +477,22 @@ size_t engram_forward_workspace_size(const engram_hash_params *params,
          engram_project_workspace_size(ntok, in_dim, out_dim, f32 ? 1 : 0);
 }
 
-int engram_forward(const engram_hash_params *params, const engram_forward_desc *desc,
-                   const int32_t *ids, const int32_t *hist_in, int32_t *hist_out,
-                   const void *table, const void *wkv, const float *q_w, const float *k_w,
-                   void *h, float *gate_out, void *workspace, size_t workspace_bytes,
-                   hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// engram_forward and engram_forward_conv: steps 1-4, then the gate alone
+// (conv == NULL) or the gate and the short convolution branch.
+int forward_impl(const engram_hash_params *params, const engram_forward_desc *desc,
+                 const engram_short_conv *conv, const int32_t *ids, const int32_t *hist_in,
+                 int32_t *hist_out, const void *table, const void *wkv, const float *q_w,
+                 const float *k_w, void *h, float *gate_out, void *workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
   int rc = check_hash_params(params);
   if (rc != ENGRAM_OK) return rc;
   rc = check_desc(desc);
   if (rc != ENGRAM_OK) return rc;
+  if (conv != nullptr && (rc = check_conv(conv)) != ENGRAM_OK) return rc;
   if (total_rows(params) > desc->table_rows) return ENGRAM_EPRIMES;
   const int64_t ntok = desc->batch * desc->seq;
   const int64_t S = (int64_t)(params->max_ngram - 1) * params->heads;
@@ -421,13 +508,21 @@ int engram_forward(const engram_hash_params *params, const engram_forward_desc *
     if (!aligned(ids, 4) || !aligned(table, 16) || !aligned(wkv, 16) || !aligned(q_w, 16) ||
         !aligned(k_w, 16) || !aligned(h, 16) || !aligned(gate_out, 4))
       return ENGRAM_EINVAL;
-    const size_t need = engram_forward_workspace_size(params, desc);
+    const size_t need = engram_forward_workspace_size(params, desc) +
+                        (conv != nullptr ? gate_conv_workspace(desc) : 0);
     if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
       return ENGRAM_EWORKSPACE;
   }
   if (!aligned(hist_in, 4) || !aligned(hist_out, 4)) return ENGRAM_EINVAL;
 
+  // The convolution's per-token stats lead the workspace; the rest is
+  // engram_forward's layout.
+  float *stats = (float *)workspace;
   char *ws = (char *)workspace;
+  if (conv != nullptr && ntok > 0) {
+    ws += gate_conv_workspace(desc);
+    workspace_bytes -= gate_conv_workspace(desc);
+  }
   const size_t esz = f32 ? 4 : 2;
   int64_t *row_ids = (int64_t *)ws;
   void *e = ws + align256((size_t)ntok * S * 8);
@@ -438,7 +533,15 @@ int engram_forward(const engram_hash_params *params, const engram_forward_desc *
   const EngramHashArgs a = make_hash_args(params, 1);
   hipError_t err = engram_launch_hash(a, params->token_map, ids, desc->batch, desc->seq,
                                       hist_in, hist_out, row_ids, stream);
-  if (err != hipSuccess || ntok == 0) return hip_status(err);
+  if (err != hipSuccess) return hip_status(err);
+  if (ntok == 0) {
+    // An empty chunk still passes the convolution's history on.
+    if (conv != nullptr)
+      err = engram_launch_short_conv(f32, make_conv_args(conv), ids, params->raw_vocab, nullptr,
+                                     nullptr, h, desc->batch, desc->seq, desc->hc, desc->dim,
+                                     stream);
+    return hip_status(err);
+  }
   err = f32 ? engram_launch_gather_f32((const float *)table, desc->table_rows, desc->row_dim,
                                        row_ids, ntok * S, (float *)e, stream)
             : engram_launch_gather_e4m3((const uint8_t *)table, desc->table_rows, row_ids,
@@ -450,10 +553,46 @@ int engram_forward(const engram_hash_params *params, const engram_forward_desc *
                                       (uint16_t *)kv, ntok, out_dim, in_dim, gemm_ws,
                                       gemm_ws_bytes, stream);
   if (err != hipSuccess) return hip_status(err);
-  err = engram_launch_gate(f32, ids, params->raw_vocab, kv, q_w, k_w, h, gate_out, ntok,
-                           desc->hc, desc->dim, desc->eps, desc->gate_clamp, stream);
+  err = engram_launch_gate(f32, ids, params->raw_vocab, kv, q_w, k_w, h, gate_out,
+                           conv != nullptr ? stats : nullptr, ntok, desc->hc, desc->dim,
+                           desc->eps, desc->gate_clamp, desc->gate_mode, stream);
+  if (err != hipSuccess || conv == nullptr) return hip_status(err);
+  err = engram_launch_short_conv(f32, make_conv_args(conv), ids, params->raw_vocab, kv, stats, h,
+                                 desc->batch, desc->seq, desc->hc, desc->dim, stream);
   return hip_status(err);
 }
+
+}  // namespace
+
+extern "C" {
+
+int engram_forward(const engram_hash_params *params, const engram_forward_desc *desc,
+                   const int32_t *ids, const int32_t *hist_in, int32_t *hist_out,
+                   const void *table, const void *wkv, const float *q_w, const float *k_w,
+                   void *h, float *gate_out, void *workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+  return forward_impl(params, desc, nullptr, ids, hist_in, hist_out, table, wkv, q_w, k_w, h,
+                      gate_out, workspace, workspace_bytes, stream);
+}
+
+size_t engram_forward_conv_workspace_size(const engram_hash_params *params,
+                                          const engram_forward_desc *desc) {
+  const size_t base = engram_forward_workspace_size(params, desc);
+  return base == 0 ? 0 : base + gate_conv_workspace(desc);
+}
+
+int engram_forward_conv(const engram_hash_params *params, const engram_forward_desc *desc,
+                        const engram_short_conv *conv, const int32_t *ids,
+                        const int32_t *hist_in, int32_t *hist_out, const void *table,
+                        const void *wkv, const float *q_w, const float *k_w, void *h,
+                        float *gate_out, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  if (conv == nullptr) return ENGRAM_EINVAL;
+  return forward_impl(params, desc, conv, ids, hist_in, hist_out, table, wkv, q_w, k_w, h,
+                      gate_out, workspace, workspace_bytes, stream);
+}
+
+
 
 size_t engram_forward_mx_workspace_size(const engram_hash_params *params,
                                         const engram_forward_desc *desc) {
@@ -513,8 +652,9 @@ int engram_forward_mx(const engram_hash_params *params, const engram_forward_des
   err = engram_launch_gemm_mx((const uint8_t *)w_codes, (const uint8_t *)w_scales, e_rows, S, kv,
                               ntok, out_dim, gemm_ws, gemm_ws_bytes, stream);
   if (err != hipSuccess) return hip_status(err);
-  err = engram_launch_gate(false, ids, params->raw_vocab, kv, q_w, k_w, h, gate_out, ntok,
-                           desc->hc, desc->dim, desc->eps, desc->gate_clamp, stream);
+  err = engram_launch_gate(false, ids, params->raw_vocab, kv, q_w, k_w, h, gate_out, nullptr,
+                           ntok, desc->hc, desc->dim, desc->eps, desc->gate_clamp,
+                           desc->gate_mode, stream);
   return hip_status(err);
 }
 

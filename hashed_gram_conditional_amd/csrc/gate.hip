@@ -4,8 +4,9 @@
 // Pages: "DeepSeek-V4.1 模型结构（5）：记忆，Engram", "门控：用当前的上下文决定查到的向量用多少"
 // (s^(m) = RMSNorm(h^(m)) . RMSNorm(k^(m)) / sqrt(d), h^(m) += alpha^(m) v, one
 // shared v for all streams), "sigmoid 之前多一步带符号的平方根" (the signed
-// square root before the sigmoid, with a clamp on |s|) and the image-token
-// paragraph (gate 0 at DEAD positions); "ds4.c 学习笔记 · Engram", "消费：学习投影 +
+// square root before the sigmoid, with a clamp on |s|, and the papers' plain
+// sigmoid(s) it departs from, also "DeepSeek Engram 详解：把静态知识从计算里拆出来"
+// §4.1) and the image-token paragraph (gate 0 at DEAD positions); "ds4.c 学习笔记 · Engram", "消费：学习投影 +
 // 余弦门控" (the learned scales q_w * k_w inside the dot, eps inside the
 // reciprocal roots of the mean squares, the update rounded to bf16 once) and
 // "布局与哈希探测" item 4 (masked rows are left untouched).
@@ -16,6 +17,10 @@
 // (sum h^2, sum k^2, sum h q_w k_w k) run first; the update then reads the
 // token's h again, which the L2 still holds (40 KiB per token), instead of
 // keeping it in registers, so more blocks fit per CU. All arithmetic is fp32.
+//
+// With a stats buffer the kernel is the first half of the short-convolution
+// variant: it stores each token's gates and the mean square of its value row
+// (the factors of the gated value's RMS) and leaves h to the convolution.
 #include "common.h"
 
 namespace {
@@ -25,56 +30,22 @@ constexpr int kMaxHc = 8;
 constexpr int kChunk = 8;        // elements per chunk
 
 template <bool F32>
-struct Chunk;
-template <>
-struct Chunk<false> {   // 8 bf16
-  uint4 v;
-  __device__ __forceinline__ void load(const void *p, int64_t i) {
-    v = reinterpret_cast<const uint4 *>(p)[i];
-  }
-  __device__ __forceinline__ float operator[](int e) const {
-    const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
-    return engram::bf16_to_f32((e & 1) ? (w >> 16) : (w & 0xFFFFu));
-  }
-  __device__ __forceinline__ static void store(void *p, int64_t i, const float f[8]) {
-    uint4 o;
-    o.x = engram::pack_bf16x2(f[0], f[1]);
-    o.y = engram::pack_bf16x2(f[2], f[3]);
-    o.z = engram::pack_bf16x2(f[4], f[5]);
-    o.w = engram::pack_bf16x2(f[6], f[7]);
-    reinterpret_cast<uint4 *>(p)[i] = o;
-  }
-};
-template <>
-struct Chunk<true> {    // 8 fp32
-  float4 a, b;
-  __device__ __forceinline__ void load(const void *p, int64_t i) {
-    a = reinterpret_cast<const float4 *>(p)[2 * i];
-    b = reinterpret_cast<const float4 *>(p)[2 * i + 1];
-  }
-  __device__ __forceinline__ float operator[](int e) const {
-    const float4 &q = e < 4 ? a : b;
-    const int r = e & 3;
-    return r == 0 ? q.x : r == 1 ? q.y : r == 2 ? q.z : q.w;
-  }
-  __device__ __forceinline__ static void store(void *p, int64_t i, const float f[8]) {
-    reinterpret_cast<float4 *>(p)[2 * i] = make_float4(f[0], f[1], f[2], f[3]);
-    reinterpret_cast<float4 *>(p)[2 * i + 1] = make_float4(f[4], f[5], f[6], f[7]);
-  }
-};
+using Chunk = engram::Chunk8<F32>;
 
 template <bool F32, int CPT>
 __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
     const int32_t *__restrict__ ids, int32_t raw_vocab, const void *__restrict__ kv,
     const float *__restrict__ q_w, const float *__restrict__ k_w, void *__restrict__ h,
-    float *__restrict__ gate_out, int hc, int dim, float eps, float clamp) {
-  __shared__ float red[kMaxThreads / engram::kWave][3 * kMaxHc];
+    float *__restrict__ gate_out, float *__restrict__ stats, int hc, int dim, float eps,
+    float clamp, int plain) {
+  __shared__ float red[kMaxThreads / engram::kWave][3 * kMaxHc + 1];
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x;
   const int nthreads = blockDim.x;
   const int32_t x = ids[t];
   if (x < 0 || x >= raw_vocab) {          // DEAD: gate 0, streams untouched
     if (gate_out != nullptr && tid < hc) gate_out[t * hc + tid] = 0.f;
+    if (stats != nullptr && tid <= hc) stats[t * (hc + 1) + tid] = 0.f;
     return;
   }
   const int cps = dim / kChunk;                   // chunks per stream
@@ -120,6 +91,19 @@ __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
   }
   const int wave = tid >> 6;
   const int lane = tid & 63;
+  if (stats != nullptr) {
+    float svv = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ci = tid + c * nthreads;
+      if (ci < cps) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) svv = fmaf(vv[c][e], vv[c][e], svv);
+      }
+    }
+    svv = engram::warp_sum(svv);
+    if (lane == 0) red[wave][3 * kMaxHc] = svv;
+  }
 #pragma unroll
   for (int m = 0; m < kMaxHc; ++m) {
     if (m < hc) {
@@ -151,7 +135,7 @@ __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
       const float rh = 1.0f / sqrtf(a * inv_d + eps);
       const float rk = 1.0f / sqrtf(b * inv_d + eps);
       const float s = c * rh * rk * inv_sqrt_d;
-      const float z = copysignf(sqrtf(fmaxf(fabsf(s), clamp)), s);
+      const float z = plain ? s : copysignf(sqrtf(fmaxf(fabsf(s), clamp)), s);
       alpha[m] = 1.0f / (1.0f + expf(-z));
     }
   }
@@ -159,6 +143,18 @@ __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
 #pragma unroll
     for (int m = 0; m < kMaxHc; ++m)
       if (m == tid) gate_out[t * hc + m] = alpha[m];
+  }
+  if (stats != nullptr) {
+    if (tid < hc) {
+#pragma unroll
+      for (int m = 0; m < kMaxHc; ++m)
+        if (m == tid) stats[t * (hc + 1) + m] = alpha[m];
+    } else if (tid == hc) {
+      float svv = 0.f;
+      for (int w = 0; w < (nthreads >> 6); ++w) svv += red[w][3 * kMaxHc];
+      stats[t * (hc + 1) + hc] = svv * inv_d;
+    }
+    return;
   }
 #pragma unroll
   for (int m = 0; m < kMaxHc; ++m) {
@@ -181,14 +177,14 @@ __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
 
 template <bool F32>
 hipError_t launch(int cpt, int threads, const int32_t *ids, int32_t raw_vocab, const void *kv,
-                  const float *q_w, const float *k_w, void *h, float *gate_out,
-                  int64_t tokens, int hc, int dim, float eps, float clamp,
+                  const float *q_w, const float *k_w, void *h, float *gate_out, float *stats,
+                  int64_t tokens, int hc, int dim, float eps, float clamp, int plain,
                   hipStream_t stream) {
 #define ENGRAM_GATE_CASE(N)                                                                 \
   case N:                                                                                   \
     hipLaunchKernelGGL((gate_kernel<F32, N>), dim3((unsigned)tokens), dim3(threads), 0,     \
-                       stream, ids, raw_vocab, kv, q_w, k_w, h, gate_out, hc, dim, eps,     \
-                       clamp);                                                              \
+                       stream, ids, raw_vocab, kv, q_w, k_w, h, gate_out, stats, hc, dim,   \
+                       eps, clamp, plain);                                                  \
     break;
   switch (cpt) {
     ENGRAM_GATE_CASE(1)
@@ -210,8 +206,8 @@ hipError_t launch(int cpt, int threads, const int32_t *ids, int32_t raw_vocab, c
 
 hipError_t engram_launch_gate(bool f32, const int32_t *ids, int32_t raw_vocab, const void *kv,
                               const float *q_w, const float *k_w, void *h, float *gate_out,
-                              int64_t tokens, int32_t hc, int32_t dim, float eps, float clamp,
-                              hipStream_t stream) {
+                              float *stats, int64_t tokens, int32_t hc, int32_t dim, float eps,
+                              float clamp, int plain, hipStream_t stream) {
   if (tokens <= 0) return hipSuccess;
   int dev = 0, cus = 256;
   hipError_t err = hipGetDevice(&dev);
@@ -224,8 +220,8 @@ hipError_t engram_launch_gate(bool f32, const int32_t *ids, int32_t raw_vocab, c
   const int needed = ((cps + engram::kWave - 1) / engram::kWave) * engram::kWave;
   if (threads > needed) threads = needed;
   const int cpt = (cps + threads - 1) / threads;
-  return f32 ? launch<true>(cpt, threads, ids, raw_vocab, kv, q_w, k_w, h, gate_out, tokens, hc,
-                            dim, eps, clamp, stream)
-             : launch<false>(cpt, threads, ids, raw_vocab, kv, q_w, k_w, h, gate_out, tokens, hc,
-                             dim, eps, clamp, stream);
+  return f32 ? launch<true>(cpt, threads, ids, raw_vocab, kv, q_w, k_w, h, gate_out, stats,
+                            tokens, hc, dim, eps, clamp, plain, stream)
+             : launch<false>(cpt, threads, ids, raw_vocab, kv, q_w, k_w, h, gate_out, stats,
+                             tokens, hc, dim, eps, clamp, plain, stream);
 }

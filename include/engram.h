@@ -22,6 +22,10 @@
  *      h_m <- bf16(h_m + alpha v); alpha = 0 and h untouched at DEAD positions
  *      ([P1] "门控", "sigmoid 之前多一步带符号的平方根"; [P4] "消费：学习投影 +
  *      余弦门控").
+ *   Variants the papers describe: the plain gate alpha = sigmoid(s) ([P5] §4.1;
+ *   engram_forward_desc.gate_mode) and the short convolution branch after the
+ *   gate, Y = SiLU(Conv1D(RMSNorm(alpha v))) + alpha v, h_m += Y ([P5] §4.2;
+ *   [P3] §三; engram_gate_conv, engram_forward_conv).
  *
  * Conventions for every entry point:
  *   - Pointers are device memory unless marked [host]. The caller owns every
@@ -59,6 +63,8 @@ extern "C" {
 #define ENGRAM_MAX_TOTAL_SEGMENTS 128  /* layers * S in one engram_hash_layers call */
 #define ENGRAM_ROW_BYTES 264      /* E4M3 row: 256 payload bytes + 8 scale bytes */
 #define ENGRAM_ROW_DIM_E4M3 256
+#define ENGRAM_MAX_CONV_TAPS 8    /* kernel size w of the short convolution */
+#define ENGRAM_MAX_CONV_HISTORY 64 /* (w - 1) * dilation */
 
 typedef enum engram_status {
   ENGRAM_OK = 0,
@@ -101,6 +107,13 @@ typedef struct engram_hash_params {
   int64_t offsets[ENGRAM_MAX_SEGMENTS];  /* off_j = p_0 + ... + p_{j-1}            */
 } engram_hash_params;
 
+typedef enum engram_gate_mode {
+  ENGRAM_GATE_SIGNED_SQRT = 0, /* sigmoid(sign(s) sqrt(max(|s|, clamp))): the released
+                                  code's gate ([P1] "sigmoid 之前多一步带符号的平方根") */
+  ENGRAM_GATE_PLAIN = 1        /* sigmoid(s): the papers' own formula ([P5] §4.1);
+                                  gate_clamp is ignored                             */
+} engram_gate_mode;
+
 /* Shapes and constants of one forward call. */
 typedef struct engram_forward_desc {
   int64_t batch;              /* B sequences                                       */
@@ -112,7 +125,39 @@ typedef struct engram_forward_desc {
   int32_t row_dim;            /* 256 for E4M3 rows; multiple of 4 for fp32 rows    */
   float eps;                  /* RMS epsilon (1e-6)                                */
   float gate_clamp;           /* c in sqrt(max(|s|, c)) (0)                        */
+  int32_t gate_mode;          /* engram_gate_mode (ENGRAM_GATE_SIGNED_SQRT)         */
+  int32_t reserved;           /* must be 0                                         */
 } engram_forward_desc;
+
+/*
+ * The short convolution branch after the gate ([P5] §4.2: depthwise, causal,
+ * kernel size 4 at dilation 3 = the largest n-gram order, so position t reads
+ * t, t-3, t-6, t-9; RMSNorm before and SiLU after; filters start at zero, which
+ * makes the branch's output the gated value itself; [P5] §9.5: decode and
+ * chunked prefill keep the last 9 positions). For stream m, channel c:
+ *   V~_t = alpha_{t,m} v_t,  n_t = V~_t / sqrt(mean_c(V~_t^2) + eps) * norm_weight[m][c],
+ *   u_t = sum_j weight[m][c][j] * n_{t - (w-1-j) dilation},  (n = 0 before the
+ *   sequence start when there is no history)
+ *   h_{t,m,c} <- round(h + SiLU(u_t) + V~_t),  except at DEAD positions, whose
+ *   streams stay untouched and whose V~ is 0 for the positions after them.
+ * History of a sequence, L = (w - 1) * dilation positions before the chunk, in
+ * factored form: state_v [B, L, dim] holds their value rows v (kv's dtype:
+ * bf16, or float for ENGRAM_ROW_F32) and state_s float [B, L, hc + 1] their
+ * gates alpha_0..alpha_{hc-1} and mean(v^2); a DEAD or pre-start position has
+ * alpha = 0. Zeroed buffers are the history of a sequence start.
+ */
+typedef struct engram_short_conv {
+  int32_t taps;               /* w (4); 1 <= w <= ENGRAM_MAX_CONV_TAPS             */
+  int32_t dilation;           /* (3); >= 1, (w - 1) * dilation <= ENGRAM_MAX_CONV_HISTORY */
+  float eps;                  /* RMSNorm epsilon of the branch, > 0                */
+  int32_t reserved;           /* must be 0                                         */
+  const float *weight;        /* device float [hc, dim, w]; zeros = the papers' init */
+  const float *norm_weight;   /* device float [hc, dim], or NULL for ones          */
+  const void *state_v_in;     /* device history before the chunk, or NULL for a    */
+  const float *state_s_in;    /*   sequence start (both NULL or both set)          */
+  void *state_v_out;          /* device history after the chunk, or NULL to skip   */
+  float *state_s_out;         /*   (both NULL or both set); may equal the inputs   */
+} engram_short_conv;
 
 /* Message for a status code (static storage). */
 const char *engram_status_string(int status);
@@ -125,6 +170,7 @@ const char *engram_last_hip_error(void);
 /* sizeof the two structs as this library was built, for bindings to check. */
 size_t engram_sizeof_hash_params(void);
 size_t engram_sizeof_forward_desc(void);
+size_t engram_sizeof_short_conv(void);
 
 /*
  * [host] Segment sizes and offsets: the first `count` primes >= base, in
@@ -339,6 +385,37 @@ int engram_forward_mx(const engram_hash_params *params, const engram_forward_des
                       const void *table, const void *w_codes, const void *w_scales,
                       const float *q_w, const float *k_w, void *h, float *gate_out,
                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Step 5 with the short convolution branch ([P5] §4.1-§4.2), given kv.
+ * Arguments as engram_gate, plus:
+ *   conv      [host] the branch's shape, weights and history (engram_short_conv)
+ *   workspace device, >= engram_gate_conv_workspace_size bytes, 256-byte
+ *             aligned: each token's gates and mean(v^2)
+ * The history is read for the chunk's first (w - 1) dilation positions and,
+ * when state_v_out is set, replaced by the last L positions of history + chunk.
+ * Errors: ENGRAM_EINVAL, ENGRAM_ESHAPE, ENGRAM_EWORKSPACE, ENGRAM_EHIP.
+ */
+size_t engram_gate_conv_workspace_size(const engram_forward_desc *desc);
+int engram_gate_conv(const engram_forward_desc *desc, const engram_short_conv *conv,
+                     const int32_t *ids, int32_t raw_vocab, const void *kv, const float *q_w,
+                     const float *k_w, void *h, float *gate_out, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Steps 1-5 with the short convolution branch: engram_forward with
+ * engram_gate_conv in place of engram_gate. Arguments as engram_forward, plus
+ * conv as engram_gate_conv.
+ * Errors: as engram_forward.
+ */
+size_t engram_forward_conv_workspace_size(const engram_hash_params *params,
+                                          const engram_forward_desc *desc);
+int engram_forward_conv(const engram_hash_params *params, const engram_forward_desc *desc,
+                        const engram_short_conv *conv, const int32_t *ids,
+                        const int32_t *hist_in, int32_t *hist_out, const void *table,
+                        const void *wkv, const float *q_w, const float *k_w, void *h,
+                        float *gate_out, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream);
 
 #ifdef __cplusplus
 }

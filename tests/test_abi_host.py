@@ -212,3 +212,58 @@ def test_one_hip_runtime_whatever_the_import_order():
                          timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip().splitlines()[-1] == "1"
+
+
+def test_gate_mode_and_short_conv_validation():
+    """Bad gate modes and convolution descriptors fail before any launch."""
+    L = E.LIB
+    d = E.forward_desc(2, 16, 4, 64, 1 << 20, 0, 256)
+    ptrs = [0x1000, 8, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000]     # ids, V, kv, qw, kw, h, gate
+    ws = E.engram_gate_conv_workspace_size(d)
+    assert ws == 2 * 16 * 5 * 4 + (-(2 * 16 * 5 * 4) % 256)
+
+    def gc(desc, conv, wsp=0x10000, wsb=ws):
+        return L.engram_gate_conv(ctypes.byref(desc), ctypes.byref(conv), *ptrs, wsp, wsb, None)
+
+    ok = E.short_conv(0x7000)
+    bad_mode = E.forward_desc(2, 16, 4, 64, 1 << 20, 0, 256, gate_mode=2)
+    assert gc(bad_mode, ok) == E.EINVAL
+    assert L.engram_gate(ctypes.byref(bad_mode), *ptrs, None) == E.EINVAL
+    d_res = E.forward_desc(2, 16, 4, 64, 1 << 20, 0, 256)
+    d_res.reserved = 1
+    assert gc(d_res, ok) == E.EINVAL
+    assert gc(d, E.short_conv(0x7000, taps=0)) == E.ESHAPE
+    assert gc(d, E.short_conv(0x7000, taps=9)) == E.ESHAPE
+    assert gc(d, E.short_conv(0x7000, dilation=0)) == E.ESHAPE
+    assert gc(d, E.short_conv(0x7000, taps=8, dilation=10)) == E.ESHAPE    # history 70 > 64
+    assert gc(d, E.short_conv(0x7000, eps=0.0)) == E.EINVAL
+    assert gc(d, E.short_conv(None)) == E.EINVAL
+    assert gc(d, E.short_conv(0x7004)) == E.EINVAL                         # weight misaligned
+    assert gc(d, E.short_conv(0x7000, state_v_in=0x8000)) == E.EINVAL     # half a history
+    assert gc(d, E.short_conv(0x7000, state_v_out=0x8000)) == E.EINVAL
+    assert gc(d, E.short_conv(0x7000, state_v_in=0x8008, state_s_in=0x9000)) == E.EINVAL
+    res = E.short_conv(0x7000)
+    res.reserved = 3
+    assert gc(d, res) == E.EINVAL
+    assert gc(d, ok, wsb=ws - 1) == E.EWORKSPACE
+    assert gc(d, ok, wsp=0x10040) == E.EWORKSPACE
+    assert gc(d, ok, wsp=None) == E.EWORKSPACE
+    assert L.engram_gate_conv(ctypes.byref(d), None, *ptrs, 0x10000, ws, None) == E.EINVAL
+
+
+def test_forward_conv_workspace_and_validation():
+    p = _params(C1)
+    d = E.forward_desc(4, 8192, 4, 5120, 384_006_168, 0, 256)
+    T = 4 * 8192
+    n = E.engram_forward_conv_workspace_size(p, d)
+    assert n == E.engram_forward_workspace_size(p, d) + T * 5 * 4
+    L = E.LIB
+    args = [0x1000, None, None, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None]
+    conv = E.short_conv(0x7000)
+    assert L.engram_forward_conv(ctypes.byref(p), ctypes.byref(d), ctypes.byref(conv), *args,
+                                 0x10000, n - 1, None) == E.EWORKSPACE
+    assert L.engram_forward_conv(ctypes.byref(p), ctypes.byref(d), None, *args, 0x10000, n,
+                                 None) == E.EINVAL
+    bad = E.short_conv(0x7000, taps=0)
+    assert L.engram_forward_conv(ctypes.byref(p), ctypes.byref(d), ctypes.byref(bad), *args,
+                                 0x10000, n, None) == E.ESHAPE
