@@ -34,17 +34,28 @@ FP8_PEAK_TFLOPS = 5000.0          # MI355X dense fp8 MFMA
 GATHER_BYTES_PER_TOKEN = 24 * 8 + 24 * 264 + 6144 * 2
 
 
+# The sources the bf16 projection kernel is built from; its committed traffic
+# figures hold while these hash to the recorded value.
+GEMM_BF16_SOURCES = ("hashed_gram_conditional_amd/csrc/gemm.hip",
+                     "hashed_gram_conditional_amd/csrc/gemm_tiles.h",
+                     "hashed_gram_conditional_amd/csrc/common.h")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def measured_traffic(kernel: str, source: str):
+def measured_traffic(kernel: str, sources):
     """HBM bytes per launch of ``kernel`` from the committed rocprofv3 PMC summary
     (FETCH_SIZE and WRITE_SIZE, each scaled by the counter's reading for a copy of
-    known size), or None when no summary matches the current kernel source."""
+    known size), or None when no summary matches the current kernel sources (the
+    sha256 of their concatenated bytes, in the order given)."""
     import glob
     import hashlib
-    sha = hashlib.sha256(open(os.path.join(ROOT, source), "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for src in sources:
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    sha = h.hexdigest()
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         for line in open(path):
             f = line.split()
@@ -229,8 +240,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "gemm_bf16_kernel (engram_project)",
                      "achieved": round(gemm_tflops, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic("gemm_bf16_kernel",
-                                                 "hashed_gram_conditional_amd/csrc/gemm.hip"),
+                     "traffic": measured_traffic("gemm_bf16_kernel", GEMM_BF16_SOURCES),
                      "algorithmic_flop": flops},
         "gather": {"kernel": "gather_e4m3_kernel (engram_gather)",
                    "achieved": round(gather_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -240,6 +250,7 @@ def main():
                       "project": round(stage_ms[2], 4), "gate": round(stage_ms[3], 4)},
         "engram_forward_ms": round(forward_ms, 4),
     }
+    out["short_conv"] = conv_prefill_bench(gw, rows, e, kv, gates, args.steps, args.warmup)
     out["hash_layers"] = hash_layers_bench(max(args.steps, 20))
     out["fp8_wkv"] = fp8_prefill_bench(gw, args.steps, args.warmup)
     if not args.no_cpu_baseline:
@@ -252,6 +263,75 @@ def main():
         torch.cuda.empty_cache()
         out["decode"] = decode_bench(args.steps, args.warmup)
     print(json.dumps(out), flush=True)
+
+
+def conv_prefill_bench(gw, rows, e, kv, gates, steps: int, warmup: int):
+    """The prefill layer with the papers' short convolution branch after the gate
+    (4 taps at dilation 3, RMSNorm, SiLU; random filters and norm weights):
+    engram_hash -> engram_gather -> engram_project -> engram_gate_conv, the last
+    also writing the 9-position history of every sequence. The gate-and-branch
+    stage runs two kernels over the token stream; its algorithmic bytes per
+    token are those of both: h, k and v read and the gates and mean square
+    written by the first, then h read and written and v read by the second."""
+    import torch
+    import hashed_gram_conditional_amd as E
+
+    w = gw.w
+    T, S = w.tokens, w.segments
+    K_in, N_out = S * w.row_dim, (w.hc + 1) * w.dim
+    g = torch.Generator(device="cuda").manual_seed(77)
+    cw = 0.3 * torch.randn((w.hc, w.dim, 4), generator=g, device="cuda")
+    nw = 1 + 0.1 * torch.randn((w.hc, w.dim), generator=g, device="cuda")
+    sv = torch.zeros((w.batch, 9, w.dim), dtype=torch.bfloat16, device="cuda")
+    ss = torch.zeros((w.batch, 9, w.hc + 1), dtype=torch.float32, device="cuda")
+    conv = E.short_conv(cw, 4, 3, 1e-6, nw, None, None, sv, ss)
+    n_ws = E.engram_gate_conv_workspace_size(gw.desc)
+    cws = torch.empty(n_ws, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+
+    def step(evs):
+        if evs:
+            evs[0].record(stream)
+        E.engram_hash(gw.params, gw.ids, w.batch, w.seq, None, None, rows)
+        if evs:
+            evs[1].record(stream)
+        E.engram_gather(gw.table, gw.rows, gw.row_format, w.row_dim, rows, T * S, e)
+        if evs:
+            evs[2].record(stream)
+        E.engram_project(e, gw.wkv, kv, T, K_in, N_out, 0)
+        if evs:
+            evs[3].record(stream)
+        E.engram_gate_conv(gw.desc, conv, gw.ids, w.raw_vocab, kv, gw.q_w, gw.k_w, gw.h, gates,
+                           cws, n_ws)
+        if evs:
+            evs[4].record(stream)
+
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = np.mean([[s_[j].elapsed_time(s_[j + 1]) for j in range(4)] for s_ in ev], axis=0)
+    ms = 1e3 * wall / steps
+    d = w.dim
+    bytes_per_token = (2 * w.hc * d * 2 + d * 2 + (w.hc + 1) * 4) + \
+                      (w.hc * d * 2 + (w.hc + 1) * d * 2 + (w.hc + 1) * 4)
+    gbps = bytes_per_token * T / (st[3] * 1e-3) / 1e9
+    del cws, sv, ss, cw, nw
+    return {"workload": "prefill layer forward as above with the short convolution branch "
+                        "(4 taps, dilation 3) and its history written",
+            "tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+            "stages_ms": {"hash": round(st[0], 4), "gather": round(st[1], 4),
+                          "project": round(st[2], 4), "gate_conv": round(st[3], 4)},
+            "gate_conv": {"kernels": "gate_kernel (gates, mean(v^2)) + short_conv_kernel + "
+                                     "conv_state_kernel",
+                          "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                          "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                          "bytes_per_token": bytes_per_token}}
 
 
 def fp8_prefill_bench(gw, steps: int, warmup: int):
@@ -413,13 +493,39 @@ def decode_bench(steps: int, warmup: int):
     torch.cuda.synchronize()
     st = np.mean([[x[j].elapsed_time(x[j + 1]) for j in range(4)] for x in se], axis=0)
     wkv_bytes = N_out * K_in * 2
+    # the same decode step with the short convolution branch: each sequence's
+    # 9-position history is read and shifted in place every step
+    g = torch.Generator(device="cuda").manual_seed(78)
+    cw = 0.3 * torch.randn((w.hc, w.dim, 4), generator=g, device="cuda")
+    sv = torch.zeros((w.batch, 9, w.dim), dtype=torch.bfloat16, device="cuda")
+    ss = torch.zeros((w.batch, 9, w.hc + 1), dtype=torch.float32, device="cuda")
+    conv = E.short_conv(cw, 4, 3, 1e-6, None, sv, ss, sv, ss)
+    ncw = E.engram_forward_conv_workspace_size(gw.params, gw.desc)
+    cws = torch.empty(ncw, dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        E.engram_forward_conv(gw.params, gw.desc, conv, gw.ids, hist, hist, gw.table, gw.wkv,
+                              gw.q_w, gw.k_w, gw.h, gates, cws, ncw)
+    torch.cuda.synchronize()
+    ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ce[0].record(stream)
+    for i in range(steps):
+        E.engram_forward_conv(gw.params, gw.desc, conv, gw.ids, hist, hist, gw.table, gw.wkv,
+                              gw.q_w, gw.k_w, gw.h, gates, cws, ncw)
+    ce[1].record(stream)
+    torch.cuda.synchronize()
+    conv_ms = ce[0].elapsed_time(ce[1]) / steps
+    del cws, sv, ss, cw
     res = {"workload": "decode: 256 sequences x 1 token with a 3-token history, 24 segments of "
                        "primes from 16,000,000 (384,006,168 x 264 B = 101.4 GB table), hc 4 x 5120",
            "tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
            "stages_ms": {"hash": round(st[0], 4), "gather": round(st[1], 4),
                          "project": round(st[2], 4), "gate": round(st[3], 4)},
            "project_weight_stream": {"achieved": round(wkv_bytes / (st[2] * 1e-3) / 1e9, 1),
-                                     "peak": HBM_PEAK_GBPS, "unit": "GB/s"}}
+                                     "peak": HBM_PEAK_GBPS, "unit": "GB/s"},
+           "short_conv": {"workload": "the same step through engram_forward_conv (4 taps, "
+                                      "dilation 3, 9-position history in place)",
+                          "tokens_per_s": round(T / (conv_ms * 1e-3), 1),
+                          "ms_per_step": round(conv_ms, 4)}}
     gw.free()
     return res
 

@@ -22,9 +22,15 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t b16) {
   return __uint_as_float(b16 << 16);
 }
 
-// Two bf16 (low half = first element) from two floats, nearest-even.
+// Two bf16 (low half = first element) from two floats, nearest-even: one
+// v_cvt_pk_bf16_f32. On gfx950 it gives the bits of f32_to_bf16_rne for every
+// finite and infinite input (checked on 3.4e7 random and tie patterns); a NaN
+// comes out as a quiet NaN.
+typedef __bf16 engram_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float engram_f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+  const engram_f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, engram_bf16x2));
 }
 
 __device__ __forceinline__ float warp_sum(float v) {

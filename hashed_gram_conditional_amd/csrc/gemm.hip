@@ -40,46 +40,13 @@
 // hardware places on one XCD (it deals block ids round-robin over 8 XCDs) form
 // one contiguous range, and tiles are walked in groups of 8 token-tiles
 // sharing weight tiles, for L2 reuse.
-#include "common.h"
+#include "gemm_tiles.h"
+
+using namespace engram_gemm;
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-#define ENGRAM_LDS(p) ((__attribute__((address_space(3))) void *)(p))
-
-constexpr int BM = 256;       // tokens per tile
 constexpr int BK = 64;        // K per stage
-constexpr int kWideThreads = 256;
-constexpr int kNarrowThreads = 512;
-constexpr int kGroupM = 8;
-constexpr int kXcds = 8;
-// Buffer resource word 3 for gfx9-family raw buffers (no format, no swizzle).
-constexpr int kBufferFlags = 0x00020000;
-
-// Tile origin of this block: block ids are renumbered so that each XCD's
-// blocks are contiguous, then walked in groups of kGroupM token-tiles.
-__device__ __forceinline__ void tile_origin(int tiles_m, int tiles_n, int bn, int &m0, int &n0) {
-  const int nblocks = tiles_m * tiles_n;
-  int bid = blockIdx.x;
-  const int full = (nblocks / kXcds) * kXcds;
-  if (bid < full) bid = (bid % kXcds) * (full / kXcds) + bid / kXcds;
-  const int in_group = kGroupM * tiles_n;
-  const int group = bid / in_group;
-  const int first_m = group * kGroupM;
-  const int gsize = min(tiles_m - first_m, kGroupM);
-  const int local = bid - group * in_group;
-  m0 = (first_m + local % gsize) * BM;
-  n0 = (local / gsize) * bn;
-}
-
-__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
-  return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
-}
-
-constexpr int BN = 256;          // wide tile width
-constexpr int kWideOutputs = 256; // accumulators per thread of a wide tile
 
 struct WideLds {
   uint16_t w[2][BN * BK];
@@ -234,46 +201,6 @@ __device__ __forceinline__ void wide_tile(const uint16_t *__restrict__ E,
 
 }
 
-// bf16 store of a finished wide tile. Accumulator r of tile (i, j) is output
-// column n0 + wn*128 + i*32 + (r/4)*8 + (lane/32)*4 + r%4 of token
-// m0 + wm*128 + j*32 + lane%32.
-__device__ __forceinline__ void wide_store_bf16(const f32x16 (&acc)[4][4],
-                                                uint16_t *__restrict__ C, int M, int N, int m0,
-                                                int n0) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wn = wave >> 1, wm = wave & 1;
-  const int frow = lane & 31, fk = lane >> 5;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int m = m0 + wm * 128 + j * 32 + frow;
-    if (m >= M) continue;
-    uint16_t *crow = C + (int64_t)m * N;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * 128 + i * 32 + g * 8 + fk * 4;
-        if (n < N) {
-          uint2 v;
-          v.x = engram::pack_bf16x2(acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1]);
-          v.y = engram::pack_bf16x2(acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]);
-          *reinterpret_cast<uint2 *>(crow + n) = v;
-        }
-      }
-    }
-  }
-}
-
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-}
-
 __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_kernel(const uint16_t *__restrict__ E, const uint16_t *__restrict__ W,
                       uint16_t *__restrict__ C, int M, int N, int K, int tiles_m, int tiles_n) {
@@ -284,34 +211,6 @@ void gemm_bf16_kernel(const uint16_t *__restrict__ E, const uint16_t *__restrict
   zero_acc(acc);
   wide_tile(E, W, M, N, K, m0, n0, 0, K / BK, acc, lds);
   wide_store_bf16(acc, C, M, N, m0, n0);
-}
-
-// ---- stream-K schedule for calls with fewer wide tiles than CUs ----------------
-// The (tile, K-step) units, tile-major, are dealt to G persistent blocks in
-// equal contiguous ranges: block b owns units [floor(b U / G), floor((b+1) U / G)).
-// A tile a block covers whole is stored as bf16 at once. A tile split between
-// blocks leaves one fp32 piece per block: a block's first piece goes to its
-// slot 0 and its last to slot 1 (the pieces between are whole tiles). The
-// fixup kernel then sums a tile's pieces in block order, so every result is
-// reproducible for a given shape and CU count.
-struct StreamK {
-  int64_t units;      // tiles * KT
-  int blocks;         // G
-  int kt;             // K-steps per tile
-  int tiles_m;
-  __device__ __forceinline__ int64_t start(int b) const { return (int64_t)b * units / blocks; }
-  // the block owning unit x: the largest b with start(b) <= x
-  __device__ __forceinline__ int owner(int64_t x) const {
-    const int64_t b = ((x + 1) * blocks + units - 1) / units - 1;
-    return (int)(b < blocks - 1 ? b : blocks - 1);
-  }
-};
-
-// Partial accumulators, thread-major per register so that one store
-// instruction of a wave covers 256 contiguous bytes: value r of thread t of
-// slot s of block b sits at ws[((b * 2 + s) * kWideOutputs + r) * kWideThreads + t].
-__device__ __forceinline__ float *piece_slot(float *ws, int b, int s) {
-  return ws + ((int64_t)(b * 2 + s) * kWideOutputs) * kWideThreads;
 }
 
 __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -351,8 +250,6 @@ void gemm_bf16_streamk_kernel(const uint16_t *__restrict__ E, const uint16_t *__
 // all 256 threads of the tile: four quads of consecutive output columns per
 // thread, loads coalesced across threads. Tiles one block finished whole exit
 // at once.
-constexpr int kFixupRegs = 16;
-constexpr int kFixupParts = kWideOutputs / kFixupRegs;
 
 __global__ __launch_bounds__(kWideThreads) void gemm_streamk_fixup_kernel(
     const float *__restrict__ ws, uint16_t *__restrict__ C, int M, int N, StreamK sk) {
@@ -389,318 +286,6 @@ __global__ __launch_bounds__(kWideThreads) void gemm_streamk_fixup_kernel(
       o.y = engram::pack_bf16x2(v[g * 4 + 2], v[g * 4 + 3]);
       *reinterpret_cast<uint2 *>(crow + n) = o;
     }
-  }
-}
-
-// ---- block-scaled FP8 (MX) projection --------------------------------------------
-// kv = e W with both operands in the table's block encoding: E4M3 values with one
-// E8M0 scale per 32 inputs. W is codes [N, K] plus scales [N, K/32]; e is the
-// looked-up rows themselves, [tokens, S, 264] (256 codes then 8 scales per
-// segment), so no dequantisation happens at all: v_mfma_scale_f32_32x32x64_f8f6f4
-// multiplies E4M3 pairs exactly, applies both 2^(scale - 127) factors per 32-input
-// block and accumulates in fp32.
-//
-// Lane layout of that MFMA (measured on gfx950 with single-instruction probes):
-// lane l of half h = l / 32 holds row l % 32; its bytes 0-15 are inputs
-// [16h, 16h + 16) of the 64 and bytes 16-31 inputs [32 + 16h, 32 + 16h + 16);
-// the scale of row r for inputs [0, 32) comes from lane r's scale operand and
-// for [32, 64) from lane r + 32's. The output layout is that of the bf16 MFMA,
-// so the epilogues are shared.
-//
-// Tiles and schedule follow gemm_bf16_kernel: 256 x 256 outputs, 4 waves of
-// 128 x 128, a K-step of 128 inputs (128 bytes per row, the same LDS rows and
-// swizzle as the bf16 kernel), two 64-input MFMA sub-steps per K-step. Each
-// thread stages one step of loads in registers: it stores quarter q of step k+1
-// to LDS before reloading that quarter with step k+2, so every load has a step to
-// arrive. Scales travel as one dword (4 blocks) per row per step.
-
-struct MxOperands {
-  const uint8_t *w_codes;    // [N, K]
-  const uint8_t *w_scales;   // [N, K / 32]
-  const uint8_t *e_rows;     // [M, S, 264]
-  int segments;              // S; K = 256 S
-};
-
-constexpr int kMxBk = 128;            // inputs per K-step
-constexpr int kRowBytes = 264;
-
-struct MxLds {
-  uint8_t w[2][BN * kMxBk];
-  uint8_t e[2][BM * kMxBk];
-  uint32_t ws[2][BN];
-  uint32_t es[2][BM];
-};
-
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ i32x8 join16(uint4 lo, uint4 hi) {
-  i32x8 v;
-  v[0] = (int)lo.x; v[1] = (int)lo.y; v[2] = (int)lo.z; v[3] = (int)lo.w;
-  v[4] = (int)hi.x; v[5] = (int)hi.y; v[6] = (int)hi.z; v[7] = (int)hi.w;
-  return v;
-}
-
-__device__ __forceinline__ uint32_t load4(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0);
-}
-
-// K-steps [ks, ke) of the MX tile at (m0, n0) into acc (zeroed by the caller).
-// Registers: the B fragments of a 64-input chunk are double-buffered, the A
-// fragments stream one tile ahead (both A fragments the MFMAs after the barrier
-// need are read before it, as other waves then start refilling the stage).
-__device__ __forceinline__ void wide_tile_mx(
-    const MxOperands &op, int M, int N, int m0, int n0, int ks, int ke, f32x16 (&acc)[4][4],
-    uint8_t *__restrict__ w0, uint8_t *__restrict__ w1, uint8_t *__restrict__ e0,
-    uint8_t *__restrict__ e1, uint32_t *__restrict__ ws0, uint32_t *__restrict__ ws1,
-    uint32_t *__restrict__ es0, uint32_t *__restrict__ es1) {
-  const int K = op.segments * 256;
-  const int KB = K / 32;                       // scale bytes per W row
-  const int RS = op.segments * kRowBytes;      // bytes per e row
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave >> 1, wm = wave & 1;
-  const int rows_w = min(BN, N - n0), rows_e = min(BM, M - m0);
-  const __amdgpu_buffer_rsrc_t rsW = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t *>(op.w_codes + (int64_t)n0 * K), 0, rows_w * K, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t rsWs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t *>(op.w_scales + (int64_t)n0 * KB), 0, rows_w * KB, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t rsE = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t *>(op.e_rows + (int64_t)m0 * RS), 0, rows_e * RS, kBufferFlags);
-  // code chunk i of this thread: row (i % 8) * 32 + t / 8, 16-byte column t % 8
-  const int g_row = tid >> 3, g_chunk = tid & 7;
-  const int ge_voff = g_row * RS + g_chunk * 16;
-  const int s_off = g_row * kMxBk + ((g_chunk ^ (g_row & 7) ^ ((g_row >> 3) & 1)) << 4);
-  const int frow = lane & 31, h = lane >> 5;
-  const int fsw = (frow & 7) ^ ((frow >> 3) & 1);
-  const int a_base = (wn * 128 + frow) * kMxBk;
-  const int b_base = (wm * 128 + frow) * kMxBk;
-  const int a_srow = wn * 128 + frow, b_srow = wm * 128 + frow;
-  // fragment chunk offsets within a row for 64-input chunk c: 4c + h and 4c + 2 + h
-  const int f0lo = ((0 + h) ^ fsw) << 4, f0hi = ((2 + h) ^ fsw) << 4;
-  const int f1lo = ((4 + h) ^ fsw) << 4, f1hi = ((6 + h) ^ fsw) << 4;
-
-  // W codes and scales go global -> LDS by direct loads: instruction i of wave w
-  // fills rows (8 w + i) * 8 + p / 8 (lane p), slot p % 8, so lane p fetches
-  // logical chunk (p % 8) ^ (row & 7) ^ ((row >> 3) & 1) = (p % 8) ^ (p / 8) ^ (i & 1).
-  const int dl_row = (wave * 8) * 8 + (lane >> 3);
-  const int dl_c0 = (lane & 7) ^ (lane >> 3);
-  const int dl_v0 = dl_row * K + dl_c0 * 16;
-  const int dl_v1 = dl_row * K + (dl_c0 ^ 1) * 16;
-  uint4 g[8];
-  uint32_t ges = 0;
-// Stage buffers are distinct restrict pointers, so the compiler can tell the
-// direct loads into one stage from reads of the other and waits for nothing.
-#define MX_W(st) ((st) ? w1 : w0)
-#define MX_E(st) ((st) ? e1 : e0)
-#define MX_WS(st) ((st) ? ws1 : ws0)
-#define MX_ES(st) ((st) ? es1 : es0)
-#define MX_WOFF(kt_) ((kt_) * kMxBk)
-#define MX_EOFF(kt_) (((kt_) >> 1) * kRowBytes + ((kt_) & 1) * kMxBk)
-#define MX_ESOFF(kt_) (((kt_) >> 1) * kRowBytes + 256 + ((kt_) & 1) * 4)
-// Half q of a step: q = 0 the W codes and scales, q = 1 the e codes and scales.
-// Direct loads of W: code chunk i (i < 8) or the scales (i = 8) of step kt_ into stage st.
-#define MX_DMAW1(kt_, st, i)                                                                  \
-  if ((i) < 8)                                                                              \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(                                               \
-        rsW, (__attribute__((address_space(3))) void *)&MX_W(st)[(wave * 8 + (i)) * 1024],  \
-        16, ((i) & 1) ? dl_v1 : dl_v0, (i) * 8 * K + MX_WOFF(kt_), 0, 0);                   \
-  else                                                                                      \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(                                               \
-        rsWs, (__attribute__((address_space(3))) void *)&MX_WS(st)[wave * 64], 4, tid * KB, \
-        (kt_) * 4, 0, 0);
-// e chunk i (i < 8) or the scales (i = 8): store the staged step into stage st,
-// then reload the register with step kt_.
-#define MX_EPAIR(st, i, kt_)                                                                  \
-  if ((i) < 8) {                                                                            \
-    *reinterpret_cast<uint4 *>(&MX_E(st)[s_off + (i) * 32 * kMxBk]) = g[i];                 \
-    g[i] = load16(rsE, ge_voff, (i) * 32 * RS + MX_EOFF(kt_));                              \
-  } else {                                                                                  \
-    MX_ES(st)[tid] = ges;                                                                   \
-    ges = load4(rsE, tid * RS, MX_ESOFF(kt_));                                              \
-  }
-// W copies of a step are issued right after the previous barrier; the 9 e
-// reloads that follow them may stay in flight across the next barrier.
-#define MX_BARRIER() asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory")
-#define MX_FRAG(buf, base, c, t)                                                              \
-  join16(*reinterpret_cast<const uint4 *>(&(buf)[(base) + (t) * 32 * kMxBk + ((c) ? f1lo : f0lo)]), \
-         *reinterpret_cast<const uint4 *>(&(buf)[(base) + (t) * 32 * kMxBk + ((c) ? f1hi : f0hi)]))
-#define MX_FRAGA(st, c, t) MX_FRAG(MX_W(st), a_base, c, t)
-#define MX_FRAGSB(st, c, dst)                                                                 \
-  _Pragma("unroll") for (int j = 0; j < 4; ++j) dst[j] = MX_FRAG(MX_E(st), b_base, c, j);
-#define MX_SCALES(st, sA, sB)                                                                 \
-  _Pragma("unroll") for (int i = 0; i < 4; ++i) sA[i] = MX_WS(st)[a_srow + i * 32];         \
-  _Pragma("unroll") for (int j = 0; j < 4; ++j) sB[j] = MX_ES(st)[b_srow + j * 32];
-// scale byte of 32-input block 2c + h of the step
-#define MX_SB(word, c) ((int)(((word) >> (8 * (2 * (c) + h))) & 0xFFu))
-#define MX_TILE(i, afrag, bfr, sbv, sa_in)                                                    \
-  {                                                                                         \
-    const int sa_ = (sa_in);                                                                \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                           \
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(afrag, bfr[j], acc[i][j], 0, \
-                                                                  0, 0, sa_, 0, sbv[j]);    \
-  }
-#define MX_FENCE() __builtin_amdgcn_sched_barrier(0)
-#define MX_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
-
-  i32x8 bC[4], bN[4], aC, aN;
-  uint32_t aS[4], bS[4];
-  int sbv[4], sa2, sa3;
-  // Prologue: W of steps ks and ks+1 by direct loads, e of step ks into stage 0,
-  // e of step ks+1 staged in registers.
-  __syncthreads();
-  _Pragma("unroll") for (int i = 0; i < 9; ++i) { MX_DMAW1(ks, 0, i) }
-  _Pragma("unroll") for (int i = 0; i < 8; ++i)
-    g[i] = load16(rsE, ge_voff, i * 32 * RS + MX_EOFF(ks));
-  ges = load4(rsE, tid * RS, MX_ESOFF(ks));
-  _Pragma("unroll") for (int i = 0; i < 9; ++i) { MX_EPAIR(0, i, ks + 1) }
-  _Pragma("unroll") for (int i = 0; i < 9; ++i) { MX_DMAW1(ks + 1, 1, i) }
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  MX_FRAGSB(0, 0, bC)
-  aC = MX_FRAGA(0, 0, 0);
-  MX_SCALES(0, aS, bS)
-
-// Step kt reads stage P. Before its barrier it stores the staged e of step
-// kt+1 into stage Q and restages e of step kt+2 (9 pairs over the first five
-// tiles); after the barrier stage P is free and takes W of step kt+2.
-#define MX_STEP(P, Q)                                                                         \
-  {                                                                                         \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) sbv[j] = MX_SB(bS[j], 0);                 \
-    MX_FRAGSB(P, 1, bN)                                                                     \
-    MX_EPAIR(Q, 0, kt + 2) MX_EPAIR(Q, 1, kt + 2)                                           \
-    aN = MX_FRAGA(P, 0, 1);                                                                 \
-    MX_TILE(0, aC, bC, sbv, MX_SB(aS[0], 0))                                                \
-    for (int s_ = 0; s_ < 2; ++s_) {                                                        \
-      MX_GROUP(0x100, 4); MX_GROUP(0x008, 1); MX_GROUP(0x200, 1); MX_GROUP(0x020, 1);       \
-      MX_GROUP(0x008, 1);                                                                   \
-    }                                                                                       \
-    MX_FENCE();                                                                             \
-    MX_EPAIR(Q, 2, kt + 2) MX_EPAIR(Q, 3, kt + 2)                                           \
-    aC = MX_FRAGA(P, 0, 2);                                                                 \
-    MX_TILE(1, aN, bC, sbv, MX_SB(aS[1], 0))                                                \
-    for (int s_ = 0; s_ < 2; ++s_) {                                                        \
-      MX_GROUP(0x100, 1); MX_GROUP(0x008, 1); MX_GROUP(0x200, 1); MX_GROUP(0x020, 1);       \
-      MX_GROUP(0x008, 1);                                                                   \
-    }                                                                                       \
-    MX_FENCE();                                                                             \
-    MX_EPAIR(Q, 4, kt + 2) MX_EPAIR(Q, 5, kt + 2)                                           \
-    aN = MX_FRAGA(P, 0, 3);                                                                 \
-    MX_TILE(2, aC, bC, sbv, MX_SB(aS[2], 0))                                                \
-    for (int s_ = 0; s_ < 2; ++s_) {                                                        \
-      MX_GROUP(0x100, 1); MX_GROUP(0x008, 1); MX_GROUP(0x200, 1); MX_GROUP(0x020, 1);       \
-      MX_GROUP(0x008, 1);                                                                   \
-    }                                                                                       \
-    MX_FENCE();                                                                             \
-    MX_EPAIR(Q, 6, kt + 2) MX_EPAIR(Q, 7, kt + 2)                                           \
-    aC = MX_FRAGA(P, 1, 0);                                                                 \
-    MX_TILE(3, aN, bC, sbv, MX_SB(aS[3], 0))                                                \
-    for (int s_ = 0; s_ < 2; ++s_) {                                                        \
-      MX_GROUP(0x100, 1); MX_GROUP(0x008, 1); MX_GROUP(0x200, 1); MX_GROUP(0x020, 1);       \
-      MX_GROUP(0x008, 1);                                                                   \
-    }                                                                                       \
-    MX_FENCE();                                                                             \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) sbv[j] = MX_SB(bS[j], 1);                 \
-    MX_EPAIR(Q, 8, kt + 2)                                                                  \
-    aN = MX_FRAGA(P, 1, 1);                                                                 \
-    MX_TILE(0, aC, bN, sbv, MX_SB(aS[0], 1))                                                \
-    MX_FENCE();                                                                             \
-    MX_TILE(1, aN, bN, sbv, MX_SB(aS[1], 1))                                                \
-    aC = MX_FRAGA(P, 1, 2);                                                                 \
-    aN = MX_FRAGA(P, 1, 3);                                                                 \
-    sa2 = MX_SB(aS[2], 1);                                                                  \
-    sa3 = MX_SB(aS[3], 1);                                                                  \
-    for (int s_ = 0; s_ < 2; ++s_) { MX_GROUP(0x008, 1); MX_GROUP(0x100, 1); MX_GROUP(0x008, 1); } \
-    MX_FENCE();                                                                             \
-    MX_BARRIER();                                                                           \
-    MX_FENCE();                                                                             \
-    /* stage Q (step kt+1): its fragments and scales; stage P takes W of step kt+2 */       \
-    MX_FRAGSB(Q, 0, bC)                                                                     \
-    MX_SCALES(Q, aS, bS)                                                                    \
-    MX_DMAW1(kt + 2, P, 0) MX_DMAW1(kt + 2, P, 1) MX_DMAW1(kt + 2, P, 2)                    \
-    MX_DMAW1(kt + 2, P, 3) MX_DMAW1(kt + 2, P, 4)                                           \
-    MX_TILE(2, aC, bN, sbv, sa2)                                                            \
-    for (int s_ = 0; s_ < 4; ++s_) { MX_GROUP(0x100, 3); MX_GROUP(0x008, 1); MX_GROUP(0x020, 1); } \
-    MX_FENCE();                                                                             \
-    MX_DMAW1(kt + 2, P, 5) MX_DMAW1(kt + 2, P, 6) MX_DMAW1(kt + 2, P, 7)                    \
-    MX_DMAW1(kt + 2, P, 8)                                                                  \
-    MX_TILE(3, aN, bN, sbv, sa3)                                                            \
-    aC = MX_FRAGA(Q, 0, 0);                                                                 \
-    for (int s_ = 0; s_ < 4; ++s_) { MX_GROUP(0x100, 1); MX_GROUP(0x008, 1); MX_GROUP(0x020, 1); } \
-    MX_FENCE();                                                                             \
-  }
-  int kt = ks;
-  for (; kt + 1 < ke; kt += 2) {
-    MX_STEP(0, 1)
-    ++kt;
-    MX_STEP(1, 0)
-    --kt;
-  }
-  if (kt < ke) MX_STEP(0, 1)
-  // Direct loads issued for steps past ke must land before the stages are reused.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#undef MX_STEP
-#undef MX_GROUP
-#undef MX_FENCE
-#undef MX_TILE
-#undef MX_SB
-#undef MX_SCALES
-#undef MX_FRAGSB
-#undef MX_FRAGA
-#undef MX_FRAG
-#undef MX_BARRIER
-#undef MX_EPAIR
-#undef MX_DMAW1
-#undef MX_ESOFF
-#undef MX_EOFF
-#undef MX_WOFF
-#undef MX_W
-#undef MX_E
-#undef MX_WS
-#undef MX_ES
-}
-
-__global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_mx_kernel(MxOperands op, uint16_t *__restrict__ C, int M, int N, int tiles_m,
-                    int tiles_n) {
-  __shared__ __align__(1024) MxLds lds;
-  int m0, n0;
-  tile_origin(tiles_m, tiles_n, BN, m0, n0);
-  f32x16 acc[4][4];
-  zero_acc(acc);
-  wide_tile_mx(op, M, N, m0, n0, 0, op.segments * 256 / kMxBk, acc, lds.w[0], lds.w[1],
-               lds.e[0], lds.e[1], lds.ws[0], lds.ws[1], lds.es[0], lds.es[1]);
-  wide_store_bf16(acc, C, M, N, m0, n0);
-}
-
-__global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_mx_streamk_kernel(MxOperands op, uint16_t *__restrict__ C, float *__restrict__ ws,
-                            int M, int N, StreamK sk) {
-  __shared__ __align__(1024) MxLds lds;
-  const int b = blockIdx.x;
-  const int64_t u0 = sk.start(b), u1 = sk.start(b + 1);
-  const int tid = threadIdx.x;
-  f32x16 acc[4][4];
-  for (int64_t u = u0; u < u1;) {
-    const int64_t tile = u / sk.kt;
-    const int ks = (int)(u - tile * sk.kt);
-    const int ke = (int)min((int64_t)sk.kt, (int64_t)ks + (u1 - u));
-    const int m0 = (int)(tile % sk.tiles_m) * BM;
-    const int n0 = (int)(tile / sk.tiles_m) * BN;
-    zero_acc(acc);
-    wide_tile_mx(op, M, N, m0, n0, ks, ke, acc, lds.w[0], lds.w[1], lds.e[0], lds.e[1],
-                 lds.ws[0], lds.ws[1], lds.es[0], lds.es[1]);
-    if (ks == 0 && ke == sk.kt) {
-      wide_store_bf16(acc, C, M, N, m0, n0);
-    } else {
-      float *dst = piece_slot(ws, b, u == u0 ? 0 : 1) + tid;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) dst[((i * 4 + j) * 16 + r) * kWideThreads] = acc[i][j][r];
-    }
-    u += ke - ks;
   }
 }
 
@@ -863,31 +448,6 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *__restrict__
 
 }  // namespace
 
-namespace {
-
-hipError_t cu_count(int &cus) {
-  int dev = 0;
-  hipError_t err = hipGetDevice(&dev);
-  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  return err;
-}
-
-// The stream-K schedule of a call, or blocks = 0 when whole wide tiles fill the CUs.
-hipError_t plan_streamk(int64_t m, int64_t n, int64_t kt, StreamK &sk) {
-  int cus = 0;
-  const hipError_t err = cu_count(cus);
-  if (err != hipSuccess) return err;
-  const int64_t tiles_m = (m + BM - 1) / BM;
-  const int64_t tiles = tiles_m * ((n + BN - 1) / BN);
-  sk.tiles_m = (int)tiles_m;
-  sk.kt = (int)kt;
-  sk.units = tiles * sk.kt;
-  sk.blocks = tiles >= cus ? 0 : (int)(sk.units < cus ? sk.units : cus);
-  return hipSuccess;
-}
-
-}  // namespace
-
 hipError_t engram_gemm_bf16_workspace(int64_t m, int64_t n, int64_t k, size_t *bytes) {
   *bytes = 0;
   if (m <= 0 || n <= 0) return hipSuccess;
@@ -919,10 +479,7 @@ hipError_t engram_launch_gemm_bf16(const uint16_t *e, const uint16_t *w, uint16_
                        stream, e, w, kv, (float *)workspace, (int)m, (int)n, (int)k, sk);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(gemm_streamk_fixup_kernel,
-                       dim3((unsigned)(tiles_m * tiles_n256 * kFixupParts)), dim3(kWideThreads),
-                       0, stream, (const float *)workspace, kv, (int)m, (int)n, sk);
-    return hipGetLastError();
+    return engram_gemm::launch_streamk_fixup((const float *)workspace, kv, m, n, sk, stream);
   }
   // No workspace: 128-wide tiles over the whole K.
   const int tiles_n128 = (int)((n + 127) / 128);
@@ -941,39 +498,10 @@ hipError_t engram_launch_gemm_f32(const float *e, const float *w, float *kv, int
   return hipGetLastError();
 }
 
-hipError_t engram_launch_gemm_mx(const uint8_t *w_codes, const uint8_t *w_scales,
-                                 const uint8_t *e_rows, int32_t segments, uint16_t *kv,
-                                 int64_t m, int64_t n, void *workspace, size_t workspace_bytes,
-                                 hipStream_t stream) {
-  if (m <= 0 || n <= 0) return hipSuccess;
-  const MxOperands op{w_codes, w_scales, e_rows, segments};
-  StreamK sk;
-  hipError_t err = plan_streamk(m, n, (int64_t)segments * 256 / kMxBk, sk);
-  if (err != hipSuccess) return err;
-  const int tiles_m = sk.tiles_m;
-  const int tiles_n = (int)((n + BN - 1) / BN);
-  const size_t need = (size_t)sk.blocks * 2 * kWideOutputs * kWideThreads * sizeof(float);
-  if (sk.blocks == 0 || workspace == nullptr || workspace_bytes < need) {
-    hipLaunchKernelGGL(gemm_mx_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kWideThreads),
-                       0, stream, op, kv, (int)m, (int)n, tiles_m, tiles_n);
-    return hipGetLastError();
-  }
-  hipLaunchKernelGGL(gemm_mx_streamk_kernel, dim3((unsigned)sk.blocks), dim3(kWideThreads), 0,
-                     stream, op, kv, (float *)workspace, (int)m, (int)n, sk);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(gemm_streamk_fixup_kernel, dim3((unsigned)(tiles_m * tiles_n * kFixupParts)),
-                     dim3(kWideThreads), 0, stream, (const float *)workspace, kv, (int)m, (int)n,
-                     sk);
+hipError_t engram_gemm::launch_streamk_fixup(const float *ws, uint16_t *kv, int64_t m, int64_t n,
+                                             const StreamK &sk, hipStream_t stream) {
+  const int64_t tiles = (int64_t)sk.tiles_m * ((n + BN - 1) / BN);
+  hipLaunchKernelGGL(gemm_streamk_fixup_kernel, dim3((unsigned)(tiles * kFixupParts)),
+                     dim3(kWideThreads), 0, stream, ws, kv, (int)m, (int)n, sk);
   return hipGetLastError();
-}
-
-hipError_t engram_gemm_mx_workspace(int64_t m, int64_t n, int32_t segments, size_t *bytes) {
-  *bytes = 0;
-  if (m <= 0 || n <= 0) return hipSuccess;
-  StreamK sk;
-  const hipError_t err = plan_streamk(m, n, (int64_t)segments * 256 / kMxBk, sk);
-  if (err != hipSuccess) return err;
-  *bytes = (size_t)sk.blocks * 2 * kWideOutputs * kWideThreads * sizeof(float);
-  return hipSuccess;
 }

@@ -217,6 +217,23 @@ def test_gate_conv_chunks_carry_history(splits):
     assert_close(_vals(ss[..., :c.hc]), alpha[:, -c.L:], "history gates")
 
 
+def test_gate_conv_many_sequence_starts_with_history():
+    """128 sequences of 37 tokens: every call is large enough for the register-
+    window kernel, whose blocks then hold several sequence starts; the second
+    chunk reads its first 9 positions' taps from the carried history."""
+    c = Case(128, 37, 2, 64, seed=25, dead_frac=0.1)
+    alpha, h_out, _ = c.oracle()
+    h_ref = c.h.clone()
+    g_ref = c.run(h_ref)
+    _check(c, h_ref, g_ref, alpha, h_out, "one shot")
+    h = c.h.clone()
+    sv, ss = c.state()
+    g1 = c.run(h, t0=0, t1=20, state_out=(sv, ss))
+    g2 = c.run(h, t0=20, t1=37, state_in=(sv, ss), state_out=(sv, ss))
+    _check(c, h, torch.cat([g1, g2], 1), alpha, h_out, "two chunks")
+    assert_close(_vals(h), _vals(h_ref), "two chunks vs one shot")
+
+
 def test_gate_conv_short_first_chunk_without_history():
     """A first chunk shorter than the reach: history rows before the sequence
     start are zero gates, i.e. zero input to the convolution."""
