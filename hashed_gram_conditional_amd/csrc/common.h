@@ -112,13 +112,15 @@ hipError_t engram_launch_hash(const EngramHashArgs &a, const int32_t *token_map,
                               const int32_t *hist_in, int32_t *hist_out,
                               int64_t *row_ids, hipStream_t stream);
 
+// host_table: the table is pinned host memory; the gather then runs on a few
+// CUs as a grid-strided kernel, leaving the rest to concurrent work.
 hipError_t engram_launch_gather_e4m3(const uint8_t *table, int64_t table_rows,
                                      const int64_t *row_ids, int64_t n_ids,
-                                     uint16_t *out, hipStream_t stream);
+                                     uint16_t *out, bool host_table, hipStream_t stream);
 
 hipError_t engram_launch_gather_rows(const uint8_t *table, int64_t table_rows,
                                      const int64_t *row_ids, int64_t n_ids, uint8_t *out,
-                                     hipStream_t stream);
+                                     bool host_table, hipStream_t stream);
 
 hipError_t engram_launch_gather_f32(const float *table, int64_t table_rows,
                                     int32_t row_dim, const int64_t *row_ids,

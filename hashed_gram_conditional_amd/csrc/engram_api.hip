@@ -187,6 +187,29 @@ size_t gate_conv_workspace(const engram_forward_desc *d) {
   return align256((size_t)(d->batch * d->seq) * (size_t)(d->hc + 1) * sizeof(float));
 }
 
+// The address through which the kernels read a table: device (or managed)
+// memory as it is, pinned host memory through its mapping into the device's
+// address space, so the kernels then read the rows over the host link. Memory
+// the device cannot reach (pageable host memory, an unknown pointer) would
+// fault in a kernel and is rejected here instead.
+int resolve_table(const void *table, int64_t table_rows, const void **dev, bool *host) {
+  *dev = table;
+  *host = false;
+  if (table_rows == 0) return ENGRAM_OK;
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, table) != hipSuccess) {
+    (void)hipGetLastError();
+    return ENGRAM_EINVAL;
+  }
+  if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged) return ENGRAM_OK;
+  if (a.type == hipMemoryTypeHost && a.devicePointer != nullptr) {
+    *dev = a.devicePointer;
+    *host = true;
+    return ENGRAM_OK;
+  }
+  return ENGRAM_EINVAL;
+}
+
 // The last HIP error an entry point returned ENGRAM_EHIP for, per host thread.
 thread_local hipError_t g_last_hip_error = hipSuccess;
 
@@ -320,10 +343,13 @@ int engram_gather(const void *table, int64_t table_rows, int32_t row_format, int
   if (row_ids == nullptr || out == nullptr || (table == nullptr && table_rows > 0))
     return ENGRAM_EINVAL;
   if (!aligned(table, 16) || !aligned(row_ids, 8) || !aligned(out, 16)) return ENGRAM_EINVAL;
+  bool host = false;
+  const int rc = resolve_table(table, table_rows, &table, &host);
+  if (rc != ENGRAM_OK) return rc;
   hipError_t e;
   if (row_format == ENGRAM_ROW_E4M3_E8M0_264)
     e = engram_launch_gather_e4m3((const uint8_t *)table, table_rows, row_ids, n_ids,
-                                  (uint16_t *)out, stream);
+                                  (uint16_t *)out, host, stream);
   else
     e = engram_launch_gather_f32((const float *)table, table_rows, row_dim, row_ids, n_ids,
                                  (float *)out, stream);
@@ -337,8 +363,11 @@ int engram_gather_rows(const void *table, int64_t table_rows, const int64_t *row
   if (row_ids == nullptr || out == nullptr || (table == nullptr && table_rows > 0))
     return ENGRAM_EINVAL;
   if (!aligned(table, 8) || !aligned(row_ids, 8) || !aligned(out, 8)) return ENGRAM_EINVAL;
+  bool host = false;
+  const int rc = resolve_table(table, table_rows, &table, &host);
+  if (rc != ENGRAM_OK) return rc;
   return hip_status(engram_launch_gather_rows((const uint8_t *)table, table_rows, row_ids,
-                                              n_ids, (uint8_t *)out, stream));
+                                              n_ids, (uint8_t *)out, host, stream));
 }
 
 size_t engram_project_mx_workspace_size(int64_t tokens, int32_t segments, int64_t out_dim) {
@@ -501,6 +530,7 @@ int forward_impl(const engram_hash_params *params, const engram_forward_desc *de
   const int64_t out_dim = (int64_t)(desc->hc + 1) * desc->dim;
   if (!f32 && in_dim % 64) return ENGRAM_ESHAPE;
   if (ntok > INT32_MAX) return ENGRAM_ESHAPE;
+  bool host = false;
   if (ntok > 0) {
     if (ids == nullptr || table == nullptr || wkv == nullptr || q_w == nullptr ||
         k_w == nullptr || h == nullptr)
@@ -512,6 +542,7 @@ int forward_impl(const engram_hash_params *params, const engram_forward_desc *de
                         (conv != nullptr ? gate_conv_workspace(desc) : 0);
     if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
       return ENGRAM_EWORKSPACE;
+    if ((rc = resolve_table(table, desc->table_rows, &table, &host)) != ENGRAM_OK) return rc;
   }
   if (!aligned(hist_in, 4) || !aligned(hist_out, 4)) return ENGRAM_EINVAL;
 
@@ -545,7 +576,7 @@ int forward_impl(const engram_hash_params *params, const engram_forward_desc *de
   err = f32 ? engram_launch_gather_f32((const float *)table, desc->table_rows, desc->row_dim,
                                        row_ids, ntok * S, (float *)e, stream)
             : engram_launch_gather_e4m3((const uint8_t *)table, desc->table_rows, row_ids,
-                                        ntok * S, (uint16_t *)e, stream);
+                                        ntok * S, (uint16_t *)e, host, stream);
   if (err != hipSuccess) return hip_status(err);
   err = f32 ? engram_launch_gemm_f32((const float *)e, (const float *)wkv, (float *)kv, ntok,
                                      out_dim, in_dim, stream)
@@ -621,6 +652,7 @@ int engram_forward_mx(const engram_hash_params *params, const engram_forward_des
   const int32_t S = (params->max_ngram - 1) * params->heads;
   const int64_t out_dim = (int64_t)(desc->hc + 1) * desc->dim;
   if (ntok > INT32_MAX) return ENGRAM_ESHAPE;
+  bool host = false;
   if (ntok > 0) {
     if (ids == nullptr || table == nullptr || w_codes == nullptr || w_scales == nullptr ||
         q_w == nullptr || k_w == nullptr || h == nullptr)
@@ -632,6 +664,7 @@ int engram_forward_mx(const engram_hash_params *params, const engram_forward_des
     const size_t need = engram_forward_mx_workspace_size(params, desc);
     if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
       return ENGRAM_EWORKSPACE;
+    if ((rc = resolve_table(table, desc->table_rows, &table, &host)) != ENGRAM_OK) return rc;
   }
   if (!aligned(hist_in, 4) || !aligned(hist_out, 4)) return ENGRAM_EINVAL;
 
@@ -647,7 +680,7 @@ int engram_forward_mx(const engram_hash_params *params, const engram_forward_des
                                       hist_in, hist_out, row_ids, stream);
   if (err != hipSuccess || ntok == 0) return hip_status(err);
   err = engram_launch_gather_rows((const uint8_t *)table, desc->table_rows, row_ids, ntok * S,
-                                  e_rows, stream);
+                                  e_rows, host, stream);
   if (err != hipSuccess) return hip_status(err);
   err = engram_launch_gemm_mx((const uint8_t *)w_codes, (const uint8_t *)w_scales, e_rows, S, kv,
                               ntok, out_dim, gemm_ws, gemm_ws_bytes, stream);

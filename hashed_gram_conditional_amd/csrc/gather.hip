@@ -68,13 +68,16 @@ __device__ __forceinline__ uint4 dequant8(uint2 q, uint32_t s) {
   return o;
 }
 
-__global__ __launch_bounds__(kThreads) void gather_e4m3_kernel(
+template <int NT>
+__global__ __launch_bounds__(NT) void gather_e4m3_kernel(
     const uint8_t *__restrict__ table, int64_t table_rows, const int64_t *__restrict__ row_ids,
     int64_t n, uint16_t *__restrict__ out) {
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
   const int l = lane & 31;
-  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const int64_t waves = (int64_t)gridDim.x * (NT >> 6);
+  for (int64_t wave = ((int64_t)blockIdx.x * NT + threadIdx.x) >> 6;
+       wave * kRowsPerWave < n; wave += waves) {
   const int64_t base = wave * kRowsPerWave;
 
   int64_t r[kSlots];
@@ -105,6 +108,7 @@ __global__ __launch_bounds__(kThreads) void gather_e4m3_kernel(
       *reinterpret_cast<uint4 *>(out + idx * ENGRAM_ROW_DIM_E4M3 + 8 * l) = o;
     }
   }
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void gather_f32_kernel(
@@ -128,39 +132,73 @@ __global__ __launch_bounds__(kThreads) void gather_f32_kernel(
 // give zero rows.
 constexpr int kRowWords = ENGRAM_ROW_BYTES / 8;
 
-__global__ __launch_bounds__(kThreads) void gather_rows_kernel(
+// U words per thread per pass, kept in flight together: a pass of the whole grid
+// covers U * threads words, then the grid strides on.
+template <int NT, int U>
+__global__ __launch_bounds__(NT) void gather_rows_kernel(
     const uint8_t *__restrict__ table, int64_t table_rows, const int64_t *__restrict__ row_ids,
     int64_t n_ids, uint8_t *__restrict__ out) {
-  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (g >= n_ids * kRowWords) return;
-  const int64_t i = g / kRowWords;
-  const int w = (int)(g - i * kRowWords);
-  const int64_t r = row_ids[i];
-  uint2 v = make_uint2(0u, 0u);
-  if (r >= 0 && r < table_rows)
-    v = *reinterpret_cast<const uint2 *>(table + r * ENGRAM_ROW_BYTES + (int64_t)w * 8);
-  *reinterpret_cast<uint2 *>(out + i * ENGRAM_ROW_BYTES + (int64_t)w * 8) = v;
+  const int64_t total = n_ids * kRowWords;
+  const int64_t threads = (int64_t)gridDim.x * NT;
+  for (int64_t g0 = (int64_t)blockIdx.x * NT + threadIdx.x; g0 < total; g0 += U * threads) {
+    uint2 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t g = g0 + u * threads;
+      v[u] = make_uint2(0u, 0u);
+      if (g < total) {
+        const int64_t i = g / kRowWords;
+        const int w = (int)(g - i * kRowWords);
+        const int64_t r = row_ids[i];
+        if (r >= 0 && r < table_rows)
+          v[u] = *reinterpret_cast<const uint2 *>(table + r * ENGRAM_ROW_BYTES + (int64_t)w * 8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t g = g0 + u * threads;
+      if (g < total) *reinterpret_cast<uint2 *>(out + g * 8) = v[u];
+    }
+  }
 }
+
+// Grid of the gathers from a host-resident table: one 1024-thread block per XCD
+// fills one CU each, so a fetch running beside the projection takes 8 of the
+// 256 CUs, while keeping about half a megabyte of reads in flight over the
+// host link.
+constexpr int kHostThreads = 1024;
+constexpr int kHostBlocks = 8;
+constexpr int kHostUnroll = 8;
 
 }  // namespace
 
 hipError_t engram_launch_gather_rows(const uint8_t *table, int64_t table_rows,
                                      const int64_t *row_ids, int64_t n_ids, uint8_t *out,
-                                     hipStream_t stream) {
+                                     bool host_table, hipStream_t stream) {
   if (n_ids <= 0) return hipSuccess;
+  if (host_table) {
+    hipLaunchKernelGGL((gather_rows_kernel<kHostThreads, kHostUnroll>), dim3(kHostBlocks),
+                       dim3(kHostThreads), 0, stream, table, table_rows, row_ids, n_ids, out);
+    return hipGetLastError();
+  }
   const int64_t blocks = (n_ids * kRowWords + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                     table, table_rows, row_ids, n_ids, out);
+  hipLaunchKernelGGL((gather_rows_kernel<kThreads, 1>), dim3((unsigned)blocks), dim3(kThreads),
+                     0, stream, table, table_rows, row_ids, n_ids, out);
   return hipGetLastError();
 }
 
 hipError_t engram_launch_gather_e4m3(const uint8_t *table, int64_t table_rows,
                                      const int64_t *row_ids, int64_t n_ids, uint16_t *out,
-                                     hipStream_t stream) {
+                                     bool host_table, hipStream_t stream) {
   if (n_ids <= 0) return hipSuccess;
+  if (host_table) {
+    hipLaunchKernelGGL(gather_e4m3_kernel<kHostThreads>, dim3(kHostBlocks), dim3(kHostThreads),
+                       0, stream, table, table_rows, row_ids, n_ids, out);
+    return hipGetLastError();
+  }
   const int64_t blocks = (n_ids + kRowsPerBlock - 1) / kRowsPerBlock;
-  hipLaunchKernelGGL(gather_e4m3_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                     table, table_rows, row_ids, n_ids, out);
+  hipLaunchKernelGGL(gather_e4m3_kernel<kThreads>, dim3((unsigned)blocks), dim3(kThreads), 0,
+                     stream, table, table_rows, row_ids, n_ids, out);
   return hipGetLastError();
 }
 

@@ -44,6 +44,21 @@
  *     out-of-range rows output zero rows). The gate decides DEAD positions from
  *     the raw id alone, so a map must pass engram_check_token_map first.
  *   - Calls that write overlapping buffers on different streams race.
+ *
+ * Host-resident tables ([P1] "放在第 1 层和第 14 层", last paragraph: the rows a
+ * step needs depend on the token ids alone, so the table can stay in host memory
+ * and the rows move to the GPU while earlier layers compute; [P5] §8.2-§8.4:
+ * prefetch on a separate path, wait for its completion event, stall =
+ * max(0, T_fetch - T_window); [P3] §五: the host link's bandwidth is the cost).
+ * Every entry point that reads a table (engram_gather, engram_gather_rows,
+ * engram_forward, engram_forward_conv, engram_forward_mx) accepts pinned host
+ * memory (hipHostMalloc, or torch's pin_memory) as well as device memory: its
+ * kernels then read the 264-byte rows over the host link themselves, straight
+ * into HBM, with no staging copy on the host. A prefetch is engram_hash +
+ * engram_gather (or engram_gather_rows) on a second stream, ordered before the
+ * consuming engram_project (or engram_project_mx) by an event. A table pointer
+ * the device cannot read (pageable host memory, an unknown address) is
+ * rejected with ENGRAM_EINVAL before any launch.
  */
 #ifndef ENGRAM_H
 #define ENGRAM_H
@@ -255,7 +270,8 @@ int engram_hash_layers(const engram_hash_params *params, int32_t layers, const i
 /*
  * Step 3: gather and dequantise rows ([P3] §2.3: fp8 E4M3 payload and E8M0
  * block scales, bf16 output; [P4] "永不常驻的 I/O 设计": 32 values share a scale).
- *   table    row_format rows: uint8 [table_rows, 264] or float [table_rows, row_dim]
+ *   table    row_format rows: uint8 [table_rows, 264] or float [table_rows, row_dim],
+ *            in device memory or in pinned host memory (see "Host-resident tables")
  *   row_ids  int64 [n_ids]; ids outside [0, table_rows) give zero rows
  *   out      [n_ids, row_dim] bf16 (E4M3 rows, row_dim = 256) or float (fp32 rows)
  * Dequantisation is exact: E4M3(q) * 2^(s - 127) rounded once to bf16 (nearest,
@@ -271,7 +287,8 @@ int engram_gather(const void *table, int64_t table_rows, int32_t row_format,
  * unchanged (256 E4M3 codes then 8 E8M0 scales each; [P4] "永不常驻的 I/O 设计"),
  * which engram_project_mx consumes without dequantisation. A row id outside
  * [0, table_rows) gives a zero row ([P3] §五).
- *   table    uint8 [table_rows, 264], 8-byte aligned
+ *   table    uint8 [table_rows, 264], 8-byte aligned, in device memory or in pinned
+ *            host memory (see "Host-resident tables")
  *   row_ids  int64 [n_ids]
  *   out      uint8 [n_ids, 264], 8-byte aligned
  * Errors: ENGRAM_EINVAL, ENGRAM_ESHAPE, ENGRAM_EHIP.
