@@ -13,10 +13,12 @@
 //
 // One block per token: 128 threads when there are enough tokens to fill the
 // chip, 512 when there are few (decode). Each thread owns CPT chunks of 8
-// elements per stream (16-byte bf16 accesses). The three reductions per stream
-// (sum h^2, sum k^2, sum h q_w k_w k) run first; the update then reads the
-// token's h again, which the L2 still holds (40 KiB per token), instead of
-// keeping it in registers, so more blocks fit per CU. All arithmetic is fp32.
+// elements per stream (16-byte bf16 accesses). Streams are handled one after
+// another: the three reductions of stream m (sum h^2, sum k^2, sum h q_w k_w k)
+// need only its own h and k, so after one barrier its gate is known and its h,
+// still in registers, is updated and stored before the next stream is read. h
+// is read from HBM once (updating all streams after all reductions re-read it,
+// and the L2 had often dropped it by then). All arithmetic is fp32.
 //
 // With a stats buffer the kernel is the first half of the short-convolution
 // variant: it stores each token's gates and the mean square of its value row
@@ -38,7 +40,9 @@ __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
     const float *__restrict__ q_w, const float *__restrict__ k_w, void *__restrict__ h,
     float *__restrict__ gate_out, float *__restrict__ stats, int hc, int dim, float eps,
     float clamp, int plain) {
-  __shared__ float red[kMaxThreads / engram::kWave][3 * kMaxHc + 1];
+  // one slot per (wave, stream): every stream's partial sums have their own
+  // place, so one barrier per stream orders writes before reads
+  __shared__ float red[kMaxThreads / engram::kWave][kMaxHc + 1][3];
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x;
   const int nthreads = blockDim.x;
@@ -51,6 +55,11 @@ __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
   const int cps = dim / kChunk;                   // chunks per stream
   const int64_t kv_row = t * (int64_t)(hc + 1) * cps;
   const int64_t h_row = t * (int64_t)hc * cps;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int nwaves = nthreads >> 6;
+  const float inv_d = 1.0f / (float)dim;
+  const float inv_sqrt_d = 1.0f / sqrtf((float)dim);
 
   Chunk<F32> vv[CPT];
 #pragma unroll
@@ -58,39 +67,6 @@ __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
     const int ci = tid + c * nthreads;
     if (ci < cps) vv[c].load(kv, kv_row + (int64_t)hc * cps + ci);
   }
-  float shh[kMaxHc], skk[kMaxHc], shk[kMaxHc];
-#pragma unroll
-  for (int m = 0; m < kMaxHc; ++m) {
-    shh[m] = 0.f;
-    skk[m] = 0.f;
-    shk[m] = 0.f;
-    if (m < hc) {
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int ci = tid + c * nthreads;
-        if (ci < cps) {
-          Chunk<F32> hc_, kc;
-          hc_.load(h, h_row + (int64_t)m * cps + ci);
-          kc.load(kv, kv_row + (int64_t)m * cps + ci);
-          const float4 *qp = reinterpret_cast<const float4 *>(q_w + (int64_t)m * dim) + 2 * ci;
-          const float4 *kp = reinterpret_cast<const float4 *>(k_w + (int64_t)m * dim) + 2 * ci;
-          const float4 q0 = qp[0], q1 = qp[1], k0 = kp[0], k1 = kp[1];
-          const float w[8] = {q0.x * k0.x, q0.y * k0.y, q0.z * k0.z, q0.w * k0.w,
-                              q1.x * k1.x, q1.y * k1.y, q1.z * k1.z, q1.w * k1.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float he = hc_[e];
-            const float ke = kc[e];
-            shh[m] = fmaf(he, he, shh[m]);
-            skk[m] = fmaf(ke, ke, skk[m]);
-            shk[m] = fmaf(he * w[e], ke, shk[m]);
-          }
-        }
-      }
-    }
-  }
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
   if (stats != nullptr) {
     float svv = 0.f;
 #pragma unroll
@@ -102,76 +78,81 @@ __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
       }
     }
     svv = engram::warp_sum(svv);
-    if (lane == 0) red[wave][3 * kMaxHc] = svv;
+    if (lane == 0) red[wave][kMaxHc][0] = svv;
   }
+
+  // Stream by stream: the gate of stream m depends on its own h and k only, so
+  // its h is reduced, gated and updated from registers before the next stream
+  // is read; h crosses HBM once in each direction.
 #pragma unroll
   for (int m = 0; m < kMaxHc; ++m) {
-    if (m < hc) {
-      const float a = engram::warp_sum(shh[m]);
-      const float b = engram::warp_sum(skk[m]);
-      const float c = engram::warp_sum(shk[m]);
-      if (lane == 0) {
-        red[wave][3 * m + 0] = a;
-        red[wave][3 * m + 1] = b;
-        red[wave][3 * m + 2] = c;
+    if (m >= hc) break;
+    Chunk<F32> hh[CPT];
+    float shh = 0.f, skk = 0.f, shk = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ci = tid + c * nthreads;
+      if (ci < cps) {
+        Chunk<F32> kc;
+        hh[c].load(h, h_row + (int64_t)m * cps + ci);
+        kc.load(kv, kv_row + (int64_t)m * cps + ci);
+        const float4 *qp = reinterpret_cast<const float4 *>(q_w + (int64_t)m * dim) + 2 * ci;
+        const float4 *kp = reinterpret_cast<const float4 *>(k_w + (int64_t)m * dim) + 2 * ci;
+        const float4 q0 = qp[0], q1 = qp[1], k0 = kp[0], k1 = kp[1];
+        const float w[8] = {q0.x * k0.x, q0.y * k0.y, q0.z * k0.z, q0.w * k0.w,
+                            q1.x * k1.x, q1.y * k1.y, q1.z * k1.z, q1.w * k1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float he = hh[c][e];
+          const float ke = kc[e];
+          shh = fmaf(he, he, shh);
+          skk = fmaf(ke, ke, skk);
+          shk = fmaf(he * w[e], ke, shk);
+        }
       }
     }
-  }
-  __syncthreads();
-  const float inv_d = 1.0f / (float)dim;
-  const float inv_sqrt_d = 1.0f / sqrtf((float)dim);
-  float alpha[kMaxHc];
-#pragma unroll
-  for (int m = 0; m < kMaxHc; ++m) {
-    alpha[m] = 0.f;
-    if (m < hc) {
-      float a = 0.f, b = 0.f, c = 0.f;
-#pragma unroll
-      for (int w = 0; w < (nthreads >> 6); ++w) {
-        a += red[w][3 * m + 0];
-        b += red[w][3 * m + 1];
-        c += red[w][3 * m + 2];
-      }
-      const float rh = 1.0f / sqrtf(a * inv_d + eps);
-      const float rk = 1.0f / sqrtf(b * inv_d + eps);
-      const float s = c * rh * rk * inv_sqrt_d;
-      const float z = plain ? s : copysignf(sqrtf(fmaxf(fabsf(s), clamp)), s);
-      alpha[m] = 1.0f / (1.0f + expf(-z));
+    shh = engram::warp_sum(shh);
+    skk = engram::warp_sum(skk);
+    shk = engram::warp_sum(shk);
+    if (lane == 0) {
+      red[wave][m][0] = shh;
+      red[wave][m][1] = skk;
+      red[wave][m][2] = shk;
     }
-  }
-  if (gate_out != nullptr && tid < hc) {
-#pragma unroll
-    for (int m = 0; m < kMaxHc; ++m)
-      if (m == tid) gate_out[t * hc + m] = alpha[m];
-  }
-  if (stats != nullptr) {
-    if (tid < hc) {
-#pragma unroll
-      for (int m = 0; m < kMaxHc; ++m)
-        if (m == tid) stats[t * (hc + 1) + m] = alpha[m];
-    } else if (tid == hc) {
-      float svv = 0.f;
-      for (int w = 0; w < (nthreads >> 6); ++w) svv += red[w][3 * kMaxHc];
-      stats[t * (hc + 1) + hc] = svv * inv_d;
+    __syncthreads();
+    float a = 0.f, b = 0.f, c2 = 0.f;
+    for (int w = 0; w < nwaves; ++w) {
+      a += red[w][m][0];
+      b += red[w][m][1];
+      c2 += red[w][m][2];
     }
-    return;
-  }
-#pragma unroll
-  for (int m = 0; m < kMaxHc; ++m) {
-    if (m < hc) {
+    const float rh = 1.0f / sqrtf(a * inv_d + eps);
+    const float rk = 1.0f / sqrtf(b * inv_d + eps);
+    const float sc = c2 * rh * rk * inv_sqrt_d;
+    const float z = plain ? sc : copysignf(sqrtf(fmaxf(fabsf(sc), clamp)), sc);
+    const float alpha = 1.0f / (1.0f + expf(-z));
+    if (tid == 0) {
+      if (gate_out != nullptr) gate_out[t * hc + m] = alpha;
+      if (stats != nullptr) stats[t * (hc + 1) + m] = alpha;
+    }
+    if (stats == nullptr) {
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         const int ci = tid + c * nthreads;
         if (ci < cps) {
-          Chunk<F32> hc_;
-          hc_.load(h, h_row + (int64_t)m * cps + ci);
           float o[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = fmaf(alpha[m], vv[c][e], hc_[e]);
+          for (int e = 0; e < 8; ++e) o[e] = fmaf(alpha, vv[c][e], hh[c][e]);
           Chunk<F32>::store(h, h_row + (int64_t)m * cps + ci, o);
         }
       }
     }
+  }
+  if (stats != nullptr && tid == 0) {
+    // the value row's partial sums were published before the first barrier
+    float svv = 0.f;
+    for (int w = 0; w < nwaves; ++w) svv += red[w][kMaxHc][0];
+    stats[t * (hc + 1) + hc] = svv * inv_d;
   }
 }
 
