@@ -322,12 +322,13 @@ def _project_ws(M, K, N):
 
 
 # Fewer 256 x 256 tiles than CUs selects split-K over the CUs (with a workspace)
-# or 128-wide tiles (without); the last three shapes (>= 256 tiles of 256 x 256)
-# take the 256-wide path, with ragged edges and 2, 1 and 7 K-steps (the wide
-# kernel runs two steps per loop iteration).
+# or 128-wide tiles (without); the last five shapes (>= 256 tiles of 256 x 256)
+# take the 256-wide path, with ragged edges and 2, 8, 4, 1 and 7 K-steps (the
+# wide kernel runs two steps per loop iteration), up to 1089 tiles.
 @pytest.mark.parametrize("M,N,K", [(1, 8, 64), (31, 264, 192), (257, 520, 1024),
                                    (300, 408, 6144), (600, 256, 128), (513, 1032, 256),
-                                   (4100, 4008, 128), (2304, 7176, 64), (4097, 4104, 448)])
+                                   (4100, 4008, 128), (4100, 4104, 512), (8448, 8200, 256),
+                                   (2304, 7176, 64), (4097, 4104, 448)])
 def test_project_bf16_shapes(M, N, K):
     rng = np.random.default_rng(M * 7 + N)
     e = gen.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32) * 3)
