@@ -213,6 +213,180 @@ void gemm_bf16_kernel(const uint16_t *__restrict__ E, const uint16_t *__restrict
   wide_store_bf16(acc, C, M, N, m0, n0);
 }
 
+// ---- skinny calls: one token tile, columns dealt to every CU ----------------------
+// With at most 256 tokens (decode) the 256 x 256 tiles number fewer than the
+// CUs. Here block b takes all tokens and its own slice of 32 * NT output columns
+// (96 or 128 for 25600 columns over 256 CUs: 224 x 96 + 32 x 128), so the blocks
+// cover N once with no K split and no partial sums. The weight streams from
+// HBM once, kSkRing - 1 K-steps ahead of use through a register ring; every
+// block reads the same E, which the L2 holds, 2 steps ahead. Both pass through
+// two LDS stages laid out as in the wide kernel (128-byte rows, the same
+// swizzle and fragment reads). Wave w owns tokens [64 w, 64 w + 64) against all
+// the block's columns. A step's E loads are issued before its weight loads, so
+// waiting for E (one step old) never waits for the weight's HBM latency. Each
+// output sums its K16 chunks in increasing order in one MFMA accumulator, as
+// the wide kernel does, so both give the same bits.
+constexpr int kSkMaxCols = 128;
+constexpr int kSkRing = 6;                // weight steps in registers
+
+struct SkinnyLds {
+  uint16_t w[2][kSkMaxCols * BK];
+  uint16_t e[2][BM * BK];
+};
+
+template <int NT>
+__device__ __forceinline__ void skinny_block(const uint16_t *__restrict__ E,
+                                             const uint16_t *__restrict__ W,
+                                             uint16_t *__restrict__ C, int M, int N, int K, int c0,
+                                             SkinnyLds &lds) {
+  const int KT = K / BK;                    // multiple of kSkRing (checked by the launcher)
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cols = min(32 * NT, N - c0);
+  const __amdgpu_buffer_rsrc_t rsW = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(W + (int64_t)c0 * K), 0, cols * K * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rsE = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(E), 0, min(M, BM) * K * 2, kBufferFlags);
+  // chunk q of a step: row q * 32 + t / 8, 16-byte column t % 8 (as in the wide kernel)
+  const int g_row = tid >> 3, g_chunk = tid & 7;
+  const int g_voff = (g_row * K + g_chunk * 8) * 2;
+  const int g_rstride = 32 * K * 2;
+  const int s_off = g_row * BK + ((g_chunk ^ (g_row & 7) ^ ((g_row >> 3) & 1)) << 3);
+  const int frow = lane & 31, fk = lane >> 5;
+  const int fsw = (frow & 7) ^ ((frow >> 3) & 1);
+  const int e_base = (wave * 64 + frow) * BK;
+
+  uint4 wr[kSkRing][4], er[2][8];
+  f32x16 acc[NT][2];
+#pragma unroll
+  for (int i = 0; i < NT; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  bf16x8 a0[NT], b0[2], a1[NT], b1[2];
+
+#define SK_KOFF(kt_) (((kt_) < KT ? (kt_) : KT - 1) * BK * 2)
+#define SK_LOADE(slot, kt_, q0, q1)                                                           \
+  _Pragma("unroll") for (int q = q0; q < q1; ++q)                                           \
+    er[slot][q] = load16(rsE, g_voff, q * g_rstride + SK_KOFF(kt_));
+#define SK_LOADW(slot, kt_, q0, q1)                                                           \
+  _Pragma("unroll") for (int q = q0; q < q1; ++q)                                           \
+    wr[slot][q] = load16(rsW, g_voff, q * g_rstride + SK_KOFF(kt_));
+#define SK_STOREE(st, slot, q0, q1)                                                           \
+  _Pragma("unroll") for (int q = q0; q < q1; ++q)                                           \
+    *reinterpret_cast<uint4 *>(&lds.e[st][s_off + q * 32 * BK]) = er[slot][q];
+#define SK_STOREW(st, slot, q0, q1)                                                           \
+  _Pragma("unroll") for (int q = q0; q < q1; ++q)                                           \
+    *reinterpret_cast<uint4 *>(&lds.w[st][s_off + q * 32 * BK]) = wr[slot][q];
+#define SK_FRAGS(st, kk, dst_a, dst_b)                                                        \
+  _Pragma("unroll") for (int i = 0; i < NT; ++i) dst_a[i] = *reinterpret_cast<const bf16x8 *>( \
+      &lds.w[st][(i * 32 + frow) * BK + ((((kk) * 2 + fk) ^ fsw) << 3)]);                   \
+  _Pragma("unroll") for (int j = 0; j < 2; ++j) dst_b[j] = *reinterpret_cast<const bf16x8 *>( \
+      &lds.e[st][e_base + j * 32 * BK + ((((kk) * 2 + fk) ^ fsw) << 3)]);
+#define SK_MMA(A, B)                                                                          \
+  _Pragma("unroll") for (int i = 0; i < NT; ++i)                                            \
+  _Pragma("unroll") for (int j = 0; j < 2; ++j)                                             \
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[i], B[j], acc[i][j], 0, 0, 0);
+#define SK_FENCE() __builtin_amdgcn_sched_barrier(0)
+// Step kt (ring slot s = kt % kSkRing) computes from stage s & 1. It loads E of
+// step kt + 2 into E slot s & 1 (stored to LDS during step kt - 1) and the
+// weight of step kt + kSkRing - 1 into the ring slot of step kt - 1 (stored
+// during step kt - 2), and stores step kt + 1 into the other stage, which every
+// wave finished reading before the previous barrier.
+#define SK_STEP(s)                                                                            \
+  {                                                                                         \
+    const int P = (s) & 1, Q = P ^ 1;                                                       \
+    const int ws_ = ((s) + 1) % kSkRing, wl_ = ((s) + kSkRing - 1) % kSkRing;               \
+    SK_FRAGS(P, 1, a1, b1);                                                                 \
+    SK_LOADE(P, kt + (s) + 2, 0, 3);                                                        \
+    SK_STOREE(Q, Q, 0, 4);                                                                  \
+    SK_MMA(a0, b0);                                                                         \
+    SK_FENCE();                                                                             \
+    SK_FRAGS(P, 2, a0, b0);                                                                 \
+    SK_LOADE(P, kt + (s) + 2, 3, 6);                                                        \
+    SK_STOREE(Q, Q, 4, 8);                                                                  \
+    SK_MMA(a1, b1);                                                                         \
+    SK_FENCE();                                                                             \
+    SK_FRAGS(P, 3, a1, b1);                                                                 \
+    SK_LOADE(P, kt + (s) + 2, 6, 8);                                                        \
+    SK_LOADW(wl_, kt + (s) + kSkRing - 1, 0, 2);                                            \
+    SK_STOREW(Q, ws_, 0, 2);                                                                \
+    SK_MMA(a0, b0);                                                                         \
+    SK_FENCE();                                                                             \
+    SK_LOADW(wl_, kt + (s) + kSkRing - 1, 2, 4);                                            \
+    SK_STOREW(Q, ws_, 2, 4);                                                                \
+    SK_MMA(a1, b1);                                                                         \
+    SK_FENCE();                                                                             \
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                       \
+    SK_FENCE();                                                                             \
+    SK_FRAGS(Q, 0, a0, b0);                                                                 \
+  }
+
+  // prologue: weight of steps 0 .. kSkRing - 2, E of steps 0 and 1; step 0 into stage 0
+#pragma unroll
+  for (int s = 0; s < kSkRing - 1; ++s) SK_LOADW(s, s, 0, 4);
+  SK_LOADE(0, 0, 0, 8);
+  SK_LOADE(1, 1, 0, 8);
+  SK_STOREW(0, 0, 0, 4);
+  SK_STOREE(0, 0, 0, 8);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  SK_FRAGS(0, 0, a0, b0);
+  for (int kt = 0; kt < KT; kt += kSkRing) {
+    SK_STEP(0) SK_STEP(1) SK_STEP(2) SK_STEP(3) SK_STEP(4) SK_STEP(5)
+  }
+#undef SK_STEP
+#undef SK_FENCE
+#undef SK_MMA
+#undef SK_FRAGS
+#undef SK_STOREW
+#undef SK_STOREE
+#undef SK_LOADW
+#undef SK_LOADE
+#undef SK_KOFF
+
+  // accumulator r of (i, j): column c0 + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4,
+  // token 64 wave + 32 j + lane % 32
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int m = wave * 64 + j * 32 + frow;
+    if (m >= M) continue;
+    uint16_t *crow = C + (int64_t)m * N;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = c0 + i * 32 + g * 8 + fk * 4;
+        if (n < N) {
+          uint2 v;
+          v.x = engram::pack_bf16x2(acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1]);
+          v.y = engram::pack_bf16x2(acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]);
+          *reinterpret_cast<uint2 *>(crow + n) = v;
+        }
+      }
+    }
+  }
+}
+
+// Block b: columns [b w_lo + min(b, wide) 32, ...), 32 more than w_lo for the
+// first `wide` blocks.
+__global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_bf16_skinny_kernel(const uint16_t *__restrict__ E, const uint16_t *__restrict__ W,
+                             uint16_t *__restrict__ C, int M, int N, int K, int w_lo, int wide) {
+  __shared__ __align__(1024) SkinnyLds lds;
+  const int b = blockIdx.x;
+  const int c0 = b * w_lo + min(b, wide) * 32;
+  if (c0 >= N) return;
+  const int nt = (w_lo + (b < wide ? 32 : 0)) / 32;
+  if (nt == 4)
+    skinny_block<4>(E, W, C, M, N, K, c0, lds);
+  else if (nt == 3)
+    skinny_block<3>(E, W, C, M, N, K, c0, lds);
+  else
+    skinny_block<2>(E, W, C, M, N, K, c0, lds);
+}
+
 __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_streamk_kernel(const uint16_t *__restrict__ E, const uint16_t *__restrict__ W,
                               uint16_t *__restrict__ C, float *__restrict__ ws, int M, int N,
@@ -446,11 +620,32 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *__restrict__
   C[g] = acc;
 }
 
+// The skinny schedule, when it applies: at most one token tile, K a multiple of
+// 8 steps, and 64-128 columns per CU. w_lo = 32 floor(n / (32 G)); the first
+// `wide` blocks take 32 columns more.
+hipError_t plan_skinny(int64_t m, int64_t n, int64_t k, int &w_lo, int &wide, int &blocks) {
+  blocks = 0;
+  if (m > BM || k % (BK * kSkRing) != 0 || n > INT32_MAX) return hipSuccess;
+  int cus = 0;
+  const hipError_t err = cu_count(cus);
+  if (err != hipSuccess) return err;
+  const int64_t lo = (n / cus) / 32 * 32;
+  if (lo < 64 || lo + 32 > kSkMaxCols) return hipSuccess;
+  w_lo = (int)lo;
+  wide = (int)((n - (int64_t)cus * lo + 31) / 32);
+  blocks = cus;
+  return hipSuccess;
+}
+
 }  // namespace
 
 hipError_t engram_gemm_bf16_workspace(int64_t m, int64_t n, int64_t k, size_t *bytes) {
   *bytes = 0;
   if (m <= 0 || n <= 0) return hipSuccess;
+  int w_lo = 0, wide = 0, sk_blocks = 0;
+  hipError_t e0 = plan_skinny(m, n, k, w_lo, wide, sk_blocks);
+  if (e0 != hipSuccess) return e0;
+  if (sk_blocks > 0) return hipSuccess;
   StreamK sk;
   const hipError_t err = plan_streamk(m, n, k / BK, sk);
   if (err != hipSuccess) return err;
@@ -462,8 +657,16 @@ hipError_t engram_launch_gemm_bf16(const uint16_t *e, const uint16_t *w, uint16_
                                    int64_t m, int64_t n, int64_t k, void *workspace,
                                    size_t workspace_bytes, hipStream_t stream) {
   if (m <= 0 || n <= 0) return hipSuccess;
+  int w_lo = 0, wide = 0, sk_blocks = 0;
+  hipError_t err = plan_skinny(m, n, k, w_lo, wide, sk_blocks);
+  if (err != hipSuccess) return err;
+  if (sk_blocks > 0) {
+    hipLaunchKernelGGL(gemm_bf16_skinny_kernel, dim3((unsigned)sk_blocks), dim3(kWideThreads), 0,
+                       stream, e, w, kv, (int)m, (int)n, (int)k, w_lo, wide);
+    return hipGetLastError();
+  }
   StreamK sk;
-  hipError_t err = plan_streamk(m, n, k / BK, sk);
+  err = plan_streamk(m, n, k / BK, sk);
   if (err != hipSuccess) return err;
   const int tiles_m = sk.tiles_m;
   const int tiles_n256 = (int)((n + BN - 1) / BN);

@@ -346,10 +346,41 @@ def test_project_bf16_shapes(M, N, K):
         assert_close(got, exact, f"kv {M}x{N}x{K} ws={nb}", atol=0.0, rtol=0.0, extra=tol)
 
 
-# Split-K partitions: 256 tokens x 25600 (decode: 100 tiles x 96 steps over the
-# CUs), two token tiles, whole tiles only (K = 64), one-step pieces (K = 448).
-@pytest.mark.parametrize("M,N,K", [(256, 25600, 6144), (257, 2048, 6144), (1000, 4000, 64),
-                                   (200, 10240, 448), (1, 8, 64)])
+# One token tile against 64-128 columns per CU: the skinny kernel (no K split,
+# no workspace; K a multiple of 6 steps of 64). 25600 columns = 32 blocks of 128
+# + 224 of 96; 16400 and 20000 mix 96- and 64-column blocks; K = 384 is one
+# unrolled loop pass.
+@pytest.mark.parametrize("M,N,K", [(256, 25600, 6144), (1, 25600, 384), (77, 16400, 768),
+                                   (256, 20000, 2304)])
+def test_project_skinny(M, N, K):
+    say(f"project skinny {M}x{N}x{K}")
+    rng = np.random.default_rng(M + 3 * N + K)
+    e = gen.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32) * 3)
+    w = gen.f32_to_bf16_bits(rng.standard_normal((N, K)).astype(np.float32) * 0.05)
+    assert E.engram_project_workspace_size(M, K, N, 0) == 0
+    de, dw = to_device(e), to_device(w)
+    kv = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    E.engram_project(de, dw, kv, M, K, N, 0)
+    torch.cuda.synchronize()
+    ef, wf = O.bf16_bits_to_f64(e), O.bf16_bits_to_f64(w)
+    exact = O.project(ef, wf)
+    assert_close(O.bf16_bits_to_f64(bf16_bits(kv)), exact, f"kv skinny {M}x{N}x{K}", atol=0.0,
+                 rtol=0.0, extra=gemm_tolerance(ef, wf, exact, True))
+    # the same rows inside a call of 256-wide tiles give the same bits: each
+    # output sums its K16 chunks in the same order
+    big = 4096
+    e_big = torch.zeros((big, K), dtype=torch.bfloat16, device=DEV)
+    e_big[:M] = de
+    kv_big = torch.empty((big, N), dtype=torch.bfloat16, device=DEV)
+    E.engram_project(e_big, dw, kv_big, big, K, N, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(kv_big[:M].view(torch.int16), kv.view(torch.int16))
+
+
+# Split-K partitions: two token tiles, whole tiles only (K = 64), one-step
+# pieces (K = 448), a one-token call with few columns.
+@pytest.mark.parametrize("M,N,K", [(257, 2048, 6144), (1000, 4000, 64), (200, 10240, 448),
+                                   (1, 8, 64), (256, 25600, 6016)])
 def test_project_split_k(M, N, K):
     say(f"project split-K {M}x{N}x{K}")
     rng = np.random.default_rng(M + N + K)
