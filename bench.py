@@ -137,8 +137,8 @@ def main():
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures the layer on one GPU only; the sharded design "
-              "is described in DESIGN.md and no multi-GPU run is made.", file=sys.stderr)
+        print("bench.py: the layer is measured on one GPU only; no multi-GPU run is made.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
