@@ -13,7 +13,7 @@ from ._binding import (  # noqa: F401
     engram_make_primes, engram_make_layer_primes, engram_check_token_map, engram_hash,
     engram_hash_layers, engram_gather,
     engram_project, engram_project_workspace_size, engram_gate, engram_forward_workspace_size,
-    engram_forward, engram_gather_rows, engram_project_mx, engram_project_mx_workspace_size,
+    engram_forward, engram_gather_rows, engram_gather_mx, engram_project_mx, engram_project_mx_workspace_size,
     engram_forward_mx, engram_forward_mx_workspace_size,
     engram_gate_conv, engram_gate_conv_workspace_size, engram_forward_conv,
     engram_forward_conv_workspace_size,

@@ -120,7 +120,8 @@ def _load():
         "engram_gate": (ctypes.c_int, [P, P, I32, P, P, P, P, P, P]),
         "engram_forward_workspace_size": (SZ, [P, P]),
         "engram_gather_rows": (ctypes.c_int, [P, I64, P, I64, P, P]),
-        "engram_project_mx": (ctypes.c_int, [P, I32, P, P, P, I64, I64, P, SZ, P]),
+        "engram_project_mx": (ctypes.c_int, [P, P, I32, P, P, P, I64, I64, P, SZ, P]),
+        "engram_gather_mx": (ctypes.c_int, [P, I64, P, I64, P, P, P]),
         "engram_project_mx_workspace_size": (SZ, [I64, I32, I64]),
         "engram_forward_mx_workspace_size": (SZ, [P, P]),
         "engram_forward_mx": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
@@ -298,11 +299,16 @@ def engram_project_mx_workspace_size(tokens: int, segments: int, out_dim: int) -
     return LIB.engram_project_mx_workspace_size(tokens, segments, out_dim)
 
 
-def engram_project_mx(e_rows, segments: int, w_codes, w_scales, kv, tokens: int, out_dim: int,
-                      workspace=None, workspace_bytes: int = 0, stream=None):
-    _check(LIB.engram_project_mx(_ptr(e_rows), segments, _ptr(w_codes), _ptr(w_scales),
-                                 _ptr(kv), tokens, out_dim, _ptr(workspace), workspace_bytes,
-                                 _stream(stream)), "engram_project_mx")
+def engram_gather_mx(table, table_rows: int, row_ids, n_ids: int, codes, scales, stream=None):
+    _check(LIB.engram_gather_mx(_ptr(table), table_rows, _ptr(row_ids), n_ids, _ptr(codes),
+                                _ptr(scales), _stream(stream)), "engram_gather_mx")
+
+
+def engram_project_mx(e_codes, e_scales, segments: int, w_codes, w_scales, kv, tokens: int,
+                      out_dim: int, workspace=None, workspace_bytes: int = 0, stream=None):
+    _check(LIB.engram_project_mx(_ptr(e_codes), _ptr(e_scales), segments, _ptr(w_codes),
+                                 _ptr(w_scales), _ptr(kv), tokens, out_dim, _ptr(workspace),
+                                 workspace_bytes, _stream(stream)), "engram_project_mx")
 
 
 def engram_forward_mx_workspace_size(params: HashParams, desc: ForwardDesc) -> int:

@@ -122,6 +122,11 @@ hipError_t engram_launch_gather_rows(const uint8_t *table, int64_t table_rows,
                                      const int64_t *row_ids, int64_t n_ids, uint8_t *out,
                                      bool host_table, hipStream_t stream);
 
+// Rows split into their codes [n_ids, 256] and scales [n_ids, 8].
+hipError_t engram_launch_gather_mx(const uint8_t *table, int64_t table_rows,
+                                   const int64_t *row_ids, int64_t n_ids, uint8_t *codes,
+                                   uint8_t *scales, bool host_table, hipStream_t stream);
+
 hipError_t engram_launch_gather_f32(const float *table, int64_t table_rows,
                                     int32_t row_dim, const int64_t *row_ids,
                                     int64_t n_ids, float *out, hipStream_t stream);
@@ -137,7 +142,8 @@ hipError_t engram_gemm_bf16_workspace(int64_t m, int64_t n, int64_t k, size_t *b
 // looked-up 264-byte rows [m, S, 264]; kv bf16 [m, n]. Split-K as for bf16
 // when a large enough workspace is given.
 hipError_t engram_launch_gemm_mx(const uint8_t *w_codes, const uint8_t *w_scales,
-                                 const uint8_t *e_rows, int32_t segments, uint16_t *kv,
+                                 const uint8_t *e_codes, const uint8_t *e_scales,
+                                 int32_t segments, uint16_t *kv,
                                  int64_t m, int64_t n, void *workspace, size_t workspace_bytes,
                                  hipStream_t stream);
 hipError_t engram_gemm_mx_workspace(int64_t m, int64_t n, int32_t segments, size_t *bytes);

@@ -370,6 +370,22 @@ int engram_gather_rows(const void *table, int64_t table_rows, const int64_t *row
                                               n_ids, (uint8_t *)out, host, stream));
 }
 
+int engram_gather_mx(const void *table, int64_t table_rows, const int64_t *row_ids,
+                     int64_t n_ids, void *codes, void *scales, hipStream_t stream) {
+  if (n_ids < 0 || table_rows < 0) return ENGRAM_ESHAPE;
+  if (n_ids == 0) return ENGRAM_OK;
+  if (row_ids == nullptr || codes == nullptr || scales == nullptr ||
+      (table == nullptr && table_rows > 0))
+    return ENGRAM_EINVAL;
+  if (!aligned(table, 8) || !aligned(row_ids, 8) || !aligned(codes, 16) || !aligned(scales, 8))
+    return ENGRAM_EINVAL;
+  bool host = false;
+  const int rc = resolve_table(table, table_rows, &table, &host);
+  if (rc != ENGRAM_OK) return rc;
+  return hip_status(engram_launch_gather_mx((const uint8_t *)table, table_rows, row_ids, n_ids,
+                                            (uint8_t *)codes, (uint8_t *)scales, host, stream));
+}
+
 size_t engram_project_mx_workspace_size(int64_t tokens, int32_t segments, int64_t out_dim) {
   if (tokens <= 0 || segments < 1 || out_dim < 1) return 0;
   size_t bytes = 0;
@@ -377,16 +393,19 @@ size_t engram_project_mx_workspace_size(int64_t tokens, int32_t segments, int64_
   return bytes;
 }
 
-int engram_project_mx(const void *e_rows, int32_t segments, const void *w_codes,
-                      const void *w_scales, void *kv, int64_t tokens, int64_t out_dim,
-                      void *workspace, size_t workspace_bytes, hipStream_t stream) {
+int engram_project_mx(const void *e_codes, const void *e_scales, int32_t segments,
+                      const void *w_codes, const void *w_scales, void *kv, int64_t tokens,
+                      int64_t out_dim, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
   if (tokens < 0 || segments < 1 || segments > ENGRAM_MAX_SEGMENTS || out_dim < 1)
     return ENGRAM_ESHAPE;
   if (out_dim % 8 || tokens > INT32_MAX || out_dim > INT32_MAX) return ENGRAM_ESHAPE;
   if (tokens == 0) return ENGRAM_OK;
-  if (e_rows == nullptr || w_codes == nullptr || w_scales == nullptr || kv == nullptr)
+  if (e_codes == nullptr || e_scales == nullptr || w_codes == nullptr || w_scales == nullptr ||
+      kv == nullptr)
     return ENGRAM_EINVAL;
-  if (!aligned(e_rows, 8) || !aligned(w_codes, 16) || !aligned(w_scales, 4) || !aligned(kv, 16))
+  if (!aligned(e_codes, 16) || !aligned(e_scales, 4) || !aligned(w_codes, 16) ||
+      !aligned(w_scales, 4) || !aligned(kv, 16))
     return ENGRAM_EINVAL;
   if (workspace != nullptr) {
     if (!aligned(workspace, 256) ||
@@ -394,8 +413,9 @@ int engram_project_mx(const void *e_rows, int32_t segments, const void *w_codes,
       return ENGRAM_EWORKSPACE;
   }
   return hip_status(engram_launch_gemm_mx((const uint8_t *)w_codes, (const uint8_t *)w_scales,
-                                          (const uint8_t *)e_rows, segments, (uint16_t *)kv,
-                                          tokens, out_dim, workspace, workspace_bytes, stream));
+                                          (const uint8_t *)e_codes, (const uint8_t *)e_scales,
+                                          segments, (uint16_t *)kv, tokens, out_dim, workspace,
+                                          workspace_bytes, stream));
 }
 
 size_t engram_project_workspace_size(int64_t tokens, int64_t in_dim, int64_t out_dim,
@@ -632,8 +652,8 @@ size_t engram_forward_mx_workspace_size(const engram_hash_params *params,
   const int64_t ntok = desc->batch * desc->seq;
   const int32_t S = (params->max_ngram - 1) * params->heads;
   const int64_t out_dim = (int64_t)(desc->hc + 1) * desc->dim;
-  return align256((size_t)ntok * S * 8) + align256((size_t)ntok * S * ENGRAM_ROW_BYTES) +
-         align256((size_t)ntok * out_dim * 2) +
+  return align256((size_t)ntok * S * 8) + align256((size_t)ntok * S * ENGRAM_ROW_DIM_E4M3) +
+         align256((size_t)ntok * S * 8) + align256((size_t)ntok * out_dim * 2) +
          engram_project_mx_workspace_size(ntok, S, out_dim);
 }
 
@@ -670,8 +690,9 @@ int engram_forward_mx(const engram_hash_params *params, const engram_forward_des
 
   char *ws = (char *)workspace;
   int64_t *row_ids = (int64_t *)ws;
-  uint8_t *e_rows = (uint8_t *)(ws + align256((size_t)ntok * S * 8));
-  uint16_t *kv = (uint16_t *)((char *)e_rows + align256((size_t)ntok * S * ENGRAM_ROW_BYTES));
+  uint8_t *e_codes = (uint8_t *)(ws + align256((size_t)ntok * S * 8));
+  uint8_t *e_scales = e_codes + align256((size_t)ntok * S * ENGRAM_ROW_DIM_E4M3);
+  uint16_t *kv = (uint16_t *)(e_scales + align256((size_t)ntok * S * 8));
   char *gemm_ws = (char *)kv + align256((size_t)ntok * out_dim * 2);
   const size_t gemm_ws_bytes = workspace_bytes - (size_t)(gemm_ws - ws);
 
@@ -679,11 +700,11 @@ int engram_forward_mx(const engram_hash_params *params, const engram_forward_des
   hipError_t err = engram_launch_hash(a, params->token_map, ids, desc->batch, desc->seq,
                                       hist_in, hist_out, row_ids, stream);
   if (err != hipSuccess || ntok == 0) return hip_status(err);
-  err = engram_launch_gather_rows((const uint8_t *)table, desc->table_rows, row_ids, ntok * S,
-                                  e_rows, host, stream);
+  err = engram_launch_gather_mx((const uint8_t *)table, desc->table_rows, row_ids, ntok * S,
+                                e_codes, e_scales, host, stream);
   if (err != hipSuccess) return hip_status(err);
-  err = engram_launch_gemm_mx((const uint8_t *)w_codes, (const uint8_t *)w_scales, e_rows, S, kv,
-                              ntok, out_dim, gemm_ws, gemm_ws_bytes, stream);
+  err = engram_launch_gemm_mx((const uint8_t *)w_codes, (const uint8_t *)w_scales, e_codes,
+                              e_scales, S, kv, ntok, out_dim, gemm_ws, gemm_ws_bytes, stream);
   if (err != hipSuccess) return hip_status(err);
   err = engram_launch_gate(false, ids, params->raw_vocab, kv, q_w, k_w, h, gate_out, nullptr,
                            ntok, desc->hc, desc->dim, desc->eps, desc->gate_clamp,

@@ -162,6 +162,44 @@ __global__ __launch_bounds__(NT) void gather_rows_kernel(
   }
 }
 
+// The same rows split for the block-scaled FP8 projection: words 0-31 of row i
+// (its 256 codes) go to codes[i * 256 ..], word 32 (its 8 scales) to
+// scales[i * 8]. With the S rows of a token side by side, codes is the token's
+// K-long row of E4M3 inputs and scales its K/32 block scales.
+template <int NT, int U>
+__global__ __launch_bounds__(NT) void gather_mx_kernel(
+    const uint8_t *__restrict__ table, int64_t table_rows, const int64_t *__restrict__ row_ids,
+    int64_t n_ids, uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
+  const int64_t total = n_ids * kRowWords;
+  const int64_t threads = (int64_t)gridDim.x * NT;
+  for (int64_t g0 = (int64_t)blockIdx.x * NT + threadIdx.x; g0 < total; g0 += U * threads) {
+    uint2 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t g = g0 + u * threads;
+      v[u] = make_uint2(0u, 0u);
+      if (g < total) {
+        const int64_t i = g / kRowWords;
+        const int w = (int)(g - i * kRowWords);
+        const int64_t r = row_ids[i];
+        if (r >= 0 && r < table_rows)
+          v[u] = *reinterpret_cast<const uint2 *>(table + r * ENGRAM_ROW_BYTES + (int64_t)w * 8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t g = g0 + u * threads;
+      if (g < total) {
+        const int64_t i = g / kRowWords;
+        const int w = (int)(g - i * kRowWords);
+        uint8_t *dst = w < kRowWords - 1 ? codes + i * ENGRAM_ROW_DIM_E4M3 + (int64_t)w * 8
+                                         : scales + i * 8;
+        *reinterpret_cast<uint2 *>(dst) = v[u];
+      }
+    }
+  }
+}
+
 // Grid of the gathers from a host-resident table: one 1024-thread block per XCD
 // fills one CU each, so a fetch running beside the projection takes 8 of the
 // 256 CUs, while keeping about half a megabyte of reads in flight over the
@@ -184,6 +222,22 @@ hipError_t engram_launch_gather_rows(const uint8_t *table, int64_t table_rows,
   const int64_t blocks = (n_ids * kRowWords + kThreads - 1) / kThreads;
   hipLaunchKernelGGL((gather_rows_kernel<kThreads, 1>), dim3((unsigned)blocks), dim3(kThreads),
                      0, stream, table, table_rows, row_ids, n_ids, out);
+  return hipGetLastError();
+}
+
+hipError_t engram_launch_gather_mx(const uint8_t *table, int64_t table_rows,
+                                   const int64_t *row_ids, int64_t n_ids, uint8_t *codes,
+                                   uint8_t *scales, bool host_table, hipStream_t stream) {
+  if (n_ids <= 0) return hipSuccess;
+  if (host_table) {
+    hipLaunchKernelGGL((gather_mx_kernel<kHostThreads, kHostUnroll>), dim3(kHostBlocks),
+                       dim3(kHostThreads), 0, stream, table, table_rows, row_ids, n_ids, codes,
+                       scales);
+    return hipGetLastError();
+  }
+  const int64_t blocks = (n_ids * kRowWords + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL((gather_mx_kernel<kThreads, 1>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                     stream, table, table_rows, row_ids, n_ids, codes, scales);
   return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
 // Step 4 with the projection weight in block-scaled FP8: kv = e W on the
-// looked-up rows as they are stored.
+// looked-up rows' own codes and scales.
 //
 // Pages: "条件记忆：DeepSeek V4.1 Engram 如何用 O(1) 查表换掉一层计算" §2.3 (the
 // weight is block-FP8; the table holds fp8 e4m3 payloads with e8m0 block
@@ -7,9 +7,12 @@
 // value projections fused into one product).
 //
 // kv = e W with both operands in the table's block encoding: E4M3 values with one
-// E8M0 scale per 32 inputs. W is codes [N, K] plus scales [N, K/32]; e is the
-// looked-up rows themselves, [tokens, S, 264] (256 codes then 8 scales per
-// segment), so no dequantisation happens at all: v_mfma_scale_f32_32x32x64_f8f6f4
+// E8M0 scale per 32 inputs. W is codes [N, K] plus scales [N, K/32], and so is e:
+// the looked-up rows' codes [tokens, K] (the S rows of a token side by side) and
+// scales [tokens, K/32], split apart by the gather so that every 128-byte K
+// slice of an e row is line-aligned (a 264-byte row stride put each slice across
+// two cache lines and cost 7 % of the kernel). No dequantisation happens at
+// all: v_mfma_scale_f32_32x32x64_f8f6f4
 // multiplies E4M3 pairs exactly, applies both 2^(scale - 127) factors per 32-input
 // block and accumulates in fp32.
 //
@@ -39,12 +42,12 @@ namespace {
 struct MxOperands {
   const uint8_t *w_codes;    // [N, K]
   const uint8_t *w_scales;   // [N, K / 32]
-  const uint8_t *e_rows;     // [M, S, 264]
+  const uint8_t *e_codes;    // [M, K]
+  const uint8_t *e_scales;   // [M, K / 32]
   int segments;              // S; K = 256 S
 };
 
 constexpr int kMxBk = 128;            // inputs per K-step
-constexpr int kRowBytes = 264;
 
 struct MxLds {
   uint8_t w[2][BN * kMxBk];
@@ -77,7 +80,6 @@ __device__ __forceinline__ void wide_tile_mx(
     uint32_t *__restrict__ es0, uint32_t *__restrict__ es1) {
   const int K = op.segments * 256;
   const int KB = K / 32;                       // scale bytes per W row
-  const int RS = op.segments * kRowBytes;      // bytes per e row
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -88,10 +90,12 @@ __device__ __forceinline__ void wide_tile_mx(
   const __amdgpu_buffer_rsrc_t rsWs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t *>(op.w_scales + (int64_t)n0 * KB), 0, rows_w * KB, kBufferFlags);
   const __amdgpu_buffer_rsrc_t rsE = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t *>(op.e_rows + (int64_t)m0 * RS), 0, rows_e * RS, kBufferFlags);
+      const_cast<uint8_t *>(op.e_codes + (int64_t)m0 * K), 0, rows_e * K, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rsEs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(op.e_scales + (int64_t)m0 * KB), 0, rows_e * KB, kBufferFlags);
   // code chunk i of this thread: row (i % 8) * 32 + t / 8, 16-byte column t % 8
   const int g_row = tid >> 3, g_chunk = tid & 7;
-  const int ge_voff = g_row * RS + g_chunk * 16;
+  const int ge_voff = g_row * K + g_chunk * 16;
   const int s_off = g_row * kMxBk + ((g_chunk ^ (g_row & 7) ^ ((g_row >> 3) & 1)) << 4);
   const int frow = lane & 31, h = lane >> 5;
   const int fsw = (frow & 7) ^ ((frow >> 3) & 1);
@@ -118,8 +122,8 @@ __device__ __forceinline__ void wide_tile_mx(
 #define MX_WS(st) ((st) ? ws1 : ws0)
 #define MX_ES(st) ((st) ? es1 : es0)
 #define MX_WOFF(kt_) ((kt_) * kMxBk)
-#define MX_EOFF(kt_) (((kt_) >> 1) * kRowBytes + ((kt_) & 1) * kMxBk)
-#define MX_ESOFF(kt_) (((kt_) >> 1) * kRowBytes + 256 + ((kt_) & 1) * 4)
+#define MX_EOFF(kt_) ((kt_) * kMxBk)
+#define MX_ESOFF(kt_) ((kt_) * 4)
 // Half q of a step: q = 0 the W codes and scales, q = 1 the e codes and scales.
 // Direct loads of W: code chunk i (i < 8) or the scales (i = 8) of step kt_ into stage st.
 #define MX_DMAW1(kt_, st, i)                                                                  \
@@ -136,10 +140,10 @@ __device__ __forceinline__ void wide_tile_mx(
 #define MX_EPAIR(st, i, kt_)                                                                  \
   if ((i) < 8) {                                                                            \
     *reinterpret_cast<uint4 *>(&MX_E(st)[s_off + (i) * 32 * kMxBk]) = g[i];                 \
-    g[i] = load16(rsE, ge_voff, (i) * 32 * RS + MX_EOFF(kt_));                              \
+    g[i] = load16(rsE, ge_voff, (i) * 32 * K + MX_EOFF(kt_));                               \
   } else {                                                                                  \
     MX_ES(st)[tid] = ges;                                                                   \
-    ges = load4(rsE, tid * RS, MX_ESOFF(kt_));                                              \
+    ges = load4(rsEs, tid * KB, MX_ESOFF(kt_));                                             \
   }
 // W copies of a step are issued right after the previous barrier; the 9 e
 // reloads that follow them may stay in flight across the next barrier.
@@ -173,8 +177,8 @@ __device__ __forceinline__ void wide_tile_mx(
   __syncthreads();
   _Pragma("unroll") for (int i = 0; i < 9; ++i) { MX_DMAW1(ks, 0, i) }
   _Pragma("unroll") for (int i = 0; i < 8; ++i)
-    g[i] = load16(rsE, ge_voff, i * 32 * RS + MX_EOFF(ks));
-  ges = load4(rsE, tid * RS, MX_ESOFF(ks));
+    g[i] = load16(rsE, ge_voff, i * 32 * K + MX_EOFF(ks));
+  ges = load4(rsEs, tid * KB, MX_ESOFF(ks));
   _Pragma("unroll") for (int i = 0; i < 9; ++i) { MX_EPAIR(0, i, ks + 1) }
   _Pragma("unroll") for (int i = 0; i < 9; ++i) { MX_DMAW1(ks + 1, 1, i) }
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -329,11 +333,12 @@ void gemm_mx_streamk_kernel(MxOperands op, uint16_t *__restrict__ C, float *__re
 }  // namespace
 
 hipError_t engram_launch_gemm_mx(const uint8_t *w_codes, const uint8_t *w_scales,
-                                 const uint8_t *e_rows, int32_t segments, uint16_t *kv,
+                                 const uint8_t *e_codes, const uint8_t *e_scales,
+                                 int32_t segments, uint16_t *kv,
                                  int64_t m, int64_t n, void *workspace, size_t workspace_bytes,
                                  hipStream_t stream) {
   if (m <= 0 || n <= 0) return hipSuccess;
-  const MxOperands op{w_codes, w_scales, e_rows, segments};
+  const MxOperands op{w_codes, w_scales, e_codes, e_scales, segments};
   StreamK sk;
   hipError_t err = plan_streamk(m, n, (int64_t)segments * 256 / kMxBk, sk);
   if (err != hipSuccess) return err;

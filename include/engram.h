@@ -51,13 +51,13 @@
  * prefetch on a separate path, wait for its completion event, stall =
  * max(0, T_fetch - T_window); [P3] §五: the host link's bandwidth is the cost).
  * Every entry point that reads a table (engram_gather, engram_gather_rows,
- * engram_forward, engram_forward_conv, engram_forward_mx) accepts pinned host
- * memory (hipHostMalloc, or torch's pin_memory) as well as device memory: its
- * kernels then read the 264-byte rows over the host link themselves, straight
- * into HBM, with no staging copy on the host. A prefetch is engram_hash +
- * engram_gather (or engram_gather_rows) on a second stream, ordered before the
- * consuming engram_project (or engram_project_mx) by an event. A table pointer
- * the device cannot read (pageable host memory, an unknown address) is
+ * engram_gather_mx, engram_forward, engram_forward_conv, engram_forward_mx)
+ * accepts pinned host memory (hipHostMalloc, or torch's pin_memory) as well as
+ * device memory: its kernels then read the 264-byte rows over the host link
+ * themselves, straight into HBM, with no staging copy on the host. A prefetch is
+ * engram_hash + engram_gather (or engram_gather_mx) on a second stream, ordered
+ * before the consuming engram_project (or engram_project_mx) by an event. A table
+ * pointer the device cannot read (pageable host memory, an unknown address) is
  * rejected with ENGRAM_EINVAL before any launch.
  */
 #ifndef ENGRAM_H
@@ -283,9 +283,8 @@ int engram_gather(const void *table, int64_t table_rows, int32_t row_format,
                   hipStream_t stream);
 
 /*
- * Step 3 for the block-scaled FP8 projection: the looked-up rows, bytes
- * unchanged (256 E4M3 codes then 8 E8M0 scales each; [P4] "永不常驻的 I/O 设计"),
- * which engram_project_mx consumes without dequantisation. A row id outside
+ * Step 3 without dequantisation: the looked-up rows, bytes unchanged (256 E4M3
+ * codes then 8 E8M0 scales each; [P4] "永不常驻的 I/O 设计"). A row id outside
  * [0, table_rows) gives a zero row ([P3] §五).
  *   table    uint8 [table_rows, 264], 8-byte aligned, in device memory or in pinned
  *            host memory (see "Host-resident tables")
@@ -297,6 +296,20 @@ int engram_gather_rows(const void *table, int64_t table_rows, const int64_t *row
                        int64_t n_ids, void *out, hipStream_t stream);
 
 /*
+ * Step 3 for engram_project_mx: the looked-up rows split into their codes and
+ * their scales (bytes unchanged), so that the S rows of a token form one
+ * K = 256 S long row of E4M3 inputs with K/32 E8M0 block scales, the layout of
+ * the FP8 weight. A row id outside [0, table_rows) gives zero codes and scales.
+ *   table    as engram_gather_rows
+ *   row_ids  int64 [n_ids]
+ *   codes    uint8 [n_ids, 256], 16-byte aligned
+ *   scales   uint8 [n_ids, 8], 8-byte aligned
+ * Errors: ENGRAM_EINVAL, ENGRAM_ESHAPE, ENGRAM_EHIP.
+ */
+int engram_gather_mx(const void *table, int64_t table_rows, const int64_t *row_ids,
+                     int64_t n_ids, void *codes, void *scales, hipStream_t stream);
+
+/*
  * Step 4: kv = e W ([P1] "每条流一个 key 的设计沿用自原版": one 6144 x 25600
  * matrix; [P4] "消费": the weight is stored with the 6144 inputs innermost).
  *   e    [tokens, in_dim]       bf16 (act_f32 = 0) or float (act_f32 = 1)
@@ -305,12 +318,15 @@ int engram_gather_rows(const void *table, int64_t table_rows, const int64_t *row
  *                               nearest-even
  *   workspace, workspace_bytes
  *        NULL, or at least engram_project_workspace_size bytes, 256-byte
- *        aligned. With fewer 256 x 256 output tiles than the GPU has CUs
- *        (small token counts: decode) a bf16 call splits K over the CUs and
- *        keeps fp32 partial tiles there, summed afterwards in a fixed order
- *        (the result depends only on the shape and the CU count); with NULL it
- *        uses narrower tiles over the whole K instead. Contents need not be
- *        initialised and are clobbered.
+ *        aligned. A bf16 call of at most 256 tokens with 64-128 output columns
+ *        per CU and in_dim % 384 == 0 (decode) deals columns to the CUs and
+ *        needs none. Other calls with fewer 256 x 256 output tiles than the GPU
+ *        has CUs split K over the CUs and keep fp32 partial tiles here, summed
+ *        afterwards in a fixed order (the result depends only on the shape and
+ *        the CU count); with NULL they use narrower tiles over the whole K.
+ *        Every other path sums each output's K in one order, so its bits do
+ *        not depend on the token count. Contents need not be initialised and
+ *        are clobbered.
  * bf16 requires in_dim % 64 == 0 and out_dim % 8 == 0; fp32 requires in_dim % 4
  * == 0 and out_dim % 4 == 0.
  * Errors: ENGRAM_EINVAL, ENGRAM_ESHAPE, ENGRAM_EWORKSPACE (non-NULL and too
@@ -331,19 +347,21 @@ size_t engram_project_workspace_size(int64_t tokens, int64_t in_dim, int64_t out
  * into one dense FP8 matrix product). Reading: the weight uses the table's own
  * block encoding, E4M3 values with one E8M0 scale per 32 consecutive inputs.
  * kv[t, c] = sum_k e[t, k] W[c, k] with e[t, 256 j + i] = E4M3(row_j[i]) *
- * 2^(row_j[256 + i / 32] - 127) taken straight from the looked-up rows (exact
- * products, fp32 accumulation in gfx950's block-scaled FP8 MFMA), rounded once
- * to bf16 nearest-even.
- *   e_rows   uint8 [tokens, segments, 264]: engram_gather_rows output
+ * 2^(row_j[256 + i / 32] - 127) taken straight from the looked-up rows' codes
+ * and scales (exact products, fp32 accumulation in gfx950's block-scaled FP8
+ * MFMA), rounded once to bf16 nearest-even.
+ *   e_codes  uint8 [tokens, 256 segments], 16-byte aligned: engram_gather_mx codes
+ *   e_scales uint8 [tokens, 8 segments], 4-byte aligned: engram_gather_mx scales
  *   w_codes  uint8 [out_dim, 256 segments], 16-byte aligned
  *   w_scales uint8 [out_dim, 8 segments] (E8M0, bias 127), 4-byte aligned
  *   kv       bf16 [tokens, out_dim]; out_dim % 8 == 0
  *   workspace as for engram_project, sized by engram_project_mx_workspace_size
  * Errors: ENGRAM_EINVAL, ENGRAM_ESHAPE, ENGRAM_EWORKSPACE, ENGRAM_EHIP.
  */
-int engram_project_mx(const void *e_rows, int32_t segments, const void *w_codes,
-                      const void *w_scales, void *kv, int64_t tokens, int64_t out_dim,
-                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+int engram_project_mx(const void *e_codes, const void *e_scales, int32_t segments,
+                      const void *w_codes, const void *w_scales, void *kv, int64_t tokens,
+                      int64_t out_dim, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream);
 
 /* [host] Bytes of workspace engram_project_mx uses (0 if none, on bad arguments
  * or on a HIP error). */
@@ -388,10 +406,10 @@ int engram_forward(const engram_hash_params *params, const engram_forward_desc *
 
 /*
  * The whole layer with the block-scaled FP8 weight: engram_hash,
- * engram_gather_rows, engram_project_mx and engram_gate in one call. Arguments
+ * engram_gather_mx, engram_project_mx and engram_gate in one call. Arguments
  * as for engram_forward, except the weight (w_codes, w_scales as for
  * engram_project_mx); desc->row_format must be ENGRAM_ROW_E4M3_E8M0_264 and h
- * is bf16. The workspace holds row ids, the looked-up rows, kv and the
+ * is bf16. The workspace holds row ids, the rows' codes and scales, kv and the
  * projection's workspace.
  * Errors: as engram_forward.
  */

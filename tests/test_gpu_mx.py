@@ -1,5 +1,6 @@
-"""Parity of the block-scaled FP8 path (engram_gather_rows, engram_project_mx,
-engram_forward_mx) with the CPU oracle. The looked-up rows match bit for bit;
+"""Parity of the block-scaled FP8 path (engram_gather_rows, engram_gather_mx,
+engram_project_mx, engram_forward_mx) with the CPU oracle. The looked-up rows
+and their split codes and scales match bit for bit;
 the projection stays within the FP8 MFMA's measured precision bound and is
 exact where every output has a single product; gates and streams follow the
 same tolerance as the bf16 path."""
@@ -41,6 +42,37 @@ def test_gather_rows_bit_exact():
     assert np.array_equal(out.cpu().numpy(), exp)
 
 
+def test_gather_mx_splits_rows_bit_exact():
+    """codes[i] = the row's 256 E4M3 bytes, scales[i] = its 8 E8M0 bytes, zeros
+    for ids outside the table; the same bits from a pinned host copy; a pageable
+    table is rejected before any launch."""
+    say("gather_mx: 5003 ids incl. out-of-range, device and pinned host table")
+    rng = np.random.default_rng(32)
+    R = 70_001
+    table = torch.from_numpy(gen.table_rows(6, np.arange(R))).to(DEV)
+    host = torch.empty(table.shape, dtype=table.dtype, pin_memory=True)
+    host.copy_(table)
+    ids = rng.integers(-5, R + 5, 5003).astype(np.int64)
+    ids[:3] = [0, R - 1, R]
+    ids_d = to_device(ids)
+    exp = O.gather_rows(lambda r: gen.table_rows(6, r), ids.reshape(-1, 1), R).reshape(-1, 264)
+    for src in (table, host):
+        codes = torch.full((ids.size, 256), 0xAB, dtype=torch.uint8, device=DEV)
+        scales = torch.full((ids.size, 8), 0xCD, dtype=torch.uint8, device=DEV)
+        E.engram_gather_mx(src, R, ids_d, ids.size, codes, scales)
+        torch.cuda.synchronize()
+        assert np.array_equal(codes.cpu().numpy(), exp[:, :256])
+        assert np.array_equal(scales.cpu().numpy(), exp[:, 256:])
+    pageable = torch.zeros((64, 264), dtype=torch.uint8)
+    codes = torch.full((8, 256), 5, dtype=torch.uint8, device=DEV)
+    scales = torch.full((8, 8), 5, dtype=torch.uint8, device=DEV)
+    with pytest.raises(E.EngramError) as ex:
+        E.engram_gather_mx(pageable, 64, ids_d, 8, codes, scales)
+    assert ex.value.status == E.EINVAL
+    torch.cuda.synchronize()
+    assert bool((codes == 5).all()) and bool((scales == 5).all())
+
+
 def _mx_case(M, N, S, seed):
     rng = np.random.default_rng(seed)
     rows = _rows_of(seed, rng.integers(0, 10 ** 9, M * S)).reshape(M, S, 264)
@@ -54,7 +86,10 @@ def _project_mx(rows, codes, scales, M, N, S, with_ws):
     n = E.engram_project_mx_workspace_size(M, S, N) if with_ws else 0
     ws = torch.empty(max(n, 256), dtype=torch.uint8, device=DEV) if n else None
     kv = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
-    E.engram_project_mx(to_device(rows), S, to_device(codes), to_device(scales), kv, M, N, ws, n)
+    e_codes = to_device(np.ascontiguousarray(rows[:, :, :256]).reshape(M, S * 256))
+    e_scales = to_device(np.ascontiguousarray(rows[:, :, 256:]).reshape(M, S * 8))
+    E.engram_project_mx(e_codes, e_scales, S, to_device(codes), to_device(scales), kv, M, N,
+                        ws, n)
     torch.cuda.synchronize()
     return O.bf16_bits_to_f64(bf16_bits(kv))
 
