@@ -111,15 +111,35 @@ def cpu_baseline(gw, target_s: float = 10.0, max_tokens: int = 8192):
                          clamp=w.gate_clamp, bf16=True)
         return time.perf_counter() - t0
 
-    n = 64
-    dt = run(n)
-    while dt < target_s / 4 and n < max_tokens:
-        n = min(max_tokens, int(n * max(2.0, min(16.0, target_s / max(dt, 1e-3)))))
+    def grow(target, cap):
+        n = 64
         dt = run(n)
+        while dt < target / 4 and n < cap:
+            n = min(cap, int(n * max(2.0, min(16.0, target / max(dt, 1e-3)))))
+            dt = run(n)
+        return n, dt
+
+    n, dt = grow(target_s, max_tokens)
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            n1, dt1 = grow(target_s / 2, max_tokens // 8)
+        single = {"value": round(n1 / dt1, 3), "unit": "tokens/s", "cores": 1,
+                  "sample": f"first {n1} tokens, {dt1:.2f} s with BLAS limited to one thread"}
+    except Exception as exc:                        # threadpoolctl missing or refused
+        log(f"single-thread oracle run skipped: {exc}")
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {n} tokens of sequence 0 of the same prefill workload, all five "
                       f"steps in fp64 numpy, table rows pre-read into host RAM; {dt:.2f} s "
-                      f"on {os.cpu_count()} host CPUs (BLAS threads {cores})"}
+                      f"on {os.cpu_count()} host CPUs (BLAS threads {cores})",
+            "cpu_model": model, "single_thread": single}
 
 
 def main():
@@ -250,6 +270,10 @@ def main():
                       "project": round(stage_ms[2], 4), "gate": round(stage_ms[3], 4)},
         "engram_forward_ms": round(forward_ms, 4),
     }
+    detail, hash_steady = gather_detail(gw, rows, e, max(args.steps // 2, 5))
+    out["gather"].update(detail)
+    out["gather"]["frac_of_torch_copy"] = round(gather_gbps / detail["torch_copy_GBps"], 4)
+    out["hash_steady"] = hash_steady
     out["short_conv"] = conv_prefill_bench(gw, rows, e, kv, gates, args.steps, args.warmup)
     out["host_tier"] = host_tier_bench(gw, rows, e, kv, gates, args.steps, args.warmup)
     out["hash_layers"] = hash_layers_bench(max(args.steps, 20))
@@ -426,6 +450,70 @@ def host_tier_bench(gw, rows, e, kv, gates, steps: int, warmup: int):
             "fetch_dequant_ms": round(deq_ms, 4),
             "fetch_dequant_rows_GBps": round(row_bytes / (deq_ms * 1e-3) / 1e9, 1),
             "decode_fetch_256_tokens_us": round(dec_ms * 1e3, 1)}
+
+
+def gather_detail(gw, rows, e, reps: int):
+    """Beside the warm (back-to-back) gather: torch's device-to-device copy rate, the
+    same gather with the L2s and the 256 MB Infinity Cache flushed before every
+    rep by writing a 1 GiB scratch buffer, and engram_hash over 32 x the prefill
+    ids in one call (the steady-state hash rate, free of launch latency)."""
+    import statistics
+    import torch
+    import hashed_gram_conditional_amd as E
+
+    w = gw.w
+    T, S = w.tokens, w.segments
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed_once(fn):
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    copy_ms = statistics.median(timed_once(lambda: dst.copy_(src)) for _ in range(5))
+    copy_gbps = 2 * n / (copy_ms * 1e-3) / 1e9
+    del src
+    cold = []
+    for _ in range(reps):
+        dst.fill_(2)
+        cold.append(timed_once(lambda: E.engram_gather(gw.table, gw.rows, gw.row_format,
+                                                        w.row_dim, rows, T * S, e)))
+    del dst
+    cold_ms = statistics.median(cold)
+    cold_gbps = GATHER_BYTES_PER_TOKEN * T / (cold_ms * 1e-3) / 1e9
+
+    ids32 = gw.ids.repeat(32, 1).contiguous()
+    B32 = ids32.shape[0]
+    rows32 = torch.empty((B32 * w.seq, S), dtype=torch.int64, device="cuda")
+    hash32 = lambda: E.engram_hash(gw.params, ids32, B32, w.seq, None, None, rows32)
+    for _ in range(3):
+        hash32()
+    torch.cuda.synchronize()
+    hash_ms = statistics.median(timed_once(hash32) for _ in range(max(reps, 10)))
+    tokens = B32 * w.seq
+    hash_bytes = 4 + 8 * S
+    del ids32, rows32
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return ({"torch_copy_GBps": round(copy_gbps, 1),
+             "torch_copy": "tensor.copy_ of 1 GiB on the device: read + write bytes over the median "
+                           "of 5 (a reference rate, not the HBM peak)",
+             "cold": {"ms": round(cold_ms, 4), "achieved": round(cold_gbps, 1),
+                      "frac": round(cold_gbps / HBM_PEAK_GBPS, 4),
+                      "flush": "1 GiB scratch written before each rep"}},
+            {"workload": f"engram_hash over 32 x the prefill ids ({B32} x {w.seq} = {tokens} "
+                         f"tokens) in one call",
+             "us": round(hash_ms * 1e3, 1), "tokens_per_s": round(tokens / (hash_ms * 1e-3), 1),
+             "bytes_per_token": hash_bytes,
+             "achieved_GBps": round(hash_bytes * tokens / (hash_ms * 1e-3) / 1e9, 1)})
 
 
 def fp8_prefill_bench(gw, steps: int, warmup: int):
