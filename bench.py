@@ -129,6 +129,26 @@ def cpu_baseline(gw, target_s: float = 10.0, max_tokens: int = 8192):
                   "sample": f"first {n1} tokens, {dt1:.2f} s with BLAS limited to one thread"}
     except Exception as exc:                        # threadpoolctl missing or refused
         log(f"single-thread oracle run skipped: {exc}")
+    # the hash and gather stages alone: the hash over every prefill token, the
+    # gather (and dequantisation) over the rows of the first 2048 tokens
+    ids_all = np.ascontiguousarray(gw.ids_np)
+    t0 = time.perf_counter()
+    rid_all, _ = O.hash_rows(ids_all, gw.token_map_np, w.compressed_vocab, gw.pad, gw.mult,
+                             primes, offs, w.max_ngram, w.heads)
+    dt_hash = time.perf_counter() - t0
+    n_g = min(2048, rid_all.shape[0])
+    sub = rid_all[:n_g]
+    need = np.unique(sub)
+    host_rows = gen.table_rows(w.table_seed, need)
+    t0 = time.perf_counter()
+    O.gather_e4m3(lambda r: host_rows[np.searchsorted(need, r)], sub, R)
+    dt_gather = time.perf_counter() - t0
+    stages = {"hash": {"tokens_per_s": round(rid_all.shape[0] / dt_hash, 1),
+                       "sample": f"all {rid_all.shape[0]} prefill tokens, {dt_hash:.3f} s"},
+              "gather": {"tokens_per_s": round(n_g / dt_gather, 1),
+                         "GBps": round(n_g * GATHER_BYTES_PER_TOKEN / dt_gather / 1e9, 4),
+                         "sample": f"rows of the first {n_g} tokens, pre-read into host RAM, "
+                                   f"{dt_gather:.2f} s"}}
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -139,7 +159,7 @@ def cpu_baseline(gw, target_s: float = 10.0, max_tokens: int = 8192):
             "sample": f"first {n} tokens of sequence 0 of the same prefill workload, all five "
                       f"steps in fp64 numpy, table rows pre-read into host RAM; {dt:.2f} s "
                       f"on {os.cpu_count()} host CPUs (BLAS threads {cores})",
-            "cpu_model": model, "single_thread": single}
+            "cpu_model": model, "single_thread": single, "stages": stages}
 
 
 def main():
