@@ -39,6 +39,9 @@ __device__ __forceinline__ float warp_sum(float v) {
   return v;
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 // Eight consecutive elements of a bf16 (F32 = false) or fp32 row, addressed by
 // chunk index: one 16-byte or two 16-byte accesses.
 template <bool F32>
@@ -65,6 +68,16 @@ struct Chunk8<false> {
     o.w = pack_bf16x2(f[6], f[7]);
     reinterpret_cast<uint4 *>(p)[i] = o;
   }
+  // the same accesses with the nontemporal hint, for data used once
+  __device__ __forceinline__ void load_nt(const void *p, int64_t i) {
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p) + i);
+    v = make_uint4(t.x, t.y, t.z, t.w);
+  }
+  __device__ __forceinline__ static void store_nt(void *p, int64_t i, const float f[8]) {
+    const u32x4 o = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                     pack_bf16x2(f[6], f[7])};
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(p) + i);
+  }
 };
 template <>
 struct Chunk8<true> {
@@ -89,6 +102,17 @@ struct Chunk8<true> {
   __device__ __forceinline__ static void store(void *p, int64_t i, const float f[8]) {
     reinterpret_cast<float4 *>(p)[2 * i] = make_float4(f[0], f[1], f[2], f[3]);
     reinterpret_cast<float4 *>(p)[2 * i + 1] = make_float4(f[4], f[5], f[6], f[7]);
+  }
+  __device__ __forceinline__ void load_nt(const void *p, int64_t i) {
+    const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p) + 2 * i);
+    const f32x4 y = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p) + 2 * i + 1);
+    a = make_float4(x.x, x.y, x.z, x.w);
+    b = make_float4(y.x, y.y, y.z, y.w);
+  }
+  __device__ __forceinline__ static void store_nt(void *p, int64_t i, const float f[8]) {
+    const f32x4 x = {f[0], f[1], f[2], f[3]}, y = {f[4], f[5], f[6], f[7]};
+    __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>(p) + 2 * i);
+    __builtin_nontemporal_store(y, reinterpret_cast<f32x4 *>(p) + 2 * i + 1);
   }
 };
 

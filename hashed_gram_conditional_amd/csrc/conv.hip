@@ -127,11 +127,11 @@ __global__ __launch_bounds__(kThreads) void short_conv_kernel(
     }
     const int64_t hi = (t * hc + m) * (int64_t)cps + ci;
     engram::Chunk8<F32> hh;
-    hh.load(h, hi);
+    hh.load_nt(h, hi);
     float o[kChunk];
 #pragma unroll
     for (int e = 0; e < kChunk; ++e) o[e] = hh[e] + (silu(u[e]) + vt[e]);
-    engram::Chunk8<F32>::store(h, hi, o);
+    engram::Chunk8<F32>::store_nt(h, hi, o);
   }
 }
 
@@ -261,12 +261,12 @@ __global__ __launch_bounds__(kThreads) void short_conv_window_kernel(
     }
     const int64_t hi = h_base + i * h_step;
     engram::Chunk8<false> hh;
-    hh.load(h, hi);
+    hh.load_nt(h, hi);
     const float a_t = s_stat[i + L][m];
     float o[kChunk];
 #pragma unroll
     for (int e = 0; e < kChunk; ++e) o[e] = hh[e] + fmaf(a_t, win[i + L][e], silu(u[e]));
-    engram::Chunk8<false>::store(h, hi, o);
+    engram::Chunk8<false>::store_nt(h, hi, o);
   }
 }
 
