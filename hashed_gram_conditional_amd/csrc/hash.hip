@@ -8,12 +8,13 @@
 // (3-token hash state); "条件记忆：DeepSeek V4.1 Engram 如何用 O(1) 查表换掉一层计算",
 // §4.4 (decode fuses the hash with the history commit).
 //
-// Layout: one block of 256 threads owns 256 consecutive flat tokens. Phase 1:
-// one thread per token builds the look-back cells once, then each layer's N-1
-// mixes (its own multipliers) into LDS. Phase 2: for each layer the block
-// writes its 256 x S int64 row ids as one contiguous, fully coalesced span of
-// that layer's [tokens, S] slice, each thread reducing mixes modulo the
-// layer's primes. Several layers in one pass follow "条件记忆：DeepSeek V4.1
+// Layout: one block of 256 threads owns TOK consecutive flat tokens (256, or
+// 64 for calls of at most 4096 tokens, such as decode steps, so that the work
+// spreads over more CUs). Phase 1: one thread per token builds the look-back
+// cells once, then each layer's N-1 mixes (its own multipliers) into LDS.
+// Phase 2: for each layer the block writes its TOK x S int64 row ids as one
+// contiguous, fully coalesced span of that layer's [tokens, S] slice, all 256
+// threads reducing mixes modulo the layer's primes. Several layers in one pass follow "条件记忆：DeepSeek V4.1
 // Engram 如何用 O(1) 查表换掉一层计算" §2.4 (every layer's ids are known before
 // the layer loop) and "DeepSeek-V4.1 模型结构（5）：记忆，Engram", "一层只有一张表"
 // (each layer has its own primes and multipliers).
@@ -28,7 +29,7 @@
 
 namespace {
 
-constexpr int kTok = 256;
+constexpr int kThreads = 256;
 
 __device__ __forceinline__ int32_t cell_value(const EngramHashArgs &a,
                                               const int32_t *__restrict__ token_map,
@@ -50,14 +51,14 @@ __device__ __forceinline__ int32_t cell_value(const EngramHashArgs &a,
   return a.pad_id;
 }
 
-template <int L>
-__global__ __launch_bounds__(kTok) void hash_kernel(
+template <int L, int TOK>
+__global__ __launch_bounds__(kThreads) void hash_kernel(
     EngramHashArgs a, const int32_t *__restrict__ token_map, const int32_t *__restrict__ ids,
     int64_t batch, int64_t seq, const int32_t *hist_in, int32_t *hist_out,
     int64_t *__restrict__ row_ids, int commit_history) {
   constexpr int kSeg = L * ENGRAM_MAX_SEGMENTS < ENGRAM_MAX_TOTAL_SEGMENTS
                            ? L * ENGRAM_MAX_SEGMENTS : ENGRAM_MAX_TOTAL_SEGMENTS;
-  __shared__ uint64_t s_mix[L][ENGRAM_MAX_NGRAM - 1][kTok];
+  __shared__ uint64_t s_mix[L][ENGRAM_MAX_NGRAM - 1][TOK];
   __shared__ uint64_t s_recip[kSeg];
   __shared__ int64_t s_off[kSeg];
   __shared__ uint32_t s_prime[kSeg];
@@ -66,16 +67,16 @@ __global__ __launch_bounds__(kTok) void hash_kernel(
   const int S = a.segments;
   const int N = a.max_ngram;
   const int H = N - 1;
-  for (int j = tid; j < L * S; j += kTok) {
+  for (int j = tid; j < L * S; j += kThreads) {
     s_prime[j] = a.prime[j];
     s_recip[j] = a.recip[j];
     s_off[j] = a.offset[j];
   }
 
   const int64_t ntok = batch * seq;
-  const int64_t tok0 = (int64_t)blockIdx.x * kTok;
+  const int64_t tok0 = (int64_t)blockIdx.x * TOK;
   const int64_t g = tok0 + tid;
-  if (g < ntok) {
+  if (tid < TOK && g < ntok) {
     const int64_t b = g / seq;
     const int64_t t = g - b * seq;
     const int32_t *row = ids + b * seq;
@@ -116,12 +117,12 @@ __global__ __launch_bounds__(kTok) void hash_kernel(
   __syncthreads();
 
   const int64_t left = ntok - tok0;
-  const int ntb = left < kTok ? (int)left : kTok;
+  const int ntb = left < TOK ? (int)left : TOK;
   const int total = ntb * S;
 #pragma unroll
   for (int l = 0; l < L; ++l) {
     int64_t *out = row_ids + (int64_t)l * ntok * S + tok0 * S;
-    for (int o = tid; o < total; o += kTok) {
+    for (int o = tid; o < total; o += kThreads) {
       const int lt = o / S;
       const int j = o - lt * S;
       const int js = l * S + j;
@@ -162,28 +163,28 @@ hipError_t engram_launch_hash(const EngramHashArgs &a, const int32_t *token_map,
   const int64_t ntok = batch * seq;
   const bool fused = hist_out != nullptr && seq == 1;
   if (ntok > 0) {
-    const dim3 grid((unsigned)((ntok + kTok - 1) / kTok));
+    const bool small = ntok <= 4096;
+    const int tok = small ? 64 : 256;
+    const dim3 grid((unsigned)((ntok + tok - 1) / tok));
     const int commit = fused ? 1 : 0;
+#define ENGRAM_HASH_CASE(Lc)                                                                  \
+  case Lc:                                                                                  \
+    if (small)                                                                              \
+      hipLaunchKernelGGL((hash_kernel<Lc, 64>), grid, dim3(kThreads), 0, stream, a, token_map, \
+                         ids, batch, seq, hist_in, hist_out, row_ids, commit);              \
+    else                                                                                    \
+      hipLaunchKernelGGL((hash_kernel<Lc, 256>), grid, dim3(kThreads), 0, stream, a,        \
+                         token_map, ids, batch, seq, hist_in, hist_out, row_ids, commit);   \
+    break;
     switch (a.layers) {
-      case 1:
-        hipLaunchKernelGGL(hash_kernel<1>, grid, dim3(kTok), 0, stream, a, token_map, ids, batch,
-                           seq, hist_in, hist_out, row_ids, commit);
-        break;
-      case 2:
-        hipLaunchKernelGGL(hash_kernel<2>, grid, dim3(kTok), 0, stream, a, token_map, ids, batch,
-                           seq, hist_in, hist_out, row_ids, commit);
-        break;
-      case 3:
-        hipLaunchKernelGGL(hash_kernel<3>, grid, dim3(kTok), 0, stream, a, token_map, ids, batch,
-                           seq, hist_in, hist_out, row_ids, commit);
-        break;
-      case 4:
-        hipLaunchKernelGGL(hash_kernel<4>, grid, dim3(kTok), 0, stream, a, token_map, ids, batch,
-                           seq, hist_in, hist_out, row_ids, commit);
-        break;
+      ENGRAM_HASH_CASE(1)
+      ENGRAM_HASH_CASE(2)
+      ENGRAM_HASH_CASE(3)
+      ENGRAM_HASH_CASE(4)
       default:
         return hipErrorInvalidValue;
     }
+#undef ENGRAM_HASH_CASE
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
