@@ -108,6 +108,21 @@ def test_hash_chunks_equal_one_shot(splits):
     assert np.array_equal(hist.cpu().numpy(), exp_hist)
 
 
+@pytest.mark.parametrize("B,T", [(1, 4096), (1, 4097), (64, 64), (65, 64), (3, 1500), (200, 1)])
+def test_hash_block_size_switch(B, T):
+    """Calls of at most 4096 tokens put 64 tokens on each block, larger calls
+    256: both sides of the switch give the oracle's ids and history."""
+    say(f"hash block-size switch: B={B} T={T}")
+    gw = GpuWorkload(C1, table=False, dense=False)
+    ids = np.ascontiguousarray(gw.ids_np.reshape(-1)[:B * T].reshape(B, T))
+    ids[0, T // 2] = -1
+    exp, exp_hist = oracle_rows(gw, ids=ids, use_hist=False)
+    hout = torch.full((B, 3), -9, dtype=torch.int32, device=DEV)
+    got = _gpu_rows(gw, ids=to_device(ids), batch=B, seq=T, hist_out=hout)
+    assert np.array_equal(got, exp)
+    assert np.array_equal(hout.cpu().numpy(), exp_hist)
+
+
 def test_hash_edge_cases():
     gw = GpuWorkload(C0, table=False, dense=False)
     V = C0.raw_vocab
