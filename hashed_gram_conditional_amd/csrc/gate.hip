@@ -18,7 +18,10 @@
 // need only its own h and k, so after one barrier its gate is known and its h,
 // still in registers, is updated and stored before the next stream is read. h
 // is read from HBM once (updating all streams after all reductions re-read it,
-// and the L2 had often dropped it by then). All arithmetic is fp32.
+// and the L2 had often dropped it by then). All arithmetic is fp32. With few
+// tokens (up to 4 streams, 2 chunks per thread) a token's whole h and k are
+// loaded at once and the streams share one barrier: the same arithmetic, one
+// memory round trip per token instead of one per stream.
 //
 // With a stats buffer the kernel is the first half of the short-convolution
 // variant: it stores each token's gates and the mean square of its value row
@@ -30,6 +33,7 @@ namespace {
 constexpr int kMaxThreads = 512;
 constexpr int kMaxHc = 8;
 constexpr int kChunk = 8;        // elements per chunk
+constexpr int kAllStreams = 4;   // streams held at once by the few-token variant
 
 template <bool F32>
 using Chunk = engram::Chunk8<F32>;
@@ -37,7 +41,7 @@ using Chunk = engram::Chunk8<F32>;
 // Every byte the gate touches is used once, so its loads and stores carry the
 // nontemporal hint (5 % faster at 32768 tokens than cached accesses).
 
-template <bool F32, int CPT>
+template <bool F32, int CPT, bool AS>
 __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
     const int32_t *__restrict__ ids, int32_t raw_vocab, const void *__restrict__ kv,
     const float *__restrict__ q_w, const float *__restrict__ k_w, void *__restrict__ h,
@@ -84,21 +88,28 @@ __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
     if (lane == 0) red[wave][kMaxHc][0] = svv;
   }
 
-  // Stream by stream: the gate of stream m depends on its own h and k only, so
-  // its h is reduced, gated and updated from registers before the next stream
-  // is read; h crosses HBM once in each direction.
-#pragma unroll
-  for (int m = 0; m < kMaxHc; ++m) {
-    if (m >= hc) break;
-    Chunk<F32> hh[CPT];
-    float shh = 0.f, skk = 0.f, shk = 0.f;
+  // The gate of stream m from its three block-wide sums.
+  auto gate_of = [&](int m) -> float {
+    float a = 0.f, b = 0.f, c2 = 0.f;
+    for (int w = 0; w < nwaves; ++w) {
+      a += red[w][m][0];
+      b += red[w][m][1];
+      c2 += red[w][m][2];
+    }
+    const float rh = 1.0f / sqrtf(a * inv_d + eps);
+    const float rk = 1.0f / sqrtf(b * inv_d + eps);
+    const float sc = c2 * rh * rk * inv_sqrt_d;
+    const float z = plain ? sc : copysignf(sqrtf(fmaxf(fabsf(sc), clamp)), sc);
+    return 1.0f / (1.0f + expf(-z));
+  };
+  // Partial sums of stream m over this thread's chunks: sum h^2, sum k^2, sum h q_w k_w k.
+  auto partial = [&](int m, const Chunk<F32> (&hm)[CPT], const Chunk<F32> (&km)[CPT], float &shh,
+                     float &skk, float &shk) {
+    shh = skk = shk = 0.f;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int ci = tid + c * nthreads;
       if (ci < cps) {
-        Chunk<F32> kc;
-        hh[c].load_nt(h, h_row + (int64_t)m * cps + ci);
-        kc.load_nt(kv, kv_row + (int64_t)m * cps + ci);
         const float4 *qp = reinterpret_cast<const float4 *>(q_w + (int64_t)m * dim) + 2 * ci;
         const float4 *kp = reinterpret_cast<const float4 *>(k_w + (int64_t)m * dim) + 2 * ci;
         const float4 q0 = qp[0], q1 = qp[1], k0 = kp[0], k1 = kp[1];
@@ -106,8 +117,8 @@ __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
                             q1.x * k1.x, q1.y * k1.y, q1.z * k1.z, q1.w * k1.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float he = hh[c][e];
-          const float ke = kc[e];
+          const float he = hm[c][e];
+          const float ke = km[c][e];
           shh = fmaf(he, he, shh);
           skk = fmaf(ke, ke, skk);
           shk = fmaf(he * w[e], ke, shk);
@@ -122,31 +133,122 @@ __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
       red[wave][m][1] = skk;
       red[wave][m][2] = shk;
     }
+  };
+  auto update = [&](int m, const Chunk<F32> (&hm)[CPT], float alpha) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ci = tid + c * nthreads;
+      if (ci < cps) {
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = fmaf(alpha, vv[c][e], hm[c][e]);
+        Chunk<F32>::store_nt(h, h_row + (int64_t)m * cps + ci, o);
+      }
+    }
+  };
+
+  if constexpr (AS) {
+    // Few tokens (decode): every stream's h and k are loaded at once and the
+    // streams share one barrier, so a token costs one memory round trip
+    // instead of one per stream.
+    Chunk<F32> hh[kAllStreams][CPT], kk[kAllStreams][CPT];
+#pragma unroll
+    for (int m = 0; m < kAllStreams; ++m) {
+      if (m < hc) {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+          const int ci = tid + c * nthreads;
+          if (ci < cps) {
+            hh[m][c].load_nt(h, h_row + (int64_t)m * cps + ci);
+            kk[m][c].load_nt(kv, kv_row + (int64_t)m * cps + ci);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < kAllStreams; ++m) {
+      if (m < hc) {
+        float shh, skk, shk;
+        partial(m, hh[m], kk[m], shh, skk, shk);
+      }
+    }
     __syncthreads();
-    float a = 0.f, b = 0.f, c2 = 0.f;
-    for (int w = 0; w < nwaves; ++w) {
-      a += red[w][m][0];
-      b += red[w][m][1];
-      c2 += red[w][m][2];
+#pragma unroll
+    for (int m = 0; m < kAllStreams; ++m) {
+      if (m < hc) {
+        const float alpha = gate_of(m);
+        if (tid == 0) {
+          if (gate_out != nullptr) gate_out[t * hc + m] = alpha;
+          if (stats != nullptr) stats[t * (hc + 1) + m] = alpha;
+        }
+        if (stats == nullptr) update(m, hh[m], alpha);
+      }
     }
-    const float rh = 1.0f / sqrtf(a * inv_d + eps);
-    const float rk = 1.0f / sqrtf(b * inv_d + eps);
-    const float sc = c2 * rh * rk * inv_sqrt_d;
-    const float z = plain ? sc : copysignf(sqrtf(fmaxf(fabsf(sc), clamp)), sc);
-    const float alpha = 1.0f / (1.0f + expf(-z));
-    if (tid == 0) {
-      if (gate_out != nullptr) gate_out[t * hc + m] = alpha;
-      if (stats != nullptr) stats[t * (hc + 1) + m] = alpha;
-    }
-    if (stats == nullptr) {
+  } else {
+    // Stream by stream: the gate of stream m depends on its own h and k only, so
+    // its h is reduced, gated and updated from registers before the next stream
+    // is read; h crosses HBM once in each direction.
+#pragma unroll
+    for (int m = 0; m < kMaxHc; ++m) {
+      if (m >= hc) break;
+      Chunk<F32> hh[CPT];
+      float shh = 0.f, skk = 0.f, shk = 0.f;
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         const int ci = tid + c * nthreads;
         if (ci < cps) {
-          float o[8];
+          Chunk<F32> kc;
+          hh[c].load_nt(h, h_row + (int64_t)m * cps + ci);
+          kc.load_nt(kv, kv_row + (int64_t)m * cps + ci);
+          const float4 *qp = reinterpret_cast<const float4 *>(q_w + (int64_t)m * dim) + 2 * ci;
+          const float4 *kp = reinterpret_cast<const float4 *>(k_w + (int64_t)m * dim) + 2 * ci;
+          const float4 q0 = qp[0], q1 = qp[1], k0 = kp[0], k1 = kp[1];
+          const float w[8] = {q0.x * k0.x, q0.y * k0.y, q0.z * k0.z, q0.w * k0.w,
+                              q1.x * k1.x, q1.y * k1.y, q1.z * k1.z, q1.w * k1.w};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = fmaf(alpha, vv[c][e], hh[c][e]);
-          Chunk<F32>::store_nt(h, h_row + (int64_t)m * cps + ci, o);
+          for (int e = 0; e < 8; ++e) {
+            const float he = hh[c][e];
+            const float ke = kc[e];
+            shh = fmaf(he, he, shh);
+            skk = fmaf(ke, ke, skk);
+            shk = fmaf(he * w[e], ke, shk);
+          }
+        }
+      }
+      shh = engram::warp_sum(shh);
+      skk = engram::warp_sum(skk);
+      shk = engram::warp_sum(shk);
+      if (lane == 0) {
+        red[wave][m][0] = shh;
+        red[wave][m][1] = skk;
+        red[wave][m][2] = shk;
+      }
+      __syncthreads();
+      float a = 0.f, b = 0.f, c2 = 0.f;
+      for (int w = 0; w < nwaves; ++w) {
+        a += red[w][m][0];
+        b += red[w][m][1];
+        c2 += red[w][m][2];
+      }
+      const float rh = 1.0f / sqrtf(a * inv_d + eps);
+      const float rk = 1.0f / sqrtf(b * inv_d + eps);
+      const float sc = c2 * rh * rk * inv_sqrt_d;
+      const float z = plain ? sc : copysignf(sqrtf(fmaxf(fabsf(sc), clamp)), sc);
+      const float alpha = 1.0f / (1.0f + expf(-z));
+      if (tid == 0) {
+        if (gate_out != nullptr) gate_out[t * hc + m] = alpha;
+        if (stats != nullptr) stats[t * (hc + 1) + m] = alpha;
+      }
+      if (stats == nullptr) {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+          const int ci = tid + c * nthreads;
+          if (ci < cps) {
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = fmaf(alpha, vv[c][e], hh[c][e]);
+            Chunk<F32>::store_nt(h, h_row + (int64_t)m * cps + ci, o);
+          }
         }
       }
     }
@@ -160,25 +262,31 @@ __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
 }
 
 template <bool F32>
-hipError_t launch(int cpt, int threads, const int32_t *ids, int32_t raw_vocab, const void *kv,
-                  const float *q_w, const float *k_w, void *h, float *gate_out, float *stats,
-                  int64_t tokens, int hc, int dim, float eps, float clamp, int plain,
-                  hipStream_t stream) {
-#define ENGRAM_GATE_CASE(N)                                                                 \
-  case N:                                                                                   \
-    hipLaunchKernelGGL((gate_kernel<F32, N>), dim3((unsigned)tokens), dim3(threads), 0,     \
-                       stream, ids, raw_vocab, kv, q_w, k_w, h, gate_out, stats, hc, dim,   \
-                       eps, clamp, plain);                                                  \
-    break;
+hipError_t launch(int cpt, int threads, bool all_streams, const int32_t *ids, int32_t raw_vocab,
+                  const void *kv, const float *q_w, const float *k_w, void *h, float *gate_out,
+                  float *stats, int64_t tokens, int hc, int dim, float eps, float clamp,
+                  int plain, hipStream_t stream) {
+#define ENGRAM_GATE_CASE(N, AS)                                                             \
+  hipLaunchKernelGGL((gate_kernel<F32, N, AS>), dim3((unsigned)tokens), dim3(threads), 0,   \
+                     stream, ids, raw_vocab, kv, q_w, k_w, h, gate_out, stats, hc, dim,     \
+                     eps, clamp, plain)
+  if (all_streams) {
+    switch (cpt) {
+      case 1: ENGRAM_GATE_CASE(1, true); break;
+      case 2: ENGRAM_GATE_CASE(2, true); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (cpt) {
-    ENGRAM_GATE_CASE(1)
-    ENGRAM_GATE_CASE(2)
-    ENGRAM_GATE_CASE(3)
-    ENGRAM_GATE_CASE(4)
-    ENGRAM_GATE_CASE(5)
-    ENGRAM_GATE_CASE(6)
-    ENGRAM_GATE_CASE(7)
-    ENGRAM_GATE_CASE(8)
+    case 1: ENGRAM_GATE_CASE(1, false); break;
+    case 2: ENGRAM_GATE_CASE(2, false); break;
+    case 3: ENGRAM_GATE_CASE(3, false); break;
+    case 4: ENGRAM_GATE_CASE(4, false); break;
+    case 5: ENGRAM_GATE_CASE(5, false); break;
+    case 6: ENGRAM_GATE_CASE(6, false); break;
+    case 7: ENGRAM_GATE_CASE(7, false); break;
+    case 8: ENGRAM_GATE_CASE(8, false); break;
     default:
       return hipErrorInvalidValue;
   }
@@ -204,8 +312,10 @@ hipError_t engram_launch_gate(bool f32, const int32_t *ids, int32_t raw_vocab, c
   const int needed = ((cps + engram::kWave - 1) / engram::kWave) * engram::kWave;
   if (threads > needed) threads = needed;
   const int cpt = (cps + threads - 1) / threads;
-  return f32 ? launch<true>(cpt, threads, ids, raw_vocab, kv, q_w, k_w, h, gate_out, stats,
-                            tokens, hc, dim, eps, clamp, plain, stream)
-             : launch<false>(cpt, threads, ids, raw_vocab, kv, q_w, k_w, h, gate_out, stats,
-                             tokens, hc, dim, eps, clamp, plain, stream);
+  // few tokens: one memory round trip per token for up to kAllStreams streams
+  const bool all_streams = tokens < 8 * (int64_t)cus && hc <= kAllStreams && cpt <= 2;
+  return f32 ? launch<true>(cpt, threads, all_streams, ids, raw_vocab, kv, q_w, k_w, h,
+                            gate_out, stats, tokens, hc, dim, eps, clamp, plain, stream)
+             : launch<false>(cpt, threads, all_streams, ids, raw_vocab, kv, q_w, k_w, h,
+                             gate_out, stats, tokens, hc, dim, eps, clamp, plain, stream);
 }
