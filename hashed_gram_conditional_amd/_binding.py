@@ -148,11 +148,25 @@ def status_string(status: int) -> str:
     return LIB.engram_status_string(int(status)).decode()
 
 
-def _ptr(t) -> Optional[int]:
-    if t is None:
-        return None
-    if isinstance(t, int):
+def _table_ptr(t) -> Optional[int]:
+    """Address of a table argument: device memory or pinned host memory (the
+    library checks which and rejects pageable memory with ENGRAM_EINVAL)."""
+    if t is None or isinstance(t, int):
         return t
+    if not t.is_contiguous():
+        raise ValueError("engram: a table tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _ptr(t) -> Optional[int]:
+    """Address of a tensor the kernels read or write in place: contiguous, and in
+    device memory or pinned host memory (a pageable host tensor would fault)."""
+    if t is None or isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("engram: tensors must be contiguous")
+    if not t.is_cuda and not t.is_pinned():
+        raise ValueError("engram: a host tensor must be pinned for the GPU to reach it")
     return t.data_ptr()
 
 
@@ -256,7 +270,7 @@ def engram_hash_layers(params: Sequence[HashParams], ids, batch: int, seq: int, 
 
 def engram_gather(table, table_rows: int, row_format: int, row_dim: int, row_ids, n_ids: int,
                   out, stream=None):
-    _check(LIB.engram_gather(_ptr(table), table_rows, row_format, row_dim, _ptr(row_ids),
+    _check(LIB.engram_gather(_table_ptr(table), table_rows, row_format, row_dim, _ptr(row_ids),
                              n_ids, _ptr(out), _stream(stream)), "engram_gather")
 
 
@@ -284,14 +298,14 @@ def engram_forward_workspace_size(params: HashParams, desc: ForwardDesc) -> int:
 def engram_forward(params: HashParams, desc: ForwardDesc, ids, hist_in, hist_out, table, wkv,
                    q_w, k_w, h, gate_out, workspace, workspace_bytes: int, stream=None):
     _check(LIB.engram_forward(ctypes.byref(params), ctypes.byref(desc), _ptr(ids),
-                              _ptr(hist_in), _ptr(hist_out), _ptr(table), _ptr(wkv),
+                              _ptr(hist_in), _ptr(hist_out), _table_ptr(table), _ptr(wkv),
                               _ptr(q_w), _ptr(k_w), _ptr(h), _ptr(gate_out),
                               _ptr(workspace), workspace_bytes, _stream(stream)),
            "engram_forward")
 
 
 def engram_gather_rows(table, table_rows: int, row_ids, n_ids: int, out, stream=None):
-    _check(LIB.engram_gather_rows(_ptr(table), table_rows, _ptr(row_ids), n_ids, _ptr(out),
+    _check(LIB.engram_gather_rows(_table_ptr(table), table_rows, _ptr(row_ids), n_ids, _ptr(out),
                                   _stream(stream)), "engram_gather_rows")
 
 
@@ -300,7 +314,7 @@ def engram_project_mx_workspace_size(tokens: int, segments: int, out_dim: int) -
 
 
 def engram_gather_mx(table, table_rows: int, row_ids, n_ids: int, codes, scales, stream=None):
-    _check(LIB.engram_gather_mx(_ptr(table), table_rows, _ptr(row_ids), n_ids, _ptr(codes),
+    _check(LIB.engram_gather_mx(_table_ptr(table), table_rows, _ptr(row_ids), n_ids, _ptr(codes),
                                 _ptr(scales), _stream(stream)), "engram_gather_mx")
 
 
@@ -319,7 +333,7 @@ def engram_forward_mx(params: HashParams, desc: ForwardDesc, ids, hist_in, hist_
                       w_codes, w_scales, q_w, k_w, h, gate_out, workspace, workspace_bytes: int,
                       stream=None):
     _check(LIB.engram_forward_mx(ctypes.byref(params), ctypes.byref(desc), _ptr(ids),
-                                 _ptr(hist_in), _ptr(hist_out), _ptr(table), _ptr(w_codes),
+                                 _ptr(hist_in), _ptr(hist_out), _table_ptr(table), _ptr(w_codes),
                                  _ptr(w_scales), _ptr(q_w), _ptr(k_w), _ptr(h), _ptr(gate_out),
                                  _ptr(workspace), workspace_bytes, _stream(stream)),
            "engram_forward_mx")
@@ -345,7 +359,7 @@ def engram_forward_conv(params: HashParams, desc: ForwardDesc, conv: ShortConv, 
                         hist_out, table, wkv, q_w, k_w, h, gate_out, workspace,
                         workspace_bytes: int, stream=None):
     _check(LIB.engram_forward_conv(ctypes.byref(params), ctypes.byref(desc), ctypes.byref(conv),
-                                   _ptr(ids), _ptr(hist_in), _ptr(hist_out), _ptr(table),
+                                   _ptr(ids), _ptr(hist_in), _ptr(hist_out), _table_ptr(table),
                                    _ptr(wkv), _ptr(q_w), _ptr(k_w), _ptr(h), _ptr(gate_out),
                                    _ptr(workspace), workspace_bytes, _stream(stream)),
            "engram_forward_conv")

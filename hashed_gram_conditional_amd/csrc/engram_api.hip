@@ -14,6 +14,14 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// batch * seq when both are >= 0 and the product is at most `limit`, else -1
+// (so a product beyond int64 cannot wrap into an accepted count).
+int64_t token_count(int64_t batch, int64_t seq, int64_t limit) {
+  if (batch < 0 || seq < 0) return -1;
+  if (seq > 0 && batch > limit / seq) return -1;
+  return batch * seq;
+}
+
 // ---- deterministic Miller-Rabin for 64-bit integers --------------------------
 // The bases 2, 3, 5, 7, 11, 13, 17, 19, 23, 29, 31 and 37 decide primality for
 // every n < 3.3 * 10^24 (Sorenson & Webster, "Strong pseudoprimes to twelve
@@ -136,7 +144,7 @@ int check_layer_params(const engram_hash_params *p, int32_t layers) {
 
 int check_desc(const engram_forward_desc *d) {
   if (d == nullptr) return ENGRAM_EINVAL;
-  if (d->batch < 0 || d->seq < 0) return ENGRAM_ESHAPE;
+  if (token_count(d->batch, d->seq, INT32_MAX) < 0 || d->table_rows < 0) return ENGRAM_ESHAPE;
   if (d->hc < 1 || d->hc > 8) return ENGRAM_ESHAPE;
   if (d->dim < 8 || d->dim % 8 != 0 || d->dim > 8192) return ENGRAM_ESHAPE;
   if (d->row_format != ENGRAM_ROW_E4M3_E8M0_264 && d->row_format != ENGRAM_ROW_F32)
@@ -312,12 +320,11 @@ int engram_hash_layers(const engram_hash_params *params, int32_t layers, const i
                        int64_t *row_ids, hipStream_t stream) {
   int rc = check_layer_params(params, layers);
   if (rc != ENGRAM_OK) return rc;
-  if (batch < 0 || seq < 0) return ENGRAM_ESHAPE;
-  const int64_t ntok = batch * seq;
+  const int64_t ntok = token_count(batch, seq, (int64_t)INT32_MAX * 64);
+  if (ntok < 0) return ENGRAM_ESHAPE;
   if (ntok > 0 && (ids == nullptr || row_ids == nullptr)) return ENGRAM_EINVAL;
   if (!aligned(ids, 4) || !aligned(row_ids, 8) || !aligned(hist_in, 4) || !aligned(hist_out, 4))
     return ENGRAM_EINVAL;
-  if (ntok > (int64_t)INT32_MAX * 64) return ENGRAM_ESHAPE;
   const EngramHashArgs a = make_hash_args(params, layers);
   return hip_status(engram_launch_hash(a, params->token_map, ids, batch, seq, hist_in, hist_out,
                                        row_ids, stream));

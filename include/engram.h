@@ -132,7 +132,8 @@ typedef enum engram_gate_mode {
 /* Shapes and constants of one forward call. */
 typedef struct engram_forward_desc {
   int64_t batch;              /* B sequences                                       */
-  int64_t seq;                /* T tokens per sequence in this chunk (decode: 1)   */
+  int64_t seq;                /* T tokens per sequence in this chunk (decode: 1);
+                                 B, T >= 0 and B * T <= 2^31 - 1, else ESHAPE      */
   int32_t hc;                 /* hyper-connection streams (4); 1 <= hc <= 8        */
   int32_t dim;                /* d, stream width (5120); multiple of 8             */
   int64_t table_rows;         /* R, rows of the table; >= sum of the primes        */
@@ -237,7 +238,8 @@ int engram_check_token_map(const int32_t *token_map, int32_t raw_vocab,
  *   row_ids  int64 [B*T, S], row_ids[t, (n-2) K + k] = (mix_{t,n} mod p) + off.
  * A DEAD cell blocks itself and every older cell, which then hash as the pad id;
  * at a DEAD position every cell is blocked ([P1] image-token paragraph; [P2]
- * "多模态细节"; [P4] item 4). B or T may be 0.
+ * "多模态细节"; [P4] item 4). B or T may be 0; B * T above 64 * (2^31 - 1)
+ * is ENGRAM_ESHAPE.
  * Errors: ENGRAM_EINVAL, ENGRAM_EMULT, ENGRAM_EPRIMES, ENGRAM_ESHAPE, ENGRAM_EHIP.
  */
 int engram_hash(const engram_hash_params *params, const int32_t *ids, int64_t batch,

@@ -115,6 +115,9 @@ def test_hash_argument_validation():
     assert _hash_status(_params(), ids=0x2001) == E.EINVAL          # misaligned
     assert _hash_status(_params(), ids=None) == E.EINVAL
     assert _hash_status(_params(), B=-1) == E.ESHAPE
+    # B * T beyond int64 must not wrap into an accepted token count
+    assert _hash_status(_params(), B=1 << 40, T=1 << 40) == E.ESHAPE
+    assert _hash_status(_params(), B=1 << 31, T=1 << 32) == E.ESHAPE
 
 
 def _hash_layers_status(params, layers=None, ids=0x2000, B=1, T=4, rows=0x3000):
@@ -197,6 +200,11 @@ def test_forward_validation_and_workspace_size():
     assert L.engram_forward(ctypes.byref(p), ctypes.byref(small), *args, 0x10000, n,
                             None) == E.EPRIMES
     assert E.status_string(E.EPRIMES).startswith("bad primes")
+    for B, T in [(1 << 40, 1 << 40), (1 << 31, 2), (-1, 4)]:       # wraps, > 2^31 - 1, < 0
+        big = E.forward_desc(B, T, 4, 5120, 384_006_168, 0, 256)
+        assert E.engram_forward_workspace_size(p, big) == 0
+        assert L.engram_forward(ctypes.byref(p), ctypes.byref(big), *args, 0x10000, n,
+                                None) == E.ESHAPE
 
 
 def test_one_hip_runtime_whatever_the_import_order():
@@ -267,3 +275,17 @@ def test_forward_conv_workspace_and_validation():
     bad = E.short_conv(0x7000, taps=0)
     assert L.engram_forward_conv(ctypes.byref(p), ctypes.byref(d), ctypes.byref(bad), *args,
                                  0x10000, n, None) == E.ESHAPE
+
+
+def test_binding_rejects_tensors_the_kernels_cannot_read():
+    import torch
+    from hashed_gram_conditional_amd import _binding as B
+    t = torch.zeros(8, 4, dtype=torch.int32)
+    with pytest.raises(ValueError, match="pinned"):
+        B._ptr(t)                                   # pageable host memory
+    with pytest.raises(ValueError, match="contiguous"):
+        B._ptr(t.t())
+    with pytest.raises(ValueError, match="contiguous"):
+        B._table_ptr(t.t())
+    assert B._table_ptr(t) == t.data_ptr()          # the library checks tables itself
+    assert B._ptr(None) is None and B._ptr(0x1000) == 0x1000
