@@ -675,6 +675,23 @@ def decode_bench(steps: int, warmup: int):
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     ms = ev[0].elapsed_time(ev[steps]) / steps
+    # the same step captured once in a HIP graph and replayed (no launch gaps
+    # between its kernels; the history advances in place on every replay)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        E.engram_forward(gw.params, gw.desc, gw.ids, hist, hist, gw.table, gw.wkv, gw.q_w,
+                         gw.k_w, gw.h, gates, ws, nws)
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    gev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    gev[0].record(stream)
+    for _ in range(steps):
+        graph.replay()
+    gev[1].record(stream)
+    torch.cuda.synchronize()
+    graph_ms = gev[0].elapsed_time(gev[1]) / steps
+    del graph
     # per-stage breakdown through the stage entry points
     T, S = w.tokens, w.segments
     K_in, N_out = S * w.row_dim, (w.hc + 1) * w.dim
@@ -722,6 +739,8 @@ def decode_bench(steps: int, warmup: int):
     res = {"workload": "decode: 256 sequences x 1 token with a 3-token history, 24 segments of "
                        "primes from 16,000,000 (384,006,168 x 264 B = 101.4 GB table), hc 4 x 5120",
            "tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+           "graph_replay": {"tokens_per_s": round(T / (graph_ms * 1e-3), 1),
+                            "ms_per_step": round(graph_ms, 4)},
            "stages_ms": {"hash": round(st[0], 4), "gather": round(st[1], 4),
                          "project": round(st[2], 4), "gate": round(st[3], 4)},
            "project_weight_stream": {"achieved": round(wkv_bytes / (st[2] * 1e-3) / 1e9, 1),
