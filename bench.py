@@ -259,6 +259,7 @@ def main():
     gemm_tflops = flops / (stage_ms[2] * 1e-3) / 1e12
     gather_gbps = GATHER_BYTES_PER_TOKEN * T / (stage_ms[1] * 1e-3) / 1e9
     tokens_per_s = T / (ms_per_step * 1e-3)
+    traffic = measured_traffic("gemm_bf16_kernel", GEMM_BF16_SOURCES)
     out = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -280,7 +281,8 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "gemm_bf16_kernel (engram_project)",
                      "achieved": round(gemm_tflops, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic("gemm_bf16_kernel", GEMM_BF16_SOURCES),
+                     "traffic": traffic["bytes"] if traffic else None,
+                     "traffic_detail": traffic,
                      "algorithmic_flop": flops},
         "gather": {"kernel": "gather_e4m3_kernel (engram_gather)",
                    "achieved": round(gather_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
