@@ -1,4 +1,5 @@
-"""engram_forward captured in a HIP graph and replayed.
+"""engram_forward captured in a HIP graph and replayed, and called from two host
+threads on two streams at once.
 
 The library allocates nothing, never synchronises and records no memset, so a
 step can be captured once and replayed with new ids written into the same input
@@ -88,6 +89,65 @@ def test_forward_graph_replays_equal_eager(w):
             assert torch.equal(_bits(gates), _bits(g_ref)), f"replay {i}: gates"
             assert torch.equal(hout, hout_ref), f"replay {i}: history"
         del graph
+    finally:
+        gw.free()
+        gc.collect()
+        torch.cuda.empty_cache()
+
+
+def test_forward_on_two_streams_from_two_threads():
+    """Two host threads call engram_forward at once, each on its own stream with
+    its own buffers (the library keeps no shared state); every result equals the
+    same call made alone."""
+    import threading
+    w = S_A
+    say(f"two streams: {w.name} x 2 threads x 4 calls")
+    gw = GpuWorkload(w)
+    try:
+        h0 = gw.h.clone()
+        n = E.engram_forward_workspace_size(gw.params, gw.desc)
+        ids = [gw.ids.clone(), torch.roll(gw.ids, shifts=1, dims=0).contiguous()]
+        ref = []
+        for x in ids:
+            ws = torch.empty(max(n, 256), dtype=torch.uint8, device=DEV)
+            h = h0.clone()
+            g = torch.empty((w.tokens, w.hc), dtype=torch.float32, device=DEV)
+            E.engram_forward(gw.params, gw.desc, x, None, None, gw.table, gw.wkv, gw.q_w,
+                             gw.k_w, h, g, ws, n)
+            torch.cuda.synchronize()
+            ref.append((h, g))
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+        bufs = [(torch.empty(max(n, 256), dtype=torch.uint8, device=DEV), h0.clone(),
+                 torch.empty((w.tokens, w.hc), dtype=torch.float32, device=DEV)) for _ in ids]
+        torch.cuda.synchronize()
+        errors = []
+        results = [[], []]
+
+        def worker(k):
+            try:
+                ws, h, g = bufs[k]
+                for _ in range(4):
+                    with torch.cuda.stream(streams[k]):
+                        h.copy_(h0)
+                        E.engram_forward(gw.params, gw.desc, ids[k], None, None, gw.table,
+                                         gw.wkv, gw.q_w, gw.k_w, h, g, ws, n,
+                                         stream=streams[k])
+                        results[k].append((h.clone(), g.clone()))
+            except Exception as ex:          # reported by the main thread
+                errors.append(ex)
+
+        threads = [threading.Thread(target=worker, args=(k,)) for k in range(2)]
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join()
+        torch.cuda.synchronize()
+        assert not errors, errors
+        for k in range(2):
+            assert len(results[k]) == 4
+            for h, g in results[k]:
+                assert torch.equal(_bits(h), _bits(ref[k][0]))
+                assert torch.equal(_bits(g), _bits(ref[k][1]))
     finally:
         gw.free()
         gc.collect()
