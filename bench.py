@@ -199,6 +199,7 @@ def main():
     e = torch.empty((T, K_in), dtype=torch.bfloat16, device="cuda")
     kv = torch.empty((T, N_out), dtype=torch.bfloat16, device="cuda")
     gates = torch.empty((T, w.hc), dtype=torch.float32, device="cuda")
+    qk_w = torch.empty((w.hc, w.dim), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     log(f"setup {time.perf_counter() - t_setup:.1f} s: {T} tokens, table {gw.rows} rows")
 
@@ -226,7 +227,8 @@ def main():
         E.engram_project(e, gw.wkv, kv, T, K_in, N_out, 0)
         if evs:
             evs[3].record(stream)
-        E.engram_gate(gw.desc, gw.ids, w.raw_vocab, kv, gw.q_w, gw.k_w, gw.h, gates)
+        E.engram_fold_gate_weights(gw.q_w, gw.k_w, w.hc, w.dim, qk_w)
+        E.engram_gate_folded(gw.desc, gw.ids, w.raw_vocab, kv, qk_w, gw.h, gates)
         if evs:
             evs[4].record(stream)
 
@@ -432,6 +434,8 @@ def host_tier_bench(gw, rows, e, kv, gates, steps: int, warmup: int):
     ready = [torch.cuda.Event(), torch.cuda.Event()]
     free = [torch.cuda.Event(), torch.cuda.Event()]
 
+    qk_w = torch.empty((w.hc, w.dim), dtype=torch.float32, device="cuda")
+
     def fetch(slot):
         side.wait_event(free[slot])
         E.engram_hash(gw.params, gw.ids, w.batch, w.seq, None, None, r_buf[slot], stream=side)
@@ -443,7 +447,8 @@ def host_tier_bench(gw, rows, e, kv, gates, steps: int, warmup: int):
         main.wait_event(ready[slot])
         E.engram_project(e_buf[slot], gw.wkv, kv, T, K_in, N_out, 0, pws if nws else None, nws,
                          stream=main)
-        E.engram_gate(gw.desc, gw.ids, w.raw_vocab, kv, gw.q_w, gw.k_w, gw.h, gates, stream=main)
+        E.engram_fold_gate_weights(gw.q_w, gw.k_w, w.hc, w.dim, qk_w, stream=main)
+        E.engram_gate_folded(gw.desc, gw.ids, w.raw_vocab, kv, qk_w, gw.h, gates, stream=main)
         free[slot].record(main)
 
     for ev in free:
@@ -560,6 +565,7 @@ def fp8_prefill_bench(gw, steps: int, warmup: int):
     gates = torch.empty((T, w.hc), dtype=torch.float32, device="cuda")
     n_ws = E.engram_project_mx_workspace_size(T, S, N_out)
     pws = torch.empty(max(n_ws, 256), dtype=torch.uint8, device="cuda")
+    qk_w = torch.empty((w.hc, w.dim), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
 
@@ -576,7 +582,8 @@ def fp8_prefill_bench(gw, steps: int, warmup: int):
                             n_ws)
         if evs:
             evs[3].record(stream)
-        E.engram_gate(gw.desc, gw.ids, w.raw_vocab, kv, gw.q_w, gw.k_w, gw.h, gates)
+        E.engram_fold_gate_weights(gw.q_w, gw.k_w, w.hc, w.dim, qk_w)
+        E.engram_gate_folded(gw.desc, gw.ids, w.raw_vocab, kv, qk_w, gw.h, gates)
         if evs:
             evs[4].record(stream)
 

@@ -12,7 +12,8 @@ from ._binding import (  # noqa: F401
     status_string, hash_params, forward_desc, short_conv,
     engram_make_primes, engram_make_layer_primes, engram_check_token_map, engram_hash,
     engram_hash_layers, engram_gather,
-    engram_project, engram_project_workspace_size, engram_gate, engram_forward_workspace_size,
+    engram_project, engram_project_workspace_size, engram_gate, engram_fold_gate_weights,
+    engram_gate_folded, engram_forward_workspace_size,
     engram_forward, engram_gather_rows, engram_gather_mx, engram_project_mx, engram_project_mx_workspace_size,
     engram_forward_mx, engram_forward_mx_workspace_size,
     engram_gate_conv, engram_gate_conv_workspace_size, engram_forward_conv,

@@ -118,6 +118,8 @@ def _load():
         "engram_project": (ctypes.c_int, [P, P, P, I64, I64, I64, I32, P, SZ, P]),
         "engram_project_workspace_size": (SZ, [I64, I64, I64, I32]),
         "engram_gate": (ctypes.c_int, [P, P, I32, P, P, P, P, P, P]),
+        "engram_fold_gate_weights": (ctypes.c_int, [P, P, I32, I32, P, P]),
+        "engram_gate_folded": (ctypes.c_int, [P, P, I32, P, P, P, P, P]),
         "engram_forward_workspace_size": (SZ, [P, P]),
         "engram_gather_rows": (ctypes.c_int, [P, I64, P, I64, P, P]),
         "engram_project_mx": (ctypes.c_int, [P, P, I32, P, P, P, I64, I64, P, SZ, P]),
@@ -289,6 +291,19 @@ def engram_gate(desc: ForwardDesc, ids, raw_vocab: int, kv, q_w, k_w, h, gate_ou
                 stream=None):
     _check(LIB.engram_gate(ctypes.byref(desc), _ptr(ids), raw_vocab, _ptr(kv), _ptr(q_w),
                            _ptr(k_w), _ptr(h), _ptr(gate_out), _stream(stream)), "engram_gate")
+
+
+def engram_fold_gate_weights(q_w, k_w, hc: int, dim: int, qk_w, stream=None):
+    """qk_w [hc, dim] = q_w * k_w (fp32), the gate's scales folded once."""
+    _check(LIB.engram_fold_gate_weights(_ptr(q_w), _ptr(k_w), hc, dim, _ptr(qk_w),
+                                        _stream(stream)), "engram_fold_gate_weights")
+
+
+def engram_gate_folded(desc: ForwardDesc, ids, raw_vocab: int, kv, qk_w, h, gate_out,
+                       stream=None):
+    _check(LIB.engram_gate_folded(ctypes.byref(desc), _ptr(ids), raw_vocab, _ptr(kv),
+                                  _ptr(qk_w), _ptr(h), _ptr(gate_out), _stream(stream)),
+           "engram_gate_folded")
 
 
 def engram_forward_workspace_size(params: HashParams, desc: ForwardDesc) -> int:

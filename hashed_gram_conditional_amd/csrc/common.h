@@ -177,12 +177,17 @@ hipError_t engram_launch_gemm_f32(const float *e, const float *w, float *kv, int
 
 // stats == NULL: the gate and the residual update. stats != NULL (float
 // [tokens, hc + 1]): gates and the value row's mean square per token, h
-// untouched. plain selects sigmoid(s) over the signed root.
+// untouched. plain selects sigmoid(s) over the signed root. k_w == NULL: q_w
+// holds the folded products q_w * k_w (engram_launch_fold_gate_weights).
 hipError_t engram_launch_gate(bool f32, const int32_t *ids, int32_t raw_vocab,
                               const void *kv, const float *q_w, const float *k_w,
                               void *h, float *gate_out, float *stats, int64_t tokens,
                               int32_t hc, int32_t dim, float eps, float clamp, int plain,
                               hipStream_t stream);
+
+// qk_w[i] = q_w[i] * k_w[i] over hc * dim fp32 values (dim a multiple of 8).
+hipError_t engram_launch_fold_gate_weights(const float *q_w, const float *k_w, float *qk_w,
+                                           int32_t hc, int32_t dim, hipStream_t stream);
 
 // Short convolution branch and its history (conv.hip).
 struct EngramConvArgs {

@@ -88,6 +88,21 @@ __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
     if (lane == 0) red[wave][kMaxHc][0] = svv;
   }
 
+  // The weights q_w * k_w of chunk ci of stream m, one fp32 product each; with
+  // k_w == NULL, q_w already holds those products (folded once per call).
+  auto scales = [&](int m, int ci, float (&w)[8]) {
+    const float4 *qp = reinterpret_cast<const float4 *>(q_w + (int64_t)m * dim) + 2 * ci;
+    const float4 q0 = qp[0], q1 = qp[1];
+    if (k_w == nullptr) {
+      w[0] = q0.x; w[1] = q0.y; w[2] = q0.z; w[3] = q0.w;
+      w[4] = q1.x; w[5] = q1.y; w[6] = q1.z; w[7] = q1.w;
+    } else {
+      const float4 *kp = reinterpret_cast<const float4 *>(k_w + (int64_t)m * dim) + 2 * ci;
+      const float4 k0 = kp[0], k1 = kp[1];
+      w[0] = q0.x * k0.x; w[1] = q0.y * k0.y; w[2] = q0.z * k0.z; w[3] = q0.w * k0.w;
+      w[4] = q1.x * k1.x; w[5] = q1.y * k1.y; w[6] = q1.z * k1.z; w[7] = q1.w * k1.w;
+    }
+  };
   // The gate of stream m from its three block-wide sums.
   auto gate_of = [&](int m) -> float {
     float a = 0.f, b = 0.f, c2 = 0.f;
@@ -110,11 +125,8 @@ __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
     for (int c = 0; c < CPT; ++c) {
       const int ci = tid + c * nthreads;
       if (ci < cps) {
-        const float4 *qp = reinterpret_cast<const float4 *>(q_w + (int64_t)m * dim) + 2 * ci;
-        const float4 *kp = reinterpret_cast<const float4 *>(k_w + (int64_t)m * dim) + 2 * ci;
-        const float4 q0 = qp[0], q1 = qp[1], k0 = kp[0], k1 = kp[1];
-        const float w[8] = {q0.x * k0.x, q0.y * k0.y, q0.z * k0.z, q0.w * k0.w,
-                            q1.x * k1.x, q1.y * k1.y, q1.z * k1.z, q1.w * k1.w};
+        float w[8];
+        scales(m, ci, w);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float he = hm[c][e];
@@ -200,11 +212,8 @@ __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
           Chunk<F32> kc;
           hh[c].load_nt(h, h_row + (int64_t)m * cps + ci);
           kc.load_nt(kv, kv_row + (int64_t)m * cps + ci);
-          const float4 *qp = reinterpret_cast<const float4 *>(q_w + (int64_t)m * dim) + 2 * ci;
-          const float4 *kp = reinterpret_cast<const float4 *>(k_w + (int64_t)m * dim) + 2 * ci;
-          const float4 q0 = qp[0], q1 = qp[1], k0 = kp[0], k1 = kp[1];
-          const float w[8] = {q0.x * k0.x, q0.y * k0.y, q0.z * k0.z, q0.w * k0.w,
-                              q1.x * k1.x, q1.y * k1.y, q1.z * k1.z, q1.w * k1.w};
+          float w[8];
+          scales(m, ci, w);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float he = hh[c][e];
@@ -318,4 +327,28 @@ hipError_t engram_launch_gate(bool f32, const int32_t *ids, int32_t raw_vocab, c
                             gate_out, stats, tokens, hc, dim, eps, clamp, plain, stream)
              : launch<false>(cpt, threads, all_streams, ids, raw_vocab, kv, q_w, k_w, h,
                              gate_out, stats, tokens, hc, dim, eps, clamp, plain, stream);
+}
+
+namespace {
+
+__global__ void fold_kernel(const float4 *__restrict__ q_w, const float4 *__restrict__ k_w,
+                            float4 *__restrict__ qk_w, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n4) {
+    const float4 q = q_w[i], k = k_w[i];
+    qk_w[i] = make_float4(q.x * k.x, q.y * k.y, q.z * k.z, q.w * k.w);
+  }
+}
+
+}  // namespace
+
+hipError_t engram_launch_fold_gate_weights(const float *q_w, const float *k_w, float *qk_w,
+                                           int32_t hc, int32_t dim, hipStream_t stream) {
+  const int64_t n4 = (int64_t)hc * dim / 4;
+  if (n4 <= 0) return hipSuccess;
+  const int threads = 256;
+  hipLaunchKernelGGL(fold_kernel, dim3((unsigned)((n4 + threads - 1) / threads)), dim3(threads), 0,
+                     stream, reinterpret_cast<const float4 *>(q_w),
+                     reinterpret_cast<const float4 *>(k_w), reinterpret_cast<float4 *>(qk_w), n4);
+  return hipGetLastError();
 }

@@ -385,8 +385,32 @@ int engram_gate(const engram_forward_desc *desc, const int32_t *ids, int32_t raw
                 const void *kv, const float *q_w, const float *k_w, void *h,
                 float *gate_out, hipStream_t stream);
 
-/* Bytes of workspace engram_forward needs (row ids, e, kv and the projection's
- * workspace), or 0 on bad args. */
+/*
+ * The two learned scales enter the gate only through their element-wise
+ * product ([P4] "消费：学习投影 + 余弦门控": the dot weights element i of h and
+ * k by q_w[i] k_w[i]), so they can be folded once into one array.
+ *   q_w, k_w float [hc, dim] device, 16-byte aligned, dim a multiple of 8
+ *   qk_w     float [hc, dim] device, 16-byte aligned, caller-owned:
+ *            qk_w[i] = q_w[i] * k_w[i] (one fp32 rounding, the product the
+ *            gate forms itself), so engram_gate_folded gives engram_gate's bits
+ * Errors: ENGRAM_EINVAL, ENGRAM_ESHAPE, ENGRAM_EHIP.
+ */
+int engram_fold_gate_weights(const float *q_w, const float *k_w, int32_t hc, int32_t dim,
+                             float *qk_w, hipStream_t stream);
+
+/*
+ * Step 5 with folded scales: engram_gate with qk_w (from engram_fold_gate_weights)
+ * in place of q_w and k_w. It reads one scale array per stream instead of two.
+ * Arguments and errors as engram_gate.
+ */
+int engram_gate_folded(const engram_forward_desc *desc, const int32_t *ids, int32_t raw_vocab,
+                       const void *kv, const float *qk_w, void *h, float *gate_out,
+                       hipStream_t stream);
+
+/* Bytes of workspace engram_forward needs (row ids, e, kv, the folded gate
+ * scales and the projection's workspace), or 0 on bad args. Calls of 1024
+ * tokens or more fold q_w * k_w there (engram_fold_gate_weights; the same
+ * bits), so the gate reads one scale array per stream. */
 size_t engram_forward_workspace_size(const engram_hash_params *params,
                                      const engram_forward_desc *desc);
 

@@ -189,7 +189,7 @@ def test_forward_validation_and_workspace_size():
     d = E.forward_desc(4, 8192, 4, 5120, 384_006_168, 0, 256)
     n = E.engram_forward_workspace_size(p, d)
     T = 4 * 8192
-    assert n == T * 24 * 8 + T * 6144 * 2 + T * 25600 * 2
+    assert n == T * 24 * 8 + T * 6144 * 2 + T * 25600 * 2 + 4 * 5120 * 4   # + folded scales
     L = E.LIB
     args = [0x1000, None, None, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None]
     assert L.engram_forward(ctypes.byref(p), ctypes.byref(d), *args, 0x10000, n - 1,
@@ -289,3 +289,22 @@ def test_binding_rejects_tensors_the_kernels_cannot_read():
         B._table_ptr(t.t())
     assert B._table_ptr(t) == t.data_ptr()          # the library checks tables itself
     assert B._ptr(None) is None and B._ptr(0x1000) == 0x1000
+
+
+@host_only
+def test_fold_and_folded_gate_validation():
+    L = E.LIB
+    assert L.engram_fold_gate_weights(0x1000, 0x2000, 0, 64, 0x3000, None) == E.ESHAPE
+    assert L.engram_fold_gate_weights(0x1000, 0x2000, 4, 60, 0x3000, None) == E.ESHAPE
+    assert L.engram_fold_gate_weights(0x1000, 0x2000, 9, 64, 0x3000, None) == E.ESHAPE
+    assert L.engram_fold_gate_weights(None, 0x2000, 4, 64, 0x3000, None) == E.EINVAL
+    assert L.engram_fold_gate_weights(0x1000, 0x2000, 4, 64, None, None) == E.EINVAL
+    assert L.engram_fold_gate_weights(0x1004, 0x2000, 4, 64, 0x3000, None) == E.EINVAL
+    d = E.forward_desc(2, 8, 4, 64, 100, 0, 256)
+    gf = lambda desc, qk: L.engram_gate_folded(ctypes.byref(desc), 0x1000, 100, 0x2000, qk,
+                                               0x4000, None, None)
+    assert gf(d, None) == E.EINVAL
+    assert gf(d, 0x3008) == E.EINVAL                                 # misaligned scales
+    assert gf(E.forward_desc(2, 8, 9, 64, 100, 0, 256), 0x3000) == E.ESHAPE
+    assert L.engram_gate_folded(ctypes.byref(d), 0x1000, 0, 0x2000, 0x3000, 0x4000, None,
+                                None) == E.EINVAL                    # raw_vocab < 1

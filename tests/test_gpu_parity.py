@@ -725,3 +725,38 @@ def test_gate_shapes(hc, dim, f32):
     got = (h_dev.cpu().numpy() if f32 else O.bf16_bits_to_f64(bf16_bits(h_dev)))
     assert_close(got.reshape(h_out.shape), h_out, f"h hc={hc} d={dim}")
     assert np.array_equal(got.reshape(h_out.shape)[dead], h[dead])
+
+
+@pytest.mark.parametrize("T,hc,dim,f32", [(37, 4, 5120, False), (37, 8, 1032, True),
+                                          (3000, 4, 5120, False), (3000, 3, 136, False),
+                                          (2500, 2, 64, True), (1, 1, 8, False)])
+def test_gate_folded_equals_gate(T, hc, dim, f32):
+    """engram_fold_gate_weights + engram_gate_folded give engram_gate's bits: the
+    folded array holds the same fp32 products the gate forms itself. Few-token
+    calls (one round trip per token) and full-chip calls (128-thread blocks)."""
+    rng = np.random.default_rng(T + hc * 1000 + dim)
+    raw = rng.integers(0, 100, T).astype(np.int32)
+    if T > 1:                                        # some DEAD positions, never all
+        raw[rng.integers(1, T, max(T // 10, 1))] = -1
+    q_w = (1 + 0.1 * rng.standard_normal((hc, dim))).astype(np.float32)
+    k_w = (1 + 0.1 * rng.standard_normal((hc, dim))).astype(np.float32)
+    h = rng.standard_normal((T, hc, dim)).astype(np.float32)
+    kv = (50 * rng.standard_normal((T, hc + 1, dim))).astype(np.float32)
+    conv = (lambda a: to_device(a)) if f32 else (lambda a: to_device(gen.f32_to_bf16_bits(a)))
+    h0, kv_dev = conv(h), conv(kv)
+    ids = to_device(raw.reshape(1, T))
+    qd, kd = to_device(q_w), to_device(k_w)
+    fmt = E.ROW_F32 if f32 else E.ROW_E4M3_E8M0_264
+    d = E.forward_desc(1, T, hc, dim, 0, fmt, 32 if f32 else 256, 1e-6, 0.0)
+    h_a, h_b = h0.clone(), h0.clone()
+    g_a = torch.full((T, hc), -1.0, dtype=torch.float32, device=DEV)
+    g_b = torch.full((T, hc), -2.0, dtype=torch.float32, device=DEV)
+    qk = torch.empty((hc, dim), dtype=torch.float32, device=DEV)
+    E.engram_gate(d, ids, 100, kv_dev, qd, kd, h_a, g_a)
+    E.engram_fold_gate_weights(qd, kd, hc, dim, qk)
+    E.engram_gate_folded(d, ids, 100, kv_dev, qk, h_b, g_b)
+    torch.cuda.synchronize()
+    assert np.array_equal(qk.cpu().numpy(), q_w * k_w)          # one fp32 product each
+    assert torch.equal(g_a, g_b)
+    assert torch.equal(_bits(h_a), _bits(h_b))
+    assert not torch.equal(_bits(h_a), _bits(h0))
