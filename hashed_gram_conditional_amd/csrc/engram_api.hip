@@ -193,9 +193,10 @@ EngramConvArgs make_conv_args(const engram_short_conv *c) {
 
 // engram_forward folds the gate's two scale arrays into one (the same fp32
 // products, so the same bits) when the call has at least this many tokens: the
-// gate then reads half the scale bytes per token (12 % faster at 32768 tokens),
-// while for a decode step the extra launch costs more than it saves.
-constexpr int64_t kFoldMinTokens = 1024;
+// gate then reads half the scale bytes per token (12 % faster at 32768 tokens,
+// 8 % at 2048 with the fold's launch counted), while at 1024 tokens and below the
+// extra launch costs more than it saves.
+constexpr int64_t kFoldMinTokens = 2048;
 
 size_t folded_scales_bytes(const engram_forward_desc *d) {
   return align256((size_t)d->hc * (size_t)d->dim * sizeof(float));

@@ -408,7 +408,7 @@ int engram_gate_folded(const engram_forward_desc *desc, const int32_t *ids, int3
                        hipStream_t stream);
 
 /* Bytes of workspace engram_forward needs (row ids, e, kv, the folded gate
- * scales and the projection's workspace), or 0 on bad args. Calls of 1024
+ * scales and the projection's workspace), or 0 on bad args. Calls of 2048
  * tokens or more fold q_w * k_w there (engram_fold_gate_weights; the same
  * bits), so the gate reads one scale array per stream. */
 size_t engram_forward_workspace_size(const engram_hash_params *params,
