@@ -190,12 +190,66 @@ def _layers_share_multipliers(ids, token_map, compressed_vocab, pad, multipliers
                                      max_ngram, heads, hist)
 
 
+def _compress_skips_map(ids, token_map, compressed_vocab):
+    """Wrong: the raw id is used as the compressed id."""
+    ids = np.asarray(ids, dtype=np.int64)
+    ok = (ids >= 0) & (ids < token_map.shape[0])
+    return np.where(ok, ids, E.DEAD)
+
+
+def _compress_no_value_check(ids, token_map, compressed_vocab):
+    """Wrong: map values outside [0, V') pass through."""
+    ids = np.asarray(ids, dtype=np.int64)
+    ok = (ids >= 0) & (ids < token_map.shape[0])
+    return np.where(ok, token_map.astype(np.int64)[np.where(ok, ids, 0)], E.DEAD)
+
+
+def _forward_tokens_variant(v_col=None, round_kv=None, reverse_keys=False, dead_by_position=False):
+    """forward_tokens with one planted mistake: v taken from block ``v_col``,
+    kv rounding forced on/off (``round_kv``), keys in reverse stream order, or
+    the DEAD flags taken by position instead of by token index."""
+    def f(tokens, row_ids, dead, *, fetch_rows=None, table_f32=None, table_rows, wkv, q_w,
+          k_w, h, hc, dim, eps, clamp, bf16):
+        tokens = np.asarray(tokens, dtype=np.int64)
+        rid = row_ids[tokens]
+        if bf16:
+            e = E.bf16_bits_to_f64(E.gather_e4m3(fetch_rows, rid, table_rows))
+        else:
+            e = E.gather_f32(table_f32, rid).astype(np.float64)
+        kv = E.project(e, wkv)
+        if (bf16 if round_kv is None else round_kv):
+            kv = E.bf16_bits_to_f64(E.round_to_bf16_bits(kv))
+        kv = kv.reshape(len(tokens), hc + 1, dim)
+        keys = kv[:, :hc, :][:, ::-1] if reverse_keys else kv[:, :hc, :]
+        v = kv[:, hc if v_col is None else v_col, :]
+        dd = np.asarray(dead)[:len(tokens)] if dead_by_position else np.asarray(dead)[tokens]
+        alpha, h_out = E.gate(h[tokens], keys, v, q_w, k_w, dd, eps, clamp)
+        out = {"e": e, "kv": kv, "alpha": alpha, "h_out": h_out}
+        if bf16:
+            out["h_out_bits"] = E.round_to_bf16_bits(h_out)
+        return out
+    f.__name__ = "_forward_tokens_" + ("v_from_key0" if v_col is not None else
+                                       "kv_unrounded" if round_kv is False else
+                                       "kv_always_rounded" if round_kv else
+                                       "keys_reversed" if reverse_keys else "dead_by_position")
+    return f
+
+
 _orig = {name: getattr(E, name) for name in
          ("mix_values", "segment_offsets", "primes_from", "ngram_cells", "gate", "project",
           "round_to_bf16_bits", "layer_primes", "hash_rows_layers", "mx_values", "short_conv",
-          "rms_norm", "gate_conv")}
+          "rms_norm", "gate_conv", "compress", "forward_tokens")}
+
+_FT_PINS = [P.test_forward_tokens_closed_form_bf16, P.test_forward_tokens_closed_form_f32]
 
 MUTATIONS = [
+    ("compress", _compress_skips_map, [P.test_compress_hand_built_map]),
+    ("compress", _compress_no_value_check, [P.test_compress_hand_built_map]),
+    ("forward_tokens", _forward_tokens_variant(v_col=0), _FT_PINS),
+    ("forward_tokens", _forward_tokens_variant(round_kv=False), _FT_PINS),
+    ("forward_tokens", _forward_tokens_variant(round_kv=True), _FT_PINS),
+    ("forward_tokens", _forward_tokens_variant(reverse_keys=True), _FT_PINS),
+    ("forward_tokens", _forward_tokens_variant(dead_by_position=True), _FT_PINS),
     ("mix_values", _mix_oldest_first, [P.test_worked_example_mix_and_indices]),
     ("mix_values", _mix_add, [P.test_worked_example_mix_and_indices]),
     ("segment_offsets", _offsets_inclusive, [P.test_worked_example_through_single_table]),

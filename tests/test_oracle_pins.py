@@ -814,3 +814,149 @@ def test_gate_conv_dead_positions():
     assert np.abs(y[0, 6]).min() > 0            # the branch is not zero there, yet h stays
     live = ~dead[0]
     np.testing.assert_allclose(ho[0, live], h[0, live] + y[0, live], rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# compression map, and the whole layer on hand-built inputs
+# ---------------------------------------------------------------------------
+
+def test_compress_hand_built_map():
+    """x' = P[x] on a six-entry map whose values include two outside [0, V'):
+    P1 "tokenizer 压缩" (the map), and the reading that a raw id outside [0, V),
+    the DEAD marker and a map value outside [0, V') all come out DEAD."""
+    tm = np.array([3, 0, 7, 9, -2, 5], dtype=np.int32)          # V = 6, V' = 8
+    ids = np.array([[0, 1, 2, 3, 4, 5, 6, -1, -5, 2, 1]], dtype=np.int32)
+    got = O.compress(ids, tm, 8)
+    assert got.tolist() == [[3, 0, 7, -1, -1, 5, -1, -1, -1, 7, 0]]
+    # with V' = 10 the value 9 is a valid compressed id
+    assert O.compress(np.array([[3]], np.int32), tm, 10).tolist() == [[9]]
+    # an invalid map value blocks its cell and every older one, like DEAD
+    # (pad' = P[0] = 3): at t = 2 the window is (7, [9 -> DEAD], 0, pad)
+    xc = O.compress(np.array([[1, 3, 2]], np.int32), tm, 8)
+    cells, dead = O.ngram_cells(xc, 3, 4)
+    assert cells[0, 2].tolist() == [7, 3, 3, 3]
+    assert cells[0, 0].tolist() == [0, 3, 3, 3]
+    assert dead[0].tolist() == [False, True, False]
+
+
+# One-hot rows make every kv row a column of W (times a power of two), so the
+# gate and the update of each stream have closed forms. Stream m of a token
+# whose row is r sees h = a_t * (1, ..., 1) and k = c_m * sigma, where sigma has
+# P[r][m] entries +1 followed by d - P[r][m] entries -1. With unit weights the
+# two mean squares are a_t^2 and c_m^2, so
+#   s = a_t c_m (2P - d) / (sqrt(a_t^2 + eps) sqrt(c_m^2 + eps) sqrt(d)),
+# i.e. sqrt(d) cos(theta) up to eps (P1 "门控").
+_FT_D = 8
+_FT_HC = 4
+_FT_P = [[8, 6, 2, 4], [2, 4, 8, 6], [6, 8, 4, 2], [8, 8, 8, 8], [4, 2, 6, 8]]
+_FT_C = [1.0, -2.0, 0.5, 4.0]                        # key scale of stream m (bf16 exact)
+_FT_POS = [5, 200, 33, 64, 255]                      # one-hot input of row r (segment 0)
+_FT_SH = [0, 1, -1, 2, 0]                            # the row's value is 2^SH
+_FT_V = np.array([0.5, -1.25, 3.0, 7.5, -0.375, 10.0, -6.0, 2.25])   # bf16 exact
+_FT_A = [1.5, -2.0, 0.75, 3.0, 1.0, -0.5]            # h scale of token t
+# token t reads rows ROWS[t] = (segment 0, segment 1); ids 5..9 are all-zero
+# rows, -1 and 10 (= R) lie outside the table
+_FT_ROWS = np.array([[0, 5], [1, 6], [2, 7], [3, 8], [-1, 9], [4, 10]], dtype=np.int64)
+_FT_DEAD = np.array([False, False, False, True, False, False])
+_FT_TOK_ROW = [0, 1, 2, 3, None, 4]                  # the one-hot row of token t
+_FT_EPS = 1e-6
+
+
+def _ft_w(row_dim):
+    """W [(hc+1) d, 2 row_dim]: column POS[r] holds the keys c_m sigma and the
+    value V (1 + 2^-10), which bf16 rounds down to V (half an ulp is >= 2^-9)."""
+    d, hc = _FT_D, _FT_HC
+    w = np.zeros(((hc + 1) * d, 2 * row_dim))
+    for r, pos in enumerate(_FT_POS):
+        p = pos % row_dim
+        for m in range(hc):
+            sig = np.where(np.arange(d) < _FT_P[r][m], 1.0, -1.0)
+            w[m * d:(m + 1) * d, p] = _FT_C[m] * sig
+        w[hc * d:, p] = _FT_V * (1.0 + 2.0 ** -10)
+    return w
+
+
+def _ft_expected(tokens, v_rounded):
+    d, hc = _FT_D, _FT_HC
+    alpha = np.zeros((len(tokens), hc))
+    h_out = np.zeros((len(tokens), hc, d))
+    for i, t in enumerate(tokens):
+        h = _FT_A[t] * np.ones((hc, d))
+        r = _FT_TOK_ROW[t]
+        if _FT_DEAD[t]:
+            h_out[i] = h
+            continue
+        if r is None:                   # zero e: k = 0 gives s = 0, v = 0 leaves h
+            alpha[i] = 0.5
+            h_out[i] = h
+            continue
+        v = 2.0 ** _FT_SH[r] * _FT_V * (1.0 if v_rounded else 1.0 + 2.0 ** -10)
+        for m in range(hc):
+            a, c = _FT_A[t], _FT_C[m] * 2.0 ** _FT_SH[r]
+            s = a * c * (2 * _FT_P[r][m] - d) / (
+                math.sqrt(a * a + _FT_EPS) * math.sqrt(c * c + _FT_EPS) * math.sqrt(d))
+            alpha[i, m] = 1.0 / (1.0 + math.exp(-math.copysign(math.sqrt(abs(s)), s)))
+            h_out[i, m] = h[m] + alpha[i, m] * v
+    return alpha, h_out
+
+
+def _ft_inputs():
+    d, hc = _FT_D, _FT_HC
+    h = np.array(_FT_A)[:, None, None] * np.ones((len(_FT_A), hc, d))
+    ones = np.ones((hc, d))
+    return h, ones
+
+
+def test_forward_tokens_closed_form_bf16():
+    """Steps 3-5 composed, on E4M3 rows: kv columns are [k^0 .. k^3 | v] with
+    key m going with stream m (P1 "门控": one key per stream, one shared value),
+    kv is rounded to bf16 before the gate and the update (P4 "消费":
+    h + gate * bf16(v)), DEAD tokens keep h, zero and out-of-range rows give
+    e = 0. Tokens are taken out of order to check the per-token indexing."""
+    R = 10
+
+    def fetch(rows):
+        out = np.zeros((len(rows), 264), dtype=np.uint8)
+        out[:, 256:] = 127                                   # scale 2^0
+        for i, r in enumerate(np.asarray(rows)):
+            if r < len(_FT_POS):
+                p = _FT_POS[r]
+                out[i, p] = 0x38                             # E4M3 1.0
+                out[i, 256 + p // 32] = 127 + _FT_SH[r]
+        return out
+
+    tokens = np.array([3, 0, 5, 1, 4, 2])
+    h, ones = _ft_inputs()
+    res = O.forward_tokens(tokens, _FT_ROWS, _FT_DEAD, fetch_rows=fetch, table_rows=R,
+                           wkv=_ft_w(256), q_w=ones, k_w=ones, h=h, hc=_FT_HC, dim=_FT_D,
+                           eps=_FT_EPS, clamp=0.0, bf16=True)
+    e_exp = np.zeros((len(tokens), 512))
+    for i, t in enumerate(tokens):
+        r = _FT_TOK_ROW[t]
+        if r is not None:
+            e_exp[i, _FT_POS[r]] = 2.0 ** _FT_SH[r]
+    assert np.array_equal(res["e"], e_exp)
+    a_exp, h_exp = _ft_expected(tokens, v_rounded=True)
+    np.testing.assert_allclose(res["alpha"], a_exp, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(res["h_out"], h_exp, rtol=0, atol=1e-12)
+    assert np.array_equal(res["h_out_bits"], O.round_to_bf16_bits(h_exp))
+    # the values here are distinct per stream and per token
+    assert len(np.unique(np.round(a_exp[[1, 2, 3, 5]], 9))) >= 6
+
+
+def test_forward_tokens_closed_form_f32():
+    """The fp32 instance keeps kv unrounded: the same construction through fp32
+    rows of 256 (C0 keeps fp32 throughout)."""
+    R = 10
+    table = np.zeros((R, 256), dtype=np.float32)
+    for r, p in enumerate(_FT_POS):
+        table[r, p] = 2.0 ** _FT_SH[r]
+    tokens = np.array([2, 4, 0, 3, 5, 1])
+    h, ones = _ft_inputs()
+    res = O.forward_tokens(tokens, _FT_ROWS, _FT_DEAD, table_f32=table, table_rows=R,
+                           wkv=_ft_w(256), q_w=ones, k_w=ones, h=h, hc=_FT_HC, dim=_FT_D,
+                           eps=_FT_EPS, clamp=0.0, bf16=False)
+    a_exp, h_exp = _ft_expected(tokens, v_rounded=False)
+    np.testing.assert_allclose(res["alpha"], a_exp, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(res["h_out"], h_exp, rtol=0, atol=1e-12)
+    assert "h_out_bits" not in res
