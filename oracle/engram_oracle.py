@@ -559,8 +559,9 @@ def forward_tokens(tokens: np.ndarray, row_ids: np.ndarray, dead: np.ndarray, *,
     bf16 workloads round e (exact), kv and the output to bf16 as the device
     path stores them; the fp32 workload keeps float64 throughout.
 
-    Returns dict with e, kv, alpha [n, hc], h_out [n, hc, d] (float64) and,
-    for bf16 workloads, h_out_bits (uint16).
+    Returns dict with e, kv, alpha [n, hc], h_out [n, hc, d] (float64),
+    kv_exact (the product before any rounding, [n, (hc+1)*d]) and, for bf16
+    workloads, h_out_bits (uint16).
     """
     tokens = np.asarray(tokens, dtype=np.int64)
     rid = row_ids[tokens]
@@ -568,13 +569,12 @@ def forward_tokens(tokens: np.ndarray, row_ids: np.ndarray, dead: np.ndarray, *,
         e = bf16_bits_to_f64(gather_e4m3(fetch_rows, rid, table_rows))
     else:
         e = gather_f32(table_f32, rid).astype(np.float64)
-    kv = project(e, wkv)
-    if bf16:
-        kv = bf16_bits_to_f64(round_to_bf16_bits(kv))
+    kv_exact = project(e, wkv)
+    kv = bf16_bits_to_f64(round_to_bf16_bits(kv_exact)) if bf16 else kv_exact
     kv = kv.reshape(len(tokens), hc + 1, dim)
     alpha, h_out = gate(h[tokens], kv[:, :hc, :], kv[:, hc, :], q_w, k_w, dead[tokens],
                         eps, clamp)
-    out = {"e": e, "kv": kv, "alpha": alpha, "h_out": h_out}
+    out = {"e": e, "kv": kv, "kv_exact": kv_exact, "alpha": alpha, "h_out": h_out}
     if bf16:
         out["h_out_bits"] = round_to_bf16_bits(h_out)
     return out

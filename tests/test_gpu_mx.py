@@ -1,14 +1,15 @@
 """Parity of the block-scaled FP8 path (engram_gather_rows, engram_gather_mx,
 engram_project_mx, engram_forward_mx) with the CPU oracle. The looked-up rows
-and their split codes and scales match bit for bit;
-the projection stays within the FP8 MFMA's measured precision bound and is
+and their split codes and scales match bit for bit; the projection is within
+1e-3 + 2e-2 of its output row's RMS of the exact product of the FP8 values and
 exact where every output has a single product; gates and streams follow the
-same tolerance as the bf16 path."""
+bf16 path's element-wise tolerance, with the kv allowance taken from the
+projection's bound."""
 import numpy as np
 import pytest
 
 import oracle as O
-from tests.gpu_util import ATOL, RTOL, assert_close, gemm_tolerance_mx, oracle_rows, say
+from tests.gpu_util import assert_close, kv_tolerance_mx, say
 from workloads import C3, gen
 
 pytestmark = pytest.mark.gpu
@@ -20,7 +21,7 @@ if not torch.cuda.is_available():
 import hashed_gram_conditional_amd as E  # noqa: E402
 from workloads.device import bf16_bits, to_device  # noqa: E402
 from workloads.harness import GpuWorkload  # noqa: E402
-from tests.test_gpu_parity import S_A, S_B, _h_input, _h_values, _sample_tokens  # noqa: E402
+from tests.test_gpu_parity import S_A, S_B, _check_forward, _sample_tokens  # noqa: E402
 
 DEV = "cuda"
 
@@ -102,7 +103,7 @@ def test_project_mx_against_oracle(M, N, S):
     say(f"project_mx {M}x{N} S={S}")
     rows, codes, scales, e, w = _mx_case(M, N, S, M * 7 + N + S)
     exact = O.project(e, w)
-    tol = gemm_tolerance_mx(e, w, exact)
+    tol = kv_tolerance_mx(exact)
     for with_ws in (True, False):
         got = _project_mx(rows, codes, scales, M, N, S, with_ws)
         assert_close(got, exact, f"kv mx {M}x{N} S={S} ws={with_ws}", atol=0, rtol=0, extra=tol)
@@ -130,26 +131,7 @@ def test_project_mx_single_products_exact():
 
 
 def _check_forward_mx(gw, h_dev, gates_dev, tokens):
-    w = gw.w
-    rid, _ = oracle_rows(gw)
-    dead = gw.dead_np()
-    h_in = _h_input(gw).reshape(w.tokens, w.hc, w.dim)
-    wf = O.mx_values(*gw.wkv_mx_np)
-    res = O.forward_tokens(tokens, rid, dead, fetch_rows=gw.fetch_rows, table_rows=gw.rows,
-                           wkv=wf, q_w=gw.dense_np["q_w"], k_w=gw.dense_np["k_w"], h=h_in,
-                           hc=w.hc, dim=w.dim, eps=w.eps, clamp=w.gate_clamp, bf16=True)
-    tok = torch.from_numpy(np.asarray(tokens)).to(DEV)
-    a_got = gates_dev[tok].cpu().numpy().astype(np.float64)
-    h_got = _h_values(gw, h_dev.reshape(w.tokens, w.hc, w.dim)[tok])
-    # the projection's bounded difference enters the gate through k and the update through v
-    exact = O.project(res["e"], wf).reshape(len(tokens), w.hc + 1, w.dim)
-    tol = gemm_tolerance_mx(res["e"], wf, exact.reshape(len(tokens), -1))
-    tol = tol.reshape(len(tokens), w.hc + 1, w.dim)
-    extra_h = res["alpha"][:, :, None] * tol[:, None, w.hc, :]
-    assert_close(a_got, res["alpha"], f"{w.name} mx gates")
-    assert np.all(a_got[dead[tokens]] == 0.0)
-    assert np.array_equal(h_got[dead[tokens]], h_in[tokens][dead[tokens]])
-    assert_close(h_got, res["h_out"], f"{w.name} mx h", extra=extra_h)
+    return _check_forward(gw, h_dev, gates_dev, tokens, wkv=O.mx_values(*gw.wkv_mx_np), mx=True)
 
 
 @pytest.mark.parametrize("w", [S_A, S_B], ids=lambda w: w.name)
@@ -172,6 +154,6 @@ def test_forward_mx_prefill_sampled():
     E.engram_forward_mx(gw.params, gw.desc, gw.ids, None, None, gw.table, gw.w_codes,
                         gw.w_scales, gw.q_w, gw.k_w, gw.h, gates, ws, n)
     torch.cuda.synchronize()
-    _check_forward_mx(gw, gw.h, gates, _sample_tokens(gw, 96, 7))
+    _check_forward_mx(gw, gw.h, gates, _sample_tokens(gw, 2048, 7))
     del ws
     gw.free()

@@ -13,7 +13,8 @@ import numpy as np
 import pytest
 
 import oracle as O
-from tests.gpu_util import ATOL, RTOL, assert_close, gemm_tolerance, oracle_rows, oracle_setup, say
+from tests.gpu_util import (ATOL, RTOL, assert_close, check_forward_chunks, gemm_tolerance,
+                            oracle_rows, oracle_setup, say)
 from workloads import C0, C1, C2, C3, C4, gen
 
 pytestmark = pytest.mark.gpu
@@ -219,8 +220,24 @@ def test_gather_out_of_range_and_ragged():
         assert np.array_equal(bf16_bits(out), exp)
 
 
-def test_gather_c2_full_size_sampled():
-    say("C2 gather: table 24,003,916 x 264 B, 131072 tokens x 24 rows")
+def _dequant_unique_rows(seed, rows, chunk=65536):
+    """The oracle's dequantised rows of ``rows`` (regenerated from the counter
+    table chunk by chunk in worker threads), uint16 bf16 bits [len(rows), 256]."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    out = np.empty((len(rows), 256), dtype=np.uint16)
+
+    def one(lo):
+        r = rows[lo:lo + chunk]
+        out[lo:lo + len(r)] = O.dequant_rows_bf16(gen.table_rows(seed, r))
+
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(one, range(0, len(rows), chunk)))
+    return out
+
+
+def test_gather_c2_every_row():
+    say("C2 gather: table 24,003,916 x 264 B, 131072 tokens x 24 rows, every row")
     gw = GpuWorkload(C2)
     try:
         rows = torch.empty((C2.tokens, 24), dtype=torch.int64, device=DEV)
@@ -230,12 +247,16 @@ def test_gather_c2_full_size_sampled():
         torch.cuda.synchronize()
         exp_rows, _ = oracle_rows(gw)
         assert np.array_equal(rows.cpu().numpy(), exp_rows)
-        rng = np.random.default_rng(12)
-        sample = np.unique(np.concatenate([rng.integers(0, C2.tokens * 24, 6000),
-                                           np.arange(24), C2.tokens * 24 - 1 - np.arange(24)]))
-        got = bf16_bits(out[torch.from_numpy(sample).to(DEV)])
-        exp = O.gather_e4m3(gw.fetch_rows, exp_rows.reshape(-1)[sample].reshape(-1, 1), gw.rows)
-        assert np.array_equal(got, exp)
+        assert exp_rows.min() >= 0 and exp_rows.max() < gw.rows
+        uniq, inv = np.unique(exp_rows.reshape(-1), return_inverse=True)
+        say(f"  {len(uniq)} distinct rows of {exp_rows.size} looked up")
+        exp_u = _dequant_unique_rows(C2.table_seed, uniq)
+        got = bf16_bits(out)
+        step = 1 << 20
+        for lo in range(0, got.shape[0], step):
+            hi = min(lo + step, got.shape[0])
+            same = np.array_equal(got[lo:hi], exp_u[inv[lo:hi]])
+            assert same, f"dequantised rows differ in lookups [{lo}, {hi})"
     finally:
         gw.free()
         _cleanup()
@@ -482,43 +503,31 @@ def _h_input(gw):
     return h.astype(np.float64) if gw.f32 else O.bf16_bits_to_f64(h)
 
 
-def _check_forward(gw, h_out_dev, gates_dev, tokens, kv_dev=None):
-    """Oracle on ``tokens`` against the device results of a full forward."""
+def _wkv_f64(gw):
+    return gw.dense_np["wkv"].astype(np.float64) if gw.f32 else \
+        O.bf16_bits_to_f64(gw.dense_np["wkv"])
+
+
+def _host(t):
+    return t.cpu().numpy() if t.dtype == torch.float32 else bf16_bits(t)
+
+
+def _check_forward(gw, h_out_dev, gates_dev, tokens, kv_dev=None, wkv=None, mx=False):
+    """Oracle on ``tokens`` against the device results of a full forward: every
+    gate and stream element at the plain tolerance (with the counted kv-rounding
+    allowance), DEAD tokens' gates zero and streams bit-identical, and the
+    device's kv (when given) within the projection's bound."""
     w = gw.w
     rid, _ = oracle_rows(gw)
-    dead = gw.dead_np()
-    h_in = _h_input(gw).reshape(w.tokens, w.hc, w.dim)
-    res = O.forward_tokens(tokens, rid, dead, fetch_rows=gw.fetch_rows,
-                           table_f32=gw.dense_np.get("table"), table_rows=gw.rows,
-                           wkv=(gw.dense_np["wkv"] if gw.f32 else
-                                O.bf16_bits_to_f64(gw.dense_np["wkv"])),
-                           q_w=gw.dense_np["q_w"], k_w=gw.dense_np["k_w"], h=h_in, hc=w.hc,
-                           dim=w.dim, eps=w.eps, clamp=w.gate_clamp, bf16=not gw.f32)
-    tok_dev = torch.from_numpy(np.asarray(tokens)).to(DEV)
-    h_got = _h_values(gw, h_out_dev.reshape(w.tokens, w.hc, w.dim)[tok_dev])
-    a_got = gates_dev[tok_dev].cpu().numpy().astype(np.float64)
-    assert_close(a_got, res["alpha"], f"{w.name} gates")
-    d = dead[tokens]
-    assert np.all(a_got[d] == 0.0)
-    # DEAD rows are left bit-identical
-    assert np.array_equal(h_got[d], h_in[tokens][d])
-    # The device's kv may differ from the oracle's by the projection's bound
-    # (fp32 accumulation, then its own bf16 rounding; the oracle rounds the exact
-    # product, half an ulp away at most). That difference reaches h through
-    # alpha * v. The bound comes from the oracle's e and W alone.
-    wf = gw.dense_np["wkv"] if gw.f32 else O.bf16_bits_to_f64(gw.dense_np["wkv"])
-    exact = O.project(res["e"], wf).reshape(len(tokens), w.hc + 1, w.dim)
-    tol = gemm_tolerance(res["e"], wf, exact.reshape(len(tokens), -1),
-                         not gw.f32).reshape(exact.shape)
-    if kv_dev is not None:
-        kv_got = kv_dev.reshape(w.tokens, w.hc + 1, w.dim)[tok_dev]
-        kv_got = (kv_got.cpu().numpy().astype(np.float64) if gw.f32 else
-                  O.bf16_bits_to_f64(bf16_bits(kv_got)))
-        assert_close(kv_got, exact, f"{w.name} kv", atol=0, rtol=0, extra=tol)
-    dv = tol[:, w.hc, :] + (0.0 if gw.f32 else 2.0 ** -9) * np.abs(exact[:, w.hc, :])
-    extra = res["alpha"][:, :, None] * dv[:, None, :]
-    assert_close(h_got, res["h_out"], f"{w.name} h", extra=extra)
-    return res
+    h_in = gw.dense_np["h"].reshape(w.tokens, w.hc, w.dim)
+    return check_forward_chunks(
+        tokens=tokens, rid=rid, dead=gw.dead_np(), fetch_rows=gw.fetch_rows,
+        table_f32=gw.dense_np.get("table"), table_rows=gw.rows,
+        wkv=_wkv_f64(gw) if wkv is None else wkv, q_w=gw.dense_np["q_w"],
+        k_w=gw.dense_np["k_w"], h_in=h_in,
+        h_out=_host(h_out_dev).reshape(w.tokens, w.hc, w.dim), gates=gates_dev.cpu().numpy(),
+        kv=None if kv_dev is None else _host(kv_dev).reshape(w.tokens, -1), hc=w.hc,
+        dim=w.dim, eps=w.eps, clamp=w.gate_clamp, bf16=not gw.f32, mx=mx, name=w.name)
 
 
 def _run_stages(gw):
@@ -630,27 +639,29 @@ def test_forward_chunked_and_deterministic():
 
 
 def _sample_tokens(gw, n_random, seed):
+    """n_random seeded tokens, the first and the last, and every DEAD-span
+    boundary +-4."""
     w = gw.w
     rng = np.random.default_rng(seed)
     pick = set(rng.integers(0, w.tokens, n_random).tolist()) | {0, w.tokens - 1}
     for b, spans in enumerate(gw.spans):
         for a, e in spans:
-            for t in (a - 2, a - 1, a, e - 1, e, e + 1, e + 2, e + 3):
-                if 0 <= t < w.seq:
+            for t in range(a - 4, e + 5):
+                if 0 <= t < w.seq and (t < a + 5 or t >= e - 4):
                     pick.add(b * w.seq + t)
     return np.array(sorted(pick))
 
 
-def test_forward_c3_full_size_sampled():
+def test_forward_c3_every_token():
     say("C3 forward: 4x8192 tokens, 6.34 GB table, wkv [25600, 6144], h [4,8192,4,5120]")
     gw = GpuWorkload(C3)
     try:
         h0 = gw.h.clone()
         rows, e, kv, gates = _run_stages(gw)
-        tokens = _sample_tokens(gw, 24, 31)
-        say(f"  oracle on {len(tokens)} sampled tokens")
-        _check_forward(gw, gw.h, gates, tokens, kv_dev=kv)
         del rows, e
+        say(f"  oracle on all {C3.tokens} tokens")
+        _check_forward(gw, gw.h, gates, np.arange(C3.tokens), kv_dev=kv)
+        del kv
         h1 = h0
         g1 = _forward(gw, h1)
         assert torch.equal(h1.view(torch.int16), gw.h.view(torch.int16))
@@ -661,14 +672,12 @@ def test_forward_c3_full_size_sampled():
 
 
 def test_forward_c4_decode_full_table():
-    say("C4 decode: 256 x 1 token, 384,006,168-row (101.4 GB) table")
+    say("C4 decode: 256 x 1 token, 384,006,168-row (101.4 GB) table, every token")
     gw = GpuWorkload(C4)
     try:
         h0 = gw.h.clone()
         rows, e, kv, gates = _run_stages(gw)
-        rng = np.random.default_rng(5)
-        tokens = np.unique(np.concatenate([[0, 1, 255], rng.integers(0, 256, 29)]))
-        _check_forward(gw, gw.h, gates, tokens, kv_dev=kv)
+        _check_forward(gw, gw.h, gates, np.arange(C4.tokens), kv_dev=kv)
         assert gates[0].abs().sum().item() == 0.0
         assert torch.equal(gw.h[0].view(torch.int16), h0[0].view(torch.int16))
         # the fused decode step: same bits, and the history after the token
