@@ -25,7 +25,8 @@ GATE_PLAIN = 1
 MAX_CONV_TAPS = 8
 MAX_CONV_HISTORY = 64
 
-OK, EINVAL, EVOCAB, EMULT, ESHAPE, EWORKSPACE, EHIP, EPRIMES = 0, -1, -2, -3, -4, -5, -6, -7
+OK, EINVAL, EVOCAB, EMULT, ESHAPE, EWORKSPACE, EHIP, EPRIMES, ESCRATCH = \
+    0, -1, -2, -3, -4, -5, -6, -7, -8
 
 
 class EngramError(RuntimeError):
@@ -128,6 +129,8 @@ def _load():
         "engram_forward_mx_workspace_size": (SZ, [P, P]),
         "engram_forward_mx": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "engram_forward": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "engram_forward_static": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, P, P]),
+        "engram_forward_static_max_bytes": (SZ, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -317,6 +320,19 @@ def engram_forward(params: HashParams, desc: ForwardDesc, ids, hist_in, hist_out
                               _ptr(q_w), _ptr(k_w), _ptr(h), _ptr(gate_out),
                               _ptr(workspace), workspace_bytes, _stream(stream)),
            "engram_forward")
+
+
+def engram_forward_static(params: HashParams, desc: ForwardDesc, ids, hist_in, hist_out, table,
+                          wkv, q_w, k_w, h, gate_out, stream=None):
+    _check(LIB.engram_forward_static(ctypes.byref(params), ctypes.byref(desc), _ptr(ids),
+                                     _ptr(hist_in), _ptr(hist_out), _table_ptr(table),
+                                     _ptr(wkv), _ptr(q_w), _ptr(k_w), _ptr(h), _ptr(gate_out),
+                                     _stream(stream)),
+           "engram_forward_static")
+
+
+def engram_forward_static_max_bytes() -> int:
+    return int(LIB.engram_forward_static_max_bytes())
 
 
 def engram_gather_rows(table, table_rows: int, row_ids, n_ids: int, out, stream=None):

@@ -4,6 +4,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "common.h"
 
 namespace {
@@ -202,6 +205,18 @@ size_t folded_scales_bytes(const engram_forward_desc *d) {
   return align256((size_t)d->hc * (size_t)d->dim * sizeof(float));
 }
 
+// Bytes of engram_forward's workspace before the projection's own part: row
+// ids, e, kv and the folded gate scales.
+size_t forward_base_bytes(const engram_hash_params *params, const engram_forward_desc *desc) {
+  const int64_t ntok = desc->batch * desc->seq;
+  const int64_t S = (int64_t)(params->max_ngram - 1) * params->heads;
+  const size_t esz = desc->row_format == ENGRAM_ROW_F32 ? 4 : 2;
+  const int64_t in_dim = S * desc->row_dim;
+  const int64_t out_dim = (int64_t)(desc->hc + 1) * desc->dim;
+  return align256((size_t)ntok * S * 8) + align256((size_t)ntok * in_dim * esz) +
+         align256((size_t)ntok * out_dim * esz) + folded_scales_bytes(desc);
+}
+
 size_t gate_conv_workspace(const engram_forward_desc *d) {
   return align256((size_t)(d->batch * d->seq) * (size_t)(d->hc + 1) * sizeof(float));
 }
@@ -252,6 +267,8 @@ const char *engram_status_string(int status) {
     case ENGRAM_EWORKSPACE: return "workspace missing or too small";
     case ENGRAM_EHIP: return "HIP launch failed";
     case ENGRAM_EPRIMES: return "bad primes/offsets or rows beyond the table";
+    case ENGRAM_ESCRATCH:
+      return "the call needs more scratch than engram_forward_static's static array holds";
     default: return "unknown status";
   }
 }
@@ -565,8 +582,7 @@ size_t engram_forward_workspace_size(const engram_hash_params *params,
   const size_t esz = f32 ? 4 : 2;
   const int64_t in_dim = S * desc->row_dim;
   const int64_t out_dim = (int64_t)(desc->hc + 1) * desc->dim;
-  return align256((size_t)ntok * S * 8) + align256((size_t)ntok * in_dim * esz) +
-         align256((size_t)ntok * out_dim * esz) + folded_scales_bytes(desc) +
+  return forward_base_bytes(params, desc) +
          engram_project_workspace_size(ntok, in_dim, out_dim, f32 ? 1 : 0);
 }
 
@@ -575,12 +591,15 @@ size_t engram_forward_workspace_size(const engram_hash_params *params,
 namespace {
 
 // engram_forward and engram_forward_conv: steps 1-4, then the gate alone
-// (conv == NULL) or the gate and the short convolution branch.
+// (conv == NULL) or the gate and the short convolution branch. With
+// `gemm_ws_optional` the workspace need only hold forward_base_bytes; the
+// projection then splits K over the CUs only if its partial tiles fit in the
+// rest (otherwise it runs 128-wide tiles, the wide kernel's bits).
 int forward_impl(const engram_hash_params *params, const engram_forward_desc *desc,
                  const engram_short_conv *conv, const int32_t *ids, const int32_t *hist_in,
                  int32_t *hist_out, const void *table, const void *wkv, const float *q_w,
                  const float *k_w, void *h, float *gate_out, void *workspace,
-                 size_t workspace_bytes, hipStream_t stream) {
+                 size_t workspace_bytes, hipStream_t stream, bool gemm_ws_optional = false) {
   int rc = check_hash_params(params);
   if (rc != ENGRAM_OK) return rc;
   rc = check_desc(desc);
@@ -602,7 +621,8 @@ int forward_impl(const engram_hash_params *params, const engram_forward_desc *de
     if (!aligned(ids, 4) || !aligned(table, 16) || !aligned(wkv, 16) || !aligned(q_w, 16) ||
         !aligned(k_w, 16) || !aligned(h, 16) || !aligned(gate_out, 4))
       return ENGRAM_EINVAL;
-    const size_t need = engram_forward_workspace_size(params, desc) +
+    const size_t need = (gemm_ws_optional ? forward_base_bytes(params, desc)
+                                          : engram_forward_workspace_size(params, desc)) +
                         (conv != nullptr ? gate_conv_workspace(desc) : 0);
     if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
       return ENGRAM_EWORKSPACE;
@@ -763,6 +783,71 @@ int engram_forward_mx(const engram_hash_params *params, const engram_forward_des
                            fold ? nullptr : k_w, h, gate_out, nullptr, ntok, desc->hc,
                            desc->dim, desc->eps, desc->gate_clamp, desc->gate_mode, stream);
   return hip_status(err);
+}
+
+}  // extern "C"
+
+// ---- engram_forward_static: the layer with no workspace argument ----------------
+// The scratch of engram_forward (row ids, e, kv, folded gate scales, the
+// projection's split-K partials) lives in this file-scope array instead of a
+// caller's buffer. Every GPU the library runs on holds its own copy for the life
+// of the process. In host code `scratch` names a host-side stand-in, not a
+// device address: host code only ever uses the address hipGetSymbolAddress
+// returns for the current device, kept per device below.
+static __device__ __align__(256) unsigned char scratch[ENGRAM_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// The device address of `scratch` on the stream's device, looked up once per
+// device with that device current. The stream must belong to the current device.
+int static_scratch(hipStream_t stream, void **out) {
+  int dev = -1, sdev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  e = hipStreamGetDevice(stream, &sdev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev != sdev || dev < 0 || dev >= kMaxScratchDevices) return ENGRAM_EINVAL;
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr) return hip_status(e == hipSuccess ? hipErrorUnknown : e);
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return ENGRAM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t engram_forward_static_max_bytes(void) { return ENGRAM_STATIC_SCRATCH_BYTES; }
+
+int engram_forward_static(const engram_hash_params *params, const engram_forward_desc *desc,
+                          const int32_t *ids, const int32_t *hist_in, int32_t *hist_out,
+                          const void *table, const void *wkv, const float *q_w,
+                          const float *k_w, void *h, float *gate_out, hipStream_t stream) {
+  int rc = check_hash_params(params);
+  if (rc != ENGRAM_OK) return rc;
+  rc = check_desc(desc);
+  if (rc != ENGRAM_OK) return rc;
+  if (forward_base_bytes(params, desc) > (size_t)ENGRAM_STATIC_SCRATCH_BYTES)
+    return ENGRAM_ESCRATCH;
+  void *ws = nullptr;
+  if ((rc = static_scratch(stream, &ws)) != ENGRAM_OK) return rc;
+  // Nothing in the scratch has to start at zero: every kernel writes what a later
+  // one reads (the split-K fixup reads only the partial tiles of this call).
+  return forward_impl(params, desc, nullptr, ids, hist_in, hist_out, table, wkv, q_w, k_w, h,
+                      gate_out, ws, ENGRAM_STATIC_SCRATCH_BYTES, stream,
+                      /*gemm_ws_optional=*/true);
 }
 
 }  // extern "C"

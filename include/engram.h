@@ -80,6 +80,9 @@ extern "C" {
 #define ENGRAM_ROW_DIM_E4M3 256
 #define ENGRAM_MAX_CONV_TAPS 8    /* kernel size w of the short convolution */
 #define ENGRAM_MAX_CONV_HISTORY 64 /* (w - 1) * dilation */
+/* Scratch array of engram_forward_static, per GPU: 64 MiB, enough for a decode
+ * step of up to 1024 tokens at hc 4 x 5120 with 24 segments. */
+#define ENGRAM_STATIC_SCRATCH_BYTES (64ull << 20)
 
 typedef enum engram_status {
   ENGRAM_OK = 0,
@@ -89,8 +92,10 @@ typedef enum engram_status {
   ENGRAM_ESHAPE = -4,     /* inconsistent shapes                                  */
   ENGRAM_EWORKSPACE = -5, /* workspace missing or too small                       */
   ENGRAM_EHIP = -6,       /* a HIP launch failed                                  */
-  ENGRAM_EPRIMES = -7     /* prime < 2 or >= 2^32, offsets not the prefix sums,
+  ENGRAM_EPRIMES = -7,    /* prime < 2 or >= 2^32, offsets not the prefix sums,
                              or rows beyond the table                             */
+  ENGRAM_ESCRATCH = -8    /* engram_forward_static: the call needs more scratch
+                             than ENGRAM_STATIC_SCRATCH_BYTES                     */
 } engram_status;
 
 typedef enum engram_row_format {
@@ -429,6 +434,37 @@ int engram_forward(const engram_hash_params *params, const engram_forward_desc *
                    const void *table, const void *wkv, const float *q_w,
                    const float *k_w, void *h, float *gate_out, void *workspace,
                    size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * engram_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). It makes engram_forward's launches, taking their
+ * scratch (row ids, e, kv, folded gate scales) from a static device array of
+ * ENGRAM_STATIC_SCRATCH_BYTES that every GPU the library runs on holds until
+ * the process ends. The call itself allocates nothing. Its results are
+ * engram_forward's bits, except where engram_forward would split the
+ * projection's K over the CUs (more than 256 tokens but fewer 256 x 256 tiles
+ * than CUs): those partial tiles do not fit, so the projection runs 128-wide
+ * tiles over the whole K instead (the bits of a call with many tokens), which
+ * can differ from the split sum in the last bits of kv.
+ *   arguments as engram_forward, without workspace / workspace_bytes
+ *   stream    must belong to the current device
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (two streams, two host threads)
+ * race. Nothing in the array needs to start at zero.
+ * Errors: as engram_forward; ENGRAM_ESCRATCH when the row ids, e, kv and folded
+ * scales of the call (engram_forward_workspace_size without the projection's
+ * part) exceed ENGRAM_STATIC_SCRATCH_BYTES (checked before any launch);
+ * ENGRAM_EINVAL when the stream is not on the current device.
+ */
+int engram_forward_static(const engram_hash_params *params, const engram_forward_desc *desc,
+                          const int32_t *ids, const int32_t *hist_in, int32_t *hist_out,
+                          const void *table, const void *wkv, const float *q_w,
+                          const float *k_w, void *h, float *gate_out, hipStream_t stream);
+
+/* [host] ENGRAM_STATIC_SCRATCH_BYTES, the largest workspace engram_forward_static
+ * can stand in for. */
+size_t engram_forward_static_max_bytes(void);
 
 /*
  * The whole layer with the block-scaled FP8 weight: engram_hash,

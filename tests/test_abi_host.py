@@ -308,3 +308,20 @@ def test_fold_and_folded_gate_validation():
     assert gf(E.forward_desc(2, 8, 9, 64, 100, 0, 256), 0x3000) == E.ESHAPE
     assert L.engram_gate_folded(ctypes.byref(d), 0x1000, 0, 0x2000, 0x3000, 0x4000, None,
                                 None) == E.EINVAL                    # raw_vocab < 1
+
+
+def test_forward_static_refuses_calls_beyond_its_array():
+    """engram_forward_static checks its scratch need on the host, before it
+    looks up the array or launches anything."""
+    p = _params(C1)
+    L = E.LIB
+    cap = E.engram_forward_static_max_bytes()
+    assert cap == 64 << 20
+    per_token = 24 * 8 + 6144 * 2 + 25600 * 2
+    args = [0x1000, None, None, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None, None]
+    fits = cap // per_token - 4
+    big = E.forward_desc(fits + 64, 1, 4, 5120, 384_006_168, 0, 256)
+    assert L.engram_forward_static(ctypes.byref(p), ctypes.byref(big), *args) == E.ESCRATCH
+    assert "static array" in E.status_string(E.ESCRATCH)
+    bad = E.forward_desc(4, 8192, 9, 5120, 384_006_168, 0, 256)      # hc > 8
+    assert L.engram_forward_static(ctypes.byref(p), ctypes.byref(bad), *args) == E.ESHAPE
