@@ -70,10 +70,12 @@ def measured_traffic(kernel: str, sources):
     return None
 
 
-def cpu_baseline(gw, target_s: float = 10.0, max_tokens: int = 8192):
+def cpu_baseline(gw, host_table, target_s: float = 10.0, max_tokens: int = 8192):
     """The oracle as it stands, timed on the host on a bounded sample: all five
     steps for the first n tokens of sequence 0 (table rows materialised in host
-    RAM beforehand, so the gather reads memory rather than regenerating rows)."""
+    RAM beforehand, so the gather reads memory rather than regenerating rows),
+    then each stage on its own workload (cpu_stages). ``host_table`` is the
+    6.34 GB table as a host numpy array."""
     import oracle as O
     from workloads import gen
 
@@ -129,37 +131,140 @@ def cpu_baseline(gw, target_s: float = 10.0, max_tokens: int = 8192):
                   "sample": f"first {n1} tokens, {dt1:.2f} s with BLAS limited to one thread"}
     except Exception as exc:                        # threadpoolctl missing or refused
         log(f"single-thread oracle run skipped: {exc}")
-    # the hash and gather stages alone: the hash over every prefill token, the
-    # gather (and dequantisation) over the rows of the first 2048 tokens
-    ids_all = np.ascontiguousarray(gw.ids_np)
-    t0 = time.perf_counter()
-    rid_all, _ = O.hash_rows(ids_all, gw.token_map_np, w.compressed_vocab, gw.pad, gw.mult,
-                             primes, offs, w.max_ngram, w.heads)
-    dt_hash = time.perf_counter() - t0
-    n_g = min(2048, rid_all.shape[0])
-    sub = rid_all[:n_g]
-    need = np.unique(sub)
-    host_rows = gen.table_rows(w.table_seed, need)
-    t0 = time.perf_counter()
-    O.gather_e4m3(lambda r: host_rows[np.searchsorted(need, r)], sub, R)
-    dt_gather = time.perf_counter() - t0
-    stages = {"hash": {"tokens_per_s": round(rid_all.shape[0] / dt_hash, 1),
-                       "sample": f"all {rid_all.shape[0]} prefill tokens, {dt_hash:.3f} s"},
-              "gather": {"tokens_per_s": round(n_g / dt_gather, 1),
-                         "GBps": round(n_g * GATHER_BYTES_PER_TOKEN / dt_gather / 1e9, 4),
-                         "sample": f"rows of the first {n_g} tokens, pre-read into host RAM, "
-                                   f"{dt_gather:.2f} s"}}
-    model = ""
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
-    except OSError:
-        pass
+    stages = cpu_stages(gw, host_table)
+    host = host_description()
     return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {n} tokens of sequence 0 of the same prefill workload, all five "
                       f"steps in fp64 numpy, table rows pre-read into host RAM; {dt:.2f} s "
-                      f"on {os.cpu_count()} host CPUs (BLAS threads {cores})",
-            "cpu_model": model, "single_thread": single, "stages": stages}
+                      f"with BLAS on {cores} threads",
+            "cpu_model": host["cpu_model"], "host": host, "single_thread": single,
+            "stages": stages}
+
+
+def host_description():
+    """nproc, the CPUs this process may run on, and /proc/cpuinfo's description of
+    the first CPU (model name, family, model, stepping, cache size)."""
+    info = {}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if not line.strip():
+                    break
+                k, _, v = line.partition(":")
+                info[k.strip()] = v.strip()
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"nproc": os.cpu_count(), "usable_cpus": affinity,
+            "cpu_model": info.get("model name", ""),
+            "cpu_family": info.get("cpu family"), "cpu_model_number": info.get("model"),
+            "stepping": info.get("stepping"), "cache_size": info.get("cache size"),
+            "vendor": info.get("vendor_id")}
+
+
+def _grow(run, target_s, start, cap):
+    """Double the sample until one run takes a quarter of target_s (or cap)."""
+    n = start
+    dt = run(n)
+    while dt < target_s / 4 and n < cap:
+        n = min(cap, int(n * max(2.0, min(16.0, target_s / max(dt, 1e-3)))))
+        dt = run(n)
+    return n, dt
+
+
+def cpu_stages(gw, host_table):
+    """The oracle's stages on their own workloads, all cores and one thread:
+    the hash over all 8 x 4096 tokens of the hash workload (C1 setup, primes from
+    16,000,000); the gather over the gather workload's tokens reading the 6.34 GB
+    table materialised in host RAM (a random row gather from memory, then the
+    dequantisation); the decode step (256 tokens with history against the
+    101.4 GB table), whose rows are regenerated from the counter generator since
+    that table does not fit host RAM. Parallel runs give each worker thread its
+    own contiguous range of tokens (tokens are independent)."""
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+    from workloads import C1, C2, C4, gen
+
+    workers = min(16, os.cpu_count() or 1)
+    out = {}
+    # hash: C1
+    tm, mult = gen.hash_setup(C1)
+    primes = O.primes_from(C1.prime_base, C1.segments)
+    offs, _ = O.segment_offsets(primes)
+    ids, _ = gen.token_ids(C1)
+    t0 = time.perf_counter()
+    O.hash_rows(ids, tm, C1.compressed_vocab, int(tm[0]), mult, primes, offs, C1.max_ngram,
+                C1.heads)
+    dt = time.perf_counter() - t0
+    out["hash"] = {"tokens_per_s": round(C1.tokens / dt, 1),
+                   "GBps": round(C1.tokens * 196 / dt / 1e9, 4), "cores": 1,
+                   "sample": f"all {C1.tokens} tokens of the 8 x 4096 hash workload, {dt:.3f} s"}
+    # gather: C2 over the materialised table
+    w = gw.w
+    R = gw.rows
+    ids2, _ = gen.token_ids(C2)
+    rid2, _ = O.hash_rows(ids2, gw.token_map_np, w.compressed_vocab, gw.pad, gw.mult,
+                          O.primes_from(C2.prime_base, C2.segments),
+                          O.segment_offsets(O.primes_from(C2.prime_base, C2.segments))[0],
+                          C2.max_ngram, C2.heads)
+    fetch = lambda r: host_table[r]
+
+    def gather_run(n, threads):
+        chunk = max(1, -(-n // threads))
+        t0 = time.perf_counter()
+        if threads == 1:
+            O.gather_e4m3(fetch, rid2[:n], R)
+        else:
+            with ThreadPoolExecutor(threads) as ex:
+                list(ex.map(lambda lo: O.gather_e4m3(fetch, rid2[lo:min(n, lo + chunk)], R),
+                            range(0, n, chunk)))
+        return time.perf_counter() - t0
+
+    g = {}
+    for label, threads in (("all_cores", workers), ("single_thread", 1)):
+        n, dt = _grow(lambda k: gather_run(k, threads), 4.0, 256, C2.tokens)
+        g[label] = {"tokens_per_s": round(n / dt, 1),
+                    "GBps": round(n * GATHER_BYTES_PER_TOKEN / dt / 1e9, 4), "cores": threads,
+                    "sample": f"first {n} tokens of the 16 x 8192 gather workload ({n * 24} "
+                              f"rows), {dt:.2f} s"}
+    g["table"] = "24,003,916 x 264 B (6.34 GB) in host RAM, rows read by fancy indexing"
+    out["gather"] = g
+    # decode: C4, rows regenerated
+    tm4, mult4 = gen.hash_setup(C4)
+    p4 = O.primes_from(C4.prime_base, C4.segments)
+    o4, R4 = O.segment_offsets(p4)
+    ids4, _ = gen.token_ids(C4)
+    hist4 = gen.history(C4, tm4)
+    d4 = gen.dense_inputs(C4)
+    wkv4 = O.bf16_bits_to_f64(d4["wkv"])
+    h4 = O.bf16_bits_to_f64(d4["h"].reshape(C4.tokens, C4.hc, C4.dim))
+    dead4 = ids4.reshape(-1) < 0
+
+    def decode_run():
+        t0 = time.perf_counter()
+        rid4, _ = O.hash_rows(ids4, tm4, C4.compressed_vocab, int(tm4[0]), mult4, p4, o4,
+                              C4.max_ngram, C4.heads, hist=hist4)
+        O.forward_tokens(np.arange(C4.tokens), rid4, dead4,
+                         fetch_rows=lambda r: gen.table_rows(C4.table_seed, r), table_rows=R4,
+                         wkv=wkv4, q_w=d4["q_w"], k_w=d4["k_w"], h=h4, hc=C4.hc, dim=C4.dim,
+                         eps=C4.eps, clamp=C4.gate_clamp, bf16=True)
+        return time.perf_counter() - t0
+
+    dt = decode_run()
+    with threadpool_limits(limits=1):
+        dt1 = decode_run()
+    out["decode"] = {"tokens_per_s": round(C4.tokens / dt, 1), "cores": workers,
+                     "single_thread_tokens_per_s": round(C4.tokens / dt1, 1),
+                     "sample": f"one decode step, 256 tokens with history, all five steps; "
+                               f"{dt:.2f} s with BLAS on all threads, {dt1:.2f} s on one",
+                     "note": "rows regenerated from the counter generator (the 101.4 GB "
+                             "table does not fit host RAM)"}
+    del wkv4, h4, d4
+    return out
 
 
 def main():
@@ -298,13 +403,22 @@ def main():
     out["gather"].update(detail)
     out["gather"]["frac_of_torch_copy"] = round(gather_gbps / detail["torch_copy_GBps"], 4)
     out["hash_steady"] = hash_steady
+    out["gather_c2"] = gather_c2_bench(gw, max(args.steps, 10))
+    out["gather_c2"]["frac_of_torch_copy_cold"] = round(
+        out["gather_c2"]["cold"]["achieved"] / detail["torch_copy_GBps"], 4)
     out["short_conv"] = conv_prefill_bench(gw, rows, e, kv, gates, args.steps, args.warmup)
-    out["host_tier"] = host_tier_bench(gw, rows, e, kv, gates, args.steps, args.warmup)
+    t_pin = time.perf_counter()
+    host = torch.empty(gw.table.shape, dtype=torch.uint8, pin_memory=True)
+    host.copy_(gw.table)
+    torch.cuda.synchronize()
+    log(f"host table pinned and filled in {time.perf_counter() - t_pin:.1f} s")
+    out["host_tier"] = host_tier_bench(gw, host, rows, e, kv, gates, args.steps, args.warmup)
     out["hash_layers"] = hash_layers_bench(max(args.steps, 20))
     out["fp8_wkv"] = fp8_prefill_bench(gw, args.steps, args.warmup)
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample ...")
-        out["cpu_baseline"] = cpu_baseline(gw)
+        log("timing the CPU oracle on bounded samples ...")
+        out["cpu_baseline"] = cpu_baseline(gw, host.numpy())
+    del host
     if not args.no_decode:
         del rows, e, kv, gates, ws
         gw.free()
@@ -383,7 +497,7 @@ def conv_prefill_bench(gw, rows, e, kv, gates, steps: int, warmup: int):
                           "bytes_per_token": bytes_per_token}}
 
 
-def host_tier_bench(gw, rows, e, kv, gates, steps: int, warmup: int):
+def host_tier_bench(gw, host, rows, e, kv, gates, steps: int, warmup: int):
     """The prefill layer with its table (6.34 GB) in pinned host memory. The
     gather kernels read the rows over the host link. (1) Lookups alone: all
     32768 tokens' rows (raw and dequantised) and one 256-token decode-sized
@@ -398,11 +512,6 @@ def host_tier_bench(gw, rows, e, kv, gates, steps: int, warmup: int):
     w = gw.w
     T, S = w.tokens, w.segments
     K_in, N_out = S * w.row_dim, (w.hc + 1) * w.dim
-    t0 = time.perf_counter()
-    host = torch.empty(gw.table.shape, dtype=torch.uint8, pin_memory=True)
-    host.copy_(gw.table)
-    torch.cuda.synchronize()
-    log(f"host table pinned and filled in {time.perf_counter() - t0:.1f} s")
     main = torch.cuda.current_stream()
     raw = torch.empty((T, S, 264), dtype=torch.uint8, device="cuda")
 
@@ -467,7 +576,7 @@ def host_tier_bench(gw, rows, e, kv, gates, steps: int, warmup: int):
     nxt = run(steps, nxt)
     torch.cuda.synchronize()
     ms = 1e3 * (time.perf_counter() - t0) / steps
-    del host, raw, e_buf, r_buf, pws
+    del raw, e_buf, r_buf, pws
     return {"workload": "prefill layer forward as above with the 6.34 GB table in pinned host "
                         "memory: each step's rows are gathered over the host link by the GPU "
                         "during the previous step's projection (two buffers, two streams)",
@@ -541,6 +650,70 @@ def gather_detail(gw, rows, e, reps: int):
              "us": round(hash_ms * 1e3, 1), "tokens_per_s": round(tokens / (hash_ms * 1e-3), 1),
              "bytes_per_token": hash_bytes,
              "achieved_GBps": round(hash_bytes * tokens / (hash_ms * 1e-3) / 1e9, 1)})
+
+
+def gather_c2_bench(gw, reps: int):
+    """engram_gather at the gather workload's own size: 16 x 8192 Zipf tokens
+    hashed against the same 24,003,916-row table (the gather workload and the
+    prefill share the table's seed and primes), 3,145,728 rows of 264 B read
+    and 1.61 GB of bf16 written per call. Warm: back-to-back calls; cold: a 1 GiB
+    scratch buffer written before every call, flushing the L2s and the 256 MB
+    Infinity Cache. Each figure is the median over ``reps`` calls timed with HIP
+    events on the launch stream."""
+    import statistics
+    import torch
+    import hashed_gram_conditional_amd as E
+    from workloads import C2, C3, gen
+    from workloads.device import to_device
+
+    assert (C2.table_seed, C2.prime_base, C2.setup_seed) == \
+        (C3.table_seed, C3.prime_base, C3.setup_seed)
+    w = C2
+    T, S = w.tokens, w.segments
+    ids_np, _ = gen.token_ids(w)
+    ids = to_device(ids_np)
+    rows = torch.empty((T, S), dtype=torch.int64, device="cuda")
+    out = torch.empty((T * S, 256), dtype=torch.bfloat16, device="cuda")
+    E.engram_hash(gw.params, ids, w.batch, w.seq, None, None, rows)
+    torch.cuda.synchronize()
+    distinct = int(torch.unique(rows).numel())
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    run = lambda: E.engram_gather(gw.table, gw.rows, gw.row_format, w.row_dim, rows, T * S, out)
+
+    def timed_once():
+        a.record(stream)
+        run()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    warm = statistics.median(timed_once() for _ in range(reps))
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    cold = []
+    for _ in range(reps):
+        flush.fill_(3)
+        cold.append(timed_once())
+    cold_ms = statistics.median(cold)
+    del flush, out, rows, ids
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    nbytes = GATHER_BYTES_PER_TOKEN * T
+    gw_ = lambda ms: nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "gather + dequant: 16 x 8192 Zipf tokens with 2 DEAD spans of 256 per "
+                        "sequence, 24 rows each from the 24,003,916 x 264 B table (6.34 GB), "
+                        "bf16 [131072, 6144] written",
+            "kernel": "gather_e4m3_kernel (engram_gather)", "bytes_per_token": GATHER_BYTES_PER_TOKEN,
+            "algorithmic_bytes": nbytes, "distinct_rows": distinct, "lookups": T * S,
+            "warm": {"ms": round(warm, 4), "achieved": round(gw_(warm), 1),
+                     "frac": round(gw_(warm) / HBM_PEAK_GBPS, 4)},
+            "cold": {"ms": round(cold_ms, 4), "achieved": round(gw_(cold_ms), 1),
+                     "frac": round(gw_(cold_ms) / HBM_PEAK_GBPS, 4),
+                     "flush": "1 GiB scratch written before each call"},
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
 
 
 def fp8_prefill_bench(gw, steps: int, warmup: int):
