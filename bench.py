@@ -267,6 +267,19 @@ def cpu_stages(gw, host_table):
     return out
 
 
+def copy_calibration(mib: int):
+    """One device-to-device copy of ``mib`` MiB: the counter reading of a copy of
+    known size scales FETCH_SIZE and WRITE_SIZE to bytes."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,6 +291,8 @@ def main():
                     help="skip the decode-step measurement on the 101 GB table")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode-step measurement (profiling its kernels)")
+    ap.add_argument("--gather-only", action="store_true",
+                    help="only the gather workload's measurement (profiling its kernel)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -295,6 +310,13 @@ def main():
     if args.decode_only:
         print(json.dumps({"decode": decode_bench(args.steps, args.warmup)}), flush=True)
         return
+    if args.gather_only:
+        from workloads import C2
+        if args.copy_calibration_mib:
+            copy_calibration(args.copy_calibration_mib)
+        print(json.dumps({"gather_c2": gather_c2_bench(GpuWorkload(C2), args.steps)}),
+              flush=True)
+        return
     t_setup = time.perf_counter()
     gw = GpuWorkload(C3)
     w = gw.w
@@ -309,13 +331,7 @@ def main():
     log(f"setup {time.perf_counter() - t_setup:.1f} s: {T} tokens, table {gw.rows} rows")
 
     if args.copy_calibration_mib:
-        n = args.copy_calibration_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(args.copy_calibration_mib)
 
     stream = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
@@ -591,7 +607,7 @@ def host_tier_bench(gw, host, rows, e, kv, gates, steps: int, warmup: int):
 def gather_detail(gw, rows, e, reps: int):
     """Beside the warm (back-to-back) gather: torch's device-to-device copy rate, the
     same gather with the L2s and the 256 MB Infinity Cache flushed before every
-    rep by writing a 1 GiB scratch buffer, and engram_hash over 32 x the prefill
+    rep by reading a 1 GiB buffer, and engram_hash over 32 x the prefill
     ids in one call (the steady-state hash rate, free of launch latency)."""
     import statistics
     import torch
@@ -617,12 +633,13 @@ def gather_detail(gw, rows, e, reps: int):
     copy_ms = statistics.median(timed_once(lambda: dst.copy_(src)) for _ in range(5))
     copy_gbps = 2 * n / (copy_ms * 1e-3) / 1e9
     del src
+    sink = torch.empty((), dtype=torch.uint8, device="cuda")
     cold = []
     for _ in range(reps):
-        dst.fill_(2)
+        torch.amax(dst, dim=0, out=sink)
         cold.append(timed_once(lambda: E.engram_gather(gw.table, gw.rows, gw.row_format,
                                                         w.row_dim, rows, T * S, e)))
-    del dst
+    del dst, sink
     cold_ms = statistics.median(cold)
     cold_gbps = GATHER_BYTES_PER_TOKEN * T / (cold_ms * 1e-3) / 1e9
 
@@ -644,7 +661,7 @@ def gather_detail(gw, rows, e, reps: int):
                            "of 5 (a reference rate, not the HBM peak)",
              "cold": {"ms": round(cold_ms, 4), "achieved": round(cold_gbps, 1),
                       "frac": round(cold_gbps / HBM_PEAK_GBPS, 4),
-                      "flush": "1 GiB scratch written before each rep"}},
+                      "flush": "1 GiB read before each rep (caches evicted, clean)"}},
             {"workload": f"engram_hash over 32 x the prefill ids ({B32} x {w.seq} = {tokens} "
                          f"tokens) in one call",
              "us": round(hash_ms * 1e3, 1), "tokens_per_s": round(tokens / (hash_ms * 1e-3), 1),
@@ -656,10 +673,13 @@ def gather_c2_bench(gw, reps: int):
     """engram_gather at the gather workload's own size: 16 x 8192 Zipf tokens
     hashed against the same 24,003,916-row table (the gather workload and the
     prefill share the table's seed and primes), 3,145,728 rows of 264 B read
-    and 1.61 GB of bf16 written per call. Warm: back-to-back calls; cold: a 1 GiB
-    scratch buffer written before every call, flushing the L2s and the 256 MB
-    Infinity Cache. Each figure is the median over ``reps`` calls timed with HIP
-    events on the launch stream."""
+    and 1.61 GB of bf16 written per call. Warm: back-to-back calls. Cold: a
+    1 GiB buffer read before every call (a max-reduction), which evicts the L2s
+    and the 256 MB Infinity Cache and leaves them holding clean lines. Cold,
+    dirty caches: the same buffer written instead, so the caches hold up to
+    ~0.27 GB of another kernel's dirty lines that the timed call must write back
+    to HBM. Each figure is the median over ``reps`` calls timed with HIP events
+    on the launch stream."""
     import statistics
     import torch
     import hashed_gram_conditional_amd as E
@@ -692,13 +712,18 @@ def gather_c2_bench(gw, reps: int):
         run()
     torch.cuda.synchronize()
     warm = statistics.median(timed_once() for _ in range(reps))
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    cold = []
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(3)
+    sink = torch.empty((), dtype=torch.uint8, device="cuda")
+    cold, dirty = [], []
     for _ in range(reps):
-        flush.fill_(3)
+        torch.amax(flush, dim=0, out=sink)
         cold.append(timed_once())
+    for i in range(reps):
+        flush.fill_(i & 7)
+        dirty.append(timed_once())
     cold_ms = statistics.median(cold)
-    del flush, out, rows, ids
+    dirty_ms = statistics.median(dirty)
+    del flush, sink, out, rows, ids
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     nbytes = GATHER_BYTES_PER_TOKEN * T
@@ -712,7 +737,11 @@ def gather_c2_bench(gw, reps: int):
                      "frac": round(gw_(warm) / HBM_PEAK_GBPS, 4)},
             "cold": {"ms": round(cold_ms, 4), "achieved": round(gw_(cold_ms), 1),
                      "frac": round(gw_(cold_ms) / HBM_PEAK_GBPS, 4),
-                     "flush": "1 GiB scratch written before each call"},
+                     "flush": "1 GiB read before each call (caches evicted, clean)"},
+            "cold_dirty_caches": {"ms": round(dirty_ms, 4), "achieved": round(gw_(dirty_ms), 1),
+                                  "frac": round(gw_(dirty_ms) / HBM_PEAK_GBPS, 4),
+                                  "flush": "1 GiB written before each call (its dirty lines "
+                                           "are written back during the call)"},
             "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
 
 
