@@ -194,6 +194,20 @@ EngramConvArgs make_conv_args(const engram_short_conv *c) {
   return a;
 }
 
+// The bf16 projection kernels address each 256-row operand panel through a
+// buffer resource whose byte count (rows * K * 2) and byte offsets are 32-bit,
+// and index their grids with int tile products: K up to 2^20 keeps a panel below
+// 2^30 bytes, and the largest grid (128-wide tiles of 512 threads) must stay
+// within 2^32 threads.
+constexpr int64_t kMaxProjectInDim = (int64_t)1 << 20;
+
+bool bf16_projection_shape_ok(int64_t tokens, int64_t in_dim, int64_t out_dim) {
+  if (in_dim > kMaxProjectInDim) return false;
+  const int64_t tiles_m = (tokens + 255) / 256;
+  const int64_t tiles_n = (out_dim + 127) / 128;
+  return tiles_m * tiles_n <= ((int64_t)1 << 32) / 512 - 1;
+}
+
 // engram_forward folds the gate's two scale arrays into one (the same fp32
 // products, so the same bits) when the call has at least this many tokens: the
 // gate then reads half the scale bytes per token (12 % faster at 32768 tokens,
@@ -435,6 +449,8 @@ int engram_project_mx(const void *e_codes, const void *e_scales, int32_t segment
   if (tokens < 0 || segments < 1 || segments > ENGRAM_MAX_SEGMENTS || out_dim < 1)
     return ENGRAM_ESHAPE;
   if (out_dim % 8 || tokens > INT32_MAX || out_dim > INT32_MAX) return ENGRAM_ESHAPE;
+  if (!bf16_projection_shape_ok(tokens, (int64_t)segments * ENGRAM_ROW_DIM_E4M3, out_dim))
+    return ENGRAM_ESHAPE;
   if (tokens == 0) return ENGRAM_OK;
   if (e_codes == nullptr || e_scales == nullptr || w_codes == nullptr || w_scales == nullptr ||
       kv == nullptr)
@@ -472,6 +488,7 @@ int engram_project(const void *e, const void *wkv, void *kv, int64_t tokens, int
     if (in_dim % 64 || out_dim % 8) return ENGRAM_ESHAPE;
   }
   if (tokens > INT32_MAX || out_dim > INT32_MAX || in_dim > INT32_MAX) return ENGRAM_ESHAPE;
+  if (!act_f32 && !bf16_projection_shape_ok(tokens, in_dim, out_dim)) return ENGRAM_ESHAPE;
   if (tokens == 0) return ENGRAM_OK;
   if (e == nullptr || wkv == nullptr || kv == nullptr) return ENGRAM_EINVAL;
   if (!aligned(e, 16) || !aligned(wkv, 16) || !aligned(kv, 16)) return ENGRAM_EINVAL;
@@ -613,6 +630,7 @@ int forward_impl(const engram_hash_params *params, const engram_forward_desc *de
   const int64_t out_dim = (int64_t)(desc->hc + 1) * desc->dim;
   if (!f32 && in_dim % 64) return ENGRAM_ESHAPE;
   if (ntok > INT32_MAX) return ENGRAM_ESHAPE;
+  if (!f32 && !bf16_projection_shape_ok(ntok, in_dim, out_dim)) return ENGRAM_ESHAPE;
   bool host = false;
   if (ntok > 0) {
     if (ids == nullptr || table == nullptr || wkv == nullptr || q_w == nullptr ||
@@ -741,6 +759,8 @@ int engram_forward_mx(const engram_hash_params *params, const engram_forward_des
   const int32_t S = (params->max_ngram - 1) * params->heads;
   const int64_t out_dim = (int64_t)(desc->hc + 1) * desc->dim;
   if (ntok > INT32_MAX) return ENGRAM_ESHAPE;
+  if (!bf16_projection_shape_ok(ntok, (int64_t)S * ENGRAM_ROW_DIM_E4M3, out_dim))
+    return ENGRAM_ESHAPE;
   bool host = false;
   if (ntok > 0) {
     if (ids == nullptr || table == nullptr || w_codes == nullptr || w_scales == nullptr ||

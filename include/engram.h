@@ -334,8 +334,11 @@ int engram_gather_mx(const void *table, int64_t table_rows, const int64_t *row_i
  *        Every other path sums each output's K in one order, so its bits do
  *        not depend on the token count. Contents need not be initialised and
  *        are clobbered.
- * bf16 requires in_dim % 64 == 0 and out_dim % 8 == 0; fp32 requires in_dim % 4
- * == 0 and out_dim % 4 == 0.
+ * bf16 requires in_dim % 64 == 0, out_dim % 8 == 0, in_dim <= 2^20 and
+ * ceil(tokens / 256) * ceil(out_dim / 128) < 2^23 (the kernels address a
+ * 256-row operand panel with 32-bit byte counts and launch at most 2^32
+ * threads); fp32 requires in_dim % 4 == 0 and out_dim % 4 == 0. The same tile
+ * bound applies to engram_project_mx and to the forward entry points.
  * Errors: ENGRAM_EINVAL, ENGRAM_ESHAPE, ENGRAM_EWORKSPACE (non-NULL and too
  * small or misaligned), ENGRAM_EHIP.
  */

@@ -325,3 +325,25 @@ def test_forward_static_refuses_calls_beyond_its_array():
     assert "static array" in E.status_string(E.ESCRATCH)
     bad = E.forward_desc(4, 8192, 9, 5120, 384_006_168, 0, 256)      # hc > 8
     assert L.engram_forward_static(ctypes.byref(p), ctypes.byref(bad), *args) == E.ESHAPE
+
+
+@host_only
+def test_projection_shapes_beyond_32_bit_offsets_are_refused():
+    """The bf16 kernels address a 256-row panel with 32-bit byte counts: in_dim
+    above 2^20, or a grid beyond 2^32 threads, is refused before any launch
+    (rather than wrapping the record and returning zeros or garbage)."""
+    L = E.LIB
+    ok = L.engram_project(0x1000, 0x2000, 0x3000, 4, 1 << 20, 64, 0, None, 0, None)
+    assert ok != E.ESHAPE                     # fake pointers: any later status but ESHAPE
+    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, (1 << 20) + 64, 64, 0, None, 0,
+                            None) == E.ESHAPE
+    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, 1 << 23, 64, 0, None, 0, None) \
+        == E.ESHAPE
+    big_m, big_n = (1 << 31) - 1, 1 << 20     # 8.4 M x 8192 tiles
+    assert L.engram_project(0x1000, 0x2000, 0x3000, big_m, 6144, big_n, 0, None, 0,
+                            None) == E.ESHAPE
+    assert L.engram_project_mx(0x1000, 0x2000, 24, 0x3000, 0x4000, 0x5000, big_m, big_n,
+                               None, 0, None) == E.ESHAPE
+    # the fp32 kernel indexes with 64-bit offsets: no in_dim limit of its own
+    assert L.engram_project(0x1000, 0x2000, 0x3000, 0, (1 << 21), 64, 1, None, 0,
+                            None) == E.OK
