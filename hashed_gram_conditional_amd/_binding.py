@@ -131,6 +131,7 @@ def _load():
         "engram_forward": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "engram_forward_static": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, P, P]),
         "engram_forward_static_max_bytes": (SZ, []),
+        "engram_transpose": (ctypes.c_int, [P, P, I64, I64, I32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -329,6 +330,11 @@ def engram_forward_static(params: HashParams, desc: ForwardDesc, ids, hist_in, h
                                      _ptr(wkv), _ptr(q_w), _ptr(k_w), _ptr(h), _ptr(gate_out),
                                      _stream(stream)),
            "engram_forward_static")
+
+
+def engram_transpose(src, dst, rows: int, cols: int, elem_bytes: int, stream=None):
+    _check(LIB.engram_transpose(_ptr(src), _ptr(dst), rows, cols, elem_bytes, _stream(stream)),
+           "engram_transpose")
 
 
 def engram_forward_static_max_bytes() -> int:

@@ -9,7 +9,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SOURCES = ["hash.hip", "gather.hip", "gemm.hip", "gemm_mx.hip", "gate.hip", "conv.hip",
-           "engram_api.hip"]
+           "layout.hip", "engram_api.hip"]
 LIB = os.path.join(PKG, "libengram.so")
 
 # Packed-fp32 instructions are disabled for every HIP translation unit.

@@ -204,3 +204,8 @@ hipError_t engram_launch_short_conv(bool f32, const EngramConvArgs &c, const int
                                     int32_t raw_vocab, const void *kv, const float *stats,
                                     void *h, int64_t batch, int64_t seq, int32_t hc,
                                     int32_t dim, hipStream_t stream);
+
+// dst[c, r] = src[r, c] for a row-major [rows, cols] array of 2- or 4-byte
+// elements (layout.hip).
+hipError_t engram_launch_transpose(const void *src, void *dst, int64_t rows, int64_t cols,
+                                   int elem_bytes, hipStream_t stream);

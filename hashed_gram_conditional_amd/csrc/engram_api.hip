@@ -551,6 +551,23 @@ int engram_gate_folded(const engram_forward_desc *desc, const int32_t *ids, int3
                                        stream));
 }
 
+int engram_transpose(const void *src, void *dst, int64_t rows, int64_t cols,
+                     int32_t elem_bytes, hipStream_t stream) {
+  if (elem_bytes != 2 && elem_bytes != 4) return ENGRAM_EINVAL;
+  if (rows < 0 || cols < 0) return ENGRAM_ESHAPE;
+  if (rows == 0 || cols == 0) return ENGRAM_OK;
+  // 64 x 64 tiles of 256 threads: at most 2^24 tiles keeps the grid within 2^32
+  // threads.
+  const int64_t tr = (rows + 63) / 64, tc = (cols + 63) / 64;
+  if (tr > ((int64_t)1 << 24) / tc) return ENGRAM_ESHAPE;
+  if (src == nullptr || dst == nullptr) return ENGRAM_EINVAL;
+  if (!aligned(src, elem_bytes) || !aligned(dst, elem_bytes)) return ENGRAM_EINVAL;
+  const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+  const uintptr_t n = (uintptr_t)(rows * cols * elem_bytes);
+  if (s0 < d0 + n && d0 < s0 + n) return ENGRAM_EINVAL;        // overlapping buffers
+  return hip_status(engram_launch_transpose(src, dst, rows, cols, elem_bytes, stream));
+}
+
 size_t engram_gate_conv_workspace_size(const engram_forward_desc *desc) {
   if (check_desc(desc) != ENGRAM_OK) return 0;
   return gate_conv_workspace(desc);

@@ -373,6 +373,26 @@ int engram_project_mx(const void *e_codes, const void *e_scales, int32_t segment
                       int64_t out_dim, void *workspace, size_t workspace_bytes,
                       hipStream_t stream);
 
+/*
+ * Re-layout of a caller's weight buffer, once, outside the per-step path:
+ * dst[c, r] = src[r, c] for a row-major [rows, cols] array of 2-byte (bf16) or
+ * 4-byte (fp32) elements. The kernels read wkv as [(hc+1) dim, S row_dim]
+ * (inputs innermost, [P4] "消费") and the gate scales as [hc, dim]. A caller
+ * holding them the other way round, wkv as [S row_dim, (hc+1) dim] (the
+ * 6144 x 25600 matrix of [P1] "每条流一个 key 的设计沿用自原版" with outputs
+ * innermost) or q_w / k_w as [dim, hc], calls
+ *   engram_transpose(wkv_in_out, wkv, S row_dim, (hc+1) dim, 2 or 4, stream)
+ *   engram_transpose(q_w_dim_hc, q_w, dim, hc, 4, stream)
+ * and passes the results to every entry point; the forward's bits are those
+ * of the same weights stored in the kernels' layout.
+ *   src, dst  device, elem_bytes-aligned, caller-owned, not overlapping
+ * Errors: ENGRAM_EINVAL (elem_bytes not 2 or 4, null, misaligned or
+ * overlapping buffers), ENGRAM_ESHAPE (negative sizes, or more than 2^24
+ * tiles of 64 x 64), ENGRAM_EHIP.
+ */
+int engram_transpose(const void *src, void *dst, int64_t rows, int64_t cols,
+                     int32_t elem_bytes, hipStream_t stream);
+
 /* [host] Bytes of workspace engram_project_mx uses (0 if none, on bad arguments
  * or on a HIP error). */
 size_t engram_project_mx_workspace_size(int64_t tokens, int32_t segments, int64_t out_dim);

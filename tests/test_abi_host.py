@@ -347,3 +347,14 @@ def test_projection_shapes_beyond_32_bit_offsets_are_refused():
     # the fp32 kernel indexes with 64-bit offsets: no in_dim limit of its own
     assert L.engram_project(0x1000, 0x2000, 0x3000, 0, (1 << 21), 64, 1, None, 0,
                             None) == E.OK
+
+
+@host_only
+def test_transpose_validation():
+    L = E.LIB
+    assert L.engram_transpose(0x1000, 0x2000, 4, 8, 3, None) == E.EINVAL      # 3-byte elements
+    assert L.engram_transpose(0x1000, 0x1010, 4, 8, 2, None) == E.EINVAL      # overlap
+    assert L.engram_transpose(0x1001, 0x9000, 4, 8, 2, None) == E.EINVAL      # misaligned
+    assert L.engram_transpose(None, None, 0, 5, 2, None) == E.OK              # empty
+    assert L.engram_transpose(0x1000, 0x9000, -1, 5, 2, None) == E.ESHAPE
+    assert L.engram_transpose(0x1000, 1 << 44, 1 << 30, 1 << 20, 2, None) == E.ESHAPE
