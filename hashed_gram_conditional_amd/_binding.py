@@ -10,7 +10,10 @@ import ctypes
 import os
 from typing import Optional, Sequence
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libengram.so")
+# ENGRAM_LIBRARY selects another build of the same library (the host-sanitized
+# one the CPU tests run); by default the in-tree libengram.so is loaded.
+_LIB_PATH = os.environ.get("ENGRAM_LIBRARY") or \
+    os.path.join(os.path.dirname(os.path.abspath(__file__)), "libengram.so")
 
 DEAD = -1
 MAX_NGRAM = 8

@@ -24,18 +24,35 @@ def hipcc():
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build_library(verbose: bool = False) -> str:
-    srcs = [os.path.join(PKG, "csrc", s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *srcs]
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for the C-ABI's host
+# code (argument validation, prime search, workspace arithmetic); the device
+# code is built as usual. Each -fsanitize= applies to the host pass only.
+SANITIZE_FLAGS = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+    "-shared-libsan", "-g",
+]
+
+
+def sources():
+    return [os.path.join(PKG, "csrc", s) for s in SOURCES]
+
+
+def build_library(verbose: bool = False, out: str = LIB, sanitize: bool = False) -> str:
+    srcs = sources()
+    tmp = out + ".tmp"
+    flags = [f for f in HIP_FLAGS if not (sanitize and f == "-O3")]
+    if sanitize:
+        flags += ["-O1", *SANITIZE_FLAGS]
+    cmd = [hipcc(), *flags, "-I", os.path.join(ROOT, "include"), "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed building {LIB}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
