@@ -308,6 +308,8 @@ def main():
 
     torch.cuda.set_device(0)
     if args.decode_only:
+        if args.copy_calibration_mib:
+            copy_calibration(args.copy_calibration_mib)
         print(json.dumps({"decode": decode_bench(args.steps, args.warmup)}), flush=True)
         return
     if args.gather_only:
