@@ -175,11 +175,28 @@ hipError_t engram_gemm_mx_workspace(int64_t m, int64_t n, int32_t segments, size
 hipError_t engram_launch_gemm_f32(const float *e, const float *w, float *kv, int64_t m,
                                   int64_t n, int64_t k, hipStream_t stream);
 
+// Which positions are DEAD. A raw id outside [0, raw_vocab) always is; with a
+// token map, so is a raw id whose compressed id lies outside
+// [0, compressed_vocab), the hash's own rule, so that the gate and the
+// convolution of a layer agree with its row ids on every position.
+struct EngramDeadRule {
+  int32_t raw_vocab;
+  int32_t compressed_vocab;
+  const int32_t *token_map;   // NULL: the raw id alone decides
+};
+
+__device__ __forceinline__ bool engram_dead(const EngramDeadRule &r, int32_t x) {
+  if (x < 0 || x >= r.raw_vocab) return true;
+  if (r.token_map == nullptr) return false;
+  const int32_t v = r.token_map[x];
+  return v < 0 || v >= r.compressed_vocab;
+}
+
 // stats == NULL: the gate and the residual update. stats != NULL (float
 // [tokens, hc + 1]): gates and the value row's mean square per token, h
 // untouched. plain selects sigmoid(s) over the signed root. k_w == NULL: q_w
 // holds the folded products q_w * k_w (engram_launch_fold_gate_weights).
-hipError_t engram_launch_gate(bool f32, const int32_t *ids, int32_t raw_vocab,
+hipError_t engram_launch_gate(bool f32, const int32_t *ids, EngramDeadRule dead_rule,
                               const void *kv, const float *q_w, const float *k_w,
                               void *h, float *gate_out, float *stats, int64_t tokens,
                               int32_t hc, int32_t dim, float eps, float clamp, int plain,
@@ -201,7 +218,7 @@ struct EngramConvArgs {
   float *state_s_out;
 };
 hipError_t engram_launch_short_conv(bool f32, const EngramConvArgs &c, const int32_t *ids,
-                                    int32_t raw_vocab, const void *kv, const float *stats,
+                                    EngramDeadRule dead_rule, const void *kv, const float *stats,
                                     void *h, int64_t batch, int64_t seq, int32_t hc,
                                     int32_t dim, hipStream_t stream);
 

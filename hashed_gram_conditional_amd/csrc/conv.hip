@@ -47,7 +47,7 @@ __device__ __forceinline__ float norm_factor(float a, float ms, float eps) {
 
 template <bool F32, int TAPS>
 __global__ __launch_bounds__(kThreads) void short_conv_kernel(
-    EngramConvArgs c, const int32_t *__restrict__ ids, int32_t raw_vocab,
+    EngramConvArgs c, const int32_t *__restrict__ ids, EngramDeadRule dead_rule,
     const void *__restrict__ kv, const float *__restrict__ stats, void *__restrict__ h,
     int64_t ntok, int64_t seq, int hc, int dim, int tpb) {
   const int cps = dim / kChunk;
@@ -89,8 +89,7 @@ __global__ __launch_bounds__(kThreads) void short_conv_kernel(
   const int64_t t0 = (int64_t)blockIdx.x * tpb;
   const int64_t t1 = t0 + tpb < ntok ? t0 + tpb : ntok;
   for (int64_t t = t0; t < t1; ++t) {
-    const int32_t x = ids[t];
-    if (x < 0 || x >= raw_vocab) continue;          // DEAD: streams untouched
+    if (engram_dead(dead_rule, ids[t])) continue;   // DEAD: streams untouched
     const int64_t b = t / seq;
     const int64_t s = t - b * seq;
     float u[kChunk], vt[kChunk];
@@ -145,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void short_conv_kernel(
 // start reads the history (or zero) instead of the window.
 template <int TAPS, int DIL, int TB>
 __global__ __launch_bounds__(kThreads) void short_conv_window_kernel(
-    EngramConvArgs c, const int32_t *__restrict__ ids, int32_t raw_vocab,
+    EngramConvArgs c, const int32_t *__restrict__ ids, EngramDeadRule dead_rule,
     const void *__restrict__ kv, const float *__restrict__ stats, void *__restrict__ h,
     int64_t ntok, int64_t seq, int hc, int dim) {
   constexpr int L = (TAPS - 1) * DIL;
@@ -203,7 +202,7 @@ __global__ __launch_bounds__(kThreads) void short_conv_window_kernel(
   }
 
   if (tid < nstat) s_stat[sr][scol] = stat_ok ? stat_v : 0.f;
-  if (tid < TB) s_ids[tid] = (t0 + tid < ntok) ? id_v : -1;
+  if (tid < TB) s_ids[tid] = (t0 + tid < ntok && !engram_dead(dead_rule, id_v)) ? id_v : -1;
   __syncthreads();
   if (!live) return;
 
@@ -237,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void short_conv_window_kernel(
       ++b;
     }
     const int32_t x = s_ids[i];
-    if (t0 + i >= ntok || x < 0 || x >= raw_vocab) continue;   // DEAD: streams untouched
+    if (x < 0) continue;          // DEAD (or past the last token): streams untouched
     float u[kChunk];
 #pragma unroll
     for (int e = 0; e < kChunk; ++e) u[e] = 0.f;
@@ -314,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void conv_state_kernel(
 
 // The convolution over the chunk's tokens.
 template <bool F32>
-hipError_t launch_conv(const EngramConvArgs &c, const int32_t *ids, int32_t raw_vocab,
+hipError_t launch_conv(const EngramConvArgs &c, const int32_t *ids, EngramDeadRule dead_rule,
                        const void *kv, const float *stats, void *h, int64_t ntok, int64_t seq,
                        int hc, int dim, hipStream_t stream) {
   int dev = 0, cus = 256;
@@ -329,7 +328,7 @@ hipError_t launch_conv(const EngramConvArgs &c, const int32_t *ids, int32_t raw_
       window_blocks <= INT32_MAX) {
     const dim3 grid((unsigned)window_blocks);
     hipLaunchKernelGGL((short_conv_window_kernel<4, 3, kWindowTokens>), grid, dim3(kThreads), 0,
-                       stream, c, ids, raw_vocab, kv, stats, h, ntok, seq, hc, dim);
+                       stream, c, ids, dead_rule, kv, stats, h, ntok, seq, hc, dim);
     return hipGetLastError();
   }
   // Runs of up to 16 tokens per thread while that still leaves about 8 blocks
@@ -340,7 +339,7 @@ hipError_t launch_conv(const EngramConvArgs &c, const int32_t *ids, int32_t raw_
 #define ENGRAM_CONV_CASE(N)                                                                 \
   case N:                                                                                   \
     hipLaunchKernelGGL((short_conv_kernel<F32, N>), grid, dim3(kThreads), 0, stream, c, ids, \
-                       raw_vocab, kv, stats, h, ntok, seq, hc, dim, (int)tpb);              \
+                       dead_rule, kv, stats, h, ntok, seq, hc, dim, (int)tpb);              \
     break;
   switch (c.taps) {
     ENGRAM_CONV_CASE(1)
@@ -359,13 +358,14 @@ hipError_t launch_conv(const EngramConvArgs &c, const int32_t *ids, int32_t raw_
 }
 
 template <bool F32>
-hipError_t launch(const EngramConvArgs &c, const int32_t *ids, int32_t raw_vocab, const void *kv,
+hipError_t launch(const EngramConvArgs &c, const int32_t *ids, EngramDeadRule dead_rule,
+                  const void *kv,
                   const float *stats, void *h, int64_t batch, int64_t seq, int hc, int dim,
                   hipStream_t stream) {
   const int64_t ntok = batch * seq;
   if (ntok > 0) {
     const hipError_t err =
-        launch_conv<F32>(c, ids, raw_vocab, kv, stats, h, ntok, seq, hc, dim, stream);
+        launch_conv<F32>(c, ids, dead_rule, kv, stats, h, ntok, seq, hc, dim, stream);
     if (err != hipSuccess) return err;
   }
   if (c.state_v_out != nullptr && batch > 0 && c.history > 0) {
@@ -382,9 +382,9 @@ hipError_t launch(const EngramConvArgs &c, const int32_t *ids, int32_t raw_vocab
 }  // namespace
 
 hipError_t engram_launch_short_conv(bool f32, const EngramConvArgs &c, const int32_t *ids,
-                                    int32_t raw_vocab, const void *kv, const float *stats,
+                                    EngramDeadRule dead_rule, const void *kv, const float *stats,
                                     void *h, int64_t batch, int64_t seq, int32_t hc,
                                     int32_t dim, hipStream_t stream) {
-  return f32 ? launch<true>(c, ids, raw_vocab, kv, stats, h, batch, seq, hc, dim, stream)
-             : launch<false>(c, ids, raw_vocab, kv, stats, h, batch, seq, hc, dim, stream);
+  return f32 ? launch<true>(c, ids, dead_rule, kv, stats, h, batch, seq, hc, dim, stream)
+             : launch<false>(c, ids, dead_rule, kv, stats, h, batch, seq, hc, dim, stream);
 }

@@ -208,6 +208,15 @@ bool bf16_projection_shape_ok(int64_t tokens, int64_t in_dim, int64_t out_dim) {
   return tiles_m * tiles_n <= ((int64_t)1 << 32) / 512 - 1;
 }
 
+// The stage entry points (engram_gate, engram_gate_conv) know only the raw ids;
+// the fused ones apply the hash's full rule, so a token map value outside
+// [0, V') makes the position DEAD in the gate exactly as in its row ids.
+EngramDeadRule raw_id_rule(int32_t raw_vocab) { return EngramDeadRule{raw_vocab, 0, nullptr}; }
+
+EngramDeadRule hash_rule(const engram_hash_params *p) {
+  return EngramDeadRule{p->raw_vocab, p->compressed_vocab, p->token_map};
+}
+
 // engram_forward folds the gate's two scale arrays into one (the same fp32
 // products, so the same bits) when the call has at least this many tokens: the
 // gate then reads half the scale bytes per token (12 % faster at 32768 tokens,
@@ -519,8 +528,9 @@ int engram_gate(const engram_forward_desc *desc, const int32_t *ids, int32_t raw
       !aligned(h, 16) || !aligned(gate_out, 4))
     return ENGRAM_EINVAL;
   if (ntok > INT32_MAX) return ENGRAM_ESHAPE;
-  return hip_status(engram_launch_gate(desc->row_format == ENGRAM_ROW_F32, ids, raw_vocab, kv,
-                                       q_w, k_w, h, gate_out, nullptr, ntok, desc->hc,
+  return hip_status(engram_launch_gate(desc->row_format == ENGRAM_ROW_F32, ids,
+                                       raw_id_rule(raw_vocab), kv, q_w, k_w, h, gate_out,
+                                       nullptr, ntok, desc->hc,
                                        desc->dim, desc->eps, desc->gate_clamp, desc->gate_mode,
                                        stream));
 }
@@ -545,8 +555,9 @@ int engram_gate_folded(const engram_forward_desc *desc, const int32_t *ids, int3
   if (!aligned(ids, 4) || !aligned(kv, 16) || !aligned(qk_w, 16) || !aligned(h, 16) ||
       !aligned(gate_out, 4))
     return ENGRAM_EINVAL;
-  return hip_status(engram_launch_gate(desc->row_format == ENGRAM_ROW_F32, ids, raw_vocab, kv,
-                                       qk_w, nullptr, h, gate_out, nullptr, ntok, desc->hc,
+  return hip_status(engram_launch_gate(desc->row_format == ENGRAM_ROW_F32, ids,
+                                       raw_id_rule(raw_vocab), kv, qk_w, nullptr, h, gate_out,
+                                       nullptr, ntok, desc->hc,
                                        desc->dim, desc->eps, desc->gate_clamp, desc->gate_mode,
                                        stream));
 }
@@ -597,12 +608,14 @@ int engram_gate_conv(const engram_forward_desc *desc, const engram_short_conv *c
   const bool f32 = desc->row_format == ENGRAM_ROW_F32;
   float *stats = (float *)workspace;
   if (ntok > 0) {
-    hipError_t err = engram_launch_gate(f32, ids, raw_vocab, kv, q_w, k_w, h, gate_out, stats,
+    hipError_t err = engram_launch_gate(f32, ids, raw_id_rule(raw_vocab), kv, q_w, k_w, h,
+                                        gate_out, stats,
                                         ntok, desc->hc, desc->dim, desc->eps, desc->gate_clamp,
                                         desc->gate_mode, stream);
     if (err != hipSuccess) return hip_status(err);
   }
-  return hip_status(engram_launch_short_conv(f32, make_conv_args(conv), ids, raw_vocab, kv, stats,
+  return hip_status(engram_launch_short_conv(f32, make_conv_args(conv), ids,
+                                             raw_id_rule(raw_vocab), kv, stats,
                                              h, desc->batch, desc->seq, desc->hc, desc->dim,
                                              stream));
 }
@@ -688,7 +701,7 @@ int forward_impl(const engram_hash_params *params, const engram_forward_desc *de
   if (ntok == 0) {
     // An empty chunk still passes the convolution's history on.
     if (conv != nullptr)
-      err = engram_launch_short_conv(f32, make_conv_args(conv), ids, params->raw_vocab, nullptr,
+      err = engram_launch_short_conv(f32, make_conv_args(conv), ids, hash_rule(params), nullptr,
                                      nullptr, h, desc->batch, desc->seq, desc->hc, desc->dim,
                                      stream);
     return hip_status(err);
@@ -707,12 +720,12 @@ int forward_impl(const engram_hash_params *params, const engram_forward_desc *de
   const bool fold = ntok >= kFoldMinTokens;
   if (fold) err = engram_launch_fold_gate_weights(q_w, k_w, qk_w, desc->hc, desc->dim, stream);
   if (err != hipSuccess) return hip_status(err);
-  err = engram_launch_gate(f32, ids, params->raw_vocab, kv, fold ? qk_w : q_w,
+  err = engram_launch_gate(f32, ids, hash_rule(params), kv, fold ? qk_w : q_w,
                            fold ? nullptr : k_w, h, gate_out, conv != nullptr ? stats : nullptr,
                            ntok, desc->hc, desc->dim, desc->eps, desc->gate_clamp,
                            desc->gate_mode, stream);
   if (err != hipSuccess || conv == nullptr) return hip_status(err);
-  err = engram_launch_short_conv(f32, make_conv_args(conv), ids, params->raw_vocab, kv, stats, h,
+  err = engram_launch_short_conv(f32, make_conv_args(conv), ids, hash_rule(params), kv, stats, h,
                                  desc->batch, desc->seq, desc->hc, desc->dim, stream);
   return hip_status(err);
 }
@@ -816,7 +829,7 @@ int engram_forward_mx(const engram_hash_params *params, const engram_forward_des
   const bool fold = ntok >= kFoldMinTokens;
   if (fold) err = engram_launch_fold_gate_weights(q_w, k_w, qk_w, desc->hc, desc->dim, stream);
   if (err != hipSuccess) return hip_status(err);
-  err = engram_launch_gate(false, ids, params->raw_vocab, kv, fold ? qk_w : q_w,
+  err = engram_launch_gate(false, ids, hash_rule(params), kv, fold ? qk_w : q_w,
                            fold ? nullptr : k_w, h, gate_out, nullptr, ntok, desc->hc,
                            desc->dim, desc->eps, desc->gate_clamp, desc->gate_mode, stream);
   return hip_status(err);

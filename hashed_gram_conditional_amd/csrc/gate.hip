@@ -43,7 +43,7 @@ using Chunk = engram::Chunk8<F32>;
 
 template <bool F32, int CPT, bool AS>
 __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
-    const int32_t *__restrict__ ids, int32_t raw_vocab, const void *__restrict__ kv,
+    const int32_t *__restrict__ ids, EngramDeadRule dead_rule, const void *__restrict__ kv,
     const float *__restrict__ q_w, const float *__restrict__ k_w, void *__restrict__ h,
     float *__restrict__ gate_out, float *__restrict__ stats, int hc, int dim, float eps,
     float clamp, int plain) {
@@ -53,8 +53,7 @@ __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x;
   const int nthreads = blockDim.x;
-  const int32_t x = ids[t];
-  if (x < 0 || x >= raw_vocab) {          // DEAD: gate 0, streams untouched
+  if (engram_dead(dead_rule, ids[t])) {   // DEAD: gate 0, streams untouched
     if (gate_out != nullptr && tid < hc) gate_out[t * hc + tid] = 0.f;
     if (stats != nullptr && tid <= hc) stats[t * (hc + 1) + tid] = 0.f;
     return;
@@ -271,13 +270,14 @@ __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
 }
 
 template <bool F32>
-hipError_t launch(int cpt, int threads, bool all_streams, const int32_t *ids, int32_t raw_vocab,
+hipError_t launch(int cpt, int threads, bool all_streams, const int32_t *ids,
+                  EngramDeadRule dead_rule,
                   const void *kv, const float *q_w, const float *k_w, void *h, float *gate_out,
                   float *stats, int64_t tokens, int hc, int dim, float eps, float clamp,
                   int plain, hipStream_t stream) {
 #define ENGRAM_GATE_CASE(N, AS)                                                             \
   hipLaunchKernelGGL((gate_kernel<F32, N, AS>), dim3((unsigned)tokens), dim3(threads), 0,   \
-                     stream, ids, raw_vocab, kv, q_w, k_w, h, gate_out, stats, hc, dim,     \
+                     stream, ids, dead_rule, kv, q_w, k_w, h, gate_out, stats, hc, dim,     \
                      eps, clamp, plain)
   if (all_streams) {
     switch (cpt) {
@@ -305,7 +305,8 @@ hipError_t launch(int cpt, int threads, bool all_streams, const int32_t *ids, in
 
 }  // namespace
 
-hipError_t engram_launch_gate(bool f32, const int32_t *ids, int32_t raw_vocab, const void *kv,
+hipError_t engram_launch_gate(bool f32, const int32_t *ids, EngramDeadRule dead_rule,
+                              const void *kv,
                               const float *q_w, const float *k_w, void *h, float *gate_out,
                               float *stats, int64_t tokens, int32_t hc, int32_t dim, float eps,
                               float clamp, int plain, hipStream_t stream) {
@@ -323,9 +324,9 @@ hipError_t engram_launch_gate(bool f32, const int32_t *ids, int32_t raw_vocab, c
   const int cpt = (cps + threads - 1) / threads;
   // few tokens: one memory round trip per token for up to kAllStreams streams
   const bool all_streams = tokens < 8 * (int64_t)cus && hc <= kAllStreams && cpt <= 2;
-  return f32 ? launch<true>(cpt, threads, all_streams, ids, raw_vocab, kv, q_w, k_w, h,
+  return f32 ? launch<true>(cpt, threads, all_streams, ids, dead_rule, kv, q_w, k_w, h,
                             gate_out, stats, tokens, hc, dim, eps, clamp, plain, stream)
-             : launch<false>(cpt, threads, all_streams, ids, raw_vocab, kv, q_w, k_w, h,
+             : launch<false>(cpt, threads, all_streams, ids, dead_rule, kv, q_w, k_w, h,
                              gate_out, stats, tokens, hc, dim, eps, clamp, plain, stream);
 }
 

@@ -402,7 +402,11 @@ size_t engram_project_mx_workspace_size(int64_t tokens, int32_t segments, int64_
  *   desc     shapes (batch, seq, hc, dim, row_format selects bf16 or fp32 I/O,
  *            eps, gate_clamp); table fields are ignored
  *   ids      int32 [B, T] raw ids; a position with an id outside [0, raw_vocab)
- *            is DEAD: alpha = 0 and its h is left untouched
+ *            is DEAD: alpha = 0 and its h is left untouched. (The fused entry
+ *            points, engram_forward and its variants, also make a position DEAD
+ *            whose token map value lies outside [0, compressed_vocab), as the
+ *            hash does, so gate and row ids agree even for a map that would
+ *            fail engram_check_token_map.)
  *   kv       [B*T, (hc+1) dim]: keys k^(0..hc-1) then the value v
  *   q_w, k_w float [hc, dim]: learned scales of stream m in row m
  *   h        [B, T, hc, dim] in/out, bf16 (E4M3 format) or float (fp32 format)

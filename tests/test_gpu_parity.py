@@ -601,6 +601,62 @@ def test_gate_on_the_oracles_kv_and_stage_rows():
                           O.gather_e4m3(gw.fetch_rows, rid, gw.rows).reshape(-1, 256))
 
 
+def test_forward_map_values_outside_the_vocabulary_are_dead():
+    """A token map that the start-up check would refuse (values outside
+    [0, V')): the fused entry points apply the hash's rule, so such positions
+    get the all-pad rows, a zero gate and untouched streams (also through the
+    short convolution), as the oracle's compress makes them DEAD."""
+    w = S_A
+    gw = GpuWorkload(w)
+    ids = gw.ids_np
+    tm = gw.token_map_np.copy()
+    hit = np.unique(ids[ids >= 0])[[3, 17, 40]]          # ids that occur in the batch
+    tm[hit] = [w.compressed_vocab, -3, w.compressed_vocab + 1000]
+    assert E.engram_check_token_map(tm, w.raw_vocab, w.compressed_vocab) == E.EVOCAB
+    tm_dev = to_device(tm)
+    params = E.hash_params(w.raw_vocab, w.compressed_vocab, w.max_ngram, w.heads, gw.pad, tm_dev,
+                           gw.mult, gw.primes, gw.offsets)
+    primes, offs, _ = oracle_setup(w)
+    rid, _ = O.hash_rows(ids, tm, w.compressed_vocab, gw.pad, gw.mult, primes, offs,
+                         w.max_ngram, w.heads)
+    dead = O.compress(ids, tm, w.compressed_vocab).reshape(-1) == O.DEAD
+    newly = dead & ~gw.dead_np()
+    assert newly.sum() >= 3
+    ws, n = gw.workspace()
+    h = gw.h.clone()
+    gates = torch.full((w.tokens, w.hc), -1.0, dtype=torch.float32, device=DEV)
+    E.engram_forward(params, gw.desc, gw.ids, None, None, gw.table, gw.wkv, gw.q_w, gw.k_w, h,
+                     gates, ws, n)
+    rows = torch.empty((w.tokens, w.segments), dtype=torch.int64, device=DEV)
+    E.engram_hash(params, gw.ids, w.batch, w.seq, None, None, rows)
+    torch.cuda.synchronize()
+    assert np.array_equal(rows.cpu().numpy(), rid)
+    check_forward_chunks(
+        tokens=np.arange(w.tokens), rid=rid, dead=dead, fetch_rows=gw.fetch_rows, table_f32=None,
+        table_rows=gw.rows, wkv=_wkv_f64(gw), q_w=gw.dense_np["q_w"], k_w=gw.dense_np["k_w"],
+        h_in=gw.dense_np["h"].reshape(w.tokens, w.hc, w.dim),
+        h_out=_host(h).reshape(w.tokens, w.hc, w.dim), gates=gates.cpu().numpy(), hc=w.hc,
+        dim=w.dim, eps=w.eps, clamp=w.gate_clamp, bf16=True, name="S_A, bad map values")
+    # the convolution branch leaves the same positions untouched
+    g = torch.Generator(device=DEV).manual_seed(5)
+    filt = 0.3 * torch.randn((w.hc, w.dim, 4), generator=g, device=DEV)   # kept alive below
+    conv = E.short_conv(filt, 4, 3, 1e-6)
+    nc = E.engram_forward_conv_workspace_size(params, gw.desc)
+    cws = torch.empty(max(nc, 256), dtype=torch.uint8, device=DEV)
+    h2 = gw.h.clone()
+    g2 = torch.full((w.tokens, w.hc), -1.0, dtype=torch.float32, device=DEV)
+    E.engram_forward_conv(params, gw.desc, conv, gw.ids, None, None, gw.table, gw.wkv, gw.q_w,
+                          gw.k_w, h2, g2, cws, nc)
+    torch.cuda.synchronize()
+    del filt
+    h0 = gw.dense_np["h"].reshape(w.tokens, w.hc, w.dim)
+    h2n = _host(h2).reshape(w.tokens, w.hc, w.dim)
+    assert np.array_equal(h2n[dead], h0[dead])
+    assert np.all(g2.cpu().numpy()[dead] == 0.0)
+    assert not np.array_equal(h2n[~dead], h0[~dead])
+    gw.free()
+
+
 def test_forward_chunked_and_deterministic():
     gw = GpuWorkload(S_A)
     w = S_A
