@@ -654,6 +654,20 @@ def test_forward_map_values_outside_the_vocabulary_are_dead():
     assert np.array_equal(h2n[dead], h0[dead])
     assert np.all(g2.cpu().numpy()[dead] == 0.0)
     assert not np.array_equal(h2n[~dead], h0[~dead])
+    # and the block-scaled FP8 layer
+    codes, scales = gen.wkv_mx(w)
+    wc, wsc = to_device(codes), to_device(scales)
+    nm = E.engram_forward_mx_workspace_size(params, gw.desc)
+    mws = torch.empty(max(nm, 256), dtype=torch.uint8, device=DEV)
+    h3 = gw.h.clone()
+    g3 = torch.full((w.tokens, w.hc), -1.0, dtype=torch.float32, device=DEV)
+    E.engram_forward_mx(params, gw.desc, gw.ids, None, None, gw.table, wc, wsc, gw.q_w, gw.k_w,
+                        h3, g3, mws, nm)
+    torch.cuda.synchronize()
+    h3n = _host(h3).reshape(w.tokens, w.hc, w.dim)
+    assert np.array_equal(h3n[dead], h0[dead])
+    assert np.all(g3.cpu().numpy()[dead] == 0.0)
+    assert np.all(g3.cpu().numpy()[~dead] > 0.0)
     gw.free()
 
 

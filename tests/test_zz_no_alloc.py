@@ -101,3 +101,49 @@ def test_static_refuses_calls_beyond_the_array():
     torch.cuda.synchronize()
     assert not h.any()
     gw.free()
+
+
+def test_static_captured_in_a_graph_replays_equal_eager():
+    """The use the entry point is for: captured once in a HIP graph (after one
+    eager call on the device, which looks the array up) and replayed with new
+    ids in the same buffer, every replay giving the eager call's bits."""
+    say("engram_forward_static captured in a HIP graph, 4 replays, 2 id batches")
+    gw = GpuWorkload(DECODE)
+    w = DECODE
+    ids_buf, h, h0 = gw.ids, gw.h, gw.h.clone()
+    ids_a = ids_buf.clone()
+    ids_b = torch.roll(ids_a, shifts=1, dims=0).contiguous()
+    gates = torch.empty((w.tokens, w.hc), dtype=torch.float32, device=DEV)
+    hout = torch.empty((w.batch, 3), dtype=torch.int32, device=DEV)
+
+    def step():
+        E.engram_forward_static(gw.params, gw.desc, ids_buf, gw.hist_in, hout, gw.table, gw.wkv,
+                                gw.q_w, gw.k_w, h, gates)
+
+    def reset(ids):
+        ids_buf.copy_(ids)
+        h.copy_(h0)
+        gates.fill_(-1.0)
+        hout.fill_(-7)
+        torch.cuda.synchronize()
+
+    ref = {}
+    for name, ids in (("a", ids_a), ("b", ids_b)):
+        reset(ids)
+        step()
+        torch.cuda.synchronize()
+        ref[name] = (h.clone(), gates.clone(), hout.clone())
+    reset(ids_a)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for name in ("a", "b", "a", "b"):
+        reset(ids_a if name == "a" else ids_b)
+        graph.replay()
+        torch.cuda.synchronize()
+        rh, rg, rs = ref[name]
+        assert torch.equal(h.view(torch.int16), rh.view(torch.int16)), name
+        assert torch.equal(gates, rg) and torch.equal(hout, rs), name
+    del graph
+    gw.free()
