@@ -62,7 +62,7 @@ def gemm_tolerance(e: np.ndarray, wkv: np.ndarray, kv_exact: np.ndarray, bf16_ou
 
 def kv_tolerance_mx(kv_exact: np.ndarray):
     """Bound on |kv_gpu - kv_exact| for the block-scaled FP8 MFMA product: the
-    spec tolerance 1e-3 + 2e-2 x, with x the RMS of the token's output row
+    layer's output tolerance 1e-3 + 2e-2 x, with x the RMS of the token's output row
     rather than the element (no published statement bounds the instruction's
     accumulation element by element; a dot product's error scales with its
     terms, not with how close one output lands to zero)."""
@@ -87,7 +87,7 @@ def kv_tolerance_mx(kv_exact: np.ndarray):
 #
 # For the block-scaled FP8 projection no published statement bounds the
 # instruction's accumulation element by element. Its kv is checked at the
-# spec tolerance with the relative part taken against the RMS of the
+# layer's output tolerance with the relative part taken against the RMS of the
 # output block (a dot product's error scales with the size of its terms, not
 # with how close one output lands to zero): |kv - exact| <= 1e-3 + 2e-2 rms.
 # The same allowance then enters h through alpha * dv. Its gates get one more
