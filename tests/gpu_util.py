@@ -98,6 +98,7 @@ def kv_tolerance_mx(kv_exact: np.ndarray):
 # they are counted, and their share must stay below GATE_ZONE_SHARE_MAX.
 
 ALLOW_SHARE_MAX = 1e-4
+ALLOW_SHARE_MAX_MX = 1e-2       # FP8 projection (measured: 1.7e-3 over 2,114 prefill tokens)
 S_ZONE = 0.01
 GATE_ZONE_SHARE_MAX = 1e-3
 
@@ -208,10 +209,10 @@ def check_forward_chunks(*, tokens, rid, dead, fetch_rows, table_f32, table_rows
     if fails:
         raise AssertionError(f"{name}: " + "; ".join(fails[:6]))
     share = stats["allowed"] / max(stats["elements"], 1)
-    if not mx:
-        assert share <= ALLOW_SHARE_MAX, (
-            f"{name}: {stats['allowed']} h elements ({share:.2e}) needed the kv-rounding "
-            f"allowance, more than {ALLOW_SHARE_MAX}")
+    cap = ALLOW_SHARE_MAX_MX if mx else ALLOW_SHARE_MAX
+    assert share <= cap, (
+        f"{name}: {stats['allowed']} h elements ({share:.2e}) needed the kv-rounding "
+        f"allowance, more than {cap}")
     n_gates = stats["tokens"] * hc
     assert stats["gates_in_zone"] <= GATE_ZONE_SHARE_MAX * n_gates, (
         f"{name}: {stats['gates_in_zone']} of {n_gates} gates needed the signed-root allowance")
