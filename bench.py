@@ -3,7 +3,8 @@
 Workload: the full prefill layer forward at the pages' shape -- 4 sequences x
 8192 Zipf(1.1) tokens with 2 DEAD spans of 256 per sequence, the 24 (order,
 head) segments of primes from 1,000,000 (24,003,916 rows x 264 B = 6.34 GB,
-generated on the device), wkv bf16 [25600, 6144], hc = 4 streams of width 5120.
+generated on the device), wkv bf16 [25600, 6144] with its rows 6208 elements
+apart (engram_wkv_row_stride), hc = 4 streams of width 5120.
 All inputs are seeded synthetic data already resident in HBM when timing
 starts.
 
@@ -295,6 +296,9 @@ def main():
                     help="only the gather workload's measurement (profiling its kernel)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
+    ap.add_argument("--wkv-ld", type=int, default=None,
+                    help="row stride of wkv in elements (0: dense rows; default: "
+                         "engram_wkv_row_stride)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: the layer is measured on one GPU only; no multi-GPU run is made.",
@@ -310,7 +314,8 @@ def main():
     if args.decode_only:
         if args.copy_calibration_mib:
             copy_calibration(args.copy_calibration_mib)
-        print(json.dumps({"decode": decode_bench(args.steps, args.warmup)}), flush=True)
+        print(json.dumps({"decode": decode_bench(args.steps, args.warmup, args.wkv_ld)}),
+              flush=True)
         return
     if args.gather_only:
         from workloads import C2
@@ -320,7 +325,7 @@ def main():
               flush=True)
         return
     t_setup = time.perf_counter()
-    gw = GpuWorkload(C3)
+    gw = GpuWorkload(C3, wkv_ld=args.wkv_ld)
     w = gw.w
     T, S = w.tokens, w.segments
     K_in, N_out = S * w.row_dim, (w.hc + 1) * w.dim
@@ -347,7 +352,7 @@ def main():
         E.engram_gather(gw.table, gw.rows, gw.row_format, w.row_dim, rows, T * S, e)
         if evs:
             evs[2].record(stream)
-        E.engram_project(e, gw.wkv, kv, T, K_in, N_out, 0)
+        E.engram_project(e, gw.wkv, kv, T, K_in, N_out, gw.wkv_ld, 0)
         if evs:
             evs[3].record(stream)
         E.engram_fold_gate_weights(gw.q_w, gw.k_w, w.hc, w.dim, qk_w)
@@ -402,7 +407,7 @@ def main():
                                "primes from 1,000,000 (24,003,916 x 264 B rows), wkv "
                                "6144 -> 5 x 5120, hc 4 x 5120",
                    "batch": w.batch, "seq": w.seq, "segments": S, "hc": w.hc, "dim": w.dim,
-                   "table_rows": gw.rows},
+                   "table_rows": gw.rows, "wkv_row_stride": gw.wkv_ld},
         "roofline": {"bound": "mfma", "kernel": "gemm_bf16_kernel (engram_project)",
                      "achieved": round(gemm_tflops, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4),
@@ -442,7 +447,7 @@ def main():
         gw.free()
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
-        out["decode"] = decode_bench(args.steps, args.warmup)
+        out["decode"] = decode_bench(args.steps, args.warmup, args.wkv_ld)
     print(json.dumps(out), flush=True)
 
 
@@ -480,7 +485,7 @@ def conv_prefill_bench(gw, rows, e, kv, gates, steps: int, warmup: int):
         E.engram_gather(gw.table, gw.rows, gw.row_format, w.row_dim, rows, T * S, e)
         if evs:
             evs[2].record(stream)
-        E.engram_project(e, gw.wkv, kv, T, K_in, N_out, 0)
+        E.engram_project(e, gw.wkv, kv, T, K_in, N_out, gw.wkv_ld, 0)
         if evs:
             evs[3].record(stream)
         E.engram_gate_conv(gw.desc, conv, gw.ids, w.raw_vocab, kv, gw.q_w, gw.k_w, gw.h, gates,
@@ -572,7 +577,7 @@ def host_tier_bench(gw, host, rows, e, kv, gates, steps: int, warmup: int):
 
     def compute(slot):
         main.wait_event(ready[slot])
-        E.engram_project(e_buf[slot], gw.wkv, kv, T, K_in, N_out, 0, pws if nws else None, nws,
+        E.engram_project(e_buf[slot], gw.wkv, kv, T, K_in, N_out, gw.wkv_ld, 0, pws if nws else None, nws,
                          stream=main)
         E.engram_fold_gate_weights(gw.q_w, gw.k_w, w.hc, w.dim, qk_w, stream=main)
         E.engram_gate_folded(gw.desc, gw.ids, w.raw_vocab, kv, qk_w, gw.h, gates, stream=main)
@@ -858,7 +863,7 @@ def hash_layers_bench(reps: int):
             "achieved_GBps": round(nbytes / (one * 1e-6) / 1e9, 1)}
 
 
-def decode_bench(steps: int, warmup: int):
+def decode_bench(steps: int, warmup: int, wkv_ld=None):
     """Decode step on the full-size table: 256 sequences x 1 new token with a
     3-token history, 384,006,168 rows (101.4 GB) in HBM; engram_forward per step
     with the history carried in place."""
@@ -868,7 +873,7 @@ def decode_bench(steps: int, warmup: int):
     from workloads.harness import GpuWorkload
 
     t0 = time.perf_counter()
-    gw = GpuWorkload(C4)
+    gw = GpuWorkload(C4, wkv_ld=wkv_ld)
     w = gw.w
     ws, nws = gw.workspace()
     gates = torch.empty((w.tokens, w.hc), dtype=torch.float32, device="cuda")
@@ -920,7 +925,7 @@ def decode_bench(steps: int, warmup: int):
         se[i][1].record(stream)
         E.engram_gather(gw.table, gw.rows, gw.row_format, w.row_dim, rows, T * S, e)
         se[i][2].record(stream)
-        E.engram_project(e, gw.wkv, kv, T, K_in, N_out, 0, pws, pws_n)
+        E.engram_project(e, gw.wkv, kv, T, K_in, N_out, gw.wkv_ld, 0, pws, pws_n)
         se[i][3].record(stream)
         E.engram_gate(gw.desc, gw.ids, w.raw_vocab, kv, gw.q_w, gw.k_w, gw.h, gates)
         se[i][4].record(stream)
@@ -950,7 +955,8 @@ def decode_bench(steps: int, warmup: int):
     conv_ms = ce[0].elapsed_time(ce[1]) / steps
     del cws, sv, ss, cw
     res = {"workload": "decode: 256 sequences x 1 token with a 3-token history, 24 segments of "
-                       "primes from 16,000,000 (384,006,168 x 264 B = 101.4 GB table), hc 4 x 5120",
+                       "primes from 16,000,000 (384,006,168 x 264 B = 101.4 GB table), hc 4 x 5120, "
+                       f"wkv rows {gw.wkv_ld} elements apart",
            "tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
            "graph_replay": {"tokens_per_s": round(T / (graph_ms * 1e-3), 1),
                             "ms_per_step": round(graph_ms, 4)},

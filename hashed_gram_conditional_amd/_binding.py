@@ -68,7 +68,7 @@ class ForwardDesc(ctypes.Structure):
         ("eps", ctypes.c_float),
         ("gate_clamp", ctypes.c_float),
         ("gate_mode", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("wkv_ld", ctypes.c_int32),
     ]
 
 
@@ -119,7 +119,8 @@ def _load():
         "engram_check_token_map": (ctypes.c_int, [P, I32, I32]),
         "engram_hash": (ctypes.c_int, [P, P, I64, I64, P, P, P, P]),
         "engram_gather": (ctypes.c_int, [P, I64, I32, I32, P, I64, P, P]),
-        "engram_project": (ctypes.c_int, [P, P, P, I64, I64, I64, I32, P, SZ, P]),
+        "engram_project": (ctypes.c_int, [P, P, P, I64, I64, I64, I64, I32, P, SZ, P]),
+        "engram_wkv_row_stride": (I64, [I64, I32]),
         "engram_project_workspace_size": (SZ, [I64, I64, I64, I32]),
         "engram_gate": (ctypes.c_int, [P, P, I32, P, P, P, P, P, P]),
         "engram_fold_gate_weights": (ctypes.c_int, [P, P, I32, I32, P, P]),
@@ -134,7 +135,7 @@ def _load():
         "engram_forward": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "engram_forward_static": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, P, P]),
         "engram_forward_static_max_bytes": (SZ, []),
-        "engram_transpose": (ctypes.c_int, [P, P, I64, I64, I32, P]),
+        "engram_transpose": (ctypes.c_int, [P, P, I64, I64, I64, I32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -211,11 +212,11 @@ def hash_params(raw_vocab: int, compressed_vocab: int, max_ngram: int, heads: in
 
 def forward_desc(batch: int, seq: int, hc: int, dim: int, table_rows: int, row_format: int,
                  row_dim: int, eps: float = 1e-6, gate_clamp: float = 0.0,
-                 gate_mode: int = GATE_SIGNED_SQRT) -> ForwardDesc:
+                 gate_mode: int = GATE_SIGNED_SQRT, wkv_ld: int = 0) -> ForwardDesc:
     d = ForwardDesc()
     d.batch, d.seq, d.hc, d.dim = batch, seq, hc, dim
     d.table_rows, d.row_format, d.row_dim = table_rows, row_format, row_dim
-    d.eps, d.gate_clamp, d.gate_mode = eps, gate_clamp, gate_mode
+    d.eps, d.gate_clamp, d.gate_mode, d.wkv_ld = eps, gate_clamp, gate_mode, wkv_ld
     return d
 
 
@@ -287,9 +288,10 @@ def engram_project_workspace_size(tokens: int, in_dim: int, out_dim: int, act_f3
     return LIB.engram_project_workspace_size(tokens, in_dim, out_dim, act_f32)
 
 
-def engram_project(e, wkv, kv, tokens: int, in_dim: int, out_dim: int, act_f32: int,
-                   workspace=None, workspace_bytes: int = 0, stream=None):
-    _check(LIB.engram_project(_ptr(e), _ptr(wkv), _ptr(kv), tokens, in_dim, out_dim, act_f32,
+def engram_project(e, wkv, kv, tokens: int, in_dim: int, out_dim: int, wkv_ld: int,
+                   act_f32: int, workspace=None, workspace_bytes: int = 0, stream=None):
+    _check(LIB.engram_project(_ptr(e), _ptr(wkv), _ptr(kv), tokens, in_dim, out_dim, wkv_ld,
+                              act_f32,
                               _ptr(workspace), workspace_bytes, _stream(stream)),
            "engram_project")
 
@@ -335,9 +337,13 @@ def engram_forward_static(params: HashParams, desc: ForwardDesc, ids, hist_in, h
            "engram_forward_static")
 
 
-def engram_transpose(src, dst, rows: int, cols: int, elem_bytes: int, stream=None):
-    _check(LIB.engram_transpose(_ptr(src), _ptr(dst), rows, cols, elem_bytes, _stream(stream)),
-           "engram_transpose")
+def engram_transpose(src, dst, rows: int, cols: int, dst_ld: int, elem_bytes: int, stream=None):
+    _check(LIB.engram_transpose(_ptr(src), _ptr(dst), rows, cols, dst_ld, elem_bytes,
+                                _stream(stream)), "engram_transpose")
+
+
+def engram_wkv_row_stride(in_dim: int, elem_bytes: int) -> int:
+    return int(LIB.engram_wkv_row_stride(in_dim, elem_bytes))
 
 
 def engram_forward_static_max_bytes() -> int:

@@ -155,8 +155,10 @@ hipError_t engram_launch_gather_f32(const float *table, int64_t table_rows,
                                     int32_t row_dim, const int64_t *row_ids,
                                     int64_t n_ids, float *out, hipStream_t stream);
 
-hipError_t engram_launch_gemm_bf16(const uint16_t *e, const uint16_t *w, uint16_t *kv,
-                                   int64_t m, int64_t n, int64_t k, void *workspace,
+// bf16 projection kv[m, n] = sum_k e[m, k] w[n, k]; w's rows are ldw >= k
+// elements apart, e and kv are dense.
+hipError_t engram_launch_gemm_bf16(const uint16_t *e, const uint16_t *w, int64_t ldw,
+                                   uint16_t *kv, int64_t m, int64_t n, int64_t k, void *workspace,
                                    size_t workspace_bytes, hipStream_t stream);
 
 // Workspace the bf16 projection uses for a split-K schedule (0 when none).
@@ -172,8 +174,8 @@ hipError_t engram_launch_gemm_mx(const uint8_t *w_codes, const uint8_t *w_scales
                                  hipStream_t stream);
 hipError_t engram_gemm_mx_workspace(int64_t m, int64_t n, int32_t segments, size_t *bytes);
 
-hipError_t engram_launch_gemm_f32(const float *e, const float *w, float *kv, int64_t m,
-                                  int64_t n, int64_t k, hipStream_t stream);
+hipError_t engram_launch_gemm_f32(const float *e, const float *w, int64_t ldw, float *kv,
+                                  int64_t m, int64_t n, int64_t k, hipStream_t stream);
 
 // Which positions are DEAD. A raw id outside [0, raw_vocab) always is; with a
 // token map, so is a raw id whose compressed id lies outside
@@ -222,7 +224,7 @@ hipError_t engram_launch_short_conv(bool f32, const EngramConvArgs &c, const int
                                     void *h, int64_t batch, int64_t seq, int32_t hc,
                                     int32_t dim, hipStream_t stream);
 
-// dst[c, r] = src[r, c] for a row-major [rows, cols] array of 2- or 4-byte
-// elements (layout.hip).
+// dst[c * dst_ld + r] = src[r, c] for a row-major [rows, cols] array of 2- or
+// 4-byte elements (layout.hip).
 hipError_t engram_launch_transpose(const void *src, void *dst, int64_t rows, int64_t cols,
-                                   int elem_bytes, hipStream_t stream);
+                                   int64_t dst_ld, int elem_bytes, hipStream_t stream);

@@ -159,7 +159,7 @@ int check_desc(const engram_forward_desc *d) {
   if (!(d->eps >= 0.f) || !(d->gate_clamp >= 0.f)) return ENGRAM_EINVAL;
   if (d->gate_mode != ENGRAM_GATE_SIGNED_SQRT && d->gate_mode != ENGRAM_GATE_PLAIN)
     return ENGRAM_EINVAL;
-  if (d->reserved != 0) return ENGRAM_EINVAL;
+  if (d->wkv_ld < 0) return ENGRAM_ESHAPE;
   return ENGRAM_OK;
 }
 
@@ -206,6 +206,17 @@ bool bf16_projection_shape_ok(int64_t tokens, int64_t in_dim, int64_t out_dim) {
   const int64_t tiles_m = (tokens + 255) / 256;
   const int64_t tiles_n = (out_dim + 127) / 128;
   return tiles_m * tiles_n <= ((int64_t)1 << 32) / 512 - 1;
+}
+
+// Row stride of wkv in elements: 0 means in_dim (dense rows). Otherwise at least
+// in_dim and a multiple of 16 bytes, so that every row starts 16-byte aligned;
+// for bf16 within the same 32-bit panel bound as in_dim.
+int wkv_row_stride(int64_t ld, int64_t in_dim, bool f32, int64_t *out) {
+  if (ld == 0) ld = in_dim;
+  if (ld < in_dim || ld % (f32 ? 4 : 8) != 0) return ENGRAM_ESHAPE;
+  if (!f32 && ld > kMaxProjectInDim) return ENGRAM_ESHAPE;
+  *out = ld;
+  return ENGRAM_OK;
 }
 
 // The stage entry points (engram_gate, engram_gate_conv) know only the raw ids;
@@ -487,8 +498,8 @@ size_t engram_project_workspace_size(int64_t tokens, int64_t in_dim, int64_t out
 }
 
 int engram_project(const void *e, const void *wkv, void *kv, int64_t tokens, int64_t in_dim,
-                   int64_t out_dim, int32_t act_f32, void *workspace, size_t workspace_bytes,
-                   hipStream_t stream) {
+                   int64_t out_dim, int64_t wkv_ld, int32_t act_f32, void *workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
   if (tokens < 0 || in_dim < 1 || out_dim < 1) return ENGRAM_ESHAPE;
   if (act_f32 != 0 && act_f32 != 1) return ENGRAM_EINVAL;
   if (act_f32) {
@@ -498,6 +509,9 @@ int engram_project(const void *e, const void *wkv, void *kv, int64_t tokens, int
   }
   if (tokens > INT32_MAX || out_dim > INT32_MAX || in_dim > INT32_MAX) return ENGRAM_ESHAPE;
   if (!act_f32 && !bf16_projection_shape_ok(tokens, in_dim, out_dim)) return ENGRAM_ESHAPE;
+  int64_t ldw = 0;
+  const int rc = wkv_row_stride(wkv_ld, in_dim, act_f32 != 0, &ldw);
+  if (rc != ENGRAM_OK) return rc;
   if (tokens == 0) return ENGRAM_OK;
   if (e == nullptr || wkv == nullptr || kv == nullptr) return ENGRAM_EINVAL;
   if (!aligned(e, 16) || !aligned(wkv, 16) || !aligned(kv, 16)) return ENGRAM_EINVAL;
@@ -506,11 +520,12 @@ int engram_project(const void *e, const void *wkv, void *kv, int64_t tokens, int
         workspace_bytes < engram_project_workspace_size(tokens, in_dim, out_dim, act_f32))
       return ENGRAM_EWORKSPACE;
   }
-  hipError_t err = act_f32 ? engram_launch_gemm_f32((const float *)e, (const float *)wkv,
-                                                    (float *)kv, tokens, out_dim, in_dim, stream)
-                           : engram_launch_gemm_bf16((const uint16_t *)e, (const uint16_t *)wkv,
-                                                     (uint16_t *)kv, tokens, out_dim, in_dim,
-                                                     workspace, workspace_bytes, stream);
+  hipError_t err =
+      act_f32 ? engram_launch_gemm_f32((const float *)e, (const float *)wkv, ldw, (float *)kv,
+                                       tokens, out_dim, in_dim, stream)
+              : engram_launch_gemm_bf16((const uint16_t *)e, (const uint16_t *)wkv, ldw,
+                                        (uint16_t *)kv, tokens, out_dim, in_dim, workspace,
+                                        workspace_bytes, stream);
   return hip_status(err);
 }
 
@@ -562,11 +577,16 @@ int engram_gate_folded(const engram_forward_desc *desc, const int32_t *ids, int3
                                        stream));
 }
 
-int engram_transpose(const void *src, void *dst, int64_t rows, int64_t cols,
+int engram_transpose(const void *src, void *dst, int64_t rows, int64_t cols, int64_t dst_ld,
                      int32_t elem_bytes, hipStream_t stream) {
   if (elem_bytes != 2 && elem_bytes != 4) return ENGRAM_EINVAL;
-  if (rows < 0 || cols < 0) return ENGRAM_ESHAPE;
+  if (rows < 0 || cols < 0 || dst_ld < 0) return ENGRAM_ESHAPE;
+  if (dst_ld == 0) dst_ld = rows;
+  if (dst_ld < rows) return ENGRAM_ESHAPE;
   if (rows == 0 || cols == 0) return ENGRAM_OK;
+  // the destination's extent, (cols - 1) dst_ld + rows elements, in bytes below 2^62
+  if (cols > 1 && dst_ld > (((int64_t)1 << 62) / elem_bytes - rows) / (cols - 1))
+    return ENGRAM_ESHAPE;
   // 64 x 64 tiles of 256 threads: at most 2^24 tiles keeps the grid within 2^32
   // threads.
   const int64_t tr = (rows + 63) / 64, tc = (cols + 63) / 64;
@@ -574,9 +594,17 @@ int engram_transpose(const void *src, void *dst, int64_t rows, int64_t cols,
   if (src == nullptr || dst == nullptr) return ENGRAM_EINVAL;
   if (!aligned(src, elem_bytes) || !aligned(dst, elem_bytes)) return ENGRAM_EINVAL;
   const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
-  const uintptr_t n = (uintptr_t)(rows * cols * elem_bytes);
-  if (s0 < d0 + n && d0 < s0 + n) return ENGRAM_EINVAL;        // overlapping buffers
-  return hip_status(engram_launch_transpose(src, dst, rows, cols, elem_bytes, stream));
+  const uintptr_t ns = (uintptr_t)(rows * cols * elem_bytes);
+  const uintptr_t nd = (uintptr_t)(((cols - 1) * dst_ld + rows) * elem_bytes);
+  if (s0 < d0 + nd && d0 < s0 + ns) return ENGRAM_EINVAL;      // overlapping buffers
+  return hip_status(engram_launch_transpose(src, dst, rows, cols, dst_ld, elem_bytes, stream));
+}
+
+int64_t engram_wkv_row_stride(int64_t in_dim, int32_t elem_bytes) {
+  if (in_dim < 1 || in_dim > kMaxProjectInDim || (elem_bytes != 2 && elem_bytes != 4)) return 0;
+  int64_t bytes = (in_dim * elem_bytes + 127) / 128 * 128;
+  if (bytes % 4096 == 0) bytes += 128;
+  return bytes / elem_bytes;
 }
 
 size_t engram_gate_conv_workspace_size(const engram_forward_desc *desc) {
@@ -661,6 +689,8 @@ int forward_impl(const engram_hash_params *params, const engram_forward_desc *de
   if (!f32 && in_dim % 64) return ENGRAM_ESHAPE;
   if (ntok > INT32_MAX) return ENGRAM_ESHAPE;
   if (!f32 && !bf16_projection_shape_ok(ntok, in_dim, out_dim)) return ENGRAM_ESHAPE;
+  int64_t ldw = 0;
+  if ((rc = wkv_row_stride(desc->wkv_ld, in_dim, f32, &ldw)) != ENGRAM_OK) return rc;
   bool host = false;
   if (ntok > 0) {
     if (ids == nullptr || table == nullptr || wkv == nullptr || q_w == nullptr ||
@@ -711,9 +741,9 @@ int forward_impl(const engram_hash_params *params, const engram_forward_desc *de
             : engram_launch_gather_e4m3((const uint8_t *)table, desc->table_rows, row_ids,
                                         ntok * S, (uint16_t *)e, host, stream);
   if (err != hipSuccess) return hip_status(err);
-  err = f32 ? engram_launch_gemm_f32((const float *)e, (const float *)wkv, (float *)kv, ntok,
-                                     out_dim, in_dim, stream)
-            : engram_launch_gemm_bf16((const uint16_t *)e, (const uint16_t *)wkv,
+  err = f32 ? engram_launch_gemm_f32((const float *)e, (const float *)wkv, ldw, (float *)kv,
+                                     ntok, out_dim, in_dim, stream)
+            : engram_launch_gemm_bf16((const uint16_t *)e, (const uint16_t *)wkv, ldw,
                                       (uint16_t *)kv, ntok, out_dim, in_dim, gemm_ws,
                                       gemm_ws_bytes, stream);
   if (err != hipSuccess) return hip_status(err);

@@ -10,6 +10,11 @@
 // W rows feed the MFMA's first operand and E rows the second, so each lane's
 // accumulator holds 4 consecutive output columns of one token and the epilogue
 // writes 8-byte bf16 quads. K advances in steps of 64 through two LDS stages.
+// W's rows sit ldw >= K elements apart (E's are dense). With rows a multiple of
+// 4 KiB apart (K = 6144: 12 KiB), a K-step's loads from all CUs fall at the
+// same offset within a memory page, and a call that streams W from HBM once
+// (the decode schedule below) loses ~10 % to it. A row stride of 128 bytes
+// more spreads them; the products and their bits do not depend on ldw.
 // In LDS, 16-byte chunk c of a 128-byte row r sits in slot
 // c ^ (r & 7) ^ ((r >> 3) & 1): the fragment reads of any 16 consecutive rows
 // (one b128 read phase) then touch 16 distinct bank groups, and so do the
@@ -59,7 +64,8 @@ struct WideLds {
 // the panel or zeros and are never used.
 __device__ __forceinline__ void wide_tile(const uint16_t *__restrict__ E,
                                           const uint16_t *__restrict__ W, int M, int N, int K,
-                                          int m0, int n0, int ks, int ke, f32x16 (&acc)[4][4],
+                                          int ldw, int m0, int n0, int ks, int ke,
+                                          f32x16 (&acc)[4][4],
                                           WideLds &lds) {
   uint16_t (*sW)[BN * BK] = lds.w;
   uint16_t (*sE)[BM * BK] = lds.e;
@@ -72,7 +78,7 @@ __device__ __forceinline__ void wide_tile(const uint16_t *__restrict__ E,
   const int rows_w = min(BN, N - n0);
   const int rows_e = min(BM, M - m0);
   const __amdgpu_buffer_rsrc_t rsW = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t *>(W + (int64_t)n0 * K), 0, rows_w * K * 2, kBufferFlags);
+      const_cast<uint16_t *>(W + (int64_t)n0 * ldw), 0, rows_w * ldw * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t rsE = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(E + (int64_t)m0 * K), 0, rows_e * K * 2, kBufferFlags);
   // A step's operands are 16 chunks of 16 bytes per thread: chunk i < 8 is W
@@ -81,8 +87,8 @@ __device__ __forceinline__ void wide_tile(const uint16_t *__restrict__ E,
   // is a multiple of 16, the slot depends on t only.
   const int g_row = tid >> 3;
   const int g_chunk = tid & 7;
-  const int g_voff = (g_row * K + g_chunk * 8) * 2;
-  const int g_rstride = 32 * K * 2;
+  const int g_voff_w = (g_row * ldw + g_chunk * 8) * 2, g_voff_e = (g_row * K + g_chunk * 8) * 2;
+  const int g_rstride_w = 32 * ldw * 2, g_rstride_e = 32 * K * 2;
   const int s_off = g_row * BK + ((g_chunk ^ (g_row & 7) ^ ((g_row >> 3) & 1)) << 3);
   // Fragment reads: lane l reads row (base + l % 32), K-chunk 2 kk + l / 32.
   const int frow = lane & 31;
@@ -97,9 +103,11 @@ __device__ __forceinline__ void wide_tile(const uint16_t *__restrict__ E,
 #define ENGRAM_LOADQ(g, kt_, q)                                                               \
   _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                           \
     if ((q) < 2)                                                                            \
-      g[(q) * 4 + i] = load16(rsW, g_voff, ((q) * 4 + i) * g_rstride + (kt_) * BK * 2);     \
+      g[(q) * 4 + i] =                                                                      \
+          load16(rsW, g_voff_w, ((q) * 4 + i) * g_rstride_w + (kt_) * BK * 2);              \
     else                                                                                    \
-      g[(q) * 4 + i] = load16(rsE, g_voff, ((q) * 4 + i - 8) * g_rstride + (kt_) * BK * 2); \
+      g[(q) * 4 + i] =                                                                      \
+          load16(rsE, g_voff_e, ((q) * 4 + i - 8) * g_rstride_e + (kt_) * BK * 2);          \
   }
 #define ENGRAM_STOREQ(g, st, q)                                                               \
   _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                           \
@@ -203,13 +211,14 @@ __device__ __forceinline__ void wide_tile(const uint16_t *__restrict__ E,
 
 __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_kernel(const uint16_t *__restrict__ E, const uint16_t *__restrict__ W,
-                      uint16_t *__restrict__ C, int M, int N, int K, int tiles_m, int tiles_n) {
+                      uint16_t *__restrict__ C, int M, int N, int K, int ldw, int tiles_m,
+                      int tiles_n) {
   __shared__ __align__(1024) WideLds lds;
   int m0, n0;
   tile_origin(tiles_m, tiles_n, BN, m0, n0);
   f32x16 acc[4][4];
   zero_acc(acc);
-  wide_tile(E, W, M, N, K, m0, n0, 0, K / BK, acc, lds);
+  wide_tile(E, W, M, N, K, ldw, m0, n0, 0, K / BK, acc, lds);
   wide_store_bf16(acc, C, M, N, m0, n0);
 }
 
@@ -237,21 +246,21 @@ struct SkinnyLds {
 template <int NT>
 __device__ __forceinline__ void skinny_block(const uint16_t *__restrict__ E,
                                              const uint16_t *__restrict__ W,
-                                             uint16_t *__restrict__ C, int M, int N, int K, int c0,
-                                             SkinnyLds &lds) {
+                                             uint16_t *__restrict__ C, int M, int N, int K,
+                                             int ldw, int c0, SkinnyLds &lds) {
   const int KT = K / BK;                    // multiple of kSkRing (checked by the launcher)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int cols = min(32 * NT, N - c0);
   const __amdgpu_buffer_rsrc_t rsW = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t *>(W + (int64_t)c0 * K), 0, cols * K * 2, kBufferFlags);
+      const_cast<uint16_t *>(W + (int64_t)c0 * ldw), 0, cols * ldw * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t rsE = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(E), 0, min(M, BM) * K * 2, kBufferFlags);
   // chunk q of a step: row q * 32 + t / 8, 16-byte column t % 8 (as in the wide kernel)
   const int g_row = tid >> 3, g_chunk = tid & 7;
-  const int g_voff = (g_row * K + g_chunk * 8) * 2;
-  const int g_rstride = 32 * K * 2;
+  const int g_voff_w = (g_row * ldw + g_chunk * 8) * 2, g_voff_e = (g_row * K + g_chunk * 8) * 2;
+  const int g_rstride_w = 32 * ldw * 2, g_rstride_e = 32 * K * 2;
   const int s_off = g_row * BK + ((g_chunk ^ (g_row & 7) ^ ((g_row >> 3) & 1)) << 3);
   const int frow = lane & 31, fk = lane >> 5;
   const int fsw = (frow & 7) ^ ((frow >> 3) & 1);
@@ -270,10 +279,10 @@ __device__ __forceinline__ void skinny_block(const uint16_t *__restrict__ E,
 #define SK_KOFF(kt_) (((kt_) < KT ? (kt_) : KT - 1) * BK * 2)
 #define SK_LOADE(slot, kt_, q0, q1)                                                           \
   _Pragma("unroll") for (int q = q0; q < q1; ++q)                                           \
-    er[slot][q] = load16(rsE, g_voff, q * g_rstride + SK_KOFF(kt_));
+    er[slot][q] = load16(rsE, g_voff_e, q * g_rstride_e + SK_KOFF(kt_));
 #define SK_LOADW(slot, kt_, q0, q1)                                                           \
   _Pragma("unroll") for (int q = q0; q < q1; ++q)                                           \
-    wr[slot][q] = load16(rsW, g_voff, q * g_rstride + SK_KOFF(kt_));
+    wr[slot][q] = load16(rsW, g_voff_w, q * g_rstride_w + SK_KOFF(kt_));
 #define SK_STOREE(st, slot, q0, q1)                                                           \
   _Pragma("unroll") for (int q = q0; q < q1; ++q)                                           \
     *reinterpret_cast<uint4 *>(&lds.e[st][s_off + q * 32 * BK]) = er[slot][q];
@@ -373,24 +382,25 @@ __device__ __forceinline__ void skinny_block(const uint16_t *__restrict__ E,
 // first `wide` blocks.
 __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_skinny_kernel(const uint16_t *__restrict__ E, const uint16_t *__restrict__ W,
-                             uint16_t *__restrict__ C, int M, int N, int K, int w_lo, int wide) {
+                             uint16_t *__restrict__ C, int M, int N, int K, int ldw, int w_lo,
+                             int wide) {
   __shared__ __align__(1024) SkinnyLds lds;
   const int b = blockIdx.x;
   const int c0 = b * w_lo + min(b, wide) * 32;
   if (c0 >= N) return;
   const int nt = (w_lo + (b < wide ? 32 : 0)) / 32;
   if (nt == 4)
-    skinny_block<4>(E, W, C, M, N, K, c0, lds);
+    skinny_block<4>(E, W, C, M, N, K, ldw, c0, lds);
   else if (nt == 3)
-    skinny_block<3>(E, W, C, M, N, K, c0, lds);
+    skinny_block<3>(E, W, C, M, N, K, ldw, c0, lds);
   else
-    skinny_block<2>(E, W, C, M, N, K, c0, lds);
+    skinny_block<2>(E, W, C, M, N, K, ldw, c0, lds);
 }
 
 __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_streamk_kernel(const uint16_t *__restrict__ E, const uint16_t *__restrict__ W,
                               uint16_t *__restrict__ C, float *__restrict__ ws, int M, int N,
-                              int K, StreamK sk) {
+                              int K, int ldw, StreamK sk) {
   __shared__ __align__(1024) WideLds lds;
   const int b = blockIdx.x;
   const int64_t u0 = sk.start(b), u1 = sk.start(b + 1);
@@ -403,7 +413,7 @@ void gemm_bf16_streamk_kernel(const uint16_t *__restrict__ E, const uint16_t *__
     const int m0 = (int)(tile % sk.tiles_m) * BM;
     const int n0 = (int)(tile / sk.tiles_m) * BN;
     zero_acc(acc);
-    wide_tile(E, W, M, N, K, m0, n0, ks, ke, acc, lds);
+    wide_tile(E, W, M, N, K, ldw, m0, n0, ks, ke, acc, lds);
     if (ks == 0 && ke == sk.kt) {
       wide_store_bf16(acc, C, M, N, m0, n0);
     } else {
@@ -466,7 +476,7 @@ __global__ __launch_bounds__(kWideThreads) void gemm_streamk_fixup_kernel(
 template <int TN>
 __global__ __launch_bounds__(kNarrowThreads) void gemm_bf16_narrow_kernel(
     const uint16_t *__restrict__ E, const uint16_t *__restrict__ W, uint16_t *__restrict__ C,
-    int M, int N, int K, int tiles_m, int tiles_n) {
+    int M, int N, int K, int ldw, int tiles_m, int tiles_n) {
   constexpr int TI = TN / 64;          // 32-row MFMA tiles per wave along n
   constexpr int WR = TN / 64;          // W-panel direct loads per wave per stage
   __shared__ __align__(1024) uint16_t sW0[TN * BK];
@@ -485,7 +495,7 @@ __global__ __launch_bounds__(kNarrowThreads) void gemm_bf16_narrow_kernel(
   const int rows_w = min(TN, N - n0);
   const int rows_e = min(BM, M - m0);
   const __amdgpu_buffer_rsrc_t rsW = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t *>(W + (int64_t)n0 * K), 0, rows_w * K * 2, kBufferFlags);
+      const_cast<uint16_t *>(W + (int64_t)n0 * ldw), 0, rows_w * ldw * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t rsE = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(E + (int64_t)m0 * K), 0, rows_e * K * 2, kBufferFlags);
   // Direct loads: row (R w + i) * 8 + p / 8 has (row & 7) = p / 8 and, R being
@@ -494,11 +504,11 @@ __global__ __launch_bounds__(kNarrowThreads) void gemm_bf16_narrow_kernel(
   const int dl_c0 = (lane & 7) ^ (lane >> 3);
   const int dl_rw = wave * WR * 8 + (lane >> 3);
   const int dl_re = wave * 32 + (lane >> 3);
-  const int dl_w0 = (dl_rw * K + dl_c0 * 8) * 2;
-  const int dl_w1 = (dl_rw * K + (dl_c0 ^ 1) * 8) * 2;
+  const int dl_w0 = (dl_rw * ldw + dl_c0 * 8) * 2;
+  const int dl_w1 = (dl_rw * ldw + (dl_c0 ^ 1) * 8) * 2;
   const int dl_e0 = (dl_re * K + dl_c0 * 8) * 2;
   const int dl_e1 = (dl_re * K + (dl_c0 ^ 1) * 8) * 2;
-  const int rstride8 = 8 * K * 2;
+  const int rstride8_w = 8 * ldw * 2, rstride8_e = 8 * K * 2;
   // Fragment reads: lane l reads row (base + l % 32), K-chunk 2 kk + l / 32.
   const int frow = lane & 31;
   const int fk = lane >> 5;
@@ -519,12 +529,12 @@ __global__ __launch_bounds__(kNarrowThreads) void gemm_bf16_narrow_kernel(
   _Pragma("unroll") for (int i = 0; i < WR; ++i) {                                          \
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, ENGRAM_LDS((dW) + (wave * WR + i) * 512), \
                                              16, (i & 1) ? dl_w1 : dl_w0,                   \
-                                             i * rstride8 + (kt_) * BK * 2, 0, 0);          \
+                                             i * rstride8_w + (kt_) * BK * 2, 0, 0);        \
   }                                                                                         \
   _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                           \
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsE, ENGRAM_LDS((dE) + (wave * 4 + i) * 512),  \
                                              16, (i & 1) ? dl_e1 : dl_e0,                   \
-                                             i * rstride8 + (kt_) * BK * 2, 0, 0);          \
+                                             i * rstride8_e + (kt_) * BK * 2, 0, 0);        \
   }
 #define ENGRAM_FRAGS(buf_w, buf_e, kk, dst_a, dst_b)                                          \
   _Pragma("unroll") for (int i = 0; i < TI; ++i) dst_a[i] =                                 \
@@ -608,13 +618,13 @@ __global__ __launch_bounds__(kNarrowThreads) void gemm_bf16_narrow_kernel(
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *__restrict__ E,
                                                        const float *__restrict__ W,
                                                        float *__restrict__ C, int64_t M,
-                                                       int64_t N, int64_t K) {
+                                                       int64_t N, int64_t K, int64_t ldw) {
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (g >= M * N) return;
   const int64_t m = g / N;
   const int64_t n = g - m * N;
   const float *e = E + m * K;
-  const float *w = W + n * K;
+  const float *w = W + n * ldw;
   float acc = 0.f;
   for (int64_t k = 0; k < K; ++k) acc = fmaf(e[k], w[k], acc);
   C[g] = acc;
@@ -653,8 +663,8 @@ hipError_t engram_gemm_bf16_workspace(int64_t m, int64_t n, int64_t k, size_t *b
   return hipSuccess;
 }
 
-hipError_t engram_launch_gemm_bf16(const uint16_t *e, const uint16_t *w, uint16_t *kv,
-                                   int64_t m, int64_t n, int64_t k, void *workspace,
+hipError_t engram_launch_gemm_bf16(const uint16_t *e, const uint16_t *w, int64_t ldw,
+                                   uint16_t *kv, int64_t m, int64_t n, int64_t k, void *workspace,
                                    size_t workspace_bytes, hipStream_t stream) {
   if (m <= 0 || n <= 0) return hipSuccess;
   int w_lo = 0, wide = 0, sk_blocks = 0;
@@ -662,7 +672,7 @@ hipError_t engram_launch_gemm_bf16(const uint16_t *e, const uint16_t *w, uint16_
   if (err != hipSuccess) return err;
   if (sk_blocks > 0) {
     hipLaunchKernelGGL(gemm_bf16_skinny_kernel, dim3((unsigned)sk_blocks), dim3(kWideThreads), 0,
-                       stream, e, w, kv, (int)m, (int)n, (int)k, w_lo, wide);
+                       stream, e, w, kv, (int)m, (int)n, (int)k, (int)ldw, w_lo, wide);
     return hipGetLastError();
   }
   StreamK sk;
@@ -672,14 +682,15 @@ hipError_t engram_launch_gemm_bf16(const uint16_t *e, const uint16_t *w, uint16_
   const int tiles_n256 = (int)((n + BN - 1) / BN);
   if (sk.blocks == 0) {
     hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)(tiles_m * tiles_n256)),
-                       dim3(kWideThreads), 0, stream, e, w, kv, (int)m, (int)n, (int)k, tiles_m,
-                       tiles_n256);
+                       dim3(kWideThreads), 0, stream, e, w, kv, (int)m, (int)n, (int)k, (int)ldw,
+                       tiles_m, tiles_n256);
     return hipGetLastError();
   }
   const size_t need = (size_t)sk.blocks * 2 * kWideOutputs * kWideThreads * sizeof(float);
   if (workspace != nullptr && workspace_bytes >= need) {
     hipLaunchKernelGGL(gemm_bf16_streamk_kernel, dim3((unsigned)sk.blocks), dim3(kWideThreads), 0,
-                       stream, e, w, kv, (float *)workspace, (int)m, (int)n, (int)k, sk);
+                       stream, e, w, kv, (float *)workspace, (int)m, (int)n, (int)k, (int)ldw,
+                       sk);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     return engram_gemm::launch_streamk_fixup((const float *)workspace, kv, m, n, sk, stream);
@@ -687,17 +698,17 @@ hipError_t engram_launch_gemm_bf16(const uint16_t *e, const uint16_t *w, uint16_
   // No workspace: 128-wide tiles over the whole K.
   const int tiles_n128 = (int)((n + 127) / 128);
   hipLaunchKernelGGL(gemm_bf16_narrow_kernel<128>, dim3((unsigned)(tiles_m * tiles_n128)),
-                     dim3(kNarrowThreads), 0, stream, e, w, kv, (int)m, (int)n, (int)k, tiles_m,
-                     tiles_n128);
+                     dim3(kNarrowThreads), 0, stream, e, w, kv, (int)m, (int)n, (int)k, (int)ldw,
+                     tiles_m, tiles_n128);
   return hipGetLastError();
 }
 
-hipError_t engram_launch_gemm_f32(const float *e, const float *w, float *kv, int64_t m,
-                                  int64_t n, int64_t k, hipStream_t stream) {
+hipError_t engram_launch_gemm_f32(const float *e, const float *w, int64_t ldw, float *kv,
+                                  int64_t m, int64_t n, int64_t k, hipStream_t stream) {
   if (m <= 0 || n <= 0) return hipSuccess;
   const int64_t blocks = (m * n + 255) / 256;
   hipLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, e, w, kv,
-                     m, n, k);
+                     m, n, k, ldw);
   return hipGetLastError();
 }
 

@@ -10,12 +10,13 @@ constexpr int kTile = 64;
 constexpr int kThreads = 256;
 
 // Each block moves one 64 x 64 tile through LDS: reads along the source rows,
-// writes along the destination rows, both coalesced. The extra column keeps
+// writes along the destination rows (dst_ld elements apart), both coalesced. The extra column keeps
 // the transposed LDS reads off a single bank.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void transpose_kernel(const T *__restrict__ src,
                                                              T *__restrict__ dst, int64_t rows,
-                                                             int64_t cols, int64_t tiles_c) {
+                                                             int64_t cols, int64_t dst_ld,
+                                                             int64_t tiles_c) {
   __shared__ T tile[kTile][kTile + 1];
   const int64_t b = blockIdx.x;
   const int64_t tr = b / tiles_c;
@@ -28,22 +29,24 @@ __global__ __launch_bounds__(kThreads) void transpose_kernel(const T *__restrict
   __syncthreads();
   for (int i = ty; i < kTile; i += kThreads / kTile) {
     const int64_t c = c0 + i, r = r0 + tx;
-    if (c < cols && r < rows) dst[c * rows + r] = tile[tx][i];
+    if (c < cols && r < rows) dst[c * dst_ld + r] = tile[tx][i];
   }
 }
 
 }  // namespace
 
 hipError_t engram_launch_transpose(const void *src, void *dst, int64_t rows, int64_t cols,
-                                   int elem_bytes, hipStream_t stream) {
+                                   int64_t dst_ld, int elem_bytes, hipStream_t stream) {
   if (rows <= 0 || cols <= 0) return hipSuccess;
   const int64_t tiles_c = (cols + kTile - 1) / kTile;
   const int64_t blocks = ((rows + kTile - 1) / kTile) * tiles_c;
   if (elem_bytes == 2)
     hipLaunchKernelGGL(transpose_kernel<uint16_t>, dim3((unsigned)blocks), dim3(kThreads), 0,
-                       stream, (const uint16_t *)src, (uint16_t *)dst, rows, cols, tiles_c);
+                       stream, (const uint16_t *)src, (uint16_t *)dst, rows, cols, dst_ld,
+                       tiles_c);
   else
     hipLaunchKernelGGL(transpose_kernel<uint32_t>, dim3((unsigned)blocks), dim3(kThreads), 0,
-                       stream, (const uint32_t *)src, (uint32_t *)dst, rows, cols, tiles_c);
+                       stream, (const uint32_t *)src, (uint32_t *)dst, rows, cols, dst_ld,
+                       tiles_c);
   return hipGetLastError();
 }

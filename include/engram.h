@@ -147,7 +147,9 @@ typedef struct engram_forward_desc {
   float eps;                  /* RMS epsilon (1e-6)                                */
   float gate_clamp;           /* c in sqrt(max(|s|, c)) (0)                        */
   int32_t gate_mode;          /* engram_gate_mode (ENGRAM_GATE_SIGNED_SQRT)         */
-  int32_t reserved;           /* must be 0                                         */
+  int32_t wkv_ld;             /* elements between consecutive wkv rows; 0 = dense
+                                 (S row_dim). See engram_project. Ignored by the
+                                 entry points that take no wkv                     */
 } engram_forward_desc;
 
 /*
@@ -321,6 +323,18 @@ int engram_gather_mx(const void *table, int64_t table_rows, const int64_t *row_i
  * matrix; [P4] "消费": the weight is stored with the 6144 inputs innermost).
  *   e    [tokens, in_dim]       bf16 (act_f32 = 0) or float (act_f32 = 1)
  *   wkv  [out_dim, in_dim]      same type; row c holds the weights of output c
+ *                               and starts wkv_ld elements after row c - 1; the
+ *                               buffer holds at least (out_dim - 1) wkv_ld +
+ *                               in_dim elements (the gaps are never read)
+ *   wkv_ld                      0 (= in_dim, dense rows), or >= in_dim and a
+ *                               multiple of 16 bytes, at most 2^20 for bf16.
+ *                               The results do not depend on it. Rows a
+ *                               multiple of 4 KiB apart (in_dim 6144 bf16)
+ *                               put every CU's loads of one K-step at the same
+ *                               offset within a memory page, which costs a
+ *                               call that streams the weight from HBM once
+ *                               (<= 256 tokens) about 10 %;
+ *                               engram_wkv_row_stride gives a stride that avoids it
  *   kv   [tokens, out_dim]      same type; fp32 accumulation, bf16 rounded to
  *                               nearest-even
  *   workspace, workspace_bytes
@@ -339,12 +353,18 @@ int engram_gather_mx(const void *table, int64_t table_rows, const int64_t *row_i
  * 256-row operand panel with 32-bit byte counts and launch at most 2^32
  * threads); fp32 requires in_dim % 4 == 0 and out_dim % 4 == 0. The same tile
  * bound applies to engram_project_mx and to the forward entry points.
- * Errors: ENGRAM_EINVAL, ENGRAM_ESHAPE, ENGRAM_EWORKSPACE (non-NULL and too
- * small or misaligned), ENGRAM_EHIP.
+ * Errors: ENGRAM_EINVAL, ENGRAM_ESHAPE (also a wkv_ld outside the rule above),
+ * ENGRAM_EWORKSPACE (non-NULL and too small or misaligned), ENGRAM_EHIP.
  */
 int engram_project(const void *e, const void *wkv, void *kv, int64_t tokens,
-                   int64_t in_dim, int64_t out_dim, int32_t act_f32, void *workspace,
-                   size_t workspace_bytes, hipStream_t stream);
+                   int64_t in_dim, int64_t out_dim, int64_t wkv_ld, int32_t act_f32,
+                   void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* [host] A wkv row stride for engram_project and engram_forward_desc.wkv_ld:
+ * in_dim rounded up to 128 bytes, plus 128 bytes when that is a multiple of
+ * 4 KiB (6144 bf16 -> 6208). 0 for in_dim outside [1, 2^20] or elem_bytes not 2
+ * or 4. */
+int64_t engram_wkv_row_stride(int64_t in_dim, int32_t elem_bytes);
 
 /* [host] Bytes of workspace engram_project uses for these sizes on the current
  * device (0 if it needs none, on bad arguments or on a HIP error). */
@@ -375,22 +395,24 @@ int engram_project_mx(const void *e_codes, const void *e_scales, int32_t segment
 
 /*
  * Re-layout of a caller's weight buffer, once, outside the per-step path:
- * dst[c, r] = src[r, c] for a row-major [rows, cols] array of 2-byte (bf16) or
- * 4-byte (fp32) elements. The kernels read wkv as [(hc+1) dim, S row_dim]
+ * dst[c * dst_ld + r] = src[r, c] for a row-major [rows, cols] array of 2-byte
+ * (bf16) or 4-byte (fp32) elements; dst_ld = 0 means rows (dense). The kernels read wkv as [(hc+1) dim, S row_dim]
  * (inputs innermost, [P4] "消费") and the gate scales as [hc, dim]. A caller
  * holding them the other way round, wkv as [S row_dim, (hc+1) dim] (the
  * 6144 x 25600 matrix of [P1] "每条流一个 key 的设计沿用自原版" with outputs
  * innermost) or q_w / k_w as [dim, hc], calls
- *   engram_transpose(wkv_in_out, wkv, S row_dim, (hc+1) dim, 2 or 4, stream)
- *   engram_transpose(q_w_dim_hc, q_w, dim, hc, 4, stream)
- * and passes the results to every entry point; the forward's bits are those
- * of the same weights stored in the kernels' layout.
- *   src, dst  device, elem_bytes-aligned, caller-owned, not overlapping
+ *   engram_transpose(wkv_in_out, wkv, S row_dim, (hc+1) dim, wkv_ld, 2 or 4, stream)
+ *   engram_transpose(q_w_dim_hc, q_w, dim, hc, 0, 4, stream)
+ * and passes the results to every entry point (wkv_ld as engram_project's, 0
+ * for dense rows); the forward's bits are those of the same weights stored in
+ * the kernels' layout.
+ *   src, dst  device, elem_bytes-aligned, caller-owned, not overlapping; dst
+ *             holds (cols - 1) dst_ld + rows elements, the gaps untouched
  * Errors: ENGRAM_EINVAL (elem_bytes not 2 or 4, null, misaligned or
- * overlapping buffers), ENGRAM_ESHAPE (negative sizes, or more than 2^24
- * tiles of 64 x 64), ENGRAM_EHIP.
+ * overlapping buffers), ENGRAM_ESHAPE (negative sizes, 0 < dst_ld < rows, or
+ * more than 2^24 tiles of 64 x 64), ENGRAM_EHIP.
  */
-int engram_transpose(const void *src, void *dst, int64_t rows, int64_t cols,
+int engram_transpose(const void *src, void *dst, int64_t rows, int64_t cols, int64_t dst_ld,
                      int32_t elem_bytes, hipStream_t stream);
 
 /* [host] Bytes of workspace engram_project_mx uses (0 if none, on bad arguments
@@ -450,7 +472,8 @@ size_t engram_forward_workspace_size(const engram_hash_params *params,
  * Steps 1-5 for one chunk of B sequences x T tokens, on one stream.
  *   ids, hist_in, hist_out   as engram_hash
  *   table                    as engram_gather, desc->row_format / row_dim
- *   wkv                      [(hc+1) dim, S row_dim], bf16 (E4M3) or float (fp32)
+ *   wkv                      [(hc+1) dim, S row_dim], bf16 (E4M3) or float (fp32),
+ *                            rows desc->wkv_ld elements apart (engram_project)
  *   q_w, k_w, h, gate_out    as engram_gate
  *   workspace                device, >= engram_forward_workspace_size bytes,
  *                            256-byte aligned; contents are scratch

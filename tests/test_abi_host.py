@@ -166,11 +166,11 @@ def test_gather_project_gate_validation():
     assert L.engram_gather(0x1000, 10, 0, 256, 0x2004, 4, 0x3000, None) == E.EINVAL
     assert L.engram_gather(0x1000, 10, 1, 30, 0x2000, 4, 0x3000, None) == E.ESHAPE
     assert L.engram_gather(None, 0, 0, 256, None, 0, None, None) == E.OK      # empty
-    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, 100, 64, 0, None, 0, None) == E.ESHAPE
-    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, 128, 60, 0, None, 0, None) == E.ESHAPE
-    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, 128, 64, 2, None, 0, None) == E.EINVAL
-    assert L.engram_project(0x1008, 0x2000, 0x3000, 4, 128, 64, 0, None, 0, None) == E.EINVAL
-    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, 128, 64, 0, 0x4010, 1 << 30, None) \
+    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, 100, 64, 0, 0, None, 0, None) == E.ESHAPE
+    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, 128, 60, 0, 0, None, 0, None) == E.ESHAPE
+    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, 128, 64, 0, 2, None, 0, None) == E.EINVAL
+    assert L.engram_project(0x1008, 0x2000, 0x3000, 4, 128, 64, 0, 0, None, 0, None) == E.EINVAL
+    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, 128, 64, 0, 0, 0x4010, 1 << 30, None) \
         == E.EWORKSPACE                                              # not 256-aligned
     d = E.forward_desc(1, 4, 4, 5120, 100, 0, 256)
     bad = E.forward_desc(1, 4, 9, 5120, 100, 0, 256)
@@ -237,9 +237,8 @@ def test_gate_mode_and_short_conv_validation():
     bad_mode = E.forward_desc(2, 16, 4, 64, 1 << 20, 0, 256, gate_mode=2)
     assert gc(bad_mode, ok) == E.EINVAL
     assert L.engram_gate(ctypes.byref(bad_mode), *ptrs, None) == E.EINVAL
-    d_res = E.forward_desc(2, 16, 4, 64, 1 << 20, 0, 256)
-    d_res.reserved = 1
-    assert gc(d_res, ok) == E.EINVAL
+    d_res = E.forward_desc(2, 16, 4, 64, 1 << 20, 0, 256, wkv_ld=-1)
+    assert gc(d_res, ok) == E.ESHAPE
     assert gc(d, E.short_conv(0x7000, taps=0)) == E.ESHAPE
     assert gc(d, E.short_conv(0x7000, taps=9)) == E.ESHAPE
     assert gc(d, E.short_conv(0x7000, dilation=0)) == E.ESHAPE
@@ -333,28 +332,61 @@ def test_projection_shapes_beyond_32_bit_offsets_are_refused():
     above 2^20, or a grid beyond 2^32 threads, is refused before any launch
     (rather than wrapping the record and returning zeros or garbage)."""
     L = E.LIB
-    ok = L.engram_project(0x1000, 0x2000, 0x3000, 4, 1 << 20, 64, 0, None, 0, None)
+    ok = L.engram_project(0x1000, 0x2000, 0x3000, 4, 1 << 20, 64, 0, 0, None, 0, None)
     assert ok != E.ESHAPE                     # fake pointers: any later status but ESHAPE
-    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, (1 << 20) + 64, 64, 0, None, 0,
+    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, (1 << 20) + 64, 64, 0, 0, None, 0,
                             None) == E.ESHAPE
-    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, 1 << 23, 64, 0, None, 0, None) \
+    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, 1 << 23, 64, 0, 0, None, 0, None) \
         == E.ESHAPE
     big_m, big_n = (1 << 31) - 1, 1 << 20     # 8.4 M x 8192 tiles
-    assert L.engram_project(0x1000, 0x2000, 0x3000, big_m, 6144, big_n, 0, None, 0,
+    assert L.engram_project(0x1000, 0x2000, 0x3000, big_m, 6144, big_n, 0, 0, None, 0,
                             None) == E.ESHAPE
     assert L.engram_project_mx(0x1000, 0x2000, 24, 0x3000, 0x4000, 0x5000, big_m, big_n,
                                None, 0, None) == E.ESHAPE
     # the fp32 kernel indexes with 64-bit offsets: no in_dim limit of its own
-    assert L.engram_project(0x1000, 0x2000, 0x3000, 0, (1 << 21), 64, 1, None, 0,
+    assert L.engram_project(0x1000, 0x2000, 0x3000, 0, (1 << 21), 64, 0, 1, None, 0,
                             None) == E.OK
 
 
 @host_only
 def test_transpose_validation():
     L = E.LIB
-    assert L.engram_transpose(0x1000, 0x2000, 4, 8, 3, None) == E.EINVAL      # 3-byte elements
-    assert L.engram_transpose(0x1000, 0x1010, 4, 8, 2, None) == E.EINVAL      # overlap
-    assert L.engram_transpose(0x1001, 0x9000, 4, 8, 2, None) == E.EINVAL      # misaligned
-    assert L.engram_transpose(None, None, 0, 5, 2, None) == E.OK              # empty
-    assert L.engram_transpose(0x1000, 0x9000, -1, 5, 2, None) == E.ESHAPE
-    assert L.engram_transpose(0x1000, 1 << 44, 1 << 30, 1 << 20, 2, None) == E.ESHAPE
+    assert L.engram_transpose(0x1000, 0x2000, 4, 8, 0, 3, None) == E.EINVAL      # 3-byte elements
+    assert L.engram_transpose(0x1000, 0x1010, 4, 8, 0, 2, None) == E.EINVAL      # overlap
+    assert L.engram_transpose(0x1001, 0x9000, 4, 8, 0, 2, None) == E.EINVAL      # misaligned
+    assert L.engram_transpose(None, None, 0, 5, 0, 2, None) == E.OK              # empty
+    assert L.engram_transpose(0x1000, 0x9000, -1, 5, 0, 2, None) == E.ESHAPE
+    assert L.engram_transpose(0x1000, 1 << 44, 1 << 30, 1 << 20, 0, 2, None) == E.ESHAPE
+    # a strided destination: dst_ld below rows, an extent beyond 2^62 bytes,
+    # and an overlap that only the strided extent reaches
+    assert L.engram_transpose(0x1000, 0x9000, 4, 8, 3, 2, None) == E.ESHAPE
+    assert L.engram_transpose(0x1000, 0x9000, 4, 8, 1 << 61, 2, None) == E.ESHAPE
+    assert L.engram_transpose(0x1100, 0x1000, 4, 8, 64, 2, None) == E.EINVAL
+
+
+@host_only
+def test_weight_row_stride_validation():
+    """wkv_ld: 0 or >= in_dim, 16-byte multiples, at most 2^20 for bf16; the same
+    rule through engram_forward_desc. Bad strides fail before any launch."""
+    L = E.LIB
+    args = (0x1000, 0x2000, 0x3000, 4, 128, 64)
+    for ld in (64, 120, 132, (1 << 20) + 8, -8):
+        assert L.engram_project(*args, ld, 0, None, 0, None) == E.ESHAPE, ld
+    assert L.engram_project(0x1000, 0x2000, 0x3000, 4, 128, 64, 130, 1, None, 0, None) \
+        == E.ESHAPE                                                  # fp32: 4-element rows
+    assert L.engram_project(0x1000, 0x2000, 0x3000, 0, 128, 64, 136, 0, None, 0, None) == E.OK
+    assert L.engram_project(0x1000, 0x2000, 0x3000, 0, 128, 64, 132, 1, None, 0, None) == E.OK
+    p = _params(C1)
+    fw = [0x1000, None, None, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None, 0x10000, 1 << 40,
+          None]
+    for ld in (-1, 6000, 6148):
+        d = E.forward_desc(4, 8192, 4, 5120, 384_006_168, 0, 256, wkv_ld=ld)
+        assert L.engram_forward(ctypes.byref(p), ctypes.byref(d), *fw) == E.ESHAPE, ld
+
+
+def test_recommended_stride():
+    assert E.engram_wkv_row_stride(6144, 2) == 6208      # 12 KiB rows -> 97 lines of 128 B
+    assert E.engram_wkv_row_stride(1024, 2) == 1024      # 2 KiB rows stay dense
+    assert E.engram_wkv_row_stride(6144, 4) == 6176
+    assert E.engram_wkv_row_stride(100, 2) == 128        # rounded up to 128 bytes
+    assert E.engram_wkv_row_stride(0, 2) == 0 and E.engram_wkv_row_stride(64, 3) == 0

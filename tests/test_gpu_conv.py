@@ -309,7 +309,7 @@ def test_forward_conv_equals_its_stages(mode):
     w = S_C
     gw = GpuWorkload(w)
     desc = E.forward_desc(w.batch, w.seq, w.hc, w.dim, gw.rows, gw.row_format, w.row_dim, w.eps,
-                          w.gate_clamp, mode)
+                          w.gate_clamp, mode, wkv_ld=gw.wkv_ld)
     g = torch.Generator(device="cpu").manual_seed(3)
     cw = (0.5 * torch.randn((w.hc, w.dim, 4), generator=g)).to(DEV)
     nw = (1 + 0.2 * torch.randn((w.hc, w.dim), generator=g)).to(DEV)
@@ -322,7 +322,7 @@ def test_forward_conv_equals_its_stages(mode):
     kv = torch.empty((T, (w.hc + 1) * w.dim), dtype=torch.bfloat16, device=DEV)
     npw = E.engram_project_workspace_size(T, S * 256, (w.hc + 1) * w.dim, 0)
     pws = torch.empty(max(npw, 256), dtype=torch.uint8, device=DEV)
-    E.engram_project(e, gw.wkv, kv, T, S * 256, (w.hc + 1) * w.dim, 0, pws, npw)
+    E.engram_project(e, gw.wkv, kv, T, S * 256, (w.hc + 1) * w.dim, gw.wkv_ld, 0, pws, npw)
     h1 = gw.h.clone()
     g1 = torch.empty((T, w.hc), dtype=torch.float32, device=DEV)
     sv1 = torch.empty((w.batch, 9, w.dim), dtype=torch.bfloat16, device=DEV)

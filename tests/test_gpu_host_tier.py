@@ -117,7 +117,7 @@ def test_prefetch_on_a_second_stream_equals_the_resident_forward():
         E.engram_gather(host, gw.rows, gw.row_format, 256, rows, T * S, e, stream=side)
         ready.record(side)
     main.wait_event(ready)
-    E.engram_project(e, gw.wkv, kv, T, K, N, 0, pws, npws, stream=main)
+    E.engram_project(e, gw.wkv, kv, T, K, N, gw.wkv_ld, 0, pws, npws, stream=main)
     E.engram_gate(gw.desc, gw.ids, w.raw_vocab, kv, gw.q_w, gw.k_w, h, g, stream=main)
     torch.cuda.synchronize()
     assert torch.equal(h.view(torch.int16), h_ref.view(torch.int16))

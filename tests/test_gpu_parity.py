@@ -376,7 +376,7 @@ def test_project_bf16_shapes(M, N, K):
     # with the workspace (split-K over the CUs when tiles are few) and without
     for wsp, nb in ((ws, nws), (None, 0)):
         kv = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
-        E.engram_project(to_device(e), to_device(w), kv, M, K, N, 0, wsp, nb)
+        E.engram_project(to_device(e), to_device(w), kv, M, K, N, 0, 0, wsp, nb)
         torch.cuda.synchronize()
         got = O.bf16_bits_to_f64(bf16_bits(kv))
         assert_close(got, exact, f"kv {M}x{N}x{K} ws={nb}", atol=0.0, rtol=0.0, extra=tol)
@@ -396,7 +396,7 @@ def test_project_skinny(M, N, K):
     assert E.engram_project_workspace_size(M, K, N, 0) == 0
     de, dw = to_device(e), to_device(w)
     kv = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
-    E.engram_project(de, dw, kv, M, K, N, 0)
+    E.engram_project(de, dw, kv, M, K, N, 0, 0)
     torch.cuda.synchronize()
     ef, wf = O.bf16_bits_to_f64(e), O.bf16_bits_to_f64(w)
     exact = O.project(ef, wf)
@@ -408,7 +408,7 @@ def test_project_skinny(M, N, K):
     e_big = torch.zeros((big, K), dtype=torch.bfloat16, device=DEV)
     e_big[:M] = de
     kv_big = torch.empty((big, N), dtype=torch.bfloat16, device=DEV)
-    E.engram_project(e_big, dw, kv_big, big, K, N, 0)
+    E.engram_project(e_big, dw, kv_big, big, K, N, 0, 0)
     torch.cuda.synchronize()
     assert torch.equal(kv_big[:M].view(torch.int16), kv.view(torch.int16))
 
@@ -429,7 +429,7 @@ def test_project_split_k(M, N, K):
     for _ in range(2):
         kv = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
         ws.fill_(0xFF)                                    # stale workspace contents
-        E.engram_project(de, dw, kv, M, K, N, 0, ws, nws)
+        E.engram_project(de, dw, kv, M, K, N, 0, 0, ws, nws)
         torch.cuda.synchronize()
         outs.append(bf16_bits(kv))
     assert np.array_equal(outs[0], outs[1])               # a fixed summation order
@@ -438,7 +438,7 @@ def test_project_split_k(M, N, K):
     assert_close(O.bf16_bits_to_f64(outs[0]), exact, f"kv split-K {M}x{N}x{K}", atol=0.0,
                  rtol=0.0, extra=gemm_tolerance(ef, wf, exact, True))
     with pytest.raises(E.EngramError):                    # a non-null workspace too small
-        E.engram_project(de, dw, kv, M, K, N, 0, ws, nws - 256)
+        E.engram_project(de, dw, kv, M, K, N, 0, 0, ws, nws - 256)
 
 
 def test_project_wide_equals_narrow():
@@ -450,10 +450,10 @@ def test_project_wide_equals_narrow():
     e = to_device(gen.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32)))
     w = to_device(gen.f32_to_bf16_bits(rng.standard_normal((N, K)).astype(np.float32) * 0.05))
     wide = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
-    E.engram_project(e, w, wide, M, K, N, 0)
+    E.engram_project(e, w, wide, M, K, N, 0, 0)
     m = 300
     narrow = torch.empty((m, N), dtype=torch.bfloat16, device=DEV)
-    E.engram_project(e[:m].contiguous(), w, narrow, m, K, N, 0)
+    E.engram_project(e[:m].contiguous(), w, narrow, m, K, N, 0, 0)
     torch.cuda.synchronize()
     assert np.array_equal(bf16_bits(wide[:m]), bf16_bits(narrow))
 
@@ -466,7 +466,7 @@ def test_project_one_hot_exact():
     ks = rng.integers(0, K, M)
     e[np.arange(M), ks] = 0x3F80                      # 1.0
     kv = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
-    E.engram_project(to_device(e), to_device(w), kv, M, K, N, 0)
+    E.engram_project(to_device(e), to_device(w), kv, M, K, N, 0, 0)
     torch.cuda.synchronize()
     assert np.array_equal(bf16_bits(kv), w.T[ks])
 
@@ -477,7 +477,7 @@ def test_project_f32():
         e = rng.standard_normal((M, K)).astype(np.float32)
         w = rng.standard_normal((N, K)).astype(np.float32)
         kv = torch.empty((M, N), dtype=torch.float32, device=DEV)
-        E.engram_project(to_device(e), to_device(w), kv, M, K, N, 1)
+        E.engram_project(to_device(e), to_device(w), kv, M, K, N, 0, 1)
         torch.cuda.synchronize()
         exact = O.project(e, w)
         assert_close(kv.cpu().numpy(), exact, "kv f32", atol=0, rtol=0,
@@ -542,8 +542,8 @@ def _run_stages(gw):
     E.engram_gather(gw.table, gw.rows, gw.row_format, w.row_dim, rows, T * S, e)
     kv = torch.empty((T, (w.hc + 1) * w.dim), dtype=dt, device=DEV)
     pws, npws = _project_ws(T, S * w.row_dim, (w.hc + 1) * w.dim) if not gw.f32 else (None, 0)
-    E.engram_project(e, gw.wkv, kv, T, S * w.row_dim, (w.hc + 1) * w.dim, int(gw.f32), pws,
-                     npws)
+    E.engram_project(e, gw.wkv, kv, T, S * w.row_dim, (w.hc + 1) * w.dim, gw.wkv_ld,
+                     int(gw.f32), pws, npws)
     gates = torch.empty((T, w.hc), dtype=torch.float32, device=DEV)
     E.engram_gate(gw.desc, gw.ids, w.raw_vocab, kv, gw.q_w, gw.k_w, gw.h, gates)
     torch.cuda.synchronize()
@@ -688,7 +688,7 @@ def test_forward_chunked_and_deterministic():
     for a, b in ((0, cut), (cut, w.seq)):
         sub = dataclasses.replace(w, seq=b - a)
         d = E.forward_desc(w.batch, b - a, w.hc, w.dim, gw.rows, gw.row_format, w.row_dim,
-                           w.eps, w.gate_clamp)
+                           w.eps, w.gate_clamp, wkv_ld=gw.wkv_ld)
         ids = gw.ids[:, a:b].contiguous()
         hc_ = h_chunks[:, a:b].contiguous()
         n = E.engram_forward_workspace_size(gw.params, d)
@@ -761,6 +761,18 @@ def test_forward_c4_decode_full_table():
         assert np.array_equal(hout.cpu().numpy(), exp_hist)
         assert torch.equal(h0.view(torch.int16), gw.h.view(torch.int16))
         assert torch.equal(g1, gates)
+        # the harness spreads the weight's rows 6208 elements apart; with dense
+        # rows the step gives the same bits
+        assert gw.wkv_ld == C4.mem_dim + 64
+        dense_desc = E.forward_desc(C4.batch, C4.seq, C4.hc, C4.dim, gw.rows, gw.row_format,
+                                    C4.row_dim, C4.eps, C4.gate_clamp, wkv_ld=0)
+        h2 = to_device(gw.dense_np["h"])
+        g2 = torch.empty_like(g1)
+        E.engram_forward(gw.params, dense_desc, gw.ids, gw.hist_in, hout, gw.table,
+                         to_device(gw.dense_np["wkv"]), gw.q_w, gw.k_w, h2, g2, ws, n)
+        torch.cuda.synchronize()
+        assert torch.equal(h2.view(torch.int16), gw.h.view(torch.int16))
+        assert torch.equal(g2, gates)
     finally:
         gw.free()
         _cleanup()

@@ -101,13 +101,18 @@ for _ in range(400):
     p, off, _ = E.engram_make_primes(1009, 6)
     params = E.hash_params(97, 97, 4, 2, 0, 0x1000, [1, 3, 5, 7], p, off)
     d = E.forward_desc(B, T, hc, dim, int(rng.integers(-1, 1 << 40)), int(rng.integers(0, 3)),
-                       int(rng.integers(0, 300)), 1e-6, 0.0)
+                       int(rng.integers(0, 300)), 1e-6, 0.0,
+                       wkv_ld=int(rng.integers(-8, 1 << 21)))
     L.engram_forward_workspace_size(ctypes.byref(params), ctypes.byref(d))
     L.engram_forward_static(ctypes.byref(params), ctypes.byref(d), 0x1000, None, None, 0x2000,
                             0x3000, 0x4000, 0x5000, 0x6000, None, None)
     L.engram_gate_conv_workspace_size(ctypes.byref(d))
     L.engram_transpose(0x1000, 1 << 44, int(rng.integers(-2, 1 << 40)),
-                       int(rng.integers(-2, 1 << 30)), int(rng.integers(0, 6)), None)
+                       int(rng.integers(-2, 1 << 30)), int(rng.integers(-2, 1 << 62)),
+                       int(rng.integers(0, 6)), None)
+    L.engram_project(0x1000, 0x2000, 0x3000, int(rng.integers(-1, 3)) * 0,
+                     int(rng.integers(-64, 1 << 21)), int(rng.integers(-8, 1 << 16)),
+                     int(rng.integers(-8, 1 << 22)), int(rng.integers(0, 2)), None, 0, None)
 print("sweep ok")
 '''
 

@@ -35,7 +35,7 @@ def _both(gw, batch, hist=True):
     """engram_forward and engram_forward_static on the first ``batch`` sequences."""
     w = gw.w
     desc = E.forward_desc(batch, w.seq, w.hc, w.dim, gw.rows, gw.row_format, w.row_dim, w.eps,
-                          w.gate_clamp)
+                          w.gate_clamp, wkv_ld=gw.wkv_ld)
     ids = gw.ids[:batch].contiguous()
     hin = gw.hist_in[:batch].contiguous() if (hist and gw.hist_in is not None) else None
     out = []
@@ -91,7 +91,8 @@ def test_static_prefill_chunk_against_the_oracle():
 
 def test_static_refuses_calls_beyond_the_array():
     gw = GpuWorkload(DECODE)
-    big = E.forward_desc(2048, 1, 4, 5120, gw.rows, gw.row_format, 256, 1e-6, 0.0)
+    big = E.forward_desc(2048, 1, 4, 5120, gw.rows, gw.row_format, 256, 1e-6, 0.0,
+                         wkv_ld=gw.wkv_ld)
     ids = torch.zeros((2048, 1), dtype=torch.int32, device=DEV)
     h = torch.zeros((2048, 1, 4, 5120), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(E.EngramError) as ex:

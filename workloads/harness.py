@@ -13,7 +13,10 @@ from .device import fill_table, to_device
 
 class GpuWorkload:
     def __init__(self, w: EngramWorkload, device: str = "cuda", table: bool = True,
-                 dense: bool = True, wkv_mx: bool = False):
+                 dense: bool = True, wkv_mx: bool = False, wkv_ld: int | None = None):
+        """wkv_ld: row stride of the device wkv in elements; None takes the
+        library's recommended stride (engram_wkv_row_stride), 0 dense rows. The
+        gaps between rows hold NaN, which no kernel may read."""
         import torch
         import hashed_gram_conditional_amd as E
 
@@ -35,9 +38,10 @@ class GpuWorkload:
         self.row_format = E.ROW_F32 if self.f32 else E.ROW_E4M3_E8M0_264
         self.table = None
         self.dense_np = None
+        self.wkv_ld = 0
         if dense and w.has_forward:
             self.dense_np = gen.dense_inputs(w, table_rows_f32=self.rows if self.f32 else 0)
-            self.wkv = to_device(self.dense_np["wkv"], device)
+            self.wkv = self._strided_wkv(self.dense_np["wkv"], wkv_ld, device)
             self.q_w = to_device(self.dense_np["q_w"], device)
             self.k_w = to_device(self.dense_np["k_w"], device)
             self.h = to_device(self.dense_np["h"], device)
@@ -51,13 +55,26 @@ class GpuWorkload:
                                          device=device)
                 fill_table(self.table, w.table_seed)
         self.desc = E.forward_desc(w.batch, w.seq, w.hc, w.dim, self.rows, self.row_format,
-                                   w.row_dim, w.eps, w.gate_clamp)
+                                   w.row_dim, w.eps, w.gate_clamp,
+                                   wkv_ld=self.wkv_ld)
         # the projection weight in block-scaled FP8 (codes, scales), host and device
         self.wkv_mx_np = None
         if wkv_mx:
             self.wkv_mx_np = gen.wkv_mx(w)
             self.w_codes = to_device(self.wkv_mx_np[0], device)
             self.w_scales = to_device(self.wkv_mx_np[1], device)
+
+    def _strided_wkv(self, wkv: np.ndarray, wkv_ld, device):
+        n, k = wkv.shape
+        ld = self.E.engram_wkv_row_stride(k, wkv.itemsize) if wkv_ld is None else (wkv_ld or k)
+        assert ld >= k
+        self.wkv_ld = ld
+        if ld == k:
+            return to_device(wkv, device)
+        nan = np.uint16(0x7FC0) if wkv.dtype == np.uint16 else np.float32("nan")
+        padded = np.full((n, ld), nan, dtype=wkv.dtype)
+        padded[:, :k] = wkv
+        return to_device(padded, device)
 
     @property
     def tokens(self) -> int:
