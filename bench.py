@@ -281,6 +281,48 @@ def copy_calibration(mib: int):
     del src, dst
 
 
+def mfma_ceiling(a, b, iters: int = 40000):
+    """The rate of a pure v_mfma_f32_32x32x16_bf16 stream (libengram_calibrate.so,
+    no memory traffic in its loop) on fragments of the projection's own operands:
+    a the gathered e, b the weight. On random bits the power limit holds the clock
+    below the one the published peak assumes; this is the ceiling of any kernel
+    computing that product on this GPU."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "hashed_gram_conditional_amd", "libengram_calibrate.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    lib.engram_calibrate_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                               ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_void_p]
+    lib.engram_calibrate_mfma_flop.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.engram_calibrate_mfma_flop.restype = ctypes.c_double
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    n_frag = min(a.numel(), b.numel()) // 8
+    stream = torch.cuda.current_stream()
+
+    def call(n):
+        rc = lib.engram_calibrate_mfma_bf16(a.data_ptr(), b.data_ptr(), n_frag, out.data_ptr(),
+                                            blocks, n, ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"engram_calibrate_mfma_bf16 failed: {rc}")
+
+    call(2000)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    call(iters)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1])
+    tflops = lib.engram_calibrate_mfma_flop(blocks, iters) / (ms * 1e-3) / 1e12
+    return {"what": "pure v_mfma_f32_32x32x16_bf16 stream on fragments of the step's e and "
+                    "wkv, one wave per SIMD, no memory traffic",
+            "achieved": round(tflops, 1), "unit": "TFLOP/s", "ms": round(ms, 2),
+            "frac_of_peak": round(tflops / BF16_PEAK_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -384,12 +426,14 @@ def main():
     fe[1].record(stream)
     torch.cuda.synchronize()
     forward_ms = fe[0].elapsed_time(fe[1]) / args.steps
+    ceiling = mfma_ceiling(e, gw.wkv[:1024, :K_in].contiguous())
 
     flops = 2.0 * T * N_out * K_in
     gemm_tflops = flops / (stage_ms[2] * 1e-3) / 1e12
     gather_gbps = GATHER_BYTES_PER_TOKEN * T / (stage_ms[1] * 1e-3) / 1e9
     tokens_per_s = T / (ms_per_step * 1e-3)
     traffic = measured_traffic("gemm_bf16_kernel", GEMM_BF16_SOURCES)
+    ceiling["projection_frac_of_ceiling"] = round(gemm_tflops / ceiling["achieved"], 4)
     out = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -414,6 +458,7 @@ def main():
                      "traffic": traffic["bytes"] if traffic else None,
                      "traffic_detail": traffic,
                      "algorithmic_flop": flops},
+        "mfma_ceiling": ceiling,
         "gather": {"kernel": "gather_e4m3_kernel (engram_gather)",
                    "achieved": round(gather_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                    "frac": round(gather_gbps / HBM_PEAK_GBPS, 4),

@@ -1,4 +1,5 @@
-"""Build step of libengram.so: compiles the HIP sources for gfx950 in-tree.
+"""Build step of libengram.so (the layer) and libengram_calibrate.so (the
+benchmark's MFMA calibration): compiles the HIP sources for gfx950 in-tree.
 
 Run ``python hashed_gram_conditional_amd/build.py`` (or ``__graft_entry__.build()``).
 """
@@ -11,6 +12,8 @@ ROOT = os.path.dirname(PKG)
 SOURCES = ["hash.hip", "gather.hip", "gemm.hip", "gemm_mx.hip", "gate.hip", "conv.hip",
            "layout.hip", "engram_api.hip"]
 LIB = os.path.join(PKG, "libengram.so")
+CALIB_SOURCE = "calibrate.hip"
+CALIB_LIB = os.path.join(PKG, "libengram_calibrate.so")
 
 # Packed-fp32 instructions are disabled for every HIP translation unit.
 HIP_FLAGS = [
@@ -55,5 +58,19 @@ def build_library(verbose: bool = False, out: str = LIB, sanitize: bool = False)
     return out
 
 
+def build_calibration(verbose: bool = False, out: str = CALIB_LIB) -> str:
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, "-o", tmp, os.path.join(PKG, "csrc", CALIB_SOURCE)]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed building {out}")
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build_library(verbose=True))
+    print(build_calibration(verbose=True))

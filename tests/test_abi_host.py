@@ -390,3 +390,22 @@ def test_recommended_stride():
     assert E.engram_wkv_row_stride(6144, 4) == 6176
     assert E.engram_wkv_row_stride(100, 2) == 128        # rounded up to 128 bytes
     assert E.engram_wkv_row_stride(0, 2) == 0 and E.engram_wkv_row_stride(64, 3) == 0
+
+
+def test_calibration_library_exports():
+    """The benchmark's MFMA calibration library loads and exports its two
+    functions; bad arguments are refused before any launch."""
+    path = os.path.join(ROOT, "hashed_gram_conditional_amd", "libengram_calibrate.so")
+    if not os.path.exists(path):
+        pytest.skip("libengram_calibrate.so not built")
+    lib = ctypes.CDLL(path)
+    lib.engram_calibrate_mfma_flop.restype = ctypes.c_double
+    lib.engram_calibrate_mfma_flop.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    assert lib.engram_calibrate_mfma_flop(256, 10) == 256 * 4 * 10 * 128 * 32768
+    f = lib.engram_calibrate_mfma_bf16
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                  ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    assert f(None, 0x2000, 64, 0x3000, 1, 1, None) == -1
+    assert f(0x1008, 0x2000, 64, 0x3000, 1, 1, None) == -1      # misaligned
+    assert f(0x1000, 0x2000, 4, 0x3000, 1, 1, None) == -1        # fewer than 8 fragments
+    assert f(0x1000, 0x2000, 64, 0x3000, 0, 1, None) == -1
