@@ -281,6 +281,34 @@ def copy_calibration(mib: int):
     del src, dst
 
 
+def _calibration_lib():
+    import ctypes
+    path = os.path.join(ROOT, "hashed_gram_conditional_amd", "libengram_calibrate.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.engram_calibrate_mfma_bf16.argtypes = [P, P, I64, P, I32, I32, P]
+    lib.engram_calibrate_mfma_fp8.argtypes = [P, P, I64, P, P, I64, P, I32, I32, P]
+    for f in (lib.engram_calibrate_mfma_flop, lib.engram_calibrate_mfma_fp8_flop):
+        f.argtypes = [I32, I32]
+        f.restype = ctypes.c_double
+    return lib
+
+
+def _time_stream(call, flop_of, iters: int):
+    import torch
+    stream = torch.cuda.current_stream()
+    call(2000)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    call(iters)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1])
+    return flop_of(iters) / (ms * 1e-3) / 1e12, ms
+
+
 def mfma_ceiling(a, b, iters: int = 40000):
     """The rate of a pure v_mfma_f32_32x32x16_bf16 stream (libengram_calibrate.so,
     no memory traffic in its loop) on fragments of the projection's own operands:
@@ -289,15 +317,7 @@ def mfma_ceiling(a, b, iters: int = 40000):
     computing that product on this GPU."""
     import ctypes
     import torch
-    path = os.path.join(ROOT, "hashed_gram_conditional_amd", "libengram_calibrate.so")
-    if not os.path.exists(path):
-        raise RuntimeError(f"{path} is not built (run __graft_entry__.build())")
-    lib = ctypes.CDLL(path)
-    lib.engram_calibrate_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                                               ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
-                                               ctypes.c_void_p]
-    lib.engram_calibrate_mfma_flop.argtypes = [ctypes.c_int32, ctypes.c_int32]
-    lib.engram_calibrate_mfma_flop.restype = ctypes.c_double
+    lib = _calibration_lib()
     blocks = torch.cuda.get_device_properties(0).multi_processor_count
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     n_frag = min(a.numel(), b.numel()) // 8
@@ -309,18 +329,39 @@ def mfma_ceiling(a, b, iters: int = 40000):
         if rc != 0:
             raise RuntimeError(f"engram_calibrate_mfma_bf16 failed: {rc}")
 
-    call(2000)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev[0].record(stream)
-    call(iters)
-    ev[1].record(stream)
-    torch.cuda.synchronize()
-    ms = ev[0].elapsed_time(ev[1])
-    tflops = lib.engram_calibrate_mfma_flop(blocks, iters) / (ms * 1e-3) / 1e12
+    tflops, ms = _time_stream(call, lambda n: lib.engram_calibrate_mfma_flop(blocks, n), iters)
     return {"what": "pure v_mfma_f32_32x32x16_bf16 stream on fragments of the step's e and "
                     "wkv, one wave per SIMD, no memory traffic",
             "achieved": round(tflops, 1), "unit": "TFLOP/s", "ms": round(ms, 2),
             "frac_of_peak": round(tflops / BF16_PEAK_TFLOPS, 4)}
+
+
+def mfma_ceiling_fp8(a, b, sa, sb, iters: int = 20000):
+    """mfma_ceiling for the FP8 projection: v_mfma_scale_f32_32x32x64_f8f6f4 on
+    32-byte fragments of the step's E4M3 codes (a: e's, b: the weight's) with
+    their E8M0 scale bytes (sa, sb)."""
+    import ctypes
+    import torch
+    lib = _calibration_lib()
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    n_frag = min(a.numel(), b.numel()) // 32
+    n_scale = min(sa.numel(), sb.numel())
+    stream = torch.cuda.current_stream()
+
+    def call(n):
+        rc = lib.engram_calibrate_mfma_fp8(a.data_ptr(), b.data_ptr(), n_frag, sa.data_ptr(),
+                                           sb.data_ptr(), n_scale, out.data_ptr(), blocks, n,
+                                           ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"engram_calibrate_mfma_fp8 failed: {rc}")
+
+    tflops, ms = _time_stream(call, lambda n: lib.engram_calibrate_mfma_fp8_flop(blocks, n),
+                              iters)
+    return {"what": "pure v_mfma_scale_f32_32x32x64_f8f6f4 stream on fragments of the step's "
+                    "e and weight codes and scales, one wave per SIMD, no memory traffic",
+            "achieved": round(tflops, 1), "unit": "TFLOP/s", "ms": round(ms, 2),
+            "frac_of_peak": round(tflops / FP8_PEAK_TFLOPS, 4)}
 
 
 def main():
@@ -852,6 +893,8 @@ def fp8_prefill_bench(gw, steps: int, warmup: int):
     st = np.mean([[s[j].elapsed_time(s[j + 1]) for j in range(4)] for s in ev], axis=0)
     ms = 1e3 * wall / steps
     tflops = 2.0 * T * N_out * S * 256 / (st[2] * 1e-3) / 1e12
+    ceiling = mfma_ceiling_fp8(e_codes, wc, e_scales, wsc)
+    ceiling["projection_frac_of_ceiling"] = round(tflops / ceiling["achieved"], 4)
     del rows, e_codes, e_scales, kv, gates, pws, wc, wsc
     return {"workload": "prefill layer forward as above, projection weight in block-scaled FP8 "
                         "(E4M3 + one E8M0 scale per 32 inputs), rows fed to the FP8 MFMA "
@@ -860,7 +903,8 @@ def fp8_prefill_bench(gw, steps: int, warmup: int):
             "stages_ms": {"hash": round(st[0], 4), "gather_mx": round(st[1], 4),
                           "project_mx": round(st[2], 4), "gate": round(st[3], 4)},
             "project_mx": {"achieved": round(tflops, 2), "peak": FP8_PEAK_TFLOPS,
-                           "unit": "TFLOP/s", "frac": round(tflops / FP8_PEAK_TFLOPS, 4)}}
+                           "unit": "TFLOP/s", "frac": round(tflops / FP8_PEAK_TFLOPS, 4)},
+            "mfma_ceiling": ceiling}
 
 
 def hash_layers_bench(reps: int):

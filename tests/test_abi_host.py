@@ -393,7 +393,7 @@ def test_recommended_stride():
 
 
 def test_calibration_library_exports():
-    """The benchmark's MFMA calibration library loads and exports its two
+    """The benchmark's MFMA calibration library loads and exports its
     functions; bad arguments are refused before any launch."""
     path = os.path.join(ROOT, "hashed_gram_conditional_amd", "libengram_calibrate.so")
     if not os.path.exists(path):
@@ -409,3 +409,13 @@ def test_calibration_library_exports():
     assert f(0x1008, 0x2000, 64, 0x3000, 1, 1, None) == -1      # misaligned
     assert f(0x1000, 0x2000, 4, 0x3000, 1, 1, None) == -1        # fewer than 8 fragments
     assert f(0x1000, 0x2000, 64, 0x3000, 0, 1, None) == -1
+    lib.engram_calibrate_mfma_fp8_flop.restype = ctypes.c_double
+    lib.engram_calibrate_mfma_fp8_flop.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    assert lib.engram_calibrate_mfma_fp8_flop(256, 10) == 256 * 4 * 10 * 128 * 131072
+    f8 = lib.engram_calibrate_mfma_fp8
+    f8.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                   ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                   ctypes.c_int32, ctypes.c_void_p]
+    assert f8(0x1010, 0x2000, 64, 0x4000, 0x5000, 8, 0x3000, 1, 1, None) == -1   # misaligned
+    assert f8(0x1000, 0x2000, 64, None, 0x5000, 8, 0x3000, 1, 1, None) == -1
+    assert f8(0x1000, 0x2000, 64, 0x4000, 0x5000, 0, 0x3000, 1, 1, None) == -1
