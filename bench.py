@@ -9,10 +9,12 @@ All inputs are seeded synthetic data already resident in HBM when timing
 starts.
 
 One step = one pass of the whole hot path over the batch: engram_hash ->
-engram_gather -> engram_project -> engram_gate, the four launches that
-engram_forward makes, called through the C ABI on torch's current stream with
-HIP events between them. W untimed warmup steps, then K timed steps bracketed by
-torch.cuda.synchronize(). Prints one JSON line.
+engram_gather -> engram_fold_gate_weights -> engram_project_gate_sums ->
+engram_gate_sums, the launches engram_forward makes at this size (its
+projection fills the CUs with whole tiles, so the key side of the gate runs in
+the projection's epilogue), called through the C ABI on torch's current stream
+with HIP events between them. W untimed warmup steps, then K timed steps
+bracketed by torch.cuda.synchronize(). Prints one JSON line.
 """
 import argparse
 import json
@@ -424,7 +426,7 @@ def main():
         copy_calibration(args.copy_calibration_mib)
 
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
 
     def step(evs):
         if evs:
@@ -435,13 +437,15 @@ def main():
         E.engram_gather(gw.table, gw.rows, gw.row_format, w.row_dim, rows, T * S, e)
         if evs:
             evs[2].record(stream)
-        E.engram_project(e, gw.wkv, kv, T, K_in, N_out, gw.wkv_ld, 0)
+        E.engram_fold_gate_weights(gw.q_w, gw.k_w, w.hc, w.dim, qk_w)
         if evs:
             evs[3].record(stream)
-        E.engram_fold_gate_weights(gw.q_w, gw.k_w, w.hc, w.dim, qk_w)
-        E.engram_gate_folded(gw.desc, gw.ids, w.raw_vocab, kv, qk_w, gw.h, gates)
+        E.engram_project_gate_sums(gw.desc, e, K_in, gw.wkv, gw.h, qk_w, kv)
         if evs:
             evs[4].record(stream)
+        E.engram_gate_sums(gw.desc, gw.ids, w.raw_vocab, kv, gw.h, gates)
+        if evs:
+            evs[5].record(stream)
 
     for _ in range(args.warmup):
         step(None)
@@ -451,10 +455,28 @@ def main():
         step(ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    stage_ms = np.mean([[s[j].elapsed_time(s[j + 1]) for j in range(4)] for s in ev], axis=0)
+    # hash, gather, fold, projection, gate
+    stage_ms = np.mean([[s[j].elapsed_time(s[j + 1]) for j in range(5)] for s in ev], axis=0)
     ms_per_step = 1e3 * wall / args.steps
 
-    # the fused entry point, for comparison (same launches, one call)
+    # the separate stages for comparison: the projection storing every key,
+    # then the gate reading them (engram_forward's path for calls that do not
+    # fill the CUs with whole tiles)
+    sep = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps + 2):
+        evs = sep[i - 2] if i >= 2 else None
+        if evs:
+            evs[0].record(stream)
+        E.engram_project(e, gw.wkv, kv, T, K_in, N_out, gw.wkv_ld, 0)
+        if evs:
+            evs[1].record(stream)
+        E.engram_gate_folded(gw.desc, gw.ids, w.raw_vocab, kv, qk_w, gw.h, gates)
+        if evs:
+            evs[2].record(stream)
+    torch.cuda.synchronize()
+    sep_ms = np.mean([[s[j].elapsed_time(s[j + 1]) for j in range(2)] for s in sep], axis=0)
+
+    # the fused entry point, for comparison (the same launches, one call)
     ws, nws = gw.workspace()
     fe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     for _ in range(2):
@@ -470,10 +492,10 @@ def main():
     ceiling = mfma_ceiling(e, gw.wkv[:1024, :K_in].contiguous())
 
     flops = 2.0 * T * N_out * K_in
-    gemm_tflops = flops / (stage_ms[2] * 1e-3) / 1e12
+    gemm_tflops = flops / (stage_ms[3] * 1e-3) / 1e12
     gather_gbps = GATHER_BYTES_PER_TOKEN * T / (stage_ms[1] * 1e-3) / 1e9
     tokens_per_s = T / (ms_per_step * 1e-3)
-    traffic = measured_traffic("gemm_bf16_kernel", GEMM_BF16_SOURCES)
+    traffic = measured_traffic("gemm_bf16_sums_kernel", GEMM_BF16_SOURCES)
     ceiling["projection_frac_of_ceiling"] = round(gemm_tflops / ceiling["achieved"], 4)
     out = {
         "metric": METRIC,
@@ -493,7 +515,8 @@ def main():
                                "6144 -> 5 x 5120, hc 4 x 5120",
                    "batch": w.batch, "seq": w.seq, "segments": S, "hc": w.hc, "dim": w.dim,
                    "table_rows": gw.rows, "wkv_row_stride": gw.wkv_ld},
-        "roofline": {"bound": "mfma", "kernel": "gemm_bf16_kernel (engram_project)",
+        "roofline": {"bound": "mfma",
+                     "kernel": "gemm_bf16_sums_kernel (engram_project_gate_sums)",
                      "achieved": round(gemm_tflops, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic["bytes"] if traffic else None,
@@ -505,7 +528,11 @@ def main():
                    "frac": round(gather_gbps / HBM_PEAK_GBPS, 4),
                    "bytes_per_token": GATHER_BYTES_PER_TOKEN},
         "stages_ms": {"hash": round(stage_ms[0], 4), "gather": round(stage_ms[1], 4),
-                      "project": round(stage_ms[2], 4), "gate": round(stage_ms[3], 4)},
+                      "fold": round(stage_ms[2], 4), "project_gate_sums": round(stage_ms[3], 4),
+                      "gate_sums": round(stage_ms[4], 4)},
+        "separate_stages_ms": {"project": round(sep_ms[0], 4), "gate": round(sep_ms[1], 4),
+                               "what": "engram_project storing every key, then "
+                                       "engram_gate_folded reading them"},
         "engram_forward_ms": round(forward_ms, 4),
     }
     detail, hash_steady = gather_detail(gw, rows, e, max(args.steps // 2, 5))
@@ -646,8 +673,6 @@ def host_tier_bench(gw, host, rows, e, kv, gates, steps: int, warmup: int):
     # pipelined steps, two e / row-id buffers
     e_buf = [e, torch.empty_like(e)]
     r_buf = [rows, torch.empty_like(rows)]
-    nws = E.engram_project_workspace_size(T, K_in, N_out, 0)
-    pws = torch.empty(max(nws, 256), dtype=torch.uint8, device="cuda")
     side = torch.cuda.Stream()
     ready = [torch.cuda.Event(), torch.cuda.Event()]
     free = [torch.cuda.Event(), torch.cuda.Event()]
@@ -663,10 +688,10 @@ def host_tier_bench(gw, host, rows, e, kv, gates, steps: int, warmup: int):
 
     def compute(slot):
         main.wait_event(ready[slot])
-        E.engram_project(e_buf[slot], gw.wkv, kv, T, K_in, N_out, gw.wkv_ld, 0, pws if nws else None, nws,
-                         stream=main)
         E.engram_fold_gate_weights(gw.q_w, gw.k_w, w.hc, w.dim, qk_w, stream=main)
-        E.engram_gate_folded(gw.desc, gw.ids, w.raw_vocab, kv, qk_w, gw.h, gates, stream=main)
+        E.engram_project_gate_sums(gw.desc, e_buf[slot], K_in, gw.wkv, gw.h, qk_w, kv,
+                                   stream=main)
+        E.engram_gate_sums(gw.desc, gw.ids, w.raw_vocab, kv, gw.h, gates, stream=main)
         free[slot].record(main)
 
     for ev in free:
@@ -685,7 +710,7 @@ def host_tier_bench(gw, host, rows, e, kv, gates, steps: int, warmup: int):
     nxt = run(steps, nxt)
     torch.cuda.synchronize()
     ms = 1e3 * (time.perf_counter() - t0) / steps
-    del raw, e_buf, r_buf, pws
+    del raw, e_buf, r_buf
     return {"workload": "prefill layer forward as above with the 6.34 GB table in pinned host "
                         "memory: each step's rows are gathered over the host link by the GPU "
                         "during the previous step's projection (two buffers, two streams)",
@@ -841,8 +866,9 @@ def gather_c2_bench(gw, reps: int):
 def fp8_prefill_bench(gw, steps: int, warmup: int):
     """The same prefill layer with the projection weight in block-scaled FP8 (E4M3
     values, one E8M0 scale per 32 inputs, quantised from the bf16 run's N(0, 0.02)
-    distribution): engram_hash -> engram_gather_mx -> engram_project_mx ->
-    engram_gate, per-stage HIP events as in the bf16 run."""
+    distribution): engram_hash -> engram_gather_mx -> engram_fold_gate_weights ->
+    engram_project_mx_gate_sums -> engram_gate_sums (engram_forward_mx's launches
+    at this size), per-stage HIP events as in the bf16 run."""
     import torch
     import hashed_gram_conditional_amd as E
     from workloads import gen
@@ -858,11 +884,9 @@ def fp8_prefill_bench(gw, steps: int, warmup: int):
     e_scales = torch.empty((T, S * 8), dtype=torch.uint8, device="cuda")
     kv = torch.empty((T, N_out), dtype=torch.bfloat16, device="cuda")
     gates = torch.empty((T, w.hc), dtype=torch.float32, device="cuda")
-    n_ws = E.engram_project_mx_workspace_size(T, S, N_out)
-    pws = torch.empty(max(n_ws, 256), dtype=torch.uint8, device="cuda")
     qk_w = torch.empty((w.hc, w.dim), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
 
     def step(evs):
         if evs:
@@ -873,14 +897,15 @@ def fp8_prefill_bench(gw, steps: int, warmup: int):
         E.engram_gather_mx(gw.table, gw.rows, rows, T * S, e_codes, e_scales)
         if evs:
             evs[2].record(stream)
-        E.engram_project_mx(e_codes, e_scales, S, wc, wsc, kv, T, N_out, pws if n_ws else None,
-                            n_ws)
+        E.engram_fold_gate_weights(gw.q_w, gw.k_w, w.hc, w.dim, qk_w)
         if evs:
             evs[3].record(stream)
-        E.engram_fold_gate_weights(gw.q_w, gw.k_w, w.hc, w.dim, qk_w)
-        E.engram_gate_folded(gw.desc, gw.ids, w.raw_vocab, kv, qk_w, gw.h, gates)
+        E.engram_project_mx_gate_sums(gw.desc, e_codes, e_scales, S, wc, wsc, gw.h, qk_w, kv)
         if evs:
             evs[4].record(stream)
+        E.engram_gate_sums(gw.desc, gw.ids, w.raw_vocab, kv, gw.h, gates)
+        if evs:
+            evs[5].record(stream)
 
     for _ in range(warmup):
         step(None)
@@ -890,18 +915,20 @@ def fp8_prefill_bench(gw, steps: int, warmup: int):
         step(ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    st = np.mean([[s[j].elapsed_time(s[j + 1]) for j in range(4)] for s in ev], axis=0)
+    # hash, gather_mx, fold, projection, gate
+    st = np.mean([[s[j].elapsed_time(s[j + 1]) for j in range(5)] for s in ev], axis=0)
     ms = 1e3 * wall / steps
-    tflops = 2.0 * T * N_out * S * 256 / (st[2] * 1e-3) / 1e12
+    tflops = 2.0 * T * N_out * S * 256 / (st[3] * 1e-3) / 1e12
     ceiling = mfma_ceiling_fp8(e_codes, wc, e_scales, wsc)
     ceiling["projection_frac_of_ceiling"] = round(tflops / ceiling["achieved"], 4)
-    del rows, e_codes, e_scales, kv, gates, pws, wc, wsc
+    del rows, e_codes, e_scales, kv, gates, wc, wsc
     return {"workload": "prefill layer forward as above, projection weight in block-scaled FP8 "
                         "(E4M3 + one E8M0 scale per 32 inputs), rows fed to the FP8 MFMA "
                         "without dequantisation",
             "tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
             "stages_ms": {"hash": round(st[0], 4), "gather_mx": round(st[1], 4),
-                          "project_mx": round(st[2], 4), "gate": round(st[3], 4)},
+                          "fold": round(st[2], 4), "project_mx_gate_sums": round(st[3], 4),
+                          "gate_sums": round(st[4], 4)},
             "project_mx": {"achieved": round(tflops, 2), "peak": FP8_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(tflops / FP8_PEAK_TFLOPS, 4)},
             "mfma_ceiling": ceiling}

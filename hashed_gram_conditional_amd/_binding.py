@@ -125,6 +125,9 @@ def _load():
         "engram_gate": (ctypes.c_int, [P, P, I32, P, P, P, P, P, P]),
         "engram_fold_gate_weights": (ctypes.c_int, [P, P, I32, I32, P, P]),
         "engram_gate_folded": (ctypes.c_int, [P, P, I32, P, P, P, P, P]),
+        "engram_project_gate_sums": (ctypes.c_int, [P, P, I64, P, P, P, P, P]),
+        "engram_gate_sums": (ctypes.c_int, [P, P, I32, P, P, P, P]),
+        "engram_project_mx_gate_sums": (ctypes.c_int, [P, P, P, I32, P, P, P, P, P, P]),
         "engram_forward_workspace_size": (SZ, [P, P]),
         "engram_gather_rows": (ctypes.c_int, [P, I64, P, I64, P, P]),
         "engram_project_mx": (ctypes.c_int, [P, P, I32, P, P, P, I64, I64, P, SZ, P]),
@@ -313,6 +316,28 @@ def engram_gate_folded(desc: ForwardDesc, ids, raw_vocab: int, kv, qk_w, h, gate
     _check(LIB.engram_gate_folded(ctypes.byref(desc), _ptr(ids), raw_vocab, _ptr(kv),
                                   _ptr(qk_w), _ptr(h), _ptr(gate_out), _stream(stream)),
            "engram_gate_folded")
+
+
+def engram_project_gate_sums(desc: ForwardDesc, e, in_dim: int, wkv, h, qk_w, kv, stream=None):
+    """The projection with the gate's key-side sums in kv's key columns."""
+    _check(LIB.engram_project_gate_sums(ctypes.byref(desc), _ptr(e), in_dim, _ptr(wkv), _ptr(h),
+                                        _ptr(qk_w), _ptr(kv), _stream(stream)),
+           "engram_project_gate_sums")
+
+
+def engram_project_mx_gate_sums(desc: ForwardDesc, e_codes, e_scales, segments: int, w_codes,
+                                w_scales, h, qk_w, kv, stream=None):
+    """engram_project_gate_sums with the block-scaled FP8 weight."""
+    _check(LIB.engram_project_mx_gate_sums(ctypes.byref(desc), _ptr(e_codes), _ptr(e_scales),
+                                           segments, _ptr(w_codes), _ptr(w_scales), _ptr(h),
+                                           _ptr(qk_w), _ptr(kv), _stream(stream)),
+           "engram_project_mx_gate_sums")
+
+
+def engram_gate_sums(desc: ForwardDesc, ids, raw_vocab: int, kv, h, gate_out, stream=None):
+    """The gate and residual update from engram_project_gate_sums' kv."""
+    _check(LIB.engram_gate_sums(ctypes.byref(desc), _ptr(ids), raw_vocab, _ptr(kv), _ptr(h),
+                                _ptr(gate_out), _stream(stream)), "engram_gate_sums")
 
 
 def engram_forward_workspace_size(params: HashParams, desc: ForwardDesc) -> int:

@@ -33,6 +33,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, engram_bf16x2));
 }
 
+// Where the projection with gate sums leaves token t's key-side sums: float2
+// index of kv row t's start (bf16 rows of (hc + 1) * dim, dim a multiple of 4).
+// Pair stream * (dim / 128) + block from there holds (sum k^2, sum h q_w k_w k)
+// over 128-column block `block` of that stream; these bytes lie in the row's
+// key columns, which that projection does not otherwise write.
+__device__ __forceinline__ int64_t gate_sums_pairs(int64_t t, int hc, int dim) {
+  return t * (int64_t)(hc + 1) * dim / 4;
+}
+
 __device__ __forceinline__ float warp_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
@@ -161,6 +170,20 @@ hipError_t engram_launch_gemm_bf16(const uint16_t *e, const uint16_t *w, int64_t
                                    uint16_t *kv, int64_t m, int64_t n, int64_t k, void *workspace,
                                    size_t workspace_bytes, hipStream_t stream);
 
+// The bf16 projection of hc keys and one value (n = (hc + 1) * dim, dim a
+// multiple of 256) over 256 x 256 tiles whatever the token count: value columns
+// stored as engram_launch_gemm_bf16's whole-tile kernel stores them, key tiles
+// replaced by the gate's sums of each token (engram::gate_sums_pairs), which
+// read h [m, hc * dim] and the folded gate weights qk_w [hc * dim].
+hipError_t engram_launch_gemm_bf16_sums(const uint16_t *e, const uint16_t *w, int64_t ldw,
+                                        const uint16_t *h, const float *qk_w, uint16_t *kv,
+                                        int64_t m, int32_t hc, int32_t dim, int64_t k,
+                                        hipStream_t stream);
+
+// Whether engram_launch_gemm_bf16 runs this shape as whole 256 x 256 tiles
+// (enough of them for every CU, no skinny decode schedule).
+hipError_t engram_gemm_bf16_whole_tiles(int64_t m, int64_t n, int64_t k, bool *whole);
+
 // Workspace the bf16 projection uses for a split-K schedule (0 when none).
 hipError_t engram_gemm_bf16_workspace(int64_t m, int64_t n, int64_t k, size_t *bytes);
 
@@ -173,6 +196,15 @@ hipError_t engram_launch_gemm_mx(const uint8_t *w_codes, const uint8_t *w_scales
                                  int64_t m, int64_t n, void *workspace, size_t workspace_bytes,
                                  hipStream_t stream);
 hipError_t engram_gemm_mx_workspace(int64_t m, int64_t n, int32_t segments, size_t *bytes);
+// The block-scaled FP8 projection over whole 256 x 256 tiles with the gate's
+// sums in the key tiles' epilogue (as engram_launch_gemm_bf16_sums), and
+// whether engram_launch_gemm_mx runs a shape as whole tiles.
+hipError_t engram_launch_gemm_mx_sums(const uint8_t *w_codes, const uint8_t *w_scales,
+                                      const uint8_t *e_codes, const uint8_t *e_scales,
+                                      int32_t segments, const uint16_t *h, const float *qk_w,
+                                      uint16_t *kv, int64_t m, int32_t hc, int32_t dim,
+                                      hipStream_t stream);
+hipError_t engram_gemm_mx_whole_tiles(int64_t m, int64_t n, int32_t segments, bool *whole);
 
 hipError_t engram_launch_gemm_f32(const float *e, const float *w, int64_t ldw, float *kv,
                                   int64_t m, int64_t n, int64_t k, hipStream_t stream);
@@ -203,6 +235,13 @@ hipError_t engram_launch_gate(bool f32, const int32_t *ids, EngramDeadRule dead_
                               void *h, float *gate_out, float *stats, int64_t tokens,
                               int32_t hc, int32_t dim, float eps, float clamp, int plain,
                               hipStream_t stream);
+
+// The gate and residual update from the sums engram_launch_gemm_bf16_sums left
+// in kv's key columns, the value row of kv and h (bf16; dim a multiple of 256).
+hipError_t engram_launch_gate_sums(const int32_t *ids, EngramDeadRule dead_rule, const void *kv,
+                                   void *h, float *gate_out, int64_t tokens, int32_t hc,
+                                   int32_t dim, float eps, float clamp, int plain,
+                                   hipStream_t stream);
 
 // qk_w[i] = q_w[i] * k_w[i] over hc * dim fp32 values (dim a multiple of 8).
 hipError_t engram_launch_fold_gate_weights(const float *q_w, const float *k_w, float *qk_w,

@@ -577,6 +577,74 @@ int engram_gate_folded(const engram_forward_desc *desc, const int32_t *ids, int3
                                        stream));
 }
 
+int engram_project_gate_sums(const engram_forward_desc *desc, const void *e, int64_t in_dim,
+                             const void *wkv, const void *h, const float *qk_w, void *kv,
+                             hipStream_t stream) {
+  int rc = check_desc(desc);
+  if (rc != ENGRAM_OK) return rc;
+  if (desc->row_format != ENGRAM_ROW_E4M3_E8M0_264) return ENGRAM_EINVAL;
+  if (desc->dim % 256 != 0 || in_dim < 1 || in_dim % 64 != 0) return ENGRAM_ESHAPE;
+  const int64_t ntok = desc->batch * desc->seq;
+  const int64_t out_dim = (int64_t)(desc->hc + 1) * desc->dim;
+  if (ntok > INT32_MAX || in_dim > INT32_MAX) return ENGRAM_ESHAPE;
+  if (!bf16_projection_shape_ok(ntok, in_dim, out_dim)) return ENGRAM_ESHAPE;
+  int64_t ldw = 0;
+  if ((rc = wkv_row_stride(desc->wkv_ld, in_dim, false, &ldw)) != ENGRAM_OK) return rc;
+  if (ntok == 0) return ENGRAM_OK;
+  if (e == nullptr || wkv == nullptr || h == nullptr || qk_w == nullptr || kv == nullptr)
+    return ENGRAM_EINVAL;
+  if (!aligned(e, 16) || !aligned(wkv, 16) || !aligned(h, 16) || !aligned(qk_w, 16) ||
+      !aligned(kv, 16))
+    return ENGRAM_EINVAL;
+  return hip_status(engram_launch_gemm_bf16_sums((const uint16_t *)e, (const uint16_t *)wkv, ldw,
+                                                 (const uint16_t *)h, qk_w, (uint16_t *)kv, ntok,
+                                                 desc->hc, desc->dim, in_dim, stream));
+}
+
+int engram_project_mx_gate_sums(const engram_forward_desc *desc, const void *e_codes,
+                                const void *e_scales, int32_t segments, const void *w_codes,
+                                const void *w_scales, const void *h, const float *qk_w,
+                                void *kv, hipStream_t stream) {
+  const int rc = check_desc(desc);
+  if (rc != ENGRAM_OK) return rc;
+  if (desc->row_format != ENGRAM_ROW_E4M3_E8M0_264) return ENGRAM_EINVAL;
+  if (segments < 1 || segments > ENGRAM_MAX_SEGMENTS || desc->dim % 256 != 0)
+    return ENGRAM_ESHAPE;
+  const int64_t ntok = desc->batch * desc->seq;
+  const int64_t out_dim = (int64_t)(desc->hc + 1) * desc->dim;
+  if (ntok > INT32_MAX) return ENGRAM_ESHAPE;
+  if (!bf16_projection_shape_ok(ntok, (int64_t)segments * ENGRAM_ROW_DIM_E4M3, out_dim))
+    return ENGRAM_ESHAPE;
+  if (ntok == 0) return ENGRAM_OK;
+  if (e_codes == nullptr || e_scales == nullptr || w_codes == nullptr || w_scales == nullptr ||
+      h == nullptr || qk_w == nullptr || kv == nullptr)
+    return ENGRAM_EINVAL;
+  if (!aligned(e_codes, 16) || !aligned(e_scales, 4) || !aligned(w_codes, 16) ||
+      !aligned(w_scales, 4) || !aligned(h, 16) || !aligned(qk_w, 16) || !aligned(kv, 16))
+    return ENGRAM_EINVAL;
+  return hip_status(engram_launch_gemm_mx_sums(
+      (const uint8_t *)w_codes, (const uint8_t *)w_scales, (const uint8_t *)e_codes,
+      (const uint8_t *)e_scales, segments, (const uint16_t *)h, qk_w, (uint16_t *)kv, ntok,
+      desc->hc, desc->dim, stream));
+}
+
+int engram_gate_sums(const engram_forward_desc *desc, const int32_t *ids, int32_t raw_vocab,
+                     const void *kv, void *h, float *gate_out, hipStream_t stream) {
+  const int rc = check_desc(desc);
+  if (rc != ENGRAM_OK) return rc;
+  if (raw_vocab < 1 || desc->row_format != ENGRAM_ROW_E4M3_E8M0_264) return ENGRAM_EINVAL;
+  if (desc->dim % 256 != 0) return ENGRAM_ESHAPE;
+  const int64_t ntok = desc->batch * desc->seq;
+  if (ntok == 0) return ENGRAM_OK;
+  if (ids == nullptr || kv == nullptr || h == nullptr) return ENGRAM_EINVAL;
+  if (!aligned(ids, 4) || !aligned(kv, 16) || !aligned(h, 16) || !aligned(gate_out, 4))
+    return ENGRAM_EINVAL;
+  if (ntok > INT32_MAX) return ENGRAM_ESHAPE;
+  return hip_status(engram_launch_gate_sums(ids, raw_id_rule(raw_vocab), kv, h, gate_out, ntok,
+                                            desc->hc, desc->dim, desc->eps, desc->gate_clamp,
+                                            desc->gate_mode, stream));
+}
+
 int engram_transpose(const void *src, void *dst, int64_t rows, int64_t cols, int64_t dst_ld,
                      int32_t elem_bytes, hipStream_t stream) {
   if (elem_bytes != 2 && elem_bytes != 4) return ENGRAM_EINVAL;
@@ -741,6 +809,25 @@ int forward_impl(const engram_hash_params *params, const engram_forward_desc *de
             : engram_launch_gather_e4m3((const uint8_t *)table, desc->table_rows, row_ids,
                                         ntok * S, (uint16_t *)e, host, stream);
   if (err != hipSuccess) return hip_status(err);
+  // Calls that fill the CUs with whole 256 x 256 tiles take the key side of the
+  // gate into the projection's epilogue: the keys never reach HBM.
+  bool sums = false;
+  if (!f32 && conv == nullptr && desc->dim % 256 == 0) {
+    err = engram_gemm_bf16_whole_tiles(ntok, out_dim, in_dim, &sums);
+    if (err != hipSuccess) return hip_status(err);
+  }
+  if (sums) {
+    err = engram_launch_fold_gate_weights(q_w, k_w, qk_w, desc->hc, desc->dim, stream);
+    if (err == hipSuccess)
+      err = engram_launch_gemm_bf16_sums((const uint16_t *)e, (const uint16_t *)wkv, ldw,
+                                         (const uint16_t *)h, qk_w, (uint16_t *)kv, ntok,
+                                         desc->hc, desc->dim, in_dim, stream);
+    if (err == hipSuccess)
+      err = engram_launch_gate_sums(ids, hash_rule(params), kv, h, gate_out, ntok, desc->hc,
+                                    desc->dim, desc->eps, desc->gate_clamp, desc->gate_mode,
+                                    stream);
+    return hip_status(err);
+  }
   err = f32 ? engram_launch_gemm_f32((const float *)e, (const float *)wkv, ldw, (float *)kv,
                                      ntok, out_dim, in_dim, stream)
             : engram_launch_gemm_bf16((const uint16_t *)e, (const uint16_t *)wkv, ldw,
@@ -853,6 +940,25 @@ int engram_forward_mx(const engram_hash_params *params, const engram_forward_des
   err = engram_launch_gather_mx((const uint8_t *)table, desc->table_rows, row_ids, ntok * S,
                                 e_codes, e_scales, host, stream);
   if (err != hipSuccess) return hip_status(err);
+  // As in engram_forward: whole tiles take the key side of the gate into the
+  // projection's epilogue.
+  bool sums = false;
+  if (desc->dim % 256 == 0) {
+    err = engram_gemm_mx_whole_tiles(ntok, out_dim, S, &sums);
+    if (err != hipSuccess) return hip_status(err);
+  }
+  if (sums) {
+    err = engram_launch_fold_gate_weights(q_w, k_w, qk_w, desc->hc, desc->dim, stream);
+    if (err == hipSuccess)
+      err = engram_launch_gemm_mx_sums((const uint8_t *)w_codes, (const uint8_t *)w_scales,
+                                       e_codes, e_scales, S, (const uint16_t *)h, qk_w, kv, ntok,
+                                       desc->hc, desc->dim, stream);
+    if (err == hipSuccess)
+      err = engram_launch_gate_sums(ids, hash_rule(params), kv, h, gate_out, ntok, desc->hc,
+                                    desc->dim, desc->eps, desc->gate_clamp, desc->gate_mode,
+                                    stream);
+    return hip_status(err);
+  }
   err = engram_launch_gemm_mx((const uint8_t *)w_codes, (const uint8_t *)w_scales, e_codes,
                               e_scales, S, kv, ntok, out_dim, gemm_ws, gemm_ws_bytes, stream);
   if (err != hipSuccess) return hip_status(err);

@@ -26,6 +26,12 @@
 // With a stats buffer the kernel is the first half of the short-convolution
 // variant: it stores each token's gates and the mean square of its value row
 // (the factors of the gated value's RMS) and leaves h to the convolution.
+//
+// gate_sums_kernel is the second half of the projection that computes the key
+// side of the gate in its epilogue (the pages' "上下文门控 + 单次 GEMM 融合" in
+// "条件记忆：DeepSeek V4.1 Engram 如何用 O(1) 查表换掉一层计算" §2.3): it reads
+// each token's sums of k^2 and h q_w k_w k per 128-column block instead of
+// the keys, 91 KB per token at hc 4 x 5120 against 133 KB.
 #include "common.h"
 
 namespace {
@@ -269,6 +275,23 @@ __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
   }
 }
 
+// Threads per token block for the gate kernels: 128 when there are enough
+// tokens to keep HBM busy (about 8 per CU), up to 512 below that (few); never
+// more threads than a stream has 8-element chunks, rounded up to whole waves.
+hipError_t gate_threads(int64_t tokens, int dim, int &threads, int &cpt, bool &few) {
+  int dev = 0, cus = 256;
+  hipError_t err = hipGetDevice(&dev);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
+  const int cps = dim / kChunk;
+  few = tokens < 8 * (int64_t)cus;
+  threads = few ? kMaxThreads : 128;
+  const int needed = ((cps + engram::kWave - 1) / engram::kWave) * engram::kWave;
+  if (threads > needed) threads = needed;
+  cpt = (cps + threads - 1) / threads;
+  return hipSuccess;
+}
+
 template <bool F32>
 hipError_t launch(int cpt, int threads, bool all_streams, const int32_t *ids,
                   EngramDeadRule dead_rule,
@@ -311,23 +334,137 @@ hipError_t engram_launch_gate(bool f32, const int32_t *ids, EngramDeadRule dead_
                               float *stats, int64_t tokens, int32_t hc, int32_t dim, float eps,
                               float clamp, int plain, hipStream_t stream) {
   if (tokens <= 0) return hipSuccess;
-  int dev = 0, cus = 256;
-  hipError_t err = hipGetDevice(&dev);
-  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  int threads = 0, cpt = 0;
+  bool few = false;
+  const hipError_t err = gate_threads(tokens, dim, threads, cpt, few);
   if (err != hipSuccess) return err;
-  const int cps = dim / kChunk;
-  // 128-thread blocks need about 8 tokens per CU to keep HBM busy; below that,
-  // spread each token over more lanes.
-  int threads = tokens >= 8 * (int64_t)cus ? 128 : kMaxThreads;
-  const int needed = ((cps + engram::kWave - 1) / engram::kWave) * engram::kWave;
-  if (threads > needed) threads = needed;
-  const int cpt = (cps + threads - 1) / threads;
   // few tokens: one memory round trip per token for up to kAllStreams streams
-  const bool all_streams = tokens < 8 * (int64_t)cus && hc <= kAllStreams && cpt <= 2;
+  const bool all_streams = few && hc <= kAllStreams && cpt <= 2;
   return f32 ? launch<true>(cpt, threads, all_streams, ids, dead_rule, kv, q_w, k_w, h,
                             gate_out, stats, tokens, hc, dim, eps, clamp, plain, stream)
              : launch<false>(cpt, threads, all_streams, ids, dead_rule, kv, q_w, k_w, h,
                              gate_out, stats, tokens, hc, dim, eps, clamp, plain, stream);
+}
+
+namespace {
+
+// The gate from the key-side sums the projection left in kv's key columns
+// (engram::gate_sums_pairs): per stream, sum h^2 from h, which is read for
+// the update anyway, and the sums of its dim / 128 column blocks, added in
+// block order within each wave and then over the waves. The value row and h
+// are read, h is written, as in gate_kernel; the keys are never read.
+template <int CPT>
+__global__ __launch_bounds__(kMaxThreads) void gate_sums_kernel(
+    const int32_t *__restrict__ ids, EngramDeadRule dead_rule, const uint16_t *__restrict__ kv,
+    void *__restrict__ h, float *__restrict__ gate_out, int hc, int dim, float eps, float clamp,
+    int plain) {
+  __shared__ float red[kMaxThreads / engram::kWave][kMaxHc][3];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nthreads = blockDim.x;
+  if (engram_dead(dead_rule, ids[t])) {   // DEAD: gate 0, streams untouched
+    if (gate_out != nullptr && tid < hc) gate_out[t * hc + tid] = 0.f;
+    return;
+  }
+  const int cps = dim / kChunk;
+  const int blocks = dim / 128;
+  const int64_t kv_row = t * (int64_t)(hc + 1) * cps;
+  const int64_t h_row = t * (int64_t)hc * cps;
+  const float2 *sums = reinterpret_cast<const float2 *>(kv) + engram::gate_sums_pairs(t, hc, dim);
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int nwaves = nthreads >> 6;
+  const float inv_d = 1.0f / (float)dim;
+  const float inv_sqrt_d = 1.0f / sqrtf((float)dim);
+
+  Chunk<false> vv[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int ci = tid + c * nthreads;
+    if (ci < cps) vv[c].load_nt(kv, kv_row + (int64_t)hc * cps + ci);
+  }
+#pragma unroll
+  for (int m = 0; m < kMaxHc; ++m) {
+    if (m >= hc) break;
+    Chunk<false> hh[CPT];
+    float shh = 0.f, skk = 0.f, shk = 0.f;
+    for (int b = tid; b < blocks; b += nthreads) {
+      const float2 s = sums[m * blocks + b];
+      skk += s.x;
+      shk += s.y;
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ci = tid + c * nthreads;
+      if (ci < cps) {
+        hh[c].load_nt(h, h_row + (int64_t)m * cps + ci);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) shh = fmaf(hh[c][e], hh[c][e], shh);
+      }
+    }
+    shh = engram::warp_sum(shh);
+    skk = engram::warp_sum(skk);
+    shk = engram::warp_sum(shk);
+    if (lane == 0) {
+      red[wave][m][0] = shh;
+      red[wave][m][1] = skk;
+      red[wave][m][2] = shk;
+    }
+    __syncthreads();
+    float a = 0.f, b = 0.f, c2 = 0.f;
+    for (int w = 0; w < nwaves; ++w) {
+      a += red[w][m][0];
+      b += red[w][m][1];
+      c2 += red[w][m][2];
+    }
+    const float rh = 1.0f / sqrtf(a * inv_d + eps);
+    const float rk = 1.0f / sqrtf(b * inv_d + eps);
+    const float sc = c2 * rh * rk * inv_sqrt_d;
+    const float z = plain ? sc : copysignf(sqrtf(fmaxf(fabsf(sc), clamp)), sc);
+    const float alpha = 1.0f / (1.0f + expf(-z));
+    if (tid == 0 && gate_out != nullptr) gate_out[t * hc + m] = alpha;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ci = tid + c * nthreads;
+      if (ci < cps) {
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = fmaf(alpha, vv[c][e], hh[c][e]);
+        Chunk<false>::store_nt(h, h_row + (int64_t)m * cps + ci, o);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t engram_launch_gate_sums(const int32_t *ids, EngramDeadRule dead_rule, const void *kv,
+                                   void *h, float *gate_out, int64_t tokens, int32_t hc,
+                                   int32_t dim, float eps, float clamp, int plain,
+                                   hipStream_t stream) {
+  if (tokens <= 0) return hipSuccess;
+  int threads = 0, cpt = 0;
+  bool few = false;
+  const hipError_t err = gate_threads(tokens, dim, threads, cpt, few);
+  if (err != hipSuccess) return err;
+#define ENGRAM_GATE_SUMS_CASE(N)                                                              \
+  hipLaunchKernelGGL((gate_sums_kernel<N>), dim3((unsigned)tokens), dim3(threads), 0, stream,  \
+                     ids, dead_rule, (const uint16_t *)kv, h, gate_out, hc, dim, eps, clamp,  \
+                     plain)
+  switch (cpt) {
+    case 1: ENGRAM_GATE_SUMS_CASE(1); break;
+    case 2: ENGRAM_GATE_SUMS_CASE(2); break;
+    case 3: ENGRAM_GATE_SUMS_CASE(3); break;
+    case 4: ENGRAM_GATE_SUMS_CASE(4); break;
+    case 5: ENGRAM_GATE_SUMS_CASE(5); break;
+    case 6: ENGRAM_GATE_SUMS_CASE(6); break;
+    case 7: ENGRAM_GATE_SUMS_CASE(7); break;
+    case 8: ENGRAM_GATE_SUMS_CASE(8); break;
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef ENGRAM_GATE_SUMS_CASE
+  return hipGetLastError();
 }
 
 namespace {

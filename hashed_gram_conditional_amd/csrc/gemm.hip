@@ -222,6 +222,27 @@ void gemm_bf16_kernel(const uint16_t *__restrict__ E, const uint16_t *__restrict
   wide_store_bf16(acc, C, M, N, m0, n0);
 }
 
+// The same tiles and order, with key tiles (columns below hc * dim) ending in
+// the gate's sums instead of bf16 keys. Their epilogue reads 128 KiB of h and
+// writes 2 KiB where the plain kernel writes 128 KiB of keys, and the gate
+// then reads 1.3 KB of sums per token instead of hc * dim keys.
+__global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_bf16_sums_kernel(const uint16_t *__restrict__ E, const uint16_t *__restrict__ W,
+                           uint16_t *__restrict__ C, int M, int N, int K, int ldw, int tiles_m,
+                           int tiles_n, const uint16_t *__restrict__ h,
+                           const float *__restrict__ qk_w, int hc, int dim) {
+  __shared__ __align__(1024) WideLds lds;
+  int m0, n0;
+  tile_origin(tiles_m, tiles_n, BN, m0, n0);
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  wide_tile(E, W, M, N, K, ldw, m0, n0, 0, K / BK, acc, lds);
+  if (n0 < hc * dim)
+    wide_store_gate_sums(acc, h, qk_w, C, M, m0, n0, hc, dim);
+  else
+    wide_store_bf16(acc, C, M, N, m0, n0);
+}
+
 // ---- skinny calls: one token tile, columns dealt to every CU ----------------------
 // With at most 256 tokens (decode) the 256 x 256 tiles number fewer than the
 // CUs. Here block b takes all tokens and its own slice of 32 * NT output columns
@@ -700,6 +721,33 @@ hipError_t engram_launch_gemm_bf16(const uint16_t *e, const uint16_t *w, int64_t
   hipLaunchKernelGGL(gemm_bf16_narrow_kernel<128>, dim3((unsigned)(tiles_m * tiles_n128)),
                      dim3(kNarrowThreads), 0, stream, e, w, kv, (int)m, (int)n, (int)k, (int)ldw,
                      tiles_m, tiles_n128);
+  return hipGetLastError();
+}
+
+hipError_t engram_gemm_bf16_whole_tiles(int64_t m, int64_t n, int64_t k, bool *whole) {
+  *whole = false;
+  if (m <= 0 || n <= 0) return hipSuccess;
+  int w_lo = 0, wide = 0, sk_blocks = 0;
+  hipError_t err = plan_skinny(m, n, k, w_lo, wide, sk_blocks);
+  if (err != hipSuccess || sk_blocks > 0) return err;
+  StreamK sk;
+  err = plan_streamk(m, n, k / BK, sk);
+  if (err != hipSuccess) return err;
+  *whole = sk.blocks == 0;
+  return hipSuccess;
+}
+
+hipError_t engram_launch_gemm_bf16_sums(const uint16_t *e, const uint16_t *w, int64_t ldw,
+                                        const uint16_t *h, const float *qk_w, uint16_t *kv,
+                                        int64_t m, int32_t hc, int32_t dim, int64_t k,
+                                        hipStream_t stream) {
+  if (m <= 0) return hipSuccess;
+  const int64_t n = (int64_t)(hc + 1) * dim;
+  const int tiles_m = (int)((m + BM - 1) / BM);
+  const int tiles_n = (int)(n / BN);
+  hipLaunchKernelGGL(gemm_bf16_sums_kernel, dim3((unsigned)(tiles_m * tiles_n)),
+                     dim3(kWideThreads), 0, stream, e, w, kv, (int)m, (int)n, (int)k, (int)ldw,
+                     tiles_m, tiles_n, h, qk_w, (int)hc, (int)dim);
   return hipGetLastError();
 }
 

@@ -298,6 +298,25 @@ void gemm_mx_kernel(MxOperands op, uint16_t *__restrict__ C, int M, int N, int t
   wide_store_bf16(acc, C, M, N, m0, n0);
 }
 
+// The same tiles with the key tiles' epilogue forming the gate's sums in place
+// of the keys (wide_store_gate_sums), as gemm_bf16_sums_kernel does.
+__global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_mx_sums_kernel(MxOperands op, uint16_t *__restrict__ C, int M, int N, int tiles_m,
+                         int tiles_n, const uint16_t *__restrict__ h,
+                         const float *__restrict__ qk_w, int hc, int dim) {
+  __shared__ __align__(1024) MxLds lds;
+  int m0, n0;
+  tile_origin(tiles_m, tiles_n, BN, m0, n0);
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  wide_tile_mx(op, M, N, m0, n0, 0, op.segments * 256 / kMxBk, acc, lds.w[0], lds.w[1],
+               lds.e[0], lds.e[1], lds.ws[0], lds.ws[1], lds.es[0], lds.es[1]);
+  if (n0 < hc * dim)
+    wide_store_gate_sums(acc, h, qk_w, C, M, m0, n0, hc, dim);
+  else
+    wide_store_bf16(acc, C, M, N, m0, n0);
+}
+
 __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_mx_streamk_kernel(MxOperands op, uint16_t *__restrict__ C, float *__restrict__ ws,
                             int M, int N, StreamK sk) {
@@ -355,6 +374,32 @@ hipError_t engram_launch_gemm_mx(const uint8_t *w_codes, const uint8_t *w_scales
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   return engram_gemm::launch_streamk_fixup((const float *)workspace, kv, m, n, sk, stream);
+}
+
+hipError_t engram_launch_gemm_mx_sums(const uint8_t *w_codes, const uint8_t *w_scales,
+                                      const uint8_t *e_codes, const uint8_t *e_scales,
+                                      int32_t segments, const uint16_t *h, const float *qk_w,
+                                      uint16_t *kv, int64_t m, int32_t hc, int32_t dim,
+                                      hipStream_t stream) {
+  if (m <= 0) return hipSuccess;
+  const MxOperands op{w_codes, w_scales, e_codes, e_scales, segments};
+  const int64_t n = (int64_t)(hc + 1) * dim;
+  const int tiles_m = (int)((m + BM - 1) / BM);
+  const int tiles_n = (int)(n / BN);
+  hipLaunchKernelGGL(gemm_mx_sums_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kWideThreads),
+                     0, stream, op, kv, (int)m, (int)n, tiles_m, tiles_n, h, qk_w, (int)hc,
+                     (int)dim);
+  return hipGetLastError();
+}
+
+hipError_t engram_gemm_mx_whole_tiles(int64_t m, int64_t n, int32_t segments, bool *whole) {
+  *whole = false;
+  if (m <= 0 || n <= 0) return hipSuccess;
+  StreamK sk;
+  const hipError_t err = plan_streamk(m, n, (int64_t)segments * 256 / kMxBk, sk);
+  if (err != hipSuccess) return err;
+  *whole = sk.blocks == 0;
+  return hipSuccess;
 }
 
 hipError_t engram_gemm_mx_workspace(int64_t m, int64_t n, int32_t segments, size_t *bytes) {

@@ -75,6 +75,71 @@ __device__ __forceinline__ void wide_store_bf16(const f32x16 (&acc)[4][4],
   }
 }
 
+// Epilogue of a finished key tile (all its columns in stream n0 / dim, dim a
+// multiple of 256): in place of the bf16 keys, each token's two sums over the
+// 128 columns of each wave's half, sum k^2 and sum h q_w k_w k, with k the
+// accumulator rounded to bf16 as the stored key would be, h the token's stream
+// (bf16 [M, hc * dim], read here) and qk_w the folded weights [hc * dim]. They
+// go to kv row m's key columns (engram::gate_sums_pairs), which the gate then
+// reads instead of the keys. Lanes l and l + 32 hold the same token and
+// alternating quads of 4 columns; their sums meet in one exchange.
+__device__ __forceinline__ void wide_store_gate_sums(const f32x16 (&acc)[4][4],
+                                                     const uint16_t *__restrict__ h,
+                                                     const float *__restrict__ qk_w,
+                                                     uint16_t *__restrict__ kv, int M, int m0,
+                                                     int n0, int hc, int dim) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wn = wave >> 1, wm = wave & 1;
+  const int frow = lane & 31, fk = lane >> 5;
+  const int key_cols = hc * dim;
+  const int stream = n0 / dim;
+  const int block = (n0 - stream * dim) / 128 + wn;
+  const int nb = n0 + wn * 128 + fk * 4;
+  float4 w[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) w[i][g] = *reinterpret_cast<const float4 *>(qk_w + nb + i * 32 + g * 8);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + wm * 128 + j * 32 + frow;
+    const bool ok = m < M;
+    // rows past M read row m0's stream (in bounds) and store nothing
+    const uint16_t *hrow = h + (int64_t)(ok ? m : m0) * key_cols + nb;
+    uint2 hv[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) hv[i][g] = *reinterpret_cast<const uint2 *>(hrow + i * 32 + g * 8);
+    float skk = 0.f, shk = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t k01 = engram::pack_bf16x2(acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1]);
+        const uint32_t k23 = engram::pack_bf16x2(acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]);
+        const float k[4] = {__uint_as_float(k01 << 16), __uint_as_float(k01 & 0xFFFF0000u),
+                            __uint_as_float(k23 << 16), __uint_as_float(k23 & 0xFFFF0000u)};
+        const float hh[4] = {__uint_as_float(hv[i][g].x << 16),
+                             __uint_as_float(hv[i][g].x & 0xFFFF0000u),
+                             __uint_as_float(hv[i][g].y << 16),
+                             __uint_as_float(hv[i][g].y & 0xFFFF0000u)};
+        const float ww[4] = {w[i][g].x, w[i][g].y, w[i][g].z, w[i][g].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          skk = fmaf(k[c], k[c], skk);
+          shk = fmaf(hh[c] * ww[c], k[c], shk);
+        }
+      }
+    skk += __shfl_xor(skk, 32, engram::kWave);
+    shk += __shfl_xor(shk, 32, engram::kWave);
+    if (fk == 0 && ok)
+      reinterpret_cast<float2 *>(kv)[engram::gate_sums_pairs(m, hc, dim) + stream * (dim / 128) +
+                                     block] = make_float2(skk, shk);
+  }
+}
+
 __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)

@@ -461,6 +461,63 @@ int engram_gate_folded(const engram_forward_desc *desc, const int32_t *ids, int3
                        const void *kv, const float *qk_w, void *h, float *gate_out,
                        hipStream_t stream);
 
+/*
+ * Steps 4 and 5 with the key side of the gate in the projection's epilogue
+ * ([P3] §2.3, the context gate fused with the single projection; [P1] "门控"
+ * and [P4] "消费：学习投影 + 余弦门控" for the sums). The gate of stream m
+ * needs of its keys only sum_i k_i^2 and sum_i h_i q_w,i k_w,i k_i, so the
+ * projection forms them per 128-column block while the keys are still in
+ * registers, and no key is written to memory. engram_forward takes this path
+ * whenever the projection fills the CUs with whole 256 x 256 tiles (bf16 rows,
+ * dim % 256 == 0, no convolution branch); these two entry points are its
+ * launches, for tests and timing.
+ *
+ * engram_project_gate_sums: kv = e W over 256 x 256 tiles, whatever the token
+ * count.
+ *   desc     batch * seq tokens, hc, dim (a multiple of 256), wkv_ld; row_format
+ *            must be ENGRAM_ROW_E4M3_E8M0_264 (bf16 activations)
+ *   e, in_dim, wkv   as engram_project (bf16; in_dim % 64 == 0)
+ *   h        [tokens, hc, dim] bf16, the streams the gate will update (read only)
+ *   qk_w     [hc, dim] float, q_w * k_w (engram_fold_gate_weights)
+ *   kv       [tokens, (hc+1) dim] bf16. The value columns [hc dim, (hc+1) dim)
+ *            get engram_project's bits for a call that fills the CUs with whole
+ *            tiles (every call of this entry point sums each output's K in that
+ *            order). The first hc * dim / 128 float pairs of each row (8-byte
+ *            aligned, inside its key columns) get, for stream m and column block
+ *            b, pair m * (dim / 128) + b = (sum k^2, sum h q_w k_w k) over
+ *            columns [128 b, 128 b + 128) of that stream, k rounded to bf16 as
+ *            engram_project would store it, fp32 sums. The other key columns
+ *            are not written.
+ * Errors: ENGRAM_EINVAL (NULL or misaligned pointers, fp32 rows),
+ * ENGRAM_ESHAPE (dim % 256, in_dim, wkv_ld or the tile bound of
+ * engram_project), ENGRAM_EHIP.
+ *
+ * engram_gate_sums: step 5 from those sums, the value columns of kv and h.
+ *   desc, ids, raw_vocab, h, gate_out   as engram_gate (bf16 rows, dim % 256 == 0)
+ *   kv       as left by engram_project_gate_sums
+ * The gates equal engram_gate's on the same keys up to the order of the fp32
+ * sums. Errors as engram_gate, and ENGRAM_EINVAL for fp32 rows.
+ */
+int engram_project_gate_sums(const engram_forward_desc *desc, const void *e, int64_t in_dim,
+                             const void *wkv, const void *h, const float *qk_w, void *kv,
+                             hipStream_t stream);
+int engram_gate_sums(const engram_forward_desc *desc, const int32_t *ids, int32_t raw_vocab,
+                     const void *kv, void *h, float *gate_out, hipStream_t stream);
+
+/*
+ * engram_project_gate_sums for the block-scaled FP8 weight: engram_project_mx's
+ * operands (e_codes, e_scales, segments, w_codes, w_scales as there) over whole
+ * 256 x 256 tiles, h and qk_w as engram_project_gate_sums, kv laid out as
+ * there (value columns with engram_project_mx's whole-tile bits, the sums in
+ * the key columns). engram_forward_mx takes this path under the same rule as
+ * engram_forward. Errors as engram_project_mx, and ENGRAM_ESHAPE for
+ * dim % 256 != 0.
+ */
+int engram_project_mx_gate_sums(const engram_forward_desc *desc, const void *e_codes,
+                                const void *e_scales, int32_t segments, const void *w_codes,
+                                const void *w_scales, const void *h, const float *qk_w,
+                                void *kv, hipStream_t stream);
+
 /* Bytes of workspace engram_forward needs (row ids, e, kv, the folded gate
  * scales and the projection's workspace), or 0 on bad args. Calls of 2048
  * tokens or more fold q_w * k_w there (engram_fold_gate_weights; the same

@@ -110,7 +110,7 @@ def _h_values(bits_or_f32):
 
 def check_forward_chunks(*, tokens, rid, dead, fetch_rows, table_f32, table_rows, wkv, q_w,
                          k_w, h_in, h_out, gates, hc, dim, eps, clamp, bf16, kv=None,
-                         mx=False, chunk=256, workers=None, name="forward"):
+                         mx=False, chunk=256, workers=None, name="forward", also=()):
     """Oracle steps 3-5 on ``tokens`` against a device forward's results.
 
     rid [n_all, S], dead [n_all]: the oracle's row ids and DEAD flags of every
@@ -119,7 +119,10 @@ def check_forward_chunks(*, tokens, rid, dead, fetch_rows, table_f32, table_rows
     projection, or None; wkv float64 [(hc+1) d, K]. Tokens are split into chunks
     that worker threads run through ``forward_tokens`` independently (tokens do
     not interact in steps 3-5), with BLAS limited to one thread per worker.
-    Raises AssertionError naming the first failures; returns counts.
+    ``also``: further (label, h_out, gates) results of the same inputs, judged
+    against the same oracle results by the same rules (one oracle pass).
+    Raises AssertionError naming the first failures; returns the counts of the
+    first result.
     """
     from concurrent.futures import ThreadPoolExecutor
     import os
@@ -155,6 +158,14 @@ def check_forward_chunks(*, tokens, rid, dead, fetch_rows, table_f32, table_rows
                 out["fail"].append(f"kv token {tk[i[0]]} block {i[1]} col {i[2]}: got "
                                    f"{got[tuple(i)]}, exact {exact[tuple(i)]}, tol {tol[tuple(i)]:.3g}"
                                    f" ({int(bad.sum())} in chunk)")
+        out["per"] = []
+        for label, h_out_r, gates_r in ((name, h_out, gates),) + tuple(also):
+            out["per"].append(judge(label, tk, dead[tk], res, exact, tol, h_out_r, gates_r))
+        out["fail"] += [f for p in out["per"] for f in p["fail"]]
+        return out
+
+    def judge(label, tk, dd, res, exact, tol, h_out, gates):
+        out = {"fail": []}
         a_got = np.asarray(gates[tk], dtype=np.float64)
         a_exp = res["alpha"]
         a_err = np.abs(a_got - a_exp)
@@ -167,15 +178,14 @@ def check_forward_chunks(*, tokens, rid, dead, fetch_rows, table_f32, table_rows
             a_tol = a_plain + np.where(zone, 0.25 * np.sqrt(2.0 * S_ZONE), 0.0)
         bad = ~(a_err <= a_tol)
         out["gates_in_zone"] = int((~(a_err <= a_plain)).sum())
-        dd = dead[tk]
         bad |= dd[:, None] & (a_got != 0.0)
         if bad.any():
             i = np.argwhere(bad)[0]
-            out["fail"].append(f"gate token {tk[i[0]]} stream {i[1]}: got {a_got[tuple(i)]}, "
+            out["fail"].append(f"{label}: gate token {tk[i[0]]} stream {i[1]}: got {a_got[tuple(i)]}, "
                                f"oracle {a_exp[tuple(i)]} ({int(bad.sum())} in chunk)")
         h_got_raw = h_out[tk]
         if dd.any() and not np.array_equal(h_got_raw[dd], h_in[tk][dd]):
-            out["fail"].append("a DEAD token's streams changed")
+            out["fail"].append(f"{label}: a DEAD token's streams changed")
         h_got = _h_values(h_got_raw)
         h_exp = res["h_out"]
         err = np.abs(h_got - h_exp)
@@ -185,7 +195,7 @@ def check_forward_chunks(*, tokens, rid, dead, fetch_rows, table_f32, table_rows
         bad = ~(err <= plain + allow)
         if bad.any():
             i = np.argwhere(bad)[0]
-            out["fail"].append(f"h token {tk[i[0]]} stream {i[1]} col {i[2]}: got "
+            out["fail"].append(f"{label}: h token {tk[i[0]]} stream {i[1]} col {i[2]}: got "
                                f"{h_got[tuple(i)]}, oracle {h_exp[tuple(i)]} "
                                f"({int(bad.sum())} in chunk)")
         out["allowed"] = int((~(err <= plain)).sum())
@@ -197,23 +207,30 @@ def check_forward_chunks(*, tokens, rid, dead, fetch_rows, table_f32, table_rows
         with ThreadPoolExecutor(workers) as ex:
             parts = list(ex.map(one, range(0, len(tokens), chunk)))
     fails = [f for p in parts for f in p["fail"]]
-    stats = {"tokens": int(sum(p["n"] for p in parts)),
-             "elements": int(sum(p["elements"] for p in parts)),
-             "allowed": int(sum(p["allowed"] for p in parts)),
-             "gates_in_zone": int(sum(p["gates_in_zone"] for p in parts)),
-             "max_gate_err": max(p["max_gate_err"] for p in parts)}
-    say(f"  {name}: {stats['tokens']} tokens checked, {stats['allowed']} of "
-        f"{stats['elements']} h elements needed the kv-rounding allowance, "
-        f"{stats['gates_in_zone']} gates the signed-root allowance, "
-        f"max |gate - oracle| {stats['max_gate_err']:.2e}")
+    labels = [name] + [a[0] for a in also]
+    all_stats = []
+    for r, label in enumerate(labels):
+        per = [p["per"][r] for p in parts]
+        stats = {"tokens": int(sum(p["n"] for p in parts)),
+                 "elements": int(sum(q["elements"] for q in per)),
+                 "allowed": int(sum(q["allowed"] for q in per)),
+                 "gates_in_zone": int(sum(q["gates_in_zone"] for q in per)),
+                 "max_gate_err": max(q["max_gate_err"] for q in per)}
+        say(f"  {label}: {stats['tokens']} tokens checked, {stats['allowed']} of "
+            f"{stats['elements']} h elements needed the kv-rounding allowance, "
+            f"{stats['gates_in_zone']} gates the signed-root allowance, "
+            f"max |gate - oracle| {stats['max_gate_err']:.2e}")
+        all_stats.append(stats)
     if fails:
         raise AssertionError(f"{name}: " + "; ".join(fails[:6]))
-    share = stats["allowed"] / max(stats["elements"], 1)
-    cap = ALLOW_SHARE_MAX_MX if mx else ALLOW_SHARE_MAX
-    assert share <= cap, (
-        f"{name}: {stats['allowed']} h elements ({share:.2e}) needed the kv-rounding "
-        f"allowance, more than {cap}")
-    n_gates = stats["tokens"] * hc
-    assert stats["gates_in_zone"] <= GATE_ZONE_SHARE_MAX * n_gates, (
-        f"{name}: {stats['gates_in_zone']} of {n_gates} gates needed the signed-root allowance")
-    return stats
+    for label, stats in zip(labels, all_stats):
+        share = stats["allowed"] / max(stats["elements"], 1)
+        cap = ALLOW_SHARE_MAX_MX if mx else ALLOW_SHARE_MAX
+        assert share <= cap, (
+            f"{label}: {stats['allowed']} h elements ({share:.2e}) needed the kv-rounding "
+            f"allowance, more than {cap}")
+        n_gates = stats["tokens"] * hc
+        assert stats["gates_in_zone"] <= GATE_ZONE_SHARE_MAX * n_gates, (
+            f"{label}: {stats['gates_in_zone']} of {n_gates} gates needed the signed-root "
+            f"allowance")
+    return all_stats[0]

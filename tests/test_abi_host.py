@@ -309,6 +309,53 @@ def test_fold_and_folded_gate_validation():
                                 None) == E.EINVAL                    # raw_vocab < 1
 
 
+@host_only
+def test_gate_sums_validation():
+    """engram_project_gate_sums / engram_project_mx_gate_sums / engram_gate_sums:
+    bf16 rows and dim % 256 only, the projections' shape rules, every pointer
+    present and aligned."""
+    L = E.LIB
+    bf16 = E.ROW_E4M3_E8M0_264
+    d = E.forward_desc(2, 300, 4, 512, 100, bf16, 256, wkv_ld=1032)
+    ps = lambda desc, k=1024, e=0x1000, w=0x2000, h=0x3000, qk=0x4000, kv=0x5000: \
+        L.engram_project_gate_sums(ctypes.byref(desc), e, k, w, h, qk, kv, None)
+    for bad_k in (0, 1000, -64):
+        assert ps(d, k=bad_k) == E.ESHAPE
+    assert ps(E.forward_desc(2, 300, 4, 320, 100, bf16, 256)) == E.ESHAPE     # dim % 256
+    assert ps(E.forward_desc(2, 300, 4, 512, 100, E.ROW_F32, 32)) == E.EINVAL
+    assert ps(E.forward_desc(2, 300, 4, 512, 100, bf16, 256, wkv_ld=1000)) == E.ESHAPE
+    assert ps(E.forward_desc(2, 300, 4, 512, 100, bf16, 256, wkv_ld=1028)) == E.ESHAPE
+    assert ps(E.forward_desc(0, 300, 4, 512, 100, bf16, 256), e=None) == E.OK  # no tokens
+    for name in ("e", "w", "h", "qk", "kv"):
+        assert ps(d, **{name: None}) == E.EINVAL, name
+        assert ps(d, **{name: 0x6008}) == E.EINVAL, name
+    big = E.forward_desc(1 << 15, 1 << 15, 4, 512, 100, bf16, 256)
+    assert ps(big) == E.ESHAPE                            # beyond the tile bound
+    gs = lambda desc, ids=0x1000, vocab=100, kv=0x2000, h=0x3000, g=None: \
+        L.engram_gate_sums(ctypes.byref(desc), ids, vocab, kv, h, g, None)
+    assert gs(E.forward_desc(2, 8, 4, 320, 100, bf16, 256)) == E.ESHAPE
+    assert gs(E.forward_desc(2, 8, 4, 512, 100, E.ROW_F32, 32)) == E.EINVAL
+    assert gs(d, vocab=0) == E.EINVAL
+    assert gs(E.forward_desc(2, 8, 9, 512, 100, bf16, 256)) == E.ESHAPE     # hc > 8
+    for kw in ({"ids": None}, {"kv": None}, {"h": None}, {"ids": 0x1002}, {"kv": 0x2008},
+               {"h": 0x3008}, {"g": 0x4002}):
+        assert gs(d, **kw) == E.EINVAL, kw
+    assert gs(E.forward_desc(0, 8, 4, 512, 100, bf16, 256), ids=None) == E.OK
+    pm = lambda desc, segs=4, ec=0x1000, es=0x2000, wc=0x3000, wsc=0x4000, h=0x5000, qk=0x6000, \
+        kv=0x7000: L.engram_project_mx_gate_sums(ctypes.byref(desc), ec, es, segs, wc, wsc, h, qk,
+                                                 kv, None)
+    for segs in (0, 65):
+        assert pm(d, segs=segs) == E.ESHAPE
+    assert pm(E.forward_desc(2, 300, 4, 320, 100, bf16, 256)) == E.ESHAPE
+    assert pm(E.forward_desc(2, 300, 4, 512, 100, E.ROW_F32, 32)) == E.EINVAL
+    assert pm(big) == E.ESHAPE
+    for name, bad in (("ec", 0x1008), ("es", 0x2002), ("wc", 0x3008), ("wsc", 0x4002),
+                      ("h", 0x5008), ("qk", 0x6008), ("kv", 0x7008)):
+        assert pm(d, **{name: None}) == E.EINVAL, name
+        assert pm(d, **{name: bad}) == E.EINVAL, name
+    assert pm(E.forward_desc(0, 300, 4, 512, 100, bf16, 256), ec=None) == E.OK
+
+
 def test_forward_static_refuses_calls_beyond_its_array():
     """engram_forward_static checks its scratch need on the host, before it
     looks up the array or launches anything."""

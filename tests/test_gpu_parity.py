@@ -512,12 +512,15 @@ def _host(t):
     return t.cpu().numpy() if t.dtype == torch.float32 else bf16_bits(t)
 
 
-def _check_forward(gw, h_out_dev, gates_dev, tokens, kv_dev=None, wkv=None, mx=False):
+def _check_forward(gw, h_out_dev, gates_dev, tokens, kv_dev=None, wkv=None, mx=False, also=()):
     """Oracle on ``tokens`` against the device results of a full forward: every
     gate and stream element at the plain tolerance (with the counted kv-rounding
     allowance), DEAD tokens' gates zero and streams bit-identical, and the
-    device's kv (when given) within the projection's bound."""
+    device's kv (when given) within the projection's bound. ``also``: more
+    (label, h, gates) device results of the same inputs, judged the same way."""
     w = gw.w
+    also = tuple((label, _host(h).reshape(w.tokens, w.hc, w.dim), g.cpu().numpy())
+                 for label, h, g in also)
     rid, _ = oracle_rows(gw)
     h_in = gw.dense_np["h"].reshape(w.tokens, w.hc, w.dim)
     return check_forward_chunks(
@@ -527,7 +530,8 @@ def _check_forward(gw, h_out_dev, gates_dev, tokens, kv_dev=None, wkv=None, mx=F
         k_w=gw.dense_np["k_w"], h_in=h_in,
         h_out=_host(h_out_dev).reshape(w.tokens, w.hc, w.dim), gates=gates_dev.cpu().numpy(),
         kv=None if kv_dev is None else _host(kv_dev).reshape(w.tokens, -1), hc=w.hc,
-        dim=w.dim, eps=w.eps, clamp=w.gate_clamp, bf16=not gw.f32, mx=mx, name=w.name)
+        dim=w.dim, eps=w.eps, clamp=w.gate_clamp, bf16=not gw.f32, mx=mx, name=w.name,
+        also=also)
 
 
 def _run_stages(gw):
@@ -722,20 +726,48 @@ def _sample_tokens(gw, n_random, seed):
     return np.array(sorted(pick))
 
 
+def _run_sums_stages(gw, h):
+    """engram_hash -> engram_gather -> engram_fold_gate_weights ->
+    engram_project_gate_sums -> engram_gate_sums: the launches engram_forward
+    makes when its projection fills the CUs with whole tiles; h in place."""
+    w = gw.w
+    T, S = w.tokens, w.segments
+    rows = torch.empty((T, S), dtype=torch.int64, device=DEV)
+    E.engram_hash(gw.params, gw.ids, w.batch, w.seq, gw.hist_in, None, rows)
+    e = torch.empty((T, S * w.row_dim), dtype=torch.bfloat16, device=DEV)
+    E.engram_gather(gw.table, gw.rows, gw.row_format, w.row_dim, rows, T * S, e)
+    del rows
+    qk = torch.empty((w.hc, w.dim), dtype=torch.float32, device=DEV)
+    E.engram_fold_gate_weights(gw.q_w, gw.k_w, w.hc, w.dim, qk)
+    kv = torch.empty((T, (w.hc + 1) * w.dim), dtype=torch.bfloat16, device=DEV)
+    E.engram_project_gate_sums(gw.desc, e, S * w.row_dim, gw.wkv, h, qk, kv)
+    gates = torch.empty((T, w.hc), dtype=torch.float32, device=DEV)
+    E.engram_gate_sums(gw.desc, gw.ids, w.raw_vocab, kv, h, gates)
+    torch.cuda.synchronize()
+    return gates
+
+
 def test_forward_c3_every_token():
+    """C3's projection fills the CUs with whole tiles, so engram_forward takes
+    the key side of the gate into the projection's epilogue; the separate
+    stages (projection, then the gate on the stored keys) are the other path.
+    Both are judged against one oracle pass over every token, and the forward
+    equals its own stage entry points bit for bit."""
     say("C3 forward: 4x8192 tokens, 6.34 GB table, wkv [25600, 6144], h [4,8192,4,5120]")
     gw = GpuWorkload(C3)
     try:
         h0 = gw.h.clone()
+        h1 = gw.h.clone()
         rows, e, kv, gates = _run_stages(gw)
         del rows, e
-        say(f"  oracle on all {C3.tokens} tokens")
-        _check_forward(gw, gw.h, gates, np.arange(C3.tokens), kv_dev=kv)
-        del kv
-        h1 = h0
         g1 = _forward(gw, h1)
-        assert torch.equal(h1.view(torch.int16), gw.h.view(torch.int16))
-        assert torch.equal(g1, gates)
+        say(f"  oracle on all {C3.tokens} tokens: the stages and engram_forward")
+        _check_forward(gw, gw.h, gates, np.arange(C3.tokens), kv_dev=kv,
+                       also=(("C3 engram_forward (gate sums in the projection)", h1, g1),))
+        del kv
+        g2 = _run_sums_stages(gw, h0)
+        assert torch.equal(h0.view(torch.int16), h1.view(torch.int16))
+        assert torch.equal(g2, g1)
     finally:
         gw.free()
         _cleanup()
