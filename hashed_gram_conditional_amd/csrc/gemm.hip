@@ -20,7 +20,7 @@
 // (one b128 read phase) then touch 16 distinct bank groups, and so do the
 // stores of two consecutive rows.
 //
-// Two kernels, both over 256-token tiles:
+// Three kernels, all over 256-token tiles:
 //
 // gemm_bf16_kernel (256 x 256 tiles, enough tiles to fill the chip). 4 waves,
 // one per SIMD, each owning a 128 x 128 block of outputs (16 MFMA tiles, 256
@@ -33,6 +33,10 @@
 // sub-step first reads the next sub-step's fragments, so their LDS latency is
 // hidden behind 16 MFMAs. One barrier per step (LDS counter only; the loads in
 // flight stay in flight) sits before the step's last 8 MFMAs.
+//
+// gemm_bf16_sums_kernel (the same tiles, order and loop) ends a key tile by
+// forming the gate's two key-side sums per token in place of storing its keys
+// (wide_store_gate_sums in gemm_tiles.h); value tiles are stored as above.
 //
 // gemm_bf16_narrow_kernel (128 x 256 tiles, used when 256-wide tiles would
 // leave CUs idle: small token counts, decode). 8 waves (2 per SIMD), each a

@@ -96,6 +96,20 @@ __device__ __forceinline__ void wide_store_gate_sums(const f32x16 (&acc)[4][4],
   const int stream = n0 / dim;
   const int block = (n0 - stream * dim) / 128 + wn;
   const int nb = n0 + wn * 128 + fk * 4;
+  // All 64 pieces of h this lane needs are requested before any arithmetic, so
+  // the tile waits for HBM once (the registers that staged the operands are
+  // free by now); rows past M read row m0's stream (in bounds) and store nothing.
+  uint2 hv[4][4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + wm * 128 + j * 32 + frow;
+    const uint16_t *hrow = h + (int64_t)(m < M ? m : m0) * key_cols + nb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        hv[j][i][g] = *reinterpret_cast<const uint2 *>(hrow + i * 32 + g * 8);
+  }
   float4 w[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -105,13 +119,6 @@ __device__ __forceinline__ void wide_store_gate_sums(const f32x16 (&acc)[4][4],
   for (int j = 0; j < 4; ++j) {
     const int m = m0 + wm * 128 + j * 32 + frow;
     const bool ok = m < M;
-    // rows past M read row m0's stream (in bounds) and store nothing
-    const uint16_t *hrow = h + (int64_t)(ok ? m : m0) * key_cols + nb;
-    uint2 hv[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) hv[i][g] = *reinterpret_cast<const uint2 *>(hrow + i * 32 + g * 8);
     float skk = 0.f, shk = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -121,10 +128,10 @@ __device__ __forceinline__ void wide_store_gate_sums(const f32x16 (&acc)[4][4],
         const uint32_t k23 = engram::pack_bf16x2(acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]);
         const float k[4] = {__uint_as_float(k01 << 16), __uint_as_float(k01 & 0xFFFF0000u),
                             __uint_as_float(k23 << 16), __uint_as_float(k23 & 0xFFFF0000u)};
-        const float hh[4] = {__uint_as_float(hv[i][g].x << 16),
-                             __uint_as_float(hv[i][g].x & 0xFFFF0000u),
-                             __uint_as_float(hv[i][g].y << 16),
-                             __uint_as_float(hv[i][g].y & 0xFFFF0000u)};
+        const float hh[4] = {__uint_as_float(hv[j][i][g].x << 16),
+                             __uint_as_float(hv[j][i][g].x & 0xFFFF0000u),
+                             __uint_as_float(hv[j][i][g].y << 16),
+                             __uint_as_float(hv[j][i][g].y & 0xFFFF0000u)};
         const float ww[4] = {w[i][g].x, w[i][g].y, w[i][g].z, w[i][g].w};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
