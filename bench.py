@@ -567,11 +567,13 @@ def main():
 def conv_prefill_bench(gw, rows, e, kv, gates, steps: int, warmup: int):
     """The prefill layer with the papers' short convolution branch after the gate
     (4 taps at dilation 3, RMSNorm, SiLU; random filters and norm weights):
-    engram_hash -> engram_gather -> engram_project -> engram_gate_conv, the last
-    also writing the 9-position history of every sequence. The gate-and-branch
-    stage runs two kernels over the token stream; its algorithmic bytes per
-    token are those of both: h, k and v read and the gates and mean square
-    written by the first, then h read and written and v read by the second."""
+    engram_hash -> engram_gather -> engram_fold_gate_weights ->
+    engram_project_gate_sums -> engram_gate_conv_sums (engram_forward_conv's
+    launches at this size), the last also writing the 9-position history of
+    every sequence. The gate-and-branch stage runs two kernels over the token
+    stream; its algorithmic bytes per token are those of both: h, v and the key
+    sums read and the gates and mean square written by the first, then h read
+    and written, v and the statistics read by the second."""
     import torch
     import hashed_gram_conditional_amd as E
 
@@ -586,8 +588,9 @@ def conv_prefill_bench(gw, rows, e, kv, gates, steps: int, warmup: int):
     conv = E.short_conv(cw, 4, 3, 1e-6, nw, None, None, sv, ss)
     n_ws = E.engram_gate_conv_workspace_size(gw.desc)
     cws = torch.empty(n_ws, dtype=torch.uint8, device="cuda")
+    qk_w = torch.empty((w.hc, w.dim), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
 
     def step(evs):
         if evs:
@@ -598,13 +601,15 @@ def conv_prefill_bench(gw, rows, e, kv, gates, steps: int, warmup: int):
         E.engram_gather(gw.table, gw.rows, gw.row_format, w.row_dim, rows, T * S, e)
         if evs:
             evs[2].record(stream)
-        E.engram_project(e, gw.wkv, kv, T, K_in, N_out, gw.wkv_ld, 0)
+        E.engram_fold_gate_weights(gw.q_w, gw.k_w, w.hc, w.dim, qk_w)
         if evs:
             evs[3].record(stream)
-        E.engram_gate_conv(gw.desc, conv, gw.ids, w.raw_vocab, kv, gw.q_w, gw.k_w, gw.h, gates,
-                           cws, n_ws)
+        E.engram_project_gate_sums(gw.desc, e, K_in, gw.wkv, gw.h, qk_w, kv)
         if evs:
             evs[4].record(stream)
+        E.engram_gate_conv_sums(gw.desc, conv, gw.ids, w.raw_vocab, kv, gw.h, gates, cws, n_ws)
+        if evs:
+            evs[5].record(stream)
 
     for _ in range(warmup):
         step(None)
@@ -614,20 +619,22 @@ def conv_prefill_bench(gw, rows, e, kv, gates, steps: int, warmup: int):
         step(ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    st = np.mean([[s_[j].elapsed_time(s_[j + 1]) for j in range(4)] for s_ in ev], axis=0)
+    # hash, gather, fold, projection, gate and branch
+    st = np.mean([[s_[j].elapsed_time(s_[j + 1]) for j in range(5)] for s_ in ev], axis=0)
     ms = 1e3 * wall / steps
     d = w.dim
-    bytes_per_token = (2 * w.hc * d * 2 + d * 2 + (w.hc + 1) * 4) + \
-                      (w.hc * d * 2 + (w.hc + 1) * d * 2 + (w.hc + 1) * 4)
-    gbps = bytes_per_token * T / (st[3] * 1e-3) / 1e9
-    del cws, sv, ss, cw, nw
+    bytes_per_token = (w.hc * d * 2 + d * 2 + w.hc * (d // 128) * 8 + (w.hc + 1) * 4) + \
+                      (2 * w.hc * d * 2 + d * 2 + (w.hc + 1) * 4)
+    gbps = bytes_per_token * T / (st[4] * 1e-3) / 1e9
+    del cws, sv, ss, cw, nw, qk_w
     return {"workload": "prefill layer forward as above with the short convolution branch "
                         "(4 taps, dilation 3) and its history written",
             "tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
             "stages_ms": {"hash": round(st[0], 4), "gather": round(st[1], 4),
-                          "project": round(st[2], 4), "gate_conv": round(st[3], 4)},
-            "gate_conv": {"kernels": "gate_kernel (gates, mean(v^2)) + short_conv_kernel + "
-                                     "conv_state_kernel",
+                          "fold": round(st[2], 4), "project_gate_sums": round(st[3], 4),
+                          "gate_conv_sums": round(st[4], 4)},
+            "gate_conv": {"kernels": "gate_sums_kernel (gates, mean(v^2)) + "
+                                     "short_conv_window_kernel + conv_state_kernel",
                           "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                           "frac": round(gbps / HBM_PEAK_GBPS, 4),
                           "bytes_per_token": bytes_per_token}}

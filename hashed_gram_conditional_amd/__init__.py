@@ -14,7 +14,7 @@ from ._binding import (  # noqa: F401
     engram_hash_layers, engram_gather,
     engram_project, engram_project_workspace_size, engram_gate, engram_fold_gate_weights,
     engram_gate_folded, engram_project_gate_sums, engram_gate_sums,
-    engram_project_mx_gate_sums, engram_forward_workspace_size,
+    engram_project_mx_gate_sums, engram_gate_conv_sums, engram_forward_workspace_size,
     engram_forward, engram_forward_static, engram_forward_static_max_bytes, engram_transpose,
     engram_wkv_row_stride,
     engram_gather_rows, engram_gather_mx, engram_project_mx, engram_project_mx_workspace_size,

@@ -128,6 +128,7 @@ def _load():
         "engram_project_gate_sums": (ctypes.c_int, [P, P, I64, P, P, P, P, P]),
         "engram_gate_sums": (ctypes.c_int, [P, P, I32, P, P, P, P]),
         "engram_project_mx_gate_sums": (ctypes.c_int, [P, P, P, I32, P, P, P, P, P, P]),
+        "engram_gate_conv_sums": (ctypes.c_int, [P, P, P, I32, P, P, P, P, SZ, P]),
         "engram_forward_workspace_size": (SZ, [P, P]),
         "engram_gather_rows": (ctypes.c_int, [P, I64, P, I64, P, P]),
         "engram_project_mx": (ctypes.c_int, [P, P, I32, P, P, P, I64, I64, P, SZ, P]),
@@ -332,6 +333,14 @@ def engram_project_mx_gate_sums(desc: ForwardDesc, e_codes, e_scales, segments: 
                                            segments, _ptr(w_codes), _ptr(w_scales), _ptr(h),
                                            _ptr(qk_w), _ptr(kv), _stream(stream)),
            "engram_project_mx_gate_sums")
+
+
+def engram_gate_conv_sums(desc: ForwardDesc, conv: ShortConv, ids, raw_vocab: int, kv, h,
+                          gate_out, workspace, workspace_bytes: int, stream=None):
+    """engram_gate_conv from engram_project_gate_sums' kv."""
+    _check(LIB.engram_gate_conv_sums(ctypes.byref(desc), ctypes.byref(conv), _ptr(ids), raw_vocab,
+                                     _ptr(kv), _ptr(h), _ptr(gate_out), _ptr(workspace),
+                                     workspace_bytes, _stream(stream)), "engram_gate_conv_sums")
 
 
 def engram_gate_sums(desc: ForwardDesc, ids, raw_vocab: int, kv, h, gate_out, stream=None):

@@ -238,9 +238,10 @@ hipError_t engram_launch_gate(bool f32, const int32_t *ids, EngramDeadRule dead_
 
 // The gate and residual update from the sums engram_launch_gemm_bf16_sums left
 // in kv's key columns, the value row of kv and h (bf16; dim a multiple of 256).
+// stats != NULL: engram_launch_gate's statistics mode on the sums instead.
 hipError_t engram_launch_gate_sums(const int32_t *ids, EngramDeadRule dead_rule, const void *kv,
-                                   void *h, float *gate_out, int64_t tokens, int32_t hc,
-                                   int32_t dim, float eps, float clamp, int plain,
+                                   void *h, float *gate_out, float *stats, int64_t tokens,
+                                   int32_t hc, int32_t dim, float eps, float clamp, int plain,
                                    hipStream_t stream);
 
 // qk_w[i] = q_w[i] * k_w[i] over hc * dim fp32 values (dim a multiple of 8).

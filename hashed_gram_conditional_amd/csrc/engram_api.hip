@@ -640,9 +640,41 @@ int engram_gate_sums(const engram_forward_desc *desc, const int32_t *ids, int32_
   if (!aligned(ids, 4) || !aligned(kv, 16) || !aligned(h, 16) || !aligned(gate_out, 4))
     return ENGRAM_EINVAL;
   if (ntok > INT32_MAX) return ENGRAM_ESHAPE;
-  return hip_status(engram_launch_gate_sums(ids, raw_id_rule(raw_vocab), kv, h, gate_out, ntok,
-                                            desc->hc, desc->dim, desc->eps, desc->gate_clamp,
-                                            desc->gate_mode, stream));
+  return hip_status(engram_launch_gate_sums(ids, raw_id_rule(raw_vocab), kv, h, gate_out, nullptr,
+                                            ntok, desc->hc, desc->dim, desc->eps,
+                                            desc->gate_clamp, desc->gate_mode, stream));
+}
+
+int engram_gate_conv_sums(const engram_forward_desc *desc, const engram_short_conv *conv,
+                          const int32_t *ids, int32_t raw_vocab, const void *kv, void *h,
+                          float *gate_out, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  int rc = check_desc(desc);
+  if (rc != ENGRAM_OK) return rc;
+  rc = check_conv(conv);
+  if (rc != ENGRAM_OK) return rc;
+  if (raw_vocab < 1 || desc->row_format != ENGRAM_ROW_E4M3_E8M0_264) return ENGRAM_EINVAL;
+  if (desc->dim % 256 != 0) return ENGRAM_ESHAPE;
+  const int64_t ntok = desc->batch * desc->seq;
+  if (ntok > INT32_MAX) return ENGRAM_ESHAPE;
+  if (ntok > 0) {
+    if (ids == nullptr || kv == nullptr || h == nullptr) return ENGRAM_EINVAL;
+    if (!aligned(ids, 4) || !aligned(kv, 16) || !aligned(h, 16) || !aligned(gate_out, 4))
+      return ENGRAM_EINVAL;
+    if (workspace == nullptr || workspace_bytes < gate_conv_workspace(desc) ||
+        !aligned(workspace, 256))
+      return ENGRAM_EWORKSPACE;
+  }
+  float *stats = (float *)workspace;
+  if (ntok > 0) {
+    const hipError_t err = engram_launch_gate_sums(ids, raw_id_rule(raw_vocab), kv, h, gate_out,
+                                                   stats, ntok, desc->hc, desc->dim, desc->eps,
+                                                   desc->gate_clamp, desc->gate_mode, stream);
+    if (err != hipSuccess) return hip_status(err);
+  }
+  return hip_status(engram_launch_short_conv(false, make_conv_args(conv), ids,
+                                             raw_id_rule(raw_vocab), kv, stats, h, desc->batch,
+                                             desc->seq, desc->hc, desc->dim, stream));
 }
 
 int engram_transpose(const void *src, void *dst, int64_t rows, int64_t cols, int64_t dst_ld,
@@ -810,9 +842,10 @@ int forward_impl(const engram_hash_params *params, const engram_forward_desc *de
                                         ntok * S, (uint16_t *)e, host, stream);
   if (err != hipSuccess) return hip_status(err);
   // Calls that fill the CUs with whole 256 x 256 tiles take the key side of the
-  // gate into the projection's epilogue: the keys never reach HBM.
+  // gate into the projection's epilogue: the keys never reach HBM. With the
+  // convolution branch the gate then leaves its statistics to the branch.
   bool sums = false;
-  if (!f32 && conv == nullptr && desc->dim % 256 == 0) {
+  if (!f32 && desc->dim % 256 == 0) {
     err = engram_gemm_bf16_whole_tiles(ntok, out_dim, in_dim, &sums);
     if (err != hipSuccess) return hip_status(err);
   }
@@ -823,10 +856,13 @@ int forward_impl(const engram_hash_params *params, const engram_forward_desc *de
                                          (const uint16_t *)h, qk_w, (uint16_t *)kv, ntok,
                                          desc->hc, desc->dim, in_dim, stream);
     if (err == hipSuccess)
-      err = engram_launch_gate_sums(ids, hash_rule(params), kv, h, gate_out, ntok, desc->hc,
-                                    desc->dim, desc->eps, desc->gate_clamp, desc->gate_mode,
-                                    stream);
-    return hip_status(err);
+      err = engram_launch_gate_sums(ids, hash_rule(params), kv, h, gate_out,
+                                    conv != nullptr ? stats : nullptr, ntok, desc->hc, desc->dim,
+                                    desc->eps, desc->gate_clamp, desc->gate_mode, stream);
+    if (err != hipSuccess || conv == nullptr) return hip_status(err);
+    return hip_status(engram_launch_short_conv(false, make_conv_args(conv), ids, hash_rule(params),
+                                               kv, stats, h, desc->batch, desc->seq, desc->hc,
+                                               desc->dim, stream));
   }
   err = f32 ? engram_launch_gemm_f32((const float *)e, (const float *)wkv, ldw, (float *)kv,
                                      ntok, out_dim, in_dim, stream)
@@ -954,9 +990,9 @@ int engram_forward_mx(const engram_hash_params *params, const engram_forward_des
                                        e_codes, e_scales, S, (const uint16_t *)h, qk_w, kv, ntok,
                                        desc->hc, desc->dim, stream);
     if (err == hipSuccess)
-      err = engram_launch_gate_sums(ids, hash_rule(params), kv, h, gate_out, ntok, desc->hc,
-                                    desc->dim, desc->eps, desc->gate_clamp, desc->gate_mode,
-                                    stream);
+      err = engram_launch_gate_sums(ids, hash_rule(params), kv, h, gate_out, nullptr, ntok,
+                                    desc->hc, desc->dim, desc->eps, desc->gate_clamp,
+                                    desc->gate_mode, stream);
     return hip_status(err);
   }
   err = engram_launch_gemm_mx((const uint8_t *)w_codes, (const uint8_t *)w_scales, e_codes,

@@ -31,7 +31,8 @@
 // side of the gate in its epilogue (the pages' "上下文门控 + 单次 GEMM 融合" in
 // "条件记忆：DeepSeek V4.1 Engram 如何用 O(1) 查表换掉一层计算" §2.3): it reads
 // each token's sums of k^2 and h q_w k_w k per 128-column block instead of
-// the keys, 91 KB per token at hc 4 x 5120 against 133 KB.
+// the keys: 93 KB per token at hc 4 x 5120 against 133 KB (52 KB against
+// 92 KB in the statistics mode).
 #include "common.h"
 
 namespace {
@@ -352,18 +353,21 @@ namespace {
 // (engram::gate_sums_pairs): per stream, sum h^2 from h, which is read for
 // the update anyway, and the sums of its dim / 128 column blocks, added in
 // block order within each wave and then over the waves. The value row and h
-// are read, h is written, as in gate_kernel; the keys are never read.
+// are read, h is written, as in gate_kernel; the keys are never read. With a
+// stats buffer it is gate_kernel's statistics mode on the sums: gates and the
+// value row's mean square per token, h only read.
 template <int CPT>
 __global__ __launch_bounds__(kMaxThreads) void gate_sums_kernel(
     const int32_t *__restrict__ ids, EngramDeadRule dead_rule, const uint16_t *__restrict__ kv,
-    void *__restrict__ h, float *__restrict__ gate_out, int hc, int dim, float eps, float clamp,
-    int plain) {
-  __shared__ float red[kMaxThreads / engram::kWave][kMaxHc][3];
+    void *__restrict__ h, float *__restrict__ gate_out, float *__restrict__ stats, int hc,
+    int dim, float eps, float clamp, int plain) {
+  __shared__ float red[kMaxThreads / engram::kWave][kMaxHc + 1][3];
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x;
   const int nthreads = blockDim.x;
   if (engram_dead(dead_rule, ids[t])) {   // DEAD: gate 0, streams untouched
     if (gate_out != nullptr && tid < hc) gate_out[t * hc + tid] = 0.f;
+    if (stats != nullptr && tid <= hc) stats[t * (hc + 1) + tid] = 0.f;
     return;
   }
   const int cps = dim / kChunk;
@@ -382,6 +386,19 @@ __global__ __launch_bounds__(kMaxThreads) void gate_sums_kernel(
   for (int c = 0; c < CPT; ++c) {
     const int ci = tid + c * nthreads;
     if (ci < cps) vv[c].load_nt(kv, kv_row + (int64_t)hc * cps + ci);
+  }
+  if (stats != nullptr) {
+    float svv = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ci = tid + c * nthreads;
+      if (ci < cps) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) svv = fmaf(vv[c][e], vv[c][e], svv);
+      }
+    }
+    svv = engram::warp_sum(svv);
+    if (lane == 0) red[wave][kMaxHc][0] = svv;
   }
 #pragma unroll
   for (int m = 0; m < kMaxHc; ++m) {
@@ -422,7 +439,11 @@ __global__ __launch_bounds__(kMaxThreads) void gate_sums_kernel(
     const float sc = c2 * rh * rk * inv_sqrt_d;
     const float z = plain ? sc : copysignf(sqrtf(fmaxf(fabsf(sc), clamp)), sc);
     const float alpha = 1.0f / (1.0f + expf(-z));
-    if (tid == 0 && gate_out != nullptr) gate_out[t * hc + m] = alpha;
+    if (tid == 0) {
+      if (gate_out != nullptr) gate_out[t * hc + m] = alpha;
+      if (stats != nullptr) stats[t * (hc + 1) + m] = alpha;
+    }
+    if (stats != nullptr) continue;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int ci = tid + c * nthreads;
@@ -434,13 +455,19 @@ __global__ __launch_bounds__(kMaxThreads) void gate_sums_kernel(
       }
     }
   }
+  if (stats != nullptr && tid == 0) {
+    // the value row's partial sums were published before the first barrier
+    float svv = 0.f;
+    for (int w = 0; w < nwaves; ++w) svv += red[w][kMaxHc][0];
+    stats[t * (hc + 1) + hc] = svv * inv_d;
+  }
 }
 
 }  // namespace
 
 hipError_t engram_launch_gate_sums(const int32_t *ids, EngramDeadRule dead_rule, const void *kv,
-                                   void *h, float *gate_out, int64_t tokens, int32_t hc,
-                                   int32_t dim, float eps, float clamp, int plain,
+                                   void *h, float *gate_out, float *stats, int64_t tokens,
+                                   int32_t hc, int32_t dim, float eps, float clamp, int plain,
                                    hipStream_t stream) {
   if (tokens <= 0) return hipSuccess;
   int threads = 0, cpt = 0;
@@ -449,8 +476,8 @@ hipError_t engram_launch_gate_sums(const int32_t *ids, EngramDeadRule dead_rule,
   if (err != hipSuccess) return err;
 #define ENGRAM_GATE_SUMS_CASE(N)                                                              \
   hipLaunchKernelGGL((gate_sums_kernel<N>), dim3((unsigned)tokens), dim3(threads), 0, stream,  \
-                     ids, dead_rule, (const uint16_t *)kv, h, gate_out, hc, dim, eps, clamp,  \
-                     plain)
+                     ids, dead_rule, (const uint16_t *)kv, h, gate_out, stats, hc, dim, eps,  \
+                     clamp, plain)
   switch (cpt) {
     case 1: ENGRAM_GATE_SUMS_CASE(1); break;
     case 2: ENGRAM_GATE_SUMS_CASE(2); break;

@@ -469,8 +469,9 @@ int engram_gate_folded(const engram_forward_desc *desc, const int32_t *ids, int3
  * projection forms them per 128-column block while the keys are still in
  * registers, and no key is written to memory. engram_forward takes this path
  * whenever the projection fills the CUs with whole 256 x 256 tiles (bf16 rows,
- * dim % 256 == 0, no convolution branch); these two entry points are its
- * launches, for tests and timing.
+ * dim % 256 == 0); these two entry points are its launches, for tests and
+ * timing (engram_forward_conv: engram_gate_conv_sums in place of
+ * engram_gate_sums).
  *
  * engram_project_gate_sums: kv = e W over 256 x 256 tiles, whatever the token
  * count.
@@ -503,6 +504,20 @@ int engram_project_gate_sums(const engram_forward_desc *desc, const void *e, int
                              hipStream_t stream);
 int engram_gate_sums(const engram_forward_desc *desc, const int32_t *ids, int32_t raw_vocab,
                      const void *kv, void *h, float *gate_out, hipStream_t stream);
+
+/*
+ * engram_gate_conv from the sums of engram_project_gate_sums: the gate's
+ * statistics (gates and the value row's mean square per token) from the sums,
+ * the value columns of kv and h, then the short convolution branch as in
+ * engram_gate_conv. engram_forward_conv takes this path under the rule of
+ * engram_forward. Arguments and errors as engram_gate_conv without q_w and k_w
+ * (they are inside the sums), bf16 rows and dim % 256 == 0 only
+ * (ENGRAM_EINVAL, ENGRAM_ESHAPE).
+ */
+int engram_gate_conv_sums(const engram_forward_desc *desc, const engram_short_conv *conv,
+                          const int32_t *ids, int32_t raw_vocab, const void *kv, void *h,
+                          float *gate_out, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream);
 
 /*
  * engram_project_gate_sums for the block-scaled FP8 weight: engram_project_mx's

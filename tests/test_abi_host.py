@@ -311,9 +311,9 @@ def test_fold_and_folded_gate_validation():
 
 @host_only
 def test_gate_sums_validation():
-    """engram_project_gate_sums / engram_project_mx_gate_sums / engram_gate_sums:
-    bf16 rows and dim % 256 only, the projections' shape rules, every pointer
-    present and aligned."""
+    """engram_project_gate_sums / engram_project_mx_gate_sums / engram_gate_sums /
+    engram_gate_conv_sums: bf16 rows and dim % 256 only, the projections' shape
+    rules, every pointer present and aligned, the convolution's workspace."""
     L = E.LIB
     bf16 = E.ROW_E4M3_E8M0_264
     d = E.forward_desc(2, 300, 4, 512, 100, bf16, 256, wkv_ld=1032)
@@ -354,6 +354,20 @@ def test_gate_sums_validation():
         assert pm(d, **{name: None}) == E.EINVAL, name
         assert pm(d, **{name: bad}) == E.EINVAL, name
     assert pm(E.forward_desc(0, 300, 4, 512, 100, bf16, 256), ec=None) == E.OK
+    conv = E.short_conv(0x8000, 4, 3, 1e-6)
+    ws_need = E.engram_gate_conv_workspace_size(d)
+    gc = lambda desc, ids=0x1000, kv=0x2000, h=0x3000, g=None, ws=0x10000, n=ws_need, cv=conv: \
+        L.engram_gate_conv_sums(ctypes.byref(desc), ctypes.byref(cv), ids, 100, kv, h, g, ws, n,
+                                None)
+    assert gc(E.forward_desc(2, 300, 4, 320, 100, bf16, 256)) == E.ESHAPE
+    assert gc(E.forward_desc(2, 300, 4, 512, 100, E.ROW_F32, 32)) == E.EINVAL
+    for kw in ({"ids": None}, {"kv": None}, {"h": None}, {"kv": 0x2008}, {"g": 0x4002}):
+        assert gc(d, **kw) == E.EINVAL, kw
+    assert gc(d, ws=None) == E.EWORKSPACE
+    assert gc(d, n=ws_need - 1) == E.EWORKSPACE
+    assert gc(d, ws=0x10010) == E.EWORKSPACE
+    bad_conv = E.short_conv(0x8000, 9, 3, 1e-6)
+    assert gc(d, cv=bad_conv) == E.ESHAPE
 
 
 def test_forward_static_refuses_calls_beyond_its_array():

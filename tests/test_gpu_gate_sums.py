@@ -329,3 +329,140 @@ def test_forward_mx_takes_the_gate_sums_path():
             assert torch.equal(g_f, g_s)
     finally:
         gw.free()
+
+
+def _sums_kv(rng, T, hc, dim, h_bits, k_bits, v_bits, q_w, k_w):
+    """kv rows as engram_project_gate_sums leaves them, formed on the host from
+    bf16 keys (fp64 sums stored as fp32) and bf16 values."""
+    kf = O.bf16_bits_to_f64(k_bits).reshape(T, hc, dim)
+    hf = O.bf16_bits_to_f64(h_bits).reshape(T, hc, dim)
+    wf = (q_w * k_w).astype(np.float64)
+    blocks = dim // 128
+    pairs = np.stack([(kf * kf).reshape(T, hc, blocks, 128).sum(-1),
+                      (hf * wf[None] * kf).reshape(T, hc, blocks, 128).sum(-1)], -1)
+    pairs = pairs.astype(np.float32)
+    kv = np.zeros((T, (hc + 1) * dim), dtype=np.uint16)
+    kv[:, hc * dim:] = v_bits.reshape(T, dim)
+    kv.view(np.uint8).reshape(T, -1)[:, :pairs[0].nbytes] = pairs.reshape(T, -1).view(np.uint8)
+    return kv
+
+
+@pytest.mark.parametrize("B,T,hc,dim,mode", [
+    (2, 300, 4, 5120, E.GATE_SIGNED_SQRT),
+    (3, 40, 2, 256, E.GATE_PLAIN),
+    (1, 333, 1, 1024, E.GATE_SIGNED_SQRT),
+])
+def test_gate_conv_sums_against_the_oracle(B, T, hc, dim, mode):
+    """engram_gate_conv_sums (the statistics from the sums, then the short
+    convolution branch) on sums formed on the host from bf16 keys: the oracle's
+    gate_conv on those keys, values and streams, DEAD positions untouched, and
+    the history the branch leaves for the next chunk."""
+    say(f"gate_conv_sums B={B} T={T} hc={hc} dim={dim} mode={mode}")
+    rng = np.random.default_rng(B * T + dim)
+    n = B * T
+    h = _bf16(rng, (n, hc, dim))
+    mix = rng.uniform(-1, 1, (n, hc, 1))
+    k = O.round_to_bf16_bits(O.bf16_bits_to_f64(_bf16(rng, (n, hc, dim))) * 0.3 +
+                             mix * O.bf16_bits_to_f64(h))
+    v = _bf16(rng, (n, dim))
+    q_w = rng.uniform(0.5, 1.5, (hc, dim)).astype(np.float32)
+    k_w = rng.uniform(0.5, 1.5, (hc, dim)).astype(np.float32)
+    cw = (0.5 * rng.standard_normal((hc, dim, 4))).astype(np.float32)
+    nw = (1 + 0.2 * rng.standard_normal((hc, dim))).astype(np.float32)
+    ids = rng.integers(0, 1000, n).astype(np.int32)
+    ids[::11] = -1
+    dead = ids < 0
+    kv = _sums_kv(rng, n, hc, dim, h, k, v, q_w, k_w)
+    desc = E.forward_desc(B, T, hc, dim, 0, E.ROW_E4M3_E8M0_264, 256, 1e-6, 1e-6,
+                          gate_mode=mode)
+    nb = E.engram_gate_conv_workspace_size(desc)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=DEV)
+    sv = torch.empty((B, 9, dim), dtype=torch.bfloat16, device=DEV)
+    ss = torch.empty((B, 9, hc + 1), dtype=torch.float32, device=DEV)
+    cw_d, nw_d = to_device(cw), to_device(nw)
+    conv = E.short_conv(cw_d, 4, 3, 1e-6, nw_d, None, None, sv, ss)
+    h_dev = to_device(h.reshape(n, -1))
+    g_dev = torch.full((n, hc), -1.0, dtype=torch.float32, device=DEV)
+    E.engram_gate_conv_sums(desc, conv, to_device(ids), 1000, to_device(kv), h_dev, g_dev, ws, nb)
+    torch.cuda.synchronize()
+    hf = O.bf16_bits_to_f64(h).reshape(B, T, hc, dim)
+    al, ho, tail = O.gate_conv(hf, O.bf16_bits_to_f64(k).reshape(B, T, hc, dim),
+                               O.bf16_bits_to_f64(v).reshape(B, T, dim), q_w, k_w,
+                               dead.reshape(B, T), 1e-6, 1e-6, cw, nw, 3, 1e-6,
+                               mode="plain" if mode == E.GATE_PLAIN else "signed_sqrt")
+    g = g_dev.cpu().numpy().reshape(B, T, hc)
+    assert_close(g, al, "gates")
+    assert np.all(g.reshape(n, hc)[dead] == 0.0)
+    got_h = bf16_bits(h_dev).reshape(n, hc, dim)
+    assert np.array_equal(got_h[dead], h[dead])
+    assert_close(O.bf16_bits_to_f64(got_h).reshape(B, T, hc, dim),
+                 O.bf16_bits_to_f64(O.round_to_bf16_bits(ho)), "h")
+    # the history: the last 9 value rows and their gates (the gated values factored)
+    vt_tail = np.asarray(tail)                       # [B, 9, hc, dim] gated values
+    ssn = ss.cpu().numpy()
+    svn = O.bf16_bits_to_f64(bf16_bits(sv))
+    assert_close(ssn[..., :hc, None] * svn[:, :, None, :], vt_tail, "history (gated values)")
+
+
+def test_forward_conv_takes_the_gate_sums_path():
+    """engram_forward_conv on S_C: the bits of its stage entry points on the
+    sums path (fold, engram_project_gate_sums, engram_gate_conv_sums) when its
+    projection fills the CUs with whole tiles, and close to the separate stages
+    (engram_project + engram_gate_conv, checked against the oracle in
+    test_gpu_conv.py): gates within 1e-4, streams within one bf16 step (where
+    the two gates' last bits flip a rounding) or 1e-3."""
+    w = S_C
+    tiles = -(-w.tokens // 256) * ((w.hc + 1) * w.dim // 256)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    gw = GpuWorkload(w)
+    try:
+        T, S = w.tokens, w.segments
+        K, N = S * 256, (w.hc + 1) * w.dim
+        g = torch.Generator(device="cpu").manual_seed(8)
+        cw = (0.5 * torch.randn((w.hc, w.dim, 4), generator=g)).to(DEV)
+        nw = (1 + 0.2 * torch.randn((w.hc, w.dim), generator=g)).to(DEV)
+        nb = E.engram_gate_conv_workspace_size(gw.desc)
+        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=DEV)
+        nf = E.engram_forward_conv_workspace_size(gw.params, gw.desc)
+        wsf = torch.empty(nf, dtype=torch.uint8, device=DEV)
+        outs = {}
+        for path in ("forward", "sums", "separate"):
+            h = gw.h.clone()
+            gt = torch.empty((T, w.hc), dtype=torch.float32, device=DEV)
+            sv = torch.empty((w.batch, 9, w.dim), dtype=torch.bfloat16, device=DEV)
+            ss = torch.empty((w.batch, 9, w.hc + 1), dtype=torch.float32, device=DEV)
+            conv = E.short_conv(cw, 4, 3, 1e-6, nw, None, None, sv, ss)
+            if path == "forward":
+                E.engram_forward_conv(gw.params, gw.desc, conv, gw.ids, None, None, gw.table,
+                                      gw.wkv, gw.q_w, gw.k_w, h, gt, wsf, nf)
+            else:
+                rows = torch.empty((T, S), dtype=torch.int64, device=DEV)
+                E.engram_hash(gw.params, gw.ids, w.batch, w.seq, None, None, rows)
+                e = torch.empty((T, K), dtype=torch.bfloat16, device=DEV)
+                E.engram_gather(gw.table, gw.rows, gw.row_format, 256, rows, T * S, e)
+                kv = torch.empty((T, N), dtype=torch.bfloat16, device=DEV)
+                if path == "sums":
+                    qk = torch.empty((w.hc, w.dim), dtype=torch.float32, device=DEV)
+                    E.engram_fold_gate_weights(gw.q_w, gw.k_w, w.hc, w.dim, qk)
+                    E.engram_project_gate_sums(gw.desc, e, K, gw.wkv, h, qk, kv)
+                    E.engram_gate_conv_sums(gw.desc, conv, gw.ids, w.raw_vocab, kv, h, gt, ws,
+                                            nb)
+                else:
+                    E.engram_project(e, gw.wkv, kv, T, K, N, gw.wkv_ld, 0)
+                    E.engram_gate_conv(gw.desc, conv, gw.ids, w.raw_vocab, kv, gw.q_w, gw.k_w,
+                                       h, gt, ws, nb)
+            torch.cuda.synchronize()
+            outs[path] = (h, gt, sv, ss)
+        hf, gf, svf, ssf = outs["forward"]
+        if tiles >= cus:
+            hs, gs, svs, sss = outs["sums"]
+            assert torch.equal(hf.view(torch.int16), hs.view(torch.int16))
+            assert torch.equal(gf, gs) and torch.equal(ssf, sss)
+            assert torch.equal(svf.view(torch.int16), svs.view(torch.int16))
+        hp, gp, _, _ = outs["separate"]
+        ga, gb = gp.cpu().numpy().astype(np.float64), gf.cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(ga - gb) <= 1e-4)
+        assert_close(O.bf16_bits_to_f64(bf16_bits(hf)), O.bf16_bits_to_f64(bf16_bits(hp)),
+                     "h: forward_conv against the separate stages", atol=1e-3, rtol=2.0 ** -7)
+    finally:
+        gw.free()
