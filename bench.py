@@ -1008,14 +1008,16 @@ def decode_bench(steps: int, warmup: int, wkv_ld=None):
         E.engram_forward(gw.params, gw.desc, gw.ids, hist, hist, gw.table, gw.wkv, gw.q_w,
                          gw.k_w, gw.h, gates, ws, nws)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    # Two events around the whole run: an event recorded between two launches
+    # leaves the GPU idle for about 6 us on this stack, 5 % of a decode step.
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record(stream)
     for i in range(steps):
         E.engram_forward(gw.params, gw.desc, gw.ids, hist, hist, gw.table, gw.wkv, gw.q_w,
                          gw.k_w, gw.h, gates, ws, nws)
-        ev[i + 1].record(stream)
+    ev[1].record(stream)
     torch.cuda.synchronize()
-    ms = ev[0].elapsed_time(ev[steps]) / steps
+    ms = ev[0].elapsed_time(ev[1]) / steps
     # the same step captured once in a HIP graph and replayed (no launch gaps
     # between its kernels; the history advances in place on every replay)
     graph = torch.cuda.CUDAGraph()
@@ -1041,19 +1043,26 @@ def decode_bench(steps: int, warmup: int, wkv_ld=None):
     kv = torch.empty((T, N_out), dtype=torch.bfloat16, device="cuda")
     pws_n = E.engram_project_workspace_size(T, K_in, N_out, 0)
     pws = torch.empty(max(pws_n, 1), dtype=torch.uint8, device="cuda")
-    se = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
-    for i in range(steps):
-        se[i][0].record(stream)
-        E.engram_hash(gw.params, gw.ids, w.batch, w.seq, hist, None, rows)
-        se[i][1].record(stream)
-        E.engram_gather(gw.table, gw.rows, gw.row_format, w.row_dim, rows, T * S, e)
-        se[i][2].record(stream)
-        E.engram_project(e, gw.wkv, kv, T, K_in, N_out, gw.wkv_ld, 0, pws, pws_n)
-        se[i][3].record(stream)
-        E.engram_gate(gw.desc, gw.ids, w.raw_vocab, kv, gw.q_w, gw.k_w, gw.h, gates)
-        se[i][4].record(stream)
-    torch.cuda.synchronize()
-    st = np.mean([[x[j].elapsed_time(x[j + 1]) for j in range(4)] for x in se], axis=0)
+    # each stage alone, `steps` back-to-back calls between two events (an event
+    # between every launch would add its idle gap to every stage)
+    def per_stage(fn):
+        for _ in range(2):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    st = [per_stage(lambda: E.engram_hash(gw.params, gw.ids, w.batch, w.seq, hist, None, rows)),
+          per_stage(lambda: E.engram_gather(gw.table, gw.rows, gw.row_format, w.row_dim, rows,
+                                            T * S, e)),
+          per_stage(lambda: E.engram_project(e, gw.wkv, kv, T, K_in, N_out, gw.wkv_ld, 0, pws,
+                                             pws_n)),
+          per_stage(lambda: E.engram_gate(gw.desc, gw.ids, w.raw_vocab, kv, gw.q_w, gw.k_w,
+                                          gw.h, gates))]
     wkv_bytes = N_out * K_in * 2
     # the same decode step with the short convolution branch: each sequence's
     # 9-position history is read and shifted in place every step
@@ -1085,6 +1094,10 @@ def decode_bench(steps: int, warmup: int, wkv_ld=None):
                             "ms_per_step": round(graph_ms, 4)},
            "stages_ms": {"hash": round(st[0], 4), "gather": round(st[1], 4),
                          "project": round(st[2], 4), "gate": round(st[3], 4)},
+           "stages_method": "each stage alone, back-to-back calls between two events; the "
+                            "hash and gather kernels (5-6 us, profiles/decode_c4_kernel_stats.md) "
+                            "are shorter than one call through the binding (about 10 us), so "
+                            "their figures are the host's issue rate",
            "project_weight_stream": {"achieved": round(wkv_bytes / (st[2] * 1e-3) / 1e9, 1),
                                      "peak": HBM_PEAK_GBPS, "unit": "GB/s"},
            "short_conv": {"workload": "the same step through engram_forward_conv (4 taps, "
