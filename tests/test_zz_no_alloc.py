@@ -148,3 +148,23 @@ def test_static_captured_in_a_graph_replays_equal_eager():
         assert torch.equal(gates, rg) and torch.equal(hout, rs), name
     del graph
     gw.free()
+
+
+def test_static_on_the_gate_sums_path():
+    """A 2,700-token call whose projection fills the CUs with whole tiles takes
+    the gate sums path in both entry points (46 MB of the array): the static
+    variant gives engram_forward's bits, then a smaller decode call on the same
+    array does too."""
+    from tests.test_gpu_gate_sums import S_C
+    say("engram_forward_static: 2,700-token call on the gate sums path, then decode")
+    gw = GpuWorkload(S_C)
+    (h0, g0, _), (h1, g1, _) = _both(gw, S_C.batch, hist=False)
+    assert torch.equal(h0.view(torch.int16), h1.view(torch.int16))
+    assert torch.equal(g0, g1)
+    assert not torch.equal(h0.view(torch.int16), gw.h.view(torch.int16))
+    gw.free()
+    gwd = GpuWorkload(DECODE)
+    (h0, g0, s0), (h1, g1, s1) = _both(gwd, 64)
+    assert torch.equal(h0.view(torch.int16), h1.view(torch.int16))
+    assert torch.equal(g0, g1) and torch.equal(s0, s1)
+    gwd.free()
