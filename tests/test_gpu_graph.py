@@ -1,5 +1,5 @@
-"""engram_forward captured in a HIP graph and replayed, and called from two host
-threads on two streams at once.
+"""engram_forward captured in a HIP graph and replayed (the skinny decode, split-K
+and gate sums paths), and called from two host threads on two streams at once.
 
 The library allocates nothing, never synchronises and records no memset, so a
 step can be captured once and replayed with new ids written into the same input
@@ -32,13 +32,18 @@ D_S = dataclasses.replace(C4, name="D_S", prime_base=1_000_000, table_seed=2002)
 # 300 tokens over few tiles: the split-K projection with its workspace and fixup
 S_A = dataclasses.replace(C3, name="S_A", seed=1100, batch=2, seq=150, prime_base=5000, hc=2,
                           dim=136, dead_random=(1, 16), table_seed=3001)
+# 2,700 tokens over 275 whole tiles: the projection with the gate's key sums,
+# the fold and the gate from the sums
+S_G = dataclasses.replace(C3, name="S_G", seed=1102, batch=3, seq=900, max_ngram=3, heads=4,
+                          prime_base=5000, hc=4, dim=1280, dead_random=(2, 20),
+                          table_seed=3003, hash_setup_seed=None)
 
 
 def _bits(t):
     return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
 
 
-@pytest.mark.parametrize("w", [D_S, S_A], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [D_S, S_A, S_G], ids=lambda w: w.name)
 def test_forward_graph_replays_equal_eager(w):
     say(f"graph {w.name}: {w.batch}x{w.seq} tokens, hc={w.hc}, d={w.dim}")
     gw = GpuWorkload(w)
