@@ -466,3 +466,54 @@ def test_forward_conv_takes_the_gate_sums_path():
                      "h: forward_conv against the separate stages", atol=1e-3, rtol=2.0 ** -7)
     finally:
         gw.free()
+
+
+def test_forward_on_a_host_table_takes_the_gate_sums_path():
+    """engram_forward with S_C's table in pinned host memory (the gather reading
+    rows over the host link) gives the bits of the HBM-resident table on the
+    gate sums path, and so does the two-stream pipeline of the benchmark's host
+    tier (hash + gather on a side stream, then fold, engram_project_gate_sums
+    and engram_gate_sums on the compute stream)."""
+    w = S_C
+    gw = GpuWorkload(w)
+    try:
+        T, S = w.tokens, w.segments
+        host = torch.empty(gw.table.shape, dtype=gw.table.dtype, pin_memory=True)
+        host.copy_(gw.table)
+        ws, n = gw.workspace()
+        outs = []
+        for table in (gw.table, host):
+            h = gw.h.clone()
+            g = torch.empty((T, w.hc), dtype=torch.float32, device=DEV)
+            E.engram_forward(gw.params, gw.desc, gw.ids, None, None, table, gw.wkv, gw.q_w,
+                             gw.k_w, h, g, ws, n)
+            torch.cuda.synchronize()
+            outs.append((h, g))
+        assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+        assert torch.equal(outs[0][1], outs[1][1])
+        side = torch.cuda.Stream()
+        main = torch.cuda.current_stream()
+        rows = torch.empty((T, S), dtype=torch.int64, device=DEV)
+        e = torch.empty((T, S * 256), dtype=torch.bfloat16, device=DEV)
+        kv = torch.empty((T, (w.hc + 1) * w.dim), dtype=torch.bfloat16, device=DEV)
+        qk = torch.empty((w.hc, w.dim), dtype=torch.float32, device=DEV)
+        h = gw.h.clone()
+        g = torch.empty((T, w.hc), dtype=torch.float32, device=DEV)
+        ready = torch.cuda.Event()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(side):
+            E.engram_hash(gw.params, gw.ids, w.batch, w.seq, None, None, rows, stream=side)
+            E.engram_gather(host, gw.rows, gw.row_format, 256, rows, T * S, e, stream=side)
+            ready.record(side)
+        E.engram_fold_gate_weights(gw.q_w, gw.k_w, w.hc, w.dim, qk, stream=main)
+        main.wait_event(ready)
+        E.engram_project_gate_sums(gw.desc, e, S * 256, gw.wkv, h, qk, kv, stream=main)
+        E.engram_gate_sums(gw.desc, gw.ids, w.raw_vocab, kv, h, g, stream=main)
+        torch.cuda.synchronize()
+        tiles = -(-T // 256) * ((w.hc + 1) * w.dim // 256)
+        if tiles >= torch.cuda.get_device_properties(0).multi_processor_count:
+            assert torch.equal(h.view(torch.int16), outs[0][0].view(torch.int16))
+            assert torch.equal(g, outs[0][1])
+        del host
+    finally:
+        gw.free()
