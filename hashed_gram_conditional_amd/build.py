@@ -9,8 +9,8 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = ["hash.hip", "gather.hip", "gemm.hip", "gemm_mx.hip", "gate.hip", "conv.hip",
-           "layout.hip", "engram_api.hip"]
+SOURCES = ["hash.hip", "gather.hip", "hash_gather.hip", "gemm.hip", "gemm_mx.hip", "gate.hip",
+           "conv.hip", "layout.hip", "engram_api.hip"]
 LIB = os.path.join(PKG, "libengram.so")
 CALIB_SOURCE = "calibrate.hip"
 CALIB_LIB = os.path.join(PKG, "libengram_calibrate.so")

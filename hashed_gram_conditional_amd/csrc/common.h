@@ -145,6 +145,16 @@ hipError_t engram_launch_hash(const EngramHashArgs &a, const int32_t *token_map,
                               const int32_t *hist_in, int32_t *hist_out,
                               int64_t *row_ids, hipStream_t stream);
 
+// Hash and gather of one Engram layer in one launch, one block per token, for
+// decode-sized calls on an HBM-resident E4M3 table: the rows (bf16, [batch *
+// seq, S * 256]) of the separate kernels, no row ids written. a.layers must be
+// 1, and hist_out NULL or seq 1 (the history committed in place).
+hipError_t engram_launch_hash_gather_e4m3(const EngramHashArgs &a, const int32_t *token_map,
+                                          const int32_t *ids, int64_t batch, int64_t seq,
+                                          const int32_t *hist_in, int32_t *hist_out,
+                                          const uint8_t *table, int64_t table_rows,
+                                          uint16_t *out, hipStream_t stream);
+
 // host_table: the table is pinned host memory; the gather then runs on a few
 // CUs as a grid-strided kernel, leaving the rest to concurrent work.
 hipError_t engram_launch_gather_e4m3(const uint8_t *table, int64_t table_rows,

@@ -235,6 +235,11 @@ EngramDeadRule hash_rule(const engram_hash_params *p) {
 // extra launch costs more than it saves.
 constexpr int64_t kFoldMinTokens = 2048;
 
+// engram_forward forms and gathers the rows in one launch (one block per token)
+// for calls of at most this many tokens; larger calls hash with several tokens
+// per block and gather with the whole grid.
+constexpr int64_t kHashGatherMaxTokens = 2048;
+
 size_t folded_scales_bytes(const engram_forward_desc *d) {
   return align256((size_t)d->hc * (size_t)d->dim * sizeof(float));
 }
@@ -825,22 +830,34 @@ int forward_impl(const engram_hash_params *params, const engram_forward_desc *de
   const size_t gemm_ws_bytes = workspace_bytes - (size_t)(gemm_ws - ws);
 
   const EngramHashArgs a = make_hash_args(params, 1);
-  hipError_t err = engram_launch_hash(a, params->token_map, ids, desc->batch, desc->seq,
-                                      hist_in, hist_out, row_ids, stream);
-  if (err != hipSuccess) return hip_status(err);
-  if (ntok == 0) {
-    // An empty chunk still passes the convolution's history on.
-    if (conv != nullptr)
-      err = engram_launch_short_conv(f32, make_conv_args(conv), ids, hash_rule(params), nullptr,
-                                     nullptr, h, desc->batch, desc->seq, desc->hc, desc->dim,
-                                     stream);
-    return hip_status(err);
+  hipError_t err = hipSuccess;
+  // Decode-sized calls on an HBM table form and gather each token's rows in one
+  // launch (the history, if any, committed in place); others hash, then gather.
+  const bool fused_rows = !f32 && !host && ntok > 0 && ntok <= kHashGatherMaxTokens &&
+                          (hist_out == nullptr || desc->seq == 1);
+  if (fused_rows) {
+    err = engram_launch_hash_gather_e4m3(a, params->token_map, ids, desc->batch, desc->seq,
+                                         hist_in, hist_out, (const uint8_t *)table,
+                                         desc->table_rows, (uint16_t *)e, stream);
+    if (err != hipSuccess) return hip_status(err);
+  } else {
+    err = engram_launch_hash(a, params->token_map, ids, desc->batch, desc->seq, hist_in,
+                             hist_out, row_ids, stream);
+    if (err != hipSuccess) return hip_status(err);
+    if (ntok == 0) {
+      // An empty chunk still passes the convolution's history on.
+      if (conv != nullptr)
+        err = engram_launch_short_conv(f32, make_conv_args(conv), ids, hash_rule(params),
+                                       nullptr, nullptr, h, desc->batch, desc->seq, desc->hc,
+                                       desc->dim, stream);
+      return hip_status(err);
+    }
+    err = f32 ? engram_launch_gather_f32((const float *)table, desc->table_rows, desc->row_dim,
+                                         row_ids, ntok * S, (float *)e, stream)
+              : engram_launch_gather_e4m3((const uint8_t *)table, desc->table_rows, row_ids,
+                                          ntok * S, (uint16_t *)e, host, stream);
+    if (err != hipSuccess) return hip_status(err);
   }
-  err = f32 ? engram_launch_gather_f32((const float *)table, desc->table_rows, desc->row_dim,
-                                       row_ids, ntok * S, (float *)e, stream)
-            : engram_launch_gather_e4m3((const uint8_t *)table, desc->table_rows, row_ids,
-                                        ntok * S, (uint16_t *)e, host, stream);
-  if (err != hipSuccess) return hip_status(err);
   // Calls that fill the CUs with whole 256 x 256 tiles take the key side of the
   // gate into the projection's epilogue: the keys never reach HBM. With the
   // convolution branch the gate then leaves its statistics to the branch.

@@ -21,7 +21,7 @@
 // exponent/mantissa position give value * 2^-120 (subnormal codes become f32
 // denormals, kept by the denormal mode), ldexp by s - 7 is exact or overflows,
 // and one nearest-even rounding to bf16 handles bf16 subnormals.
-#include "common.h"
+#include "row_device.h"
 
 namespace {
 
@@ -30,43 +30,7 @@ constexpr int kRowsPerWave = 2 * kSlots;
 constexpr int kThreads = 256;
 constexpr int kRowsPerBlock = kRowsPerWave * (kThreads / engram::kWave);
 
-__device__ __forceinline__ uint32_t dequant_byte_exact(uint32_t byte, uint32_t s) {
-  const uint32_t sign = (byte & 0x80u) << 8;
-  const uint32_t mag = byte & 0x7Fu;
-  if (mag == 0x7Fu || s == 0xFFu) return 0x7FC0u | sign;     // E4M3 NaN, E8M0 NaN
-  const float f = ldexpf(__uint_as_float(mag << 20), (int)s - 7);
-  return engram::f32_to_bf16_rne(f) | sign;
-}
-
-__device__ __forceinline__ uint32_t dequant_pair_fast(uint32_t word, float scale, bool hi) {
-  const auto f = hi ? __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true)
-                    : __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
-  const uint32_t lo32 = __float_as_uint(f[0] * scale);
-  const uint32_t hi32 = __float_as_uint(f[1] * scale);
-  return (lo32 >> 16) | (hi32 & 0xFFFF0000u);
-}
-
-__device__ __forceinline__ uint4 dequant8(uint2 q, uint32_t s) {
-  uint4 o;
-  if (s - 10u <= 236u) {
-    const float scale = __uint_as_float(s << 23);
-    o.x = dequant_pair_fast(q.x, scale, false);
-    o.y = dequant_pair_fast(q.x, scale, true);
-    o.z = dequant_pair_fast(q.y, scale, false);
-    o.w = dequant_pair_fast(q.y, scale, true);
-  } else {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t word = i < 2 ? q.x : q.y;
-      const int sh = (i & 1) * 16;
-      w[i] = dequant_byte_exact((word >> sh) & 0xFFu, s) |
-             (dequant_byte_exact((word >> (sh + 8)) & 0xFFu, s) << 16);
-    }
-    o = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-  return o;
-}
+using engram_rows::dequant8;
 
 template <int NT>
 __global__ __launch_bounds__(NT) void gather_e4m3_kernel(

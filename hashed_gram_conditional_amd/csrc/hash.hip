@@ -25,31 +25,13 @@
 // is below 1), so one conditional subtraction gives the exact remainder
 // (Barrett, "Implementing the RSA public key encryption algorithm on a standard
 // digital signal processor", CRYPTO 1986).
-#include "common.h"
+#include "row_device.h"
 
 namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ int32_t cell_value(const EngramHashArgs &a,
-                                              const int32_t *__restrict__ token_map,
-                                              const int32_t *__restrict__ row,
-                                              const int32_t *__restrict__ hist, int64_t u) {
-  // Value of the cell at chunk position u (u < 0: the history before the chunk):
-  // a compressed id, or -1 for DEAD.
-  const int H = a.max_ngram - 1;
-  if (u >= 0) {
-    const int32_t x = row[u];
-    if (x < 0 || x >= a.raw_vocab) return -1;
-    const int32_t v = token_map[x];
-    return (v >= 0 && v < a.compressed_vocab) ? v : -1;
-  }
-  if (hist != nullptr) {
-    const int32_t v = hist[H + u];
-    return (v >= 0 && v < a.compressed_vocab) ? v : -1;
-  }
-  return a.pad_id;
-}
+using engram_rows::cell_value;
 
 template <int L, int TOK>
 __global__ __launch_bounds__(kThreads) void hash_kernel(
@@ -83,17 +65,7 @@ __global__ __launch_bounds__(kThreads) void hash_kernel(
     const int32_t *hist = hist_in ? hist_in + b * H : nullptr;
     int32_t vals[ENGRAM_MAX_NGRAM];
     uint64_t cells[ENGRAM_MAX_NGRAM];
-    bool blocked = false;
-#pragma unroll
-    for (int i = 0; i < ENGRAM_MAX_NGRAM; ++i) {
-      if (i < N) {
-        const int32_t v = cell_value(a, token_map, row, hist, t - i);
-        vals[i] = v;
-        // A DEAD cell blocks itself and every older cell: they hash as the pad id.
-        blocked = blocked || (v < 0);
-        cells[i] = blocked ? (uint64_t)a.pad_id : (uint64_t)v;
-      }
-    }
+    engram_rows::token_cells(a, token_map, row, hist, t, vals, cells);
 #pragma unroll
     for (int l = 0; l < L; ++l) {
       uint64_t mix = 0;
@@ -126,11 +98,8 @@ __global__ __launch_bounds__(kThreads) void hash_kernel(
       const int lt = o / S;
       const int j = o - lt * S;
       const int js = l * S + j;
-      const uint64_t x = s_mix[l][j / a.heads][lt];
-      const uint64_t p = s_prime[js];
-      uint64_t r = x - __umul64hi(x, s_recip[js]) * p;
-      if (r >= p) r -= p;
-      out[o] = (int64_t)r + s_off[js];
+      out[o] = engram_rows::row_id(s_mix[l][j / a.heads][lt], s_prime[js], s_recip[js],
+                                   s_off[js]);
     }
   }
 }
