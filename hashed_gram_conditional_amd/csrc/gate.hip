@@ -18,10 +18,16 @@
 // need only its own h and k, so after one barrier its gate is known and its h,
 // still in registers, is updated and stored before the next stream is read. h
 // is read from HBM once (updating all streams after all reductions re-read it,
-// and the L2 had often dropped it by then). All arithmetic is fp32. With few
-// tokens (up to 4 streams, 2 chunks per thread) a token's whole h and k are
-// loaded at once and the streams share one barrier: the same arithmetic, one
-// memory round trip per token instead of one per stream.
+// and the L2 had often dropped it by then). All arithmetic is fp32.
+//
+// Few tokens (decode, up to 2 chunks per thread): gate_stream_kernel gives every
+// (token, stream) pair a block of its own, 4 per CU at 256 tokens x 4 streams,
+// so a stream's loads, its one barrier and its update overlap the other
+// streams' instead of queueing behind them in one block. Its thread count,
+// chunk ownership and reduction order are the per-token kernel's, so the bits
+// are too. The statistics mode keeps the per-token block, which loads a token's
+// whole h and k at once (up to 4 streams) and lets the streams share one
+// barrier.
 //
 // With a stats buffer the kernel is the first half of the short-convolution
 // variant: it stores each token's gates and the mean square of its value row
@@ -276,6 +282,100 @@ __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
   }
 }
 
+// One (token, stream) pair per block, blockIdx.x the token and blockIdx.y the
+// stream: gate_kernel's arithmetic for that stream (the same chunks per thread,
+// fma order, wave sums and order of the waves' partial sums), without the
+// statistics output.
+template <bool F32, int CPT>
+__global__ __launch_bounds__(kMaxThreads) void gate_stream_kernel(
+    const int32_t *__restrict__ ids, EngramDeadRule dead_rule, const void *__restrict__ kv,
+    const float *__restrict__ q_w, const float *__restrict__ k_w, void *__restrict__ h,
+    float *__restrict__ gate_out, int hc, int dim, float eps, float clamp, int plain) {
+  __shared__ float red[kMaxThreads / engram::kWave][3];
+  const int64_t t = blockIdx.x;
+  const int m = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int nthreads = blockDim.x;
+  if (engram_dead(dead_rule, ids[t])) {   // DEAD: gate 0, the stream untouched
+    if (gate_out != nullptr && tid == 0) gate_out[t * hc + m] = 0.f;
+    return;
+  }
+  const int cps = dim / kChunk;
+  const int64_t kv_row = t * (int64_t)(hc + 1) * cps;
+  const int64_t h_row = (t * (int64_t)hc + m) * cps;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int nwaves = nthreads >> 6;
+  Chunk<F32> vv[CPT], hh[CPT], kk[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int ci = tid + c * nthreads;
+    if (ci < cps) {
+      vv[c].load_nt(kv, kv_row + (int64_t)hc * cps + ci);
+      hh[c].load_nt(h, h_row + ci);
+      kk[c].load_nt(kv, kv_row + (int64_t)m * cps + ci);
+    }
+  }
+  float shh = 0.f, skk = 0.f, shk = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int ci = tid + c * nthreads;
+    if (ci < cps) {
+      // q_w * k_w of the chunk (with k_w == NULL, q_w holds the products)
+      const float4 *qp = reinterpret_cast<const float4 *>(q_w + (int64_t)m * dim) + 2 * ci;
+      const float4 q0 = qp[0], q1 = qp[1];
+      float w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+      if (k_w != nullptr) {
+        const float4 *kp = reinterpret_cast<const float4 *>(k_w + (int64_t)m * dim) + 2 * ci;
+        const float4 k0 = kp[0], k1 = kp[1];
+        w[0] *= k0.x; w[1] *= k0.y; w[2] *= k0.z; w[3] *= k0.w;
+        w[4] *= k1.x; w[5] *= k1.y; w[6] *= k1.z; w[7] *= k1.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float he = hh[c][e];
+        const float ke = kk[c][e];
+        shh = fmaf(he, he, shh);
+        skk = fmaf(ke, ke, skk);
+        shk = fmaf(he * w[e], ke, shk);
+      }
+    }
+  }
+  shh = engram::warp_sum(shh);
+  skk = engram::warp_sum(skk);
+  shk = engram::warp_sum(shk);
+  if (lane == 0) {
+    red[wave][0] = shh;
+    red[wave][1] = skk;
+    red[wave][2] = shk;
+  }
+  __syncthreads();
+  float a = 0.f, b = 0.f, c2 = 0.f;
+  for (int w = 0; w < nwaves; ++w) {
+    a += red[w][0];
+    b += red[w][1];
+    c2 += red[w][2];
+  }
+  const float inv_d = 1.0f / (float)dim;
+  const float inv_sqrt_d = 1.0f / sqrtf((float)dim);
+  const float rh = 1.0f / sqrtf(a * inv_d + eps);
+  const float rk = 1.0f / sqrtf(b * inv_d + eps);
+  const float sc = c2 * rh * rk * inv_sqrt_d;
+  const float z = plain ? sc : copysignf(sqrtf(fmaxf(fabsf(sc), clamp)), sc);
+  const float alpha = 1.0f / (1.0f + expf(-z));
+  if (tid == 0 && gate_out != nullptr) gate_out[t * hc + m] = alpha;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int ci = tid + c * nthreads;
+    if (ci < cps) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = fmaf(alpha, vv[c][e], hh[c][e]);
+      Chunk<F32>::store_nt(h, h_row + ci, o);
+    }
+  }
+}
+
 // Threads per token block for the gate kernels: 128 when there are enough
 // tokens to keep HBM busy (about 8 per CU), up to 512 below that (few); never
 // more threads than a stream has 8-element chunks, rounded up to whole waves.
@@ -294,7 +394,7 @@ hipError_t gate_threads(int64_t tokens, int dim, int &threads, int &cpt, bool &f
 }
 
 template <bool F32>
-hipError_t launch(int cpt, int threads, bool all_streams, const int32_t *ids,
+hipError_t launch(int cpt, int threads, bool few, bool all_streams, const int32_t *ids,
                   EngramDeadRule dead_rule,
                   const void *kv, const float *q_w, const float *k_w, void *h, float *gate_out,
                   float *stats, int64_t tokens, int hc, int dim, float eps, float clamp,
@@ -303,6 +403,18 @@ hipError_t launch(int cpt, int threads, bool all_streams, const int32_t *ids,
   hipLaunchKernelGGL((gate_kernel<F32, N, AS>), dim3((unsigned)tokens), dim3(threads), 0,   \
                      stream, ids, dead_rule, kv, q_w, k_w, h, gate_out, stats, hc, dim,     \
                      eps, clamp, plain)
+  if (few && stats == nullptr && cpt <= 2) {
+#define ENGRAM_GATE_STREAM_CASE(N)                                                          \
+  hipLaunchKernelGGL((gate_stream_kernel<F32, N>), dim3((unsigned)tokens, (unsigned)hc),     \
+                     dim3(threads), 0, stream, ids, dead_rule, kv, q_w, k_w, h, gate_out, hc, \
+                     dim, eps, clamp, plain)
+    if (cpt == 1)
+      ENGRAM_GATE_STREAM_CASE(1);
+    else
+      ENGRAM_GATE_STREAM_CASE(2);
+#undef ENGRAM_GATE_STREAM_CASE
+    return hipGetLastError();
+  }
   if (all_streams) {
     switch (cpt) {
       case 1: ENGRAM_GATE_CASE(1, true); break;
@@ -339,11 +451,12 @@ hipError_t engram_launch_gate(bool f32, const int32_t *ids, EngramDeadRule dead_
   bool few = false;
   const hipError_t err = gate_threads(tokens, dim, threads, cpt, few);
   if (err != hipSuccess) return err;
-  // few tokens: one memory round trip per token for up to kAllStreams streams
+  // few tokens: a block per (token, stream); with the statistics output one
+  // memory round trip per token for up to kAllStreams streams
   const bool all_streams = few && hc <= kAllStreams && cpt <= 2;
-  return f32 ? launch<true>(cpt, threads, all_streams, ids, dead_rule, kv, q_w, k_w, h,
+  return f32 ? launch<true>(cpt, threads, few, all_streams, ids, dead_rule, kv, q_w, k_w, h,
                             gate_out, stats, tokens, hc, dim, eps, clamp, plain, stream)
-             : launch<false>(cpt, threads, all_streams, ids, dead_rule, kv, q_w, k_w, h,
+             : launch<false>(cpt, threads, few, all_streams, ids, dead_rule, kv, q_w, k_w, h,
                              gate_out, stats, tokens, hc, dim, eps, clamp, plain, stream);
 }
 

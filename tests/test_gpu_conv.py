@@ -144,11 +144,15 @@ def test_gate_conv_matches_oracle(B, T, hc, d, taps, dil, f32, mode, norm):
     _check(c, h, gates, alpha, h_out, f"gate_conv {mode}")
 
 
-def test_gate_conv_zero_filters_equal_gate():
+@pytest.mark.parametrize("B,T,hc,d,f32", [(2, 40, 4, 136, False), (256, 1, 4, 5120, False),
+                                           (64, 1, 8, 5120, False), (32, 2, 4, 5120, True)],
+                         ids=["80x4x136", "decode256x4x5120", "64x8x5120", "f32_64x4x5120"])
+def test_gate_conv_zero_filters_equal_gate(B, T, hc, d, f32):
     """Filters at zero (the papers' init): the branch adds exactly the gated
-    value, so engram_gate_conv agrees with engram_gate; the gates are the same
-    bits (same reduction)."""
-    c = Case(2, 40, 4, 136, seed=7)
+    value, so engram_gate_conv agrees with engram_gate. The gates are the same
+    bits: with few tokens engram_gate runs one block per (token, stream) and the
+    statistics pass one block per token, with the same reduction per stream."""
+    c = Case(B, T, hc, d, f32=f32, seed=7)
     zero = torch.zeros_like(c.cw)
     h1 = c.h.clone()
     g1 = c.run(h1, cw=zero)
@@ -157,7 +161,13 @@ def test_gate_conv_zero_filters_equal_gate():
     E.engram_gate(c.desc(), c.ids, RAW_VOCAB, c.kv, c.q_w, c.k_w, h2, g2)
     torch.cuda.synchronize()
     assert torch.equal(g1.reshape(-1, c.hc), g2)
-    assert_close(_vals(h1), _vals(h2), "zero filters vs plain gate", atol=0.0, rtol=2.0 ** -7)
+    # The gate forms h + alpha v in one fma, the convolution pass in separate fp32
+    # steps: where the sum cancels, the two differ by fp32 roundings at the scale
+    # of the operands before the bf16 rounding of the result.
+    v = _vals(c.kv).reshape(c.B, c.T, c.hc + 1, c.d)[:, :, c.hc:]
+    ops = 2.0 ** -23 * (np.abs(_vals(c.h)) + np.abs(v))
+    assert_close(_vals(h1), _vals(h2), "zero filters vs plain gate", atol=0.0, rtol=2.0 ** -7,
+                 extra=ops)
 
 
 @pytest.mark.parametrize("f32", [False, True], ids=["bf16", "f32"])
