@@ -941,7 +941,25 @@ def fp8_prefill_bench(gw, steps: int, warmup: int):
     tflops = 2.0 * T * N_out * S * 256 / (st[3] * 1e-3) / 1e12
     ceiling = mfma_ceiling_fp8(e_codes, wc, e_scales, wsc)
     ceiling["projection_frac_of_ceiling"] = round(tflops / ceiling["achieved"], 4)
-    del rows, e_codes, e_scales, kv, gates, wc, wsc
+    # the decode-sized projection: the first 256 tokens' rows against the same
+    # weight (engram_project_mx alone, back-to-back calls between two events)
+    dec = 256
+    kv_dec = torch.empty((dec, N_out), dtype=torch.bfloat16, device="cuda")
+    n_dec = E.engram_project_mx_workspace_size(dec, S, N_out)
+    ws_dec = torch.empty(n_dec, dtype=torch.uint8, device="cuda") if n_dec else None
+    for _ in range(3):
+        E.engram_project_mx(e_codes[:dec], e_scales[:dec], S, wc, wsc, kv_dec, dec, N_out,
+                            ws_dec, n_dec)
+    dev_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    dev_ev[0].record(stream)
+    for _ in range(20):
+        E.engram_project_mx(e_codes[:dec], e_scales[:dec], S, wc, wsc, kv_dec, dec, N_out,
+                            ws_dec, n_dec)
+    dev_ev[1].record(stream)
+    torch.cuda.synchronize()
+    dec_us = 1e3 * dev_ev[0].elapsed_time(dev_ev[1]) / 20
+    w_bytes = N_out * S * 256 * (1 + 1 / 32)
+    del rows, e_codes, e_scales, kv, gates, wc, wsc, kv_dec, ws_dec
     return {"workload": "prefill layer forward as above, projection weight in block-scaled FP8 "
                         "(E4M3 + one E8M0 scale per 32 inputs), rows fed to the FP8 MFMA "
                         "without dequantisation",
@@ -951,7 +969,11 @@ def fp8_prefill_bench(gw, steps: int, warmup: int):
                           "gate_sums": round(st[4], 4)},
             "project_mx": {"achieved": round(tflops, 2), "peak": FP8_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(tflops / FP8_PEAK_TFLOPS, 4)},
-            "mfma_ceiling": ceiling}
+            "mfma_ceiling": ceiling,
+            "decode_projection": {"tokens": dec, "us": round(dec_us, 2),
+                                  "weight_GBps": round(w_bytes / (dec_us * 1e-6) / 1e9, 1),
+                                  "what": "engram_project_mx on 256 tokens' rows (the decode "
+                                          "size), 20 back-to-back calls between two events"}}
 
 
 def hash_layers_bench(reps: int):

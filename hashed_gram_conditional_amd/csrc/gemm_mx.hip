@@ -32,6 +32,9 @@
 // k+1 to LDS and at once reloads each with step k+2, spread over the step's
 // first tiles, so every load has a full step to arrive. Scales travel as one
 // dword (4 blocks) per row per step.
+//
+// Calls of at most 256 tokens (decode) run gemm_mx_skinny_kernel: every CU takes
+// all tokens against its own weight rows, with no split of K (below).
 
 #include "gemm_tiles.h"
 
@@ -349,6 +352,220 @@ void gemm_mx_streamk_kernel(MxOperands op, uint16_t *__restrict__ C, float *__re
   }
 }
 
+// ---- skinny calls: one token tile, columns dealt to every CU ----------------------
+// gemm_bf16_skinny_kernel's schedule on the block-scaled operands. With at most
+// 256 tokens (decode) block b takes every token against its own 32 * NT weight
+// rows (96 or 128 for 25600 rows over 256 CUs), so the weight crosses HBM once
+// and nothing is split over K. The weight streams kMsRing - 1 K-steps ahead
+// through a register ring, e (the same for every block, from L2) 2 steps ahead;
+// both pass through two LDS stages in gemm_mx_kernel's layout and fragment order.
+// Wave w owns tokens [64 w, 64 w + 64). Each output sums its 64-input chunks in
+// increasing order in one accumulator with the same MFMA and scale bytes as
+// gemm_mx_kernel, so the two give the same bits. Every thread loads a weight
+// row's scale dword (threads 128-255 repeat rows 0-127 into spare LDS words), so
+// no thread-dependent branch splits the loop.
+constexpr int kMsMaxCols = 128;
+constexpr int kMsRing = 6;
+struct MxSkLds {
+  uint8_t w[2][kMsMaxCols * kMxBk];
+  uint8_t e[2][BM * kMxBk];
+  uint32_t ws[2][2 * kMsMaxCols];   // entries 128-255 repeat 0-127
+  uint32_t es[2][BM];
+};
+
+template <int NT>
+__device__ __forceinline__ void mx_skinny_block(const MxOperands &op, uint16_t *__restrict__ C, int M,
+                                                int N, int c0, MxSkLds &lds) {
+  const int K = op.segments * 256;
+  const int KB = K / 32;
+  const int KT = K / kMxBk;                 // a multiple of kMsRing (checked by the launcher)
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cols = min(32 * NT, N - c0);
+  const int toks = min(M, BM);
+  const __amdgpu_buffer_rsrc_t rsW = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(op.w_codes + (int64_t)c0 * K), 0, cols * K, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rsWs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(op.w_scales + (int64_t)c0 * KB), 0, cols * KB, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rsE = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(op.e_codes), 0, toks * K, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rsEs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(op.e_scales), 0, toks * KB, kBufferFlags);
+  // code chunk q of a step: row q * 32 + t / 8, 16-byte column t % 8
+  const int g_row = tid >> 3, g_chunk = tid & 7;
+  const int g_voff = g_row * K + g_chunk * 16;
+  const int s_off = g_row * kMxBk + ((g_chunk ^ (g_row & 7) ^ ((g_row >> 3) & 1)) << 4);
+  const int frow = lane & 31, h = lane >> 5;
+  const int fsw = (frow & 7) ^ ((frow >> 3) & 1);
+  const int b_base = (wave * 64 + frow) * kMxBk;
+  const int f0lo = ((0 + h) ^ fsw) << 4, f0hi = ((2 + h) ^ fsw) << 4;
+  const int f1lo = ((4 + h) ^ fsw) << 4, f1hi = ((6 + h) ^ fsw) << 4;
+
+  uint4 wr[kMsRing][4], er[2][8];
+  uint32_t wsr[kMsRing], esr[2];
+  f32x16 acc[NT][2];
+#pragma unroll
+  for (int i = 0; i < NT; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  i32x8 b0[2], b1[2], aC, aN;
+  uint32_t aS[NT], bS[2];
+
+#define MS_KT(kt_) ((kt_) < KT ? (kt_) : KT - 1)
+#define MS_LOADE(slot, kt_, q0, q1)                                                           \
+  _Pragma("unroll") for (int q = q0; q < q1; ++q)                                           \
+    er[slot][q] = load16(rsE, g_voff, q * 32 * K + MS_KT(kt_) * kMxBk);
+#define MS_LOADES(slot, kt_) esr[slot] = load4(rsEs, tid * KB, MS_KT(kt_) * 4);
+#define MS_LOADW(slot, kt_)                                                                   \
+  _Pragma("unroll") for (int q = 0; q < 4; ++q)                                             \
+    wr[slot][q] = load16(rsW, g_voff, q * 32 * K + MS_KT(kt_) * kMxBk);                     \
+  wsr[slot] = load4(rsWs, (tid & 127) * KB, MS_KT(kt_) * 4);
+#define MS_STOREE(st, slot, q0, q1)                                                           \
+  _Pragma("unroll") for (int q = q0; q < q1; ++q)                                           \
+    *reinterpret_cast<uint4 *>(&lds.e[st][s_off + q * 32 * kMxBk]) = er[slot][q];
+#define MS_STOREES(st, slot) lds.es[st][tid] = esr[slot];
+#define MS_STOREW(st, slot)                                                                   \
+  _Pragma("unroll") for (int q = 0; q < 4; ++q)                                             \
+    *reinterpret_cast<uint4 *>(&lds.w[st][s_off + q * 32 * kMxBk]) = wr[slot][q];           \
+  lds.ws[st][tid] = wsr[slot];
+#define MS_FRAG(buf, base, c)                                                                 \
+  join16(*reinterpret_cast<const uint4 *>(&(buf)[(base) + ((c) ? f1lo : f0lo)]),            \
+         *reinterpret_cast<const uint4 *>(&(buf)[(base) + ((c) ? f1hi : f0hi)]))
+#define MS_FRAGA(st, c, i) MS_FRAG(lds.w[st], ((i) * 32 + frow) * kMxBk, c)
+#define MS_FRAGSB(st, c, dst_b)                                                               \
+  _Pragma("unroll") for (int j = 0; j < 2; ++j)                                             \
+    dst_b[j] = MS_FRAG(lds.e[st], b_base + j * 32 * kMxBk, c);
+#define MS_SCALES(st)                                                                         \
+  _Pragma("unroll") for (int i = 0; i < NT; ++i) aS[i] = lds.ws[st][i * 32 + frow];         \
+  _Pragma("unroll") for (int j = 0; j < 2; ++j) bS[j] = lds.es[st][wave * 64 + j * 32 + frow];
+#define MS_SB(word, c) ((int)(((word) >> (8 * (2 * (c) + h))) & 0xFFu))
+#define MS_TILE(i, A, B, c)                                                                   \
+  _Pragma("unroll") for (int j = 0; j < 2; ++j)                                             \
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                            \
+        A, B[j], acc[i][j], 0, 0, 0, MS_SB(aS[i], c), 0, MS_SB(bS[j], c));
+#define MS_FENCE() __builtin_amdgcn_sched_barrier(0)
+// Step kt (ring slot s = kt % kMsRing) computes from stage s & 1: its first
+// 64-input chunk over the tiles, with the A fragment of the next tile read ahead,
+// then the second. Spread over the first chunk's tiles it stores e and the
+// weight of step kt + 1 (loaded earlier) into the other stage, and loads e of
+// step kt + 2 and the weight of step kt + kMsRing - 1.
+#define MS_STEP(s)                                                                            \
+  {                                                                                         \
+    const int P = (s) & 1, Q = P ^ 1;                                                       \
+    const int ws_ = ((s) + 1) % kMsRing, wl_ = ((s) + kMsRing - 1) % kMsRing;               \
+    _Pragma("unroll") for (int i = 0; i < NT; ++i) {                                        \
+      aN = i + 1 < NT ? MS_FRAGA(P, 0, i + 1) : MS_FRAGA(P, 1, 0);                          \
+      if (i == 0) { MS_FRAGSB(P, 1, b1) }                                                   \
+      if (i == 0) { MS_LOADE(P, kt + (s) + 2, 0, 4) MS_STOREE(Q, Q, 0, 4) }                 \
+      if (i == 1) { MS_LOADE(P, kt + (s) + 2, 4, 8) MS_LOADES(P, kt + (s) + 2)              \
+                    MS_STOREE(Q, Q, 4, 8) MS_STOREES(Q, Q) }                                \
+      if (i == (NT > 2 ? 2 : NT - 1)) { MS_LOADW(wl_, kt + (s) + kMsRing - 1) MS_STOREW(Q, ws_) } \
+      MS_TILE(i, aC, b0, 0)                                                                 \
+      aC = aN;                                                                              \
+      MS_FENCE();                                                                           \
+    }                                                                                       \
+    _Pragma("unroll") for (int i = 0; i < NT; ++i) {                                        \
+      if (i + 1 < NT) aN = MS_FRAGA(P, 1, i + 1);                                           \
+      MS_TILE(i, aC, b1, 1)                                                                 \
+      if (i + 1 < NT) aC = aN;                                                              \
+      MS_FENCE();                                                                           \
+    }                                                                                       \
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                       \
+    MS_FENCE();                                                                             \
+    MS_FRAGSB(Q, 0, b0)                                                                     \
+    aC = MS_FRAGA(Q, 0, 0);                                                                 \
+    MS_SCALES(Q)                                                                            \
+  }
+  // prologue: the weight of steps 0 .. kMsRing - 2, E of steps 0 and 1; step 0 into stage 0
+#pragma unroll
+  for (int s = 0; s < kMsRing - 1; ++s) { MS_LOADW(s, s) }
+  MS_LOADE(0, 0, 0, 8)
+  MS_LOADES(0, 0)
+  MS_LOADE(1, 1, 0, 8)
+  MS_LOADES(1, 1)
+  MS_STOREW(0, 0)
+  MS_STOREE(0, 0, 0, 8)
+  MS_STOREES(0, 0)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  MS_FRAGSB(0, 0, b0)
+  aC = MS_FRAGA(0, 0, 0);
+  MS_SCALES(0)
+  for (int kt = 0; kt < KT; kt += kMsRing) {
+    MS_STEP(0) MS_STEP(1) MS_STEP(2) MS_STEP(3) MS_STEP(4) MS_STEP(5)
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#undef MS_STEP
+#undef MS_FENCE
+#undef MS_TILE
+#undef MS_FRAGA
+#undef MS_FRAGSB
+#undef MS_SB
+#undef MS_SCALES
+#undef MS_FRAG
+#undef MS_STOREW
+#undef MS_STOREES
+#undef MS_STOREE
+#undef MS_LOADW
+#undef MS_LOADES
+#undef MS_LOADE
+#undef MS_KT
+  // accumulator r of (i, j): column c0 + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4,
+  // token 64 wave + 32 j + lane % 32
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int m = wave * 64 + j * 32 + frow;
+    if (m >= M) continue;
+    uint16_t *crow = C + (int64_t)m * N;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = c0 + i * 32 + g * 8 + h * 4;
+        if (n < N) {
+          uint2 v;
+          v.x = engram::pack_bf16x2(acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1]);
+          v.y = engram::pack_bf16x2(acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]);
+          *reinterpret_cast<uint2 *>(crow + n) = v;
+        }
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_mx_skinny_kernel(MxOperands op, uint16_t *__restrict__ C, int M, int N, int w_lo, int wide) {
+  __shared__ __align__(1024) MxSkLds lds;
+  const int b = blockIdx.x;
+  const int c0 = b * w_lo + min(b, wide) * 32;
+  if (c0 >= N) return;
+  const int nt = (w_lo + (b < wide ? 32 : 0)) / 32;
+  if (nt == 4) mx_skinny_block<4>(op, C, M, N, c0, lds);
+  else if (nt == 3) mx_skinny_block<3>(op, C, M, N, c0, lds);
+  else mx_skinny_block<2>(op, C, M, N, c0, lds);
+}
+
+// The skinny schedule, when it applies: at most one token tile, whole rings of
+// K-steps, and 64-128 weight rows per CU. w_lo = 32 floor(n / (32 G)); the first
+// `wide` blocks take 32 rows more.
+hipError_t plan_mx_skinny(int64_t m, int64_t n, int32_t segments, int &w_lo, int &wide,
+                          int &blocks) {
+  blocks = 0;
+  const int64_t kt = (int64_t)segments * 256 / kMxBk;
+  if (m > BM || kt % kMsRing != 0 || n > INT32_MAX) return hipSuccess;
+  int cus = 0;
+  const hipError_t err = cu_count(cus);
+  if (err != hipSuccess) return err;
+  const int64_t lo = (n / cus) / 32 * 32;
+  if (lo < 64 || lo + 32 > kMsMaxCols) return hipSuccess;
+  w_lo = (int)lo;
+  wide = (int)((n - (int64_t)cus * lo + 31) / 32);
+  blocks = cus;
+  return hipSuccess;
+}
+
 }  // namespace
 
 hipError_t engram_launch_gemm_mx(const uint8_t *w_codes, const uint8_t *w_scales,
@@ -358,8 +575,16 @@ hipError_t engram_launch_gemm_mx(const uint8_t *w_codes, const uint8_t *w_scales
                                  hipStream_t stream) {
   if (m <= 0 || n <= 0) return hipSuccess;
   const MxOperands op{w_codes, w_scales, e_codes, e_scales, segments};
+  int w_lo = 0, wide = 0, sk_blocks = 0;
+  hipError_t err = plan_mx_skinny(m, n, segments, w_lo, wide, sk_blocks);
+  if (err != hipSuccess) return err;
+  if (sk_blocks > 0) {
+    hipLaunchKernelGGL(gemm_mx_skinny_kernel, dim3((unsigned)sk_blocks), dim3(kWideThreads), 0,
+                       stream, op, kv, (int)m, (int)n, w_lo, wide);
+    return hipGetLastError();
+  }
   StreamK sk;
-  hipError_t err = plan_streamk(m, n, (int64_t)segments * 256 / kMxBk, sk);
+  err = plan_streamk(m, n, (int64_t)segments * 256 / kMxBk, sk);
   if (err != hipSuccess) return err;
   const int tiles_m = sk.tiles_m;
   const int tiles_n = (int)((n + BN - 1) / BN);
@@ -405,8 +630,12 @@ hipError_t engram_gemm_mx_whole_tiles(int64_t m, int64_t n, int32_t segments, bo
 hipError_t engram_gemm_mx_workspace(int64_t m, int64_t n, int32_t segments, size_t *bytes) {
   *bytes = 0;
   if (m <= 0 || n <= 0) return hipSuccess;
+  int w_lo = 0, wide = 0, sk_blocks = 0;
+  hipError_t err = plan_mx_skinny(m, n, segments, w_lo, wide, sk_blocks);
+  if (err != hipSuccess) return err;
+  if (sk_blocks > 0) return hipSuccess;
   StreamK sk;
-  const hipError_t err = plan_streamk(m, n, (int64_t)segments * 256 / kMxBk, sk);
+  err = plan_streamk(m, n, (int64_t)segments * 256 / kMxBk, sk);
   if (err != hipSuccess) return err;
   *bytes = (size_t)sk.blocks * 2 * kWideOutputs * kWideThreads * sizeof(float);
   return hipSuccess;

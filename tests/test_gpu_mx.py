@@ -84,6 +84,10 @@ def _mx_case(M, N, S, seed):
 
 
 def _project_mx(rows, codes, scales, M, N, S, with_ws):
+    return O.bf16_bits_to_f64(_project_mx_bits(rows, codes, scales, M, N, S, with_ws))
+
+
+def _project_mx_bits(rows, codes, scales, M, N, S, with_ws):
     n = E.engram_project_mx_workspace_size(M, S, N) if with_ws else 0
     ws = torch.empty(max(n, 256), dtype=torch.uint8, device=DEV) if n else None
     kv = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
@@ -92,7 +96,7 @@ def _project_mx(rows, codes, scales, M, N, S, with_ws):
     E.engram_project_mx(e_codes, e_scales, S, to_device(codes), to_device(scales), kv, M, N,
                         ws, n)
     torch.cuda.synchronize()
-    return O.bf16_bits_to_f64(bf16_bits(kv))
+    return bf16_bits(kv)
 
 
 # shapes: tiny, ragged, a wide-tile grid (>= 256 tiles), the decode shape split
@@ -107,6 +111,24 @@ def test_project_mx_against_oracle(M, N, S):
     for with_ws in (True, False):
         got = _project_mx(rows, codes, scales, M, N, S, with_ws)
         assert_close(got, exact, f"kv mx {M}x{N} S={S} ws={with_ws}", atol=0, rtol=0, extra=tol)
+
+
+@pytest.mark.parametrize("N", [25600, 16384], ids=["rows_96_128_per_CU", "rows_64_per_CU"])
+def test_project_mx_decode_bits_equal_wide_tiles(N):
+    """Calls of at most 256 tokens take the skinny schedule (every token against
+    one CU's weight rows, K not split); a 300-token call without a workspace
+    takes one block per 256 x 256 tile over the whole K. Both sum each output's
+    64-input chunks in order in one accumulator, so a decode call's kv is the
+    bits of the same rows in the larger call."""
+    S, big = 24, 300
+    say(f"project_mx decode vs wide tiles, N={N}")
+    rng = np.random.default_rng(N)
+    rows = _rows_of(N, rng.integers(0, 10 ** 9, big * S)).reshape(big, S, 264)
+    codes, scales = gen.quantize_mx_e4m3(rng.normal(0.0, 0.02, (N, S * 256)))
+    ref = _project_mx_bits(rows, codes, scales, big, N, S, with_ws=False)
+    for m in (256, 200, 1):
+        got = _project_mx_bits(rows[:m], codes, scales, m, N, S, with_ws=True)
+        assert np.array_equal(got, ref[:m]), f"{m} tokens"
 
 
 def test_project_mx_single_products_exact():
