@@ -25,9 +25,8 @@
 // so a stream's loads, its one barrier and its update overlap the other
 // streams' instead of queueing behind them in one block. Its thread count,
 // chunk ownership and reduction order are the per-token kernel's, so the bits
-// are too. The statistics mode keeps the per-token block, which loads a token's
-// whole h and k at once (up to 4 streams) and lets the streams share one
-// barrier.
+// are too; the block of stream 0 also forms the statistics mode's mean square
+// of the value row.
 //
 // With a stats buffer the kernel is the first half of the short-convolution
 // variant: it stores each token's gates and the mean square of its value row
@@ -46,7 +45,6 @@ namespace {
 constexpr int kMaxThreads = 512;
 constexpr int kMaxHc = 8;
 constexpr int kChunk = 8;        // elements per chunk
-constexpr int kAllStreams = 4;   // streams held at once by the few-token variant
 
 template <bool F32>
 using Chunk = engram::Chunk8<F32>;
@@ -54,7 +52,7 @@ using Chunk = engram::Chunk8<F32>;
 // Every byte the gate touches is used once, so its loads and stores carry the
 // nontemporal hint (5 % faster at 32768 tokens than cached accesses).
 
-template <bool F32, int CPT, bool AS>
+template <bool F32, int CPT>
 __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
     const int32_t *__restrict__ ids, EngramDeadRule dead_rule, const void *__restrict__ kv,
     const float *__restrict__ q_w, const float *__restrict__ k_w, void *__restrict__ h,
@@ -115,100 +113,7 @@ __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
       w[4] = q1.x * k1.x; w[5] = q1.y * k1.y; w[6] = q1.z * k1.z; w[7] = q1.w * k1.w;
     }
   };
-  // The gate of stream m from its three block-wide sums.
-  auto gate_of = [&](int m) -> float {
-    float a = 0.f, b = 0.f, c2 = 0.f;
-    for (int w = 0; w < nwaves; ++w) {
-      a += red[w][m][0];
-      b += red[w][m][1];
-      c2 += red[w][m][2];
-    }
-    const float rh = 1.0f / sqrtf(a * inv_d + eps);
-    const float rk = 1.0f / sqrtf(b * inv_d + eps);
-    const float sc = c2 * rh * rk * inv_sqrt_d;
-    const float z = plain ? sc : copysignf(sqrtf(fmaxf(fabsf(sc), clamp)), sc);
-    return 1.0f / (1.0f + expf(-z));
-  };
-  // Partial sums of stream m over this thread's chunks: sum h^2, sum k^2, sum h q_w k_w k.
-  auto partial = [&](int m, const Chunk<F32> (&hm)[CPT], const Chunk<F32> (&km)[CPT], float &shh,
-                     float &skk, float &shk) {
-    shh = skk = shk = 0.f;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ci = tid + c * nthreads;
-      if (ci < cps) {
-        float w[8];
-        scales(m, ci, w);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float he = hm[c][e];
-          const float ke = km[c][e];
-          shh = fmaf(he, he, shh);
-          skk = fmaf(ke, ke, skk);
-          shk = fmaf(he * w[e], ke, shk);
-        }
-      }
-    }
-    shh = engram::warp_sum(shh);
-    skk = engram::warp_sum(skk);
-    shk = engram::warp_sum(shk);
-    if (lane == 0) {
-      red[wave][m][0] = shh;
-      red[wave][m][1] = skk;
-      red[wave][m][2] = shk;
-    }
-  };
-  auto update = [&](int m, const Chunk<F32> (&hm)[CPT], float alpha) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ci = tid + c * nthreads;
-      if (ci < cps) {
-        float o[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = fmaf(alpha, vv[c][e], hm[c][e]);
-        Chunk<F32>::store_nt(h, h_row + (int64_t)m * cps + ci, o);
-      }
-    }
-  };
-
-  if constexpr (AS) {
-    // Few tokens (decode): every stream's h and k are loaded at once and the
-    // streams share one barrier, so a token costs one memory round trip
-    // instead of one per stream.
-    Chunk<F32> hh[kAllStreams][CPT], kk[kAllStreams][CPT];
-#pragma unroll
-    for (int m = 0; m < kAllStreams; ++m) {
-      if (m < hc) {
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-          const int ci = tid + c * nthreads;
-          if (ci < cps) {
-            hh[m][c].load_nt(h, h_row + (int64_t)m * cps + ci);
-            kk[m][c].load_nt(kv, kv_row + (int64_t)m * cps + ci);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < kAllStreams; ++m) {
-      if (m < hc) {
-        float shh, skk, shk;
-        partial(m, hh[m], kk[m], shh, skk, shk);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < kAllStreams; ++m) {
-      if (m < hc) {
-        const float alpha = gate_of(m);
-        if (tid == 0) {
-          if (gate_out != nullptr) gate_out[t * hc + m] = alpha;
-          if (stats != nullptr) stats[t * (hc + 1) + m] = alpha;
-        }
-        if (stats == nullptr) update(m, hh[m], alpha);
-      }
-    }
-  } else {
+  {
     // Stream by stream: the gate of stream m depends on its own h and k only, so
     // its h is reduced, gated and updated from registers before the next stream
     // is read; h crosses HBM once in each direction.
@@ -284,20 +189,29 @@ __global__ __launch_bounds__(kMaxThreads) void gate_kernel(
 
 // One (token, stream) pair per block, blockIdx.x the token and blockIdx.y the
 // stream: gate_kernel's arithmetic for that stream (the same chunks per thread,
-// fma order, wave sums and order of the waves' partial sums), without the
-// statistics output.
+// fma order, wave sums and order of the waves' partial sums). With a stats
+// buffer the block stores the stream's gate there instead of updating h, and
+// the block of stream 0 also stores the value row's mean square.
 template <bool F32, int CPT>
 __global__ __launch_bounds__(kMaxThreads) void gate_stream_kernel(
     const int32_t *__restrict__ ids, EngramDeadRule dead_rule, const void *__restrict__ kv,
     const float *__restrict__ q_w, const float *__restrict__ k_w, void *__restrict__ h,
-    float *__restrict__ gate_out, int hc, int dim, float eps, float clamp, int plain) {
+    float *__restrict__ gate_out, float *__restrict__ stats, int hc, int dim, float eps,
+    float clamp, int plain) {
   __shared__ float red[kMaxThreads / engram::kWave][3];
+  __shared__ float red_v[kMaxThreads / engram::kWave];
   const int64_t t = blockIdx.x;
   const int m = blockIdx.y;
   const int tid = threadIdx.x;
   const int nthreads = blockDim.x;
   if (engram_dead(dead_rule, ids[t])) {   // DEAD: gate 0, the stream untouched
-    if (gate_out != nullptr && tid == 0) gate_out[t * hc + m] = 0.f;
+    if (tid == 0) {
+      if (gate_out != nullptr) gate_out[t * hc + m] = 0.f;
+      if (stats != nullptr) {
+        stats[t * (hc + 1) + m] = 0.f;
+        if (m == 0) stats[t * (hc + 1) + hc] = 0.f;
+      }
+    }
     return;
   }
   const int cps = dim / kChunk;
@@ -315,6 +229,20 @@ __global__ __launch_bounds__(kMaxThreads) void gate_stream_kernel(
       hh[c].load_nt(h, h_row + ci);
       kk[c].load_nt(kv, kv_row + (int64_t)m * cps + ci);
     }
+  }
+  const bool value_stats = stats != nullptr && m == 0;
+  if (value_stats) {
+    float svv = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ci = tid + c * nthreads;
+      if (ci < cps) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) svv = fmaf(vv[c][e], vv[c][e], svv);
+      }
+    }
+    svv = engram::warp_sum(svv);
+    if (lane == 0) red_v[wave] = svv;
   }
   float shh = 0.f, skk = 0.f, shk = 0.f;
 #pragma unroll
@@ -363,7 +291,16 @@ __global__ __launch_bounds__(kMaxThreads) void gate_stream_kernel(
   const float sc = c2 * rh * rk * inv_sqrt_d;
   const float z = plain ? sc : copysignf(sqrtf(fmaxf(fabsf(sc), clamp)), sc);
   const float alpha = 1.0f / (1.0f + expf(-z));
-  if (tid == 0 && gate_out != nullptr) gate_out[t * hc + m] = alpha;
+  if (tid == 0) {
+    if (gate_out != nullptr) gate_out[t * hc + m] = alpha;
+    if (stats != nullptr) stats[t * (hc + 1) + m] = alpha;
+    if (value_stats) {
+      float svv = 0.f;
+      for (int w = 0; w < nwaves; ++w) svv += red_v[w];
+      stats[t * (hc + 1) + hc] = svv * inv_d;
+    }
+  }
+  if (stats != nullptr) return;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int ci = tid + c * nthreads;
@@ -394,20 +331,20 @@ hipError_t gate_threads(int64_t tokens, int dim, int &threads, int &cpt, bool &f
 }
 
 template <bool F32>
-hipError_t launch(int cpt, int threads, bool few, bool all_streams, const int32_t *ids,
+hipError_t launch(int cpt, int threads, bool few, const int32_t *ids,
                   EngramDeadRule dead_rule,
                   const void *kv, const float *q_w, const float *k_w, void *h, float *gate_out,
                   float *stats, int64_t tokens, int hc, int dim, float eps, float clamp,
                   int plain, hipStream_t stream) {
-#define ENGRAM_GATE_CASE(N, AS)                                                             \
-  hipLaunchKernelGGL((gate_kernel<F32, N, AS>), dim3((unsigned)tokens), dim3(threads), 0,   \
+#define ENGRAM_GATE_CASE(N)                                                                 \
+  hipLaunchKernelGGL((gate_kernel<F32, N>), dim3((unsigned)tokens), dim3(threads), 0,       \
                      stream, ids, dead_rule, kv, q_w, k_w, h, gate_out, stats, hc, dim,     \
                      eps, clamp, plain)
-  if (few && stats == nullptr && cpt <= 2) {
+  if (few && cpt <= 2) {
 #define ENGRAM_GATE_STREAM_CASE(N)                                                          \
   hipLaunchKernelGGL((gate_stream_kernel<F32, N>), dim3((unsigned)tokens, (unsigned)hc),     \
-                     dim3(threads), 0, stream, ids, dead_rule, kv, q_w, k_w, h, gate_out, hc, \
-                     dim, eps, clamp, plain)
+                     dim3(threads), 0, stream, ids, dead_rule, kv, q_w, k_w, h, gate_out,    \
+                     stats, hc, dim, eps, clamp, plain)
     if (cpt == 1)
       ENGRAM_GATE_STREAM_CASE(1);
     else
@@ -415,23 +352,15 @@ hipError_t launch(int cpt, int threads, bool few, bool all_streams, const int32_
 #undef ENGRAM_GATE_STREAM_CASE
     return hipGetLastError();
   }
-  if (all_streams) {
-    switch (cpt) {
-      case 1: ENGRAM_GATE_CASE(1, true); break;
-      case 2: ENGRAM_GATE_CASE(2, true); break;
-      default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-  }
   switch (cpt) {
-    case 1: ENGRAM_GATE_CASE(1, false); break;
-    case 2: ENGRAM_GATE_CASE(2, false); break;
-    case 3: ENGRAM_GATE_CASE(3, false); break;
-    case 4: ENGRAM_GATE_CASE(4, false); break;
-    case 5: ENGRAM_GATE_CASE(5, false); break;
-    case 6: ENGRAM_GATE_CASE(6, false); break;
-    case 7: ENGRAM_GATE_CASE(7, false); break;
-    case 8: ENGRAM_GATE_CASE(8, false); break;
+    case 1: ENGRAM_GATE_CASE(1); break;
+    case 2: ENGRAM_GATE_CASE(2); break;
+    case 3: ENGRAM_GATE_CASE(3); break;
+    case 4: ENGRAM_GATE_CASE(4); break;
+    case 5: ENGRAM_GATE_CASE(5); break;
+    case 6: ENGRAM_GATE_CASE(6); break;
+    case 7: ENGRAM_GATE_CASE(7); break;
+    case 8: ENGRAM_GATE_CASE(8); break;
     default:
       return hipErrorInvalidValue;
   }
@@ -451,13 +380,11 @@ hipError_t engram_launch_gate(bool f32, const int32_t *ids, EngramDeadRule dead_
   bool few = false;
   const hipError_t err = gate_threads(tokens, dim, threads, cpt, few);
   if (err != hipSuccess) return err;
-  // few tokens: a block per (token, stream); with the statistics output one
-  // memory round trip per token for up to kAllStreams streams
-  const bool all_streams = few && hc <= kAllStreams && cpt <= 2;
-  return f32 ? launch<true>(cpt, threads, few, all_streams, ids, dead_rule, kv, q_w, k_w, h,
-                            gate_out, stats, tokens, hc, dim, eps, clamp, plain, stream)
-             : launch<false>(cpt, threads, few, all_streams, ids, dead_rule, kv, q_w, k_w, h,
-                             gate_out, stats, tokens, hc, dim, eps, clamp, plain, stream);
+  // few tokens: a block per (token, stream)
+  return f32 ? launch<true>(cpt, threads, few, ids, dead_rule, kv, q_w, k_w, h, gate_out, stats,
+                            tokens, hc, dim, eps, clamp, plain, stream)
+             : launch<false>(cpt, threads, few, ids, dead_rule, kv, q_w, k_w, h, gate_out, stats,
+                             tokens, hc, dim, eps, clamp, plain, stream);
 }
 
 namespace {

@@ -149,9 +149,9 @@ def test_gate_conv_matches_oracle(B, T, hc, d, taps, dil, f32, mode, norm):
                          ids=["80x4x136", "decode256x4x5120", "64x8x5120", "f32_64x4x5120"])
 def test_gate_conv_zero_filters_equal_gate(B, T, hc, d, f32):
     """Filters at zero (the papers' init): the branch adds exactly the gated
-    value, so engram_gate_conv agrees with engram_gate. The gates are the same
-    bits: with few tokens engram_gate runs one block per (token, stream) and the
-    statistics pass one block per token, with the same reduction per stream."""
+    value, so engram_gate_conv agrees with engram_gate, and the gates are the
+    same bits (the statistics pass reduces each stream as the update does; with
+    few tokens both run one block per (token, stream))."""
     c = Case(B, T, hc, d, f32=f32, seed=7)
     zero = torch.zeros_like(c.cw)
     h1 = c.h.clone()
