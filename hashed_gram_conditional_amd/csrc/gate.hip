@@ -11,8 +11,9 @@
 // reciprocal roots of the mean squares, the update rounded to bf16 once) and
 // "布局与哈希探测" item 4 (masked rows are left untouched).
 //
-// One block per token: 128 threads when there are enough tokens to fill the
-// chip, 512 when there are few (decode). Each thread owns CPT chunks of 8
+// gate_kernel: one block per token, 128 threads when there are enough tokens
+// to fill the chip (512 for few tokens whose streams are too wide for
+// gate_stream_kernel, below). Each thread owns CPT chunks of 8
 // elements per stream (16-byte bf16 accesses). Streams are handled one after
 // another: the three reductions of stream m (sum h^2, sum k^2, sum h q_w k_w k)
 // need only its own h and k, so after one barrier its gate is known and its h,
