@@ -99,10 +99,12 @@ def _project_mx_bits(rows, codes, scales, M, N, S, with_ws):
     return bf16_bits(kv)
 
 
-# shapes: tiny, ragged, a wide-tile grid (>= 256 tiles), the decode shape split
-# over the CUs, odd K-step counts (S = 1, 3: 2 and 6 steps; S = 5: 10)
+# shapes: tiny, ragged, a wide-tile grid (>= 256 tiles), the decode shape (the
+# skinny schedule), a decode-sized call whose 8 K-steps do not fill the skinny
+# schedule's 6-step ring (split over K instead), odd K-step counts (S = 1, 3: 2
+# and 6 steps; S = 5: 10)
 @pytest.mark.parametrize("M,N,S", [(1, 8, 1), (31, 264, 3), (300, 520, 24), (257, 1032, 5),
-                                   (4100, 4104, 1), (256, 25600, 24)])
+                                   (4100, 4104, 1), (256, 25600, 24), (200, 20480, 4)])
 def test_project_mx_against_oracle(M, N, S):
     say(f"project_mx {M}x{N} S={S}")
     rows, codes, scales, e, w = _mx_case(M, N, S, M * 7 + N + S)
