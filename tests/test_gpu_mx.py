@@ -9,8 +9,8 @@ import numpy as np
 import pytest
 
 import oracle as O
-from tests.gpu_util import assert_close, kv_tolerance_mx, say
-from workloads import C3, gen
+from tests.gpu_util import assert_close, kv_tolerance_mx, oracle_rows, say
+from workloads import C3, C4, gen
 
 pytestmark = pytest.mark.gpu
 
@@ -21,7 +21,7 @@ if not torch.cuda.is_available():
 import hashed_gram_conditional_amd as E  # noqa: E402
 from workloads.device import bf16_bits, to_device  # noqa: E402
 from workloads.harness import GpuWorkload  # noqa: E402
-from tests.test_gpu_parity import S_A, S_B, _check_forward, _sample_tokens  # noqa: E402
+from tests.test_gpu_parity import S_A, S_B, _check_forward, _cleanup, _sample_tokens  # noqa: E402
 
 DEV = "cuda"
 
@@ -181,3 +181,25 @@ def test_forward_mx_prefill_sampled():
     _check_forward_mx(gw, gw.h, gates, _sample_tokens(gw, 2048, 7))
     del ws
     gw.free()
+
+
+def test_forward_mx_c4_decode_every_token():
+    """The decode step with the block-scaled FP8 weight: 256 sequences x 1 token
+    with their history on the 384,006,168-row (101.4 GB) table, the projection
+    in the skinny schedule. Every token against the oracle at the gate
+    tolerance, and the history after the token."""
+    say("forward_mx C4 decode: 256 x 1 token, 101.4 GB table, every token")
+    gw = GpuWorkload(C4, wkv_mx=True)
+    try:
+        ws, n = gw.workspace_mx()
+        gates = torch.full((C4.tokens, C4.hc), -1.0, dtype=torch.float32, device=DEV)
+        hout = torch.empty((C4.batch, 3), dtype=torch.int32, device=DEV)
+        E.engram_forward_mx(gw.params, gw.desc, gw.ids, gw.hist_in, hout, gw.table, gw.w_codes,
+                            gw.w_scales, gw.q_w, gw.k_w, gw.h, gates, ws, n)
+        torch.cuda.synchronize()
+        _check_forward_mx(gw, gw.h, gates, np.arange(C4.tokens))
+        _, exp_hist = oracle_rows(gw)
+        assert np.array_equal(hout.cpu().numpy(), exp_hist)
+    finally:
+        gw.free()
+        _cleanup()
