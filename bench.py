@@ -1121,6 +1121,28 @@ def decode_bench(steps: int, warmup: int, wkv_ld=None):
     torch.cuda.synchronize()
     conv_ms = ce[0].elapsed_time(ce[1]) / steps
     del cws, sv, ss, cw
+    # the same decode step with the block-scaled FP8 weight (quantised from the
+    # same wkv): engram_forward_mx, the history in place
+    from workloads import gen
+    from workloads.device import to_device
+    codes, scales = gen.wkv_mx(w)
+    wc, wsc = to_device(codes), to_device(scales)
+    del codes, scales
+    nmx = E.engram_forward_mx_workspace_size(gw.params, gw.desc)
+    mws = torch.empty(max(nmx, 1), dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        E.engram_forward_mx(gw.params, gw.desc, gw.ids, hist, hist, gw.table, wc, wsc, gw.q_w,
+                            gw.k_w, gw.h, gates, mws, nmx)
+    torch.cuda.synchronize()
+    me = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    me[0].record(stream)
+    for i in range(steps):
+        E.engram_forward_mx(gw.params, gw.desc, gw.ids, hist, hist, gw.table, wc, wsc, gw.q_w,
+                            gw.k_w, gw.h, gates, mws, nmx)
+    me[1].record(stream)
+    torch.cuda.synchronize()
+    mx_ms = me[0].elapsed_time(me[1]) / steps
+    del wc, wsc, mws
     res = {"workload": "decode: 256 sequences x 1 token with a 3-token history, 24 segments of "
                        "primes from 16,000,000 (384,006,168 x 264 B = 101.4 GB table), hc 4 x 5120, "
                        f"wkv rows {gw.wkv_ld} elements apart",
@@ -1138,7 +1160,12 @@ def decode_bench(steps: int, warmup: int, wkv_ld=None):
            "short_conv": {"workload": "the same step through engram_forward_conv (4 taps, "
                                       "dilation 3, 9-position history in place)",
                           "tokens_per_s": round(T / (conv_ms * 1e-3), 1),
-                          "ms_per_step": round(conv_ms, 4)}}
+                          "ms_per_step": round(conv_ms, 4)},
+           "fp8_wkv": {"workload": "the same step through engram_forward_mx, the projection "
+                                   "weight in block-scaled FP8 (E4M3 + one E8M0 scale per 32 "
+                                   "inputs)",
+                       "tokens_per_s": round(T / (mx_ms * 1e-3), 1),
+                       "ms_per_step": round(mx_ms, 4)}}
     gw.free()
     return res
 
