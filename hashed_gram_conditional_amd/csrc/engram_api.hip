@@ -987,12 +987,23 @@ int engram_forward_mx(const engram_hash_params *params, const engram_forward_des
   const size_t gemm_ws_bytes = workspace_bytes - (size_t)(gemm_ws - ws);
 
   const EngramHashArgs a = make_hash_args(params, 1);
-  hipError_t err = engram_launch_hash(a, params->token_map, ids, desc->batch, desc->seq,
-                                      hist_in, hist_out, row_ids, stream);
-  if (err != hipSuccess || ntok == 0) return hip_status(err);
-  err = engram_launch_gather_mx((const uint8_t *)table, desc->table_rows, row_ids, ntok * S,
-                                e_codes, e_scales, host, stream);
-  if (err != hipSuccess) return hip_status(err);
+  hipError_t err = hipSuccess;
+  // Decode-sized calls on an HBM table form and split each token's rows in one
+  // launch, as engram_forward does; others hash, then gather.
+  if (!host && ntok > 0 && ntok <= kHashGatherMaxTokens &&
+      (hist_out == nullptr || desc->seq == 1)) {
+    err = engram_launch_hash_gather_mx(a, params->token_map, ids, desc->batch, desc->seq,
+                                       hist_in, hist_out, (const uint8_t *)table,
+                                       desc->table_rows, e_codes, e_scales, stream);
+    if (err != hipSuccess) return hip_status(err);
+  } else {
+    err = engram_launch_hash(a, params->token_map, ids, desc->batch, desc->seq, hist_in,
+                             hist_out, row_ids, stream);
+    if (err != hipSuccess || ntok == 0) return hip_status(err);
+    err = engram_launch_gather_mx((const uint8_t *)table, desc->table_rows, row_ids, ntok * S,
+                                  e_codes, e_scales, host, stream);
+    if (err != hipSuccess) return hip_status(err);
+  }
   // As in engram_forward: whole tiles take the key side of the gate into the
   // projection's epilogue.
   bool sums = false;

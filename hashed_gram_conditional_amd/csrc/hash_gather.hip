@@ -15,7 +15,9 @@
 // (engram_rows::row_id); then each half-wave owns rows h, h + 4, ... of the
 // token, issues all its loads before converting any, and writes each row as
 // the gather kernel does (lane l: payload bytes 8l..8l+7 and scale l/4, 8 bf16
-// out, engram_rows::dequant8). The rows are the separate kernels' bits.
+// out, engram_rows::dequant8). The rows are the separate kernels' bits. The
+// split variant (for the block-scaled FP8 projection) copies each row's codes
+// and scales apart instead, as the row-splitting gather does.
 #include "row_device.h"
 
 namespace {
@@ -24,10 +26,12 @@ constexpr int kThreads = 128;
 constexpr int kHalves = kThreads / 32;
 constexpr int kMaxRowsPerHalf = (ENGRAM_MAX_SEGMENTS + kHalves - 1) / kHalves;
 
+template <bool SPLIT>
 __global__ __launch_bounds__(kThreads) void hash_gather_e4m3_kernel(
     EngramHashArgs a, const int32_t *__restrict__ token_map, const int32_t *__restrict__ ids,
     int64_t seq, const int32_t *hist_in, int32_t *hist_out, int commit_history,
-    const uint8_t *__restrict__ table, int64_t table_rows, uint16_t *__restrict__ out) {
+    const uint8_t *__restrict__ table, int64_t table_rows, uint16_t *__restrict__ out,
+    uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
   __shared__ uint64_t s_mix[ENGRAM_MAX_NGRAM - 1];
   __shared__ int64_t s_rid[ENGRAM_MAX_SEGMENTS];
   const int tid = threadIdx.x;
@@ -83,13 +87,28 @@ __global__ __launch_bounds__(kThreads) void hash_gather_e4m3_kernel(
       }
     }
   }
-  uint16_t *dst = out + g * (int64_t)S * ENGRAM_ROW_DIM_E4M3;
+  if constexpr (SPLIT) {
+    // row j of the token: its 256 codes and its 8 scales, bytes unchanged
 #pragma unroll
-  for (int k = 0; k < kMaxRowsPerHalf; ++k) {
-    const int j = half + k * kHalves;
-    if (j < S) {
-      const uint4 o = in[k] ? engram_rows::dequant8(q[k], sc[k]) : make_uint4(0u, 0u, 0u, 0u);
-      *reinterpret_cast<uint4 *>(dst + j * ENGRAM_ROW_DIM_E4M3 + 8 * l) = o;
+    for (int k = 0; k < kMaxRowsPerHalf; ++k) {
+      const int j = half + k * kHalves;
+      if (j < S) {
+        const int64_t r = g * (int64_t)S + j;
+        *reinterpret_cast<uint2 *>(codes + r * ENGRAM_ROW_DIM_E4M3 + 8 * l) =
+            in[k] ? q[k] : make_uint2(0u, 0u);
+        // lane l holds scale byte l / 4
+        if ((l & 3) == 0) scales[r * 8 + (l >> 2)] = in[k] ? (uint8_t)sc[k] : (uint8_t)0;
+      }
+    }
+  } else {
+    uint16_t *dst = out + g * (int64_t)S * ENGRAM_ROW_DIM_E4M3;
+#pragma unroll
+    for (int k = 0; k < kMaxRowsPerHalf; ++k) {
+      const int j = half + k * kHalves;
+      if (j < S) {
+        const uint4 o = in[k] ? engram_rows::dequant8(q[k], sc[k]) : make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4 *>(dst + j * ENGRAM_ROW_DIM_E4M3 + 8 * l) = o;
+      }
     }
   }
 }
@@ -104,8 +123,22 @@ hipError_t engram_launch_hash_gather_e4m3(const EngramHashArgs &a, const int32_t
   const int64_t ntok = batch * seq;
   if (ntok <= 0) return hipSuccess;
   if (a.layers != 1 || (hist_out != nullptr && seq != 1)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(hash_gather_e4m3_kernel, dim3((unsigned)ntok), dim3(kThreads), 0, stream, a,
-                     token_map, ids, seq, hist_in, hist_out, hist_out != nullptr ? 1 : 0, table,
-                     table_rows, out);
+  hipLaunchKernelGGL(hash_gather_e4m3_kernel<false>, dim3((unsigned)ntok), dim3(kThreads), 0,
+                     stream, a, token_map, ids, seq, hist_in, hist_out,
+                     hist_out != nullptr ? 1 : 0, table, table_rows, out, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t engram_launch_hash_gather_mx(const EngramHashArgs &a, const int32_t *token_map,
+                                        const int32_t *ids, int64_t batch, int64_t seq,
+                                        const int32_t *hist_in, int32_t *hist_out,
+                                        const uint8_t *table, int64_t table_rows, uint8_t *codes,
+                                        uint8_t *scales, hipStream_t stream) {
+  const int64_t ntok = batch * seq;
+  if (ntok <= 0) return hipSuccess;
+  if (a.layers != 1 || (hist_out != nullptr && seq != 1)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(hash_gather_e4m3_kernel<true>, dim3((unsigned)ntok), dim3(kThreads), 0,
+                     stream, a, token_map, ids, seq, hist_in, hist_out,
+                     hist_out != nullptr ? 1 : 0, table, table_rows, nullptr, codes, scales);
   return hipGetLastError();
 }

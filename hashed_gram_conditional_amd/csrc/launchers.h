@@ -17,6 +17,13 @@ hipError_t engram_launch_hash_gather_e4m3(const EngramHashArgs &a, const int32_t
                                           const int32_t *hist_in, int32_t *hist_out,
                                           const uint8_t *table, int64_t table_rows,
                                           uint16_t *out, hipStream_t stream);
+// The same rows split into codes [ntok * S, 256] and scales [ntok * S, 8], as
+// engram_launch_gather_mx writes them.
+hipError_t engram_launch_hash_gather_mx(const EngramHashArgs &a, const int32_t *token_map,
+                                        const int32_t *ids, int64_t batch, int64_t seq,
+                                        const int32_t *hist_in, int32_t *hist_out,
+                                        const uint8_t *table, int64_t table_rows, uint8_t *codes,
+                                        uint8_t *scales, hipStream_t stream);
 
 // host_table: the table is pinned host memory; the gather then runs on a few
 // CUs as a grid-strided kernel, leaving the rest to concurrent work.

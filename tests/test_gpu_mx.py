@@ -187,10 +187,12 @@ def test_forward_mx_c4_decode_every_token():
     """The decode step with the block-scaled FP8 weight: 256 sequences x 1 token
     with their history on the 384,006,168-row (101.4 GB) table, the projection
     in the skinny schedule. Every token against the oracle at the gate
-    tolerance, and the history after the token."""
+    tolerance, the history after the token, and the bits of the stage entry
+    points."""
     say("forward_mx C4 decode: 256 x 1 token, 101.4 GB table, every token")
     gw = GpuWorkload(C4, wkv_mx=True)
     try:
+        h0 = gw.h.clone()
         ws, n = gw.workspace_mx()
         gates = torch.full((C4.tokens, C4.hc), -1.0, dtype=torch.float32, device=DEV)
         hout = torch.empty((C4.batch, 3), dtype=torch.int32, device=DEV)
@@ -200,6 +202,22 @@ def test_forward_mx_c4_decode_every_token():
         _check_forward_mx(gw, gw.h, gates, np.arange(C4.tokens))
         _, exp_hist = oracle_rows(gw)
         assert np.array_equal(hout.cpu().numpy(), exp_hist)
+        # the step forms and splits the rows in one launch; the stage entry points
+        # (hash, then the row-splitting gather, the projection, the gate) give its bits
+        T, S = C4.tokens, C4.segments
+        rows = torch.empty((T, S), dtype=torch.int64, device=DEV)
+        E.engram_hash(gw.params, gw.ids, C4.batch, C4.seq, gw.hist_in, None, rows)
+        e_codes = torch.empty((T, S * 256), dtype=torch.uint8, device=DEV)
+        e_scales = torch.empty((T, S * 8), dtype=torch.uint8, device=DEV)
+        E.engram_gather_mx(gw.table, gw.rows, rows, T * S, e_codes, e_scales)
+        N = (C4.hc + 1) * C4.dim
+        kv = torch.empty((T, N), dtype=torch.bfloat16, device=DEV)
+        E.engram_project_mx(e_codes, e_scales, S, gw.w_codes, gw.w_scales, kv, T, N)
+        g2 = torch.empty_like(gates)
+        E.engram_gate(gw.desc, gw.ids, C4.raw_vocab, kv, gw.q_w, gw.k_w, h0, g2)
+        torch.cuda.synchronize()
+        assert torch.equal(h0.view(torch.int16), gw.h.view(torch.int16))
+        assert torch.equal(g2, gates)
     finally:
         gw.free()
         _cleanup()
