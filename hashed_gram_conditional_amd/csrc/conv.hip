@@ -139,8 +139,8 @@ __global__ __launch_bounds__(kThreads) void short_conv_kernel(
 // tokens and 256 (stream, 8-channel) pairs. The value chunks of the rows
 // [t0 - L, t0 + TB) are loaded once into a register window (each tap of each
 // token then indexes it statically), the rows' gates and mean squares once into
-// LDS, and the fully unrolled token loop has only independent loads left (h),
-// so many are in flight per thread. A tap whose row lies before its sequence's
+// LDS, and the run's h chunks are requested with them, so the fully unrolled
+// token loop waits for memory once. A tap whose row lies before its sequence's
 // start reads the history (or zero) instead of the window.
 template <int TAPS, int DIL, int TB>
 __global__ __launch_bounds__(kThreads) void short_conv_window_kernel(
@@ -200,6 +200,16 @@ __global__ __launch_bounds__(kThreads) void short_conv_window_kernel(
     row = row < 0 ? 0 : row >= ntok ? ntok - 1 : row;
     win[r].load(kv, row * kv_row + (int64_t)hc * cps + ci);
   }
+  // The run's h chunks as well: the loop below stores to h, so a load left in
+  // it could not be issued before the previous token's store and each token
+  // would wait for HBM in turn. Rows past the chunk read its last token's row.
+  const int64_t h_step = (int64_t)hc * cps;
+  engram::Chunk8<false> hh[TB];
+#pragma unroll
+  for (int i = 0; i < TB; ++i) {
+    const int64_t row = t0 + i < ntok ? t0 + i : ntok - 1;
+    hh[i].load_nt(h, (row * hc + m) * (int64_t)cps + ci);
+  }
 
   if (tid < nstat) s_stat[sr][scol] = stat_ok ? stat_v : 0.f;
   if (tid < TB) s_ids[tid] = (t0 + tid < ntok && !engram_dead(dead_rule, id_v)) ? id_v : -1;
@@ -227,7 +237,6 @@ __global__ __launch_bounds__(kThreads) void short_conv_window_kernel(
   const int seq32 = (int)seq;
   int b = (int)(t0 / seq32);
   int s = (int)(t0 - (int64_t)b * seq32) - 1;
-  const int64_t h_step = (int64_t)hc * cps;
   const int64_t h_base = (t0 * hc + m) * (int64_t)cps + ci;
 #pragma unroll
   for (int i = 0; i < TB; ++i) {
@@ -258,14 +267,11 @@ __global__ __launch_bounds__(kThreads) void short_conv_window_kernel(
         for (int e = 0; e < kChunk; ++e) u[e] = fmaf(w[e][j], rr * v[e], u[e]);
       }
     }
-    const int64_t hi = h_base + i * h_step;
-    engram::Chunk8<false> hh;
-    hh.load_nt(h, hi);
     const float a_t = s_stat[i + L][m];
     float o[kChunk];
 #pragma unroll
-    for (int e = 0; e < kChunk; ++e) o[e] = hh[e] + fmaf(a_t, win[i + L][e], silu(u[e]));
-    engram::Chunk8<false>::store_nt(h, hi, o);
+    for (int e = 0; e < kChunk; ++e) o[e] = hh[i][e] + fmaf(a_t, win[i + L][e], silu(u[e]));
+    engram::Chunk8<false>::store_nt(h, h_base + i * h_step, o);
   }
 }
 
