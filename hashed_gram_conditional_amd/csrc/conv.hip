@@ -29,7 +29,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kChunk = 8;
 constexpr int kMaxHcConv = 8;
-constexpr int kWindowTokens = 8;
+constexpr int kWindowTokens = 12;   // 228 VGPRs, 2 waves per SIMD (16 tokens: 256 and 1 wave)
 
 // The kernels issue few memory operations per arithmetic one, so they use the
 // hardware's exp2, reciprocal and reciprocal square root (about 1 ulp each)

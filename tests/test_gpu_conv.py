@@ -228,10 +228,11 @@ def test_gate_conv_chunks_carry_history(splits):
 
 
 def test_gate_conv_many_sequence_starts_with_history():
-    """128 sequences of 37 tokens: every call is large enough for the register-
-    window kernel, whose blocks then hold several sequence starts; the second
-    chunk reads its first 9 positions' taps from the carried history."""
-    c = Case(128, 37, 2, 64, seed=25, dead_frac=0.1)
+    """192 sequences of 37 tokens: every call (the chunks hold 3,840 and 3,264
+    tokens) is large enough for the register-window kernel, whose blocks then
+    hold several sequence starts; the second chunk reads its first 9
+    positions' taps from the carried history."""
+    c = Case(192, 37, 2, 64, seed=25, dead_frac=0.1)
     alpha, h_out, _ = c.oracle()
     h_ref = c.h.clone()
     g_ref = c.run(h_ref)
