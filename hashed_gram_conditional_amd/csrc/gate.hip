@@ -11,7 +11,7 @@
 // reciprocal roots of the mean squares, the update rounded to bf16 once) and
 // "布局与哈希探测" item 4 (masked rows are left untouched).
 //
-// gate_kernel: one block per token, 128 threads when there are enough tokens
+// gate_kernel: one block per token, 256 threads when there are enough tokens
 // to fill the chip (512 for few tokens whose streams are too wide for
 // gate_stream_kernel, below). Each thread owns CPT chunks of 8
 // elements per stream (16-byte bf16 accesses). Streams are handled one after
@@ -324,7 +324,7 @@ hipError_t gate_threads(int64_t tokens, int dim, int &threads, int &cpt, bool &f
   if (err != hipSuccess) return err;
   const int cps = dim / kChunk;
   few = tokens < 8 * (int64_t)cus;
-  threads = few ? kMaxThreads : 128;
+  threads = few ? kMaxThreads : 256;
   const int needed = ((cps + engram::kWave - 1) / engram::kWave) * engram::kWave;
   if (threads > needed) threads = needed;
   cpt = (cps + threads - 1) / threads;
