@@ -245,6 +245,17 @@ def test_gate_conv_many_sequence_starts_with_history():
     assert_close(_vals(h), _vals(h_ref), "two chunks vs one shot")
 
 
+
+def test_gate_conv_window_ragged_tail():
+    """97 sequences of 37 tokens: 3,589 tokens, one past a multiple of the
+    register-window kernel's 12-token blocks, so its last block holds a single
+    token; every position is checked against the oracle."""
+    c = Case(97, 37, 2, 64, seed=31, dead_frac=0.1)
+    alpha, h_out, _ = c.oracle()
+    h = c.h.clone()
+    g = c.run(h)
+    _check(c, h, g, alpha, h_out, "ragged tail")
+
 def test_gate_conv_short_first_chunk_without_history():
     """A first chunk shorter than the reach: history rows before the sequence
     start are zero gates, i.e. zero input to the convolution."""
